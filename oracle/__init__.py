@@ -1,0 +1,168 @@
+"""CPU oracle for the HSTU jagged causal attention forward.
+
+TEST INFRASTRUCTURE.  Only the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The HIP library and
+its Python binding never import it, and it imports nothing from them: the two
+share no code.  The only module both sides read is ``workloads`` (seeded input
+generation, no attention arithmetic).
+
+Two independent evaluations of the same definition live here:
+
+* ``fwd`` / ``rows``: the plain row-by-row fp64 loop in ``hstu_oracle.c``
+  (OpenMP over (sequence, head) pairs), built with gcc;
+* ``dense_unfused``: numpy fp64, one sequence at a time, written as the five
+  unfused steps the Ascend HSTU blog ("都是生成式推荐，为什么昇腾这么快？",
+  §1) gives as its PyTorch definition: scores = Q K^T, scores *= alpha,
+  silu, multiply by mask / n with an explicit lower-triangular 0/1 mask
+  (§3.1-§3.2), then scores @ V.  Jagged packing follows §4.2 of that page.
+
+Parity status: pinned.  The test suite ties these functions to closed forms
+(hand-worked 2- and 3-token cases), to identities that reduce to textbook
+operations (sign-flip -> masked GEMM, constant rows -> prefix sum, row 0),
+and to invariants (linearity, causality, segment independence).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "hstu_oracle.c")
+LIBRARY = os.path.join(HERE, "libhstu_oracle.so")
+
+_DTYPE_CODE = {"bf16": 0, "fp16": 1, "fp32": 2}
+
+
+def build(output: str = LIBRARY, plant: int = 0) -> str:
+    """Compile the C oracle with gcc (-O2, OpenMP).  `plant` != 0 builds a
+    copy with one deliberate mistake (see the C source) for pin tests."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+           f"-DORACLE_PLANT={int(plant)}", SOURCE, "-o", output + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(output + ".tmp", output)
+    return output
+
+
+_libs = {}
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    path = path or LIBRARY
+    if path in _libs:
+        return _libs[path]
+    if path == LIBRARY and (not os.path.exists(path)
+                            or os.path.getmtime(path) < os.path.getmtime(SOURCE)):
+        build(path)
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, f64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    lib.hstu_oracle_fwd.argtypes = [vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, f64, f64, vp]
+    lib.hstu_oracle_fwd.restype = ctypes.c_int
+    lib.hstu_oracle_rows.argtypes = [vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, f64, f64, vp, vp, i64, vp]
+    lib.hstu_oracle_rows.restype = ctypes.c_int
+    lib.hstu_oracle_threads.argtypes = []
+    lib.hstu_oracle_threads.restype = ctypes.c_int
+    _libs[path] = lib
+    return lib
+
+
+def _storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    want = {"bf16": np.uint16, "fp16": np.float16, "fp32": np.float32}[dtype]
+    x = np.ascontiguousarray(x)
+    if x.dtype != want:
+        raise TypeError(f"{dtype} values must be stored as {np.dtype(want).name}, got {x.dtype}")
+    return x
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def fwd(q, k, v, offsets, heads: int, d: int, alpha: float, n: float, dtype: str,
+        lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+    """Full fp64 output (T, heads, d)."""
+    lib = lib or load()
+    q, k, v = (_storage(a, dtype) for a in (q, k, v))
+    off = np.ascontiguousarray(offsets, dtype=np.int32)
+    T = int(off[-1]) if len(off) else 0
+    out = np.zeros((T, heads, d), dtype=np.float64)
+    for a in (q, k, v):
+        if a.size < T * heads * d:
+            raise ValueError("q/k/v smaller than offsets imply")
+    rc = lib.hstu_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[dtype], _ptr(off),
+                             len(off) - 1, heads, d, float(alpha), float(n), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments (malformed offsets or sizes)")
+    return out
+
+
+def rows(q, k, v, offsets, heads: int, d: int, alpha: float, n: float, dtype: str,
+         tokens, head_ids, lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+    """fp64 outputs (m, d) at global tokens[m], heads head_ids[m]."""
+    lib = lib or load()
+    q, k, v = (_storage(a, dtype) for a in (q, k, v))
+    off = np.ascontiguousarray(offsets, dtype=np.int32)
+    tok = np.ascontiguousarray(tokens, dtype=np.int64)
+    hd = np.ascontiguousarray(head_ids, dtype=np.int32)
+    if tok.shape != hd.shape:
+        raise ValueError("tokens and head_ids differ in length")
+    out = np.zeros((len(tok), d), dtype=np.float64)
+    rc = lib.hstu_oracle_rows(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[dtype], _ptr(off),
+                              len(off) - 1, heads, d, float(alpha), float(n),
+                              _ptr(tok), _ptr(hd), len(tok), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle rejected the sampled rows")
+    return out
+
+
+def threads(lib: Optional[ctypes.CDLL] = None) -> int:
+    return int((lib or load()).hstu_oracle_threads())
+
+
+# ---------------------------------------------------------------------------
+# Dense unfused evaluation (numpy fp64), for small inputs.
+# ---------------------------------------------------------------------------
+
+def widen(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact fp64 image of stored values (bf16 bits are widened through fp32)."""
+    if dtype == "bf16":
+        u = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return u.view(np.float32).astype(np.float64)
+    return np.asarray(x).astype(np.float64)
+
+
+def _silu(x: np.ndarray) -> np.ndarray:
+    # x * sigmoid(x); np.exp(-|x|) never overflows.
+    e = np.exp(-np.abs(x))
+    sig = np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+    return x * sig
+
+
+def dense_unfused(q, k, v, offsets, heads: int, d: int, alpha: float, n: float,
+                  dtype: str) -> np.ndarray:
+    """Per sequence: the (heads, s, s) score tensor is formed in full, then
+    scaled, passed through SiLU, multiplied by tril(ones)/n and applied to V."""
+    Q, K, V = (widen(a, dtype).reshape(-1, heads, d) for a in (q, k, v))
+    off = np.asarray(offsets, dtype=np.int64)
+    out = np.zeros((int(off[-1]), heads, d), dtype=np.float64)
+    for i in range(len(off) - 1):
+        a, b = int(off[i]), int(off[i + 1])
+        s = b - a
+        if s == 0:
+            continue
+        Qi = Q[a:b].transpose(1, 0, 2)  # (heads, s, d)
+        Ki = K[a:b].transpose(1, 0, 2)
+        Vi = V[a:b].transpose(1, 0, 2)
+        x = np.matmul(Qi, Ki.transpose(0, 2, 1))  # (heads, s, s)
+        x = x * alpha
+        x = _silu(x)
+        mask = np.tril(np.ones((s, s), dtype=np.float64))
+        x = x * (mask / n)
+        o = np.matmul(x, Vi)  # (heads, s, d)
+        out[a:b] = o.transpose(1, 0, 2)
+    return out

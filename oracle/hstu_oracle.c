@@ -1,0 +1,212 @@
+/*
+ * hstu_oracle.c -- plain fp64 CPU oracle for the HSTU jagged causal attention
+ * forward.  TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may call it; the library path never does, and
+ * this file shares no code, header or constant with it.
+ *
+ * What it computes (the plain definition, evaluated row by row):
+ *
+ *   for sequence i with tokens [off[i], off[i+1]), head h, local row r:
+ *     out[off[i]+r, h, :] = (1/n) * sum_{c=0..r} silu(alpha * <q_r, k_c>) * v_c
+ *
+ * Sources, by page and section:
+ *   - Ascend HSTU blog ("都是生成式推荐，为什么昇腾这么快？"), §1: the formula
+ *     HSTU(Q,K,V) = (mask/n) * silu(QK^T / alpha^-1) V and the five-step
+ *     PyTorch definition (matmul, *= alpha, silu, *= mask/n, matmul).
+ *   - same page, §3.1-§3.2: the mask is the decoder-only causal mask; the
+ *     diagonal block gets a lower-triangular mask, so position c <= r is kept
+ *     (diagonal included).
+ *   - same page, §4.2: jagged tensors, values (total, heads, d) plus offsets;
+ *     each segment is an independent sample, so no cross-sequence terms.
+ *   - HSTU paper translation ("行动胜于言语…"), §3: phi_2 is SiLU.
+ *
+ * Readings taken where the pages are silent (each listed in the design notes):
+ *   - alpha multiplies the scores before SiLU; n is a caller-given scalar;
+ *   - the mask multiplies after SiLU (0/1), so masked terms are exactly 0;
+ *   - inputs are the already-rounded stored values, widened exactly to fp64;
+ *     alpha and n are the fp64 images of the float32 values the GPU call gets.
+ *
+ * Element types of q/k/v: 0 = bfloat16 bits (uint16), 1 = IEEE binary16
+ * (uint16 bits), 2 = float32.  Output is always fp64.
+ *
+ * ORACLE_PLANT (compile-time, default 0) plants one deliberate mistake so the
+ * test suite can show that its pins catch it; the built library used for
+ * parity is always compiled with ORACLE_PLANT=0.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#ifndef ORACLE_PLANT
+#define ORACLE_PLANT 0
+#endif
+
+/* ---- exact widening of the stored element types ------------------------- */
+
+static double widen_bf16(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double widen_fp16(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1f;
+    int mant = h & 0x3ff;
+    double mag;
+    if (expo == 0) {
+        mag = ldexp((double)mant, -24); /* subnormal: mant * 2^-24 */
+    } else if (expo == 31) {
+        mag = mant ? NAN : INFINITY;
+    } else {
+        mag = ldexp((double)(mant | 0x400), expo - 25); /* (1.mant) * 2^(e-15) */
+    }
+    return sign ? -mag : mag;
+}
+
+static double load_elem(const void* base, int dtype, int64_t idx) {
+    switch (dtype) {
+    case 0: return widen_bf16(((const uint16_t*)base)[idx]);
+    case 1: return widen_fp16(((const uint16_t*)base)[idx]);
+    default: return (double)((const float*)base)[idx];
+    }
+}
+
+/* ---- the pointwise nonlinearity ------------------------------------------ */
+
+/* silu(x) = x * sigmoid(x), with the sigmoid written in the form that never
+ * forms exp of a large positive number. */
+static double silu(double x) {
+#if ORACLE_PLANT == 2
+    x = -x; /* planted: sign error inside the nonlinearity */
+#endif
+    if (x >= 0.0) return x / (1.0 + exp(-x));
+    double e = exp(x);
+    return x * e / (1.0 + e);
+}
+
+/* ---- one output row -------------------------------------------------------- */
+
+/* Computes the d outputs of (sequence start `s0`, local row r, head h) into
+ * acc[0..d).  Widening q, k and v per element keeps memory small; the cost is
+ * irrelevant for an oracle. */
+static void one_row(const void* q, const void* k, const void* v, int dtype,
+                    int64_t s0, int64_t r, int heads, int d, int h,
+                    double alpha, double n, double* qrow, double* acc) {
+    const int64_t row_stride = (int64_t)heads * d;
+    for (int e = 0; e < d; ++e) {
+        qrow[e] = load_elem(q, dtype, (s0 + r) * row_stride + (int64_t)h * d + e);
+        acc[e] = 0.0;
+    }
+    int64_t c_end = r; /* inclusive: the causal mask keeps the diagonal */
+#if ORACLE_PLANT == 1
+    c_end = r - 1; /* planted: diagonal dropped */
+#endif
+    int64_t c_begin = 0;
+#if ORACLE_PLANT == 5
+    c_begin = -s0; /* planted: attends back across the sequence boundary */
+#endif
+    for (int64_t c = c_begin; c <= c_end; ++c) {
+        int64_t krow = s0 + c;
+#if ORACLE_PLANT == 4
+        /* planted: transposed score operand, <q_c, k_r> instead of <q_r, k_c> */
+        double dot = 0.0;
+        for (int e = 0; e < d; ++e)
+            dot += load_elem(q, dtype, krow * row_stride + (int64_t)h * d + e) *
+                   load_elem(k, dtype, (s0 + r) * row_stride + (int64_t)h * d + e);
+#else
+        double dot = 0.0;
+        for (int e = 0; e < d; ++e)
+            dot += qrow[e] * load_elem(k, dtype, krow * row_stride + (int64_t)h * d + e);
+#endif
+#if ORACLE_PLANT == 3
+        double w = alpha * silu(dot); /* planted: alpha applied after SiLU */
+#else
+        double w = silu(alpha * dot);
+#endif
+        for (int e = 0; e < d; ++e)
+            acc[e] += w * load_elem(v, dtype, krow * row_stride + (int64_t)h * d + e);
+    }
+    double inv_n = 1.0 / n;
+#if ORACLE_PLANT == 6
+    inv_n = 1.0; /* planted: normaliser dropped */
+#endif
+    for (int e = 0; e < d; ++e) acc[e] *= inv_n;
+}
+
+/* ---- entry points ---------------------------------------------------------- */
+
+/* Full output: out is fp64 (T, heads, d), T = off[num_seqs].  Returns 0, or -1
+ * on malformed offsets (off[0] != 0 or decreasing).  d <= 1024. */
+int hstu_oracle_fwd(const void* q, const void* k, const void* v, int dtype,
+                    const int32_t* off, int num_seqs, int heads, int d,
+                    double alpha, double n, double* out) {
+    if (num_seqs < 0 || heads < 1 || d < 1 || d > 1024) return -1;
+    if (num_seqs > 0 && off[0] != 0) return -1;
+    for (int i = 0; i < num_seqs; ++i)
+        if (off[i + 1] < off[i]) return -1;
+    const int64_t row_stride = (int64_t)heads * d;
+    const int64_t items = (int64_t)num_seqs * heads;
+#pragma omp parallel
+    {
+        double qrow[1024], acc[1024];
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t it = 0; it < items; ++it) {
+            int i = (int)(it / heads), h = (int)(it % heads);
+            int64_t s0 = off[i], len = (int64_t)off[i + 1] - off[i];
+            for (int64_t r = 0; r < len; ++r) {
+                one_row(q, k, v, dtype, s0, r, heads, d, h, alpha, n, qrow, acc);
+                double* o = out + (s0 + r) * row_stride + (int64_t)h * d;
+                for (int e = 0; e < d; ++e) o[e] = acc[e];
+            }
+        }
+    }
+    return 0;
+}
+
+/* Sampled rows: for m = 0..count-1, out_rows[m, 0..d) is the output at global
+ * token tok[m] and head hd[m].  The token's sequence is found by a binary
+ * search over the offsets.  Returns 0, or -1 on a token or head out of range. */
+int hstu_oracle_rows(const void* q, const void* k, const void* v, int dtype,
+                     const int32_t* off, int num_seqs, int heads, int d,
+                     double alpha, double n, const int64_t* tok, const int32_t* hd,
+                     int64_t count, double* out_rows) {
+    if (num_seqs < 1 || heads < 1 || d < 1 || d > 1024) return -1;
+    int64_t T = off[num_seqs];
+    for (int64_t m = 0; m < count; ++m)
+        if (tok[m] < 0 || tok[m] >= T || hd[m] < 0 || hd[m] >= heads) return -1;
+#pragma omp parallel
+    {
+        double qrow[1024];
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t m = 0; m < count; ++m) {
+            /* largest i with off[i] <= tok, among non-empty sequences */
+            int lo = 0, hi = num_seqs - 1;
+            while (lo < hi) {
+                int mid = (lo + hi + 1) / 2;
+                if (off[mid] <= tok[m]) lo = mid; else hi = mid - 1;
+            }
+            int64_t s0 = off[lo];
+            one_row(q, k, v, dtype, s0, tok[m] - s0, heads, d, hd[m], alpha, n, qrow,
+                    out_rows + m * (int64_t)d);
+        }
+    }
+    return 0;
+}
+
+/* Number of threads an OpenMP parallel region here uses (for reporting). */
+int hstu_oracle_threads(void) {
+    int t = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        {
+#ifdef _OPENMP
+            extern int omp_get_num_threads(void);
+            t = omp_get_num_threads();
+#endif
+        }
+    }
+    return t;
+}

@@ -1,0 +1,212 @@
+"""Seeded synthetic inputs for the HSTU jagged attention forward.
+
+This module holds no part of the attention arithmetic.  It only draws
+sequence lengths and i.i.d. normal values, rounds them to the element type
+the call runs in, and builds int32 prefix-sum offsets.  Both the CPU oracle
+(under ``oracle/``) and the HIP library consume what it returns; neither of
+them is imported here.
+
+The five named workloads follow the shapes the pages measure:
+  * the Ascend HSTU blog ("都是生成式推荐，为什么昇腾这么快？") times
+    QKV (b=16, heads=4, s=4096, d=64) in §2.2, §3.2 and §5.2, and bounds real
+    lengths by 0 < s <= 20480 in §3.1;
+  * the HSTU paper translation ("行动胜于言语…", §3.2) notes that user history
+    lengths are skewed, which the skewed-length workload stands in for.
+No public dataset is involved; every value is synthetic.
+
+Element types are carried as numpy arrays:
+  * "fp32": float32
+  * "fp16": float16 (numpy's cast rounds to nearest even)
+  * "bf16": uint16 holding bfloat16 bit patterns, rounded to nearest even
+    from float32 by the integer rule below.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional
+
+import numpy as np
+
+DTYPES = ("bf16", "fp16", "fp32")
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest, ties to even); return uint16 bits.
+
+    Inputs here are finite normals, so the NaN/overflow corner of the rounding
+    rule does not arise; a NaN input is kept a quiet NaN anyway.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        r[nan] = np.uint16(0x7FC0)
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def cast_values(x32: np.ndarray, dtype: str) -> np.ndarray:
+    """Round a float32 array to the storage form of `dtype` (see module doc)."""
+    if dtype == "fp32":
+        return np.ascontiguousarray(x32, dtype=np.float32)
+    if dtype == "fp16":
+        return np.ascontiguousarray(x32, dtype=np.float32).astype(np.float16)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x32)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def widen_to_f32(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float32 image of stored values (for display and sums in tests)."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(x)
+    return np.asarray(x, dtype=np.float32)
+
+
+def offsets_from_lengths(lengths) -> np.ndarray:
+    lengths = np.asarray(lengths, dtype=np.int64)
+    if (lengths < 0).any():
+        raise ValueError("negative sequence length")
+    off = np.zeros(len(lengths) + 1, dtype=np.int64)
+    np.cumsum(lengths, out=off[1:])
+    if off[-1] > np.iinfo(np.int32).max:
+        raise ValueError("total length does not fit int32 offsets")
+    return off.astype(np.int32)
+
+
+@dataclasses.dataclass
+class Case:
+    """One synthetic call: jagged q/k/v (T, heads, d) plus offsets and scalars."""
+
+    name: str
+    dtype: str
+    heads: int
+    d: int
+    offsets: np.ndarray  # int32 [num_seqs + 1]
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    alpha: float  # the float32 value handed to the kernel
+    n: float  # the float32 value handed to the kernel
+    description: str = ""
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.offsets) - 1
+
+    @property
+    def total(self) -> int:
+        return int(self.offsets[-1])
+
+    @property
+    def lengths(self) -> np.ndarray:
+        return np.diff(self.offsets.astype(np.int64))
+
+    def useful_flops(self) -> float:
+        """4 * heads * d * sum_i s_i (s_i + 1) / 2: both products, causal half
+        including the diagonal, nothing for the skipped upper triangle."""
+        s = self.lengths.astype(np.float64)
+        return float(4.0 * self.heads * self.d * np.sum(s * (s + 1.0) / 2.0))
+
+    def algorithmic_bytes(self) -> float:
+        """q, k, v read once and out written once, plus the offsets."""
+        elt = {"bf16": 2, "fp16": 2, "fp32": 4}[self.dtype]
+        return float(4 * elt * self.total * self.heads * self.d + 4 * (self.num_seqs + 1))
+
+
+def f32(x: float) -> float:
+    """The float32 value nearest to x, as a Python float."""
+    return float(np.float32(x))
+
+
+def make_case(lengths, heads: int, d: int, dtype: str, seed: int, sigma: float = 1.0,
+              alpha: Optional[float] = None, n: Optional[float] = None,
+              name: str = "custom", description: str = "") -> Case:
+    """Jagged case from explicit lengths; values i.i.d. N(0, sigma^2)."""
+    if dtype not in DTYPES:
+        raise ValueError(dtype)
+    offsets = offsets_from_lengths(lengths)
+    T = int(offsets[-1])
+    rng = np.random.default_rng(seed)
+    shape = (T, heads, d)
+    vals = []
+    for _ in range(3):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        if sigma != 1.0:
+            x *= np.float32(sigma)
+        vals.append(cast_values(x, dtype))
+    if alpha is None:
+        alpha = 1.0 / math.sqrt(d)
+    if n is None:
+        n = float(max(1, int(np.max(np.diff(offsets))) if len(offsets) > 1 else 1))
+    return Case(name=name, dtype=dtype, heads=heads, d=d, offsets=offsets,
+                q=vals[0], k=vals[1], v=vals[2], alpha=f32(alpha), n=f32(n),
+                description=description)
+
+
+# ---------------------------------------------------------------------------
+# The five named workloads.  Seed = 1000 + workload number; lengths are drawn
+# before values from the same generator.
+# ---------------------------------------------------------------------------
+
+WORKLOADS: Dict[int, str] = {
+    1: "dense causal, 1 x 256 tokens, heads 2, d 64, fp32",
+    2: "dense causal as 16 equal jagged sequences of 4096, heads 4, d 64, bf16",
+    3: "jagged causal, 64 skewed lengths max(16, ceil(8192 u^3)), heads 4, d 128, bf16",
+    4: "long jagged causal, 8 lengths U[8192, 20480], heads 4, d 64, bf16",
+    5: "many short jagged causal, 4096 lengths U[1, 256], heads 2, d 128, fp16",
+}
+
+
+def workload_lengths(num: int, rng: np.random.Generator) -> List[int]:
+    if num == 1:
+        return [256]
+    if num == 2:
+        return [4096] * 16
+    if num == 3:
+        u = rng.random(64)
+        return [int(x) for x in np.maximum(16, np.ceil(8192.0 * u ** 3))]
+    if num == 4:
+        return [int(x) for x in rng.integers(8192, 20480, size=8, endpoint=True)]
+    if num == 5:
+        return [int(x) for x in rng.integers(1, 256, size=4096, endpoint=True)]
+    raise ValueError(f"no workload {num}")
+
+
+_SPEC = {
+    # num: (heads, d, dtype, sigma, alpha, n-rule)
+    1: (2, 64, "fp32", 1.0, 1.0 / math.sqrt(64), lambda L: 256.0),
+    2: (4, 64, "bf16", 1.0, 1.0 / 8.0, lambda L: 4096.0),
+    3: (4, 128, "bf16", 1.0, 1.0 / math.sqrt(128), lambda L: float(max(L))),
+    4: (4, 64, "bf16", 1.0, 1.0 / 8.0, lambda L: 20480.0),
+    5: (2, 128, "fp16", 0.5, 1.0 / math.sqrt(128), lambda L: 256.0),
+}
+
+
+def workload(num: int, values: bool = True) -> Case:
+    """Build named workload `num` (1..5).  With values=False only the lengths,
+    offsets and scalars are filled (q/k/v are empty arrays)."""
+    heads, d, dtype, sigma, alpha, n_rule = _SPEC[num]
+    rng = np.random.default_rng(1000 + num)
+    lengths = workload_lengths(num, rng)
+    offsets = offsets_from_lengths(lengths)
+    T = int(offsets[-1])
+    if values:
+        vals = []
+        for _ in range(3):
+            x = rng.standard_normal((T, heads, d), dtype=np.float32)
+            if sigma != 1.0:
+                x *= np.float32(sigma)
+            vals.append(cast_values(x, dtype))
+    else:
+        empty = cast_values(np.zeros((0, heads, d), np.float32), dtype)
+        vals = [empty, empty, empty]
+    return Case(name=f"w{num}", dtype=dtype, heads=heads, d=d, offsets=offsets,
+                q=vals[0], k=vals[1], v=vals[2], alpha=f32(alpha), n=f32(n_rule(lengths)),
+                description=WORKLOADS[num])
