@@ -1,0 +1,171 @@
+#!/usr/bin/env python3
+"""Benchmark: HSTU jagged causal attention forward on one MI355X.
+
+One step = one hstu_attn_fwd call (work-list kernel + attention kernel) over
+the whole batch, inputs resident in HBM.  Default workload: 16 sequences of
+4096 tokens, heads 4, d 64, bf16 (the QKV (16, 4, 4096, 64) shape the Ascend
+HSTU blog times in §2.2, §3.2 and §5.2), re-laid as a jagged batch.
+
+Prints one JSON line.  `value` is useful TFLOP/s: 4 * heads * d *
+sum_i s_i (s_i + 1) / 2 per call over the measured call time.  The roofline
+object reports the attention kernel's own average duration (HIP events the
+library records on the call's stream during the timed region).  The
+cpu_baseline object times the fp64 CPU oracle on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
+PEAK_HBM_GBS = 8000.0
+METRIC = "HSTU attn fwd useful TFLOP/s, % bf16 MFMA peak; ms at QKV(16,4,4096,64)"
+# HBM bytes per dispatch of the attention kernel, from rocprofv3 --pmc
+# FETCH_SIZE and WRITE_SIZE (KiB), scaled by the copy-kernel calibration.
+# None until counters have been collected for the current kernel.
+TRAFFIC_BYTES = {}
+
+
+def to_device(case):
+    import torch
+    def conv(x):
+        if case.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(
+                torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    return (conv(case.q), conv(case.k), conv(case.v),
+            torch.from_numpy(case.offsets.astype(np.int32)).cuda())
+
+
+def cpu_baseline(case, budget_s: float):
+    """Time the oracle on whole sequences of the workload (all heads).  Each
+    oracle call takes enough sequences to give every OpenMP thread a
+    (sequence, head) pair; calls continue in input order until about budget_s
+    of wall time has been spent."""
+    import oracle
+    lib = oracle.load()
+    threads = oracle.threads(lib)
+    off = case.offsets
+    per_call = max(1, -(-threads // case.heads))
+    done_flops, done_s, seqs = 0.0, 0.0, 0
+    i = 0
+    while i < case.num_seqs and done_s < budget_s:
+        j = min(case.num_seqs, i + per_call)
+        a, b = int(off[i]), int(off[j])
+        sub = (off[i:j + 1] - off[i]).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.fwd(case.q[a:b], case.k[a:b], case.v[a:b], sub, case.heads, case.d, case.alpha,
+                   case.n, case.dtype, lib=lib)
+        done_s += time.perf_counter() - t0
+        s = case.lengths[i:j].astype(np.float64)
+        done_flops += float(np.sum(4.0 * case.heads * case.d * s * (s + 1.0) / 2.0))
+        seqs += j - i
+        i = j
+    used = min(threads, per_call * case.heads)
+    return {"value": done_flops / done_s / 1e12, "unit": "TFLOP/s", "cores": used,
+            "kind": "oracle",
+            "sample": f"{seqs} of {case.num_seqs} sequences, all heads; fp64 loop oracle "
+                      f"(OpenMP over (sequence, head)), {done_s:.1f} s wall, "
+                      f"{threads} threads available"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each GPU would run its own share of sequences with no exchange).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import generative_recommendation_attention_amd as hstu
+
+    torch.cuda.set_device(0)
+    case = workloads.workload(args.workload)
+    q, k, v, off = to_device(case)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    flops = case.useful_flops()
+
+    for _ in range(args.warmup):
+        hstu.hstu_attn_fwd(q, k, v, off, case.alpha, case.n, out=out)
+    torch.cuda.synchronize()
+
+    hstu.hstu_profile_read(reset=True)
+    hstu.hstu_profile_enable(True)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        hstu.hstu_attn_fwd(q, k, v, off, case.alpha, case.n, out=out)
+    end.record(stream)
+    torch.cuda.synchronize()
+    hstu.hstu_profile_enable(False)
+    total_ms = start.elapsed_time(end)
+    kt = hstu.hstu_profile_read(reset=True)
+    ms = total_ms / args.steps
+    value = flops / (ms * 1e-3) / 1e12
+
+    attn_ms = kt.attn_ms / max(1, kt.calls)
+    sched_ms = kt.sched_ms / max(1, kt.calls)
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    peak = PEAK_MFMA_TFLOPS[case.dtype]
+    traffic = TRAFFIC_BYTES.get(args.workload)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                "kernel": "attn_fwd_mfma16" if case.dtype != "fp32" else "attn_fwd_mfma_f32",
+                "kernel_ms": round(attn_ms, 5), "sched_kernel_ms": round(sched_ms, 5),
+                "hbm_frac": round(case.algorithmic_bytes() / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                  4)}
+
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = cpu_baseline(case, args.cpu_budget)
+
+    L = case.lengths
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic",
+        "pct_bf16_mfma_peak": round(100.0 * value / PEAK_MFMA_TFLOPS["bf16"], 2),
+        "config": {"workload": case.description, "num_seqs": case.num_seqs,
+                   "total_tokens": case.total, "max_seq_len": int(L.max()), "heads": case.heads,
+                   "d": case.d, "alpha": case.alpha, "n": case.n,
+                   "useful_gflop": round(flops / 1e9, 3)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

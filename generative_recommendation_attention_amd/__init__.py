@@ -1,0 +1,189 @@
+"""HSTU jagged causal attention forward on AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libhstu.so`` (the C ABI in ``include/hstu.h``).
+Every step of the computation runs in the library's HIP kernels; this module
+only checks and marshals arguments.  PyTorch supplies device memory and the
+current stream.  There is no CPU fallback: without the built library every
+call raises.
+
+    out = hstu_attn_fwd(q, k, v, seq_offsets, alpha, n)
+
+q, k, v: (T, heads, d) CUDA tensors (bfloat16, float16 or float32), contiguous;
+seq_offsets: int32 CUDA tensor [num_seqs + 1] of prefix sums.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libhstu.so")
+
+HSTU_OK = 0
+HSTU_ERR_INVALID_ARG = -1
+HSTU_ERR_UNSUPPORTED = -2
+HSTU_ERR_HIP = -3
+HSTU_ERR_NO_MEMORY = -4
+HSTU_ERR_BAD_OFFSETS = -5
+
+HSTU_BF16, HSTU_FP16, HSTU_FP32 = 0, 1, 2
+
+# Every symbol include/hstu.h declares.
+EXPORTS = ("hstu_attn_fwd", "hstu_attn_fwd_bf16", "hstu_attn_fwd_fp16", "hstu_attn_fwd_fp32",
+           "hstu_validate_offsets", "hstu_status_string", "hstu_last_hip_error",
+           "hstu_release_workspace", "hstu_profile_enable", "hstu_profile_read")
+
+
+class HstuError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(what)
+
+
+class KernelTimes(ctypes.Structure):
+    _fields_ = [("calls", ctypes.c_int64), ("sched_ms", ctypes.c_double),
+                ("attn_ms", ctypes.c_double), ("dropped", ctypes.c_int64)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def library_path() -> str:
+    return LIBRARY
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libhstu.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIBRARY
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"{p} is missing: build it with "
+            "`python -m generative_recommendation_attention_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(p)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    fwd = [vp, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp]
+    lib.hstu_attn_fwd.argtypes = fwd + [ctypes.c_int]
+    lib.hstu_attn_fwd.restype = ctypes.c_int
+    for name in ("hstu_attn_fwd_bf16", "hstu_attn_fwd_fp16", "hstu_attn_fwd_fp32"):
+        getattr(lib, name).argtypes = fwd
+        getattr(lib, name).restype = ctypes.c_int
+    lib.hstu_validate_offsets.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_int64), vp]
+    lib.hstu_validate_offsets.restype = ctypes.c_int
+    lib.hstu_status_string.argtypes = [ctypes.c_int]
+    lib.hstu_status_string.restype = ctypes.c_char_p
+    lib.hstu_last_hip_error.argtypes = []
+    lib.hstu_last_hip_error.restype = ctypes.c_int
+    lib.hstu_release_workspace.argtypes = []
+    lib.hstu_release_workspace.restype = None
+    lib.hstu_profile_enable.argtypes = [ctypes.c_int]
+    lib.hstu_profile_enable.restype = ctypes.c_int
+    lib.hstu_profile_read.argtypes = [ctypes.POINTER(KernelTimes), ctypes.c_int]
+    lib.hstu_profile_read.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != HSTU_OK:
+        lib = load_library()
+        msg = lib.hstu_status_string(status).decode()
+        if status == HSTU_ERR_HIP:
+            msg += f" (hipError {lib.hstu_last_hip_error()})"
+        raise HstuError(status, f"{what}: {msg}")
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.bfloat16: HSTU_BF16, torch.float16: HSTU_FP16, torch.float32: HSTU_FP32}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported element type {t.dtype}")
+    return codes[t.dtype]
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def hstu_attn_fwd(q, k, v, seq_offsets, alpha: float, n: float, out=None, stream=None):
+    """Jagged causal HSTU attention forward; returns `out` (T, heads, d)."""
+    import torch
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one (T, heads, d) shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one element type")
+    for t in (q, k, v, seq_offsets):
+        if not t.is_cuda:
+            raise ValueError("all tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if seq_offsets.dtype != torch.int32 or seq_offsets.dim() != 1 or seq_offsets.numel() < 1:
+        raise ValueError("seq_offsets must be a 1-D int32 tensor of num_seqs + 1 entries")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    T, heads, d = q.shape
+    num_seqs = seq_offsets.numel() - 1
+    lib = load_library()
+    st = lib.hstu_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), seq_offsets.data_ptr(),
+                           num_seqs, heads, d, float(alpha), float(n), out.data_ptr(),
+                           _stream_handle(stream), _dtype_code(q))
+    _check(st, "hstu_attn_fwd")
+    return out
+
+
+def _typed(name: str, code: int):
+    def fn(q, k, v, seq_offsets, alpha: float, n: float, out=None, stream=None):
+        if _dtype_code(q) != code:
+            raise TypeError(f"{name} takes {['bfloat16', 'float16', 'float32'][code]} tensors")
+        if out is None:
+            import torch
+            out = torch.empty_like(q)
+        T, heads, d = q.shape
+        lib = load_library()
+        st = getattr(lib, name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), seq_offsets.data_ptr(),
+                                seq_offsets.numel() - 1, heads, d, float(alpha), float(n),
+                                out.data_ptr(), _stream_handle(stream))
+        _check(st, name)
+        return out
+    fn.__name__ = name
+    fn.__doc__ = f"{name}: hstu_attn_fwd with the element type fixed."
+    return fn
+
+
+hstu_attn_fwd_bf16 = _typed("hstu_attn_fwd_bf16", HSTU_BF16)
+hstu_attn_fwd_fp16 = _typed("hstu_attn_fwd_fp16", HSTU_FP16)
+hstu_attn_fwd_fp32 = _typed("hstu_attn_fwd_fp32", HSTU_FP32)
+
+
+def hstu_validate_offsets(seq_offsets, stream=None) -> int:
+    """Synchronous device-offset check; returns T = off[num_seqs]."""
+    lib = load_library()
+    total = ctypes.c_int64(0)
+    st = lib.hstu_validate_offsets(seq_offsets.data_ptr(), seq_offsets.numel() - 1,
+                                   ctypes.byref(total), _stream_handle(stream))
+    _check(st, "hstu_validate_offsets")
+    return int(total.value)
+
+
+def hstu_release_workspace() -> None:
+    load_library().hstu_release_workspace()
+
+
+def hstu_profile_enable(on: bool) -> None:
+    _check(load_library().hstu_profile_enable(1 if on else 0), "hstu_profile_enable")
+
+
+def hstu_profile_read(reset: bool = True) -> KernelTimes:
+    t = KernelTimes()
+    _check(load_library().hstu_profile_read(ctypes.byref(t), 1 if reset else 0),
+           "hstu_profile_read")
+    return t

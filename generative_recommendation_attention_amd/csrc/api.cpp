@@ -1,0 +1,304 @@
+// C ABI of the HSTU forward (declared in include/hstu.h): argument checks on
+// the host, the per-(device, stream) scratch area, event-based kernel timing,
+// and the two launches (work list, attention) on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "hstu.h"
+#include "internal.h"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+hstu_status_t hip_fail(hipError_t e) {
+    g_last_hip = (int)e;
+    return HSTU_ERR_HIP;
+}
+
+// ---- scratch areas ----------------------------------------------------------
+
+struct Scratch {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+
+std::mutex g_scratch_mu;
+std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
+
+// Returns a scratch area of at least `bytes` for (device, stream).  Growing an
+// area first waits for the stream, so no kernel still reads the old one.
+hstu_status_t scratch_for(int dev, hipStream_t stream, size_t bytes, void** out) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    Scratch& s = g_scratch[std::make_pair(dev, stream)];
+    if (s.bytes < bytes) {
+        size_t want = bytes < 4096 ? 4096 : bytes;
+        want = (want + 4095) & ~(size_t)4095;
+        if (s.ptr) {
+            hipError_t e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return hip_fail(e);
+            (void)hipFree(s.ptr);
+            s.ptr = nullptr;
+            s.bytes = 0;
+        }
+        if (getenv("HSTU_FAIL_ALLOC") && atoi(getenv("HSTU_FAIL_ALLOC")) != 0)
+            return HSTU_ERR_NO_MEMORY;
+        void* p = nullptr;
+        hipError_t e = hipMalloc(&p, want);
+        if (e != hipSuccess) {
+            g_last_hip = (int)e;
+            return HSTU_ERR_NO_MEMORY;
+        }
+        s.ptr = p;
+        s.bytes = want;
+    }
+    *out = s.ptr;
+    return HSTU_OK;
+}
+
+// ---- device checks ----------------------------------------------------------
+
+std::mutex g_dev_mu;
+std::map<int, bool> g_dev_ok;
+
+hstu_status_t check_device(int* dev_out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    *dev_out = dev;
+    std::lock_guard<std::mutex> lock(g_dev_mu);
+    auto it = g_dev_ok.find(dev);
+    if (it == g_dev_ok.end()) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return hip_fail(e);
+        const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        it = g_dev_ok.emplace(dev, ok).first;
+    }
+    return it->second ? HSTU_OK : HSTU_ERR_UNSUPPORTED;
+}
+
+// ---- kernel timing ----------------------------------------------------------
+
+struct TimedCall {
+    hipEvent_t e[3];
+};
+
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<TimedCall> g_prof_pending;
+std::vector<TimedCall> g_prof_free;
+hstu_kernel_times_t g_prof_total = {0, 0.0, 0.0, 0};
+constexpr size_t PROF_RING = 4096;
+
+bool prof_take(TimedCall* tc) {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    if (!g_prof_on) return false;
+    if (g_prof_pending.size() >= PROF_RING) {
+        g_prof_total.dropped++;
+        return false;
+    }
+    if (!g_prof_free.empty()) {
+        *tc = g_prof_free.back();
+        g_prof_free.pop_back();
+        return true;
+    }
+    for (int i = 0; i < 3; ++i) {
+        if (hipEventCreate(&tc->e[i]) != hipSuccess) {
+            for (int j = 0; j < i; ++j) (void)hipEventDestroy(tc->e[j]);
+            g_prof_total.dropped++;
+            return false;
+        }
+    }
+    return true;
+}
+
+void prof_commit(const TimedCall& tc) {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    g_prof_pending.push_back(tc);
+}
+
+// ---- argument checks --------------------------------------------------------
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+hstu_status_t check_args(const void* q, const void* k, const void* v, const int32_t* off,
+                         int32_t num_seqs, int32_t heads, int32_t d, float alpha, float n,
+                         const void* out, int dtype) {
+    if (dtype != HSTU_BF16 && dtype != HSTU_FP16 && dtype != HSTU_FP32) return HSTU_ERR_UNSUPPORTED;
+    if (num_seqs < 0 || heads < 1) return HSTU_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return HSTU_ERR_UNSUPPORTED;
+    if (!std::isfinite(alpha) || !std::isfinite(n) || n == 0.0f) return HSTU_ERR_INVALID_ARG;
+    if (num_seqs == 0) return HSTU_OK;
+    if (!q || !k || !v || !off || !out) return HSTU_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return HSTU_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(off) & 3u) != 0) return HSTU_ERR_INVALID_ARG;
+    if (out == q || out == k || out == v) return HSTU_ERR_INVALID_ARG;
+    return HSTU_OK;
+}
+
+bool validate_env() {
+    const char* s = getenv("HSTU_VALIDATE");
+    return s && atoi(s) != 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+hstu_status_t hstu_attn_fwd(const void* q, const void* k, const void* v,
+                            const int32_t* seq_offsets, int32_t num_seqs, int32_t heads,
+                            int32_t d, float alpha, float n, void* out, hipStream_t stream,
+                            hstu_dtype_t dtype) {
+    hstu_status_t st = check_args(q, k, v, seq_offsets, num_seqs, heads, d, alpha, n, out, dtype);
+    if (st != HSTU_OK || num_seqs == 0) return st;
+    int dev = 0;
+    st = check_device(&dev);
+    if (st != HSTU_OK) return st;
+
+    const hstu::Dtype dt = static_cast<hstu::Dtype>(dtype);
+    void* ws = nullptr;
+    st = scratch_for(dev, stream, hstu::worklist_bytes(num_seqs), &ws);
+    if (st != HSTU_OK) return st;
+    const hstu::WorkList wl = hstu::worklist_carve(ws, num_seqs);
+
+    hstu::FwdParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.out = out;
+    p.offsets = seq_offsets;
+    p.num_seqs = num_seqs;
+    p.heads = heads;
+    p.d = d;
+    p.alpha = alpha;
+    p.n = n;
+
+    TimedCall tc;
+    const bool timed = prof_take(&tc);
+    hipError_t e;
+    if (timed && (e = hipEventRecord(tc.e[0], stream)) != hipSuccess) return hip_fail(e);
+    e = hstu::launch_schedule(seq_offsets, num_seqs, heads, hstu::q_tile_rows(dt, d), wl, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if (timed && (e = hipEventRecord(tc.e[1], stream)) != hipSuccess) return hip_fail(e);
+    e = hstu::launch_attention(p, dt, wl, 0, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if (timed) {
+        if ((e = hipEventRecord(tc.e[2], stream)) != hipSuccess) return hip_fail(e);
+        prof_commit(tc);
+    }
+    if (validate_env()) {
+        int ctl[hstu::CTL_WORDS];
+        e = hipMemcpyAsync(ctl, wl.ctl, sizeof ctl, hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_fail(e);
+        if (ctl[hstu::CTL_FLAGS] != 0) return HSTU_ERR_BAD_OFFSETS;
+    }
+    return HSTU_OK;
+}
+
+hstu_status_t hstu_attn_fwd_bf16(const void* q, const void* k, const void* v,
+                                 const int32_t* seq_offsets, int32_t num_seqs, int32_t heads,
+                                 int32_t d, float alpha, float n, void* out, hipStream_t stream) {
+    return hstu_attn_fwd(q, k, v, seq_offsets, num_seqs, heads, d, alpha, n, out, stream,
+                         HSTU_BF16);
+}
+
+hstu_status_t hstu_attn_fwd_fp16(const void* q, const void* k, const void* v,
+                                 const int32_t* seq_offsets, int32_t num_seqs, int32_t heads,
+                                 int32_t d, float alpha, float n, void* out, hipStream_t stream) {
+    return hstu_attn_fwd(q, k, v, seq_offsets, num_seqs, heads, d, alpha, n, out, stream,
+                         HSTU_FP16);
+}
+
+hstu_status_t hstu_attn_fwd_fp32(const void* q, const void* k, const void* v,
+                                 const int32_t* seq_offsets, int32_t num_seqs, int32_t heads,
+                                 int32_t d, float alpha, float n, void* out, hipStream_t stream) {
+    return hstu_attn_fwd(q, k, v, seq_offsets, num_seqs, heads, d, alpha, n, out, stream,
+                         HSTU_FP32);
+}
+
+hstu_status_t hstu_validate_offsets(const int32_t* seq_offsets, int32_t num_seqs,
+                                    int64_t* total, hipStream_t stream) {
+    if (num_seqs < 0) return HSTU_ERR_INVALID_ARG;
+    if (num_seqs > 0 && !seq_offsets) return HSTU_ERR_INVALID_ARG;
+    if (num_seqs == 0) {
+        if (total) *total = 0;
+        return HSTU_OK;
+    }
+    std::vector<int32_t> h((size_t)num_seqs + 1);
+    hipError_t e = hipMemcpyAsync(h.data(), seq_offsets, sizeof(int32_t) * h.size(),
+                                  hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if (total) *total = h[num_seqs];
+    if (h[0] != 0) return HSTU_ERR_BAD_OFFSETS;
+    for (int32_t i = 0; i < num_seqs; ++i)
+        if (h[i + 1] < h[i]) return HSTU_ERR_BAD_OFFSETS;
+    return HSTU_OK;
+}
+
+const char* hstu_status_string(hstu_status_t status) {
+    switch (status) {
+    case HSTU_OK: return "ok";
+    case HSTU_ERR_INVALID_ARG: return "invalid argument";
+    case HSTU_ERR_UNSUPPORTED: return "unsupported head size, element type or device";
+    case HSTU_ERR_HIP: return "HIP runtime error";
+    case HSTU_ERR_NO_MEMORY: return "scratch allocation failed";
+    case HSTU_ERR_BAD_OFFSETS: return "malformed sequence offsets";
+    }
+    return "unknown status";
+}
+
+int hstu_last_hip_error(void) { return g_last_hip; }
+
+void hstu_release_workspace(void) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    for (auto it = g_scratch.begin(); it != g_scratch.end();) {
+        if (it->first.first == dev) {
+            if (it->second.ptr) (void)hipFree(it->second.ptr);
+            it = g_scratch.erase(it);
+        } else {
+            ++it;
+        }
+    }
+}
+
+hstu_status_t hstu_profile_enable(int on) {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    g_prof_on = on != 0;
+    return HSTU_OK;
+}
+
+hstu_status_t hstu_profile_read(hstu_kernel_times_t* out, int reset) {
+    if (!out) return HSTU_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    for (const TimedCall& tc : g_prof_pending) {
+        hipError_t e = hipEventSynchronize(tc.e[2]);
+        if (e != hipSuccess) return hip_fail(e);
+        float a = 0.f, b = 0.f;
+        e = hipEventElapsedTime(&a, tc.e[0], tc.e[1]);
+        if (e == hipSuccess) e = hipEventElapsedTime(&b, tc.e[1], tc.e[2]);
+        if (e != hipSuccess) return hip_fail(e);
+        g_prof_total.calls++;
+        g_prof_total.sched_ms += a;
+        g_prof_total.attn_ms += b;
+        g_prof_free.push_back(tc);
+    }
+    g_prof_pending.clear();
+    *out = g_prof_total;
+    if (reset) g_prof_total = hstu_kernel_times_t{0, 0.0, 0.0, 0};
+    return HSTU_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+/*
+ * hstu.h -- C ABI of the HSTU jagged causal attention forward for AMD MI355X
+ * (gfx950).
+ *
+ * Operation (Ascend HSTU blog "都是生成式推荐，为什么昇腾这么快？", §1: the
+ * formula HSTU(Q,K,V) = (mask/n) * silu(Q K^T / alpha^-1) V and its five-step
+ * PyTorch definition; §3.2: causal mask generated inside the operator, diagonal
+ * blocks lower-triangular, blocks above the diagonal skipped; §4.2: jagged
+ * values + offsets input):
+ *
+ *   for every sequence i (tokens off[i] .. off[i+1]-1), head h, local row r:
+ *     out[off[i]+r][h][:] = (1/n) * sum_{c=0..r} silu(alpha * <q[off[i]+r][h], k[off[i]+c][h]>)
+ *                                                * v[off[i]+c][h][:]
+ *   silu(x) = x / (1 + e^-x)   (HSTU paper translation "行动胜于言语…", §3: phi_2 = SiLU)
+ *
+ * Sequences never attend to each other; the mask keeps c <= r (diagonal
+ * included) and multiplies after SiLU, so masked terms are exactly zero.
+ *
+ * Layouts (all device pointers, caller-owned):
+ *   q, k, v, out : row-major (T, heads, d) of one element type, T = off[num_seqs];
+ *                  the row of token t, head h starts at element (t*heads + h)*d.
+ *                  16-byte aligned.  out must not overlap q, k, v or the offsets.
+ *   seq_offsets  : int32[num_seqs + 1], off[0] = 0, non-decreasing.  Lives on the
+ *                  device; the host never reads it.  Empty sequences are allowed.
+ *   alpha, n     : float32 scalars; alpha multiplies the scores before SiLU, n
+ *                  divides the result.  n must be finite and non-zero, alpha finite.
+ *
+ * Element types: bfloat16 and float16 run on the matrix cores with float32
+ * accumulation, the SiLU in float32 and the weights rounded to the input type
+ * (nearest even) before the second product; float32 runs both products in
+ * float32.  out has the same element type as q/k/v, rounded to nearest even.
+ * Supported head sizes: d = 64 and d = 128; heads >= 1; num_seqs >= 0 (0 is a
+ * no-op).
+ *
+ * Streams and memory: every device operation is enqueued on `stream` (0 = the
+ * null stream); no call synchronises the host except hstu_validate_offsets and
+ * hstu_profile_read.  The library owns a small grow-only scratch area per
+ * (device, stream): a work list of 12 bytes per sequence plus a header.  It is
+ * allocated on the first call that needs more; later calls with no more
+ * sequences allocate nothing.  Two calls on the same stream are ordered by the
+ * stream; calls on different streams use different scratch areas.
+ *
+ * Errors: argument checks happen on the host before anything is enqueued; a
+ * failed check returns a negative status and leaves the stream untouched.  A
+ * failed HIP call returns HSTU_ERR_HIP and its hipError_t is kept for
+ * hstu_last_hip_error() (per thread).  Malformed device offsets (off[0] != 0 or
+ * decreasing) are not detected by the forward call itself: sequences with a
+ * negative length are treated as empty, and what is computed for the rest is
+ * unspecified; hstu_validate_offsets checks them synchronously.
+ */
+#ifndef HSTU_H_
+#define HSTU_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+    HSTU_OK = 0,
+    HSTU_ERR_INVALID_ARG = -1, /* null pointer, negative count, bad scalar, misaligned */
+    HSTU_ERR_UNSUPPORTED = -2, /* d or dtype not supported, or no gfx950 device */
+    HSTU_ERR_HIP = -3,         /* a HIP runtime call failed (see hstu_last_hip_error) */
+    HSTU_ERR_NO_MEMORY = -4,   /* the scratch area could not be grown */
+    HSTU_ERR_BAD_OFFSETS = -5  /* hstu_validate_offsets found malformed offsets */
+} hstu_status_t;
+
+typedef enum { HSTU_BF16 = 0, HSTU_FP16 = 1, HSTU_FP32 = 2 } hstu_dtype_t;
+
+/* The forward pass with the element type given by `dtype`.  The first eleven
+ * parameters are the call's data; see the file comment for their meaning. */
+hstu_status_t hstu_attn_fwd(const void* q, const void* k, const void* v,
+                            const int32_t* seq_offsets, int32_t num_seqs, int32_t heads,
+                            int32_t d, float alpha, float n, void* out, hipStream_t stream,
+                            hstu_dtype_t dtype);
+
+/* The same call with the element type fixed by the name. */
+hstu_status_t hstu_attn_fwd_bf16(const void* q, const void* k, const void* v,
+                                 const int32_t* seq_offsets, int32_t num_seqs, int32_t heads,
+                                 int32_t d, float alpha, float n, void* out, hipStream_t stream);
+hstu_status_t hstu_attn_fwd_fp16(const void* q, const void* k, const void* v,
+                                 const int32_t* seq_offsets, int32_t num_seqs, int32_t heads,
+                                 int32_t d, float alpha, float n, void* out, hipStream_t stream);
+hstu_status_t hstu_attn_fwd_fp32(const void* q, const void* k, const void* v,
+                                 const int32_t* seq_offsets, int32_t num_seqs, int32_t heads,
+                                 int32_t d, float alpha, float n, void* out, hipStream_t stream);
+
+/* Checks device offsets synchronously: off[0] == 0 and non-decreasing.  Writes
+ * T = off[num_seqs] to *total (may be NULL).  Returns HSTU_OK or
+ * HSTU_ERR_BAD_OFFSETS; synchronises `stream`. */
+hstu_status_t hstu_validate_offsets(const int32_t* seq_offsets, int32_t num_seqs,
+                                    int64_t* total, hipStream_t stream);
+
+/* Human-readable name of a status. */
+const char* hstu_status_string(hstu_status_t status);
+
+/* The hipError_t (as int) of the last failed HIP call on this thread. */
+int hstu_last_hip_error(void);
+
+/* Frees every scratch area the library holds on the current device.  Must not
+ * race with calls in flight on that device (synchronise first). */
+void hstu_release_workspace(void);
+
+/* ---- kernel timing (for benchmarks) -------------------------------------- */
+
+/* Per-kernel time accumulated over calls made while profiling was on. */
+typedef struct {
+    int64_t calls;        /* forward calls timed */
+    double sched_ms;      /* total time of the work-list kernel */
+    double attn_ms;       /* total time of the attention kernel */
+    int64_t dropped;      /* calls not timed because the event ring was full */
+} hstu_kernel_times_t;
+
+/* on != 0: from now on each forward call on this thread's current device
+ * records HIP events on its stream around its two kernels. */
+hstu_status_t hstu_profile_enable(int on);
+
+/* Waits for the recorded events, adds their durations to *out and, if reset,
+ * clears the accumulated totals. */
+hstu_status_t hstu_profile_read(hstu_kernel_times_t* out, int reset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSTU_H_ */

@@ -1,0 +1,103 @@
+"""The C ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments before touching any device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import generative_recommendation_attention_amd as hstu
+from generative_recommendation_attention_amd import build as hstu_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hstu.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hstu.LIBRARY):
+        hstu_build.build()
+    return hstu.load_library()
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hstu_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_forward_family():
+    names = declared_functions()
+    for n in ("hstu_attn_fwd", "hstu_attn_fwd_bf16", "hstu_attn_fwd_fp16", "hstu_attn_fwd_fp32"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(hstu.EXPORTS)
+
+
+def _call(lib, q=16, k=16, v=16, off=16, num_seqs=1, heads=1, d=64, alpha=0.1, n=1.0,
+          out=32, dtype=hstu.HSTU_BF16):
+    return lib.hstu_attn_fwd(q, k, v, off, num_seqs, heads, d, alpha, n, out, None, dtype)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(k=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(v=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(off=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(out=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(num_seqs=-1), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(heads=0), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(d=96), hstu.HSTU_ERR_UNSUPPORTED),
+    (dict(d=0), hstu.HSTU_ERR_UNSUPPORTED),
+    (dict(dtype=7), hstu.HSTU_ERR_UNSUPPORTED),
+    (dict(n=0.0), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(n=float("inf")), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(alpha=float("nan")), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(q=24), hstu.HSTU_ERR_INVALID_ARG),       # misaligned
+    (dict(out=40), hstu.HSTU_ERR_INVALID_ARG),     # misaligned
+    (dict(off=18), hstu.HSTU_ERR_INVALID_ARG),     # misaligned offsets
+    (dict(out=16), hstu.HSTU_ERR_INVALID_ARG),     # out aliases q
+])
+def test_argument_checks(lib, kw, status):
+    assert _call(lib, **kw) == status
+
+
+def test_empty_batch_is_a_no_op(lib):
+    assert _call(lib, q=None, k=None, v=None, off=None, out=None, num_seqs=0) == hstu.HSTU_OK
+
+
+def test_typed_entry_points_check_arguments(lib):
+    for name in ("hstu_attn_fwd_bf16", "hstu_attn_fwd_fp16", "hstu_attn_fwd_fp32"):
+        fn = getattr(lib, name)
+        assert fn(16, 16, 16, 16, 1, 1, 80, 0.1, 1.0, 32, None) == hstu.HSTU_ERR_UNSUPPORTED
+        assert fn(None, None, None, None, 0, 1, 64, 0.1, 1.0, None, None) == hstu.HSTU_OK
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4, -5):
+        assert lib.hstu_status_string(st)
+    assert lib.hstu_status_string(-99) == b"unknown status"
+
+
+def test_validate_offsets_argument_checks(lib):
+    assert lib.hstu_validate_offsets(None, -1, None, None) == hstu.HSTU_ERR_INVALID_ARG
+    assert lib.hstu_validate_offsets(None, 1, None, None) == hstu.HSTU_ERR_INVALID_ARG
+    total = ctypes.c_int64(5)
+    assert lib.hstu_validate_offsets(None, 0, ctypes.byref(total), None) == hstu.HSTU_OK
+    assert total.value == 0
+
+
+def test_profile_read_without_calls(lib):
+    t = hstu.KernelTimes()
+    assert lib.hstu_profile_read(None, 0) == hstu.HSTU_ERR_INVALID_ARG
+    assert lib.hstu_profile_read(ctypes.byref(t), 1) == hstu.HSTU_OK
+    assert t.calls == 0
+
+
+def test_python_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        hstu.load_library(str(tmp_path / "nope.so"))
