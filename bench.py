@@ -88,6 +88,9 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--copy-calibrate", action="store_true",
+                    help="run only a plain 1 GiB device copy (3 times), the reference for "
+                         "scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -99,6 +102,15 @@ def main() -> int:
     import generative_recommendation_attention_amd as hstu
 
     torch.cuda.set_device(0)
+    if args.copy_calibrate:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
+                          "copies": 3}), flush=True)
+        return 0
     case = workloads.workload(args.workload)
     q, k, v, off = to_device(case)
     out = torch.empty_like(q)

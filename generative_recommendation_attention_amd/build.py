@@ -31,6 +31,7 @@ def hipcc() -> str:
 def command(output: str = LIBRARY, extra=()) -> list:
     return ([hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form",
              "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
             + list(extra) + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", output])
 

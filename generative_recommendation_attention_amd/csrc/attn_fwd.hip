@@ -12,9 +12,10 @@
 // register file.
 //
 // Persistent workgroups pull items (sequence, head, Q tile) from the work list
-// built by schedule.hip.  Per item, each wave owns 32 query rows and walks the
-// key/value tiles 0..(last tile that reaches its rows), staged through LDS and
-// double buffered: while tile c is consumed, tile c+1 is in flight from HBM.
+// built by schedule.hip.  Per item, each wave owns 32 or 64 query rows and
+// walks the key/value tiles 0..(last tile that reaches its rows), staged
+// through LDS and double buffered: while tile c is consumed, tile c+1 is in
+// flight from HBM.
 //
 // Transposed products.  With v_mfma_f32_32x32x16_{bf16,f16} a lane's C/D
 // registers hold one column and 16 rows of a 32x32 block:
@@ -22,9 +23,9 @@
 // Computing S^T = K Q^T (keys down, queries across) therefore leaves each lane
 // with one query and 16 keys, which is the k-slice the second product
 // O^T = V^T P^T needs in its B operand.  The keys a lane holds for k-step t are
-// {16t + 8*(e/4) + 4*(lane/32) + e%4 : e = 0..7}; V^T is stored in LDS with
-// bits 2 and 3 of the key index swapped inside each group of 16, so a lane's
-// eight matching V values are one contiguous 16-byte read.
+// {16t + 8*(e/4) + 4*(lane/32) + e%4 : e = 0..7}.  For bf16/fp16, V stays
+// row-major in LDS and gfx950's transposing LDS read hands each lane exactly
+// those keys for its head-dim row of V^T; the fp32 kernel needs no transpose.
 //
 // Scaling.  With m = -alpha*log2(e)*s, silu(alpha*s) = -(m / log2(e)) *
 // 1/(1 + 2^m).  The kernel forms p = m * rcp(1 + exp2(m)) (one multiply, two
@@ -85,11 +86,6 @@ struct Mfma<_Float16> {
     }
 };
 
-// Position in LDS of key `kv` inside its group of 16: bits 2 and 3 swapped.
-__device__ __forceinline__ int vt_pos(int kv) {
-    return (kv & ~12) | ((kv & 4) << 1) | ((kv & 8) >> 1);
-}
-
 // -log2(e) * silu(alpha*s), given m = -alpha*log2(e)*s.
 __device__ __forceinline__ float silu_scaled(float m) {
     const float t = __builtin_amdgcn_exp2f(m);
@@ -97,132 +93,203 @@ __device__ __forceinline__ float silu_scaled(float m) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 / fp16: one wave = 32 query rows; NW waves per workgroup.
+// Buffer resources.  Every load and store goes through a raw buffer whose
+// range ends at the current sequence's last token: a load past it returns
+// zero and a store past it is dropped, so tile tails need no predicates and
+// nothing outside the sequence is ever touched.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int NW, int BK>
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int RSRC_WORD3 = 0x00020000;  // gfx9 raw buffer, 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, RSRC_WORD3);
+}
+
+// LDS transposing read of four 16-bit values (gfx950 ds_read_b64_tr_b16).
+// Within each group of 16 lanes, lane i receives element (i % 4) of the
+// 8 bytes addressed by lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12 of its group.
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+// ---------------------------------------------------------------------------
+// bf16 / fp16: one wave = QB blocks of 32 query rows; NW waves per workgroup.
+// K and V tiles are both stored row-major in LDS (row stride D + 8 elements).
+// The S^T = K Q^T product reads K rows with ds_read_b128; the O^T = V^T P^T
+// product reads V^T with two transposing reads per 16-key step: for lane l
+// (j = l % 16, half h = (l / 16) % 2, g = l / 32) the first read covers keys
+// 16u + 4g + (0..3) and the second 16u + 8 + 4g + (0..3), at head-dim column
+// 32*db + 16h + (l % 16), matching the keys S^T leaves in the lane.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NW, int QB, int BK>
 struct Tile16 {
-    static constexpr int BQ = NW * 32;              // query rows per item
+    static constexpr int ROWS_W = 32 * QB;          // query rows per wave
+    static constexpr int BQ = NW * ROWS_W;          // query rows per item
     static constexpr int THREADS = NW * 64;
-    static constexpr int KSTR = D + 8;              // K row stride in LDS (elements)
-    static constexpr int VSTR = BK + 8;             // V^T row stride in LDS (elements)
-    static constexpr int K_ELEMS = BK * KSTR;
-    static constexpr int V_ELEMS = D * VSTR;
-    static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-    static constexpr int K_CHUNKS = BK * D / 8 / THREADS;   // 16-byte K loads per thread
-    static constexpr int V_UNITS = BK * D / 16 / THREADS;   // (2 rows x 8 cols) V units per thread
-    static_assert(K_CHUNKS * THREADS * 8 == BK * D, "K tile must split evenly");
-    static_assert(V_UNITS * THREADS * 16 == BK * D, "V tile must split evenly");
+    static constexpr int STR = D + 8;               // LDS row stride (elements)
+    static constexpr int TILE = BK * STR;           // elements per K or V tile
+    static constexpr int CHUNKS = BK * D / 8 / THREADS;  // 16-byte loads per thread per tensor
+    static_assert(CHUNKS * THREADS * 8 == BK * D, "tile must split evenly over the threads");
     static_assert(BK % 32 == 0 && D % 32 == 0, "tile shape");
 };
 
-template <typename T, int D, int NW, int BK>
+template <typename T, int D, int NW, int QB, int BK>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma16(KernelArgs a) {
-    using Cfg = Tile16<T, D, NW, BK>;
+    using Cfg = Tile16<T, D, NW, QB, BK>;
     using M = Mfma<T>;
     using v8 = typename M::v8;
     using v4 = typename M::v4;
+    constexpr int ROWS_W = Cfg::ROWS_W;
     constexpr int BQ = Cfg::BQ;
-    constexpr int KSTR = Cfg::KSTR;
-    constexpr int VSTR = Cfg::VSTR;
+    constexpr int STR = Cfg::STR;
+    constexpr int TILE = Cfg::TILE;
+    constexpr int NKB = BK / 32;   // 32-key blocks per tile
+    constexpr int NKS = D / 16;    // k-steps of the first product
+    constexpr int NDB = D / 32;    // 32-wide head-dim blocks of the output
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Cfg::BUF_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * TILE];  // [buffer][K, V]
     __shared__ int s_item;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wv = tid >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5;
     const int l32 = lane & 31;
     const int H = a.heads;
-    const int64_t row_stride = (int64_t)H * D;  // elements between consecutive tokens
+    const int64_t row_stride = (int64_t)H * D;      // elements between consecutive tokens
+    const int row_bytes = (int)(row_stride * 2);
     const int total = a.wl.ctl[CTL_TOTAL];
     const int mode = a.wl.ctl[CTL_MODE];
+
+    // Lane-constant parts of the LDS addresses.
+    const int k_rd = l32 * STR + g * 8;                               // K operand
+    const int v_rd = (4 * g + ((lane & 15) >> 2)) * STR +             // V^T operand
+                     ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+    // Staging: chunk i of this thread is row r_i, 8-element column c_i.
+    int st_goff[Cfg::CHUNKS], st_loff[Cfg::CHUNKS];
+#pragma unroll
+    for (int i = 0; i < Cfg::CHUNKS; ++i) {
+        const int id = tid + i * Cfg::THREADS;
+        const int r = id / (D / 8), c8 = id % (D / 8);
+        st_goff[i] = r * row_bytes + c8 * 16;
+        st_loff[i] = r * STR + c8 * 8;
+    }
 
     for (;;) {
         if (tid == 0) s_item = atomicAdd(a.wl.ctl + CTL_NEXT, 1);
         __syncthreads();
-        const int w = s_item;
+        const int w = __builtin_amdgcn_readfirstlane(s_item);
         if (w >= total) break;
         const Item it = decode_item(a.wl, mode, a.num_seqs, H, w);
-        const int start = a.offsets[it.seq];
-        const int s = a.offsets[it.seq + 1] - start;
-        const int q0 = it.qtile * BQ;
+        const int seq = __builtin_amdgcn_readfirstlane(it.seq);
+        const int head = __builtin_amdgcn_readfirstlane(it.head);
+        const int qtile = __builtin_amdgcn_readfirstlane(it.qtile);
+        const int start = a.offsets[seq];
+        const int s = a.offsets[seq + 1] - start;
+        const int q0 = qtile * BQ;
         const int kv_end = min(s, q0 + BQ);
         const int n_tiles = (kv_end + BK - 1) / BK;
-        const int wr0 = q0 + wv * 32;  // this wave's first query row (local)
+        const int wr0 = q0 + wv * ROWS_W;   // this wave's first query row (local)
         const bool wave_live = wr0 < s;
-        const int my_row = wr0 + l32;
-        const int64_t head_off = (int64_t)it.head * D;
-        const int64_t seq_base = (int64_t)start * row_stride + head_off;
+        const int64_t seq_base = (int64_t)start * row_stride + (int64_t)head * D;
 
-        // Q^T operand: query my_row, head-dim slice [16*ks + 8*g, +8).
-        v8 qop[D / 16];
+        // Q^T operand: query rows wr0 + 32*qb + l32, head-dim slice [16*ks + 8*g, +8).
+        v8 qop[QB][NKS];
         {
-            const uint4* qp = reinterpret_cast<const uint4*>(a.q + seq_base +
-                                                            (int64_t)my_row * row_stride);
+            const __amdgpu_buffer_rsrc_t rq =
+                    make_rsrc(a.q + seq_base + (int64_t)wr0 * row_stride,
+                              (int64_t)(s - wr0) * row_bytes);
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                uint4 x = make_uint4(0, 0, 0, 0);
-                if (my_row < s) x = qp[ks * 2 + g];
-                qop[ks] = __builtin_bit_cast(v8, x);
-            }
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    qop[qb][ks] = __builtin_bit_cast(
+                            v8, __builtin_amdgcn_raw_buffer_load_b128(
+                                        rq, (qb * 32 + l32) * row_bytes + (ks * 16 + g * 8) * 2, 0, 0));
         }
-        f32x16 o[D / 32];
+        f32x16 o[NDB][QB];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[db] = (f32x16){};
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) o[db][qb] = (f32x16){};
 
-        // Staging registers for one K/V tile.
-        uint4 kreg[Cfg::K_CHUNKS];
-        uint4 vreg[Cfg::V_UNITS][2];
-
+        u32x4 kreg[Cfg::CHUNKS], vreg[Cfg::CHUNKS];
         auto load_tile = [&](int c) {
             const int k0 = c * BK;
+            const int64_t off = seq_base + (int64_t)k0 * row_stride;
+            const int64_t bytes = (int64_t)(s - k0) * row_bytes;
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + off, bytes);
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + off, bytes);
 #pragma unroll
-            for (int i = 0; i < Cfg::K_CHUNKS; ++i) {
-                const int id = tid + i * Cfg::THREADS;
-                const int r = id / (D / 8), c8 = id % (D / 8);
-                uint4 x = make_uint4(0, 0, 0, 0);
-                if (k0 + r < s)
-                    x = *reinterpret_cast<const uint4*>(a.k + seq_base +
-                                                        (int64_t)(k0 + r) * row_stride + c8 * 8);
-                kreg[i] = x;
-            }
-#pragma unroll
-            for (int i = 0; i < Cfg::V_UNITS; ++i) {
-                const int id = tid + i * Cfg::THREADS;
-                const int rp = id / (D / 8), c8 = id % (D / 8);
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-                    const int r = 2 * rp + h2;
-                    uint4 x = make_uint4(0, 0, 0, 0);
-                    if (k0 + r < s)
-                        x = *reinterpret_cast<const uint4*>(
-                                a.v + seq_base + (int64_t)(k0 + r) * row_stride + c8 * 8);
-                    vreg[i][h2] = x;
-                }
+            for (int i = 0; i < Cfg::CHUNKS; ++i) {
+                kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, st_goff[i], 0, 0);
+                vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, st_goff[i], 0, 0);
             }
         };
         auto store_tile = [&](int buf) {
-            uint16_t* kl = lds + buf * Cfg::BUF_ELEMS;
-            uint16_t* vl = kl + Cfg::K_ELEMS;
+            uint16_t* kl = lds + buf * 2 * TILE;
+            uint16_t* vl = kl + TILE;
 #pragma unroll
-            for (int i = 0; i < Cfg::K_CHUNKS; ++i) {
-                const int id = tid + i * Cfg::THREADS;
-                const int r = id / (D / 8), c8 = id % (D / 8);
-                *reinterpret_cast<uint4*>(kl + r * KSTR + c8 * 8) = kreg[i];
+            for (int i = 0; i < Cfg::CHUNKS; ++i) {
+                *reinterpret_cast<u32x4*>(kl + st_loff[i]) = kreg[i];
+                *reinterpret_cast<u32x4*>(vl + st_loff[i]) = vreg[i];
             }
+        };
+
+        // One key/value tile, one 32-key block at a time: S^T for the block,
+        // the pointwise pass and the second product over the block's two
+        // 16-key steps.  On the tile that crosses the diagonal, scores with
+        // key > query are zeroed before the pointwise pass: silu(0) = 0, so
+        // they contribute exactly nothing (the mask multiplies after SiLU).
+        auto compute = [&](const uint16_t* kl, const uint16_t* vl, int k0, bool diag) {
 #pragma unroll
-            for (int i = 0; i < Cfg::V_UNITS; ++i) {
-                const int id = tid + i * Cfg::THREADS;
-                const int rp = id / (D / 8), c8 = id % (D / 8);
-                const int pos = vt_pos(2 * rp);
-                const uint32_t* x0 = reinterpret_cast<const uint32_t*>(&vreg[i][0]);
-                const uint32_t* x1 = reinterpret_cast<const uint32_t*>(&vreg[i][1]);
+            for (int kb = 0; kb < NKB; ++kb) {
+                f32x16 st[QB];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t lo = (x0[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-                    const uint32_t hi = (x1[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-                    *reinterpret_cast<uint32_t*>(vl + (c8 * 8 + e) * VSTR + pos) = lo | (hi << 16);
+                for (int qb = 0; qb < QB; ++qb) st[qb] = (f32x16){};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const v8 ka = *reinterpret_cast<const v8*>(kl + k_rd + kb * 32 * STR + ks * 16);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) st[qb] = M::mma(ka, qop[qb][ks], st[qb]);
+                }
+                if (diag) {
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) {
+                        // keep key k0 + 32kb + 8(r/4) + 4g + r%4 <= query wr0 + 32qb + l32
+                        const int lim = wr0 - k0 + 32 * (qb - kb) + l32 - 4 * g;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            st[qb][r] = (8 * (r >> 2) + (r & 3) <= lim) ? st[qb][r] : 0.0f;
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int u = kb * 2 + t;
+                    v8 pb[QB];
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) {
+                        f32x8 pf;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            pf[e] = silu_scaled(st[qb][8 * t + e] * a.score_scale);
+                        pb[qb] = __builtin_convertvector(pf, v8);
+                    }
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const uint16_t* vp = vl + v_rd + u * 16 * STR + db * 32;
+                        const i16x4 lo = lds_read_tr16(vp);
+                        const i16x4 hi = lds_read_tr16(vp + 8 * STR);
+                        const v8 va = __builtin_bit_cast(
+                                v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                        for (int qb = 0; qb < QB; ++qb) o[db][qb] = M::mma(va, pb[qb], o[db][qb]);
+                    }
                 }
             }
         };
@@ -235,66 +302,34 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma16(KernelArgs a) {
             const bool more = c + 1 < n_tiles;
             if (more) load_tile(c + 1);
             const int k0 = c * BK;
-            const bool skip = !wave_live || k0 > wr0 + 31;
-            if (!skip) {
-                const uint16_t* kl = lds + (c & 1) * Cfg::BUF_ELEMS;
-                const uint16_t* vl = kl + Cfg::K_ELEMS;
-                const bool partial = k0 + BK - 1 > wr0;
-                // S^T = K Q^T, one 32-key block at a time.
-                f32x16 st[BK / 32];
-#pragma unroll
-                for (int kb = 0; kb < BK / 32; ++kb) {
-                    st[kb] = (f32x16){};
-#pragma unroll
-                    for (int ks = 0; ks < D / 16; ++ks) {
-                        const v8 ka = *reinterpret_cast<const v8*>(
-                                kl + (kb * 32 + l32) * KSTR + ks * 16 + g * 8);
-                        st[kb] = M::mma(ka, qop[ks], st[kb]);
-                    }
-                }
-                // Pointwise pass and the second product, per 16-key step.
-#pragma unroll
-                for (int kb = 0; kb < BK / 32; ++kb) {
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        f32x8 pf;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            float p = silu_scaled(st[kb][8 * t + e] * a.score_scale);
-                            if (partial) {
-                                const int kv = k0 + kb * 32 + 16 * t + 8 * (e >> 2) + 4 * g + (e & 3);
-                                p = (kv <= my_row) ? p : 0.0f;
-                            }
-                            pf[e] = p;
-                        }
-                        const v8 pb = __builtin_convertvector(pf, v8);
-#pragma unroll
-                        for (int db = 0; db < D / 32; ++db) {
-                            const v8 va = *reinterpret_cast<const v8*>(
-                                    vl + (db * 32 + l32) * VSTR + (kb * 2 + t) * 16 + g * 8);
-                            o[db] = M::mma(va, pb, o[db]);
-                        }
-                    }
-                }
+            if (wave_live && k0 <= wr0 + ROWS_W - 1) {
+                const uint16_t* kl = lds + (c & 1) * 2 * TILE;
+                compute(kl, kl + TILE, k0, k0 + BK - 1 > wr0);
             }
             if (more) store_tile((c + 1) & 1);
             __syncthreads();
         }
 
-        // Epilogue: lane holds query my_row, head-dim rows 32*db + 8*i + 4*g + (0..3).
-        if (my_row < s) {
-            uint16_t* op = a.out + seq_base + (int64_t)my_row * row_stride;
+        // Epilogue: lane holds query wr0 + 32*qb + l32 and head-dim rows
+        // 32*db + 8*i + 4*g + (0..3).  Stores past the sequence are dropped.
+        if (wave_live) {
+            const __amdgpu_buffer_rsrc_t ro =
+                    make_rsrc(a.out + seq_base + (int64_t)wr0 * row_stride,
+                              (int64_t)(s - wr0) * row_bytes);
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
+            for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    f32x4 x;
+                for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) x[j] = o[db][4 * i + j] * a.out_scale;
-                    const v4 y = __builtin_convertvector(x, v4);
-                    *reinterpret_cast<v4*>(op + db * 32 + 8 * i + 4 * g) = y;
-                }
-            }
+                    for (int i = 0; i < 4; ++i) {
+                        f32x4 x;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) x[j] = o[db][qb][4 * i + j] * a.out_scale;
+                        const v4 y = __builtin_convertvector(x, v4);
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                                __builtin_bit_cast(u32x2, y), ro,
+                                (qb * 32 + l32) * row_bytes + (db * 32 + 8 * i + 4 * g) * 2, 0, 0);
+                    }
         }
     }
 }
@@ -436,6 +471,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
 // ---------------------------------------------------------------------------
 constexpr int NW16 = 4;
 constexpr int BK16 = 64;
+template <int D> struct QBlocks { static constexpr int value = D == 64 ? 2 : 1; };
 constexpr int NWF = 4;
 constexpr int BKF = 32;
 
@@ -481,7 +517,7 @@ hipError_t launch16(const FwdParams& p, WorkList wl, int grid, hipStream_t strea
     a.heads = p.heads;
     a.score_scale = -p.alpha * LOG2E;
     a.out_scale = -LN2 / p.n;
-    auto fn = attn_fwd_mfma16<T, D, NW16, BK16>;
+    auto fn = attn_fwd_mfma16<T, D, NW16, QBlocks<D>::value, BK16>;
     if (grid <= 0) {
         static int cached = 0;
         if (!cached) cached = resident_grid(fn, NW16 * 64);
@@ -517,8 +553,9 @@ hipError_t launch_f32(const FwdParams& p, WorkList wl, int grid, hipStream_t str
 }  // namespace
 
 int q_tile_rows(Dtype dt, int d) {
-    (void)d;
-    return dt == Dtype::FP32 ? TileF32<64, NWF, BKF>::BQ : Tile16<__bf16, 64, NW16, BK16>::BQ;
+    if (dt == Dtype::FP32) return TileF32<64, NWF, BKF>::BQ;
+    return d == 64 ? Tile16<__bf16, 64, NW16, QBlocks<64>::value, BK16>::BQ
+                   : Tile16<__bf16, 128, NW16, QBlocks<128>::value, BK16>::BQ;
 }
 
 hipError_t launch_attention(const FwdParams& p, Dtype dt, WorkList wl, int grid,
