@@ -134,6 +134,7 @@ hstu_status_t check_args(const void* q, const void* k, const void* v, const int3
                          const void* out, int dtype) {
     if (dtype != HSTU_BF16 && dtype != HSTU_FP16 && dtype != HSTU_FP32) return HSTU_ERR_UNSUPPORTED;
     if (num_seqs < 0 || heads < 1) return HSTU_ERR_INVALID_ARG;
+    if ((long long)num_seqs * heads > 0x7fffffffLL) return HSTU_ERR_UNSUPPORTED;
     if (d != 64 && d != 128) return HSTU_ERR_UNSUPPORTED;
     if (!std::isfinite(alpha) || !std::isfinite(n) || n == 0.0f) return HSTU_ERR_INVALID_ARG;
     if (num_seqs == 0) return HSTU_OK;
@@ -148,6 +149,15 @@ hstu_status_t check_args(const void* q, const void* k, const void* v, const int3
 bool validate_env() {
     const char* s = getenv("HSTU_VALIDATE");
     return s && atoi(s) != 0;
+}
+
+// HSTU_SCHED_SORT=bitonic|input forces one ranking path of the scheduler.
+hstu::SortChoice sort_choice_env() {
+    const char* s = getenv("HSTU_SCHED_SORT");
+    if (!s) return hstu::SortChoice::AUTO;
+    if (std::strcmp(s, "bitonic") == 0) return hstu::SortChoice::BITONIC;
+    if (std::strcmp(s, "input") == 0) return hstu::SortChoice::INPUT_ORDER;
+    return hstu::SortChoice::AUTO;
 }
 
 }  // namespace
@@ -166,9 +176,9 @@ hstu_status_t hstu_attn_fwd(const void* q, const void* k, const void* v,
 
     const hstu::Dtype dt = static_cast<hstu::Dtype>(dtype);
     void* ws = nullptr;
-    st = scratch_for(dev, stream, hstu::worklist_bytes(num_seqs), &ws);
+    st = scratch_for(dev, stream, hstu::worklist_bytes(num_seqs, heads), &ws);
     if (st != HSTU_OK) return st;
-    const hstu::WorkList wl = hstu::worklist_carve(ws, num_seqs);
+    const hstu::WorkList wl = hstu::worklist_carve(ws, num_seqs, heads);
 
     hstu::FwdParams p;
     p.q = q;
@@ -186,7 +196,8 @@ hstu_status_t hstu_attn_fwd(const void* q, const void* k, const void* v,
     const bool timed = prof_take(&tc);
     hipError_t e;
     if (timed && (e = hipEventRecord(tc.e[0], stream)) != hipSuccess) return hip_fail(e);
-    e = hstu::launch_schedule(seq_offsets, num_seqs, heads, hstu::q_tile_rows(dt, d), wl, stream);
+    e = hstu::launch_schedule(seq_offsets, num_seqs, heads, hstu::q_tile_rows(dt, d), wl, stream,
+                              sort_choice_env());
     if (e != hipSuccess) return hip_fail(e);
     if (timed && (e = hipEventRecord(tc.e[1], stream)) != hipSuccess) return hip_fail(e);
     e = hstu::launch_attention(p, dt, wl, 0, stream);

@@ -104,9 +104,30 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int RSRC_WORD3 = 0x00020000;  // gfx9 raw buffer, 32-bit data format
 
+// s_waitcnt immediate that waits for at most n outstanding vector-memory
+// operations and does not wait on the other counters (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+#define VMCNT_LE(n) ((((n) & 15) | ((((n) >> 4) & 3) << 14)) | (7 << 4) | (15 << 8))
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
     const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int)bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, RSRC_WORD3);
+}
+
+// 16-byte load from a raw buffer straight into LDS: lane l's bytes land at
+// lds_base + 16*l (lds_base must be wave-uniform).  The builtin exists only
+// for the device; the host pass, which compiles kernel bodies into launch
+// stubs but never runs them, gets an empty body.
+__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, unsigned char* lds_base,
+                                              int voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef __attribute__((address_space(3))) void lds_void;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voffset, 0, 0, 0);
+#else
+    (void)r;
+    (void)lds_base;
+    (void)voffset;
+#endif
 }
 
 // LDS transposing read of four 16-bit values (gfx950 ds_read_b64_tr_b16).
@@ -118,25 +139,57 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 / fp16: one wave = QB blocks of 32 query rows; NW waves per workgroup.
-// K and V tiles are both stored row-major in LDS (row stride D + 8 elements).
-// The S^T = K Q^T product reads K rows with ds_read_b128; the O^T = V^T P^T
-// product reads V^T with two transposing reads per 16-key step: for lane l
-// (j = l % 16, half h = (l / 16) % 2, g = l / 32) the first read covers keys
-// 16u + 4g + (0..3) and the second 16u + 8 + 4g + (0..3), at head-dim column
-// 32*db + 16h + (l % 16), matching the keys S^T leaves in the lane.
+// bf16 / fp16 kernel.
+//
+// Shape: NW waves per workgroup, QB blocks of 32 query rows per wave, key/value
+// tiles of BK rows (NKB = BK/32 blocks of 32 keys).  Tiles live in LDS
+// unpadded, 16-byte chunks XOR-swizzled by row so that both read patterns are
+// free of bank conflicts (measured on gfx950):
+//   K (16-byte reads of 32 consecutive rows):      chunk ^ kswz(row)
+//   V (transposing 8-byte reads of 4-row groups):   chunk ^ vswz(row)
+// Tiles are copied straight from HBM into LDS (16-byte loads whose lanes land
+// at consecutive LDS addresses), two K buffers and three V buffers deep, so
+// tile c+2 streams in while tile c is consumed; one barrier per tile.
+//
+// A wave's item runs in three phases over the workgroup's tiles:
+//   A  tiles whose keys all precede the wave's rows: a software pipeline over
+//      32-key blocks, per block b the MFMAs of S(b+1) and of P(b) V are
+//      interleaved with the SiLU of S(b);
+//   B  tiles holding the wave's diagonal: plain order, scores above the
+//      diagonal zeroed before SiLU (silu(0) = 0);
+//   C  tiles past the wave's rows: staging and barriers only.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int NW, int QB, int BK>
 struct Tile16 {
-    static constexpr int ROWS_W = 32 * QB;          // query rows per wave
-    static constexpr int BQ = NW * ROWS_W;          // query rows per item
-    static constexpr int THREADS = NW * 64;
-    static constexpr int STR = D + 8;               // LDS row stride (elements)
-    static constexpr int TILE = BK * STR;           // elements per K or V tile
-    static constexpr int CHUNKS = BK * D / 8 / THREADS;  // 16-byte loads per thread per tensor
-    static_assert(CHUNKS * THREADS * 8 == BK * D, "tile must split evenly over the threads");
+    static constexpr int ROWS_W = 32 * QB;            // query rows per wave
+    static constexpr int BQ = NW * ROWS_W;            // query rows per item
+    static constexpr int NKB = BK / 32;               // 32-key blocks per tile
+    static constexpr int ROW_BYTES = D * 2;           // one K or V row in LDS
+    static constexpr int CHUNKS = ROW_BYTES / 16;     // 16-byte chunks per row
+    static constexpr int TILE_BYTES = BK * ROW_BYTES;
+    // The second product of a block's last 16 keys runs in the next block's
+    // body, one barrier later when tiles hold one block: V then needs a fourth
+    // buffer.
+    static constexpr int NBUF_K = 2, NBUF_V = NKB == 1 ? 4 : 3;
+    static constexpr int LDS_BYTES = (NBUF_K + NBUF_V) * TILE_BYTES;
+    static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;   // rows one wave load covers
+    static constexpr int LOADS = TILE_BYTES / 1024 / NW;     // loads per wave per tensor
+    static_assert(LOADS * NW * 1024 == TILE_BYTES, "tile must split into whole wave loads");
     static_assert(BK % 32 == 0 && D % 32 == 0, "tile shape");
 };
+
+// K: 16 lanes of a 16-byte read hit 16 consecutive rows at one chunk.
+template <int CHUNKS>
+__device__ __forceinline__ int kswz(int r) {
+    if constexpr (CHUNKS == 8) return (r >> 1) & 7;
+    else return (2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1)) & (CHUNKS - 1);
+}
+// V: a 16-lane transposing read hits 4 consecutive rows at two adjacent chunks.
+template <int CHUNKS>
+__device__ __forceinline__ int vswz(int r) {
+    if constexpr (CHUNKS == 8) return (2 * (r & 3) + ((r >> 2) & 1)) & 7;
+    else return (2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1)) & (CHUNKS - 1);
+}
 
 template <typename T, int D, int NW, int QB, int BK>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma16(KernelArgs a) {
@@ -146,13 +199,14 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma16(KernelArgs a) {
     using v4 = typename M::v4;
     constexpr int ROWS_W = Cfg::ROWS_W;
     constexpr int BQ = Cfg::BQ;
-    constexpr int STR = Cfg::STR;
-    constexpr int TILE = Cfg::TILE;
-    constexpr int NKB = BK / 32;   // 32-key blocks per tile
+    constexpr int NKB = Cfg::NKB;
+    constexpr int CH = Cfg::CHUNKS;
+    constexpr int RB = Cfg::ROW_BYTES;
+    constexpr int TB = Cfg::TILE_BYTES;
     constexpr int NKS = D / 16;    // k-steps of the first product
     constexpr int NDB = D / 32;    // 32-wide head-dim blocks of the output
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * TILE];  // [buffer][K, V]
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[Cfg::LDS_BYTES];
     __shared__ int s_item;
 
     const int tid = threadIdx.x;
@@ -162,30 +216,34 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma16(KernelArgs a) {
     const int l32 = lane & 31;
     const int H = a.heads;
     const int64_t row_stride = (int64_t)H * D;      // elements between consecutive tokens
-    const int row_bytes = (int)(row_stride * 2);
-    const int total = a.wl.ctl[CTL_TOTAL];
-    const int mode = a.wl.ctl[CTL_MODE];
+    const int row_bytes = (int)(row_stride * 2);    // bytes between consecutive tokens
 
-    // Lane-constant parts of the LDS addresses.
-    const int k_rd = l32 * STR + g * 8;                               // K operand
-    const int v_rd = (4 * g + ((lane & 15) >> 2)) * STR +             // V^T operand
-                     ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
-    // Staging: chunk i of this thread is row r_i, 8-element column c_i.
-    int st_goff[Cfg::CHUNKS], st_loff[Cfg::CHUNKS];
+    // Lane-constant parts of the addresses.
+    // K operand, key block kb, k-step ks: row 32kb + l32, logical chunk 2ks + g.
+    const int k_row = l32;
+    // V^T operand, 16-key step u, head-dim block db: two transposing reads at
+    // rows 16u + 4g + (lane%16)/4 (+8), byte column 2*(32db + 16h + 4(lane%4)).
+    const int v_row = 4 * g + ((lane & 15) >> 2);
+    const int v_colb = 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    // Tile loads: this wave's load i covers rows (wv + NW*i) * ROWS_PER_LOAD + ...
+    int ld_goff[Cfg::LOADS][2];   // [i][K, V] global byte offset inside the tile
 #pragma unroll
-    for (int i = 0; i < Cfg::CHUNKS; ++i) {
-        const int id = tid + i * Cfg::THREADS;
-        const int r = id / (D / 8), c8 = id % (D / 8);
-        st_goff[i] = r * row_bytes + c8 * 16;
-        st_loff[i] = r * STR + c8 * 8;
+    for (int i = 0; i < Cfg::LOADS; ++i) {
+        const int r = (wv + NW * i) * Cfg::ROWS_PER_LOAD + lane / CH;
+        const int pc = lane % CH;
+        ld_goff[i][0] = r * row_bytes + 16 * (pc ^ kswz<CH>(r));
+        ld_goff[i][1] = r * row_bytes + 16 * (pc ^ vswz<CH>(r));
     }
 
-    for (;;) {
-        if (tid == 0) s_item = atomicAdd(a.wl.ctl + CTL_NEXT, 1);
-        __syncthreads();
-        const int w = __builtin_amdgcn_readfirstlane(s_item);
-        if (w >= total) break;
-        const Item it = decode_item(a.wl, mode, a.num_seqs, H, w);
+    auto k_buf = [&](int c) -> const unsigned char* { return lds + (c & 1) * TB; };
+    auto v_buf = [&](int c) -> const unsigned char* {
+        return lds + Cfg::NBUF_K * TB + (c % Cfg::NBUF_V) * TB;
+    };
+
+    ItemSource src;
+    int qx, w;
+    while (src.next(a.wl, &s_item, &qx, &w)) {
+        const Item it = decode_item(a.wl, a.num_seqs, H, qx, w);
         const int seq = __builtin_amdgcn_readfirstlane(it.seq);
         const int head = __builtin_amdgcn_readfirstlane(it.head);
         const int qtile = __builtin_amdgcn_readfirstlane(it.qtile);
@@ -194,11 +252,31 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma16(KernelArgs a) {
         const int q0 = qtile * BQ;
         const int kv_end = min(s, q0 + BQ);
         const int n_tiles = (kv_end + BK - 1) / BK;
-        const int wr0 = q0 + wv * ROWS_W;   // this wave's first query row (local)
-        const bool wave_live = wr0 < s;
+        const int wr0 = q0 + wv * ROWS_W;                // this wave's first query row
+        const bool live = wr0 < s;
+        // Blocks of 32 keys that are entirely below the wave's first row, and
+        // the last block the wave needs.
+        const int full_blocks = live ? wr0 / 32 : 0;
+        const int last_block = live ? (min(wr0 + ROWS_W, s) - 1) / 32 : -1;
+        const int tiles_a = full_blocks / NKB;             // phase A tiles
+        const int tiles_ab = live ? last_block / NKB + 1 : 0;   // phases A and B
         const int64_t seq_base = (int64_t)start * row_stride + (int64_t)head * D;
 
-        // Q^T operand: query rows wr0 + 32*qb + l32, head-dim slice [16*ks + 8*g, +8).
+        auto issue_loads = [&](int c) {
+            const int k0 = c * BK;
+            const int64_t off = seq_base + (int64_t)k0 * row_stride;
+            const int64_t bytes = (int64_t)(s - k0) * row_bytes;
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + off, bytes);
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + off, bytes);
+#pragma unroll
+            for (int i = 0; i < Cfg::LOADS; ++i) {
+                const int dst = (wv + NW * i) * 1024;
+                load16_to_lds(rk, lds + (c & 1) * TB + dst, ld_goff[i][0]);
+                load16_to_lds(rv, lds + Cfg::NBUF_K * TB + (c % Cfg::NBUF_V) * TB + dst, ld_goff[i][1]);
+            }
+        };
+
+        // Q^T operand: query rows wr0 + 32*qb + l32, head-dim slice [16ks + 8g, +8).
         v8 qop[QB][NKS];
         {
             const __amdgpu_buffer_rsrc_t rq =
@@ -218,101 +296,164 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma16(KernelArgs a) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) o[db][qb] = (f32x16){};
 
-        u32x4 kreg[Cfg::CHUNKS], vreg[Cfg::CHUNKS];
-        auto load_tile = [&](int c) {
-            const int k0 = c * BK;
-            const int64_t off = seq_base + (int64_t)k0 * row_stride;
-            const int64_t bytes = (int64_t)(s - k0) * row_bytes;
-            const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + off, bytes);
-            const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + off, bytes);
+        // ---- building blocks ------------------------------------------------
+        // S^T for block b (keys 32b .. 32b+31) into st[qb].
+        auto qk = [&](int b, f32x16* st) {
+            const int c = b / NKB, kb = b % NKB;
+            const unsigned char* kl = k_buf(c);
+            const int r = kb * 32 + k_row;
 #pragma unroll
-            for (int i = 0; i < Cfg::CHUNKS; ++i) {
-                kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, st_goff[i], 0, 0);
-                vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, st_goff[i], 0, 0);
+            for (int qb = 0; qb < QB; ++qb) st[qb] = (f32x16){};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const v8 ka = *reinterpret_cast<const v8*>(kl + r * RB + 16 * ((2 * ks + g) ^ kswz<CH>(r)));
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) st[qb] = M::mma(ka, qop[qb][ks], st[qb]);
             }
         };
-        auto store_tile = [&](int buf) {
-            uint16_t* kl = lds + buf * 2 * TILE;
-            uint16_t* vl = kl + TILE;
+        // Weights for the 16-key step t of a block (registers 8t .. 8t+7).
+        auto weights = [&](const f32x16* st, int t, v8* pb) {
 #pragma unroll
-            for (int i = 0; i < Cfg::CHUNKS; ++i) {
-                *reinterpret_cast<u32x4*>(kl + st_loff[i]) = kreg[i];
-                *reinterpret_cast<u32x4*>(vl + st_loff[i]) = vreg[i];
+            for (int qb = 0; qb < QB; ++qb) {
+                f32x8 pf;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pf[e] = silu_scaled(st[qb][8 * t + e] * a.score_scale);
+                pb[qb] = __builtin_convertvector(pf, v8);
             }
         };
-
-        // One key/value tile, one 32-key block at a time: S^T for the block,
-        // the pointwise pass and the second product over the block's two
-        // 16-key steps.  On the tile that crosses the diagonal, scores with
-        // key > query are zeroed before the pointwise pass: silu(0) = 0, so
-        // they contribute exactly nothing (the mask multiplies after SiLU).
-        auto compute = [&](const uint16_t* kl, const uint16_t* vl, int k0, bool diag) {
+        // O^T += V^T P^T for the 16-key step t of block b.
+        auto pv = [&](int b, int t, const v8* pb) {
+            const int c = b / NKB, kb = b % NKB;
+            const unsigned char* vl = v_buf(c);
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                f32x16 st[QB];
+            for (int db = 0; db < NDB; ++db) {
+                const int r0 = kb * 32 + 16 * t + v_row;
+                const int cb = 64 * db + v_colb;          // byte column inside the row
+                const int c0 = cb >> 4, cw = cb & 15;
+                const i16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(
+                        vl + r0 * RB + 16 * (c0 ^ vswz<CH>(r0)) + cw));
+                const i16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(
+                        vl + (r0 + 8) * RB + 16 * (c0 ^ vswz<CH>(r0 + 8)) + cw));
+                const v8 va = __builtin_bit_cast(
+                        v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) st[qb] = (f32x16){};
+                for (int qb = 0; qb < QB; ++qb) o[db][qb] = M::mma(va, pb[qb], o[db][qb]);
+            }
+        };
+        // A block on or past the diagonal: keys above each query row are zeroed.
+        auto masked_block = [&](int b) {
+            f32x16 st[QB];
+            qk(b, st);
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const v8 ka = *reinterpret_cast<const v8*>(kl + k_rd + kb * 32 * STR + ks * 16);
+            for (int qb = 0; qb < QB; ++qb) {
+                // keep key 32b + 8(r/4) + 4g + r%4 <= query wr0 + 32qb + l32
+                const int lim = wr0 + 32 * qb + l32 - 32 * b - 4 * g;
 #pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) st[qb] = M::mma(ka, qop[qb][ks], st[qb]);
-                }
-                if (diag) {
+                for (int r = 0; r < 16; ++r)
+                    st[qb][r] = (8 * (r >> 2) + (r & 3) <= lim) ? st[qb][r] : 0.0f;
+            }
 #pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) {
-                        // keep key k0 + 32kb + 8(r/4) + 4g + r%4 <= query wr0 + 32qb + l32
-                        const int lim = wr0 - k0 + 32 * (qb - kb) + l32 - 4 * g;
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            st[qb][r] = (8 * (r >> 2) + (r & 3) <= lim) ? st[qb][r] : 0.0f;
-                    }
-                }
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int u = kb * 2 + t;
-                    v8 pb[QB];
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) {
-                        f32x8 pf;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            pf[e] = silu_scaled(st[qb][8 * t + e] * a.score_scale);
-                        pb[qb] = __builtin_convertvector(pf, v8);
-                    }
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        const uint16_t* vp = vl + v_rd + u * 16 * STR + db * 32;
-                        const i16x4 lo = lds_read_tr16(vp);
-                        const i16x4 hi = lds_read_tr16(vp + 8 * STR);
-                        const v8 va = __builtin_bit_cast(
-                                v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-                        for (int qb = 0; qb < QB; ++qb) o[db][qb] = M::mma(va, pb[qb], o[db][qb]);
-                    }
-                }
+            for (int t = 0; t < 2; ++t) {
+                v8 pb[QB];
+                weights(st, t, pb);
+                pv(b, t, pb);
             }
         };
 
-        load_tile(0);
-        store_tile(0);
+        // ---- prologue: tiles 0 and 1 in flight, wait for tile 0 --------------
+        issue_loads(0);
+        if (n_tiles > 1) issue_loads(1);
+        if (n_tiles > 1)
+            __builtin_amdgcn_s_waitcnt(VMCNT_LE(Cfg::LOADS * 2));
+        else
+            __builtin_amdgcn_s_waitcnt(VMCNT_LE(0));
         __syncthreads();
 
-        for (int c = 0; c < n_tiles; ++c) {
-            const bool more = c + 1 < n_tiles;
-            if (more) load_tile(c + 1);
-            const int k0 = c * BK;
-            if (wave_live && k0 <= wr0 + ROWS_W - 1) {
-                const uint16_t* kl = lds + (c & 1) * 2 * TILE;
-                compute(kl, kl + TILE, k0, k0 + BK - 1 > wr0);
-            }
-            if (more) store_tile((c + 1) & 1);
+        // One barrier per tile.  At barrier c every wave has finished its loads
+        // of tile c+1 and every read of K buffer c%2 and of the V buffer tile c+2
+        // goes to; then tile c+2 is issued into those two buffers.
+        auto tile_sync = [&](int c) {
+            __builtin_amdgcn_s_waitcnt(VMCNT_LE(0));
             __syncthreads();
+            if (c + 2 < n_tiles) issue_loads(c + 2);
+        };
+
+        // ---- phase A: pipelined full blocks -----------------------------------
+        // Body of block b: the matrix cores run S(b+1) and the second product of
+        // block b-1's last 16 keys while S(b)'s first half goes through SiLU, then
+        // the product of b's first 16 keys while the second half does.  Tile c's
+        // barrier comes right before the body of its last block, the first body
+        // that reads tile c+1 (its K).  Score and weight arrays alternate by
+        // block parity, so nothing is copied.
+        const int nA = tiles_a * NKB;
+        f32x16 sc[2][QB];
+        v8 pc[2][QB];   // weights of a block's last 16 keys, used one body later
+        auto body = [&](int b, f32x16* cur, f32x16* nxt, const v8* p_prev, v8* p_out) {
+            if (b % NKB == NKB - 1) tile_sync(b / NKB);
+            if (b + 1 < nA) qk(b + 1, nxt);
+            if (b > 0) pv(b - 1, 1, p_prev);
+            v8 p0[QB];
+            weights(cur, 0, p0);
+            pv(b, 0, p0);
+            weights(cur, 1, p_out);
+            // Interleave: 12 MFMAs (next scores, previous product) over the
+            // first SiLU half, 4 (this block's first product) over the second.
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // LDS reads
+#pragma unroll
+            for (int i = 0; i < 12; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);   // VALU
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 22, 0);
+            }
+        };
+        if (nA > 0) {
+            qk(0, sc[0]);
+            int b = 0;
+            for (; b + 1 < nA; b += 2) {
+                body(b, sc[0], sc[1], pc[1], pc[0]);
+                body(b + 1, sc[1], sc[0], pc[0], pc[1]);
+            }
+            if (b < nA) {
+                body(b, sc[0], sc[1], pc[1], pc[0]);
+                pv(b, 1, pc[0]);
+            } else {
+                pv(b - 1, 1, pc[1]);
+            }
         }
+        int c = tiles_a;
+        // ---- phase B: the tiles holding the wave's diagonal --------------------
+        // Plain order; the barrier comes after the tile's blocks, since the
+        // last one still reads this tile's K.
+        for (; c < tiles_ab; ++c) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const int b = c * NKB + kb;
+                if (b < full_blocks) {
+                    f32x16 st[QB];
+                    qk(b, st);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        v8 pb[QB];
+                        weights(st, t, pb);
+                        pv(b, t, pb);
+                    }
+                } else if (b <= last_block) {
+                    masked_block(b);
+                }
+            }
+            tile_sync(c);
+        }
+        // ---- phase C: staging only --------------------------------------------
+        for (; c < n_tiles; ++c) tile_sync(c);
 
         // Epilogue: lane holds query wr0 + 32*qb + l32 and head-dim rows
         // 32*db + 8*i + 4*g + (0..3).  Stores past the sequence are dropped.
-        if (wave_live) {
+        if (live) {
             const __amdgpu_buffer_rsrc_t ro =
                     make_rsrc(a.out + seq_base + (int64_t)wr0 * row_stride,
                               (int64_t)(s - wr0) * row_bytes);
@@ -377,15 +518,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
     const int l32 = lane & 31;
     const int H = a.heads;
     const int64_t row_stride = (int64_t)H * D;
-    const int total = a.wl.ctl[CTL_TOTAL];
-    const int mode = a.wl.ctl[CTL_MODE];
 
-    for (;;) {
-        if (tid == 0) s_item = atomicAdd(a.wl.ctl + CTL_NEXT, 1);
-        __syncthreads();
-        const int w = s_item;
-        if (w >= total) break;
-        const Item it = decode_item(a.wl, mode, a.num_seqs, H, w);
+    ItemSource src;
+    int qx, w;
+    while (src.next(a.wl, &s_item, &qx, &w)) {
+        const Item it = decode_item(a.wl, a.num_seqs, H, qx, w);
         const int start = a.offsets[it.seq];
         const int s = a.offsets[it.seq + 1] - start;
         const int q0 = it.qtile * BQ;
@@ -470,8 +607,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
 // Launch configuration per (element type, head size).
 // ---------------------------------------------------------------------------
 constexpr int NW16 = 4;
-constexpr int BK16 = 64;
 template <int D> struct QBlocks { static constexpr int value = D == 64 ? 2 : 1; };
+template <int D> struct KeyTile { static constexpr int value = D == 64 ? 64 : 32; };
 constexpr int NWF = 4;
 constexpr int BKF = 32;
 
@@ -517,7 +654,7 @@ hipError_t launch16(const FwdParams& p, WorkList wl, int grid, hipStream_t strea
     a.heads = p.heads;
     a.score_scale = -p.alpha * LOG2E;
     a.out_scale = -LN2 / p.n;
-    auto fn = attn_fwd_mfma16<T, D, NW16, QBlocks<D>::value, BK16>;
+    auto fn = attn_fwd_mfma16<T, D, NW16, QBlocks<D>::value, KeyTile<D>::value>;
     if (grid <= 0) {
         static int cached = 0;
         if (!cached) cached = resident_grid(fn, NW16 * 64);
@@ -554,8 +691,8 @@ hipError_t launch_f32(const FwdParams& p, WorkList wl, int grid, hipStream_t str
 
 int q_tile_rows(Dtype dt, int d) {
     if (dt == Dtype::FP32) return TileF32<64, NWF, BKF>::BQ;
-    return d == 64 ? Tile16<__bf16, 64, NW16, QBlocks<64>::value, BK16>::BQ
-                   : Tile16<__bf16, 128, NW16, QBlocks<128>::value, BK16>::BQ;
+    return d == 64 ? Tile16<__bf16, 64, NW16, QBlocks<64>::value, KeyTile<64>::value>::BQ
+                   : Tile16<__bf16, 128, NW16, QBlocks<128>::value, KeyTile<128>::value>::BQ;
 }
 
 hipError_t launch_attention(const FwdParams& p, Dtype dt, WorkList wl, int grid,

@@ -7,51 +7,78 @@
 
 namespace hstu {
 
+// Work items are (sequence, head, Q tile) triples, split over NQ queues (one
+// per XCD of an MI355X; a workgroup starts with the queue of the XCD it runs
+// on, so the items sharing one sequence's keys and values run under one L2).
+constexpr int NQ = 8;
+constexpr int CTL_LINE = 32;  // ints per queue counter: one 128-byte line each
+
 // Words at the start of the scratch area (int32).
 enum : int {
-    CTL_NEXT = 0,   // next work item to hand out (device atomic)
-    CTL_TOTAL = 1,  // number of work items
-    CTL_FLAGS = 2,  // bit 0: off[0] != 0, bit 1: a decreasing offset, bit 2: item count overflow
-    CTL_MODE = 3,   // MODE_BANDS or MODE_SEQS
-    CTL_WORDS = 16
+    CTL_NEXT = 0,                 // NEXT + CTL_LINE*x: next item of queue x (device atomic)
+    CTL_TOTAL = NQ * CTL_LINE,    // TOTAL + x: items in queue x
+    CTL_FLAGS = CTL_TOTAL + NQ,   // bit 0: off[0] != 0, bit 1: a decreasing offset,
+                                  // bit 2: item count overflow
+    CTL_MODE = CTL_FLAGS + 1,     // QUEUE_BANDS or QUEUE_PAIRS
+    CTL_WORDS = CTL_TOTAL + 2 * NQ
 };
 
-// How work items are numbered.
-//  MODE_BANDS: sequences are sorted by Q-tile count, longest first.  Items go in
-//    order of decreasing Q-tile index j (the cost of an item is j + 1 key/value
-//    tiles), so the heaviest items are handed out first.  Sorted rank m and the
-//    next rank's count bound a "band" of levels in which exactly m + 1
-//    sequences take part; prefix[m] is the first item of band m.
-//  MODE_SEQS: sequences in input order, Q tiles of each from last to first;
-//    prefix[i] is the first item of sequence i.  Used when there are more
-//    sequences than the one-workgroup sort takes.
-enum : int { MODE_BANDS = 0, MODE_SEQS = 1 };
+// QUEUE_BANDS: ranks sorted, items level by level (below).  QUEUE_PAIRS: input
+// order (more sequences than the sort takes), items pair by pair, each pair's
+// Q tiles from last to first; qprefix then holds each pair's first item.
+enum : int { QUEUE_BANDS = 0, QUEUE_PAIRS = 1 };
+
+// The scheduler ranks sequences by Q-tile count, largest first (or keeps input
+// order above SORT_MAX sequences).  Pairs p = rank * heads + head are dealt to
+// the queues in snake order: round i = p / NQ goes to queues 0..NQ-1 when i is
+// even and NQ-1..0 when odd, so heavy pairs spread evenly.  Inside a queue,
+// whose pairs are then in non-increasing tile count, items go level by level
+// from the last Q tile down: the level-j items of every pair with more than j
+// tiles, pair by pair.  "Band" b of a queue holds the levels in which exactly
+// its first b + 1 pairs take part; qprefix holds each band's first item.
 constexpr int SORT_MAX = 16384;
 
-struct WorkList {
-    int* ctl;     // CTL_WORDS
-    int* order;   // [num_seqs]      sequence id at each schedule rank
-    int* ntile;   // [num_seqs + 1]  Q-tile count at each rank, then 0
-    int* prefix;  // [num_seqs + 1]  first item of each band / sequence, then the total
-};
-
-inline size_t worklist_bytes(int num_seqs) {
-    size_t n = (size_t)num_seqs;
-    return sizeof(int) * (CTL_WORDS + n + 2 * (n + 1)) + 256;
+// Pair dealt to position i of queue x.
+__host__ __device__ inline int queue_pair(int i, int x) {
+    return i * NQ + ((i & 1) ? NQ - 1 - x : x);
 }
 
-inline WorkList worklist_carve(void* base, int num_seqs) {
+struct WorkList {
+    int* ctl;      // CTL_WORDS
+    int* order;    // [num_seqs]      sequence id at each rank
+    int* ntile;    // [num_seqs]      Q-tile count at each rank
+    int* qprefix;  // [NQ * (qlen + 1)] first item of each band of a queue, then the total
+    int qlen;      // max pairs per queue = ceil(num_seqs * heads / NQ)
+};
+
+inline int queue_len(int num_seqs, int heads) {
+    const long long pairs = (long long)num_seqs * heads;
+    return (int)((pairs + NQ - 1) / NQ);
+}
+
+inline size_t worklist_bytes(int num_seqs, int heads) {
+    const size_t qlen = (size_t)queue_len(num_seqs, heads);
+    return sizeof(int) * (CTL_WORDS + 2 * (size_t)num_seqs + NQ * (qlen + 1)) + 256;
+}
+
+inline WorkList worklist_carve(void* base, int num_seqs, int heads) {
     int* p = static_cast<int*>(base);
     WorkList wl;
     wl.ctl = p;
     wl.order = p + CTL_WORDS;
     wl.ntile = wl.order + num_seqs;
-    wl.prefix = wl.ntile + num_seqs + 1;
+    wl.qprefix = wl.ntile + num_seqs;
+    wl.qlen = queue_len(num_seqs, heads);
     return wl;
 }
 
+// How the scheduler ranks sequences.  AUTO: counting sort on tile counts
+// (bitonic sort if a count is too large for its histogram; input order above
+// SORT_MAX sequences).  The other two force one path, for tests.
+enum class SortChoice : int { AUTO = 0, BITONIC = 1, INPUT_ORDER = 2 };
+
 hipError_t launch_schedule(const int32_t* offsets, int num_seqs, int heads, int q_tile_rows,
-                           WorkList wl, hipStream_t stream);
+                           WorkList wl, hipStream_t stream, SortChoice choice);
 
 enum class Dtype : int { BF16 = 0, FP16 = 1, FP32 = 2 };
 

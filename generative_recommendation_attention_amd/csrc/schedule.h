@@ -1,13 +1,14 @@
-// Device-side decoding of a work-item number into (sequence, head, Q tile).
+// Device-side work distribution: queue selection, item fetch and decoding of
+// an item number into (sequence, head, Q tile).
 //
 // The Ascend HSTU blog ("都是生成式推荐，为什么昇腾这么快？", §3.2) classifies
 // each (Q block, K block) pair as all-ones, lower-triangular or all-zero and
 // skips the all-zero ones; §4.2 computes only the real tokens of a jagged
-// batch.  Here a work item is one Q tile of one (sequence, head); the tile
-// pairs above the diagonal are never enumerated, and a Q tile exists only for
-// real tokens.  The HSTU paper translation (§3.2) views the ragged attention
-// as a grouped GEMM of differently sized problems; items are ordered longest
-// first so that a pool of persistent workgroups ends with short ones.
+// batch.  Here a work item is one Q tile of one (sequence, head); tile pairs
+// above the diagonal are never enumerated, and Q tiles exist only for real
+// tokens.  The HSTU paper translation (§3.2) views the ragged attention as a
+// grouped GEMM of differently sized problems; sequences are ranked longest
+// first so the pool of persistent workgroups ends on short items.
 #pragma once
 
 #include "internal.h"
@@ -39,26 +40,73 @@ __device__ inline int wave_search(const int* __restrict__ a, int n, int w) {
     return lo;
 }
 
-__device__ inline Item decode_item(const WorkList& wl, int mode, int num_seqs, int heads, int w) {
-    Item it;
-    const int m = wave_search(wl.prefix, num_seqs, w);
-    const int local = w - wl.prefix[m];
-    if (mode == MODE_BANDS) {
-        // Band m: levels ntile[m+1] .. ntile[m]-1, ranks 0..m take part.
-        const int per_level = (m + 1) * heads;
-        const int lvl = local / per_level;
-        const int rem = local - lvl * per_level;
-        const int rank = rem / heads;
-        it.head = rem - rank * heads;
-        it.qtile = wl.ntile[m] - 1 - lvl;
+// The XCD this wave runs on (hardware register XCC_ID, bits 3:0).
+__device__ inline int current_xcd() {
+    return (int)(__builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & 15u);
+}
+
+// Pairs in queue x when there are `pairs` (rank, head) pairs in total: every
+// full round gives each queue one pair; the last, partial round gives its
+// first pairs % NQ positions (which queues those are depends on the round's
+// direction).
+__device__ inline int queue_pairs(int pairs, int x) {
+    const int full = pairs / NQ, rem = pairs % NQ;
+    const int pos = (full & 1) ? NQ - 1 - x : x;  // x's position in the last round
+    return full + (pos < rem ? 1 : 0);
+}
+
+// Item w of queue x.
+__device__ inline Item decode_item(const WorkList& wl, int num_seqs, int heads, int x, int w) {
+    const int pairs = num_seqs * heads;
+    const int* pre = wl.qprefix + x * (wl.qlen + 1);
+    const int b = wave_search(pre, queue_pairs(pairs, x), w);   // band (or pair)
+    const int local = w - pre[b];
+    if (wl.ctl[CTL_MODE] == QUEUE_PAIRS) {
+        const int p = queue_pair(b, x);
+        const int rank = p / heads;
+        Item it;
+        it.head = p - rank * heads;
+        it.qtile = wl.ntile[rank] - 1 - local;
         it.seq = wl.order[rank];
-    } else {
-        const int lvl = local / heads;
-        it.head = local - lvl * heads;
-        it.qtile = wl.ntile[m] - 1 - lvl;
-        it.seq = m;
+        return it;
     }
+    const int per_level = b + 1;                                 // pairs taking part
+    const int lvl = local / per_level;
+    const int i = local - lvl * per_level;                       // pair position in queue
+    const int p = queue_pair(i, x);
+    const int rank = p / heads;
+    const int top = wl.ntile[queue_pair(b, x) / heads];          // tiles of the band's last pair
+    Item it;
+    it.head = p - rank * heads;
+    it.qtile = top - 1 - lvl;
+    it.seq = wl.order[rank];
     return it;
 }
+
+// Hands out items to a workgroup: its own XCD's queue first, then the others
+// in turn once that one is empty.  Thread 0 takes the item with an atomic and
+// shares it through LDS; the caller must call next() from every thread.
+struct ItemSource {
+    int queue;   // queue currently being drained
+    int tried;   // queues already found empty
+    __device__ ItemSource() : queue(current_xcd() % NQ), tried(0) {}
+
+    // Returns false when every queue is empty.  On true, *x and *w name the item.
+    __device__ bool next(const WorkList& wl, int* slot, int* x, int* w) {
+        for (;;) {
+            if (threadIdx.x == 0) slot[0] = atomicAdd(wl.ctl + CTL_NEXT + CTL_LINE * queue, 1);
+            __syncthreads();
+            const int got = __builtin_amdgcn_readfirstlane(slot[0]);
+            __syncthreads();
+            if (got < wl.ctl[CTL_TOTAL + queue]) {
+                *x = queue;
+                *w = got;
+                return true;
+            }
+            if (++tried >= NQ) return false;
+            queue = (queue + 1) % NQ;
+        }
+    }
+};
 
 }  // namespace hstu

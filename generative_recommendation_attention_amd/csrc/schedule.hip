@@ -1,11 +1,12 @@
-// Work-list build: one workgroup turns the jagged offsets into the numbering
-// of work items that the attention kernel decodes (see schedule.h).
+// Work-list build: one workgroup turns the jagged offsets into the queues the
+// attention kernel drains (see schedule.h and internal.h).
 //
-// Bands mode (num_seqs <= SORT_MAX): Q-tile counts are sorted in LDS (bitonic,
-// descending, ties by sequence id) and the band prefix is a scan of
-//   (ntile[m] - ntile[m+1]) * (m + 1) * heads.
-// Sequences mode: identity order, prefix = scan of ntile[i] * heads.
-// The kernel also resets the item counter, so a forward call needs no memset.
+// 1. Rank the sequences by Q-tile count, largest first: a counting sort (LDS
+//    histogram + scatter) when the largest count fits the histogram, else an
+//    LDS bitonic sort; above SORT_MAX sequences, input order.
+// 2. Deal the (rank, head) pairs to the NQ queues in snake order and scan,
+//    per queue, the item count of each band into qprefix.
+// 3. Reset every queue's item counter, so a forward call needs no memset.
 #include "internal.h"
 
 namespace hstu {
@@ -13,36 +14,59 @@ namespace hstu {
 namespace {
 
 constexpr int SCHED_THREADS = 1024;
+constexpr int SCHED_WAVES = SCHED_THREADS / 64;
+constexpr int HIST_MAX = 8192;  // tile-count values the counting sort handles
 
-// Inclusive scan of one value per thread across the workgroup (64-bit).
-__device__ long long block_inclusive_scan(long long x, long long* buf) {
-    const int tid = threadIdx.x;
-    buf[tid] = x;
-    __syncthreads();
-    for (int off = 1; off < SCHED_THREADS; off <<= 1) {
-        long long y = (tid >= off) ? buf[tid - off] : 0;
-        __syncthreads();
-        buf[tid] += y;
-        __syncthreads();
+enum : int { RANK_COUNTING = 0, RANK_BITONIC = 1, RANK_INPUT = 2 };
+
+struct SchedShared {
+    long long wave_sum[SCHED_WAVES][NQ];
+    long long carry[NQ];
+    int flags;
+    int max_tiles;
+};
+
+// Inclusive scan over threads of one value per thread, segmented by
+// thread % seg (seg = 1: a plain scan; seg = NQ: one scan per queue, since the
+// thread index and the pair index agree mod NQ).  Returns the thread's
+// inclusive prefix within its segment.  Callers separate two calls with a
+// barrier.
+__device__ long long segmented_scan(long long v, int seg, SchedShared& sh) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int off = seg; off < 64; off <<= 1) {
+        const long long y = __shfl_up(v, off, 64);
+        if (lane >= off) v += y;
     }
-    long long r = buf[tid];
+    // The wave's last `seg` lanes hold its per-segment totals.
+    if (lane >= 64 - seg) sh.wave_sum[wave][lane % seg] = v;
     __syncthreads();
-    return r;
+    if (tid < seg) {
+        long long run = 0;
+        for (int w = 0; w < SCHED_WAVES; ++w) {
+            const long long t = sh.wave_sum[w][tid];
+            sh.wave_sum[w][tid] = run;
+            run += t;
+        }
+    }
+    __syncthreads();
+    return v + sh.wave_sum[wave][lane % seg];
 }
 
 __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
         const int32_t* __restrict__ off, int num_seqs, int heads, int bq, WorkList wl,
-        int mode) {
-    extern __shared__ unsigned long long keys[];  // bands mode only
-    __shared__ long long scan_buf[SCHED_THREADS];
-    __shared__ int s_flags;
+        int force_kind) {
+    extern __shared__ unsigned long long dyn[];
+    __shared__ SchedShared sh;
     const int tid = threadIdx.x;
-    if (tid == 0) s_flags = 0;
+    if (tid < NQ) sh.carry[tid] = 0;
+    if (tid == 0) {
+        sh.flags = 0;
+        sh.max_tiles = 0;
+    }
     __syncthreads();
 
     int flags = 0;
     if (tid == 0 && num_seqs > 0 && off[0] != 0) flags |= 1;
-
     auto tiles_of = [&](int i) -> int {
         long long s = (long long)off[i + 1] - (long long)off[i];
         if (s < 0) {
@@ -52,7 +76,46 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
         return (int)((s + bq - 1) / bq);
     };
 
-    if (mode == MODE_BANDS) {
+    // ---- 1. ranking -------------------------------------------------------
+    int my_max = 0;
+    for (int i = tid; i < num_seqs; i += SCHED_THREADS) my_max = max(my_max, tiles_of(i));
+    atomicMax(&sh.max_tiles, my_max);
+    __syncthreads();
+    const int maxT = sh.max_tiles;
+    int kind = force_kind;
+    if (kind == RANK_COUNTING && maxT >= HIST_MAX) kind = RANK_BITONIC;
+    if (num_seqs > SORT_MAX) kind = RANK_INPUT;
+
+    // LDS layout: counting = hist[HIST_MAX] | cursor[HIST_MAX] | sorted[SORT_MAX] (ints);
+    //             bitonic  = keys[pow2 >= num_seqs] (u64).
+    int* hist = reinterpret_cast<int*>(dyn);
+    int* cursor = hist + HIST_MAX;
+    int* sorted = cursor + HIST_MAX;
+    unsigned long long* keys = dyn;
+
+    if (kind == RANK_COUNTING) {
+        for (int v = tid; v <= maxT; v += SCHED_THREADS) hist[v] = 0;
+        __syncthreads();
+        for (int i = tid; i < num_seqs; i += SCHED_THREADS) atomicAdd(&hist[tiles_of(i)], 1);
+        __syncthreads();
+        // cursor[v] = number of sequences with more than v tiles (scan over v descending).
+        for (int base = 0; base <= maxT; base += SCHED_THREADS) {
+            const int v = maxT - (base + tid);
+            const long long h = (v >= 0) ? hist[v] : 0;
+            const long long inc = segmented_scan(h, 1, sh);
+            if (v >= 0) cursor[v] = (int)(sh.carry[0] + inc - h);
+            __syncthreads();
+            if (tid == SCHED_THREADS - 1) sh.carry[0] += inc;
+            __syncthreads();
+        }
+        for (int i = tid; i < num_seqs; i += SCHED_THREADS) {
+            const int t = tiles_of(i);
+            const int pos = atomicAdd(&cursor[t], 1);
+            wl.order[pos] = i;
+            wl.ntile[pos] = t;
+            sorted[pos] = t;
+        }
+    } else if (kind == RANK_BITONIC) {
         int P = 1;
         while (P < num_seqs) P <<= 1;
         for (int i = tid; i < P; i += SCHED_THREADS) {
@@ -63,7 +126,6 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
             keys[i] = key;
         }
         __syncthreads();
-        // Bitonic sort, descending overall.
         for (int kk = 2; kk <= P; kk <<= 1) {
             for (int j = kk >> 1; j > 0; j >>= 1) {
                 for (int i = tid; i < P; i += SCHED_THREADS) {
@@ -90,67 +152,97 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
             wl.ntile[i] = tiles_of(i);
         }
     }
-    if (tid == 0) wl.ntile[num_seqs] = 0;
+    __syncthreads();
+    if (tid < NQ) sh.carry[tid] = 0;
+    __syncthreads();
+    auto tiles_at_rank = [&](int m) -> int {
+        if (kind == RANK_COUNTING) return sorted[m];
+        if (kind == RANK_BITONIC) return (int)(keys[m] >> 32);
+        return tiles_of(m);
+    };
 
-    // Exclusive scan of the per-rank item counts, in chunks of SCHED_THREADS.
-    long long carry = 0;
-    for (int base = 0; base < num_seqs; base += SCHED_THREADS) {
-        const int m = base + tid;
+    // ---- 2. per-queue band prefix --------------------------------------------
+    // Thread t of a chunk takes queue x = t % NQ, position i = (base + t) / NQ.
+    // Band i of queue x spans levels [tiles of position i+1, tiles of position i)
+    // with i + 1 pairs, so its item count is (t_i - t_{i+1}) * (i + 1).
+    const int pairs = num_seqs * heads;
+    const int row = wl.qlen + 1;
+    const int full = pairs / NQ, rem = pairs % NQ;
+    auto position_exists = [&](int i, int x) {
+        if (i < full) return true;
+        if (i > full) return false;
+        const int pos = (full & 1) ? NQ - 1 - x : x;
+        return pos < rem;
+    };
+    for (int base = 0; base < pairs + NQ; base += SCHED_THREADS) {
+        const int x = tid % NQ;
+        const int i = (base + tid) / NQ;
         long long term = 0;
-        if (m < num_seqs) {
-            if (mode == MODE_BANDS) {
-                const long long nm = (long long)(keys[m] >> 32);
-                const long long nn = (m + 1 < num_seqs) ? (long long)(keys[m + 1] >> 32) : 0;
-                term = (nm - nn) * (long long)(m + 1) * heads;
-            } else {
-                term = (long long)tiles_of(m) * heads;
-            }
+        const bool here = position_exists(i, x);
+        if (here) {
+            const long long ti = tiles_at_rank(queue_pair(i, x) / heads);
+            const long long tn = position_exists(i + 1, x) ? tiles_at_rank(queue_pair(i + 1, x) / heads) : 0;
+            term = (kind == RANK_INPUT) ? ti : (ti - tn) * (long long)(i + 1);
         }
-        const long long inc = block_inclusive_scan(term, scan_buf);
-        const long long exc = carry + inc - term;
-        if (m < num_seqs) wl.prefix[m] = (int)min(exc, (long long)0x7fffffff);
-        // The last thread's inclusive value is the chunk total.
-        if (tid == SCHED_THREADS - 1) scan_buf[0] = inc;
+        const long long inc = segmented_scan(term, NQ, sh);
+        const long long exc = sh.carry[x] + inc - term;
+        if (here) wl.qprefix[x * row + i] = (int)min(exc, (long long)0x7fffffff);
         __syncthreads();
-        carry += scan_buf[0];
+        // The last NQ threads hold each queue's chunk total.
+        if (tid >= SCHED_THREADS - NQ) sh.carry[x] += inc;
         __syncthreads();
     }
-    if (carry > 0x7fffffffLL) {
-        flags |= 4;
-        carry = 0;  // refuse to run rather than wrap
+
+    // ---- 3. totals and counters --------------------------------------------
+    if (tid < NQ) {
+        long long total = sh.carry[tid];
+        if (total > 0x7fffffffLL) {
+            flags |= 4;
+            total = 0;  // refuse to run rather than wrap
+        }
+        const int pos = (full & 1) ? NQ - 1 - tid : tid;
+        const int n = full + (pos < rem ? 1 : 0);
+        wl.qprefix[tid * row + n] = (int)total;
+        wl.ctl[CTL_NEXT + CTL_LINE * tid] = 0;
+        wl.ctl[CTL_TOTAL + tid] = (int)total;
     }
-    if (flags) atomicOr(&s_flags, flags);
+    if (flags) atomicOr(&sh.flags, flags);
     __syncthreads();
     if (tid == 0) {
-        wl.prefix[num_seqs] = (int)carry;
-        wl.ctl[CTL_NEXT] = 0;
-        wl.ctl[CTL_TOTAL] = (int)carry;
-        wl.ctl[CTL_FLAGS] = s_flags;
-        wl.ctl[CTL_MODE] = mode;
+        wl.ctl[CTL_FLAGS] = sh.flags;
+        wl.ctl[CTL_MODE] = (kind == RANK_INPUT) ? QUEUE_PAIRS : QUEUE_BANDS;
     }
 }
 
 }  // namespace
 
 hipError_t launch_schedule(const int32_t* offsets, int num_seqs, int heads, int q_tile_rows,
-                           WorkList wl, hipStream_t stream) {
-    const int mode = (num_seqs <= SORT_MAX) ? MODE_BANDS : MODE_SEQS;
+                           WorkList wl, hipStream_t stream, SortChoice choice) {
+    int kind = RANK_COUNTING;
+    if (choice == SortChoice::BITONIC) kind = RANK_BITONIC;
+    if (choice == SortChoice::INPUT_ORDER) kind = RANK_INPUT;
+    constexpr size_t counting_lds = sizeof(int) * (2 * (size_t)HIST_MAX + SORT_MAX);
+    constexpr size_t bitonic_lds = sizeof(unsigned long long) * SORT_MAX;
+    constexpr size_t max_lds = counting_lds > bitonic_lds ? counting_lds : bitonic_lds;
     size_t lds = 0;
-    if (mode == MODE_BANDS) {
+    if (num_seqs <= SORT_MAX && kind != RANK_INPUT) {
         int P = 1;
         while (P < num_seqs) P <<= 1;
-        lds = sizeof(unsigned long long) * (size_t)P;
+        const size_t need_bitonic = sizeof(unsigned long long) * (size_t)P;
+        const size_t need_counting = sizeof(int) * (2 * (size_t)HIST_MAX + (size_t)num_seqs);
+        // The device decides between counting and bitonic ranking, so provide both.
+        lds = need_bitonic > need_counting ? need_bitonic : need_counting;
     }
     static bool attr_done = false;
     if (!attr_done) {
         hipError_t e = hipFuncSetAttribute((const void*)schedule_kernel,
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)(sizeof(unsigned long long) * SORT_MAX));
+                                           (int)max_lds);
         if (e != hipSuccess) return e;
         attr_done = true;
     }
     hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(SCHED_THREADS), lds, stream, offsets,
-                       num_seqs, heads, q_tile_rows, wl, mode);
+                       num_seqs, heads, q_tile_rows, wl, kind);
     return hipGetLastError();
 }
 

@@ -208,6 +208,22 @@ def test_more_sequences_than_the_sort_takes():
     assert_close(g, ref, "bf16", "20000 sequences")
 
 
+@pytest.mark.parametrize("sort", ["bitonic", "input"])
+def test_scheduler_ranking_paths_agree(sort, monkeypatch):
+    """Every ranking path of the scheduler (counting sort, bitonic sort, input
+    order) must give bit-identical output: an item's result never depends on
+    which workgroup runs it or when."""
+    rng = np.random.default_rng(23)
+    lengths = [int(x) for x in rng.integers(0, 700, size=300)]
+    case = workloads.make_case(lengths, 2, 64, "bf16", seed=24, n=700.0)
+    q, k, v, off = device_case(case)
+    ref = hstu.hstu_attn_fwd(q, k, v, off, case.alpha, case.n)
+    monkeypatch.setenv("HSTU_SCHED_SORT", sort)
+    got = hstu.hstu_attn_fwd(q, k, v, off, case.alpha, case.n)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
 def test_profiling_counts_calls():
     case = workloads.make_case([512, 512], 2, 64, "bf16", seed=19, n=512.0)
     q, k, v, off = device_case(case)
