@@ -167,10 +167,7 @@ struct Tile16 {
     static constexpr int ROW_BYTES = D * 2;           // one K or V row in LDS
     static constexpr int CHUNKS = ROW_BYTES / 16;     // 16-byte chunks per row
     static constexpr int TILE_BYTES = BK * ROW_BYTES;
-    // The second product of a block's last 16 keys runs in the next block's
-    // body, one barrier later when tiles hold one block: V then needs a fourth
-    // buffer.
-    static constexpr int NBUF_K = 2, NBUF_V = NKB == 1 ? 4 : 3;
+    static constexpr int NBUF_K = 2, NBUF_V = 3;
     static constexpr int LDS_BYTES = (NBUF_K + NBUF_V) * TILE_BYTES;
     static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;   // rows one wave load covers
     static constexpr int LOADS = TILE_BYTES / 1024 / NW;     // loads per wave per tensor
@@ -379,51 +376,29 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma16(KernelArgs a) {
         };
 
         // ---- phase A: pipelined full blocks -----------------------------------
-        // Body of block b: the matrix cores run S(b+1) and the second product of
-        // block b-1's last 16 keys while S(b)'s first half goes through SiLU, then
-        // the product of b's first 16 keys while the second half does.  Tile c's
-        // barrier comes right before the body of its last block, the first body
-        // that reads tile c+1 (its K).  Score and weight arrays alternate by
-        // block parity, so nothing is copied.
+        // Body of block b: S(b+1) on the matrix cores while S(b) goes through
+        // SiLU, then P(b) V.  Tile c's barrier comes right before the body of its
+        // last block, the first body that reads tile c+1 (its K).  Two score
+        // arrays alternate by block parity, so nothing is copied.
         const int nA = tiles_a * NKB;
         f32x16 sc[2][QB];
-        v8 pc[2][QB];   // weights of a block's last 16 keys, used one body later
-        auto body = [&](int b, f32x16* cur, f32x16* nxt, const v8* p_prev, v8* p_out) {
+        auto body = [&](int b, f32x16* cur, f32x16* nxt) {
             if (b % NKB == NKB - 1) tile_sync(b / NKB);
             if (b + 1 < nA) qk(b + 1, nxt);
-            if (b > 0) pv(b - 1, 1, p_prev);
-            v8 p0[QB];
+            v8 p0[QB], p1[QB];
             weights(cur, 0, p0);
             pv(b, 0, p0);
-            weights(cur, 1, p_out);
-            // Interleave: 12 MFMAs (next scores, previous product) over the
-            // first SiLU half, 4 (this block's first product) over the second.
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // LDS reads
-#pragma unroll
-            for (int i = 0; i < 12; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);   // VALU
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 22, 0);
-            }
+            weights(cur, 1, p1);
+            pv(b, 1, p1);
         };
         if (nA > 0) {
             qk(0, sc[0]);
             int b = 0;
             for (; b + 1 < nA; b += 2) {
-                body(b, sc[0], sc[1], pc[1], pc[0]);
-                body(b + 1, sc[1], sc[0], pc[0], pc[1]);
+                body(b, sc[0], sc[1]);
+                body(b + 1, sc[1], sc[0]);
             }
-            if (b < nA) {
-                body(b, sc[0], sc[1], pc[1], pc[0]);
-                pv(b, 1, pc[0]);
-            } else {
-                pv(b - 1, 1, pc[1]);
-            }
+            if (b < nA) body(b, sc[0], sc[1]);
         }
         int c = tiles_a;
         // ---- phase B: the tiles holding the wave's diagonal --------------------
