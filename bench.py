@@ -31,10 +31,32 @@ import workloads  # noqa: E402
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
 PEAK_HBM_GBS = 8000.0
 METRIC = "HSTU attn fwd useful TFLOP/s, % bf16 MFMA peak; ms at QKV(16,4,4096,64)"
-# HBM bytes per dispatch of the attention kernel, from rocprofv3 --pmc
-# FETCH_SIZE and WRITE_SIZE (KiB), scaled by the copy-kernel calibration.
-# None until counters have been collected for the current kernel.
-TRAFFIC_BYTES = {}
+# HBM traffic per dispatch of the attention kernel, from two rocprofv3 --pmc
+# runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
+# same counter reads for a plain 1 GiB device copy (bench.py --copy-calibrate):
+# FETCH_SIZE reads 0.5 GiB for that copy's 1 GiB of reads, WRITE_SIZE 1 GiB.
+# The figures hold for the kernel source with the SHA-256 below; for any other
+# source the bench reports traffic as null.
+TRAFFIC = {
+    "kernel_source": "generative_recommendation_attention_amd/csrc/attn_fwd.hip",
+    "kernel_sha256": "dfcea0bd2a979172a9ddd7f80920138f4526546e7b433c85d7d3273d19947a66",
+    "fetch_scale": 2.0,
+    "write_scale": 1.0,
+    "fetch_kib": {2: 89665.2},
+    "write_kib": {2: 32928.2},
+}
+
+
+def traffic_bytes(workload: int):
+    import hashlib
+    path = os.path.join(ROOT, TRAFFIC["kernel_source"])
+    with open(path, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if sha != TRAFFIC["kernel_sha256"] or workload not in TRAFFIC["fetch_kib"]:
+        return None
+    kib = (TRAFFIC["fetch_kib"][workload] * TRAFFIC["fetch_scale"] +
+           TRAFFIC["write_kib"][workload] * TRAFFIC["write_scale"])
+    return round(kib * 1024.0)
 
 
 def to_device(case):
@@ -141,7 +163,7 @@ def main() -> int:
     sched_ms = kt.sched_ms / max(1, kt.calls)
     achieved = flops / (attn_ms * 1e-3) / 1e12
     peak = PEAK_MFMA_TFLOPS[case.dtype]
-    traffic = TRAFFIC_BYTES.get(args.workload)
+    traffic = traffic_bytes(args.workload)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel": "attn_fwd_mfma16" if case.dtype != "fp32" else "attn_fwd_mfma_f32",

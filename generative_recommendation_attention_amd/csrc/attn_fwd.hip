@@ -189,7 +189,7 @@ __device__ __forceinline__ int vswz(int r) {
 }
 
 template <typename T, int D, int NW, int QB, int BK>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_mfma16(KernelArgs a) {
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
     using Cfg = Tile16<T, D, NW, QB, BK>;
     using M = Mfma<T>;
     using v8 = typename M::v8;
