@@ -114,6 +114,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, RSRC_WORD3);
 }
 
+// Same, for a byte count already known to fit in 32 bits (no 64-bit compares).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc32(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, max(bytes, 0),
+                                             RSRC_WORD3);
+}
+
 // 16-byte load from a raw buffer straight into LDS: lane l's bytes land at
 // lds_base + 16*l (lds_base must be wave-uniform).  The builtin exists only
 // for the device; the host pass, which compiles kernel bodies into launch
@@ -148,8 +154,13 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
 //   K (16-byte reads of 32 consecutive rows):      chunk ^ kswz(row)
 //   V (transposing 8-byte reads of 4-row groups):   chunk ^ vswz(row)
 // Tiles are copied straight from HBM into LDS (16-byte loads whose lanes land
-// at consecutive LDS addresses), two K buffers and three V buffers deep, so
-// tile c+2 streams in while tile c is consumed; one barrier per tile.
+// at consecutive LDS addresses) into NSLOT = PF+1 slots (a K and a V buffer
+// each; tile c uses slot c % NSLOT), so tiles c+1 .. c+PF stream in while
+// tile c is consumed; one barrier per tile.  Every operand read is a
+// lane-constant VGPR plus an immediate offset: the swizzles depend only on
+// row bits that 32-key blocks and 16-key steps leave unchanged, and the main
+// loop is unrolled over whole slot rotations so that slot, block and step
+// offsets are compile-time constants.
 //
 // A wave's item runs in three phases over the workgroup's tiles:
 //   A  tiles whose keys all precede the wave's rows: a software pipeline over
@@ -159,7 +170,7 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
 //      diagonal zeroed before SiLU (silu(0) = 0);
 //   C  tiles past the wave's rows: staging and barriers only.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int NW, int QB, int BK>
+template <typename T, int D, int NW, int QB, int BK, int PF>
 struct Tile16 {
     static constexpr int ROWS_W = 32 * QB;            // query rows per wave
     static constexpr int BQ = NW * ROWS_W;            // query rows per item
@@ -167,12 +178,14 @@ struct Tile16 {
     static constexpr int ROW_BYTES = D * 2;           // one K or V row in LDS
     static constexpr int CHUNKS = ROW_BYTES / 16;     // 16-byte chunks per row
     static constexpr int TILE_BYTES = BK * ROW_BYTES;
-    static constexpr int NBUF_K = 2, NBUF_V = 3;
-    static constexpr int LDS_BYTES = (NBUF_K + NBUF_V) * TILE_BYTES;
+    static constexpr int NSLOT = PF + 1;                 // tiles in flight: PF
+    static constexpr int LDS_BYTES = 2 * NSLOT * TILE_BYTES;
     static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;   // rows one wave load covers
     static constexpr int LOADS = TILE_BYTES / 1024 / NW;     // loads per wave per tensor
     static_assert(LOADS * NW * 1024 == TILE_BYTES, "tile must split into whole wave loads");
     static_assert(BK % 32 == 0 && D % 32 == 0, "tile shape");
+    static_assert(PF >= 2 && (PF - 1) * 2 * LOADS <= 63, "prefetch depth");
+    static_assert(LDS_BYTES <= 65536, "LDS reads use 16-bit immediate offsets");
 };
 
 // K: 16 lanes of a 16-byte read hit 16 consecutive rows at one chunk.
@@ -188,9 +201,9 @@ __device__ __forceinline__ int vswz(int r) {
     else return (2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1)) & (CHUNKS - 1);
 }
 
-template <typename T, int D, int NW, int QB, int BK>
+template <typename T, int D, int NW, int QB, int BK, int PF>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
-    using Cfg = Tile16<T, D, NW, QB, BK>;
+    using Cfg = Tile16<T, D, NW, QB, BK, PF>;
     using M = Mfma<T>;
     using v8 = typename M::v8;
     using v4 = typename M::v4;
@@ -204,7 +217,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
     constexpr int NDB = D / 32;    // 32-wide head-dim blocks of the output
 
     __shared__ __attribute__((aligned(1024))) unsigned char lds[Cfg::LDS_BYTES];
-    __shared__ int s_item;
+    __shared__ int s_item[NQ];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -232,20 +245,29 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
         ld_goff[i][1] = r * row_bytes + 16 * (pc ^ vswz<CH>(r));
     }
 
-    auto k_buf = [&](int c) -> const unsigned char* { return lds + (c & 1) * TB; };
-    auto v_buf = [&](int c) -> const unsigned char* {
-        return lds + Cfg::NBUF_K * TB + (c % Cfg::NBUF_V) * TB;
-    };
+    // Operand offsets inside a slot.  K row 32kb + l32 has the swizzle of row
+    // l32, and V rows 32kb + 16t + v_row (+8) those of rows v_row (+8), so
+    // the block and step only add multiples of 32 and 16 rows.
+    int k_off[NKS], v_lo[NDB], v_hi[NDB];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) k_off[ks] = k_row * RB + 16 * ((2 * ks + g) ^ kswz<CH>(k_row));
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        const int cb = 64 * db + v_colb;          // byte column inside the row
+        v_lo[db] = v_row * RB + 16 * ((cb >> 4) ^ vswz<CH>(v_row)) + (cb & 15);
+        v_hi[db] = (v_row + 8) * RB + 16 * ((cb >> 4) ^ vswz<CH>(v_row + 8)) + (cb & 15);
+    }
+    constexpr int NS = Cfg::NSLOT;
 
     ItemSource src;
     int qx, w;
-    while (src.next(a.wl, &s_item, &qx, &w)) {
+    while (src.next(a.wl, s_item, &qx, &w)) {
         const Item it = decode_item(a.wl, a.num_seqs, H, qx, w);
         const int seq = __builtin_amdgcn_readfirstlane(it.seq);
         const int head = __builtin_amdgcn_readfirstlane(it.head);
         const int qtile = __builtin_amdgcn_readfirstlane(it.qtile);
-        const int start = a.offsets[seq];
-        const int s = a.offsets[seq + 1] - start;
+        const int start = __builtin_amdgcn_readfirstlane(a.offsets[seq]);
+        const int s = __builtin_amdgcn_readfirstlane(a.offsets[seq + 1]) - start;
         const int q0 = qtile * BQ;
         const int kv_end = min(s, q0 + BQ);
         const int n_tiles = (kv_end + BK - 1) / BK;
@@ -259,17 +281,27 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
         const int tiles_ab = live ? last_block / NKB + 1 : 0;   // phases A and B
         const int64_t seq_base = (int64_t)start * row_stride + (int64_t)head * D;
 
+        // Tile c into slot c % NS.  The buffer range covers the tile's rows
+        // that exist (none past the sequence).
         auto issue_loads = [&](int c) {
             const int k0 = c * BK;
             const int64_t off = seq_base + (int64_t)k0 * row_stride;
-            const int64_t bytes = (int64_t)(s - k0) * row_bytes;
-            const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + off, bytes);
-            const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + off, bytes);
+            // (clamped below by make_rsrc32; min then max, not a clamp, which
+            // would become a vector-only instruction and a non-scalar resource)
+            const int bytes = min(s - k0, BK) * row_bytes;
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc32(a.k + off, bytes);
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc32(a.v + off, bytes);
+            // Computed at run time from an opaque copy of c: with the slot
+            // known at compile time the compiler keeps one destination per slot
+            // and load in scalar registers, which the kernel does not have.
+            int cs = c;
+            asm volatile("" : "+s"(cs));
+            const int slot = cs % NS;
 #pragma unroll
             for (int i = 0; i < Cfg::LOADS; ++i) {
                 const int dst = (wv + NW * i) * 1024;
-                load16_to_lds(rk, lds + (c & 1) * TB + dst, ld_goff[i][0]);
-                load16_to_lds(rv, lds + Cfg::NBUF_K * TB + (c % Cfg::NBUF_V) * TB + dst, ld_goff[i][1]);
+                load16_to_lds(rk, lds + slot * TB + dst, ld_goff[i][0]);
+                load16_to_lds(rv, lds + (NS + slot) * TB + dst, ld_goff[i][1]);
             }
         };
 
@@ -294,16 +326,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
             for (int qb = 0; qb < QB; ++qb) o[db][qb] = (f32x16){};
 
         // ---- building blocks ------------------------------------------------
-        // S^T for block b (keys 32b .. 32b+31) into st[qb].
-        auto qk = [&](int b, f32x16* st) {
-            const int c = b / NKB, kb = b % NKB;
-            const unsigned char* kl = k_buf(c);
-            const int r = kb * 32 + k_row;
+        // S^T for key block kb of the tile in `slot` into st[qb].
+        auto qk = [&](int slot, int kb, f32x16* st) {
+            const unsigned char* kl = lds + slot * TB + kb * 32 * RB;
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) st[qb] = (f32x16){};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                const v8 ka = *reinterpret_cast<const v8*>(kl + r * RB + 16 * ((2 * ks + g) ^ kswz<CH>(r)));
+                const v8 ka = *reinterpret_cast<const v8*>(kl + k_off[ks]);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) st[qb] = M::mma(ka, qop[qb][ks], st[qb]);
             }
@@ -318,29 +348,39 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
                 pb[qb] = __builtin_convertvector(pf, v8);
             }
         };
-        // O^T += V^T P^T for the 16-key step t of block b.
-        auto pv = [&](int b, int t, const v8* pb) {
-            const int c = b / NKB, kb = b % NKB;
-            const unsigned char* vl = v_buf(c);
+        // O^T += V^T P^T for the 16-key step t of key block kb in `slot`.
+        auto pv = [&](int slot, int kb, int t, const v8* pb) {
+            const unsigned char* vl = lds + (NS + slot) * TB + (kb * 32 + 16 * t) * RB;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const int r0 = kb * 32 + 16 * t + v_row;
-                const int cb = 64 * db + v_colb;          // byte column inside the row
-                const int c0 = cb >> 4, cw = cb & 15;
-                const i16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(
-                        vl + r0 * RB + 16 * (c0 ^ vswz<CH>(r0)) + cw));
-                const i16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(
-                        vl + (r0 + 8) * RB + 16 * (c0 ^ vswz<CH>(r0 + 8)) + cw));
+                const i16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(vl + v_lo[db]));
+                const i16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(vl + v_hi[db]));
                 const v8 va = __builtin_bit_cast(
                         v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) o[db][qb] = M::mma(va, pb[qb], o[db][qb]);
             }
         };
-        // A block on or past the diagonal: keys above each query row are zeroed.
-        auto masked_block = [&](int b) {
+        // Operand reads and the second product, for the pipelined body.
+        auto kread = [&](int slot, int kb, int ks) -> v8 {
+            return *reinterpret_cast<const v8*>(lds + slot * TB + kb * 32 * RB + k_off[ks]);
+        };
+        auto vread = [&](int slot, int kb, int t, int db) -> v8 {
+            const unsigned char* vl = lds + (NS + slot) * TB + (kb * 32 + 16 * t) * RB;
+            const i16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(vl + v_lo[db]));
+            const i16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(vl + v_hi[db]));
+            return __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        auto mma_pv = [&](const v8* va, const v8* pb) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) o[db][qb] = M::mma(va[db], pb[qb], o[db][qb]);
+        };
+        // Block b on or past the diagonal: keys above each query row are zeroed.
+        auto masked_block = [&](int slot, int kb, int b) {
             f32x16 st[QB];
-            qk(b, st);
+            qk(slot, kb, st);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 // keep key 32b + 8(r/4) + 4g + r%4 <= query wr0 + 32qb + l32
@@ -353,78 +393,136 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
             for (int t = 0; t < 2; ++t) {
                 v8 pb[QB];
                 weights(st, t, pb);
-                pv(b, t, pb);
+                pv(slot, kb, t, pb);
             }
         };
 
-        // ---- prologue: tiles 0 and 1 in flight, wait for tile 0 --------------
-        issue_loads(0);
-        if (n_tiles > 1) issue_loads(1);
-        if (n_tiles > 1)
-            __builtin_amdgcn_s_waitcnt(VMCNT_LE(Cfg::LOADS * 2));
-        else
-            __builtin_amdgcn_s_waitcnt(VMCNT_LE(0));
+        // ---- prologue: tiles 0 .. PF-1 in flight, wait for tile 0 -------------
+        // Tiles are always issued PF ahead, also past the sequence (their buffer
+        // range is empty, so they read nothing), which keeps the number of loads
+        // in flight after tile c+1 fixed: a wait on the load counter then
+        // covers exactly the tiles up to c+1.  Loads return in issue order.
+#pragma unroll
+        for (int c = 0; c < PF; ++c) issue_loads(c);
+        __builtin_amdgcn_s_waitcnt(VMCNT_LE((PF - 1) * 2 * Cfg::LOADS));
         __syncthreads();
 
         // One barrier per tile.  At barrier c every wave has finished its loads
-        // of tile c+1 and every read of K buffer c%2 and of the V buffer tile c+2
-        // goes to; then tile c+2 is issued into those two buffers.
+        // of tile c+1 and every read of tile c-1 (slot (c+PF) % NS); then tile
+        // c+PF is issued into that slot.
         auto tile_sync = [&](int c) {
-            __builtin_amdgcn_s_waitcnt(VMCNT_LE(0));
+            __builtin_amdgcn_s_waitcnt(VMCNT_LE((PF - 2) * 2 * Cfg::LOADS));
             __syncthreads();
-            if (c + 2 < n_tiles) issue_loads(c + 2);
+            issue_loads(c + PF);
         };
 
         // ---- phase A: pipelined full blocks -----------------------------------
-        // Body of block b: S(b+1) on the matrix cores while S(b) goes through
-        // SiLU, then P(b) V.  Tile c's barrier comes right before the body of its
-        // last block, the first body that reads tile c+1 (its K).  Two score
-        // arrays alternate by block parity, so nothing is copied.
-        const int nA = tiles_a * NKB;
+        // Body of block b: the SiLU of S(b) on the vector ALUs while the matrix
+        // cores run S(b+1) and P(b) V.  All operands of the body are read from
+        // LDS first; the SiLU of the first 16 keys overlaps the products of the
+        // previous block's last 16 keys and the first half of S(b+1), the SiLU
+        // of the last 16 keys overlaps P V of the first 16 and the second half
+        // of S(b+1); the product of the last 16 keys waits for the next body (so
+        // no product has to wait for the SiLU right before it).  Tile c's
+        // barrier comes right before the body of its last block, the first body
+        // that reads tile c+1 (its K).  Two score arrays alternate by block
+        // parity, so nothing is copied.  The main loop
+        // runs GT tiles per trip (whole slot rotations, an even number of
+        // blocks), so every slot, block and parity is a constant in the unrolled
+        // code; the remaining tiles take the same body with computed slots.  The
+        // last body also computes S of the first block past phase A, which
+        // phase B computes again with its mask (that tile is loaded: it holds
+        // the wave's diagonal).
+        constexpr int GT = (NS * NKB) % 2 == 0 ? NS : 2 * NS;
         f32x16 sc[2][QB];
-        auto body = [&](int b, f32x16* cur, f32x16* nxt) {
-            if (b % NKB == NKB - 1) tile_sync(b / NKB);
-            if (b + 1 < nA) qk(b + 1, nxt);
+        v8 p1d[QB], v1d[NDB];   // deferred: weights and V^T of the last block's keys 16..31
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) p1d[qb] = (v8){};
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) v1d[db] = (v8){};
+        auto body = [&](int slot, int kb, int next_slot, int next_kb, bool sync, int c,
+                        f32x16* cur, f32x16* nxt) {
+            if (sync) tile_sync(c);
+            v8 ka[NKS], va0[NDB], va1[NDB];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) ka[ks] = kread(next_slot, next_kb, ks);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                va0[db] = vread(slot, kb, 0, db);
+                va1[db] = vread(slot, kb, 1, db);
+            }
             v8 p0[QB], p1[QB];
             weights(cur, 0, p0);
-            pv(b, 0, p0);
+            mma_pv(v1d, p1d);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) nxt[qb] = (f32x16){};
+#pragma unroll
+            for (int ks = 0; ks < NKS / 2; ++ks)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) nxt[qb] = M::mma(ka[ks], qop[qb][ks], nxt[qb]);
             weights(cur, 1, p1);
-            pv(b, 1, p1);
+            mma_pv(va0, p0);
+#pragma unroll
+            for (int ks = NKS / 2; ks < NKS; ++ks)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) nxt[qb] = M::mma(ka[ks], qop[qb][ks], nxt[qb]);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) p1d[qb] = p1[qb];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) v1d[db] = va1[db];
         };
-        if (nA > 0) {
-            qk(0, sc[0]);
-            int b = 0;
-            for (; b + 1 < nA; b += 2) {
-                body(b, sc[0], sc[1]);
-                body(b + 1, sc[1], sc[0]);
+        if (tiles_a > 0) {
+            qk(0, 0, sc[0]);
+            const int groups = tiles_a / GT;
+            for (int gi = 0; gi < groups; ++gi) {
+#pragma unroll
+                for (int j = 0; j < GT; ++j)
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb) {
+                        const int par = (j * NKB + kb) & 1;
+                        const bool last = kb == NKB - 1;
+                        body(j % NS, kb, last ? (j + 1) % NS : j % NS, last ? 0 : kb + 1, last,
+                             gi * GT + j, sc[par], sc[par ^ 1]);
+                    }
             }
-            if (b < nA) body(b, sc[0], sc[1]);
+            const int nA = tiles_a * NKB;
+            auto body_at = [&](int b, f32x16* cur, f32x16* nxt) {
+                const int c = b / NKB, kb = b % NKB, bn = b + 1;
+                body(c % NS, kb, (bn / NKB) % NS, bn % NKB, kb == NKB - 1, c, cur, nxt);
+            };
+            for (int b = groups * GT * NKB; b < nA; b += 2) {
+                body_at(b, sc[0], sc[1]);
+                if (b + 1 < nA) body_at(b + 1, sc[1], sc[0]);
+            }
+            mma_pv(v1d, p1d);   // the last block's keys 16..31
         }
         int c = tiles_a;
         // ---- phase B: the tiles holding the wave's diagonal --------------------
         // Plain order; the barrier comes after the tile's blocks, since the
         // last one still reads this tile's K.
         for (; c < tiles_ab; ++c) {
+            const int slot = c % NS;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 const int b = c * NKB + kb;
                 if (b < full_blocks) {
                     f32x16 st[QB];
-                    qk(b, st);
+                    qk(slot, kb, st);
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
                         v8 pb[QB];
                         weights(st, t, pb);
-                        pv(b, t, pb);
+                        pv(slot, kb, t, pb);
                     }
                 } else if (b <= last_block) {
-                    masked_block(b);
+                    masked_block(slot, kb, b);
                 }
             }
             tile_sync(c);
         }
         // ---- phase C: staging only --------------------------------------------
         for (; c < n_tiles; ++c) tile_sync(c);
+        __builtin_amdgcn_s_waitcnt(VMCNT_LE(0));   // nothing left landing in LDS
 
         // Epilogue: lane holds query wr0 + 32*qb + l32 and head-dim rows
         // 32*db + 8*i + 4*g + (0..3).  Stores past the sequence are dropped.
@@ -484,7 +582,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
     constexpr int BQ = Cfg::BQ;
     __shared__ __attribute__((aligned(16))) float kl[BK * Cfg::KSTR];
     __shared__ __attribute__((aligned(16))) float vl[BK * Cfg::VSTR];
-    __shared__ int s_item;
+    __shared__ int s_item[NQ];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -496,7 +594,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
 
     ItemSource src;
     int qx, w;
-    while (src.next(a.wl, &s_item, &qx, &w)) {
+    while (src.next(a.wl, s_item, &qx, &w)) {
         const Item it = decode_item(a.wl, a.num_seqs, H, qx, w);
         const int start = a.offsets[it.seq];
         const int s = a.offsets[it.seq + 1] - start;
@@ -584,6 +682,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
 constexpr int NW16 = 4;
 template <int D> struct QBlocks { static constexpr int value = D == 64 ? 2 : 1; };
 template <int D> struct KeyTile { static constexpr int value = D == 64 ? 64 : 32; };
+template <int D> struct Prefetch { static constexpr int value = 2; };
 constexpr int NWF = 4;
 constexpr int BKF = 32;
 
@@ -629,7 +728,7 @@ hipError_t launch16(const FwdParams& p, WorkList wl, int grid, hipStream_t strea
     a.heads = p.heads;
     a.score_scale = -p.alpha * LOG2E;
     a.out_scale = -LN2 / p.n;
-    auto fn = attn_fwd_mfma16<T, D, NW16, QBlocks<D>::value, KeyTile<D>::value>;
+    auto fn = attn_fwd_mfma16<T, D, NW16, QBlocks<D>::value, KeyTile<D>::value, Prefetch<D>::value>;
     if (grid <= 0) {
         static int cached = 0;
         if (!cached) cached = resident_grid(fn, NW16 * 64);
@@ -666,8 +765,10 @@ hipError_t launch_f32(const FwdParams& p, WorkList wl, int grid, hipStream_t str
 
 int q_tile_rows(Dtype dt, int d) {
     if (dt == Dtype::FP32) return TileF32<64, NWF, BKF>::BQ;
-    return d == 64 ? Tile16<__bf16, 64, NW16, QBlocks<64>::value, KeyTile<64>::value>::BQ
-                   : Tile16<__bf16, 128, NW16, QBlocks<128>::value, KeyTile<128>::value>::BQ;
+    return d == 64 ? Tile16<__bf16, 64, NW16, QBlocks<64>::value, KeyTile<64>::value,
+                            Prefetch<64>::value>::BQ
+                   : Tile16<__bf16, 128, NW16, QBlocks<128>::value, KeyTile<128>::value,
+                            Prefetch<128>::value>::BQ;
 }
 
 hipError_t launch_attention(const FwdParams& p, Dtype dt, WorkList wl, int grid,

@@ -83,13 +83,16 @@ __device__ inline Item decode_item(const WorkList& wl, int num_seqs, int heads, 
     return it;
 }
 
-// Hands out items to a workgroup: its own XCD's queue first, then the others
-// in turn once that one is empty.  Thread 0 takes the item with an atomic and
-// shares it through LDS; the caller must call next() from every thread.
+// Hands out items to a workgroup: its own XCD's queue first, then, once that
+// one is empty, the queue with the most items left.  Thread 0 takes an item
+// with an atomic and shares it through LDS; when the queue it drew from is
+// found empty, threads 0..NQ-1 read every queue's counter at once (one round
+// trip instead of one atomic per queue), so a workgroup that runs out of work
+// learns it in two round trips.  The caller passes NQ ints of LDS and calls
+// next() from every thread.
 struct ItemSource {
     int queue;   // queue currently being drained
-    int tried;   // queues already found empty
-    __device__ ItemSource() : queue(current_xcd() % NQ), tried(0) {}
+    __device__ ItemSource() : queue(current_xcd() % NQ) {}
 
     // Returns false when every queue is empty.  On true, *x and *w name the item.
     __device__ bool next(const WorkList& wl, int* slot, int* x, int* w) {
@@ -103,8 +106,26 @@ struct ItemSource {
                 *w = got;
                 return true;
             }
-            if (++tried >= NQ) return false;
-            queue = (queue + 1) % NQ;
+            if (threadIdx.x < NQ) {
+                const int q = threadIdx.x;
+                const int taken = __hip_atomic_load(wl.ctl + CTL_NEXT + CTL_LINE * q,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                slot[q] = wl.ctl[CTL_TOTAL + q] - taken;
+            }
+            __syncthreads();
+            int best = -1, most = 0;
+#pragma unroll
+            for (int i = 1; i <= NQ; ++i) {
+                const int q = (queue + i) % NQ;
+                const int left = slot[q];
+                if (left > most) {
+                    most = left;
+                    best = q;
+                }
+            }
+            __syncthreads();
+            if (best < 0) return false;
+            queue = __builtin_amdgcn_readfirstlane(best);
         }
     }
 };
