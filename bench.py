@@ -39,11 +39,11 @@ METRIC = "HSTU attn fwd useful TFLOP/s, % bf16 MFMA peak; ms at QKV(16,4,4096,64
 # source the bench reports traffic as null.
 TRAFFIC = {
     "kernel_source": "generative_recommendation_attention_amd/csrc/attn_fwd.hip",
-    "kernel_sha256": "dfcea0bd2a979172a9ddd7f80920138f4526546e7b433c85d7d3273d19947a66",
+    "kernel_sha256": "b76c73e8076a973570c75d4d3690ec7488b368447def24c3d98246ea556056dd",
     "fetch_scale": 2.0,
     "write_scale": 1.0,
-    "fetch_kib": {2: 89665.2},
-    "write_kib": {2: 32928.2},
+    "fetch_kib": {2: 108617.5},
+    "write_kib": {2: 37939.0},
 }
 
 
