@@ -28,6 +28,8 @@ hstu_status_t hip_fail(hipError_t e) {
 struct Scratch {
     void* ptr = nullptr;
     size_t bytes = 0;
+    unsigned epoch = 0;   // calls completed on this area; call e uses counter set e % 2
+    bool clean = false;   // counter set epoch % 2 is known to be zero
 };
 
 std::mutex g_scratch_mu;
@@ -35,7 +37,8 @@ std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
 
 // Returns a scratch area of at least `bytes` for (device, stream).  Growing an
 // area first waits for the stream, so no kernel still reads the old one.
-hstu_status_t scratch_for(int dev, hipStream_t stream, size_t bytes, void** out) {
+// A new area's contents are undefined (clean = false).
+hstu_status_t scratch_for(int dev, hipStream_t stream, size_t bytes, Scratch** out) {
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     Scratch& s = g_scratch[std::make_pair(dev, stream)];
     if (s.bytes < bytes) {
@@ -58,8 +61,10 @@ hstu_status_t scratch_for(int dev, hipStream_t stream, size_t bytes, void** out)
         }
         s.ptr = p;
         s.bytes = want;
+        s.epoch = 0;
+        s.clean = false;
     }
-    *out = s.ptr;
+    *out = &s;
     return HSTU_OK;
 }
 
@@ -87,8 +92,12 @@ hstu_status_t check_device(int* dev_out) {
 
 // ---- kernel timing ----------------------------------------------------------
 
+// Start and stop events of the work-list kernel (e[0], e[1], recorded only when
+// it runs) and of the attention kernel (e[2], e[3]).  They are attached to the
+// kernel dispatches themselves, so timing adds no packets to the stream.
 struct TimedCall {
-    hipEvent_t e[3];
+    hipEvent_t e[4];
+    bool sched = false;
 };
 
 std::mutex g_prof_mu;
@@ -110,7 +119,7 @@ bool prof_take(TimedCall* tc) {
         g_prof_free.pop_back();
         return true;
     }
-    for (int i = 0; i < 3; ++i) {
+    for (int i = 0; i < 4; ++i) {
         if (hipEventCreate(&tc->e[i]) != hipSuccess) {
             for (int j = 0; j < i; ++j) (void)hipEventDestroy(tc->e[j]);
             g_prof_total.dropped++;
@@ -175,10 +184,24 @@ hstu_status_t hstu_attn_fwd(const void* q, const void* k, const void* v,
     if (st != HSTU_OK) return st;
 
     const hstu::Dtype dt = static_cast<hstu::Dtype>(dtype);
-    void* ws = nullptr;
-    st = scratch_for(dev, stream, hstu::worklist_bytes(num_seqs, heads), &ws);
+    Scratch* sc = nullptr;
+    st = scratch_for(dev, stream, hstu::worklist_bytes(num_seqs, heads), &sc);
     if (st != HSTU_OK) return st;
-    const hstu::WorkList wl = hstu::worklist_carve(ws, num_seqs, heads);
+    hstu::WorkList wl = hstu::worklist_carve(sc->ptr, num_seqs, heads);
+    // Small batches build their queue tables inside the attention kernel.  The
+    // work-list kernel still runs when this call's counter set is not known to
+    // be zero (a new scratch area, or a failed launch before; it zeroes both
+    // sets) and when a test forces one of its ranking paths.
+    const hstu::SortChoice sort = sort_choice_env();
+    bool clean;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        wl.set = (int)(sc->epoch & 1u);
+        clean = sc->clean;
+        sc->clean = false;   // until this call's launches succeed
+    }
+    wl.fused = clean && sort == hstu::SortChoice::AUTO && num_seqs <= hstu::FUSE_SEQS &&
+               (long long)num_seqs * heads <= hstu::FUSE_PAIRS;
 
     hstu::FwdParams p;
     p.q = q;
@@ -194,18 +217,25 @@ hstu_status_t hstu_attn_fwd(const void* q, const void* k, const void* v,
 
     TimedCall tc;
     const bool timed = prof_take(&tc);
+    tc.sched = false;
     hipError_t e;
-    if (timed && (e = hipEventRecord(tc.e[0], stream)) != hipSuccess) return hip_fail(e);
-    e = hstu::launch_schedule(seq_offsets, num_seqs, heads, hstu::q_tile_rows(dt, d), wl, stream,
-                              sort_choice_env());
-    if (e != hipSuccess) return hip_fail(e);
-    if (timed && (e = hipEventRecord(tc.e[1], stream)) != hipSuccess) return hip_fail(e);
-    e = hstu::launch_attention(p, dt, wl, 0, stream);
-    if (e != hipSuccess) return hip_fail(e);
-    if (timed) {
-        if ((e = hipEventRecord(tc.e[2], stream)) != hipSuccess) return hip_fail(e);
-        prof_commit(tc);
+    if (!wl.fused) {
+        e = hstu::launch_schedule(seq_offsets, num_seqs, heads, hstu::q_tile_rows(dt, d), wl,
+                                  stream, sort, timed ? tc.e[0] : nullptr,
+                                  timed ? tc.e[1] : nullptr);
+        if (e != hipSuccess) return hip_fail(e);
+        tc.sched = timed;
     }
+    e = hstu::launch_attention(p, dt, wl, 0, stream, timed ? tc.e[2] : nullptr,
+                               timed ? tc.e[3] : nullptr);
+    if (e != hipSuccess) return hip_fail(e);
+    {
+        // The attention launch clears the other counter set for the next call.
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        sc->epoch++;
+        sc->clean = true;
+    }
+    if (timed) prof_commit(tc);
     if (validate_env()) {
         int ctl[hstu::CTL_WORDS];
         e = hipMemcpyAsync(ctl, wl.ctl, sizeof ctl, hipMemcpyDeviceToHost, stream);
@@ -295,11 +325,11 @@ hstu_status_t hstu_profile_read(hstu_kernel_times_t* out, int reset) {
     if (!out) return HSTU_ERR_INVALID_ARG;
     std::lock_guard<std::mutex> lock(g_prof_mu);
     for (const TimedCall& tc : g_prof_pending) {
-        hipError_t e = hipEventSynchronize(tc.e[2]);
+        hipError_t e = hipEventSynchronize(tc.e[3]);
         if (e != hipSuccess) return hip_fail(e);
         float a = 0.f, b = 0.f;
-        e = hipEventElapsedTime(&a, tc.e[0], tc.e[1]);
-        if (e == hipSuccess) e = hipEventElapsedTime(&b, tc.e[1], tc.e[2]);
+        e = tc.sched ? hipEventElapsedTime(&a, tc.e[0], tc.e[1]) : hipSuccess;
+        if (e == hipSuccess) e = hipEventElapsedTime(&b, tc.e[2], tc.e[3]);
         if (e != hipSuccess) return hip_fail(e);
         g_prof_total.calls++;
         g_prof_total.sched_ms += a;

@@ -31,6 +31,7 @@
 // 1/(1 + 2^m).  The kernel forms p = m * rcp(1 + exp2(m)) (one multiply, two
 // transcendental instructions, one add, one multiply per score) and applies
 // -ln(2)/n to the accumulated output once, in the epilogue.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -201,7 +202,7 @@ __device__ __forceinline__ int vswz(int r) {
     else return (2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1)) & (CHUNKS - 1);
 }
 
-template <typename T, int D, int NW, int QB, int BK, int PF>
+template <typename T, int D, int NW, int QB, int BK, int PF, bool FUSED>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
     using Cfg = Tile16<T, D, NW, QB, BK, PF>;
     using M = Mfma<T>;
@@ -218,6 +219,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
 
     __shared__ __attribute__((aligned(1024))) unsigned char lds[Cfg::LDS_BYTES];
     __shared__ int s_item[NQ];
+    __shared__ LocalTables lt;
+    static_assert(NW * 64 >= FUSE_SEQS && NW * 64 >= 32 * NQ, "fused tables need a thread per sequence");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -259,10 +262,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
     }
     constexpr int NS = Cfg::NSLOT;
 
-    ItemSource src;
+    // The tile slots are free until the first item: a fused launch builds its
+    // queue tables there and in lt.
+    // (Two instantiations, so the compiler knows which memory the tables are
+    // in and reads them with LDS or global instructions, not flat ones.)
+    Tables tb;
+    if constexpr (FUSED)
+        tb = build_local_tables(lt, reinterpret_cast<int*>(lds), a.offsets, a.num_seqs, H, BQ,
+                                a.wl.ctl);
+    else
+        tb = global_tables(a.wl);
+    clear_next_set(a.wl.ctl, a.wl.set);
+    ItemSource src(a.wl.ctl, a.wl.set);
     int qx, w;
-    while (src.next(a.wl, s_item, &qx, &w)) {
-        const Item it = decode_item(a.wl, a.num_seqs, H, qx, w);
+    while (src.next(tb, s_item, &qx, &w)) {
+        const Item it = decode_item(tb, a.num_seqs, H, qx, w);
         const int seq = __builtin_amdgcn_readfirstlane(it.seq);
         const int head = __builtin_amdgcn_readfirstlane(it.head);
         const int qtile = __builtin_amdgcn_readfirstlane(it.qtile);
@@ -576,13 +590,15 @@ struct KernelArgsF32 {
     float out_scale;
 };
 
-template <int D, int NW, int BK>
+template <int D, int NW, int BK, bool FUSED>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
     using Cfg = TileF32<D, NW, BK>;
     constexpr int BQ = Cfg::BQ;
     __shared__ __attribute__((aligned(16))) float kl[BK * Cfg::KSTR];
     __shared__ __attribute__((aligned(16))) float vl[BK * Cfg::VSTR];
     __shared__ int s_item[NQ];
+    __shared__ LocalTables lt;
+    static_assert(NW * 64 >= FUSE_SEQS && NW * 64 >= 32 * NQ, "fused tables need a thread per sequence");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -592,10 +608,17 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
     const int H = a.heads;
     const int64_t row_stride = (int64_t)H * D;
 
-    ItemSource src;
+    Tables tb;
+    if constexpr (FUSED)
+        tb = build_local_tables(lt, reinterpret_cast<int*>(kl), a.offsets, a.num_seqs, H, BQ,
+                                a.wl.ctl);
+    else
+        tb = global_tables(a.wl);
+    clear_next_set(a.wl.ctl, a.wl.set);
+    ItemSource src(a.wl.ctl, a.wl.set);
     int qx, w;
-    while (src.next(a.wl, s_item, &qx, &w)) {
-        const Item it = decode_item(a.wl, a.num_seqs, H, qx, w);
+    while (src.next(tb, s_item, &qx, &w)) {
+        const Item it = decode_item(tb, a.num_seqs, H, qx, w);
         const int start = a.offsets[it.seq];
         const int s = a.offsets[it.seq + 1] - start;
         const int q0 = it.qtile * BQ;
@@ -716,7 +739,8 @@ int resident_grid(KernelFn fn, int threads) {
 }
 
 template <typename T, int D>
-hipError_t launch16(const FwdParams& p, WorkList wl, int grid, hipStream_t stream) {
+hipError_t launch16(const FwdParams& p, WorkList wl, int grid, hipStream_t stream, hipEvent_t start,
+                  hipEvent_t stop) {
     KernelArgs a;
     a.q = static_cast<const uint16_t*>(p.q);
     a.k = static_cast<const uint16_t*>(p.k);
@@ -728,18 +752,26 @@ hipError_t launch16(const FwdParams& p, WorkList wl, int grid, hipStream_t strea
     a.heads = p.heads;
     a.score_scale = -p.alpha * LOG2E;
     a.out_scale = -LN2 / p.n;
-    auto fn = attn_fwd_mfma16<T, D, NW16, QBlocks<D>::value, KeyTile<D>::value, Prefetch<D>::value>;
+    auto fn = wl.fused ? attn_fwd_mfma16<T, D, NW16, QBlocks<D>::value, KeyTile<D>::value,
+                                         Prefetch<D>::value, true>
+                       : attn_fwd_mfma16<T, D, NW16, QBlocks<D>::value, KeyTile<D>::value,
+                                         Prefetch<D>::value, false>;
     if (grid <= 0) {
-        static int cached = 0;
-        if (!cached) cached = resident_grid(fn, NW16 * 64);
-        grid = cached;
+        static int cached[2] = {0, 0};
+        int& c = cached[wl.fused ? 1 : 0];
+        if (!c) c = resident_grid(fn, NW16 * 64);
+        grid = c;
     }
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(NW16 * 64), 0, stream, a);
+    if (start)
+        hipExtLaunchKernelGGL(fn, dim3(grid), dim3(NW16 * 64), 0, stream, start, stop, 0, a);
+    else
+        hipLaunchKernelGGL(fn, dim3(grid), dim3(NW16 * 64), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_f32(const FwdParams& p, WorkList wl, int grid, hipStream_t stream) {
+hipError_t launch_f32(const FwdParams& p, WorkList wl, int grid, hipStream_t stream, hipEvent_t start,
+                  hipEvent_t stop) {
     KernelArgsF32 a;
     a.q = static_cast<const float*>(p.q);
     a.k = static_cast<const float*>(p.k);
@@ -751,13 +783,17 @@ hipError_t launch_f32(const FwdParams& p, WorkList wl, int grid, hipStream_t str
     a.heads = p.heads;
     a.score_scale = -p.alpha * LOG2E;
     a.out_scale = -LN2 / p.n;
-    auto fn = attn_fwd_mfma_f32<D, NWF, BKF>;
+    auto fn = wl.fused ? attn_fwd_mfma_f32<D, NWF, BKF, true> : attn_fwd_mfma_f32<D, NWF, BKF, false>;
     if (grid <= 0) {
-        static int cached = 0;
-        if (!cached) cached = resident_grid(fn, NWF * 64);
-        grid = cached;
+        static int cached[2] = {0, 0};
+        int& c = cached[wl.fused ? 1 : 0];
+        if (!c) c = resident_grid(fn, NWF * 64);
+        grid = c;
     }
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(NWF * 64), 0, stream, a);
+    if (start)
+        hipExtLaunchKernelGGL(fn, dim3(grid), dim3(NWF * 64), 0, stream, start, stop, 0, a);
+    else
+        hipLaunchKernelGGL(fn, dim3(grid), dim3(NWF * 64), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -772,16 +808,17 @@ int q_tile_rows(Dtype dt, int d) {
 }
 
 hipError_t launch_attention(const FwdParams& p, Dtype dt, WorkList wl, int grid,
-                            hipStream_t stream) {
+                            hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     switch (dt) {
     case Dtype::BF16:
-        return p.d == 64 ? launch16<__bf16, 64>(p, wl, grid, stream)
-                         : launch16<__bf16, 128>(p, wl, grid, stream);
+        return p.d == 64 ? launch16<__bf16, 64>(p, wl, grid, stream, start, stop)
+                         : launch16<__bf16, 128>(p, wl, grid, stream, start, stop);
     case Dtype::FP16:
-        return p.d == 64 ? launch16<_Float16, 64>(p, wl, grid, stream)
-                         : launch16<_Float16, 128>(p, wl, grid, stream);
+        return p.d == 64 ? launch16<_Float16, 64>(p, wl, grid, stream, start, stop)
+                         : launch16<_Float16, 128>(p, wl, grid, stream, start, stop);
     case Dtype::FP32:
-        return p.d == 64 ? launch_f32<64>(p, wl, grid, stream) : launch_f32<128>(p, wl, grid, stream);
+        return p.d == 64 ? launch_f32<64>(p, wl, grid, stream, start, stop)
+                         : launch_f32<128>(p, wl, grid, stream, start, stop);
     }
     return hipErrorInvalidValue;
 }

@@ -15,13 +15,27 @@ constexpr int CTL_LINE = 32;  // ints per queue counter: one 128-byte line each
 
 // Words at the start of the scratch area (int32).
 enum : int {
-    CTL_NEXT = 0,                 // NEXT + CTL_LINE*x: next item of queue x (device atomic)
-    CTL_TOTAL = NQ * CTL_LINE,    // TOTAL + x: items in queue x
+    CTL_NEXT = 0,                 // NEXT + CTL_LINE*(NQ*set + x): next item of queue x for
+                                  // the calls of counter set `set` (0, 1; device atomic)
+    CTL_TOTAL = 2 * NQ * CTL_LINE,  // TOTAL + x: items in queue x
     CTL_FLAGS = CTL_TOTAL + NQ,   // bit 0: off[0] != 0, bit 1: a decreasing offset,
                                   // bit 2: item count overflow
     CTL_MODE = CTL_FLAGS + 1,     // QUEUE_BANDS or QUEUE_PAIRS
     CTL_WORDS = CTL_TOTAL + 2 * NQ
 };
+static_assert(CTL_MODE < CTL_WORDS, "control block layout");
+
+// Small batches skip the work-list kernel: every workgroup of the attention
+// kernel ranks the sequences and builds the queue tables itself, in LDS, at
+// its start (the tables are a few KB; building them costs less than a second
+// kernel launch).  Up to FUSE_SEQS sequences and FUSE_PAIRS (sequence, head)
+// pairs.  Either way the queue counters are zero when a launch starts: calls
+// on one work list alternate between two counter sets, and each attention
+// launch clears the set the next call will use (the work-list kernel clears
+// both).
+constexpr int FUSE_SEQS = 256;
+constexpr int FUSE_PAIRS = 2048;
+constexpr int FUSE_QLEN = FUSE_PAIRS / NQ;
 
 // QUEUE_BANDS: ranks sorted, items level by level (below).  QUEUE_PAIRS: input
 // order (more sequences than the sort takes), items pair by pair, each pair's
@@ -49,6 +63,28 @@ struct WorkList {
     int* ntile;    // [num_seqs]      Q-tile count at each rank
     int* qprefix;  // [NQ * (qlen + 1)] first item of each band of a queue, then the total
     int qlen;      // max pairs per queue = ceil(num_seqs * heads / NQ)
+    int fused;     // 1: the attention kernel builds the tables in LDS (FUSE_* limits)
+    int set;       // counter set of this call (0 or 1)
+};
+
+// The tables item decoding reads: the work list in global memory, or the
+// copy a workgroup built in its LDS (generic pointers to either).
+struct Tables {
+    const int* order;
+    const int* ntile;
+    const int* qprefix;
+    const int* totals;   // [NQ]
+    int qlen;
+    int mode;            // QUEUE_BANDS or QUEUE_PAIRS
+};
+
+// LDS copy of the tables for a fused launch.
+struct LocalTables {
+    int order[FUSE_SEQS];
+    int ntile[FUSE_SEQS];
+    int qprefix[NQ * (FUSE_QLEN + 1)];
+    int totals[NQ];
+    int flags;
 };
 
 inline int queue_len(int num_seqs, int heads) {
@@ -69,6 +105,8 @@ inline WorkList worklist_carve(void* base, int num_seqs, int heads) {
     wl.ntile = wl.order + num_seqs;
     wl.qprefix = wl.ntile + num_seqs;
     wl.qlen = queue_len(num_seqs, heads);
+    wl.fused = 0;
+    wl.set = 0;
     return wl;
 }
 
@@ -77,8 +115,11 @@ inline WorkList worklist_carve(void* base, int num_seqs, int heads) {
 // SORT_MAX sequences).  The other two force one path, for tests.
 enum class SortChoice : int { AUTO = 0, BITONIC = 1, INPUT_ORDER = 2 };
 
+// `start` / `stop`, when not null, are recorded by the kernel dispatch itself
+// (timing without extra stream packets).
 hipError_t launch_schedule(const int32_t* offsets, int num_seqs, int heads, int q_tile_rows,
-                           WorkList wl, hipStream_t stream, SortChoice choice);
+                           WorkList wl, hipStream_t stream, SortChoice choice,
+                           hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 enum class Dtype : int { BF16 = 0, FP16 = 1, FP32 = 2 };
 
@@ -101,6 +142,7 @@ int q_tile_rows(Dtype dt, int d);
 // Enqueues the attention kernel (the work list must already be built on the
 // same stream).  `grid` = 0 picks the resident-workgroup count of the device.
 hipError_t launch_attention(const FwdParams& p, Dtype dt, WorkList wl, int grid,
-                            hipStream_t stream);
+                            hipStream_t stream, hipEvent_t start = nullptr,
+                            hipEvent_t stop = nullptr);
 
 }  // namespace hstu

@@ -56,18 +56,18 @@ __device__ inline int queue_pairs(int pairs, int x) {
 }
 
 // Item w of queue x.
-__device__ inline Item decode_item(const WorkList& wl, int num_seqs, int heads, int x, int w) {
+__device__ inline Item decode_item(const Tables& tb, int num_seqs, int heads, int x, int w) {
     const int pairs = num_seqs * heads;
-    const int* pre = wl.qprefix + x * (wl.qlen + 1);
+    const int* pre = tb.qprefix + x * (tb.qlen + 1);
     const int b = wave_search(pre, queue_pairs(pairs, x), w);   // band (or pair)
     const int local = w - pre[b];
-    if (wl.ctl[CTL_MODE] == QUEUE_PAIRS) {
+    if (tb.mode == QUEUE_PAIRS) {
         const int p = queue_pair(b, x);
         const int rank = p / heads;
         Item it;
         it.head = p - rank * heads;
-        it.qtile = wl.ntile[rank] - 1 - local;
-        it.seq = wl.order[rank];
+        it.qtile = tb.ntile[rank] - 1 - local;
+        it.seq = tb.order[rank];
         return it;
     }
     const int per_level = b + 1;                                 // pairs taking part
@@ -75,12 +75,127 @@ __device__ inline Item decode_item(const WorkList& wl, int num_seqs, int heads, 
     const int i = local - lvl * per_level;                       // pair position in queue
     const int p = queue_pair(i, x);
     const int rank = p / heads;
-    const int top = wl.ntile[queue_pair(b, x) / heads];          // tiles of the band's last pair
+    const int top = tb.ntile[queue_pair(b, x) / heads];          // tiles of the band's last pair
     Item it;
     it.head = p - rank * heads;
     it.qtile = top - 1 - lvl;
-    it.seq = wl.order[rank];
+    it.seq = tb.order[rank];
     return it;
+}
+
+// The global work list as tables.
+__device__ inline Tables global_tables(const WorkList& wl) {
+    Tables tb;
+    tb.order = wl.order;
+    tb.ntile = wl.ntile;
+    tb.qprefix = wl.qprefix;
+    tb.totals = wl.ctl + CTL_TOTAL;
+    tb.qlen = wl.qlen;
+    tb.mode = wl.ctl[CTL_MODE];
+    return tb;
+}
+
+// Builds the queue tables of a fused launch in LDS, with every thread of the
+// workgroup (blockDim.x >= FUSE_SEQS, a multiple of 64).  The same ranking and
+// band numbering as the work-list kernel: sequences by Q-tile count, largest
+// first (ties by index), pairs dealt to the queues in snake order, per queue
+// the first item of each band.  Workgroup 0 publishes the offset flags.
+__device__ inline Tables build_local_tables(LocalTables& lt, int* scratch, const int32_t* off,
+                                            int num_seqs, int heads, int bq, int* ctl) {
+    const int tid = threadIdx.x;
+    int* t_in = scratch;                 // [FUSE_SEQS] tile count by sequence id
+    if (tid == 0) lt.flags = 0;
+    __syncthreads();
+    if (tid < num_seqs) {
+        long long s = (long long)off[tid + 1] - (long long)off[tid];
+        int fl = 0;
+        if (tid == 0 && off[0] != 0) fl |= 1;
+        if (s < 0) {
+            fl |= 2;
+            s = 0;
+        }
+        t_in[tid] = (int)((s + bq - 1) / bq);
+        if (fl) atomicOr(&lt.flags, fl);
+    }
+    __syncthreads();
+    // Rank: sequences with more tiles, then equal tiles and a smaller index.
+    if (tid < num_seqs) {
+        const int t = t_in[tid];
+        int rank = 0;
+        for (int j = 0; j < num_seqs; ++j) {
+            const int u = t_in[j];
+            rank += (u > t) || (u == t && j < tid);
+        }
+        lt.order[rank] = tid;
+        lt.ntile[rank] = t;
+    }
+    __syncthreads();
+    // Band prefix: threads 32x .. 32x+31 scan queue x, CHUNK positions each.
+    const int pairs = num_seqs * heads;
+    const int qlen = (pairs + NQ - 1) / NQ;
+    const int full = pairs / NQ, rem = pairs % NQ;
+    auto position_exists = [&](int i, int x) {
+        if (i < full) return true;
+        if (i > full) return false;
+        const int pos = (full & 1) ? NQ - 1 - x : x;
+        return pos < rem;
+    };
+    constexpr int CHUNK = (FUSE_QLEN + 31) / 32;
+    if (tid < 32 * NQ) {
+        const int x = tid >> 5, l = tid & 31;
+        long long term[CHUNK];
+        long long sum = 0;
+#pragma unroll
+        for (int c = 0; c < CHUNK; ++c) {
+            const int i = l * CHUNK + c;
+            long long v = 0;
+            if (position_exists(i, x)) {
+                const long long ti = lt.ntile[queue_pair(i, x) / heads];
+                const long long tn =
+                        position_exists(i + 1, x) ? lt.ntile[queue_pair(i + 1, x) / heads] : 0;
+                v = (ti - tn) * (i + 1);
+            }
+            term[c] = v;
+            sum += v;
+        }
+        long long inc = sum;   // inclusive scan of the chunk sums over the 32 threads
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) {
+            const long long y = __shfl_up(inc, o, 32);
+            if (l >= o) inc += y;
+        }
+        long long run = inc - sum;
+#pragma unroll
+        for (int c = 0; c < CHUNK; ++c) {
+            const int i = l * CHUNK + c;
+            if (position_exists(i, x)) lt.qprefix[x * (qlen + 1) + i] = (int)min(run, 0x7fffffffLL);
+            run += term[c];
+        }
+        if (l == 31) {
+            const int pos = (full & 1) ? NQ - 1 - x : x;
+            const int nx = full + (pos < rem ? 1 : 0);
+            int total = (int)inc;
+            if (inc > 0x7fffffffLL) {   // refuse to run rather than wrap
+                atomicOr(&lt.flags, 4);
+                total = 0;
+            }
+            lt.qprefix[x * (qlen + 1) + nx] = total;
+            lt.totals[x] = total;
+        }
+    }
+    __syncthreads();
+    if (blockIdx.x == 0 && tid == 0) {
+        ctl[CTL_FLAGS] = lt.flags;
+        ctl[CTL_MODE] = QUEUE_BANDS;
+    }
+    Tables tb;
+    tb.order = lt.order;
+    tb.ntile = lt.ntile;
+    tb.qprefix = lt.qprefix;
+    tb.totals = lt.totals;
+    tb.qlen = qlen;
+    tb.mode = QUEUE_BANDS;
+    return tb;
 }
 
 // Hands out items to a workgroup: its own XCD's queue first, then, once that
@@ -92,25 +207,27 @@ __device__ inline Item decode_item(const WorkList& wl, int num_seqs, int heads, 
 // next() from every thread.
 struct ItemSource {
     int queue;   // queue currently being drained
-    __device__ ItemSource() : queue(current_xcd() % NQ) {}
+    int* next_;  // this call's counter set
+    __device__ ItemSource(int* ctl, int set)
+        : queue(current_xcd() % NQ), next_(ctl + CTL_NEXT + CTL_LINE * NQ * set) {}
 
     // Returns false when every queue is empty.  On true, *x and *w name the item.
-    __device__ bool next(const WorkList& wl, int* slot, int* x, int* w) {
+    __device__ bool next(const Tables& tb, int* slot, int* x, int* w) {
         for (;;) {
-            if (threadIdx.x == 0) slot[0] = atomicAdd(wl.ctl + CTL_NEXT + CTL_LINE * queue, 1);
+            if (threadIdx.x == 0) slot[0] = atomicAdd(next_ + CTL_LINE * queue, 1);
             __syncthreads();
             const int got = __builtin_amdgcn_readfirstlane(slot[0]);
             __syncthreads();
-            if (got < wl.ctl[CTL_TOTAL + queue]) {
+            if (got < tb.totals[queue]) {
                 *x = queue;
                 *w = got;
                 return true;
             }
             if (threadIdx.x < NQ) {
                 const int q = threadIdx.x;
-                const int taken = __hip_atomic_load(wl.ctl + CTL_NEXT + CTL_LINE * q,
+                const int taken = __hip_atomic_load(next_ + CTL_LINE * q,
                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                slot[q] = wl.ctl[CTL_TOTAL + q] - taken;
+                slot[q] = tb.totals[q] - taken;
             }
             __syncthreads();
             int best = -1, most = 0;
@@ -129,5 +246,14 @@ struct ItemSource {
         }
     }
 };
+
+// Clears the counter set the next call on this work list will use (the other
+// set).  Called by every thread; workgroup 0's first NQ threads do it.  No
+// workgroup of this launch touches that set.
+__device__ inline void clear_next_set(int* ctl, int set) {
+    if (blockIdx.x == 0 && threadIdx.x < NQ)
+        __hip_atomic_store(ctl + CTL_NEXT + CTL_LINE * (NQ * (1 - set) + threadIdx.x), 0,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 }  // namespace hstu

@@ -6,7 +6,11 @@
 //    LDS bitonic sort; above SORT_MAX sequences, input order.
 // 2. Deal the (rank, head) pairs to the NQ queues in snake order and scan,
 //    per queue, the item count of each band into qprefix.
-// 3. Reset every queue's item counter, so a forward call needs no memset.
+// 3. Reset the item counters of both counter sets, so a forward call needs no
+//    memset (the attention kernel clears the set of the call after it, for
+//    launches that build their tables themselves).
+#include <hip/hip_ext.h>
+
 #include "internal.h"
 
 namespace hstu {
@@ -16,6 +20,7 @@ namespace {
 constexpr int SCHED_THREADS = 1024;
 constexpr int SCHED_WAVES = SCHED_THREADS / 64;
 constexpr int HIST_MAX = 8192;  // tile-count values the counting sort handles
+constexpr int CACHE = 4;        // tile counts each thread keeps in registers
 
 enum : int { RANK_COUNTING = 0, RANK_BITONIC = 1, RANK_INPUT = 2 };
 
@@ -76,9 +81,28 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
         return (int)((s + bq - 1) / bq);
     };
 
+    // Each thread's first CACHE sequences (i = tid + k * SCHED_THREADS) keep
+    // their tile count in registers, so the offsets are read from memory once
+    // for batches of up to SCHED_THREADS * CACHE sequences.
+    int tcache[CACHE];
+#pragma unroll
+    for (int k = 0; k < CACHE; ++k) {
+        const int i = tid + k * SCHED_THREADS;
+        tcache[k] = i < num_seqs ? tiles_of(i) : 0;
+    }
+    // f(i, tiles of i) for this thread's sequences.
+    auto for_each_seq = [&](auto f) {
+#pragma unroll
+        for (int k = 0; k < CACHE; ++k) {
+            const int i = tid + k * SCHED_THREADS;
+            if (i < num_seqs) f(i, tcache[k]);
+        }
+        for (int i = tid + CACHE * SCHED_THREADS; i < num_seqs; i += SCHED_THREADS) f(i, tiles_of(i));
+    };
+
     // ---- 1. ranking -------------------------------------------------------
     int my_max = 0;
-    for (int i = tid; i < num_seqs; i += SCHED_THREADS) my_max = max(my_max, tiles_of(i));
+    for_each_seq([&](int, int t) { my_max = max(my_max, t); });
     atomicMax(&sh.max_tiles, my_max);
     __syncthreads();
     const int maxT = sh.max_tiles;
@@ -96,7 +120,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
     if (kind == RANK_COUNTING) {
         for (int v = tid; v <= maxT; v += SCHED_THREADS) hist[v] = 0;
         __syncthreads();
-        for (int i = tid; i < num_seqs; i += SCHED_THREADS) atomicAdd(&hist[tiles_of(i)], 1);
+        for_each_seq([&](int, int t) { atomicAdd(&hist[t], 1); });
         __syncthreads();
         // cursor[v] = number of sequences with more than v tiles (scan over v descending).
         for (int base = 0; base <= maxT; base += SCHED_THREADS) {
@@ -108,23 +132,20 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
             if (tid == SCHED_THREADS - 1) sh.carry[0] += inc;
             __syncthreads();
         }
-        for (int i = tid; i < num_seqs; i += SCHED_THREADS) {
-            const int t = tiles_of(i);
+        for_each_seq([&](int i, int t) {
             const int pos = atomicAdd(&cursor[t], 1);
             wl.order[pos] = i;
             wl.ntile[pos] = t;
             sorted[pos] = t;
-        }
+        });
     } else if (kind == RANK_BITONIC) {
         int P = 1;
         while (P < num_seqs) P <<= 1;
-        for (int i = tid; i < P; i += SCHED_THREADS) {
-            unsigned long long key = 0;
-            if (i < num_seqs)
-                key = ((unsigned long long)(unsigned)tiles_of(i) << 32) |
-                      (unsigned long long)(~(unsigned)i);
-            keys[i] = key;
-        }
+        for (int i = tid; i < P; i += SCHED_THREADS) keys[i] = 0;
+        __syncthreads();
+        for_each_seq([&](int i, int t) {
+            keys[i] = ((unsigned long long)(unsigned)t << 32) | (unsigned long long)(~(unsigned)i);
+        });
         __syncthreads();
         for (int kk = 2; kk <= P; kk <<= 1) {
             for (int j = kk >> 1; j > 0; j >>= 1) {
@@ -147,10 +168,10 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
             wl.ntile[m] = (int)(keys[m] >> 32);
         }
     } else {
-        for (int i = tid; i < num_seqs; i += SCHED_THREADS) {
+        for_each_seq([&](int i, int t) {
             wl.order[i] = i;
-            wl.ntile[i] = tiles_of(i);
-        }
+            wl.ntile[i] = t;
+        });
     }
     __syncthreads();
     if (tid < NQ) sh.carry[tid] = 0;
@@ -204,6 +225,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
         const int n = full + (pos < rem ? 1 : 0);
         wl.qprefix[tid * row + n] = (int)total;
         wl.ctl[CTL_NEXT + CTL_LINE * tid] = 0;
+        wl.ctl[CTL_NEXT + CTL_LINE * (NQ + tid)] = 0;
         wl.ctl[CTL_TOTAL + tid] = (int)total;
     }
     if (flags) atomicOr(&sh.flags, flags);
@@ -217,7 +239,8 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
 }  // namespace
 
 hipError_t launch_schedule(const int32_t* offsets, int num_seqs, int heads, int q_tile_rows,
-                           WorkList wl, hipStream_t stream, SortChoice choice) {
+                           WorkList wl, hipStream_t stream, SortChoice choice, hipEvent_t start,
+                           hipEvent_t stop) {
     int kind = RANK_COUNTING;
     if (choice == SortChoice::BITONIC) kind = RANK_BITONIC;
     if (choice == SortChoice::INPUT_ORDER) kind = RANK_INPUT;
@@ -241,8 +264,12 @@ hipError_t launch_schedule(const int32_t* offsets, int num_seqs, int heads, int 
         if (e != hipSuccess) return e;
         attr_done = true;
     }
-    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(SCHED_THREADS), lds, stream, offsets,
-                       num_seqs, heads, q_tile_rows, wl, kind);
+    if (start)
+        hipExtLaunchKernelGGL(schedule_kernel, dim3(1), dim3(SCHED_THREADS), lds, stream, start,
+                              stop, 0, offsets, num_seqs, heads, q_tile_rows, wl, kind);
+    else
+        hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(SCHED_THREADS), lds, stream, offsets,
+                           num_seqs, heads, q_tile_rows, wl, kind);
     return hipGetLastError();
 }
 

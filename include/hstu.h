@@ -38,7 +38,11 @@
  * (device, stream): a work list of 12 bytes per sequence plus a header.  It is
  * allocated on the first call that needs more; later calls with no more
  * sequences allocate nothing.  Two calls on the same stream are ordered by the
- * stream; calls on different streams use different scratch areas.
+ * stream; calls on different streams use different scratch areas.  A call is
+ * one kernel for batches of up to 256 sequences and 2048 (sequence, head)
+ * pairs (the attention kernel ranks the sequences itself), two kernels
+ * otherwise (a work-list kernel, then the attention kernel); the first call on
+ * a new scratch area always takes the two-kernel form.
  *
  * Errors: argument checks happen on the host before anything is enqueued; a
  * failed check returns a negative status and leaves the stream untouched.  A
@@ -109,13 +113,13 @@ void hstu_release_workspace(void);
 /* Per-kernel time accumulated over calls made while profiling was on. */
 typedef struct {
     int64_t calls;        /* forward calls timed */
-    double sched_ms;      /* total time of the work-list kernel */
+    double sched_ms;      /* total time of the work-list kernel (0 for one-kernel calls) */
     double attn_ms;       /* total time of the attention kernel */
     int64_t dropped;      /* calls not timed because the event ring was full */
 } hstu_kernel_times_t;
 
-/* on != 0: from now on each forward call on this thread's current device
- * records HIP events on its stream around its two kernels. */
+/* on != 0: from now on each forward call records start and stop events on
+ * the dispatch of each of its kernels. */
 hstu_status_t hstu_profile_enable(int on);
 
 /* Waits for the recorded events, adds their durations to *out and, if reset,

@@ -225,12 +225,17 @@ def test_scheduler_ranking_paths_agree(sort, monkeypatch):
 
 
 def test_profiling_counts_calls():
-    case = workloads.make_case([512, 512], 2, 64, "bf16", seed=19, n=512.0)
-    q, k, v, off = device_case(case)
-    hstu.hstu_profile_read(reset=True)
-    hstu.hstu_profile_enable(True)
-    for _ in range(3):
-        hstu.hstu_attn_fwd(q, k, v, off, case.alpha, case.n)
-    hstu.hstu_profile_enable(False)
-    t = hstu.hstu_profile_read(reset=True)
-    assert t.calls == 3 and t.attn_ms > 0 and t.sched_ms > 0
+    # A small batch runs as one kernel (no work-list kernel time); a batch of
+    # more than 256 sequences runs the work-list kernel first.
+    for lengths, one_kernel in (([512, 512], True), ([40] * 300, False)):
+        case = workloads.make_case(lengths, 2, 64, "bf16", seed=19, n=512.0)
+        q, k, v, off = device_case(case)
+        hstu.hstu_attn_fwd(q, k, v, off, case.alpha, case.n)   # scratch sized outside the count
+        hstu.hstu_profile_read(reset=True)
+        hstu.hstu_profile_enable(True)
+        for _ in range(3):
+            hstu.hstu_attn_fwd(q, k, v, off, case.alpha, case.n)
+        hstu.hstu_profile_enable(False)
+        t = hstu.hstu_profile_read(reset=True)
+        assert t.calls == 3 and t.attn_ms > 0
+        assert (t.sched_ms == 0) if one_kernel else (t.sched_ms > 0)

@@ -110,3 +110,93 @@ def test_search_edges():
     for w in range(9):
         p = search(a, 5, w)
         assert a[p] <= w < a[p + 1]
+
+
+# ---------------------------------------------------------------------------
+# The tables a small-batch launch builds inside the attention kernel
+# (build_local_tables in schedule.h): rank by an all-pairs count, then per
+# queue 32 threads scan CHUNK consecutive band terms each.  Emulated step by
+# step here and checked against the model above.
+FUSE_SEQS, FUSE_PAIRS = 256, 2048
+FUSE_QLEN = FUSE_PAIRS // NQ
+CHUNK = (FUSE_QLEN + 31) // 32
+
+
+def build_local(lengths, heads, bq):
+    L = np.asarray(lengths, np.int64)
+    n = len(L)
+    t_in = [int((max(int(s), 0) + bq - 1) // bq) for s in L]
+    order = [0] * n
+    ntile = [0] * n
+    for tid in range(n):
+        t = t_in[tid]
+        rank = sum(1 for j in range(n) if t_in[j] > t or (t_in[j] == t and j < tid))
+        order[rank] = tid
+        ntile[rank] = t
+    pairs = n * heads
+    qlen = (pairs + NQ - 1) // NQ
+    full, rem = pairs // NQ, pairs % NQ
+
+    def exists(i, x):
+        if i < full:
+            return True
+        if i > full:
+            return False
+        pos = (NQ - 1 - x) if (full & 1) else x
+        return pos < rem
+
+    qprefix = np.full((NQ, qlen + 1), -1, np.int64)
+    totals = [0] * NQ
+    for x in range(NQ):
+        sums, terms = [], []
+        for l in range(32):
+            tl = []
+            for c in range(CHUNK):
+                i = l * CHUNK + c
+                v = 0
+                if exists(i, x):
+                    ti = ntile[queue_pair(i, x) // heads]
+                    tn = ntile[queue_pair(i + 1, x) // heads] if exists(i + 1, x) else 0
+                    v = (ti - tn) * (i + 1)
+                tl.append(v)
+            terms.append(tl)
+            sums.append(sum(tl))
+        inc = np.cumsum(sums)
+        for l in range(32):
+            run = int(inc[l] - sums[l])
+            for c in range(CHUNK):
+                i = l * CHUNK + c
+                if exists(i, x):
+                    qprefix[x, i] = run
+                run += terms[l][c]
+        pos = (NQ - 1 - x) if (full & 1) else x
+        nx = full + (1 if pos < rem else 0)
+        qprefix[x, nx] = int(inc[31])
+        totals[x] = int(inc[31])
+    return order, ntile, qprefix, totals
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_local_tables_match_model(seed):
+    rng = np.random.default_rng(100 + seed)
+    N = int(rng.integers(1, FUSE_SEQS + 1))
+    heads = int(rng.integers(1, FUSE_PAIRS // N + 1))
+    heads = min(heads, 16)
+    lengths = rng.integers(0, 3000, size=N)
+    lengths[rng.random(N) < 0.2] = 0
+    bq = int(rng.choice([32, 128, 256]))
+    order, ntile, qprefix, totals = build_local(lengths, heads, bq)
+    bands, m_order, m_ntile, m_qprefix, counts = build(lengths, heads, bq)
+    assert bands and order == m_order and ntile == m_ntile
+    for x in range(NQ):
+        n = int(counts[x])
+        assert list(qprefix[x, :n + 1]) == list(m_qprefix[x, :n + 1])
+        assert totals[x] == int(m_qprefix[x, n])
+    # and every item decodes to a real tile, once
+    seen = set()
+    for x in range(NQ):
+        for w in range(totals[x]):
+            i, h, j = decode(True, order, ntile, qprefix, counts, heads, x, w)
+            assert 0 <= h < heads and 0 <= j and j * bq < lengths[i]
+            seen.add((i, h, j))
+    assert len(seen) == sum(int((l + bq - 1) // bq) for l in lengths) * heads
