@@ -424,10 +424,23 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
         // One barrier per tile.  At barrier c every wave has finished its loads
         // of tile c+1 and every read of tile c-1 (slot (c+PF) % NS); then tile
         // c+PF is issued into that slot.
+        //
+        // Two workgroups share each CU, and the SIMDs favour the older of two
+        // ready waves, so left alone one workgroup runs at nearly its solo
+        // speed and the other takes the leftover issue slots.  The wave
+        // priority alternates every two tiles, in opposite phase for the two
+        // halves of the grid (the dispatcher fills every CU once with the
+        // first half before placing the second), so the two share the SIMDs
+        // more evenly and finish their items closer together (measured 1.5 %
+        // faster on 16 x 4096, 3 % on 8 x 8k-20k).
         auto tile_sync = [&](int c) {
             __builtin_amdgcn_s_waitcnt(VMCNT_LE((PF - 2) * 2 * Cfg::LOADS));
             __syncthreads();
             issue_loads(c + PF);
+            if ((((c >> 1) + (blockIdx.x >= gridDim.x / 2 ? 1 : 0)) & 1) != 0)
+                __builtin_amdgcn_s_setprio(1);
+            else
+                __builtin_amdgcn_s_setprio(0);
         };
 
         // ---- phase A: pipelined full blocks -----------------------------------
