@@ -16,6 +16,11 @@ Two independent evaluations of the same definition live here:
   silu, multiply by mask / n with an explicit lower-triangular 0/1 mask
   (§3.1-§3.2), then scores @ V.  Jagged packing follows §4.2 of that page.
 
+The ``num_targets`` arguments give the target-aware (M-FALCON) mask of the
+HSTU paper translation (§3.4, Appendix H, Algorithm 1 and Fig. 11): the last
+t tokens of a sequence are candidates that see the history and themselves
+only.  ``num_targets=None`` is the plain causal mask.
+
 Parity status: pinned.  The test suite ties these functions to closed forms
 (hand-worked 2- and 3-token cases), to identities that reduce to textbook
 operations (sign-flip -> masked GEMM, constant rows -> prefix sum, row 0),
@@ -65,6 +70,13 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hstu_oracle_rows.argtypes = [vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, f64, f64, vp, vp, i64, vp]
     lib.hstu_oracle_rows.restype = ctypes.c_int
+    lib.hstu_oracle_fwd_targets.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, f64, f64, vp]
+    lib.hstu_oracle_fwd_targets.restype = ctypes.c_int
+    lib.hstu_oracle_rows_targets.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, f64, f64, vp, vp, i64,
+                                             vp]
+    lib.hstu_oracle_rows_targets.restype = ctypes.c_int
     lib.hstu_oracle_threads.argtypes = []
     lib.hstu_oracle_threads.restype = ctypes.c_int
     _libs[path] = lib
@@ -83,38 +95,51 @@ def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
 
+def _targets(num_targets, num_seqs: int):
+    if num_targets is None:
+        return None
+    t = np.ascontiguousarray(num_targets, dtype=np.int32)
+    if t.shape != (num_seqs,):
+        raise ValueError("num_targets needs one count per sequence")
+    return t
+
+
 def fwd(q, k, v, offsets, heads: int, d: int, alpha: float, n: float, dtype: str,
-        lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+        lib: Optional[ctypes.CDLL] = None, num_targets=None) -> np.ndarray:
     """Full fp64 output (T, heads, d)."""
     lib = lib or load()
     q, k, v = (_storage(a, dtype) for a in (q, k, v))
     off = np.ascontiguousarray(offsets, dtype=np.int32)
+    tg = _targets(num_targets, len(off) - 1)
     T = int(off[-1]) if len(off) else 0
     out = np.zeros((T, heads, d), dtype=np.float64)
     for a in (q, k, v):
         if a.size < T * heads * d:
             raise ValueError("q/k/v smaller than offsets imply")
-    rc = lib.hstu_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[dtype], _ptr(off),
-                             len(off) - 1, heads, d, float(alpha), float(n), _ptr(out))
+    rc = lib.hstu_oracle_fwd_targets(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[dtype], _ptr(off),
+                                     None if tg is None else _ptr(tg), len(off) - 1, heads, d,
+                                     float(alpha), float(n), _ptr(out))
     if rc != 0:
         raise ValueError("oracle rejected the arguments (malformed offsets or sizes)")
     return out
 
 
 def rows(q, k, v, offsets, heads: int, d: int, alpha: float, n: float, dtype: str,
-         tokens, head_ids, lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+         tokens, head_ids, lib: Optional[ctypes.CDLL] = None, num_targets=None) -> np.ndarray:
     """fp64 outputs (m, d) at global tokens[m], heads head_ids[m]."""
     lib = lib or load()
     q, k, v = (_storage(a, dtype) for a in (q, k, v))
     off = np.ascontiguousarray(offsets, dtype=np.int32)
+    tg = _targets(num_targets, len(off) - 1)
     tok = np.ascontiguousarray(tokens, dtype=np.int64)
     hd = np.ascontiguousarray(head_ids, dtype=np.int32)
     if tok.shape != hd.shape:
         raise ValueError("tokens and head_ids differ in length")
     out = np.zeros((len(tok), d), dtype=np.float64)
-    rc = lib.hstu_oracle_rows(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[dtype], _ptr(off),
-                              len(off) - 1, heads, d, float(alpha), float(n),
-                              _ptr(tok), _ptr(hd), len(tok), _ptr(out))
+    rc = lib.hstu_oracle_rows_targets(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[dtype], _ptr(off),
+                                      None if tg is None else _ptr(tg), len(off) - 1, heads, d,
+                                      float(alpha), float(n), _ptr(tok), _ptr(hd), len(tok),
+                                      _ptr(out))
     if rc != 0:
         raise ValueError("oracle rejected the sampled rows")
     return out
@@ -143,10 +168,25 @@ def _silu(x: np.ndarray) -> np.ndarray:
     return x * sig
 
 
+def falcon_mask(s: int, t: int) -> np.ndarray:
+    """The (s, s) 0/1 mask of Algorithm 1 (HSTU paper translation, Appendix H):
+    lower-triangular, then entries (i, j) with i, j >= s - t and i != j
+    cleared, so the last t (candidate) rows see the history and themselves."""
+    m = np.tril(np.ones((s, s), dtype=np.float64))
+    h = s - t
+    for i in range(h, s):
+        for j in range(h, s):
+            if i != j:
+                m[i, j] = 0.0
+    return m
+
+
 def dense_unfused(q, k, v, offsets, heads: int, d: int, alpha: float, n: float,
-                  dtype: str) -> np.ndarray:
+                  dtype: str, num_targets=None) -> np.ndarray:
     """Per sequence: the (heads, s, s) score tensor is formed in full, then
-    scaled, passed through SiLU, multiplied by tril(ones)/n and applied to V."""
+    scaled, passed through SiLU, multiplied by the 0/1 mask / n and applied to
+    V.  The mask is tril(ones), or falcon_mask with the sequence's candidate
+    count when num_targets is given."""
     Q, K, V = (widen(a, dtype).reshape(-1, heads, d) for a in (q, k, v))
     off = np.asarray(offsets, dtype=np.int64)
     out = np.zeros((int(off[-1]), heads, d), dtype=np.float64)
@@ -161,7 +201,10 @@ def dense_unfused(q, k, v, offsets, heads: int, d: int, alpha: float, n: float,
         x = np.matmul(Qi, Ki.transpose(0, 2, 1))  # (heads, s, s)
         x = x * alpha
         x = _silu(x)
-        mask = np.tril(np.ones((s, s), dtype=np.float64))
+        if num_targets is None:
+            mask = np.tril(np.ones((s, s), dtype=np.float64))
+        else:
+            mask = falcon_mask(s, min(max(int(num_targets[i]), 0), s))
         x = x * (mask / n)
         o = np.matmul(x, Vi)  # (heads, s, d)
         out[a:b] = o.transpose(1, 0, 2)

@@ -20,6 +20,15 @@
  *     each segment is an independent sample, so no cross-sequence terms.
  *   - HSTU paper translation ("行动胜于言语…"), §3: phi_2 is SiLU.
  *
+ * Target-aware mask (the M-FALCON mask), for the *_targets entry points:
+ *   - HSTU paper translation, §3.4 and Appendix H (Algorithm 1 and Fig. 11):
+ *     a sequence is n history tokens followed by b_m candidate tokens; the
+ *     causal lower-triangular mask is kept and, in addition, entries (i, j)
+ *     with i, j >= n and i != j are masked, so a candidate sees the history
+ *     and itself only.  Per sequence the caller gives the candidate count t;
+ *     history length = s - t.  The mask stays multiplicative 0/1 after SiLU
+ *     (the -inf of the pseudo-code is for softmax models).
+ *
  * Readings taken where the pages are silent (each listed in the design notes):
  *   - alpha multiplies the scores before SiLU; n is a caller-given scalar;
  *   - the mask multiplies after SiLU (0/1), so masked terms are exactly 0;
@@ -91,8 +100,10 @@ static double silu(double x) {
 /* Computes the d outputs of (sequence start `s0`, local row r, head h) into
  * acc[0..d).  Widening q, k and v per element keeps memory small; the cost is
  * irrelevant for an oracle. */
+/* `hist` is the sequence's history length: keys c >= hist (candidates) count
+ * only for c == r.  hist = sequence length gives the plain causal mask. */
 static void one_row(const void* q, const void* k, const void* v, int dtype,
-                    int64_t s0, int64_t r, int heads, int d, int h,
+                    int64_t s0, int64_t r, int64_t hist, int heads, int d, int h,
                     double alpha, double n, double* qrow, double* acc) {
     const int64_t row_stride = (int64_t)heads * d;
     for (int e = 0; e < d; ++e) {
@@ -108,6 +119,14 @@ static void one_row(const void* q, const void* k, const void* v, int dtype,
     c_begin = -s0; /* planted: attends back across the sequence boundary */
 #endif
     for (int64_t c = c_begin; c <= c_end; ++c) {
+        /* a candidate key is seen by its own row only */
+#if ORACLE_PLANT == 7
+        (void)hist; /* planted: candidates see each other */
+#elif ORACLE_PLANT == 8
+        if (c >= hist && r >= hist) continue; /* planted: candidate misses itself */
+#else
+        if (c >= hist && c != r) continue;
+#endif
         int64_t krow = s0 + c;
 #if ORACLE_PLANT == 4
         /* planted: transposed score operand, <q_c, k_r> instead of <q_r, k_c> */
@@ -137,11 +156,13 @@ static void one_row(const void* q, const void* k, const void* v, int dtype,
 
 /* ---- entry points ---------------------------------------------------------- */
 
-/* Full output: out is fp64 (T, heads, d), T = off[num_seqs].  Returns 0, or -1
- * on malformed offsets (off[0] != 0 or decreasing).  d <= 1024. */
-int hstu_oracle_fwd(const void* q, const void* k, const void* v, int dtype,
-                    const int32_t* off, int num_seqs, int heads, int d,
-                    double alpha, double n, double* out) {
+/* Full output: out is fp64 (T, heads, d), T = off[num_seqs].  ntgt is null
+ * (plain causal mask) or the candidate count of each sequence (clamped to
+ * [0, length]).  Returns 0, or -1 on malformed offsets (off[0] != 0 or
+ * decreasing).  d <= 1024. */
+int hstu_oracle_fwd_targets(const void* q, const void* k, const void* v, int dtype,
+                            const int32_t* off, const int32_t* ntgt, int num_seqs, int heads,
+                            int d, double alpha, double n, double* out) {
     if (num_seqs < 0 || heads < 1 || d < 1 || d > 1024) return -1;
     if (num_seqs > 0 && off[0] != 0) return -1;
     for (int i = 0; i < num_seqs; ++i)
@@ -155,8 +176,11 @@ int hstu_oracle_fwd(const void* q, const void* k, const void* v, int dtype,
         for (int64_t it = 0; it < items; ++it) {
             int i = (int)(it / heads), h = (int)(it % heads);
             int64_t s0 = off[i], len = (int64_t)off[i + 1] - off[i];
+            int64_t t = ntgt ? ntgt[i] : 0;
+            if (t < 0) t = 0;
+            if (t > len) t = len;
             for (int64_t r = 0; r < len; ++r) {
-                one_row(q, k, v, dtype, s0, r, heads, d, h, alpha, n, qrow, acc);
+                one_row(q, k, v, dtype, s0, r, len - t, heads, d, h, alpha, n, qrow, acc);
                 double* o = out + (s0 + r) * row_stride + (int64_t)h * d;
                 for (int e = 0; e < d; ++e) o[e] = acc[e];
             }
@@ -165,13 +189,20 @@ int hstu_oracle_fwd(const void* q, const void* k, const void* v, int dtype,
     return 0;
 }
 
+int hstu_oracle_fwd(const void* q, const void* k, const void* v, int dtype,
+                    const int32_t* off, int num_seqs, int heads, int d,
+                    double alpha, double n, double* out) {
+    return hstu_oracle_fwd_targets(q, k, v, dtype, off, 0, num_seqs, heads, d, alpha, n, out);
+}
+
 /* Sampled rows: for m = 0..count-1, out_rows[m, 0..d) is the output at global
  * token tok[m] and head hd[m].  The token's sequence is found by a binary
- * search over the offsets.  Returns 0, or -1 on a token or head out of range. */
-int hstu_oracle_rows(const void* q, const void* k, const void* v, int dtype,
-                     const int32_t* off, int num_seqs, int heads, int d,
-                     double alpha, double n, const int64_t* tok, const int32_t* hd,
-                     int64_t count, double* out_rows) {
+ * search over the offsets.  ntgt as for hstu_oracle_fwd_targets.  Returns 0,
+ * or -1 on a token or head out of range. */
+int hstu_oracle_rows_targets(const void* q, const void* k, const void* v, int dtype,
+                             const int32_t* off, const int32_t* ntgt, int num_seqs, int heads,
+                             int d, double alpha, double n, const int64_t* tok,
+                             const int32_t* hd, int64_t count, double* out_rows) {
     if (num_seqs < 1 || heads < 1 || d < 1 || d > 1024) return -1;
     int64_t T = off[num_seqs];
     for (int64_t m = 0; m < count; ++m)
@@ -187,12 +218,23 @@ int hstu_oracle_rows(const void* q, const void* k, const void* v, int dtype,
                 int mid = (lo + hi + 1) / 2;
                 if (off[mid] <= tok[m]) lo = mid; else hi = mid - 1;
             }
-            int64_t s0 = off[lo];
-            one_row(q, k, v, dtype, s0, tok[m] - s0, heads, d, hd[m], alpha, n, qrow,
+            int64_t s0 = off[lo], len = (int64_t)off[lo + 1] - off[lo];
+            int64_t t = ntgt ? ntgt[lo] : 0;
+            if (t < 0) t = 0;
+            if (t > len) t = len;
+            one_row(q, k, v, dtype, s0, tok[m] - s0, len - t, heads, d, hd[m], alpha, n, qrow,
                     out_rows + m * (int64_t)d);
         }
     }
     return 0;
+}
+
+int hstu_oracle_rows(const void* q, const void* k, const void* v, int dtype,
+                     const int32_t* off, int num_seqs, int heads, int d,
+                     double alpha, double n, const int64_t* tok, const int32_t* hd,
+                     int64_t count, double* out_rows) {
+    return hstu_oracle_rows_targets(q, k, v, dtype, off, 0, num_seqs, heads, d, alpha, n, tok,
+                                    hd, count, out_rows);
 }
 
 /* Number of threads an OpenMP parallel region here uses (for reporting). */

@@ -57,9 +57,9 @@ def _parse_tokens(text: str, heads: int, d: int, evaluate) -> np.ndarray:
     return np.array(rows, dtype=np.float64)
 
 
-def golden_cases() -> List[Dict]:
+def golden_cases(path: str = GOLDEN) -> List[Dict]:
     cases, cur = [], None
-    with open(GOLDEN, encoding="utf-8") as f:
+    with open(path, encoding="utf-8") as f:
         for raw in f:
             line = raw.strip()
             if not line or line.startswith("#"):
@@ -82,7 +82,9 @@ def golden_cases() -> List[Dict]:
             arrs[name] = (_parse_tokens(c[name], heads, d, float) if T else
                           np.zeros((0, heads, d)))
         expect = _parse_tokens(c["expect"], heads, d, _eval) if T else np.zeros((0, heads, d))
-        out.append(dict(name=c["name"], heads=heads, d=d, offsets=offsets,
+        targets = (np.array([int(x) for x in c["targets"].split()], dtype=np.int32)
+                   if "targets" in c else None)
+        out.append(dict(name=c["name"], heads=heads, d=d, offsets=offsets, targets=targets,
                         alpha=float(c["alpha"]), n=float(c["n"]), expect=expect, **arrs))
     return out
 
