@@ -12,6 +12,10 @@ object reports the attention kernel's own average duration (HIP events the
 library records on the call's stream during the timed region).  The
 cpu_baseline object times the fp64 CPU oracle on a bounded sample of the same
 workload.
+
+--targets times hstu_attn_fwd_targets instead, on 16 users x (3072 history +
+1024 candidates) (the target-aware mask of M-FALCON ranking, HSTU paper
+translation Appendix H); useful FLOPs then count the pairs that mask keeps.
 """
 from __future__ import annotations
 
@@ -31,6 +35,7 @@ import workloads  # noqa: E402
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
 PEAK_HBM_GBS = 8000.0
 METRIC = "HSTU attn fwd useful TFLOP/s, % bf16 MFMA peak; ms at QKV(16,4,4096,64)"
+METRIC_TARGETS = "HSTU target-aware attn fwd useful TFLOP/s (M-FALCON mask)"
 # HBM traffic per dispatch of the attention kernel, from two rocprofv3 --pmc
 # runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
 # same counter reads for a plain 1 GiB device copy (bench.py --copy-calibrate):
@@ -70,6 +75,18 @@ def to_device(case):
             torch.from_numpy(case.offsets.astype(np.int32)).cuda())
 
 
+def seen_pairs(case) -> float:
+    """(query, key) pairs the mask keeps, summed over sequences: s(s+1)/2 for
+    the causal mask; with t candidates after a history of h = s - t tokens,
+    h(h+1)/2 for the history rows plus h + 1 for each candidate."""
+    s = case.lengths.astype(np.float64)
+    if case.num_targets is None:
+        return float(np.sum(s * (s + 1.0) / 2.0))
+    t = np.clip(case.num_targets.astype(np.float64), 0.0, s)
+    h = s - t
+    return float(np.sum(h * (h + 1.0) / 2.0 + t * (h + 1.0)))
+
+
 def cpu_baseline(case, budget_s: float):
     """Time the oracle on whole sequences of the workload (all heads).  Each
     oracle call takes enough sequences to give every OpenMP thread a
@@ -87,11 +104,14 @@ def cpu_baseline(case, budget_s: float):
         a, b = int(off[i]), int(off[j])
         sub = (off[i:j + 1] - off[i]).astype(np.int32)
         t0 = time.perf_counter()
+        tg = None if case.num_targets is None else case.num_targets[i:j]
         oracle.fwd(case.q[a:b], case.k[a:b], case.v[a:b], sub, case.heads, case.d, case.alpha,
-                   case.n, case.dtype, lib=lib)
+                   case.n, case.dtype, lib=lib, num_targets=tg)
         done_s += time.perf_counter() - t0
-        s = case.lengths[i:j].astype(np.float64)
-        done_flops += float(np.sum(4.0 * case.heads * case.d * s * (s + 1.0) / 2.0))
+        part = workloads.Case(name="", dtype=case.dtype, heads=case.heads, d=case.d,
+                              offsets=sub, q=case.q[:0], k=case.k[:0], v=case.v[:0],
+                              alpha=case.alpha, n=case.n, num_targets=tg)
+        done_flops += 4.0 * case.heads * case.d * seen_pairs(part)
         seqs += j - i
         i = j
     used = min(threads, per_call * case.heads)
@@ -110,6 +130,8 @@ def main() -> int:
     # settle after idle; the default warm-up covers that.
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--targets", action="store_true",
+                    help="time the target-aware forward on 16 x (3072 history + 1024 candidates)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibrate", action="store_true",
@@ -135,14 +157,22 @@ def main() -> int:
         print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
                           "copies": 3}), flush=True)
         return 0
-    case = workloads.workload(args.workload)
+    case = workloads.targets_workload() if args.targets else workloads.workload(args.workload)
     q, k, v, off = to_device(case)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
-    flops = case.useful_flops()
+    flops = 4.0 * case.heads * case.d * seen_pairs(case)
+    if args.targets:
+        tg = torch.from_numpy(case.num_targets.astype(np.int32)).cuda()
+
+        def call():
+            hstu.hstu_attn_fwd_targets(q, k, v, off, tg, case.alpha, case.n, out=out)
+    else:
+        def call():
+            hstu.hstu_attn_fwd(q, k, v, off, case.alpha, case.n, out=out)
 
     for _ in range(args.warmup):
-        hstu.hstu_attn_fwd(q, k, v, off, case.alpha, case.n, out=out)
+        call()
     torch.cuda.synchronize()
 
     hstu.hstu_profile_read(reset=True)
@@ -152,7 +182,7 @@ def main() -> int:
     torch.cuda.synchronize()
     start.record(stream)
     for _ in range(args.steps):
-        hstu.hstu_attn_fwd(q, k, v, off, case.alpha, case.n, out=out)
+        call()
     end.record(stream)
     torch.cuda.synchronize()
     hstu.hstu_profile_enable(False)
@@ -165,7 +195,7 @@ def main() -> int:
     sched_ms = kt.sched_ms / max(1, kt.calls)
     achieved = flops / (attn_ms * 1e-3) / 1e12
     peak = PEAK_MFMA_TFLOPS[case.dtype]
-    traffic = traffic_bytes(args.workload)
+    traffic = None if args.targets else traffic_bytes(args.workload)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel": "attn_fwd_mfma16" if case.dtype != "fp32" else "attn_fwd_mfma_f32",
@@ -179,7 +209,7 @@ def main() -> int:
 
     L = case.lengths
     line = {
-        "metric": METRIC,
+        "metric": METRIC_TARGETS if args.targets else METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -195,6 +225,7 @@ def main() -> int:
         "config": {"workload": case.description, "num_seqs": case.num_seqs,
                    "total_tokens": case.total, "max_seq_len": int(L.max()), "heads": case.heads,
                    "d": case.d, "alpha": case.alpha, "n": case.n,
+                   **({"candidates_per_seq": int(case.num_targets[0])} if args.targets else {}),
                    "useful_gflop": round(flops / 1e9, 3)},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -31,7 +31,7 @@ HSTU_BF16, HSTU_FP16, HSTU_FP32 = 0, 1, 2
 
 # Every symbol include/hstu.h declares.
 EXPORTS = ("hstu_attn_fwd", "hstu_attn_fwd_bf16", "hstu_attn_fwd_fp16", "hstu_attn_fwd_fp32",
-           "hstu_validate_offsets", "hstu_status_string", "hstu_last_hip_error",
+           "hstu_attn_fwd_targets", "hstu_validate_offsets", "hstu_status_string", "hstu_last_hip_error",
            "hstu_release_workspace", "hstu_profile_enable", "hstu_profile_read")
 
 
@@ -71,6 +71,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     for name in ("hstu_attn_fwd_bf16", "hstu_attn_fwd_fp16", "hstu_attn_fwd_fp32"):
         getattr(lib, name).argtypes = fwd
         getattr(lib, name).restype = ctypes.c_int
+    lib.hstu_attn_fwd_targets.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp,
+                                          ctypes.c_int]
+    lib.hstu_attn_fwd_targets.restype = ctypes.c_int
     lib.hstu_validate_offsets.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_int64), vp]
     lib.hstu_validate_offsets.restype = ctypes.c_int
     lib.hstu_status_string.argtypes = [ctypes.c_int]
@@ -112,8 +115,7 @@ def _stream_handle(stream) -> int:
     return int(stream.cuda_stream)
 
 
-def hstu_attn_fwd(q, k, v, seq_offsets, alpha: float, n: float, out=None, stream=None):
-    """Jagged causal HSTU attention forward; returns `out` (T, heads, d)."""
+def _check_tensors(q, k, v, seq_offsets, out):
     import torch
     if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must share one (T, heads, d) shape")
@@ -130,6 +132,12 @@ def hstu_attn_fwd(q, k, v, seq_offsets, alpha: float, n: float, out=None, stream
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    return out
+
+
+def hstu_attn_fwd(q, k, v, seq_offsets, alpha: float, n: float, out=None, stream=None):
+    """Jagged causal HSTU attention forward; returns `out` (T, heads, d)."""
+    out = _check_tensors(q, k, v, seq_offsets, out)
     T, heads, d = q.shape
     num_seqs = seq_offsets.numel() - 1
     lib = load_library()
@@ -137,6 +145,28 @@ def hstu_attn_fwd(q, k, v, seq_offsets, alpha: float, n: float, out=None, stream
                            num_seqs, heads, d, float(alpha), float(n), out.data_ptr(),
                            _stream_handle(stream), _dtype_code(q))
     _check(st, "hstu_attn_fwd")
+    return out
+
+
+def hstu_attn_fwd_targets(q, k, v, seq_offsets, num_targets, alpha: float, n: float, out=None,
+                          stream=None):
+    """HSTU attention forward under the target-aware mask: the last
+    num_targets[i] tokens of sequence i are candidates that see the history
+    and themselves only.  num_targets: int32 device tensor of num_seqs entries."""
+    import torch
+    out = _check_tensors(q, k, v, seq_offsets, out)
+    num_seqs = seq_offsets.numel() - 1
+    if (num_targets.dtype != torch.int32 or num_targets.dim() != 1 or
+            num_targets.numel() != num_seqs or not num_targets.is_cuda or
+            not num_targets.is_contiguous()):
+        raise ValueError("num_targets must be a contiguous 1-D int32 GPU tensor of num_seqs entries")
+    T, heads, d = q.shape
+    lib = load_library()
+    st = lib.hstu_attn_fwd_targets(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                   seq_offsets.data_ptr(), num_targets.data_ptr(), num_seqs,
+                                   heads, d, float(alpha), float(n), out.data_ptr(),
+                                   _stream_handle(stream), _dtype_code(q))
+    _check(st, "hstu_attn_fwd_targets")
     return out
 
 

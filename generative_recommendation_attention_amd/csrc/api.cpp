@@ -169,14 +169,11 @@ hstu::SortChoice sort_choice_env() {
     return hstu::SortChoice::AUTO;
 }
 
-}  // namespace
-
-extern "C" {
-
-hstu_status_t hstu_attn_fwd(const void* q, const void* k, const void* v,
-                            const int32_t* seq_offsets, int32_t num_seqs, int32_t heads,
-                            int32_t d, float alpha, float n, void* out, hipStream_t stream,
-                            hstu_dtype_t dtype) {
+// One forward call; num_targets null means the plain causal mask.
+hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
+                            const int32_t* seq_offsets, const int32_t* num_targets,
+                            int32_t num_seqs, int32_t heads, int32_t d, float alpha, float n,
+                            void* out, hipStream_t stream, int dtype) {
     hstu_status_t st = check_args(q, k, v, seq_offsets, num_seqs, heads, d, alpha, n, out, dtype);
     if (st != HSTU_OK || num_seqs == 0) return st;
     int dev = 0;
@@ -209,6 +206,7 @@ hstu_status_t hstu_attn_fwd(const void* q, const void* k, const void* v,
     p.v = v;
     p.out = out;
     p.offsets = seq_offsets;
+    p.num_targets = num_targets;
     p.num_seqs = num_seqs;
     p.heads = heads;
     p.d = d;
@@ -244,6 +242,28 @@ hstu_status_t hstu_attn_fwd(const void* q, const void* k, const void* v,
         if (ctl[hstu::CTL_FLAGS] != 0) return HSTU_ERR_BAD_OFFSETS;
     }
     return HSTU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hstu_status_t hstu_attn_fwd(const void* q, const void* k, const void* v,
+                            const int32_t* seq_offsets, int32_t num_seqs, int32_t heads,
+                            int32_t d, float alpha, float n, void* out, hipStream_t stream,
+                            hstu_dtype_t dtype) {
+    return attn_fwd_call(q, k, v, seq_offsets, nullptr, num_seqs, heads, d, alpha, n, out,
+                         stream, dtype);
+}
+
+hstu_status_t hstu_attn_fwd_targets(const void* q, const void* k, const void* v,
+                                    const int32_t* seq_offsets, const int32_t* num_targets,
+                                    int32_t num_seqs, int32_t heads, int32_t d, float alpha,
+                                    float n, void* out, hipStream_t stream, hstu_dtype_t dtype) {
+    if (num_seqs > 0 && (!num_targets || (reinterpret_cast<uintptr_t>(num_targets) & 3u) != 0))
+        return HSTU_ERR_INVALID_ARG;
+    return attn_fwd_call(q, k, v, seq_offsets, num_targets, num_seqs, heads, d, alpha, n, out,
+                         stream, dtype);
 }
 
 hstu_status_t hstu_attn_fwd_bf16(const void* q, const void* k, const void* v,

@@ -59,6 +59,7 @@ struct KernelArgs {
     const uint16_t* v;
     uint16_t* out;
     const int32_t* offsets;
+    const int32_t* ntgt;   // candidates per sequence (target-aware mask), or null
     WorkList wl;
     int num_seqs;
     int heads;
@@ -202,7 +203,9 @@ __device__ __forceinline__ int vswz(int r) {
     else return (2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1)) & (CHUNKS - 1);
 }
 
-template <typename T, int D, int NW, int QB, int BK, int PF, bool FUSED>
+// TGT: the target-aware mask (a.ntgt non-null); a separate instantiation so
+// that the plain causal form carries none of its registers.
+template <typename T, int D, int NW, int QB, int BK, int PF, bool FUSED, bool TGT>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
     using Cfg = Tile16<T, D, NW, QB, BK, PF>;
     using M = Mfma<T>;
@@ -282,14 +285,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
         const int qtile = __builtin_amdgcn_readfirstlane(it.qtile);
         const int start = __builtin_amdgcn_readfirstlane(a.offsets[seq]);
         const int s = __builtin_amdgcn_readfirstlane(a.offsets[seq + 1]) - start;
+        // Target-aware mask: the last t tokens are candidates, which see the
+        // first `hist` tokens and themselves only (hist = s: plain causal).
+        int hist = s;
+        if constexpr (TGT)
+            hist = s - min(max(__builtin_amdgcn_readfirstlane(a.ntgt[seq]), 0), s);
         const int q0 = qtile * BQ;
         const int kv_end = min(s, q0 + BQ);
         const int n_tiles = (kv_end + BK - 1) / BK;
         const int wr0 = q0 + wv * ROWS_W;                // this wave's first query row
         const bool live = wr0 < s;
-        // Blocks of 32 keys that are entirely below the wave's first row, and
-        // the last block the wave needs.
-        const int full_blocks = live ? wr0 / 32 : 0;
+        // Blocks of 32 keys that are entirely below the wave's first row and
+        // the first candidate (unmasked for every row of the wave), and the
+        // last block the wave needs.
+        const int full_blocks = live ? (TGT ? min(wr0, hist) : wr0) / 32 : 0;
         const int last_block = live ? (min(wr0 + ROWS_W, s) - 1) / 32 : -1;
         const int tiles_a = full_blocks / NKB;             // phase A tiles
         const int tiles_ab = live ? last_block / NKB + 1 : 0;   // phases A and B
@@ -391,17 +400,32 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) o[db][qb] = M::mma(va[db], pb[qb], o[db][qb]);
         };
-        // Block b on or past the diagonal: keys above each query row are zeroed.
+        // Block b on or past the diagonal, or holding candidate keys: scores
+        // of keys a row does not see are zeroed (silu(0) = 0).  Register r of
+        // lane (l32, g) holds key 32b + 8(r/4) + 4g + r%4 of query row
+        // wr0 + 32qb + l32, which sees it iff key <= row and (key < hist or
+        // key == row).
         auto masked_block = [&](int slot, int kb, int b) {
             f32x16 st[QB];
             qk(slot, kb, st);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                // keep key 32b + 8(r/4) + 4g + r%4 <= query wr0 + 32qb + l32
-                const int lim = wr0 + 32 * qb + l32 - 32 * b - 4 * g;
+                // offsets from the lane's first key: the row itself, and the
+                // bound below which keys are seen (min(row, hist); the
+                // condition above is key == row or key < min(row, hist))
+                const int eq = wr0 + 32 * qb + l32 - 32 * b - 4 * g;
+                if constexpr (TGT) {
+                    const int lt = min(wr0 + 32 * qb + l32, hist) - 32 * b - 4 * g;
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    st[qb][r] = (8 * (r >> 2) + (r & 3) <= lim) ? st[qb][r] : 0.0f;
+                    for (int r = 0; r < 16; ++r) {
+                        const int o = 8 * (r >> 2) + (r & 3);
+                        st[qb][r] = (o < lt || o == eq) ? st[qb][r] : 0.0f;
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        st[qb][r] = (8 * (r >> 2) + (r & 3) <= eq) ? st[qb][r] : 0.0f;
+                }
             }
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
@@ -524,7 +548,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
             mma_pv(v1d, p1d);   // the last block's keys 16..31
         }
         int c = tiles_a;
-        // ---- phase B: the tiles holding the wave's diagonal --------------------
+        // ---- phase B: the tiles holding the wave's diagonal (and the first -----
+        // candidate) ------------------------------------------------------------
         // Plain order; the barrier comes after the tile's blocks, since the
         // last one still reads this tile's K.
         for (; c < tiles_ab; ++c) {
@@ -541,7 +566,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
                         weights(st, t, pb);
                         pv(slot, kb, t, pb);
                     }
-                } else if (b <= last_block) {
+                } else if (b <= last_block && (!TGT || 32 * b < hist || 32 * b + 31 >= wr0)) {
+                    // (blocks of candidate keys below the wave's rows are seen
+                    // by none of them)
                     masked_block(slot, kb, b);
                 }
             }
@@ -596,6 +623,7 @@ struct KernelArgsF32 {
     const float* v;
     float* out;
     const int32_t* offsets;
+    const int32_t* ntgt;   // candidates per sequence (target-aware mask), or null
     WorkList wl;
     int num_seqs;
     int heads;
@@ -634,6 +662,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
         const Item it = decode_item(tb, a.num_seqs, H, qx, w);
         const int start = a.offsets[it.seq];
         const int s = a.offsets[it.seq + 1] - start;
+        const int hist = a.ntgt ? s - min(max(a.ntgt[it.seq], 0), s) : s;   // as above
         const int q0 = it.qtile * BQ;
         const int kv_end = min(s, q0 + BQ);
         const int n_tiles = (kv_end + BK - 1) / BK;
@@ -669,9 +698,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
                 *reinterpret_cast<float4*>(vl + r * Cfg::VSTR + c4 * 4) = xv;
             }
             __syncthreads();
-            const bool skip = !wave_live || k0 > wr0 + 31;
+            // Skip tiles no row of the wave sees: past its last row, or all
+            // candidate keys below its first row.
+            const bool skip = !wave_live || k0 > wr0 + 31 || (k0 >= hist && k0 + BK - 1 < wr0);
             if (!skip) {
-                const bool partial = k0 + BK - 1 > wr0;
+                const bool partial = k0 + BK - 1 > wr0 || k0 + BK > hist;
 #pragma unroll
                 for (int kb = 0; kb < BK / 32; ++kb) {
                     f32x16 st = (f32x16){};
@@ -683,7 +714,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
                     for (int r = 0; r < 16; ++r) {
                         const int kvl = kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
                         float p = silu_scaled(st[r] * a.score_scale);
-                        if (partial) p = (k0 + kvl <= my_row) ? p : 0.0f;
+                        if (partial) {
+                            const int key = k0 + kvl;
+                            p = (key <= my_row && (key < hist || key == my_row)) ? p : 0.0f;
+                        }
 #pragma unroll
                         for (int db = 0; db < D / 32; ++db)
                             o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(
@@ -760,18 +794,21 @@ hipError_t launch16(const FwdParams& p, WorkList wl, int grid, hipStream_t strea
     a.v = static_cast<const uint16_t*>(p.v);
     a.out = static_cast<uint16_t*>(p.out);
     a.offsets = p.offsets;
+    a.ntgt = p.num_targets;
     a.wl = wl;
     a.num_seqs = p.num_seqs;
     a.heads = p.heads;
     a.score_scale = -p.alpha * LOG2E;
     a.out_scale = -LN2 / p.n;
-    auto fn = wl.fused ? attn_fwd_mfma16<T, D, NW16, QBlocks<D>::value, KeyTile<D>::value,
-                                         Prefetch<D>::value, true>
-                       : attn_fwd_mfma16<T, D, NW16, QBlocks<D>::value, KeyTile<D>::value,
-                                         Prefetch<D>::value, false>;
+    constexpr int QB = QBlocks<D>::value, BK = KeyTile<D>::value, PF = Prefetch<D>::value;
+    const bool tgt = p.num_targets != nullptr;
+    auto fn = wl.fused ? (tgt ? attn_fwd_mfma16<T, D, NW16, QB, BK, PF, true, true>
+                              : attn_fwd_mfma16<T, D, NW16, QB, BK, PF, true, false>)
+                       : (tgt ? attn_fwd_mfma16<T, D, NW16, QB, BK, PF, false, true>
+                              : attn_fwd_mfma16<T, D, NW16, QB, BK, PF, false, false>);
     if (grid <= 0) {
-        static int cached[2] = {0, 0};
-        int& c = cached[wl.fused ? 1 : 0];
+        static int cached[4] = {0, 0, 0, 0};
+        int& c = cached[(wl.fused ? 1 : 0) + (tgt ? 2 : 0)];
         if (!c) c = resident_grid(fn, NW16 * 64);
         grid = c;
     }
@@ -791,6 +828,7 @@ hipError_t launch_f32(const FwdParams& p, WorkList wl, int grid, hipStream_t str
     a.v = static_cast<const float*>(p.v);
     a.out = static_cast<float*>(p.out);
     a.offsets = p.offsets;
+    a.ntgt = p.num_targets;
     a.wl = wl;
     a.num_seqs = p.num_seqs;
     a.heads = p.heads;

@@ -129,6 +129,7 @@ struct FwdParams {
     const void* v;
     void* out;
     const int32_t* offsets;
+    const int32_t* num_targets;   // candidates per sequence, or null (plain causal)
     int num_seqs;
     int heads;
     int d;

@@ -92,6 +92,26 @@ hstu_status_t hstu_attn_fwd_fp32(const void* q, const void* k, const void* v,
                                  const int32_t* seq_offsets, int32_t num_seqs, int32_t heads,
                                  int32_t d, float alpha, float n, void* out, hipStream_t stream);
 
+/* The forward pass under the target-aware mask of M-FALCON inference (HSTU
+ * paper translation "行动胜于言语…", §3.4 and Appendix H: candidates appended
+ * after a user history are scored in one pass; each candidate attends to the
+ * whole history and to itself, never to the other candidates, Fig. 11).
+ *
+ *   num_targets : device int32[num_seqs]; the last t_i tokens of sequence i are
+ *                 candidates (t_i is clamped to [0, s_i], s_i the length).  With
+ *                 h_i = s_i - t_i, local row r keeps key c iff c <= r and
+ *                 (c < h_i or c == r).  Rows r < h_i (the history) see the plain
+ *                 causal mask; t_i = 0 gives hstu_attn_fwd exactly.
+ *
+ * All other parameters, layouts, element types and errors are those of
+ * hstu_attn_fwd; num_targets is caller-owned, read on the device only, and
+ * must be non-null and 4-byte aligned when num_seqs > 0 (else
+ * HSTU_ERR_INVALID_ARG). */
+hstu_status_t hstu_attn_fwd_targets(const void* q, const void* k, const void* v,
+                                    const int32_t* seq_offsets, const int32_t* num_targets,
+                                    int32_t num_seqs, int32_t heads, int32_t d, float alpha,
+                                    float n, void* out, hipStream_t stream, hstu_dtype_t dtype);
+
 /* Checks device offsets synchronously: off[0] == 0 and non-decreasing.  Writes
  * T = off[num_seqs] to *total (may be NULL).  Returns HSTU_OK or
  * HSTU_ERR_BAD_OFFSETS; synchronises `stream`. */

@@ -77,6 +77,32 @@ def test_typed_entry_points_check_arguments(lib):
         assert fn(None, None, None, None, 0, 1, 64, 0.1, 1.0, None, None) == hstu.HSTU_OK
 
 
+def _call_targets(lib, tg=48, **kw):
+    a = dict(q=16, k=16, v=16, off=16, num_seqs=1, heads=1, d=64, alpha=0.1, n=1.0, out=32,
+             dtype=hstu.HSTU_BF16)
+    a.update(kw)
+    return lib.hstu_attn_fwd_targets(a["q"], a["k"], a["v"], a["off"], tg, a["num_seqs"],
+                                     a["heads"], a["d"], a["alpha"], a["n"], a["out"], None,
+                                     a["dtype"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(tg=None), hstu.HSTU_ERR_INVALID_ARG),     # candidate counts missing
+    (dict(tg=50), hstu.HSTU_ERR_INVALID_ARG),       # misaligned counts
+    (dict(q=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(d=96), hstu.HSTU_ERR_UNSUPPORTED),
+    (dict(n=0.0), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(out=16), hstu.HSTU_ERR_INVALID_ARG),
+])
+def test_targets_argument_checks(lib, kw, status):
+    assert _call_targets(lib, **kw) == status
+
+
+def test_targets_empty_batch_is_a_no_op(lib):
+    assert _call_targets(lib, tg=None, q=None, k=None, v=None, off=None, out=None,
+                         num_seqs=0) == hstu.HSTU_OK
+
+
 def test_status_strings(lib):
     for st in (0, -1, -2, -3, -4, -5):
         assert lib.hstu_status_string(st)

@@ -95,6 +95,8 @@ class Case:
     alpha: float  # the float32 value handed to the kernel
     n: float  # the float32 value handed to the kernel
     description: str = ""
+    # candidates at the end of each sequence (target-aware mask), or None
+    num_targets: Optional[np.ndarray] = None
 
     @property
     def num_seqs(self) -> int:
@@ -210,3 +212,34 @@ def workload(num: int, values: bool = True) -> Case:
     return Case(name=f"w{num}", dtype=dtype, heads=heads, d=d, offsets=offsets,
                 q=vals[0], k=vals[1], v=vals[2], alpha=f32(alpha), n=f32(n_rule(lengths)),
                 description=WORKLOADS[num])
+
+
+# ---------------------------------------------------------------------------
+# Ranking with appended candidates (M-FALCON micro-batches, HSTU paper
+# translation §3.4 and Appendix H: one micro-batch of b_m candidates follows
+# each user's history; Fig. 13 uses b_m = 1024).  Same token count, heads, d
+# and scalars as the 16 x 4096 causal workload: 16 users, history 3072,
+# 1024 candidates each.  Seed 1100.
+# ---------------------------------------------------------------------------
+
+TARGETS_DESCRIPTION = ("target-aware, 16 users x (3072 history + 1024 candidates), "
+                       "heads 4, d 64, bf16")
+
+
+def targets_workload(values: bool = True, history: int = 3072, candidates: int = 1024,
+                     users: int = 16) -> Case:
+    rng = np.random.default_rng(1100)
+    heads, d, dtype = 4, 64, "bf16"
+    lengths = [history + candidates] * users
+    offsets = offsets_from_lengths(lengths)
+    T = int(offsets[-1])
+    if values:
+        vals = [cast_values(rng.standard_normal((T, heads, d), dtype=np.float32), dtype)
+                for _ in range(3)]
+    else:
+        empty = cast_values(np.zeros((0, heads, d), np.float32), dtype)
+        vals = [empty, empty, empty]
+    return Case(name="targets", dtype=dtype, heads=heads, d=d, offsets=offsets,
+                q=vals[0], k=vals[1], v=vals[2], alpha=f32(1.0 / 8.0),
+                n=f32(float(history + candidates)), description=TARGETS_DESCRIPTION,
+                num_targets=np.full(users, candidates, dtype=np.int32))
