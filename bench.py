@@ -44,11 +44,11 @@ METRIC_TARGETS = "HSTU target-aware attn fwd useful TFLOP/s (M-FALCON mask)"
 # source the bench reports traffic as null.
 TRAFFIC = {
     "kernel_source": "generative_recommendation_attention_amd/csrc/attn_fwd.hip",
-    "kernel_sha256": "848f8c674f0ae1520e49a0f2726438f7d084b75487946f755653568d8749c7bd",
+    "kernel_sha256": "7d5a1851dbe7f040b4b1212d26300bb444fa49bd3f67216a4e434d62b4c1378e",
     "fetch_scale": 2.0,
     "write_scale": 1.0,
-    "fetch_kib": {2: 95227.2},
-    "write_kib": {2: 37937.8},
+    "fetch_kib": {2: 102957.0},
+    "write_kib": {2: 37944.3},
 }
 
 
