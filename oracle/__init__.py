@@ -21,6 +21,11 @@ HSTU paper translation (§3.4, Appendix H, Algorithm 1 and Fig. 11): the last
 t tokens of a sequence are candidates that see the history and themselves
 only.  ``num_targets=None`` is the plain causal mask.
 
+``fwd_cached`` / ``rows_cached`` are the later micro-batches of the same
+algorithm (Appendix H, the encoder-level K/V cache): candidates with their own
+q, k, v attend to a cached history's K and V plus themselves, each request's
+history and candidates given by their own offsets.
+
 Parity status: pinned.  The test suite ties these functions to closed forms
 (hand-worked 2- and 3-token cases), to identities that reduce to textbook
 operations (sign-flip -> masked GEMM, constant rows -> prefix sum, row 0),
@@ -77,6 +82,13 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                              ctypes.c_int, ctypes.c_int, f64, f64, vp, vp, i64,
                                              vp]
     lib.hstu_oracle_rows_targets.restype = ctypes.c_int
+    lib.hstu_oracle_fwd_cached.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, vp, vp,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, f64, f64, vp]
+    lib.hstu_oracle_fwd_cached.restype = ctypes.c_int
+    lib.hstu_oracle_rows_cached.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, vp, vp,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_int, f64, f64,
+                                            vp, vp, i64, vp]
+    lib.hstu_oracle_rows_cached.restype = ctypes.c_int
     lib.hstu_oracle_threads.argtypes = []
     lib.hstu_oracle_threads.restype = ctypes.c_int
     _libs[path] = lib
@@ -140,6 +152,59 @@ def rows(q, k, v, offsets, heads: int, d: int, alpha: float, n: float, dtype: st
                                       None if tg is None else _ptr(tg), len(off) - 1, heads, d,
                                       float(alpha), float(n), _ptr(tok), _ptr(hd), len(tok),
                                       _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle rejected the sampled rows")
+    return out
+
+
+def _cached_args(q, k, v, k_cache, v_cache, cand_offsets, hist_offsets, heads, d, dtype):
+    q, k, v, kc, vc = (_storage(a, dtype) for a in (q, k, v, k_cache, v_cache))
+    coff = np.ascontiguousarray(cand_offsets, dtype=np.int32)
+    hoff = np.ascontiguousarray(hist_offsets, dtype=np.int32)
+    if coff.shape != hoff.shape or len(coff) < 1:
+        raise ValueError("candidate and history offsets need num_seqs + 1 entries each")
+    Tc, Th = int(coff[-1]), int(hoff[-1])
+    for a in (q, k, v):
+        if a.size < Tc * heads * d:
+            raise ValueError("q/k/v smaller than the candidate offsets imply")
+    for a in (kc, vc):
+        if a.size < Th * heads * d:
+            raise ValueError("cached k/v smaller than the history offsets imply")
+    return q, k, v, kc, vc, coff, hoff
+
+
+def fwd_cached(q, k, v, cand_offsets, k_cache, v_cache, hist_offsets, heads: int, d: int,
+               alpha: float, n: float, dtype: str,
+               lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+    """Full fp64 output (Tc, heads, d) of the candidates against a cached history."""
+    lib = lib or load()
+    q, k, v, kc, vc, coff, hoff = _cached_args(q, k, v, k_cache, v_cache, cand_offsets,
+                                               hist_offsets, heads, d, dtype)
+    out = np.zeros((int(coff[-1]), heads, d), dtype=np.float64)
+    rc = lib.hstu_oracle_fwd_cached(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc),
+                                    _DTYPE_CODE[dtype], _ptr(coff), _ptr(hoff), len(coff) - 1,
+                                    heads, d, float(alpha), float(n), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments (malformed offsets or sizes)")
+    return out
+
+
+def rows_cached(q, k, v, cand_offsets, k_cache, v_cache, hist_offsets, heads: int, d: int,
+                alpha: float, n: float, dtype: str, tokens, head_ids,
+                lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+    """fp64 outputs (m, d) of candidate rows tokens[m] (global), heads head_ids[m]."""
+    lib = lib or load()
+    q, k, v, kc, vc, coff, hoff = _cached_args(q, k, v, k_cache, v_cache, cand_offsets,
+                                               hist_offsets, heads, d, dtype)
+    tok = np.ascontiguousarray(tokens, dtype=np.int64)
+    hd = np.ascontiguousarray(head_ids, dtype=np.int32)
+    if tok.shape != hd.shape:
+        raise ValueError("tokens and head_ids differ in length")
+    out = np.zeros((len(tok), d), dtype=np.float64)
+    rc = lib.hstu_oracle_rows_cached(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc),
+                                     _DTYPE_CODE[dtype], _ptr(coff), _ptr(hoff), len(coff) - 1,
+                                     heads, d, float(alpha), float(n), _ptr(tok), _ptr(hd),
+                                     len(tok), _ptr(out))
     if rc != 0:
         raise ValueError("oracle rejected the sampled rows")
     return out

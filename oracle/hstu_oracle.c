@@ -29,6 +29,17 @@
  *     history length = s - t.  The mask stays multiplicative 0/1 after SiLU
  *     (the -inf of the pseudo-code is for softmax models).
  *
+ * Cached history (the later micro-batches of M-FALCON), for the *_cached
+ * entry points:
+ *   - HSTU paper translation, Appendix H (the encoder-level cache and
+ *     Algorithm 1's loop over micro-batches): K and V of the n history tokens
+ *     are kept from an earlier pass; a micro-batch then computes Q, K, V for
+ *     its b_m candidates only and attends, under the mask above, to the cached
+ *     history plus itself.  Written out, candidate j of request i gets
+ *       (1/n) * ( sum_{c < h_i} silu(alpha <q_j, kc_c>) vc_c
+ *                 + silu(alpha <q_j, k_j>) v_j ),
+ *     kc, vc the cached history rows of request i, h_i their count.
+ *
  * Readings taken where the pages are silent (each listed in the design notes):
  *   - alpha multiplies the scores before SiLU; n is a caller-given scalar;
  *   - the mask multiplies after SiLU (0/1), so masked terms are exactly 0;
@@ -154,6 +165,41 @@ static void one_row(const void* q, const void* k, const void* v, int dtype,
     for (int e = 0; e < d; ++e) acc[e] *= inv_n;
 }
 
+/* One candidate row against a cached history: history rows [hs0, hs0 + hlen)
+ * of kc/vc, the candidate at global row `row` of q/k/v.  Result in acc[0..d). */
+static void cached_row(const void* q, const void* k, const void* v, const void* kc,
+                       const void* vc, int dtype, int64_t row, int64_t hs0, int64_t hlen,
+                       int heads, int d, int h, double alpha, double n, double* qrow,
+                       double* acc) {
+    const int64_t row_stride = (int64_t)heads * d;
+    const int64_t hoff = (int64_t)h * d;
+    for (int e = 0; e < d; ++e) {
+        qrow[e] = load_elem(q, dtype, row * row_stride + hoff + e);
+        acc[e] = 0.0;
+    }
+    int64_t c_end = hlen;
+#if ORACLE_PLANT == 9
+    c_end = hlen - 1; /* planted: last history key missed */
+#endif
+    for (int64_t c = 0; c < c_end; ++c) {
+        double dot = 0.0;
+        for (int e = 0; e < d; ++e)
+            dot += qrow[e] * load_elem(kc, dtype, (hs0 + c) * row_stride + hoff + e);
+        double w = silu(alpha * dot);
+        for (int e = 0; e < d; ++e)
+            acc[e] += w * load_elem(vc, dtype, (hs0 + c) * row_stride + hoff + e);
+    }
+    /* the candidate's own key and value */
+    double dot = 0.0;
+    for (int e = 0; e < d; ++e) dot += qrow[e] * load_elem(k, dtype, row * row_stride + hoff + e);
+    double w = silu(alpha * dot);
+#if ORACLE_PLANT == 10
+    w = 0.0; /* planted: candidate misses itself */
+#endif
+    for (int e = 0; e < d; ++e) acc[e] += w * load_elem(v, dtype, row * row_stride + hoff + e);
+    for (int e = 0; e < d; ++e) acc[e] /= n;
+}
+
 /* ---- entry points ---------------------------------------------------------- */
 
 /* Full output: out is fp64 (T, heads, d), T = off[num_seqs].  ntgt is null
@@ -235,6 +281,72 @@ int hstu_oracle_rows(const void* q, const void* k, const void* v, int dtype,
                      int64_t count, double* out_rows) {
     return hstu_oracle_rows_targets(q, k, v, dtype, off, 0, num_seqs, heads, d, alpha, n, tok,
                                     hd, count, out_rows);
+}
+
+static int offsets_ok(const int32_t* off, int num_seqs) {
+    if (num_seqs > 0 && off[0] != 0) return 0;
+    for (int i = 0; i < num_seqs; ++i)
+        if (off[i + 1] < off[i]) return 0;
+    return 1;
+}
+
+/* Cached-history form: q, k, v, out are the candidates (Tc, heads, d) with
+ * offsets coff; kc, vc the cached history (Th, heads, d) with offsets hoff;
+ * request i has coff[i+1]-coff[i] candidates and hoff[i+1]-hoff[i] history
+ * rows.  out is fp64.  Returns 0, or -1 on malformed offsets.  d <= 1024. */
+int hstu_oracle_fwd_cached(const void* q, const void* k, const void* v, const void* kc,
+                           const void* vc, int dtype, const int32_t* coff, const int32_t* hoff,
+                           int num_seqs, int heads, int d, double alpha, double n, double* out) {
+    if (num_seqs < 0 || heads < 1 || d < 1 || d > 1024) return -1;
+    if (!offsets_ok(coff, num_seqs) || !offsets_ok(hoff, num_seqs)) return -1;
+    const int64_t row_stride = (int64_t)heads * d;
+    const int64_t items = (int64_t)num_seqs * heads;
+#pragma omp parallel
+    {
+        double qrow[1024], acc[1024];
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t it = 0; it < items; ++it) {
+            int i = (int)(it / heads), h = (int)(it % heads);
+            for (int64_t row = coff[i]; row < coff[i + 1]; ++row) {
+                cached_row(q, k, v, kc, vc, dtype, row, hoff[i], (int64_t)hoff[i + 1] - hoff[i],
+                           heads, d, h, alpha, n, qrow, acc);
+                double* o = out + row * row_stride + (int64_t)h * d;
+                for (int e = 0; e < d; ++e) o[e] = acc[e];
+            }
+        }
+    }
+    return 0;
+}
+
+/* Sampled rows of the cached-history form: out_rows[m, 0..d) is candidate
+ * row tok[m] (global index into q), head hd[m].  Returns 0, or -1 on a token
+ * or head out of range or malformed offsets. */
+int hstu_oracle_rows_cached(const void* q, const void* k, const void* v, const void* kc,
+                            const void* vc, int dtype, const int32_t* coff, const int32_t* hoff,
+                            int num_seqs, int heads, int d, double alpha, double n,
+                            const int64_t* tok, const int32_t* hd, int64_t count,
+                            double* out_rows) {
+    if (num_seqs < 1 || heads < 1 || d < 1 || d > 1024) return -1;
+    if (!offsets_ok(coff, num_seqs) || !offsets_ok(hoff, num_seqs)) return -1;
+    int64_t T = coff[num_seqs];
+    for (int64_t m = 0; m < count; ++m)
+        if (tok[m] < 0 || tok[m] >= T || hd[m] < 0 || hd[m] >= heads) return -1;
+#pragma omp parallel
+    {
+        double qrow[1024];
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t m = 0; m < count; ++m) {
+            int lo = 0, hi = num_seqs - 1;   /* largest i with coff[i] <= tok */
+            while (lo < hi) {
+                int mid = (lo + hi + 1) / 2;
+                if (coff[mid] <= tok[m]) lo = mid; else hi = mid - 1;
+            }
+            cached_row(q, k, v, kc, vc, dtype, tok[m], hoff[lo],
+                       (int64_t)hoff[lo + 1] - hoff[lo], heads, d, hd[m], alpha, n, qrow,
+                       out_rows + m * (int64_t)d);
+        }
+    }
+    return 0;
 }
 
 /* Number of threads an OpenMP parallel region here uses (for reporting). */
