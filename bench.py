@@ -15,7 +15,9 @@ workload.
 
 --targets times hstu_attn_fwd_targets instead, on 16 users x (3072 history +
 1024 candidates) (the target-aware mask of M-FALCON ranking, HSTU paper
-translation Appendix H); useful FLOPs then count the pairs that mask keeps.
+translation Appendix H); useful FLOPs then count the pairs that mask keeps.  --cached times
+hstu_attn_fwd_cached on 16 users x (3072 cached history rows, 1024 candidates)
+(M-FALCON's later micro-batches): t (h + 1) pairs per request.
 """
 from __future__ import annotations
 
@@ -36,6 +38,7 @@ PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
 PEAK_HBM_GBS = 8000.0
 METRIC = "HSTU attn fwd useful TFLOP/s, % bf16 MFMA peak; ms at QKV(16,4,4096,64)"
 METRIC_TARGETS = "HSTU target-aware attn fwd useful TFLOP/s (M-FALCON mask)"
+METRIC_CACHED = "HSTU cached-history attn fwd useful TFLOP/s (M-FALCON micro-batch)"
 # HBM traffic per dispatch of the attention kernel, from two rocprofv3 --pmc
 # runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
 # same counter reads for a plain 1 GiB device copy (bench.py --copy-calibrate):
@@ -87,6 +90,37 @@ def seen_pairs(case) -> float:
     return float(np.sum(h * (h + 1.0) / 2.0 + t * (h + 1.0)))
 
 
+def cpu_baseline_cached(cc, budget_s: float):
+    """The oracle's cached-history form on whole requests, in input order,
+    until about budget_s of wall time has been spent."""
+    import oracle
+    lib = oracle.load()
+    threads = oracle.threads(lib)
+    c = cc.cand
+    per_call = max(1, -(-threads // c.heads))
+    done_flops, done_s, seqs, i = 0.0, 0.0, 0, 0
+    while i < c.num_seqs and done_s < budget_s:
+        j = min(c.num_seqs, i + per_call)
+        a, b = int(c.offsets[i]), int(c.offsets[j])
+        ha, hb = int(cc.hist_offsets[i]), int(cc.hist_offsets[j])
+        t0 = time.perf_counter()
+        oracle.fwd_cached(c.q[a:b], c.k[a:b], c.v[a:b], c.offsets[i:j + 1] - c.offsets[i],
+                          cc.k_cache[ha:hb], cc.v_cache[ha:hb],
+                          cc.hist_offsets[i:j + 1] - cc.hist_offsets[i], c.heads, c.d, c.alpha,
+                          c.n, c.dtype, lib=lib)
+        done_s += time.perf_counter() - t0
+        t = c.lengths[i:j].astype(np.float64)
+        h = cc.hist_lengths[i:j].astype(np.float64)
+        done_flops += float(np.sum(4.0 * c.heads * c.d * t * (h + 1.0)))
+        seqs += j - i
+        i = j
+    return {"value": done_flops / done_s / 1e12, "unit": "TFLOP/s",
+            "cores": min(threads, per_call * c.heads), "kind": "oracle",
+            "sample": f"{seqs} of {c.num_seqs} requests, all heads; fp64 loop oracle "
+                      f"(OpenMP over (request, head)), {done_s:.1f} s wall, "
+                      f"{threads} threads available"}
+
+
 def cpu_baseline(case, budget_s: float):
     """Time the oracle on whole sequences of the workload (all heads).  Each
     oracle call takes enough sequences to give every OpenMP thread a
@@ -132,6 +166,9 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--targets", action="store_true",
                     help="time the target-aware forward on 16 x (3072 history + 1024 candidates)")
+    ap.add_argument("--cached", action="store_true",
+                    help="time the cached-history forward on 16 x (3072 cached rows, "
+                         "1024 candidates)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibrate", action="store_true",
@@ -157,12 +194,32 @@ def main() -> int:
         print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
                           "copies": 3}), flush=True)
         return 0
-    case = workloads.targets_workload() if args.targets else workloads.workload(args.workload)
+    cc = None
+    if args.cached:
+        cc = workloads.cached_workload()
+        case = cc.cand
+    elif args.targets:
+        case = workloads.targets_workload()
+    else:
+        case = workloads.workload(args.workload)
     q, k, v, off = to_device(case)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
     flops = 4.0 * case.heads * case.d * seen_pairs(case)
-    if args.targets:
+    alg_bytes = case.algorithmic_bytes()
+    if args.cached:
+        hist_case = workloads.Case(name="", dtype=case.dtype, heads=case.heads, d=case.d,
+                                   offsets=cc.hist_offsets, q=cc.k_cache, k=cc.k_cache,
+                                   v=cc.v_cache, alpha=case.alpha, n=case.n)
+        kc, vc, hoff = to_device(hist_case)[1:]
+        t = case.lengths.astype(np.float64)
+        flops = float(np.sum(4.0 * case.heads * case.d * t * (cc.hist_lengths + 1.0)))
+        elt = 4 if case.dtype == "fp32" else 2
+        alg_bytes += 2.0 * elt * cc.k_cache.size + 4 * (case.num_seqs + 1)
+
+        def call():
+            hstu.hstu_attn_fwd_cached(q, k, v, off, kc, vc, hoff, case.alpha, case.n, out=out)
+    elif args.targets:
         tg = torch.from_numpy(case.num_targets.astype(np.int32)).cuda()
 
         def call():
@@ -195,21 +252,21 @@ def main() -> int:
     sched_ms = kt.sched_ms / max(1, kt.calls)
     achieved = flops / (attn_ms * 1e-3) / 1e12
     peak = PEAK_MFMA_TFLOPS[case.dtype]
-    traffic = None if args.targets else traffic_bytes(args.workload)
+    traffic = None if (args.targets or args.cached) else traffic_bytes(args.workload)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel": "attn_fwd_mfma16" if case.dtype != "fp32" else "attn_fwd_mfma_f32",
                 "kernel_ms": round(attn_ms, 5), "sched_kernel_ms": round(sched_ms, 5),
-                "hbm_frac": round(case.algorithmic_bytes() / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                                  4)}
+                "hbm_frac": round(alg_bytes / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
     cpu = None
     if args.cpu_budget > 0:
-        cpu = cpu_baseline(case, args.cpu_budget)
+        cpu = (cpu_baseline_cached(cc, args.cpu_budget) if args.cached else
+               cpu_baseline(case, args.cpu_budget))
 
     L = case.lengths
     line = {
-        "metric": METRIC_TARGETS if args.targets else METRIC,
+        "metric": (METRIC_CACHED if args.cached else METRIC_TARGETS if args.targets else METRIC),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -226,6 +283,7 @@ def main() -> int:
                    "total_tokens": case.total, "max_seq_len": int(L.max()), "heads": case.heads,
                    "d": case.d, "alpha": case.alpha, "n": case.n,
                    **({"candidates_per_seq": int(case.num_targets[0])} if args.targets else {}),
+                   **({"cached_history_per_seq": int(cc.hist_lengths[0])} if args.cached else {}),
                    "useful_gflop": round(flops / 1e9, 3)},
         "roofline": roofline,
         "cpu_baseline": cpu,

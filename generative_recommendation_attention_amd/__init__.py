@@ -31,7 +31,7 @@ HSTU_BF16, HSTU_FP16, HSTU_FP32 = 0, 1, 2
 
 # Every symbol include/hstu.h declares.
 EXPORTS = ("hstu_attn_fwd", "hstu_attn_fwd_bf16", "hstu_attn_fwd_fp16", "hstu_attn_fwd_fp32",
-           "hstu_attn_fwd_targets", "hstu_validate_offsets", "hstu_status_string", "hstu_last_hip_error",
+           "hstu_attn_fwd_targets", "hstu_attn_fwd_cached", "hstu_validate_offsets", "hstu_status_string", "hstu_last_hip_error",
            "hstu_release_workspace", "hstu_profile_enable", "hstu_profile_read")
 
 
@@ -74,6 +74,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hstu_attn_fwd_targets.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp,
                                           ctypes.c_int]
     lib.hstu_attn_fwd_targets.restype = ctypes.c_int
+    lib.hstu_attn_fwd_cached.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, vp,
+                                         vp, ctypes.c_int]
+    lib.hstu_attn_fwd_cached.restype = ctypes.c_int
     lib.hstu_validate_offsets.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_int64), vp]
     lib.hstu_validate_offsets.restype = ctypes.c_int
     lib.hstu_status_string.argtypes = [ctypes.c_int]
@@ -167,6 +170,42 @@ def hstu_attn_fwd_targets(q, k, v, seq_offsets, num_targets, alpha: float, n: fl
                                    heads, d, float(alpha), float(n), out.data_ptr(),
                                    _stream_handle(stream), _dtype_code(q))
     _check(st, "hstu_attn_fwd_targets")
+    return out
+
+
+def hstu_attn_fwd_cached(q, k, v, cand_offsets, k_cache, v_cache, hist_offsets, alpha: float,
+                         n: float, out=None, stream=None):
+    """Candidates (q, k, v: (T_cand, heads, d), offsets cand_offsets) scored
+    against a cached history (k_cache, v_cache: (T_hist, heads, d), offsets
+    hist_offsets): each candidate sees its request's history and itself."""
+    import torch
+    out = _check_tensors(q, k, v, cand_offsets, out)
+    num_seqs = cand_offsets.numel() - 1
+    T, heads, d = q.shape
+    for t in (k_cache, v_cache):
+        if (t.dim() != 3 or t.shape[1:] != q.shape[1:] or t.dtype != q.dtype or not t.is_cuda
+                or not t.is_contiguous()):
+            raise ValueError("k_cache and v_cache must be contiguous GPU tensors "
+                             "(T_hist, heads, d) of q's element type")
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must share one shape")
+    if (hist_offsets.dtype != torch.int32 or hist_offsets.dim() != 1 or
+            hist_offsets.numel() != num_seqs + 1 or not hist_offsets.is_cuda or
+            not hist_offsets.is_contiguous()):
+        raise ValueError("hist_offsets must be a contiguous 1-D int32 GPU tensor of "
+                         "num_seqs + 1 entries")
+    lib = load_library()
+    if T == 0:
+        return out   # no candidate rows: nothing to compute
+    empty_cache = k_cache.numel() == 0   # no history at all: the library takes null caches
+    st = lib.hstu_attn_fwd_cached(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                  cand_offsets.data_ptr(),
+                                  None if empty_cache else k_cache.data_ptr(),
+                                  None if empty_cache else v_cache.data_ptr(),
+                                  hist_offsets.data_ptr(), num_seqs, heads,
+                                  d, float(alpha), float(n), out.data_ptr(),
+                                  _stream_handle(stream), _dtype_code(q))
+    _check(st, "hstu_attn_fwd_cached")
     return out
 
 

@@ -169,11 +169,20 @@ hstu::SortChoice sort_choice_env() {
     return hstu::SortChoice::AUTO;
 }
 
-// One forward call; num_targets null means the plain causal mask.
+// Extra inputs of the masked forms: candidate counts (target-aware mask), or
+// a cached history (K, V and their offsets); all null for the causal mask.
+struct MaskInputs {
+    const int32_t* num_targets = nullptr;
+    const void* k_cache = nullptr;
+    const void* v_cache = nullptr;
+    const int32_t* hist_offsets = nullptr;
+};
+
+// One forward call.
 hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
-                            const int32_t* seq_offsets, const int32_t* num_targets,
-                            int32_t num_seqs, int32_t heads, int32_t d, float alpha, float n,
-                            void* out, hipStream_t stream, int dtype) {
+                            const int32_t* seq_offsets, const MaskInputs& mi, int32_t num_seqs,
+                            int32_t heads, int32_t d, float alpha, float n, void* out,
+                            hipStream_t stream, int dtype) {
     hstu_status_t st = check_args(q, k, v, seq_offsets, num_seqs, heads, d, alpha, n, out, dtype);
     if (st != HSTU_OK || num_seqs == 0) return st;
     int dev = 0;
@@ -206,7 +215,10 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
     p.v = v;
     p.out = out;
     p.offsets = seq_offsets;
-    p.num_targets = num_targets;
+    p.num_targets = mi.num_targets;
+    p.k_cache = mi.k_cache;
+    p.v_cache = mi.v_cache;
+    p.hist_offsets = mi.hist_offsets;
     p.num_seqs = num_seqs;
     p.heads = heads;
     p.d = d;
@@ -252,7 +264,7 @@ hstu_status_t hstu_attn_fwd(const void* q, const void* k, const void* v,
                             const int32_t* seq_offsets, int32_t num_seqs, int32_t heads,
                             int32_t d, float alpha, float n, void* out, hipStream_t stream,
                             hstu_dtype_t dtype) {
-    return attn_fwd_call(q, k, v, seq_offsets, nullptr, num_seqs, heads, d, alpha, n, out,
+    return attn_fwd_call(q, k, v, seq_offsets, MaskInputs{}, num_seqs, heads, d, alpha, n, out,
                          stream, dtype);
 }
 
@@ -262,8 +274,30 @@ hstu_status_t hstu_attn_fwd_targets(const void* q, const void* k, const void* v,
                                     float n, void* out, hipStream_t stream, hstu_dtype_t dtype) {
     if (num_seqs > 0 && (!num_targets || (reinterpret_cast<uintptr_t>(num_targets) & 3u) != 0))
         return HSTU_ERR_INVALID_ARG;
-    return attn_fwd_call(q, k, v, seq_offsets, num_targets, num_seqs, heads, d, alpha, n, out,
-                         stream, dtype);
+    MaskInputs mi;
+    mi.num_targets = num_targets;
+    return attn_fwd_call(q, k, v, seq_offsets, mi, num_seqs, heads, d, alpha, n, out, stream,
+                         dtype);
+}
+
+hstu_status_t hstu_attn_fwd_cached(const void* q, const void* k, const void* v,
+                                   const int32_t* cand_offsets, const void* k_cache,
+                                   const void* v_cache, const int32_t* hist_offsets,
+                                   int32_t num_seqs, int32_t heads, int32_t d, float alpha,
+                                   float n, void* out, hipStream_t stream, hstu_dtype_t dtype) {
+    if (num_seqs > 0) {
+        // Both caches null: no request has a history (T_hist = 0).
+        if (!hist_offsets || (!k_cache) != (!v_cache)) return HSTU_ERR_INVALID_ARG;
+        if (!aligned16(k_cache) || !aligned16(v_cache)) return HSTU_ERR_INVALID_ARG;
+        if ((reinterpret_cast<uintptr_t>(hist_offsets) & 3u) != 0) return HSTU_ERR_INVALID_ARG;
+        if (out == k_cache || out == v_cache) return HSTU_ERR_INVALID_ARG;
+    }
+    MaskInputs mi;
+    mi.k_cache = k_cache;
+    mi.v_cache = v_cache;
+    mi.hist_offsets = hist_offsets;
+    return attn_fwd_call(q, k, v, cand_offsets, mi, num_seqs, heads, d, alpha, n, out, stream,
+                         dtype);
 }
 
 hstu_status_t hstu_attn_fwd_bf16(const void* q, const void* k, const void* v,

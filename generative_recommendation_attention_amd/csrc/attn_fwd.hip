@@ -60,12 +60,28 @@ struct KernelArgs {
     uint16_t* out;
     const int32_t* offsets;
     const int32_t* ntgt;   // candidates per sequence (target-aware mask), or null
+    const uint16_t* kc;    // cached history K, V (MASK_CACHED), or null
+    const uint16_t* vc;
+    const int32_t* hoff;   // history offsets (MASK_CACHED), or null
     WorkList wl;
     int num_seqs;
     int heads;
     float score_scale;  // -alpha * log2(e)
     float out_scale;    // -ln(2) / n
 };
+
+// Which keys a query row sees.
+//  CAUSAL : key <= row.
+//  TARGETS: the last t tokens of a sequence are candidates that see the
+//           history and themselves only: key <= row and (key < hist or
+//           key == row), hist = s - t.
+//  CACHED : the query rows are candidates whose history K/V come from a
+//           cache.  The kernel works on a virtual sequence: the history
+//           padded with zero rows to a whole number of key tiles (`hist`
+//           keys, read from the cache), then the candidates (read from k, v,
+//           rows hist.. of the virtual sequence); the mask is TARGETS' with
+//           that hist.  Zero keys and values add exactly nothing.
+enum : int { MASK_CAUSAL = 0, MASK_TARGETS = 1, MASK_CACHED = 2 };
 
 template <typename T>
 struct Mfma;
@@ -203,10 +219,11 @@ __device__ __forceinline__ int vswz(int r) {
     else return (2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1)) & (CHUNKS - 1);
 }
 
-// TGT: the target-aware mask (a.ntgt non-null); a separate instantiation so
-// that the plain causal form carries none of its registers.
-template <typename T, int D, int NW, int QB, int BK, int PF, bool FUSED, bool TGT>
+// MASK: one of the MASK_* modes; separate instantiations, so that the plain
+// causal form carries none of the other modes' registers.
+template <typename T, int D, int NW, int QB, int BK, int PF, bool FUSED, int MASK>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
+    constexpr bool TGT = MASK != MASK_CAUSAL;    // hist-based mask
     using Cfg = Tile16<T, D, NW, QB, BK, PF>;
     using M = Mfma<T>;
     using v8 = typename M::v8;
@@ -284,15 +301,29 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
         const int head = __builtin_amdgcn_readfirstlane(it.head);
         const int qtile = __builtin_amdgcn_readfirstlane(it.qtile);
         const int start = __builtin_amdgcn_readfirstlane(a.offsets[seq]);
-        const int s = __builtin_amdgcn_readfirstlane(a.offsets[seq + 1]) - start;
-        // Target-aware mask: the last t tokens are candidates, which see the
-        // first `hist` tokens and themselves only (hist = s: plain causal).
-        int hist = s;
-        if constexpr (TGT)
-            hist = s - min(max(__builtin_amdgcn_readfirstlane(a.ntgt[seq]), 0), s);
-        const int q0 = qtile * BQ;
+        const int len = __builtin_amdgcn_readfirstlane(a.offsets[seq + 1]) - start;
+        // s: length of the (virtual) sequence; hist: keys below it are seen
+        // by every later row (s for the causal mask); shift: virtual row of
+        // the first query row.
+        int s = len, hist = len, shift = 0, hstart = 0, hlen = 0;
+        if constexpr (MASK == MASK_TARGETS)
+            hist = len - min(max(__builtin_amdgcn_readfirstlane(a.ntgt[seq]), 0), len);
+        if constexpr (MASK == MASK_CACHED) {
+            hstart = __builtin_amdgcn_readfirstlane(a.hoff[seq]);
+            hlen = max(__builtin_amdgcn_readfirstlane(a.hoff[seq + 1]) - hstart, 0);
+            hist = (hlen + BK - 1) / BK * BK;
+            shift = hist;
+            s = hist + len;
+        }
+        const int q0 = shift + qtile * BQ;
         const int kv_end = min(s, q0 + BQ);
         const int n_tiles = (kv_end + BK - 1) / BK;
+        // Key tiles that hold only candidates below the workgroup's first row
+        // are seen by none of its rows: the tile sequence jumps over them.
+        // Loop tile c is key tile c below nh and c + jump from there on.
+        const int nh = TGT ? (hist + BK - 1) / BK : n_tiles;
+        const int jump = TGT ? max(q0 / BK - nh, 0) : 0;
+        const int n_iter = n_tiles - jump;
         const int wr0 = q0 + wv * ROWS_W;                // this wave's first query row
         const bool live = wr0 < s;
         // Blocks of 32 keys that are entirely below the wave's first row and
@@ -300,20 +331,35 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
         // last block the wave needs.
         const int full_blocks = live ? (TGT ? min(wr0, hist) : wr0) / 32 : 0;
         const int last_block = live ? (min(wr0 + ROWS_W, s) - 1) / 32 : -1;
-        const int tiles_a = full_blocks / NKB;             // phase A tiles
-        const int tiles_ab = live ? last_block / NKB + 1 : 0;   // phases A and B
+        const int tiles_a = full_blocks / NKB;             // phase A tiles (all below nh)
+        const int last_tile = last_block / NKB;
+        const int tiles_ab = live ? (last_tile >= nh ? last_tile - jump : last_tile) + 1 : 0;
         const int64_t seq_base = (int64_t)start * row_stride + (int64_t)head * D;
 
-        // Tile c into slot c % NS.  The buffer range covers the tile's rows
-        // that exist (none past the sequence).
+        // Loop tile c into slot c % NS.  The buffer range covers the tile's
+        // rows that some row of the workgroup sees (none past kv_end, none
+        // past the cached history).
         auto issue_loads = [&](int c) {
-            const int k0 = c * BK;
-            const int64_t off = seq_base + (int64_t)k0 * row_stride;
+            const int kt = c >= nh ? c + jump : c;
+            const int k0 = kt * BK;
             // (clamped below by make_rsrc32; min then max, not a clamp, which
             // would become a vector-only instruction and a non-scalar resource)
-            const int bytes = min(s - k0, BK) * row_bytes;
-            const __amdgpu_buffer_rsrc_t rk = make_rsrc32(a.k + off, bytes);
-            const __amdgpu_buffer_rsrc_t rv = make_rsrc32(a.v + off, bytes);
+            const uint16_t* kp;
+            const uint16_t* vp;
+            int bytes;
+            if (MASK == MASK_CACHED && kt < nh) {
+                const int64_t off = ((int64_t)hstart + k0) * row_stride + (int64_t)head * D;
+                kp = a.kc + off;
+                vp = a.vc + off;
+                bytes = min(hlen - k0, BK) * row_bytes;
+            } else {
+                const int64_t off = seq_base + (int64_t)(k0 - shift) * row_stride;
+                kp = a.k + off;
+                vp = a.v + off;
+                bytes = min(kv_end - k0, BK) * row_bytes;
+            }
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc32(kp, bytes);
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc32(vp, bytes);
             // Computed at run time from an opaque copy of c: with the slot
             // known at compile time the compiler keeps one destination per slot
             // and load in scalar registers, which the kernel does not have.
@@ -332,7 +378,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
         v8 qop[QB][NKS];
         {
             const __amdgpu_buffer_rsrc_t rq =
-                    make_rsrc(a.q + seq_base + (int64_t)wr0 * row_stride,
+                    make_rsrc(a.q + seq_base + (int64_t)(wr0 - shift) * row_stride,
                               (int64_t)(s - wr0) * row_bytes);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
@@ -554,9 +600,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
         // last one still reads this tile's K.
         for (; c < tiles_ab; ++c) {
             const int slot = c % NS;
+            const int kt = c >= nh ? c + jump : c;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                const int b = c * NKB + kb;
+                const int b = kt * NKB + kb;
                 if (b < full_blocks) {
                     f32x16 st[QB];
                     qk(slot, kb, st);
@@ -575,14 +622,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
             tile_sync(c);
         }
         // ---- phase C: staging only --------------------------------------------
-        for (; c < n_tiles; ++c) tile_sync(c);
+        for (; c < n_iter; ++c) tile_sync(c);
         __builtin_amdgcn_s_waitcnt(VMCNT_LE(0));   // nothing left landing in LDS
 
         // Epilogue: lane holds query wr0 + 32*qb + l32 and head-dim rows
         // 32*db + 8*i + 4*g + (0..3).  Stores past the sequence are dropped.
         if (live) {
             const __amdgpu_buffer_rsrc_t ro =
-                    make_rsrc(a.out + seq_base + (int64_t)wr0 * row_stride,
+                    make_rsrc(a.out + seq_base + (int64_t)(wr0 - shift) * row_stride,
                               (int64_t)(s - wr0) * row_bytes);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
@@ -624,6 +671,9 @@ struct KernelArgsF32 {
     float* out;
     const int32_t* offsets;
     const int32_t* ntgt;   // candidates per sequence (target-aware mask), or null
+    const float* kc;       // cached history K, V, or null
+    const float* vc;
+    const int32_t* hoff;   // history offsets: the cached-history form when non-null
     WorkList wl;
     int num_seqs;
     int heads;
@@ -660,12 +710,24 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
     int qx, w;
     while (src.next(tb, s_item, &qx, &w)) {
         const Item it = decode_item(tb, a.num_seqs, H, qx, w);
+        // Virtual sequence, key-tile jump and mask as in the 16-bit kernel.
         const int start = a.offsets[it.seq];
-        const int s = a.offsets[it.seq + 1] - start;
-        const int hist = a.ntgt ? s - min(max(a.ntgt[it.seq], 0), s) : s;   // as above
-        const int q0 = it.qtile * BQ;
+        const int len = a.offsets[it.seq + 1] - start;
+        int s = len, hist = len, shift = 0, hstart = 0, hlen = 0;
+        if (a.hoff) {
+            hstart = a.hoff[it.seq];
+            hlen = max(a.hoff[it.seq + 1] - hstart, 0);
+            hist = (hlen + BK - 1) / BK * BK;
+            shift = hist;
+            s = hist + len;
+        } else if (a.ntgt) {
+            hist = len - min(max(a.ntgt[it.seq], 0), len);
+        }
+        const int q0 = shift + it.qtile * BQ;
         const int kv_end = min(s, q0 + BQ);
         const int n_tiles = (kv_end + BK - 1) / BK;
+        const int nh = (hist + BK - 1) / BK;
+        const int jump = max(q0 / BK - nh, 0);
         const int wr0 = q0 + wv * 32;
         const bool wave_live = wr0 < s;
         const int my_row = wr0 + l32;
@@ -673,7 +735,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
 
         float qf[D / 2];
         {
-            const float* qp = a.q + seq_base + (int64_t)my_row * row_stride;
+            const float* qp = a.q + seq_base + (int64_t)(my_row - shift) * row_stride;
 #pragma unroll
             for (int ks = 0; ks < D / 2; ++ks) qf[ks] = (my_row < s) ? qp[2 * ks + g] : 0.0f;
         }
@@ -681,15 +743,24 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) o[db] = (f32x16){};
 
-        for (int c = 0; c < n_tiles; ++c) {
-            const int k0 = c * BK;
+        for (int c = 0; c < n_tiles - jump; ++c) {
+            const int k0 = (c >= nh ? c + jump : c) * BK;
+            const bool from_cache = a.hoff && k0 < hist;
 #pragma unroll
             for (int i = 0; i < Cfg::CHUNKS; ++i) {
                 const int id = tid + i * Cfg::THREADS;
                 const int r = id / (D / 4), c4 = id % (D / 4);
                 float4 xk = make_float4(0.f, 0.f, 0.f, 0.f), xv = xk;
-                if (k0 + r < s) {
-                    const int64_t off = seq_base + (int64_t)(k0 + r) * row_stride + c4 * 4;
+                if (from_cache) {
+                    if (k0 + r < hlen) {
+                        const int64_t off = ((int64_t)hstart + k0 + r) * row_stride +
+                                            (int64_t)it.head * D + c4 * 4;
+                        xk = *reinterpret_cast<const float4*>(a.kc + off);
+                        xv = *reinterpret_cast<const float4*>(a.vc + off);
+                    }
+                } else if (k0 + r < kv_end) {
+                    const int64_t off =
+                            seq_base + (int64_t)(k0 - shift + r) * row_stride + c4 * 4;
                     xk = *reinterpret_cast<const float4*>(a.k + off);
                     xv = *reinterpret_cast<const float4*>(a.v + off);
                 }
@@ -729,7 +800,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
         }
 
         if (my_row < s) {
-            float* op = a.out + seq_base + (int64_t)my_row * row_stride;
+            float* op = a.out + seq_base + (int64_t)(my_row - shift) * row_stride;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -795,20 +866,28 @@ hipError_t launch16(const FwdParams& p, WorkList wl, int grid, hipStream_t strea
     a.out = static_cast<uint16_t*>(p.out);
     a.offsets = p.offsets;
     a.ntgt = p.num_targets;
+    a.kc = static_cast<const uint16_t*>(p.k_cache);
+    a.vc = static_cast<const uint16_t*>(p.v_cache);
+    a.hoff = p.hist_offsets;
     a.wl = wl;
     a.num_seqs = p.num_seqs;
     a.heads = p.heads;
     a.score_scale = -p.alpha * LOG2E;
     a.out_scale = -LN2 / p.n;
     constexpr int QB = QBlocks<D>::value, BK = KeyTile<D>::value, PF = Prefetch<D>::value;
-    const bool tgt = p.num_targets != nullptr;
-    auto fn = wl.fused ? (tgt ? attn_fwd_mfma16<T, D, NW16, QB, BK, PF, true, true>
-                              : attn_fwd_mfma16<T, D, NW16, QB, BK, PF, true, false>)
-                       : (tgt ? attn_fwd_mfma16<T, D, NW16, QB, BK, PF, false, true>
-                              : attn_fwd_mfma16<T, D, NW16, QB, BK, PF, false, false>);
+    const int mode = p.hist_offsets ? MASK_CACHED : p.num_targets ? MASK_TARGETS : MASK_CAUSAL;
+    using Fn = void (*)(KernelArgs);
+    static constexpr Fn fns[2][3] = {
+            {attn_fwd_mfma16<T, D, NW16, QB, BK, PF, false, MASK_CAUSAL>,
+             attn_fwd_mfma16<T, D, NW16, QB, BK, PF, false, MASK_TARGETS>,
+             attn_fwd_mfma16<T, D, NW16, QB, BK, PF, false, MASK_CACHED>},
+            {attn_fwd_mfma16<T, D, NW16, QB, BK, PF, true, MASK_CAUSAL>,
+             attn_fwd_mfma16<T, D, NW16, QB, BK, PF, true, MASK_TARGETS>,
+             attn_fwd_mfma16<T, D, NW16, QB, BK, PF, true, MASK_CACHED>}};
+    const Fn fn = fns[wl.fused ? 1 : 0][mode];
     if (grid <= 0) {
-        static int cached[4] = {0, 0, 0, 0};
-        int& c = cached[(wl.fused ? 1 : 0) + (tgt ? 2 : 0)];
+        static int cached[2][3] = {};
+        int& c = cached[wl.fused ? 1 : 0][mode];
         if (!c) c = resident_grid(fn, NW16 * 64);
         grid = c;
     }
@@ -829,6 +908,9 @@ hipError_t launch_f32(const FwdParams& p, WorkList wl, int grid, hipStream_t str
     a.out = static_cast<float*>(p.out);
     a.offsets = p.offsets;
     a.ntgt = p.num_targets;
+    a.kc = static_cast<const float*>(p.k_cache);
+    a.vc = static_cast<const float*>(p.v_cache);
+    a.hoff = p.hist_offsets;
     a.wl = wl;
     a.num_seqs = p.num_seqs;
     a.heads = p.heads;

@@ -130,6 +130,10 @@ struct FwdParams {
     void* out;
     const int32_t* offsets;
     const int32_t* num_targets;   // candidates per sequence, or null (plain causal)
+    // Cached-history form (offsets, q, k, v, out are then the candidates'):
+    const void* k_cache;          // history K, V (T_hist, heads, d), or null
+    const void* v_cache;
+    const int32_t* hist_offsets;  // int32[num_seqs + 1], or null (not the cached form)
     int num_seqs;
     int heads;
     int d;

@@ -112,6 +112,40 @@ hstu_status_t hstu_attn_fwd_targets(const void* q, const void* k, const void* v,
                                     int32_t num_seqs, int32_t heads, int32_t d, float alpha,
                                     float n, void* out, hipStream_t stream, hstu_dtype_t dtype);
 
+/* The later micro-batches of M-FALCON: candidates scored against a cached
+ * history (HSTU paper translation, Appendix H: K and V of the history are
+ * cached across micro-batches and requests; a micro-batch computes q, k, v
+ * for its candidates only).  For request i with h_i cached history rows and
+ * t_i candidates, candidate j (global row cand_offsets[i] + j) gets
+ *
+ *   out[j] = (1/n) * ( sum_{c < h_i} silu(alpha <q[j], k_cache[hist_offsets[i] + c]>)
+ *                                     * v_cache[hist_offsets[i] + c]
+ *                      + silu(alpha <q[j], k[j]>) * v[j] )
+ *
+ * i.e. the target-aware mask over history + candidates, computed for the
+ * candidate rows only.
+ *
+ *   q, k, v, out     : the candidates, (T_cand, heads, d), T_cand = cand_offsets[num_seqs];
+ *                      layout, alignment and aliasing as in hstu_attn_fwd.
+ *   cand_offsets     : device int32[num_seqs + 1], as seq_offsets of hstu_attn_fwd.
+ *   k_cache, v_cache : the cached history K and V, (T_hist, heads, d), same element
+ *                      type, 16-byte aligned, T_hist = hist_offsets[num_seqs];
+ *                      read only; out must not overlap them.  Both may be NULL
+ *                      when T_hist = 0 (every hist_offsets entry 0): then no
+ *                      cache row is read.
+ *   hist_offsets     : device int32[num_seqs + 1], off[0] = 0, non-decreasing (an
+ *                      empty history is allowed: candidates then see themselves only).
+ *
+ * Element types, streams, scratch and errors as in hstu_attn_fwd;
+ * hist_offsets must be non-null when num_seqs > 0, and the two cache pointers
+ * both null or both non-null (else HSTU_ERR_INVALID_ARG).  Malformed history offsets are not detected
+ * (hstu_validate_offsets checks them). */
+hstu_status_t hstu_attn_fwd_cached(const void* q, const void* k, const void* v,
+                                   const int32_t* cand_offsets, const void* k_cache,
+                                   const void* v_cache, const int32_t* hist_offsets,
+                                   int32_t num_seqs, int32_t heads, int32_t d, float alpha,
+                                   float n, void* out, hipStream_t stream, hstu_dtype_t dtype);
+
 /* Checks device offsets synchronously: off[0] == 0 and non-decreasing.  Writes
  * T = off[num_seqs] to *total (may be NULL).  Returns HSTU_OK or
  * HSTU_ERR_BAD_OFFSETS; synchronises `stream`. */

@@ -103,6 +103,36 @@ def test_targets_empty_batch_is_a_no_op(lib):
                          num_seqs=0) == hstu.HSTU_OK
 
 
+def _call_cached(lib, kc=64, vc=80, hoff=96, **kw):
+    a = dict(q=16, k=16, v=16, off=16, num_seqs=1, heads=1, d=64, alpha=0.1, n=1.0, out=32,
+             dtype=hstu.HSTU_BF16)
+    a.update(kw)
+    return lib.hstu_attn_fwd_cached(a["q"], a["k"], a["v"], a["off"], kc, vc, hoff,
+                                    a["num_seqs"], a["heads"], a["d"], a["alpha"], a["n"],
+                                    a["out"], None, a["dtype"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kc=None), hstu.HSTU_ERR_INVALID_ARG),    # one cache without the other
+    (dict(vc=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(kc=None, vc=None, d=96), hstu.HSTU_ERR_UNSUPPORTED),   # no caches: allowed
+    (dict(hoff=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(kc=72), hstu.HSTU_ERR_INVALID_ARG),      # misaligned cache
+    (dict(hoff=98), hstu.HSTU_ERR_INVALID_ARG),    # misaligned history offsets
+    (dict(out=64), hstu.HSTU_ERR_INVALID_ARG),     # out aliases the cached K
+    (dict(q=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(d=96), hstu.HSTU_ERR_UNSUPPORTED),
+    (dict(dtype=5), hstu.HSTU_ERR_UNSUPPORTED),
+])
+def test_cached_argument_checks(lib, kw, status):
+    assert _call_cached(lib, **kw) == status
+
+
+def test_cached_empty_batch_is_a_no_op(lib):
+    assert _call_cached(lib, kc=None, vc=None, hoff=None, q=None, k=None, v=None, off=None,
+                        out=None, num_seqs=0) == hstu.HSTU_OK
+
+
 def test_status_strings(lib):
     for st in (0, -1, -2, -3, -4, -5):
         assert lib.hstu_status_string(st)

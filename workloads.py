@@ -243,3 +243,63 @@ def targets_workload(values: bool = True, history: int = 3072, candidates: int =
                 q=vals[0], k=vals[1], v=vals[2], alpha=f32(1.0 / 8.0),
                 n=f32(float(history + candidates)), description=TARGETS_DESCRIPTION,
                 num_targets=np.full(users, candidates, dtype=np.int32))
+
+
+# ---------------------------------------------------------------------------
+# Later micro-batches against a cached history (M-FALCON with the
+# encoder-level K/V cache, HSTU paper translation Appendix H): 16 users, a
+# cached history of 3072 rows each (K and V only), one micro-batch of 1024
+# candidates each (q, k, v).  Seed 1200: history K, V, then candidate q, k, v.
+# ---------------------------------------------------------------------------
+
+CACHED_DESCRIPTION = ("cached history, 16 users x (3072 cached history rows, "
+                      "1024 candidates), heads 4, d 64, bf16")
+
+
+@dataclasses.dataclass
+class CachedCase:
+    """Candidates (a Case: q, k, v, offsets) plus the cached history K, V and
+    their offsets."""
+
+    cand: Case
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    hist_offsets: np.ndarray  # int32 [num_seqs + 1]
+
+    @property
+    def hist_lengths(self) -> np.ndarray:
+        return np.diff(self.hist_offsets.astype(np.int64))
+
+
+def make_cached_case(hist_lengths, cand_lengths, heads: int, d: int, dtype: str, seed: int,
+                     sigma: float = 1.0, alpha: Optional[float] = None,
+                     n: Optional[float] = None) -> CachedCase:
+    """History K, V then candidate q, k, v, i.i.d. N(0, sigma^2), one generator."""
+    if len(hist_lengths) != len(cand_lengths):
+        raise ValueError("one history length per request")
+    rng = np.random.default_rng(seed)
+    hoff = offsets_from_lengths(hist_lengths)
+    coff = offsets_from_lengths(cand_lengths)
+
+    def draw(rows):
+        x = rng.standard_normal((rows, heads, d), dtype=np.float32)
+        if sigma != 1.0:
+            x *= np.float32(sigma)
+        return cast_values(x, dtype)
+
+    kc, vc = draw(int(hoff[-1])), draw(int(hoff[-1]))
+    q, k, v = draw(int(coff[-1])), draw(int(coff[-1])), draw(int(coff[-1]))
+    if alpha is None:
+        alpha = 1.0 / math.sqrt(d)
+    if n is None:
+        n = float(max([1] + [int(a) + int(b) for a, b in zip(hist_lengths, cand_lengths)]))
+    cand = Case(name="cached", dtype=dtype, heads=heads, d=d, offsets=coff, q=q, k=k, v=v,
+                alpha=f32(alpha), n=f32(n))
+    return CachedCase(cand=cand, k_cache=kc, v_cache=vc, hist_offsets=hoff)
+
+
+def cached_workload(history: int = 3072, candidates: int = 1024, users: int = 16) -> CachedCase:
+    c = make_cached_case([history] * users, [candidates] * users, 4, 64, "bf16", seed=1200,
+                         alpha=1.0 / 8.0, n=float(history + candidates))
+    c.cand.description = CACHED_DESCRIPTION
+    return c
