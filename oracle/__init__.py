@@ -26,6 +26,11 @@ algorithm (Appendix H, the encoder-level K/V cache): candidates with their own
 q, k, v attend to a cached history's K and V plus themselves, each request's
 history and candidates given by their own offsets.
 
+``bwd`` / ``bwd_rows`` are the gradients with respect to q, k and v: the
+derivative of the forward definition, per kept (row, key) pair, for an
+upstream gradient dout (the pages only say that the backward recomputes the
+attention instead of storing it, HSTU paper translation Appendix G).
+
 Parity status: pinned.  The test suite ties these functions to closed forms
 (hand-worked 2- and 3-token cases), to identities that reduce to textbook
 operations (sign-flip -> masked GEMM, constant rows -> prefix sum, row 0),
@@ -89,6 +94,13 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                             ctypes.c_int, ctypes.c_int, ctypes.c_int, f64, f64,
                                             vp, vp, i64, vp]
     lib.hstu_oracle_rows_cached.restype = ctypes.c_int
+    lib.hstu_oracle_bwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, f64, f64, vp, vp, vp]
+    lib.hstu_oracle_bwd.restype = ctypes.c_int
+    lib.hstu_oracle_bwd_rows.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, f64, f64, ctypes.c_int, vp,
+                                         vp, i64, vp]
+    lib.hstu_oracle_bwd_rows.restype = ctypes.c_int
     lib.hstu_oracle_threads.argtypes = []
     lib.hstu_oracle_threads.restype = ctypes.c_int
     _libs[path] = lib
@@ -205,6 +217,52 @@ def rows_cached(q, k, v, cand_offsets, k_cache, v_cache, hist_offsets, heads: in
                                      _DTYPE_CODE[dtype], _ptr(coff), _ptr(hoff), len(coff) - 1,
                                      heads, d, float(alpha), float(n), _ptr(tok), _ptr(hd),
                                      len(tok), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle rejected the sampled rows")
+    return out
+
+
+def bwd(q, k, v, dout, offsets, heads: int, d: int, alpha: float, n: float, dtype: str,
+        lib: Optional[ctypes.CDLL] = None, num_targets=None):
+    """(dq, dk, dv), each fp64 (T, heads, d), for upstream gradient dout."""
+    lib = lib or load()
+    q, k, v, dout = (_storage(a, dtype) for a in (q, k, v, dout))
+    off = np.ascontiguousarray(offsets, dtype=np.int32)
+    tg = _targets(num_targets, len(off) - 1)
+    T = int(off[-1]) if len(off) else 0
+    for a in (q, k, v, dout):
+        if a.size < T * heads * d:
+            raise ValueError("q/k/v/dout smaller than offsets imply")
+    dq, dk, dv = (np.zeros((T, heads, d), dtype=np.float64) for _ in range(3))
+    rc = lib.hstu_oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _DTYPE_CODE[dtype],
+                             _ptr(off), None if tg is None else _ptr(tg), len(off) - 1, heads, d,
+                             float(alpha), float(n), _ptr(dq), _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments (malformed offsets or sizes)")
+    return dq, dk, dv
+
+
+BWD_KIND = {"dq": 0, "dk": 1, "dv": 2}
+
+
+def bwd_rows(q, k, v, dout, offsets, heads: int, d: int, alpha: float, n: float, dtype: str,
+             kind: str, tokens, head_ids, lib: Optional[ctypes.CDLL] = None,
+             num_targets=None) -> np.ndarray:
+    """fp64 gradient rows (m, d): kind 'dq' at query tokens[m], 'dk' / 'dv' at
+    key tokens[m], heads head_ids[m]."""
+    lib = lib or load()
+    q, k, v, dout = (_storage(a, dtype) for a in (q, k, v, dout))
+    off = np.ascontiguousarray(offsets, dtype=np.int32)
+    tg = _targets(num_targets, len(off) - 1)
+    tok = np.ascontiguousarray(tokens, dtype=np.int64)
+    hd = np.ascontiguousarray(head_ids, dtype=np.int32)
+    if tok.shape != hd.shape:
+        raise ValueError("tokens and head_ids differ in length")
+    out = np.zeros((len(tok), d), dtype=np.float64)
+    rc = lib.hstu_oracle_bwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _DTYPE_CODE[dtype],
+                                  _ptr(off), None if tg is None else _ptr(tg), len(off) - 1,
+                                  heads, d, float(alpha), float(n), BWD_KIND[kind], _ptr(tok),
+                                  _ptr(hd), len(tok), _ptr(out))
     if rc != 0:
         raise ValueError("oracle rejected the sampled rows")
     return out

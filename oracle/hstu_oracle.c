@@ -40,6 +40,16 @@
  *                 + silu(alpha <q_j, k_j>) v_j ),
  *     kc, vc the cached history rows of request i, h_i their count.
  *
+ * Backward (the *_bwd entry points): the pages say only that the attention is
+ * recomputed in the backward pass instead of storing the h x N x N attention
+ * tensor (HSTU paper translation, Appendix G).  The gradients here are the
+ * derivative of the forward definition above, written out per (row r, key c)
+ * pair that the mask keeps, with x = alpha <q_r, k_c> and dO the gradient of
+ * the loss with respect to out:
+ *   dv_c += silu(x) / n * dO_r
+ *   g     = (alpha / n) * silu'(x) * <dO_r, v_c>,  silu'(x) = sig(x) (1 + x (1 - sig(x)))
+ *   dq_r += g * k_c,   dk_c += g * q_r
+ *
  * Readings taken where the pages are silent (each listed in the design notes):
  *   - alpha multiplies the scores before SiLU; n is a caller-given scalar;
  *   - the mask multiplies after SiLU (0/1), so masked terms are exactly 0;
@@ -281,6 +291,139 @@ int hstu_oracle_rows(const void* q, const void* k, const void* v, int dtype,
                      int64_t count, double* out_rows) {
     return hstu_oracle_rows_targets(q, k, v, dtype, off, 0, num_seqs, heads, d, alpha, n, tok,
                                     hd, count, out_rows);
+}
+
+/* ---- backward ------------------------------------------------------------- */
+
+static double dsilu(double x) {
+    double sg = x >= 0.0 ? 1.0 / (1.0 + exp(-x)) : exp(x) / (1.0 + exp(x));
+#if ORACLE_PLANT == 11
+    return sg; /* planted: the sigmoid taken for the derivative of silu */
+#else
+    return sg * (1.0 + x * (1.0 - sg));
+#endif
+}
+
+/* Does row r of a sequence with history length hist see key c? */
+static int sees(int64_t r, int64_t c, int64_t hist) {
+    return c <= r && (c < hist || c == r);
+}
+
+/* The gradient terms of one (row r, key c) pair of sequence start s0, head h:
+ * adds to the d-element rows dq_r (if non-null), dk_c and dv_c (if non-null). */
+static void pair_grads(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                       int64_t s0, int64_t r, int64_t c, int heads, int d, int h, double alpha,
+                       double n, double* dq_r, double* dk_c, double* dv_c) {
+    const int64_t rs = (int64_t)heads * d, ho = (int64_t)h * d;
+    const int64_t qr = (s0 + r) * rs + ho, kc = (s0 + c) * rs + ho;
+    double dot = 0.0, dov = 0.0;
+    for (int e = 0; e < d; ++e) {
+        dot += load_elem(q, dtype, qr + e) * load_elem(k, dtype, kc + e);
+        dov += load_elem(dout, dtype, qr + e) * load_elem(v, dtype, kc + e);
+    }
+    const double x = alpha * dot;
+    double chain = alpha;
+#if ORACLE_PLANT == 13
+    chain = 1.0; /* planted: alpha dropped from the chain rule */
+#endif
+    const double g = chain / n * dsilu(x) * dov;
+    const double w = silu(x) / n;
+    for (int e = 0; e < d; ++e) {
+        if (dq_r) dq_r[e] += g * load_elem(k, dtype, kc + e);
+        if (dk_c) {
+#if ORACLE_PLANT == 12
+            dk_c[e] += g * load_elem(k, dtype, qr + e); /* planted: k for q */
+#else
+            dk_c[e] += g * load_elem(q, dtype, qr + e);
+#endif
+        }
+        if (dv_c) dv_c[e] += w * load_elem(dout, dtype, qr + e);
+    }
+}
+
+/* Gradients of the forward (causal, or target-aware when ntgt is non-null)
+ * with respect to q, k and v for upstream gradient dout (same storage type as
+ * q); dq, dk, dv are fp64 (T, heads, d) and are overwritten.  Returns 0, or -1
+ * on malformed offsets.  Each (sequence, head) pair writes only its own rows. */
+int hstu_oracle_bwd(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                    const int32_t* off, const int32_t* ntgt, int num_seqs, int heads, int d,
+                    double alpha, double n, double* dq, double* dk, double* dv) {
+    if (num_seqs < 0 || heads < 1 || d < 1) return -1;
+    if (num_seqs > 0 && off[0] != 0) return -1;
+    for (int i = 0; i < num_seqs; ++i)
+        if (off[i + 1] < off[i]) return -1;
+    const int64_t rs = (int64_t)heads * d;
+    const int64_t T = num_seqs > 0 ? off[num_seqs] : 0;
+    memset(dq, 0, sizeof(double) * T * rs);
+    memset(dk, 0, sizeof(double) * T * rs);
+    memset(dv, 0, sizeof(double) * T * rs);
+    const int64_t items = (int64_t)num_seqs * heads;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t it = 0; it < items; ++it) {
+        int i = (int)(it / heads), h = (int)(it % heads);
+        int64_t s0 = off[i], len = (int64_t)off[i + 1] - off[i];
+        int64_t t = ntgt ? ntgt[i] : 0;
+        if (t < 0) t = 0;
+        if (t > len) t = len;
+        for (int64_t r = 0; r < len; ++r)
+            for (int64_t c = 0; c < len; ++c) {
+                double* dq_r = dq + (s0 + r) * rs + (int64_t)h * d;
+                double* dk_c = dk + (s0 + c) * rs + (int64_t)h * d;
+                double* dv_c = dv + (s0 + c) * rs + (int64_t)h * d;
+#if ORACLE_PLANT == 14
+                if (c > r) { /* planted: the key gradients also take keys above the diagonal */
+                    pair_grads(q, k, v, dout, dtype, s0, r, c, heads, d, h, alpha, n, 0, dk_c,
+                               dv_c);
+                    continue;
+                }
+#endif
+                if (sees(r, c, len - t))
+                    pair_grads(q, k, v, dout, dtype, s0, r, c, heads, d, h, alpha, n, dq_r, dk_c,
+                               dv_c);
+            }
+    }
+    return 0;
+}
+
+/* Sampled gradient rows: kind 0 = dq at query token tok[m], 1 = dk and 2 = dv
+ * at key token tok[m], head hd[m]; out_rows[m, 0..d).  Returns 0, or -1 on
+ * bad arguments.  d <= 1024. */
+int hstu_oracle_bwd_rows(const void* q, const void* k, const void* v, const void* dout,
+                         int dtype, const int32_t* off, const int32_t* ntgt, int num_seqs,
+                         int heads, int d, double alpha, double n, int kind, const int64_t* tok,
+                         const int32_t* hd, int64_t count, double* out_rows) {
+    if (num_seqs < 1 || heads < 1 || d < 1 || d > 1024 || kind < 0 || kind > 2) return -1;
+    int64_t T = off[num_seqs];
+    for (int64_t m = 0; m < count; ++m)
+        if (tok[m] < 0 || tok[m] >= T || hd[m] < 0 || hd[m] >= heads) return -1;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t m = 0; m < count; ++m) {
+        int lo = 0, hi = num_seqs - 1;   /* largest i with off[i] <= tok */
+        while (lo < hi) {
+            int mid = (lo + hi + 1) / 2;
+            if (off[mid] <= tok[m]) lo = mid; else hi = mid - 1;
+        }
+        int64_t s0 = off[lo], len = (int64_t)off[lo + 1] - off[lo];
+        int64_t t = ntgt ? ntgt[lo] : 0;
+        if (t < 0) t = 0;
+        if (t > len) t = len;
+        const int64_t x = tok[m] - s0;
+        double acc[1024], other[1024];
+        for (int e = 0; e < d; ++e) acc[e] = other[e] = 0.0;
+        if (kind == 0) {
+            for (int64_t c = 0; c < len; ++c)
+                if (sees(x, c, len - t))
+                    pair_grads(q, k, v, dout, dtype, s0, x, c, heads, d, hd[m], alpha, n, acc, 0,
+                               0);
+        } else {
+            for (int64_t r = 0; r < len; ++r)
+                if (sees(r, x, len - t))
+                    pair_grads(q, k, v, dout, dtype, s0, r, x, heads, d, hd[m], alpha, n, 0,
+                               kind == 1 ? acc : other, kind == 2 ? acc : other);
+        }
+        for (int e = 0; e < d; ++e) out_rows[m * (int64_t)d + e] = acc[e];
+    }
+    return 0;
 }
 
 static int offsets_ok(const int32_t* off, int num_seqs) {
