@@ -31,7 +31,8 @@ HSTU_BF16, HSTU_FP16, HSTU_FP32 = 0, 1, 2
 
 # Every symbol include/hstu.h declares.
 EXPORTS = ("hstu_attn_fwd", "hstu_attn_fwd_bf16", "hstu_attn_fwd_fp16", "hstu_attn_fwd_fp32",
-           "hstu_attn_fwd_targets", "hstu_attn_fwd_cached", "hstu_validate_offsets", "hstu_status_string", "hstu_last_hip_error",
+           "hstu_attn_fwd_targets", "hstu_attn_fwd_cached", "hstu_attn_bwd",
+           "hstu_attn_bwd_targets", "hstu_validate_offsets", "hstu_status_string", "hstu_last_hip_error",
            "hstu_release_workspace", "hstu_profile_enable", "hstu_profile_read")
 
 
@@ -77,6 +78,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hstu_attn_fwd_cached.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, vp,
                                          vp, ctypes.c_int]
     lib.hstu_attn_fwd_cached.restype = ctypes.c_int
+    lib.hstu_attn_bwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp, vp, vp,
+                                  ctypes.c_int]
+    lib.hstu_attn_bwd.restype = ctypes.c_int
+    lib.hstu_attn_bwd_targets.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp,
+                                          vp, vp, ctypes.c_int]
+    lib.hstu_attn_bwd_targets.restype = ctypes.c_int
     lib.hstu_validate_offsets.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_int64), vp]
     lib.hstu_validate_offsets.restype = ctypes.c_int
     lib.hstu_status_string.argtypes = [ctypes.c_int]
@@ -256,3 +263,41 @@ def hstu_profile_read(reset: bool = True) -> KernelTimes:
     _check(load_library().hstu_profile_read(ctypes.byref(t), 1 if reset else 0),
            "hstu_profile_read")
     return t
+
+
+def hstu_attn_bwd(q, k, v, dout, seq_offsets, alpha: float, n: float, num_targets=None,
+                  grads=None, stream=None):
+    """Gradients (dq, dk, dv) of the forward (target-aware when num_targets is
+    given) for the upstream gradient dout.  bfloat16 / float16 only.  `grads`
+    may supply three preallocated output tensors."""
+    import torch
+    _check_tensors(q, k, v, seq_offsets, torch.empty_like(q))
+    if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_cuda or \
+            not dout.is_contiguous():
+        raise ValueError("dout must be a contiguous GPU tensor shaped and typed like q")
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
+    for t in grads:
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("gradient outputs must be contiguous GPU tensors shaped like q")
+    dq, dk, dv = grads
+    T, heads, d = q.shape
+    num_seqs = seq_offsets.numel() - 1
+    if T == 0:
+        return dq, dk, dv
+    lib = load_library()
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), seq_offsets.data_ptr())
+    tail = (num_seqs, heads, d, float(alpha), float(n), dq.data_ptr(), dk.data_ptr(),
+            dv.data_ptr(), _stream_handle(stream), _dtype_code(q))
+    if num_targets is None:
+        st = lib.hstu_attn_bwd(*args, *tail)
+        _check(st, "hstu_attn_bwd")
+    else:
+        if (num_targets.dtype != torch.int32 or num_targets.dim() != 1 or
+                num_targets.numel() != num_seqs or not num_targets.is_cuda or
+                not num_targets.is_contiguous()):
+            raise ValueError("num_targets must be a contiguous 1-D int32 GPU tensor of "
+                             "num_seqs entries")
+        st = lib.hstu_attn_bwd_targets(*args, num_targets.data_ptr(), *tail)
+        _check(st, "hstu_attn_bwd_targets")
+    return dq, dk, dv

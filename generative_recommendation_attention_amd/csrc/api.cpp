@@ -256,6 +256,84 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
     return HSTU_OK;
 }
 
+// One backward call: the dK/dV kernel, then the dQ kernel, on one work list
+// of BWD_TILE_ROWS-row items (each launch takes one of the two counter sets).
+hstu_status_t attn_bwd_call(const void* q, const void* k, const void* v, const void* dout,
+                            const int32_t* seq_offsets, const int32_t* num_targets,
+                            int32_t num_seqs, int32_t heads, int32_t d, float alpha, float n,
+                            void* dq, void* dk, void* dv, hipStream_t stream, int dtype) {
+    hstu_status_t st = check_args(q, k, v, seq_offsets, num_seqs, heads, d, alpha, n, dq, dtype);
+    if (st != HSTU_OK) return st;
+    if (dtype == HSTU_FP32) return HSTU_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return HSTU_OK;
+    if (!dout || !dk || !dv) return HSTU_ERR_INVALID_ARG;
+    if (!aligned16(dout) || !aligned16(dk) || !aligned16(dv)) return HSTU_ERR_INVALID_ARG;
+    const void* ins[4] = {q, k, v, dout};
+    const void* outs[3] = {dq, dk, dv};
+    for (const void* o : outs)
+        for (const void* i : ins)
+            if (o == i) return HSTU_ERR_INVALID_ARG;
+    if (dq == dk || dq == dv || dk == dv) return HSTU_ERR_INVALID_ARG;
+    int dev = 0;
+    st = check_device(&dev);
+    if (st != HSTU_OK) return st;
+
+    const hstu::Dtype dt = static_cast<hstu::Dtype>(dtype);
+    Scratch* sc = nullptr;
+    st = scratch_for(dev, stream, hstu::worklist_bytes(num_seqs, heads), &sc);
+    if (st != HSTU_OK) return st;
+    hstu::WorkList wl = hstu::worklist_carve(sc->ptr, num_seqs, heads);
+    const hstu::SortChoice sort = sort_choice_env();
+    bool clean;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        wl.set = (int)(sc->epoch & 1u);
+        clean = sc->clean;
+        sc->clean = false;
+    }
+    wl.fused = clean && sort == hstu::SortChoice::AUTO && num_seqs <= hstu::FUSE_SEQS &&
+               (long long)num_seqs * heads <= hstu::FUSE_PAIRS;
+
+    hstu::BwdParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.dout = dout;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.offsets = seq_offsets;
+    p.num_targets = num_targets;
+    p.num_seqs = num_seqs;
+    p.heads = heads;
+    p.d = d;
+    p.alpha = alpha;
+    p.n = n;
+
+    TimedCall tc;
+    const bool timed = prof_take(&tc);
+    tc.sched = false;
+    hipError_t e;
+    if (!wl.fused) {
+        e = hstu::launch_schedule(seq_offsets, num_seqs, heads, hstu::BWD_TILE_ROWS, wl, stream,
+                                  sort, timed ? tc.e[0] : nullptr, timed ? tc.e[1] : nullptr);
+        if (e != hipSuccess) return hip_fail(e);
+        tc.sched = timed;
+    }
+    e = hstu::launch_backward(p, dt, wl, stream, timed ? tc.e[2] : nullptr,
+                              timed ? tc.e[3] : nullptr);
+    if (e != hipSuccess) return hip_fail(e);
+    {
+        // Two launches: this call's set, then the other; the second cleared
+        // this call's set, which the next call takes again.
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        sc->epoch += 2;
+        sc->clean = true;
+    }
+    if (timed) prof_commit(tc);
+    return HSTU_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -278,6 +356,25 @@ hstu_status_t hstu_attn_fwd_targets(const void* q, const void* k, const void* v,
     mi.num_targets = num_targets;
     return attn_fwd_call(q, k, v, seq_offsets, mi, num_seqs, heads, d, alpha, n, out, stream,
                          dtype);
+}
+
+hstu_status_t hstu_attn_bwd(const void* q, const void* k, const void* v, const void* dout,
+                            const int32_t* seq_offsets, int32_t num_seqs, int32_t heads,
+                            int32_t d, float alpha, float n, void* dq, void* dk, void* dv,
+                            hipStream_t stream, hstu_dtype_t dtype) {
+    return attn_bwd_call(q, k, v, dout, seq_offsets, nullptr, num_seqs, heads, d, alpha, n, dq,
+                         dk, dv, stream, dtype);
+}
+
+hstu_status_t hstu_attn_bwd_targets(const void* q, const void* k, const void* v,
+                                    const void* dout, const int32_t* seq_offsets,
+                                    const int32_t* num_targets, int32_t num_seqs, int32_t heads,
+                                    int32_t d, float alpha, float n, void* dq, void* dk,
+                                    void* dv, hipStream_t stream, hstu_dtype_t dtype) {
+    if (num_seqs > 0 && (!num_targets || (reinterpret_cast<uintptr_t>(num_targets) & 3u) != 0))
+        return HSTU_ERR_INVALID_ARG;
+    return attn_bwd_call(q, k, v, dout, seq_offsets, num_targets, num_seqs, heads, d, alpha, n,
+                         dq, dk, dv, stream, dtype);
 }
 
 hstu_status_t hstu_attn_fwd_cached(const void* q, const void* k, const void* v,

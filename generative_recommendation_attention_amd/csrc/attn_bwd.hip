@@ -1,0 +1,522 @@
+// HSTU jagged attention backward on gfx950 matrix cores (bf16 / fp16).
+//
+// Forward, per sequence and head:  out[r] = (1/n) sum_{c seen by r} silu(x_rc) v_c,
+// x_rc = alpha <q_r, k_c>.  For an upstream gradient dO, per kept pair (r, c):
+//
+//   dv_c += silu(x_rc) / n * dO_r
+//   g_rc  = (alpha / n) * silu'(x_rc) * <dO_r, v_c>,  silu'(x) = sig(x) (1 + x (1 - sig(x)))
+//   dq_r += g_rc * k_c,        dk_c += g_rc * q_r
+//
+// The pages give only the idea: the backward recomputes the attention block by
+// block instead of storing the h x N x N tensor, and accumulates gradients on
+// chip (HSTU paper translation, Appendix G).  Here two kernels, so that no
+// gradient is accumulated with atomics:
+//
+//   attn_bwd_dkv: a work item is (sequence, head, 128-key tile); each wave
+//     keeps 32 keys' K and V in registers and the dK, dV accumulators for them,
+//     and streams the 32-row query blocks at or below its keys (Q and dO staged
+//     in LDS):  S = Q K^T and dP = dO V^T (keys across, queries down), then
+//     P = silu(alpha S) and dS = dP * silu'(alpha S) in registers, then
+//     dV^T += dO^T P and dK^T += Q^T dS (the contraction over queries takes P
+//     and dS straight from the accumulators; dO^T and Q^T come from gfx950's
+//     transposing LDS read, as V^T does in the forward).
+//   attn_bwd_dq: a work item is (sequence, head, 128-query tile); each wave
+//     keeps 32 queries' Q and dO in registers and streams the 32-key blocks up
+//     to its diagonal (K and V staged in LDS): S^T = K Q^T and dP^T = V dO^T,
+//     dS^T in registers, dQ^T += K^T dS^T.
+//
+// S and dP are recomputed by both kernels (seven block products per kept
+// block pair instead of five) in exchange for no atomics and no fp32 dQ
+// buffer.  The 1/n and alpha/n factors are applied once, in the epilogues.
+//
+// Tiles in LDS: 32 rows per block, 16-byte chunks XOR-swizzled per row; an
+// operand read both ways (row reads and transposing reads) is staged twice,
+// once in each swizzle, so neither read pattern has bank conflicts.  Two
+// slots: block c+1 streams in (straight from HBM into LDS) while block c is
+// consumed; one barrier per block.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "internal.h"
+#include "schedule.h"
+
+namespace hstu {
+
+namespace {
+
+constexpr float BWD_LOG2E = 1.4426950408889634f;
+
+struct BwdArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* dout;
+    uint16_t* dq;
+    uint16_t* dk;
+    uint16_t* dv;
+    const int32_t* offsets;
+    const int32_t* ntgt;   // candidates per sequence (target-aware mask), or null
+    WorkList wl;
+    int num_seqs;
+    int heads;
+    float alpha;
+    float dv_scale;   // 1 / n
+    float g_scale;    // alpha / n
+};
+
+// Shapes shared by both kernels: 4 waves of 32 rows (128 rows per item), 32-row
+// streamed blocks.
+template <int D>
+struct BwdCfg {
+    static constexpr int NW = 4;
+    static constexpr int ROWS = 32 * NW;              // rows per item
+    static constexpr int RB = 2 * D;                  // bytes per row in LDS
+    static constexpr int CH = RB / 16;                // 16-byte chunks per row
+    static constexpr int ARR = 32 * RB;               // one 32-row array in LDS
+    static constexpr int RPL = 1024 / RB;             // rows one wave load covers
+    static constexpr int LPA = ARR / 1024 / NW;       // wave loads per array
+    static constexpr int NKS = D / 16;                // k-steps over the head dim
+    static constexpr int NDB = D / 32;                // 32-wide head-dim blocks
+    static_assert(LPA * NW * 1024 == ARR, "array must split into whole wave loads");
+};
+
+// Per-lane pieces of the staging and operand addresses (see the forward).
+template <int D>
+struct LaneOffsets {
+    using C = BwdCfg<D>;
+    int gk[C::LPA], gv[C::LPA];   // global byte offsets of this lane's loads (row-read, transposed swizzle)
+    int dst[C::LPA];              // LDS byte offset of each load inside an array
+    int rowrd[C::NKS];            // row read of row l32, k-step ks
+    int tr_lo[C::NDB], tr_hi[C::NDB];   // transposing reads, head-dim block db
+    __device__ LaneOffsets(int lane, int wv, int row_bytes) {
+        constexpr int CH = C::CH;
+#pragma unroll
+        for (int i = 0; i < C::LPA; ++i) {
+            const int L = wv + C::NW * i;
+            const int r = L * C::RPL + lane / CH;
+            const int pc = lane % CH;
+            gk[i] = r * row_bytes + 16 * (pc ^ kswz<CH>(r));
+            gv[i] = r * row_bytes + 16 * (pc ^ vswz<CH>(r));
+            dst[i] = L * 1024;
+        }
+        const int g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) rowrd[ks] = l32 * C::RB + 16 * ((2 * ks + g) ^ kswz<CH>(l32));
+        const int v_row = 4 * g + ((lane & 15) >> 2);
+        const int v_colb = 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+            const int cb = 64 * db + v_colb;
+            tr_lo[db] = v_row * C::RB + 16 * ((cb >> 4) ^ vswz<CH>(v_row)) + (cb & 15);
+            tr_hi[db] = (v_row + 8) * C::RB + 16 * ((cb >> 4) ^ vswz<CH>(v_row + 8)) + (cb & 15);
+        }
+    }
+};
+
+// Stages 32 rows of one tensor (rows [row0, row0 + 32) of a sequence whose
+// first row is at `base`) into an LDS array, in the row-read swizzle (tr =
+// false) or the transposing-read swizzle (tr = true).  Rows at or past
+// `rows_avail` read as zero.
+template <int D>
+__device__ __forceinline__ void stage(const uint16_t* base, int64_t row_stride, int row0,
+                                      int rows_avail, int row_bytes, unsigned char* arr,
+                                      const LaneOffsets<D>& lo, bool tr) {
+    const int n = min(rows_avail - row0, 32);
+    const __amdgpu_buffer_rsrc_t r =
+            make_rsrc32(base + (int64_t)row0 * row_stride, n * row_bytes);
+#pragma unroll
+    for (int i = 0; i < BwdCfg<D>::LPA; ++i)
+        load16_to_lds(r, arr + lo.dst[i], tr ? lo.gv[i] : lo.gk[i]);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ typename Mfma<T>::v8 row_read(const unsigned char* arr, int off) {
+    return *reinterpret_cast<const typename Mfma<T>::v8*>(arr + off);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ typename Mfma<T>::v8 tr_read(const unsigned char* arr, int t,
+                                                        const LaneOffsets<D>& lo, int db) {
+    const unsigned char* p = arr + 16 * t * BwdCfg<D>::RB;
+    const i16x4 a = lds_read_tr16(reinterpret_cast<const uint16_t*>(p + lo.tr_lo[db]));
+    const i16x4 b = lds_read_tr16(reinterpret_cast<const uint16_t*>(p + lo.tr_hi[db]));
+    return __builtin_bit_cast(typename Mfma<T>::v8,
+                              __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// 32 rows x D of a row-major tensor as the B operand of the row-by-head-dim
+// product (lane: row l32, head-dim slice 16ks + 8g .. +8); rows past the
+// range read as zero.
+template <typename T, int D>
+__device__ __forceinline__ void load_rows_b(const uint16_t* base, int64_t row_stride, int rows,
+                                            int row_bytes, int l32, int g,
+                                            typename Mfma<T>::v8* op) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base, (int64_t)rows * row_bytes);
+#pragma unroll
+    for (int ks = 0; ks < BwdCfg<D>::NKS; ++ks)
+        op[ks] = __builtin_bit_cast(typename Mfma<T>::v8,
+                                    __builtin_amdgcn_raw_buffer_load_b128(
+                                            r, l32 * row_bytes + (ks * 16 + g * 8) * 2, 0, 0));
+}
+
+// P and dS for one accumulator register: x = alpha s, sig = 1/(1 + e^-x),
+// p = silu(x) = x sig, ds = dp * sig (1 + x (1 - sig)).
+__device__ __forceinline__ void pointwise(float s, float dp, float alpha, float* p, float* ds) {
+    const float x = alpha * s;
+    const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-BWD_LOG2E * x));
+    *p = x * sig;
+    *ds = dp * (sig * __builtin_fmaf(x, 1.0f - sig, 1.0f));
+}
+
+// Writes a transposed accumulator (head-dim rows x 32 tokens: lane = token
+// l32, registers = head-dim rows 32db + 8(r/4) + 4g + r%4) scaled, rounded to
+// T; tokens at or past `rows` are dropped.
+template <typename T, int D>
+__device__ __forceinline__ void store_rows(uint16_t* base, int rows, int row_bytes, int l32, int g,
+                                           const f32x16* acc, float scale) {
+    using v4 = typename Mfma<T>::v4;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base, (int64_t)rows * row_bytes);
+#pragma unroll
+    for (int db = 0; db < BwdCfg<D>::NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f32x4 x;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = acc[db][4 * i + j] * scale;
+            const v4 y = __builtin_convertvector(x, v4);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, y), r,
+                                                  l32 * row_bytes + (db * 32 + 8 * i + 4 * g) * 2,
+                                                  0, 0);
+        }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV.  Item (sequence, head, key tile kt): keys [128 kt, 128 kt + 128).
+// Wave wv owns keys kw0 .. kw0 + 31, kw0 = 128 kt + 32 wv; query block j
+// (rows 32 j .. 32 j + 31) is streamed for j from 4 kt on.  For the wave, a
+// block below its keys is skipped, the block on its diagonal (and, with the
+// target-aware mask, any block when its keys reach the candidates) is masked,
+// and the rest are full.  LDS slot: Q (row reads), Q (transposed), dO (row
+// reads), dO (transposed).
+// ---------------------------------------------------------------------------
+template <typename T, int D, bool FUSED, bool TGT>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkv(BwdArgs a) {
+    using C = BwdCfg<D>;
+    using M = Mfma<T>;
+    using v8 = typename M::v8;
+    constexpr int SLOT = 4 * C::ARR;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * SLOT];
+    __shared__ int s_item[NQ];
+    __shared__ LocalTables lt;
+    static_assert(C::NW * 64 >= FUSE_SEQS && C::NW * 64 >= 32 * NQ, "fused tables need a thread per sequence");
+    static_assert(2 * SLOT + (int)sizeof(LocalTables) <= 160 * 1024, "LDS");
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5;
+    const int l32 = lane & 31;
+    const int H = a.heads;
+    const int64_t row_stride = (int64_t)H * D;
+    const int row_bytes = (int)(row_stride * 2);
+    const LaneOffsets<D> lo(lane, wv, row_bytes);
+
+    Tables tb;
+    if constexpr (FUSED)
+        tb = build_local_tables(lt, reinterpret_cast<int*>(lds), a.offsets, a.num_seqs, H, C::ROWS,
+                                a.wl.ctl);
+    else
+        tb = global_tables(a.wl);
+    clear_next_set(a.wl.ctl, a.wl.set);
+    ItemSource src(a.wl.ctl, a.wl.set);
+    int qx, w;
+    while (src.next(tb, s_item, &qx, &w)) {
+        const Item it = decode_item(tb, a.num_seqs, H, qx, w);
+        const int seq = __builtin_amdgcn_readfirstlane(it.seq);
+        const int head = __builtin_amdgcn_readfirstlane(it.head);
+        const int start = __builtin_amdgcn_readfirstlane(a.offsets[seq]);
+        const int s = __builtin_amdgcn_readfirstlane(a.offsets[seq + 1]) - start;
+        const int ntile = (s + C::ROWS - 1) / C::ROWS;
+        const int kt = ntile - 1 - __builtin_amdgcn_readfirstlane(it.qtile);   // costliest first
+        int hist = s;
+        if constexpr (TGT) hist = s - min(max(__builtin_amdgcn_readfirstlane(a.ntgt[seq]), 0), s);
+        const int k0i = kt * C::ROWS;
+        const int kw0 = k0i + 32 * wv;
+        const bool live = kw0 < s;
+        // Query blocks: from the item's first key to the sequence end; when
+        // every key of the item is a candidate, only its own rows see them.
+        const int q_end = (TGT && k0i >= hist) ? min(s, k0i + C::ROWS) : s;
+        const int j0 = k0i / 32;
+        const int nblk = (q_end + 31) / 32 - j0;
+        const int64_t seq_base = (int64_t)start * row_stride + (int64_t)head * D;
+        const uint16_t* qb = a.q + seq_base;
+        const uint16_t* ob = a.dout + seq_base;
+
+        v8 kop[C::NKS], vop[C::NKS];
+        load_rows_b<T, D>(a.k + seq_base + (int64_t)kw0 * row_stride, row_stride, s - kw0,
+                          row_bytes, l32, g, kop);
+        load_rows_b<T, D>(a.v + seq_base + (int64_t)kw0 * row_stride, row_stride, s - kw0,
+                          row_bytes, l32, g, vop);
+        f32x16 dk[C::NDB], dv[C::NDB];
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) dk[db] = dv[db] = (f32x16){};
+
+        auto issue = [&](int c) {
+            unsigned char* sl = lds + (c & 1) * SLOT;
+            const int row0 = 32 * (j0 + c);
+            stage<D>(qb, row_stride, row0, q_end, row_bytes, sl, lo, false);
+            stage<D>(qb, row_stride, row0, q_end, row_bytes, sl + C::ARR, lo, true);
+            stage<D>(ob, row_stride, row0, q_end, row_bytes, sl + 2 * C::ARR, lo, false);
+            stage<D>(ob, row_stride, row0, q_end, row_bytes, sl + 3 * C::ARR, lo, true);
+        };
+        if (nblk > 0) issue(0);
+        for (int c = 0; c < nblk; ++c) {
+            __builtin_amdgcn_s_waitcnt(VMCNT_LE(0));
+            __syncthreads();
+            if (c + 1 < nblk) issue(c + 1);
+            const unsigned char* sl = lds + (c & 1) * SLOT;
+            const int q0 = 32 * (j0 + c);
+            const bool skip = !live || q0 < kw0 || (TGT && kw0 >= hist && q0 > kw0);
+            if (!skip) {
+                f32x16 st = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+                for (int ks = 0; ks < C::NKS; ++ks) {
+                    st = M::mma(row_read<T, D>(sl, lo.rowrd[ks]), kop[ks], st);
+                    dp = M::mma(row_read<T, D>(sl + 2 * C::ARR, lo.rowrd[ks]), vop[ks], dp);
+                }
+                // lane: key kw0 + l32; register r: query q0 + 8(r/4) + 4g + r%4
+                const bool masked = q0 == kw0 || (TGT && kw0 + 31 >= hist);
+                const int key = kw0 + l32;
+                f32x16 p, ds;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float pr, dsr;
+                    pointwise(st[r], dp[r], a.alpha, &pr, &dsr);
+                    if (masked) {
+                        const int qr = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
+                        const bool keep = key <= qr && (key < hist || key == qr);
+                        pr = keep ? pr : 0.0f;
+                        dsr = keep ? dsr : 0.0f;
+                    }
+                    p[r] = pr;
+                    ds[r] = dsr;
+                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    f32x8 pf, df;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        pf[e] = p[8 * t + e];
+                        df[e] = ds[8 * t + e];
+                    }
+                    const v8 pb = __builtin_convertvector(pf, v8);
+                    const v8 db8 = __builtin_convertvector(df, v8);
+#pragma unroll
+                    for (int db = 0; db < C::NDB; ++db) {
+                        dv[db] = M::mma(tr_read<T, D>(sl + 3 * C::ARR, t, lo, db), pb, dv[db]);
+                        dk[db] = M::mma(tr_read<T, D>(sl + C::ARR, t, lo, db), db8, dk[db]);
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(VMCNT_LE(0));
+        __syncthreads();   // every read of the last block is done before the next item stages
+        if (live) {
+            const int64_t off = seq_base + (int64_t)kw0 * row_stride;
+            store_rows<T, D>(a.dk + off, s - kw0, row_bytes, l32, g, dk, a.g_scale);
+            store_rows<T, D>(a.dv + off, s - kw0, row_bytes, l32, g, dv, a.dv_scale);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ.  Item (sequence, head, query tile): rows [128 qt, 128 qt + 128).  Wave
+// wv owns rows wr0 .. wr0 + 31 and streams key blocks 0 .. up to its
+// diagonal; with the target-aware mask, key blocks holding only candidates
+// below the workgroup's rows are skipped altogether.  LDS slot: K (row reads),
+// K (transposed), V (row reads).
+// ---------------------------------------------------------------------------
+template <typename T, int D, bool FUSED, bool TGT>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdArgs a) {
+    using C = BwdCfg<D>;
+    using M = Mfma<T>;
+    using v8 = typename M::v8;
+    constexpr int SLOT = 3 * C::ARR;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * SLOT];
+    __shared__ int s_item[NQ];
+    __shared__ LocalTables lt;
+    static_assert(C::NW * 64 >= FUSE_SEQS && C::NW * 64 >= 32 * NQ, "fused tables need a thread per sequence");
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5;
+    const int l32 = lane & 31;
+    const int H = a.heads;
+    const int64_t row_stride = (int64_t)H * D;
+    const int row_bytes = (int)(row_stride * 2);
+    const LaneOffsets<D> lo(lane, wv, row_bytes);
+
+    Tables tb;
+    if constexpr (FUSED)
+        tb = build_local_tables(lt, reinterpret_cast<int*>(lds), a.offsets, a.num_seqs, H, C::ROWS,
+                                a.wl.ctl);
+    else
+        tb = global_tables(a.wl);
+    clear_next_set(a.wl.ctl, a.wl.set);
+    ItemSource src(a.wl.ctl, a.wl.set);
+    int qx, w;
+    while (src.next(tb, s_item, &qx, &w)) {
+        const Item it = decode_item(tb, a.num_seqs, H, qx, w);
+        const int seq = __builtin_amdgcn_readfirstlane(it.seq);
+        const int head = __builtin_amdgcn_readfirstlane(it.head);
+        const int qtile = __builtin_amdgcn_readfirstlane(it.qtile);
+        const int start = __builtin_amdgcn_readfirstlane(a.offsets[seq]);
+        const int s = __builtin_amdgcn_readfirstlane(a.offsets[seq + 1]) - start;
+        int hist = s;
+        if constexpr (TGT) hist = s - min(max(__builtin_amdgcn_readfirstlane(a.ntgt[seq]), 0), s);
+        const int q0 = qtile * C::ROWS;
+        const int wr0 = q0 + 32 * wv;
+        const bool live = wr0 < s;
+        const int kv_end = min(s, q0 + C::ROWS);
+        // Key blocks 0 .. nh-1 hold history keys; blocks nh .. q0/32 - 1 hold
+        // only candidates below every row of the item and are jumped over.
+        const int nb_all = (kv_end + 31) / 32;
+        const int nh = TGT ? (hist + 31) / 32 : nb_all;
+        const int jump = TGT ? max(q0 / 32 - nh, 0) : 0;
+        const int nblk = nb_all - jump;
+        const int64_t seq_base = (int64_t)start * row_stride + (int64_t)head * D;
+        const uint16_t* kb = a.k + seq_base;
+        const uint16_t* vb = a.v + seq_base;
+
+        v8 qop[C::NKS], oop[C::NKS];
+        load_rows_b<T, D>(a.q + seq_base + (int64_t)wr0 * row_stride, row_stride, s - wr0,
+                          row_bytes, l32, g, qop);
+        load_rows_b<T, D>(a.dout + seq_base + (int64_t)wr0 * row_stride, row_stride, s - wr0,
+                          row_bytes, l32, g, oop);
+        f32x16 dq[C::NDB];
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) dq[db] = (f32x16){};
+
+        auto issue = [&](int c) {
+            unsigned char* sl = lds + (c & 1) * SLOT;
+            const int row0 = 32 * (c >= nh ? c + jump : c);
+            stage<D>(kb, row_stride, row0, kv_end, row_bytes, sl, lo, false);
+            stage<D>(kb, row_stride, row0, kv_end, row_bytes, sl + C::ARR, lo, true);
+            stage<D>(vb, row_stride, row0, kv_end, row_bytes, sl + 2 * C::ARR, lo, false);
+        };
+        if (nblk > 0) issue(0);
+        for (int c = 0; c < nblk; ++c) {
+            __builtin_amdgcn_s_waitcnt(VMCNT_LE(0));
+            __syncthreads();
+            if (c + 1 < nblk) issue(c + 1);
+            const unsigned char* sl = lds + (c & 1) * SLOT;
+            const int k0 = 32 * (c >= nh ? c + jump : c);
+            const bool skip = !live || k0 > wr0 || (TGT && k0 >= hist && k0 + 31 < wr0);
+            if (!skip) {
+                f32x16 st = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+                for (int ks = 0; ks < C::NKS; ++ks) {
+                    st = M::mma(row_read<T, D>(sl, lo.rowrd[ks]), qop[ks], st);
+                    dp = M::mma(row_read<T, D>(sl + 2 * C::ARR, lo.rowrd[ks]), oop[ks], dp);
+                }
+                // lane: query wr0 + l32; register r: key k0 + 8(r/4) + 4g + r%4
+                const bool masked = k0 + 31 >= wr0 || (TGT && k0 + 31 >= hist);
+                const int row = wr0 + l32;
+                f32x16 ds;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float pr, dsr;
+                    pointwise(st[r], dp[r], a.alpha, &pr, &dsr);
+                    if (masked) {
+                        const int key = k0 + 8 * (r >> 2) + 4 * g + (r & 3);
+                        dsr = (key <= row && (key < hist || key == row)) ? dsr : 0.0f;
+                    }
+                    ds[r] = dsr;
+                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    f32x8 df;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) df[e] = ds[8 * t + e];
+                    const v8 db8 = __builtin_convertvector(df, v8);
+#pragma unroll
+                    for (int db = 0; db < C::NDB; ++db)
+                        dq[db] = M::mma(tr_read<T, D>(sl + C::ARR, t, lo, db), db8, dq[db]);
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(VMCNT_LE(0));
+        __syncthreads();
+        if (live)
+            store_rows<T, D>(a.dq + seq_base + (int64_t)wr0 * row_stride, s - wr0, row_bytes, l32,
+                             g, dq, a.g_scale);
+    }
+}
+
+template <typename T, int D, bool TGT>
+hipError_t launch_bwd_typed(const BwdParams& p, WorkList wl, hipStream_t stream,
+                            hipEvent_t start, hipEvent_t stop) {
+    BwdArgs a;
+    a.q = static_cast<const uint16_t*>(p.q);
+    a.k = static_cast<const uint16_t*>(p.k);
+    a.v = static_cast<const uint16_t*>(p.v);
+    a.dout = static_cast<const uint16_t*>(p.dout);
+    a.dq = static_cast<uint16_t*>(p.dq);
+    a.dk = static_cast<uint16_t*>(p.dk);
+    a.dv = static_cast<uint16_t*>(p.dv);
+    a.offsets = p.offsets;
+    a.ntgt = p.num_targets;
+    a.num_seqs = p.num_seqs;
+    a.heads = p.heads;
+    a.alpha = p.alpha;
+    a.dv_scale = 1.0f / p.n;
+    a.g_scale = p.alpha / p.n;
+    using Fn = void (*)(BwdArgs);
+    const Fn f_dkv = wl.fused ? attn_bwd_dkv<T, D, true, TGT> : attn_bwd_dkv<T, D, false, TGT>;
+    const Fn f_dq = wl.fused ? attn_bwd_dq<T, D, true, TGT> : attn_bwd_dq<T, D, false, TGT>;
+    static int grids[2][2] = {};
+    int& g_dkv = grids[wl.fused ? 1 : 0][0];
+    int& g_dq = grids[wl.fused ? 1 : 0][1];
+    if (!g_dkv) g_dkv = resident_grid(f_dkv, 256);
+    if (!g_dq) g_dq = resident_grid(f_dq, 256);
+    // dK/dV on this call's counter set, then dQ on the other one (each launch
+    // clears the set the one after it uses).
+    a.wl = wl;
+    if (start)
+        hipExtLaunchKernelGGL(f_dkv, dim3(g_dkv), dim3(256), 0, stream, start, nullptr, 0, a);
+    else
+        hipLaunchKernelGGL(f_dkv, dim3(g_dkv), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.wl.set = wl.set ^ 1;
+    if (stop)
+        hipExtLaunchKernelGGL(f_dq, dim3(g_dq), dim3(256), 0, stream, nullptr, stop, 0, a);
+    else
+        hipLaunchKernelGGL(f_dq, dim3(g_dq), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_mask(const BwdParams& p, WorkList wl, hipStream_t stream, hipEvent_t start,
+                           hipEvent_t stop) {
+    return p.num_targets ? launch_bwd_typed<T, D, true>(p, wl, stream, start, stop)
+                         : launch_bwd_typed<T, D, false>(p, wl, stream, start, stop);
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BwdParams& p, Dtype dt, WorkList wl, hipStream_t stream,
+                           hipEvent_t start, hipEvent_t stop) {
+    if (dt == Dtype::BF16)
+        return p.d == 64 ? launch_bwd_mask<__bf16, 64>(p, wl, stream, start, stop)
+                         : launch_bwd_mask<__bf16, 128>(p, wl, stream, start, stop);
+    if (dt == Dtype::FP16)
+        return p.d == 64 ? launch_bwd_mask<_Float16, 64>(p, wl, stream, start, stop)
+                         : launch_bwd_mask<_Float16, 128>(p, wl, stream, start, stop);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace hstu

@@ -144,6 +144,47 @@ struct FwdParams {
 // Rows of Q handled by one work item for this element type and head size.
 int q_tile_rows(Dtype dt, int d);
 
+// Compute units of the current device.
+int device_cus();
+
+// Workgroups of `fn` (with `threads` threads) that fit on the device at once.
+template <typename KernelFn>
+int resident_grid(KernelFn fn, int threads) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess ||
+        per_cu <= 0)
+        per_cu = 1;
+    return per_cu * device_cus();
+}
+
+// Backward: gradients of the forward with respect to q, k and v for an
+// upstream gradient dout (bf16 / fp16 only).  Work items are 128-row tiles of
+// each (sequence, head): the work list must be built with BWD_TILE_ROWS.
+constexpr int BWD_TILE_ROWS = 128;
+
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    const int32_t* offsets;
+    const int32_t* num_targets;   // candidates per sequence, or null (plain causal)
+    int num_seqs;
+    int heads;
+    int d;
+    float alpha;
+    float n;
+};
+
+// Enqueues the dK/dV kernel (on counter set wl.set) and then the dQ kernel
+// (on the other set).  `start` / `stop`, when given, are recorded on the
+// first and second dispatch.
+hipError_t launch_backward(const BwdParams& p, Dtype dt, WorkList wl, hipStream_t stream,
+                           hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+
 // Enqueues the attention kernel (the work list must already be built on the
 // same stream).  `grid` = 0 picks the resident-workgroup count of the device.
 hipError_t launch_attention(const FwdParams& p, Dtype dt, WorkList wl, int grid,

@@ -146,6 +146,39 @@ hstu_status_t hstu_attn_fwd_cached(const void* q, const void* k, const void* v,
                                    int32_t num_seqs, int32_t heads, int32_t d, float alpha,
                                    float n, void* out, hipStream_t stream, hstu_dtype_t dtype);
 
+/* Backward: gradients of hstu_attn_fwd (or, with num_targets, of
+ * hstu_attn_fwd_targets) with respect to q, k and v, for the upstream
+ * gradient dout = dLoss/dout.  The attention is recomputed block by block and
+ * nothing of size T x T is stored (HSTU paper translation, Appendix G); the
+ * gradients are the derivative of the forward definition.  Per sequence,
+ * head and kept (row r, key c) pair, with x = alpha <q_r, k_c>:
+ *
+ *   dv_c += silu(x) / n * dout_r
+ *   g     = (alpha / n) * silu'(x) * <dout_r, v_c>,  silu'(x) = sig(x) (1 + x (1 - sig(x)))
+ *   dq_r += g * k_c,   dk_c += g * q_r
+ *
+ *   q, k, v, dout  : (T, heads, d) inputs as for the forward; dout has their type.
+ *   dq, dk, dv     : (T, heads, d) outputs of the same type, fully written
+ *                    (rounded to nearest even from fp32 accumulation); 16-byte
+ *                    aligned, none overlapping another or any input.
+ *   num_targets    : as for hstu_attn_fwd_targets (device int32[num_seqs]).
+ *
+ * Element types: bfloat16 and float16 only (HSTU_FP32 returns
+ * HSTU_ERR_UNSUPPORTED).  P = silu(x) and the score gradient are rounded to
+ * the input type before their products, as the forward rounds its weights.
+ * A call is two kernels (dk/dv, then dq; plus the work-list kernel on a new
+ * scratch area or for more than 256 sequences).  Streams, scratch and errors
+ * as for hstu_attn_fwd. */
+hstu_status_t hstu_attn_bwd(const void* q, const void* k, const void* v, const void* dout,
+                            const int32_t* seq_offsets, int32_t num_seqs, int32_t heads,
+                            int32_t d, float alpha, float n, void* dq, void* dk, void* dv,
+                            hipStream_t stream, hstu_dtype_t dtype);
+hstu_status_t hstu_attn_bwd_targets(const void* q, const void* k, const void* v,
+                                    const void* dout, const int32_t* seq_offsets,
+                                    const int32_t* num_targets, int32_t num_seqs, int32_t heads,
+                                    int32_t d, float alpha, float n, void* dq, void* dk,
+                                    void* dv, hipStream_t stream, hstu_dtype_t dtype);
+
 /* Checks device offsets synchronously: off[0] == 0 and non-decreasing.  Writes
  * T = off[num_seqs] to *total (may be NULL).  Returns HSTU_OK or
  * HSTU_ERR_BAD_OFFSETS; synchronises `stream`. */

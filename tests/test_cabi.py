@@ -133,6 +133,47 @@ def test_cached_empty_batch_is_a_no_op(lib):
                         out=None, num_seqs=0) == hstu.HSTU_OK
 
 
+def _call_bwd(lib, dout=48, dq=64, dk=80, dv=96, tg=None, **kw):
+    a = dict(q=16, k=16, v=16, off=16, num_seqs=1, heads=1, d=64, alpha=0.1, n=1.0,
+             dtype=hstu.HSTU_BF16)
+    a.update(kw)
+    head = (a["q"], a["k"], a["v"], dout, a["off"])
+    tail = (a["num_seqs"], a["heads"], a["d"], a["alpha"], a["n"], dq, dk, dv, None, a["dtype"])
+    if tg is None:
+        return lib.hstu_attn_bwd(*head, *tail)
+    return lib.hstu_attn_bwd_targets(*head, tg, *tail)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dout=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(dq=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(dk=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(dv=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(dk=72), hstu.HSTU_ERR_INVALID_ARG),       # misaligned
+    (dict(dq=48), hstu.HSTU_ERR_INVALID_ARG),       # dq aliases dout
+    (dict(dk=64), hstu.HSTU_ERR_INVALID_ARG),       # dk aliases dq
+    (dict(dv=16), hstu.HSTU_ERR_INVALID_ARG),       # dv aliases q
+    (dict(dtype=hstu.HSTU_FP32), hstu.HSTU_ERR_UNSUPPORTED),
+    (dict(d=96), hstu.HSTU_ERR_UNSUPPORTED),
+    (dict(n=0.0), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(tg=0), hstu.HSTU_ERR_INVALID_ARG),        # target counts missing
+    (dict(tg=50), hstu.HSTU_ERR_INVALID_ARG),       # misaligned target counts
+])
+def test_bwd_argument_checks(lib, kw, status):
+    kw = dict(kw)
+    if kw.get("tg") == 0:
+        kw["tg"] = None
+        assert lib.hstu_attn_bwd_targets(16, 16, 16, 48, 16, None, 1, 1, 64, 0.1, 1.0, 64, 80,
+                                         96, None, hstu.HSTU_BF16) == status
+        return
+    assert _call_bwd(lib, **kw) == status
+
+
+def test_bwd_empty_batch_is_a_no_op(lib):
+    assert _call_bwd(lib, dout=None, dq=None, dk=None, dv=None, q=None, k=None, v=None, off=None,
+                     num_seqs=0) == hstu.HSTU_OK
+
+
 def test_status_strings(lib):
     for st in (0, -1, -2, -3, -4, -5):
         assert lib.hstu_status_string(st)
