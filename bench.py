@@ -17,7 +17,11 @@ workload.
 1024 candidates) (the target-aware mask of M-FALCON ranking, HSTU paper
 translation Appendix H); useful FLOPs then count the pairs that mask keeps.  --cached times
 hstu_attn_fwd_cached on 16 users x (3072 cached history rows, 1024 candidates)
-(M-FALCON's later micro-batches): t (h + 1) pairs per request.
+(M-FALCON's later micro-batches): t (h + 1) pairs per request.  --backward
+times hstu_attn_bwd (dq, dk, dv) on the 16 x 4096 workload: useful FLOPs are
+the five products of a recomputing backward, 10 * heads * d per kept pair
+(2.5x the forward's); the kernels run seven (S and dP are formed by both the
+dK/dV and the dQ kernel).
 """
 from __future__ import annotations
 
@@ -38,6 +42,7 @@ PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
 PEAK_HBM_GBS = 8000.0
 METRIC = "HSTU attn fwd useful TFLOP/s, % bf16 MFMA peak; ms at QKV(16,4,4096,64)"
 METRIC_TARGETS = "HSTU target-aware attn fwd useful TFLOP/s (M-FALCON mask)"
+METRIC_BWD = "HSTU attn bwd (dq, dk, dv) useful TFLOP/s"
 METRIC_CACHED = "HSTU cached-history attn fwd useful TFLOP/s (M-FALCON micro-batch)"
 # HBM traffic per dispatch of the attention kernel, from two rocprofv3 --pmc
 # runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
@@ -121,6 +126,33 @@ def cpu_baseline_cached(cc, budget_s: float):
                       f"{threads} threads available"}
 
 
+def cpu_baseline_bwd(case, dout, budget_s: float):
+    """The oracle's backward on whole sequences, in input order, until about
+    budget_s of wall time has been spent."""
+    import oracle
+    lib = oracle.load()
+    threads = oracle.threads(lib)
+    off = case.offsets
+    per_call = max(1, -(-threads // case.heads))
+    done_flops, done_s, seqs, i = 0.0, 0.0, 0, 0
+    while i < case.num_seqs and done_s < budget_s:
+        j = min(case.num_seqs, i + per_call)
+        a, b = int(off[i]), int(off[j])
+        t0 = time.perf_counter()
+        oracle.bwd(case.q[a:b], case.k[a:b], case.v[a:b], dout[a:b], off[i:j + 1] - off[i],
+                   case.heads, case.d, case.alpha, case.n, case.dtype, lib=lib)
+        done_s += time.perf_counter() - t0
+        s = case.lengths[i:j].astype(np.float64)
+        done_flops += float(np.sum(10.0 * case.heads * case.d * s * (s + 1.0) / 2.0))
+        seqs += j - i
+        i = j
+    return {"value": done_flops / done_s / 1e12, "unit": "TFLOP/s",
+            "cores": min(threads, per_call * case.heads), "kind": "oracle",
+            "sample": f"{seqs} of {case.num_seqs} sequences, all heads; fp64 loop oracle "
+                      f"backward (OpenMP over (sequence, head)), {done_s:.1f} s wall, "
+                      f"{threads} threads available"}
+
+
 def cpu_baseline(case, budget_s: float):
     """Time the oracle on whole sequences of the workload (all heads).  Each
     oracle call takes enough sequences to give every OpenMP thread a
@@ -166,6 +198,8 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--targets", action="store_true",
                     help="time the target-aware forward on 16 x (3072 history + 1024 candidates)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (dq, dk, dv) on the chosen workload")
     ap.add_argument("--cached", action="store_true",
                     help="time the cached-history forward on 16 x (3072 cached rows, "
                          "1024 candidates)")
@@ -175,6 +209,8 @@ def main() -> int:
                     help="run only a plain 1 GiB device copy (3 times), the reference for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
+    if args.targets + args.cached + args.backward > 1:
+        ap.error("--targets, --cached and --backward are separate benchmarks")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(each GPU would run its own share of sequences with no exchange).",
@@ -224,6 +260,19 @@ def main() -> int:
 
         def call():
             hstu.hstu_attn_fwd_targets(q, k, v, off, tg, case.alpha, case.n, out=out)
+    elif args.backward:
+        dout_host = workloads.make_case(list(case.lengths), case.heads, case.d, case.dtype,
+                                        seed=2000).q
+        dout = to_device(workloads.Case(name="", dtype=case.dtype, heads=case.heads, d=case.d,
+                                        offsets=case.offsets, q=dout_host, k=dout_host,
+                                        v=dout_host, alpha=case.alpha, n=case.n))[0]
+        grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
+        flops *= 2.5
+        # q, k, v, dout read once, dq, dk, dv written once
+        alg_bytes *= 7.0 / 4.0
+
+        def call():
+            hstu.hstu_attn_bwd(q, k, v, dout, off, case.alpha, case.n, grads=grads)
     else:
         def call():
             hstu.hstu_attn_fwd(q, k, v, off, case.alpha, case.n, out=out)
@@ -252,21 +301,28 @@ def main() -> int:
     sched_ms = kt.sched_ms / max(1, kt.calls)
     achieved = flops / (attn_ms * 1e-3) / 1e12
     peak = PEAK_MFMA_TFLOPS[case.dtype]
-    traffic = None if (args.targets or args.cached) else traffic_bytes(args.workload)
+    traffic = (None if (args.targets or args.cached or args.backward)
+               else traffic_bytes(args.workload))
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-                "kernel": "attn_fwd_mfma16" if case.dtype != "fp32" else "attn_fwd_mfma_f32",
+                "kernel": ("attn_bwd_dkv + attn_bwd_dq" if args.backward else
+                           "attn_fwd_mfma16" if case.dtype != "fp32" else "attn_fwd_mfma_f32"),
                 "kernel_ms": round(attn_ms, 5), "sched_kernel_ms": round(sched_ms, 5),
                 "hbm_frac": round(alg_bytes / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
     cpu = None
     if args.cpu_budget > 0:
-        cpu = (cpu_baseline_cached(cc, args.cpu_budget) if args.cached else
-               cpu_baseline(case, args.cpu_budget))
+        if args.cached:
+            cpu = cpu_baseline_cached(cc, args.cpu_budget)
+        elif args.backward:
+            cpu = cpu_baseline_bwd(case, dout_host, args.cpu_budget)
+        else:
+            cpu = cpu_baseline(case, args.cpu_budget)
 
     L = case.lengths
     line = {
-        "metric": (METRIC_CACHED if args.cached else METRIC_TARGETS if args.targets else METRIC),
+        "metric": (METRIC_CACHED if args.cached else METRIC_TARGETS if args.targets else
+                   METRIC_BWD if args.backward else METRIC),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
