@@ -42,6 +42,7 @@ PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
 PEAK_HBM_GBS = 8000.0
 METRIC = "HSTU attn fwd useful TFLOP/s, % bf16 MFMA peak; ms at QKV(16,4,4096,64)"
 METRIC_TARGETS = "HSTU target-aware attn fwd useful TFLOP/s (M-FALCON mask)"
+METRIC_DENSE = "HSTU attn fwd useful TFLOP/s, dense (b, heads, s, d) layout"
 METRIC_BWD = "HSTU attn bwd (dq, dk, dv) useful TFLOP/s"
 METRIC_CACHED = "HSTU cached-history attn fwd useful TFLOP/s (M-FALCON micro-batch)"
 # HBM traffic per dispatch of the attention kernel, from two rocprofv3 --pmc
@@ -198,6 +199,9 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--targets", action="store_true",
                     help="time the target-aware forward on 16 x (3072 history + 1024 candidates)")
+    ap.add_argument("--dense", action="store_true",
+                    help="time hstu_attn_fwd_dense on the chosen workload's shape laid out "
+                         "(batch, heads, seq_len, d) (equal lengths only)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (dq, dk, dv) on the chosen workload")
     ap.add_argument("--cached", action="store_true",
@@ -209,8 +213,8 @@ def main() -> int:
                     help="run only a plain 1 GiB device copy (3 times), the reference for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
-    if args.targets + args.cached + args.backward > 1:
-        ap.error("--targets, --cached and --backward are separate benchmarks")
+    if args.targets + args.cached + args.backward + args.dense > 1:
+        ap.error("--targets, --cached, --backward and --dense are separate benchmarks")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(each GPU would run its own share of sequences with no exchange).",
@@ -260,6 +264,17 @@ def main() -> int:
 
         def call():
             hstu.hstu_attn_fwd_targets(q, k, v, off, tg, case.alpha, case.n, out=out)
+    elif args.dense:
+        L = case.lengths
+        if L.size == 0 or np.any(L != L[0]):
+            ap.error("--dense needs a workload of equal lengths")
+        B, S, H, D = case.num_seqs, int(L[0]), case.heads, case.d
+        qd, kd, vd = (x.reshape(B, S, H, D).permute(0, 2, 1, 3).contiguous()
+                      for x in (q, k, v))
+        outd = torch.empty_like(qd)
+
+        def call():
+            hstu.hstu_attn_fwd_dense(qd, kd, vd, case.alpha, case.n, out=outd)
     elif args.backward:
         dout_host = workloads.make_case(list(case.lengths), case.heads, case.d, case.dtype,
                                         seed=2000).q
@@ -301,7 +316,7 @@ def main() -> int:
     sched_ms = kt.sched_ms / max(1, kt.calls)
     achieved = flops / (attn_ms * 1e-3) / 1e12
     peak = PEAK_MFMA_TFLOPS[case.dtype]
-    traffic = (None if (args.targets or args.cached or args.backward)
+    traffic = (None if (args.targets or args.cached or args.backward or args.dense)
                else traffic_bytes(args.workload))
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
@@ -322,7 +337,7 @@ def main() -> int:
     L = case.lengths
     line = {
         "metric": (METRIC_CACHED if args.cached else METRIC_TARGETS if args.targets else
-                   METRIC_BWD if args.backward else METRIC),
+                   METRIC_BWD if args.backward else METRIC_DENSE if args.dense else METRIC),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -340,6 +355,7 @@ def main() -> int:
                    "d": case.d, "alpha": case.alpha, "n": case.n,
                    **({"candidates_per_seq": int(case.num_targets[0])} if args.targets else {}),
                    **({"cached_history_per_seq": int(cc.hist_lengths[0])} if args.cached else {}),
+                   **({"layout": "(batch, heads, seq_len, d)"} if args.dense else {}),
                    "useful_gflop": round(flops / 1e9, 3)},
         "roofline": roofline,
         "cpu_baseline": cpu,

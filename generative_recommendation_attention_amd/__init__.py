@@ -31,7 +31,7 @@ HSTU_BF16, HSTU_FP16, HSTU_FP32 = 0, 1, 2
 
 # Every symbol include/hstu.h declares.
 EXPORTS = ("hstu_attn_fwd", "hstu_attn_fwd_bf16", "hstu_attn_fwd_fp16", "hstu_attn_fwd_fp32",
-           "hstu_attn_fwd_targets", "hstu_attn_fwd_cached", "hstu_attn_bwd",
+           "hstu_attn_fwd_targets", "hstu_attn_fwd_cached", "hstu_attn_fwd_dense", "hstu_attn_bwd",
            "hstu_attn_bwd_targets", "hstu_validate_offsets", "hstu_status_string", "hstu_last_hip_error",
            "hstu_release_workspace", "hstu_profile_enable", "hstu_profile_read")
 
@@ -78,6 +78,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hstu_attn_fwd_cached.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, vp,
                                          vp, ctypes.c_int]
     lib.hstu_attn_fwd_cached.restype = ctypes.c_int
+    lib.hstu_attn_fwd_dense.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, f32, vp, vp,
+                                        ctypes.c_int]
+    lib.hstu_attn_fwd_dense.restype = ctypes.c_int
     lib.hstu_attn_bwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp, vp, vp,
                                   ctypes.c_int]
     lib.hstu_attn_bwd.restype = ctypes.c_int
@@ -301,3 +304,29 @@ def hstu_attn_bwd(q, k, v, dout, seq_offsets, alpha: float, n: float, num_target
         st = lib.hstu_attn_bwd_targets(*args, num_targets.data_ptr(), *tail)
         _check(st, "hstu_attn_bwd_targets")
     return dq, dk, dv
+
+
+def hstu_attn_fwd_dense(q, k, v, alpha: float, n: float, out=None, stream=None):
+    """Causal HSTU attention forward on dense (batch, heads, seq_len, d)
+    tensors (every position is a token); returns `out` of the same shape."""
+    import torch
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one (batch, heads, seq_len, d) shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one element type")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous GPU tensors")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    B, heads, S, d = q.shape
+    if q.numel() == 0:
+        return out
+    lib = load_library()
+    st = lib.hstu_attn_fwd_dense(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, heads, S, d,
+                                 float(alpha), float(n), out.data_ptr(), _stream_handle(stream),
+                                 _dtype_code(q))
+    _check(st, "hstu_attn_fwd_dense")
+    return out

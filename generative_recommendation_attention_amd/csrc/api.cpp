@@ -30,6 +30,11 @@ struct Scratch {
     size_t bytes = 0;
     unsigned epoch = 0;   // calls completed on this area; call e uses counter set e % 2
     bool clean = false;   // counter set epoch % 2 is known to be zero
+    // Offsets i * len of the dense layout, written at ramp_at by an earlier
+    // call on this area (ramp_count = 0: none).
+    size_t ramp_at = 0;
+    int ramp_count = 0;
+    int64_t ramp_len = 0;
 };
 
 std::mutex g_scratch_mu;
@@ -63,9 +68,17 @@ hstu_status_t scratch_for(int dev, hipStream_t stream, size_t bytes, Scratch** o
         s.bytes = want;
         s.epoch = 0;
         s.clean = false;
+        s.ramp_count = 0;
     }
     *out = &s;
     return HSTU_OK;
+}
+
+// A call whose work list reaches `bytes` into the area overwrites a dense
+// offset ramp stored there.
+void forget_ramp_under(Scratch* sc, size_t bytes) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (sc->ramp_count && bytes > sc->ramp_at) sc->ramp_count = 0;
 }
 
 // ---- device checks ----------------------------------------------------------
@@ -176,6 +189,9 @@ struct MaskInputs {
     const void* k_cache = nullptr;
     const void* v_cache = nullptr;
     const int32_t* hist_offsets = nullptr;
+    // Dense (B, heads, S, D) layout: num_seqs = B, dense_len = S, no offsets.
+    bool dense = false;
+    int64_t dense_len = 0;
 };
 
 // One forward call.
@@ -183,7 +199,10 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
                             const int32_t* seq_offsets, const MaskInputs& mi, int32_t num_seqs,
                             int32_t heads, int32_t d, float alpha, float n, void* out,
                             hipStream_t stream, int dtype) {
-    hstu_status_t st = check_args(q, k, v, seq_offsets, num_seqs, heads, d, alpha, n, out, dtype);
+    // (the dense entry point checks its own arguments and passes no offsets)
+    hstu_status_t st = mi.dense ? HSTU_OK
+                                : check_args(q, k, v, seq_offsets, num_seqs, heads, d, alpha, n,
+                                             out, dtype);
     if (st != HSTU_OK || num_seqs == 0) return st;
     int dev = 0;
     st = check_device(&dev);
@@ -191,9 +210,31 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
 
     const hstu::Dtype dt = static_cast<hstu::Dtype>(dtype);
     Scratch* sc = nullptr;
-    st = scratch_for(dev, stream, hstu::worklist_bytes(num_seqs, heads), &sc);
+    const size_t wl_bytes = (hstu::worklist_bytes(num_seqs, heads) + 255) & ~(size_t)255;
+    const size_t ramp_bytes = mi.dense ? sizeof(int32_t) * ((size_t)num_seqs + 1) : 0;
+    st = scratch_for(dev, stream, wl_bytes + ramp_bytes, &sc);
     if (st != HSTU_OK) return st;
     hstu::WorkList wl = hstu::worklist_carve(sc->ptr, num_seqs, heads);
+    forget_ramp_under(sc, wl_bytes);
+    if (mi.dense) {
+        // Offsets i * S in the scratch area, written once per (area, B, S).
+        int32_t* ramp = reinterpret_cast<int32_t*>(static_cast<char*>(sc->ptr) + wl_bytes);
+        bool have;
+        {
+            std::lock_guard<std::mutex> lock(g_scratch_mu);
+            have = sc->ramp_count == num_seqs && sc->ramp_len == mi.dense_len &&
+                   sc->ramp_at == wl_bytes;
+        }
+        if (!have) {
+            hipError_t e = hstu::launch_fill_ramp(ramp, num_seqs + 1, (int)mi.dense_len, stream);
+            if (e != hipSuccess) return hip_fail(e);
+            std::lock_guard<std::mutex> lock(g_scratch_mu);
+            sc->ramp_count = num_seqs;
+            sc->ramp_len = mi.dense_len;
+            sc->ramp_at = wl_bytes;
+        }
+        seq_offsets = ramp;
+    }
     // Small batches build their queue tables inside the attention kernel.  The
     // work-list kernel still runs when this call's counter set is not known to
     // be zero (a new scratch area, or a failed launch before; it zeroes both
@@ -219,6 +260,8 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
     p.k_cache = mi.k_cache;
     p.v_cache = mi.v_cache;
     p.hist_offsets = mi.hist_offsets;
+    p.dense = mi.dense;
+    p.dense_len = mi.dense_len;
     p.num_seqs = num_seqs;
     p.heads = heads;
     p.d = d;
@@ -283,6 +326,7 @@ hstu_status_t attn_bwd_call(const void* q, const void* k, const void* v, const v
     st = scratch_for(dev, stream, hstu::worklist_bytes(num_seqs, heads), &sc);
     if (st != HSTU_OK) return st;
     hstu::WorkList wl = hstu::worklist_carve(sc->ptr, num_seqs, heads);
+    forget_ramp_under(sc, hstu::worklist_bytes(num_seqs, heads));
     const hstu::SortChoice sort = sort_choice_env();
     bool clean;
     {
@@ -356,6 +400,26 @@ hstu_status_t hstu_attn_fwd_targets(const void* q, const void* k, const void* v,
     mi.num_targets = num_targets;
     return attn_fwd_call(q, k, v, seq_offsets, mi, num_seqs, heads, d, alpha, n, out, stream,
                          dtype);
+}
+
+hstu_status_t hstu_attn_fwd_dense(const void* q, const void* k, const void* v, int32_t batch,
+                                  int32_t heads, int32_t seq_len, int32_t d, float alpha, float n,
+                                  void* out, hipStream_t stream, hstu_dtype_t dtype) {
+    if (dtype != HSTU_BF16 && dtype != HSTU_FP16 && dtype != HSTU_FP32) return HSTU_ERR_UNSUPPORTED;
+    if (batch < 0 || heads < 1 || seq_len < 0) return HSTU_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return HSTU_ERR_UNSUPPORTED;
+    if ((long long)batch * seq_len > 0x7fffffffLL || (long long)batch * heads > 0x7fffffffLL)
+        return HSTU_ERR_UNSUPPORTED;
+    if (!std::isfinite(alpha) || !std::isfinite(n) || n == 0.0f) return HSTU_ERR_INVALID_ARG;
+    if (batch == 0 || seq_len == 0) return HSTU_OK;
+    if (!q || !k || !v || !out) return HSTU_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return HSTU_ERR_INVALID_ARG;
+    if (out == q || out == k || out == v) return HSTU_ERR_INVALID_ARG;
+    MaskInputs mi;
+    mi.dense = true;
+    mi.dense_len = seq_len;
+    return attn_fwd_call(q, k, v, nullptr, mi, batch, heads, d, alpha, n, out, stream, dtype);
 }
 
 hstu_status_t hstu_attn_bwd(const void* q, const void* k, const void* v, const void* dout,

@@ -54,6 +54,8 @@ struct KernelArgs {
     const uint16_t* vc;
     const int32_t* hoff;   // history offsets (MASK_CACHED), or null
     WorkList wl;
+    int64_t row_stride;    // elements between consecutive tokens of one head
+    int64_t head_stride;   // elements between heads of one token
     int num_seqs;
     int heads;
     float score_scale;  // -alpha * log2(e)
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
     const int g = lane >> 5;
     const int l32 = lane & 31;
     const int H = a.heads;
-    const int64_t row_stride = (int64_t)H * D;      // elements between consecutive tokens
+    const int64_t row_stride = a.row_stride;        // elements between consecutive tokens
     const int row_bytes = (int)(row_stride * 2);    // bytes between consecutive tokens
 
     // Lane-constant parts of the addresses.
@@ -238,7 +240,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
         const int tiles_a = full_blocks / NKB;             // phase A tiles (all below nh)
         const int last_tile = last_block / NKB;
         const int tiles_ab = live ? (last_tile >= nh ? last_tile - jump : last_tile) + 1 : 0;
-        const int64_t seq_base = (int64_t)start * row_stride + (int64_t)head * D;
+        // Sequence i's rows of head h start at off[i] * heads * D + h * head_stride:
+        // the jagged (T, heads, D) layout has head_stride D and row stride
+        // heads * D, the dense (B, heads, S, D) one (off[i] = i S) S * D and D.
+        const int64_t seq_base = (int64_t)start * H * D + (int64_t)head * a.head_stride;
 
         // Loop tile c into slot c % NS.  The buffer range covers the tile's
         // rows that some row of the workgroup sees (none past kv_end, none
@@ -579,6 +584,8 @@ struct KernelArgsF32 {
     const float* vc;
     const int32_t* hoff;   // history offsets: the cached-history form when non-null
     WorkList wl;
+    int64_t row_stride;
+    int64_t head_stride;
     int num_seqs;
     int heads;
     float score_scale;
@@ -601,7 +608,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
     const int g = lane >> 5;
     const int l32 = lane & 31;
     const int H = a.heads;
-    const int64_t row_stride = (int64_t)H * D;
+    const int64_t row_stride = a.row_stride;
 
     Tables tb;
     if constexpr (FUSED)
@@ -635,7 +642,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
         const int wr0 = q0 + wv * 32;
         const bool wave_live = wr0 < s;
         const int my_row = wr0 + l32;
-        const int64_t seq_base = (int64_t)start * row_stride + (int64_t)it.head * D;
+        const int64_t seq_base = (int64_t)start * H * D + (int64_t)it.head * a.head_stride;
 
         float qf[D / 2];
         {
@@ -744,6 +751,8 @@ hipError_t launch16(const FwdParams& p, WorkList wl, int grid, hipStream_t strea
     a.kc = static_cast<const uint16_t*>(p.k_cache);
     a.vc = static_cast<const uint16_t*>(p.v_cache);
     a.hoff = p.hist_offsets;
+    a.row_stride = p.dense ? p.d : (int64_t)p.heads * p.d;
+    a.head_stride = p.dense ? p.dense_len * p.d : p.d;
     a.wl = wl;
     a.num_seqs = p.num_seqs;
     a.heads = p.heads;
@@ -786,6 +795,8 @@ hipError_t launch_f32(const FwdParams& p, WorkList wl, int grid, hipStream_t str
     a.kc = static_cast<const float*>(p.k_cache);
     a.vc = static_cast<const float*>(p.v_cache);
     a.hoff = p.hist_offsets;
+    a.row_stride = p.dense ? p.d : (int64_t)p.heads * p.d;
+    a.head_stride = p.dense ? p.dense_len * p.d : p.d;
     a.wl = wl;
     a.num_seqs = p.num_seqs;
     a.heads = p.heads;

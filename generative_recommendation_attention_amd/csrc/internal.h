@@ -123,6 +123,9 @@ hipError_t launch_schedule(const int32_t* offsets, int num_seqs, int heads, int 
 
 enum class Dtype : int { BF16 = 0, FP16 = 1, FP32 = 2 };
 
+// Writes dst[i] = i * step for i < count (offsets of equal-length sequences).
+hipError_t launch_fill_ramp(int32_t* dst, int count, int step, hipStream_t stream);
+
 struct FwdParams {
     const void* q;
     const void* k;
@@ -134,6 +137,9 @@ struct FwdParams {
     const void* k_cache;          // history K, V (T_hist, heads, d), or null
     const void* v_cache;
     const int32_t* hist_offsets;  // int32[num_seqs + 1], or null (not the cached form)
+    // Dense (B, heads, S, D) layout: offsets are then i * S, S = dense_len.
+    bool dense = false;
+    int64_t dense_len = 0;
     int num_seqs;
     int heads;
     int d;

@@ -238,6 +238,20 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
 
 }  // namespace
 
+namespace {
+__global__ void fill_ramp_kernel(int32_t* dst, int count, int step) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count) dst[i] = i * step;
+}
+}  // namespace
+
+hipError_t launch_fill_ramp(int32_t* dst, int count, int step, hipStream_t stream) {
+    if (count <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_ramp_kernel, dim3((count + 255) / 256), dim3(256), 0, stream, dst,
+                       count, step);
+    return hipGetLastError();
+}
+
 hipError_t launch_schedule(const int32_t* offsets, int num_seqs, int heads, int q_tile_rows,
                            WorkList wl, hipStream_t stream, SortChoice choice, hipEvent_t start,
                            hipEvent_t stop) {

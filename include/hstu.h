@@ -146,6 +146,20 @@ hstu_status_t hstu_attn_fwd_cached(const void* q, const void* k, const void* v,
                                    int32_t num_seqs, int32_t heads, int32_t d, float alpha,
                                    float n, void* out, hipStream_t stream, hstu_dtype_t dtype);
 
+/* The forward on the dense padded layout of the Ascend HSTU blog's PyTorch
+ * definition (§1: Q, K, V of shape (b, heads, s, d); §4.1 describes this
+ * padded layout before replacing it by the jagged one): q, k, v, out are
+ * row-major (batch, heads, seq_len, d), element (b, h, r, e) at
+ * ((b * heads + h) * seq_len + r) * d + e, and every one of the seq_len
+ * positions of every batch entry is a token (the causal mask runs over all of
+ * them; padding, if any, is computed like any other row).  No offsets are
+ * passed: the library writes i * seq_len into its scratch area once per
+ * (stream, batch, seq_len).  batch * seq_len < 2^31.  Element types, scalars,
+ * alignment, aliasing, streams and errors as in hstu_attn_fwd. */
+hstu_status_t hstu_attn_fwd_dense(const void* q, const void* k, const void* v, int32_t batch,
+                                  int32_t heads, int32_t seq_len, int32_t d, float alpha, float n,
+                                  void* out, hipStream_t stream, hstu_dtype_t dtype);
+
 /* Backward: gradients of hstu_attn_fwd (or, with num_targets, of
  * hstu_attn_fwd_targets) with respect to q, k and v, for the upstream
  * gradient dout = dLoss/dout.  The attention is recomputed block by block and

@@ -174,6 +174,25 @@ def test_bwd_empty_batch_is_a_no_op(lib):
                      num_seqs=0) == hstu.HSTU_OK
 
 
+@pytest.mark.parametrize("args,status", [
+    ((None, 16, 16, 2, 1, 8, 64, 0.1, 1.0, 32), hstu.HSTU_ERR_INVALID_ARG),
+    ((16, 16, 16, -1, 1, 8, 64, 0.1, 1.0, 32), hstu.HSTU_ERR_INVALID_ARG),
+    ((16, 16, 16, 2, 0, 8, 64, 0.1, 1.0, 32), hstu.HSTU_ERR_INVALID_ARG),
+    ((16, 16, 16, 2, 1, -8, 64, 0.1, 1.0, 32), hstu.HSTU_ERR_INVALID_ARG),
+    ((16, 16, 16, 2, 1, 8, 80, 0.1, 1.0, 32), hstu.HSTU_ERR_UNSUPPORTED),
+    ((16, 16, 16, 2, 1, 8, 64, 0.1, 0.0, 32), hstu.HSTU_ERR_INVALID_ARG),
+    ((16, 16, 16, 2, 1, 8, 64, 0.1, 1.0, 16), hstu.HSTU_ERR_INVALID_ARG),   # out aliases q
+    ((24, 16, 16, 2, 1, 8, 64, 0.1, 1.0, 32), hstu.HSTU_ERR_INVALID_ARG),   # misaligned
+    ((16, 16, 16, 70000, 1, 70000, 64, 0.1, 1.0, 32), hstu.HSTU_ERR_UNSUPPORTED),
+    ((None, None, None, 0, 1, 8, 64, 0.1, 1.0, None), hstu.HSTU_OK),        # empty batch
+    ((None, None, None, 3, 1, 0, 64, 0.1, 1.0, None), hstu.HSTU_OK),        # empty sequences
+])
+def test_dense_argument_checks(lib, args, status):
+    # (every case has an argument the host rejects, so no device work is ever
+    # enqueued with these stand-in pointers)
+    assert lib.hstu_attn_fwd_dense(*args, None, hstu.HSTU_BF16) == status
+
+
 def test_status_strings(lib):
     for st in (0, -1, -2, -3, -4, -5):
         assert lib.hstu_status_string(st)
