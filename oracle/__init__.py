@@ -31,6 +31,10 @@ derivative of the forward definition, per kept (row, key) pair, for an
 upstream gradient dout (the pages only say that the backward recomputes the
 attention instead of storing it, HSTU paper translation Appendix G).
 
+``layer_in`` / ``layer_out`` are the layer's surroundings (HSTU paper
+translation §3, §3.3): [u | v | q | k] = silu(W1 x + b1) per token, and
+y = x + W2 (LN(a) * u) + b2 with LN over heads * d.
+
 Parity status: pinned.  The test suite ties these functions to closed forms
 (hand-worked 2- and 3-token cases), to identities that reduce to textbook
 operations (sign-flip -> masked GEMM, constant rows -> prefix sum, row 0),
@@ -101,6 +105,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                          ctypes.c_int, ctypes.c_int, f64, f64, ctypes.c_int, vp,
                                          vp, i64, vp]
     lib.hstu_oracle_bwd_rows.restype = ctypes.c_int
+    lib.hstu_oracle_layer_in.argtypes = [vp, vp, vp, ctypes.c_int, i64, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]
+    lib.hstu_oracle_layer_in.restype = ctypes.c_int
+    lib.hstu_oracle_layer_out.argtypes = [vp, vp, vp, vp, vp, f64, vp, vp, ctypes.c_int, i64,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    lib.hstu_oracle_layer_out.restype = ctypes.c_int
     lib.hstu_oracle_threads.argtypes = []
     lib.hstu_oracle_threads.restype = ctypes.c_int
     _libs[path] = lib
@@ -266,6 +276,51 @@ def bwd_rows(q, k, v, dout, offsets, heads: int, d: int, alpha: float, n: float,
     if rc != 0:
         raise ValueError("oracle rejected the sampled rows")
     return out
+
+
+def _f64(a, n: int) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    if a.shape != (n,):
+        raise ValueError(f"expected {n} parameters, got shape {a.shape}")
+    return a
+
+
+def layer_in(x, w1, b1, heads: int, d: int, dtype: str, lib: Optional[ctypes.CDLL] = None):
+    """(u, v, q, k), each fp64 (T, heads, d): silu(x W1^T + b1) split in that
+    order.  x: (T, d_model), w1: (4 heads d, d_model) in the storage type."""
+    lib = lib or load()
+    x, w1 = _storage(x, dtype), _storage(w1, dtype)
+    T, dm = x.shape
+    hd = heads * d
+    if w1.shape != (4 * hd, dm):
+        raise ValueError("w1 must be (4 * heads * d, d_model)")
+    b1 = _f64(b1, 4 * hd)
+    outs = [np.zeros((T, heads, d), dtype=np.float64) for _ in range(4)]
+    rc = lib.hstu_oracle_layer_in(_ptr(x), _ptr(w1), _ptr(b1), _DTYPE_CODE[dtype], T, dm, heads,
+                                  d, *(_ptr(o) for o in outs))
+    if rc != 0:
+        raise ValueError("oracle rejected the layer arguments")
+    return tuple(outs)
+
+
+def layer_out(attn, u, x, gamma, beta, eps: float, w2, b2, heads: int, d: int, dtype: str,
+              lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+    """y fp64 (T, d_model) = x + (LN(attn) * u) W2^T + b2.  attn, u: (T, heads,
+    d); x: (T, d_model); w2: (d_model, heads d), all in the storage type."""
+    lib = lib or load()
+    attn, u, x, w2 = (_storage(a, dtype) for a in (attn, u, x, w2))
+    T, dm = x.shape
+    hd = heads * d
+    if attn.size != T * hd or u.size != T * hd or w2.shape != (dm, hd):
+        raise ValueError("layer_out shapes do not match")
+    gamma, beta, b2 = _f64(gamma, hd), _f64(beta, hd), _f64(b2, dm)
+    y = np.zeros((T, dm), dtype=np.float64)
+    rc = lib.hstu_oracle_layer_out(_ptr(attn), _ptr(u), _ptr(x), _ptr(gamma), _ptr(beta),
+                                   float(eps), _ptr(w2), _ptr(b2), _DTYPE_CODE[dtype], T, dm,
+                                   heads, d, _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle rejected the layer arguments")
+    return y
 
 
 def threads(lib: Optional[ctypes.CDLL] = None) -> int:

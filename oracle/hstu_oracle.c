@@ -50,6 +50,19 @@
  *   g     = (alpha / n) * silu'(x) * <dO_r, v_c>,  silu'(x) = sig(x) (1 + x (1 - sig(x)))
  *   dq_r += g * k_c,   dk_c += g * q_r
  *
+ * Layer surroundings (the *_layer_* entry points): HSTU paper translation,
+ * §3 (f1 and f2 are one linear layer each, f_i(X) = W_i X + b_i; phi_1 is
+ * SiLU; Norm is layer normalisation; the layers are joined by residual
+ * connections; the attention output is used as Norm(A(X)V(X)) * U(X), fed to
+ * f2) and §3.3 (phi_1(f_1(.)) is one fused operator, and so are the layer
+ * norm, the optional dropout and the output MLP).  Written out per token t:
+ *   [u | v | q | k] = silu(W1 x_t + b1)       (W1: 4*heads*d rows of d_model)
+ *   y_t = x_t + W2 (LN(a_t) * u_t) + b2        (W2: d_model rows of heads*d)
+ *   LN(a) = (a - mean(a)) / sqrt(var(a) + eps) * gamma + beta   (over heads*d,
+ *           biased variance)
+ * Readings: the split order U, V, Q, K and each part's (heads, d) layout; no
+ * dropout (inference); the residual adds x.
+ *
  * Readings taken where the pages are silent (each listed in the design notes):
  *   - alpha multiplies the scores before SiLU; n is a caller-given scalar;
  *   - the mask multiplies after SiLU (0/1), so masked terms are exactly 0;
@@ -422,6 +435,71 @@ int hstu_oracle_bwd_rows(const void* q, const void* k, const void* v, const void
                                kind == 1 ? acc : other, kind == 2 ? acc : other);
         }
         for (int e = 0; e < d; ++e) out_rows[m * (int64_t)d + e] = acc[e];
+    }
+    return 0;
+}
+
+/* ---- layer surroundings ---------------------------------------------------- */
+
+/* Input projection: x (T, d_model) and w1 (4*heads*d, d_model) in the storage
+ * type; b1 fp64 [4*heads*d].  Writes u, v, q, k, each fp64 (T, heads, d).
+ * Returns 0, or -1 on bad sizes. */
+int hstu_oracle_layer_in(const void* x, const void* w1, const double* b1, int dtype, int64_t T,
+                         int dm, int heads, int d, double* u, double* v, double* q, double* k) {
+    if (T < 0 || dm < 1 || heads < 1 || d < 1) return -1;
+    const int64_t hd = (int64_t)heads * d, n_out = 4 * hd;
+    double* part[4] = {u, v, q, k};
+#if ORACLE_PLANT == 15
+    part[0] = v; /* planted: U and V swapped */
+    part[1] = u;
+#endif
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t c = 0; c < n_out; ++c) {
+            double z = b1[c];
+            for (int e = 0; e < dm; ++e)
+                z += load_elem(x, dtype, t * dm + e) * load_elem(w1, dtype, c * dm + e);
+            part[c / hd][t * hd + c % hd] = silu(z);
+        }
+    return 0;
+}
+
+/* Output projection: attn, u (T, heads, d) and x (T, d_model), w2 (d_model,
+ * heads*d) in the storage type; gamma, beta fp64 [heads*d], b2 fp64
+ * [d_model].  Writes y fp64 (T, d_model).  Returns 0, or -1 on bad sizes. */
+int hstu_oracle_layer_out(const void* attn, const void* u, const void* x, const double* gamma,
+                          const double* beta, double eps, const void* w2, const double* b2,
+                          int dtype, int64_t T, int dm, int heads, int d, double* y) {
+    if (T < 0 || dm < 1 || heads < 1 || d < 1 || heads * d > 4096) return -1;
+    const int64_t hd = (int64_t)heads * d;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        double z[4096];
+        double mean = 0.0, var = 0.0;
+        for (int64_t c = 0; c < hd; ++c) mean += load_elem(attn, dtype, t * hd + c);
+        mean /= (double)hd;
+        for (int64_t c = 0; c < hd; ++c) {
+            const double a = load_elem(attn, dtype, t * hd + c) - mean;
+            var += a * a;
+        }
+#if ORACLE_PLANT == 16
+        var /= (double)(hd - 1); /* planted: unbiased variance */
+#else
+        var /= (double)hd;
+#endif
+        const double rstd = 1.0 / sqrt(var + eps);
+        for (int64_t c = 0; c < hd; ++c) {
+            const double ln = (load_elem(attn, dtype, t * hd + c) - mean) * rstd * gamma[c] + beta[c];
+            z[c] = ln * load_elem(u, dtype, t * hd + c);
+        }
+        for (int o = 0; o < dm; ++o) {
+            double acc = b2[o];
+#if ORACLE_PLANT != 17
+            acc += load_elem(x, dtype, t * dm + o); /* (planted 17: residual dropped) */
+#endif
+            for (int64_t c = 0; c < hd; ++c) acc += z[c] * load_elem(w2, dtype, (int64_t)o * hd + c);
+            y[t * dm + o] = acc;
+        }
     }
     return 0;
 }
