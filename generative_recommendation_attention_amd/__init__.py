@@ -32,6 +32,7 @@ HSTU_BF16, HSTU_FP16, HSTU_FP32 = 0, 1, 2
 # Every symbol include/hstu.h declares.
 EXPORTS = ("hstu_attn_fwd", "hstu_attn_fwd_bf16", "hstu_attn_fwd_fp16", "hstu_attn_fwd_fp32",
            "hstu_attn_fwd_targets", "hstu_attn_fwd_cached", "hstu_attn_fwd_dense", "hstu_attn_bwd",
+           "hstu_layer_in_proj", "hstu_layer_out_proj",
            "hstu_attn_bwd_targets", "hstu_validate_offsets", "hstu_status_string", "hstu_last_hip_error",
            "hstu_release_workspace", "hstu_profile_enable", "hstu_profile_read")
 
@@ -81,6 +82,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hstu_attn_fwd_dense.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, f32, vp, vp,
                                         ctypes.c_int]
     lib.hstu_attn_fwd_dense.restype = ctypes.c_int
+    i64 = ctypes.c_int64
+    lib.hstu_layer_in_proj.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp,
+                                       ctypes.c_int]
+    lib.hstu_layer_in_proj.restype = ctypes.c_int
+    lib.hstu_layer_out_proj.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, i64, i32, i32, i32, vp,
+                                        vp, ctypes.c_int]
+    lib.hstu_layer_out_proj.restype = ctypes.c_int
     lib.hstu_attn_bwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp, vp, vp,
                                   ctypes.c_int]
     lib.hstu_attn_bwd.restype = ctypes.c_int
@@ -329,4 +337,64 @@ def hstu_attn_fwd_dense(q, k, v, alpha: float, n: float, out=None, stream=None):
                                  float(alpha), float(n), out.data_ptr(), _stream_handle(stream),
                                  _dtype_code(q))
     _check(st, "hstu_attn_fwd_dense")
+    return out
+
+
+def _gpu_contig(name, t, dtype=None, shape=None):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def hstu_layer_in_proj(x, w1, b1, heads: int, d: int, out=None, stream=None):
+    """(u, v, q, k) = split(silu(x @ w1.T + b1)), each (T, heads, d).
+    x: (T, d_model); w1: (4 heads d, d_model) of x's type; b1: float32."""
+    import torch
+    T, dm = x.shape
+    hd = heads * d
+    _gpu_contig("x", x)
+    _gpu_contig("w1", w1, x.dtype, (4 * hd, dm))
+    _gpu_contig("b1", b1, torch.float32, (4 * hd,))
+    if out is None:
+        out = tuple(torch.empty((T, heads, d), dtype=x.dtype, device=x.device) for _ in range(4))
+    for i, t in enumerate(out):
+        _gpu_contig(f"out[{i}]", t, x.dtype, (T, heads, d))
+    if T == 0:
+        return out
+    lib = load_library()
+    st = lib.hstu_layer_in_proj(x.data_ptr(), w1.data_ptr(), b1.data_ptr(), T, dm, heads, d,
+                                *(t.data_ptr() for t in out), _stream_handle(stream),
+                                _dtype_code(x))
+    _check(st, "hstu_layer_in_proj")
+    return out
+
+
+def hstu_layer_out_proj(attn, u, x, gamma, beta, eps: float, w2, b2, out=None, stream=None):
+    """y = x + (layer_norm(attn) * u) @ w2.T + b2 (norm over heads * d).
+    attn, u: (T, heads, d); x: (T, d_model); w2: (d_model, heads d);
+    gamma, beta, b2: float32."""
+    import torch
+    T, heads, d = attn.shape
+    hd = heads * d
+    dm = x.shape[1]
+    _gpu_contig("attn", attn)
+    _gpu_contig("u", u, attn.dtype, attn.shape)
+    _gpu_contig("x", x, attn.dtype, (T, dm))
+    _gpu_contig("w2", w2, attn.dtype, (dm, hd))
+    for name, t, n in (("gamma", gamma, hd), ("beta", beta, hd), ("b2", b2, dm)):
+        _gpu_contig(name, t, torch.float32, (n,))
+    if out is None:
+        out = torch.empty_like(x)
+    _gpu_contig("out", out, x.dtype, x.shape)
+    if T == 0:
+        return out
+    lib = load_library()
+    st = lib.hstu_layer_out_proj(attn.data_ptr(), u.data_ptr(), x.data_ptr(), gamma.data_ptr(),
+                                 beta.data_ptr(), float(eps), w2.data_ptr(), b2.data_ptr(), T, dm,
+                                 heads, d, out.data_ptr(), _stream_handle(stream),
+                                 _dtype_code(attn))
+    _check(st, "hstu_layer_out_proj")
     return out

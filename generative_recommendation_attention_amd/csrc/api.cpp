@@ -422,6 +422,87 @@ hstu_status_t hstu_attn_fwd_dense(const void* q, const void* k, const void* v, i
     return attn_fwd_call(q, k, v, nullptr, mi, batch, heads, d, alpha, n, out, stream, dtype);
 }
 
+hstu_status_t hstu_layer_in_proj(const void* x, const void* w1, const float* b1,
+                                 int64_t num_tokens, int32_t d_model, int32_t heads, int32_t d,
+                                 void* u, void* v, void* q, void* k, hipStream_t stream,
+                                 hstu_dtype_t dtype) {
+    if (dtype == HSTU_FP32) return HSTU_ERR_UNSUPPORTED;
+    if (dtype != HSTU_BF16 && dtype != HSTU_FP16) return HSTU_ERR_UNSUPPORTED;
+    if (num_tokens < 0 || heads < 1 || d < 1) return HSTU_ERR_INVALID_ARG;
+    const long long hd = (long long)heads * d;
+    if ((d_model != 128 && d_model != 256 && d_model != 512) ||
+        (hd != 128 && hd != 256 && hd != 512))
+        return HSTU_ERR_UNSUPPORTED;
+    if (num_tokens > (1LL << 40)) return HSTU_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return HSTU_OK;
+    const void* ptrs[8] = {x, w1, b1, u, v, q, k, nullptr};
+    for (int i = 0; i < 7; ++i)
+        if (!ptrs[i] || !aligned16(ptrs[i])) return HSTU_ERR_INVALID_ARG;
+    const void* outs[4] = {u, v, q, k};
+    for (int i = 0; i < 4; ++i) {
+        if (outs[i] == x || outs[i] == w1 || outs[i] == b1) return HSTU_ERR_INVALID_ARG;
+        for (int j = 0; j < i; ++j)
+            if (outs[i] == outs[j]) return HSTU_ERR_INVALID_ARG;
+    }
+    int dev = 0;
+    hstu_status_t st = check_device(&dev);
+    if (st != HSTU_OK) return st;
+    hstu::LayerParams p;
+    p.x = x;
+    p.w1 = w1;
+    p.b1 = b1;
+    p.uvqk[0] = u;
+    p.uvqk[1] = v;
+    p.uvqk[2] = q;
+    p.uvqk[3] = k;
+    p.T = num_tokens;
+    p.d_model = d_model;
+    p.heads_d = (int)hd;
+    hipError_t e = hstu::launch_layer_in(p, static_cast<hstu::Dtype>(dtype), stream);
+    return e == hipSuccess ? HSTU_OK : hip_fail(e);
+}
+
+hstu_status_t hstu_layer_out_proj(const void* attn, const void* u, const void* x,
+                                  const float* gamma, const float* beta, float eps,
+                                  const void* w2, const float* b2, int64_t num_tokens,
+                                  int32_t d_model, int32_t heads, int32_t d, void* y,
+                                  hipStream_t stream, hstu_dtype_t dtype) {
+    if (dtype == HSTU_FP32) return HSTU_ERR_UNSUPPORTED;
+    if (dtype != HSTU_BF16 && dtype != HSTU_FP16) return HSTU_ERR_UNSUPPORTED;
+    if (num_tokens < 0 || heads < 1 || d < 1) return HSTU_ERR_INVALID_ARG;
+    if (!std::isfinite(eps) || eps < 0.0f) return HSTU_ERR_INVALID_ARG;
+    const long long hd = (long long)heads * d;
+    if ((d_model != 128 && d_model != 256 && d_model != 512) ||
+        (hd != 128 && hd != 256 && hd != 512))
+        return HSTU_ERR_UNSUPPORTED;
+    if (num_tokens > (1LL << 40)) return HSTU_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return HSTU_OK;
+    const void* ins[7] = {attn, u, x, gamma, beta, w2, b2};
+    for (const void* pin : ins)
+        if (!pin || !aligned16(pin)) return HSTU_ERR_INVALID_ARG;
+    if (!y || !aligned16(y)) return HSTU_ERR_INVALID_ARG;
+    for (const void* pin : ins)
+        if (y == pin) return HSTU_ERR_INVALID_ARG;
+    int dev = 0;
+    hstu_status_t st = check_device(&dev);
+    if (st != HSTU_OK) return st;
+    hstu::LayerParams p;
+    p.attn = attn;
+    p.u = u;
+    p.x = x;
+    p.gamma = gamma;
+    p.beta = beta;
+    p.eps = eps;
+    p.w2 = w2;
+    p.b2 = b2;
+    p.y = y;
+    p.T = num_tokens;
+    p.d_model = d_model;
+    p.heads_d = (int)hd;
+    hipError_t e = hstu::launch_layer_out(p, static_cast<hstu::Dtype>(dtype), stream);
+    return e == hipSuccess ? HSTU_OK : hip_fail(e);
+}
+
 hstu_status_t hstu_attn_bwd(const void* q, const void* k, const void* v, const void* dout,
                             const int32_t* seq_offsets, int32_t num_seqs, int32_t heads,
                             int32_t d, float alpha, float n, void* dq, void* dk, void* dv,

@@ -163,6 +163,31 @@ int resident_grid(KernelFn fn, int threads) {
     return per_cu * device_cus();
 }
 
+// The layer's surroundings (bf16 / fp16): input projection with SiLU and
+// split, layer norm times U with output projection and residual.
+struct LayerParams {
+    // layer_in
+    const void* x = nullptr;       // (T, d_model)
+    const void* w1 = nullptr;      // (4 heads d, d_model)
+    const float* b1 = nullptr;     // [4 heads d]
+    void* uvqk[4] = {nullptr, nullptr, nullptr, nullptr};   // each (T, heads, d)
+    // layer_out
+    const void* attn = nullptr;    // (T, heads, d)
+    const void* u = nullptr;       // (T, heads, d)
+    const float* gamma = nullptr;  // [heads d]
+    const float* beta = nullptr;   // [heads d]
+    const void* w2 = nullptr;      // (d_model, heads d)
+    const float* b2 = nullptr;     // [d_model]
+    void* y = nullptr;             // (T, d_model)
+    float eps = 0.0f;
+    int64_t T = 0;
+    int d_model = 0;
+    int heads_d = 0;
+};
+
+hipError_t launch_layer_in(const LayerParams& p, Dtype dt, hipStream_t stream);
+hipError_t launch_layer_out(const LayerParams& p, Dtype dt, hipStream_t stream);
+
 // Backward: gradients of the forward with respect to q, k and v for an
 // upstream gradient dout (bf16 / fp16 only).  Work items are 128-row tiles of
 // each (sequence, head): the work list must be built with BWD_TILE_ROWS.

@@ -1,0 +1,369 @@
+// The HSTU layer's surroundings of the attention, on the matrix cores (bf16 /
+// fp16), HSTU paper translation §3 and §3.3: f1 and f2 are one linear layer
+// each, phi_1 = SiLU, Norm = layer normalisation, residual connections; the
+// paper fuses phi_1(f_1(.)) into one operator and the layer norm with the
+// output MLP into another.  Per token t:
+//
+//   layer_in:   [u | v | q | k] = silu(W1 x_t + b1)
+//               (W1: (4 heads d) x d_model, row-major; each part written as
+//               (T, heads, d), the layout the attention reads)
+//   layer_out:  y_t = x_t + W2 (LN(a_t) * u_t) + b2
+//               (W2: d_model x (heads d); LN over heads d with gamma, beta)
+//
+// Both are products with a small inner dimension K (d_model or heads d, at
+// most 512), so each wave keeps its 32 tokens' whole K-long rows as MFMA B
+// operands in registers: layer_out normalises and gates them there (the
+// prologue), then both kernels stream the weight matrix through LDS in
+// chunks of output features (double buffered, one barrier per chunk) and
+// apply bias, SiLU or residual in the epilogue.  The products are computed
+// transposed (features down, tokens across), so a lane ends with one token
+// and runs of 4 consecutive features: 8-byte stores.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace hstu {
+
+namespace {
+
+template <int K>
+struct LayerCfg {
+    static constexpr int NW = 4;
+    static constexpr int ROWS = 32 * NW;           // tokens per workgroup
+    static constexpr int NC = 64;                  // output features per chunk
+    static constexpr int NB = NC / 32;             // 32-feature blocks per chunk
+    static constexpr int RB = 2 * K;               // bytes of one weight row
+    static constexpr int CH = RB / 16;             // 16-byte chunks per row
+    static constexpr int CHUNK_BYTES = NC * RB;
+    static constexpr int LOADS = CHUNK_BYTES / 1024 / NW;   // wave loads per chunk
+    static constexpr int RPL = 1024 / RB;          // rows one wave load covers
+    static constexpr int NKS = K / 16;             // k-steps
+    static_assert(K == 128 || K == 256 || K == 512, "inner dimension");
+    static_assert(LOADS * NW * 1024 == CHUNK_BYTES, "chunk must split into whole wave loads");
+};
+
+// Swizzle of a weight row's 16-byte chunks: 16 consecutive rows read at one
+// logical chunk land in 16 different physical chunks.
+__device__ __forceinline__ int wswz(int r) {
+    return 2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1);
+}
+
+template <int K>
+struct WeightStage {
+    using C = LayerCfg<K>;
+    int goff[C::LOADS];   // global byte offset of each of this lane's loads
+    int dst[C::LOADS];    // LDS byte offset (wave-uniform part) of each load
+    int rd[C::NKS];       // LDS byte offset of row l32, logical chunk 2ks + g
+    __device__ WeightStage(int lane, int wv) {
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i) {
+            const int L = wv + C::NW * i;
+            const int r = L * C::RPL + lane / C::CH;
+            const int pc = lane % C::CH;
+            goff[i] = r * C::RB + 16 * (pc ^ wswz(r));
+            dst[i] = L * 1024;
+        }
+        const int g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) rd[ks] = l32 * C::RB + 16 * ((2 * ks + g) ^ wswz(l32));
+    }
+    // Rows [c0, c0 + NC) of the (n x K) weight matrix into `buf`; rows past n
+    // read as zero.
+    __device__ void issue(const uint16_t* w, int n, int c0, unsigned char* buf) const {
+        const __amdgpu_buffer_rsrc_t r =
+                make_rsrc32(w + (int64_t)c0 * K, min(n - c0, C::NC) * C::RB);
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i) load16_to_lds(r, buf + dst[i], goff[i]);
+    }
+};
+
+// The products of one chunk: acc[b] = sum_k W[c0 + 32 b + i][k] * Z[token j][k]
+// (i: feature within the block, j: the lane's token).
+template <typename T, int K>
+__device__ __forceinline__ void chunk_products(const unsigned char* buf, const WeightStage<K>& st,
+                                               const typename Mfma<T>::v8* z, f32x16* acc) {
+    using C = LayerCfg<K>;
+    using M = Mfma<T>;
+#pragma unroll
+    for (int b = 0; b < C::NB; ++b) acc[b] = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks)
+#pragma unroll
+        for (int b = 0; b < C::NB; ++b) {
+            const typename M::v8 wa =
+                    *reinterpret_cast<const typename M::v8*>(buf + b * 32 * C::RB + st.rd[ks]);
+            acc[b] = M::mma(wa, z[ks], acc[b]);
+        }
+}
+
+struct LayerInArgs {
+    const uint16_t* x;
+    const uint16_t* w1;
+    const float* b1;
+    uint16_t* out[4];   // u, v, q, k
+    int64_t T;
+    int heads_d;        // heads * d
+    int chunks_per_wg;  // output chunks per workgroup (grid.y splits them)
+};
+
+template <typename T, int K>
+__global__ __launch_bounds__(256, 2) void layer_in_kernel(LayerInArgs a) {
+    using C = LayerCfg<K>;
+    using M = Mfma<T>;
+    using v4 = typename M::v4;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * C::CHUNK_BYTES];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 5, l32 = lane & 31;
+    const int64_t t0 = (int64_t)blockIdx.x * C::ROWS + 32 * wv;   // the wave's first token
+    const int n = 4 * a.heads_d;
+    const int nchunks = n / C::NC;
+    const int c_begin = blockIdx.y * a.chunks_per_wg;
+    const int c_end = min(nchunks, c_begin + a.chunks_per_wg);
+    const WeightStage<K> st(lane, wv);
+
+    // The wave's 32 token rows as B operands (token l32, k = 16 ks + 8 g ..).
+    typename M::v8 z[C::NKS];
+    {
+        const int64_t rows = a.T - t0;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(a.x + t0 * K, (rows < 0 ? 0 : rows) * C::RB);
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks)
+            z[ks] = __builtin_bit_cast(typename M::v8,
+                                       __builtin_amdgcn_raw_buffer_load_b128(
+                                               r, l32 * C::RB + (16 * ks + 8 * g) * 2, 0, 0));
+    }
+    const int64_t tok = t0 + l32;
+    const bool tok_live = tok < a.T;
+
+    if (c_begin < c_end) st.issue(a.w1, n, c_begin * C::NC, lds);
+    for (int c = c_begin; c < c_end; ++c) {
+        __builtin_amdgcn_s_waitcnt(VMCNT_LE(0));
+        __syncthreads();
+        const int slot = (c - c_begin) & 1;
+        if (c + 1 < c_end) st.issue(a.w1, n, (c + 1) * C::NC, lds + (slot ^ 1) * C::CHUNK_BYTES);
+        f32x16 acc[C::NB];
+        chunk_products<T, K>(lds + slot * C::CHUNK_BYTES, st, z, acc);
+        // Epilogue: lane holds token `tok`, features c0 + 32 b + 8 i + 4 g + (0..3).
+        if (tok_live) {
+#pragma unroll
+            for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int f = c * C::NC + 32 * b + 8 * i + 4 * g;   // first of 4 features
+                    const f32x4 bias = *reinterpret_cast<const f32x4*>(a.b1 + f);
+                    f32x4 y;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float s = acc[b][4 * i + j] + bias[j];
+                        y[j] = s * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * s));
+                    }
+                    const int part = f / a.heads_d;    // u, v, q, k (4 features never straddle)
+                    const int pos = f - part * a.heads_d;
+                    const v4 yv = __builtin_convertvector(y, v4);
+                    *reinterpret_cast<u32x2*>(a.out[part] + tok * a.heads_d + pos) =
+                            __builtin_bit_cast(u32x2, yv);
+                }
+        }
+    }
+}
+
+struct LayerOutArgs {
+    const uint16_t* attn;
+    const uint16_t* u;
+    const uint16_t* x;
+    const float* gamma;
+    const float* beta;
+    const uint16_t* w2;
+    const float* b2;
+    uint16_t* y;
+    int64_t T;
+    int d_model;
+    float eps;
+    int chunks_per_wg;
+};
+
+template <typename T, int K>
+__global__ __launch_bounds__(256, 2) void layer_out_kernel(LayerOutArgs a) {
+    using C = LayerCfg<K>;
+    using M = Mfma<T>;
+    using v8 = typename M::v8;
+    using v4 = typename M::v4;
+    typedef float f32x8v __attribute__((ext_vector_type(8)));
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * C::CHUNK_BYTES];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 5, l32 = lane & 31;
+    const int64_t t0 = (int64_t)blockIdx.x * C::ROWS + 32 * wv;
+    const int n = a.d_model;
+    const int nchunks = n / C::NC;
+    const int c_begin = blockIdx.y * a.chunks_per_wg;
+    const int c_end = min(nchunks, c_begin + a.chunks_per_wg);
+    const WeightStage<K> st(lane, wv);
+    if (c_begin < c_end) st.issue(a.w2, n, c_begin * C::NC, lds);   // overlaps the prologue
+
+    // Prologue: the attention rows of the wave's 32 tokens (token l32,
+    // features 16 ks + 8 g ..), normalised over all K features (the lane and
+    // its partner lane ^ 32 hold one token's features between them), scaled,
+    // shifted and gated by u, rounded to T: the B operands of the product.
+    v8 z[C::NKS];
+    const int64_t rows = a.T - t0;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.attn + t0 * K, (rows < 0 ? 0 : rows) * C::RB);
+    const __amdgpu_buffer_rsrc_t ru = make_rsrc(a.u + t0 * K, (rows < 0 ? 0 : rows) * C::RB);
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks)
+        z[ks] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(
+                                               ra, l32 * C::RB + (16 * ks + 8 * g) * 2, 0, 0));
+    float sum = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum += (float)z[ks][e];
+    sum += __shfl_xor(sum, 32);
+    const float mean = sum * (1.0f / K);
+    float sq = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float dlt = (float)z[ks][e] - mean;
+            sq += dlt * dlt;
+        }
+    sq += __shfl_xor(sq, 32);
+    const float rstd = __builtin_amdgcn_rsqf(sq * (1.0f / K) + a.eps);
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+        const int k0 = 16 * ks + 8 * g;
+        const v8 uu = __builtin_bit_cast(
+                v8, __builtin_amdgcn_raw_buffer_load_b128(ru, l32 * C::RB + k0 * 2, 0, 0));
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(a.gamma + k0);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(a.gamma + k0 + 4);
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(a.beta + k0);
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(a.beta + k0 + 4);
+        f32x8v zz;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float gm = e < 4 ? g0[e] : g1[e - 4];
+            const float bt = e < 4 ? b0[e] : b1[e - 4];
+            zz[e] = (((float)z[ks][e] - mean) * rstd * gm + bt) * (float)uu[e];
+        }
+        z[ks] = __builtin_convertvector(zz, v8);
+    }
+    const int64_t tok = t0 + l32;
+    const bool tok_live = tok < a.T;
+
+    for (int c = c_begin; c < c_end; ++c) {
+        __builtin_amdgcn_s_waitcnt(VMCNT_LE(0));
+        __syncthreads();
+        const int slot = (c - c_begin) & 1;
+        if (c + 1 < c_end) st.issue(a.w2, n, (c + 1) * C::NC, lds + (slot ^ 1) * C::CHUNK_BYTES);
+        f32x16 acc[C::NB];
+        chunk_products<T, K>(lds + slot * C::CHUNK_BYTES, st, z, acc);
+        // Epilogue: residual and bias; lane holds token `tok`, output
+        // features f .. f + 3.
+        if (tok_live) {
+#pragma unroll
+            for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int f = c * C::NC + 32 * b + 8 * i + 4 * g;
+                    const f32x4 bias = *reinterpret_cast<const f32x4*>(a.b2 + f);
+                    const v4 xr = __builtin_bit_cast(
+                            v4, *reinterpret_cast<const u32x2*>(a.x + tok * n + f));
+                    f32x4 y;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) y[j] = acc[b][4 * i + j] + bias[j] + (float)xr[j];
+                    const v4 yv = __builtin_convertvector(y, v4);
+                    *reinterpret_cast<u32x2*>(a.y + tok * n + f) = __builtin_bit_cast(u32x2, yv);
+                }
+        }
+    }
+}
+
+// Splits the output chunks over grid.y so that the launch has at least two
+// workgroups per compute unit.
+int chunks_per_wg(int64_t m_tiles, int nchunks) {
+    const int64_t want = 2LL * device_cus();
+    int split = (int)((want + m_tiles - 1) / m_tiles);
+    split = split < 1 ? 1 : (split > nchunks ? nchunks : split);
+    return (nchunks + split - 1) / split;
+}
+
+template <typename T, int K>
+hipError_t layer_in_typed(const LayerParams& p, hipStream_t stream) {
+    using C = LayerCfg<K>;
+    LayerInArgs a;
+    a.x = static_cast<const uint16_t*>(p.x);
+    a.w1 = static_cast<const uint16_t*>(p.w1);
+    a.b1 = p.b1;
+    for (int i = 0; i < 4; ++i) a.out[i] = static_cast<uint16_t*>(p.uvqk[i]);
+    a.T = p.T;
+    a.heads_d = p.heads_d;
+    const int64_t m_tiles = (p.T + C::ROWS - 1) / C::ROWS;
+    const int nchunks = 4 * p.heads_d / C::NC;
+    a.chunks_per_wg = chunks_per_wg(m_tiles, nchunks);
+    const dim3 grid((unsigned)m_tiles, (unsigned)((nchunks + a.chunks_per_wg - 1) / a.chunks_per_wg));
+    hipLaunchKernelGGL((layer_in_kernel<T, K>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <typename T, int K>
+hipError_t layer_out_typed(const LayerParams& p, hipStream_t stream) {
+    using C = LayerCfg<K>;
+    LayerOutArgs a;
+    a.attn = static_cast<const uint16_t*>(p.attn);
+    a.u = static_cast<const uint16_t*>(p.u);
+    a.x = static_cast<const uint16_t*>(p.x);
+    a.gamma = p.gamma;
+    a.beta = p.beta;
+    a.w2 = static_cast<const uint16_t*>(p.w2);
+    a.b2 = p.b2;
+    a.y = static_cast<uint16_t*>(p.y);
+    a.T = p.T;
+    a.d_model = p.d_model;
+    a.eps = p.eps;
+    const int64_t m_tiles = (p.T + C::ROWS - 1) / C::ROWS;
+    const int nchunks = p.d_model / C::NC;
+    a.chunks_per_wg = chunks_per_wg(m_tiles, nchunks);
+    const dim3 grid((unsigned)m_tiles, (unsigned)((nchunks + a.chunks_per_wg - 1) / a.chunks_per_wg));
+    hipLaunchKernelGGL((layer_out_kernel<T, K>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t layer_in_k(const LayerParams& p, hipStream_t s) {
+    switch (p.d_model) {
+    case 128: return layer_in_typed<T, 128>(p, s);
+    case 256: return layer_in_typed<T, 256>(p, s);
+    case 512: return layer_in_typed<T, 512>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+hipError_t layer_out_k(const LayerParams& p, hipStream_t s) {
+    switch (p.heads_d) {
+    case 128: return layer_out_typed<T, 128>(p, s);
+    case 256: return layer_out_typed<T, 256>(p, s);
+    case 512: return layer_out_typed<T, 512>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_layer_in(const LayerParams& p, Dtype dt, hipStream_t stream) {
+    if (dt == Dtype::BF16) return layer_in_k<__bf16>(p, stream);
+    if (dt == Dtype::FP16) return layer_in_k<_Float16>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_layer_out(const LayerParams& p, Dtype dt, hipStream_t stream) {
+    if (dt == Dtype::BF16) return layer_out_k<__bf16>(p, stream);
+    if (dt == Dtype::FP16) return layer_out_k<_Float16>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace hstu

@@ -160,6 +160,39 @@ hstu_status_t hstu_attn_fwd_dense(const void* q, const void* k, const void* v, i
                                   int32_t heads, int32_t seq_len, int32_t d, float alpha, float n,
                                   void* out, hipStream_t stream, hstu_dtype_t dtype);
 
+/* The layer around the attention (HSTU paper translation, §3: f1 and f2 are
+ * one linear layer each, phi_1 is SiLU, Norm is layer normalisation, layers
+ * are joined by residual connections; §3.3: phi_1(f_1(.)) is one fused
+ * operator, and so are the layer norm and the output MLP).  bfloat16 /
+ * float16 (HSTU_FP32 returns HSTU_ERR_UNSUPPORTED); d_model and heads * d each
+ * 128, 256 or 512.  All pointers are device pointers, 16-byte aligned,
+ * caller-owned; outputs overlap no input.  fp32 accumulation; outputs rounded
+ * to nearest even.
+ *
+ * hstu_layer_in_proj: per token t (num_tokens = T),
+ *   [u | v | q | k] = silu(w1 x_t + b1)
+ *   x : (T, d_model);  w1 : (4 heads d, d_model) row-major (one output feature
+ *   per row);  b1 : float32 [4 heads d].  Output feature j of part p (p = 0..3
+ *   for u, v, q, k) is row p * heads * d + j of w1; each part is written as
+ *   (T, heads, d) (feature j = h * d + e), the layout hstu_attn_fwd reads. */
+hstu_status_t hstu_layer_in_proj(const void* x, const void* w1, const float* b1,
+                                 int64_t num_tokens, int32_t d_model, int32_t heads, int32_t d,
+                                 void* u, void* v, void* q, void* k, hipStream_t stream,
+                                 hstu_dtype_t dtype);
+
+/* hstu_layer_out_proj: per token t,
+ *   y_t = x_t + w2 (LN(a_t) * u_t) + b2,
+ *   LN(a) = (a - mean(a)) / sqrt(var(a) + eps) * gamma + beta  over the heads * d
+ *   features of the token (biased variance);
+ *   attn (a), u : (T, heads, d);  x, y : (T, d_model);  w2 : (d_model, heads d)
+ *   row-major;  gamma, beta : float32 [heads d];  b2 : float32 [d_model];
+ *   eps >= 0 and finite.  No dropout (inference). */
+hstu_status_t hstu_layer_out_proj(const void* attn, const void* u, const void* x,
+                                  const float* gamma, const float* beta, float eps,
+                                  const void* w2, const float* b2, int64_t num_tokens,
+                                  int32_t d_model, int32_t heads, int32_t d, void* y,
+                                  hipStream_t stream, hstu_dtype_t dtype);
+
 /* Backward: gradients of hstu_attn_fwd (or, with num_targets, of
  * hstu_attn_fwd_targets) with respect to q, k and v, for the upstream
  * gradient dout = dLoss/dout.  The attention is recomputed block by block and

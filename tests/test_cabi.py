@@ -193,6 +193,46 @@ def test_dense_argument_checks(lib, args, status):
     assert lib.hstu_attn_fwd_dense(*args, None, hstu.HSTU_BF16) == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(b1=24), hstu.HSTU_ERR_INVALID_ARG),         # misaligned bias
+    (dict(u=16), hstu.HSTU_ERR_INVALID_ARG),          # u aliases x
+    (dict(q=64), hstu.HSTU_ERR_INVALID_ARG),          # q aliases u
+    (dict(dm=192), hstu.HSTU_ERR_UNSUPPORTED),
+    (dict(heads=3), hstu.HSTU_ERR_UNSUPPORTED),       # heads * d = 192
+    (dict(T=-1), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(dtype=hstu.HSTU_FP32), hstu.HSTU_ERR_UNSUPPORTED),
+    (dict(T=0, x=None, w1=None, b1=None, u=None, v=None, q=None, k=None), hstu.HSTU_OK),
+])
+def test_layer_in_argument_checks(lib, kw, status):
+    a = dict(x=16, w1=32, b1=48, T=4, dm=256, heads=4, d=64, u=64, v=80, q=96, k=112,
+             dtype=hstu.HSTU_BF16)
+    a.update(kw)
+    assert lib.hstu_layer_in_proj(a["x"], a["w1"], a["b1"], a["T"], a["dm"], a["heads"], a["d"],
+                                  a["u"], a["v"], a["q"], a["k"], None, a["dtype"]) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(attn=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(gamma=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(y=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(y=48), hstu.HSTU_ERR_INVALID_ARG),          # y aliases x
+    (dict(eps=-1.0), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(dm=64), hstu.HSTU_ERR_UNSUPPORTED),
+    (dict(dtype=hstu.HSTU_FP32), hstu.HSTU_ERR_UNSUPPORTED),
+    (dict(T=0, attn=None, u=None, x=None, gamma=None, beta=None, w2=None, b2=None, y=None),
+     hstu.HSTU_OK),
+])
+def test_layer_out_argument_checks(lib, kw, status):
+    a = dict(attn=16, u=32, x=48, gamma=64, beta=80, eps=1e-5, w2=96, b2=112, T=4, dm=256,
+             heads=4, d=64, y=128, dtype=hstu.HSTU_BF16)
+    a.update(kw)
+    assert lib.hstu_layer_out_proj(a["attn"], a["u"], a["x"], a["gamma"], a["beta"], a["eps"],
+                                   a["w2"], a["b2"], a["T"], a["dm"], a["heads"], a["d"], a["y"],
+                                   None, a["dtype"]) == status
+
+
 def test_status_strings(lib):
     for st in (0, -1, -2, -3, -4, -5):
         assert lib.hstu_status_string(st)
