@@ -189,6 +189,93 @@ def cpu_baseline(case, budget_s: float):
                       f"{threads} threads available"}
 
 
+def bench_layer(args) -> int:
+    """One layer forward: hstu_layer_in_proj, hstu_attn_fwd, hstu_layer_out_proj
+    on the chosen workload with d_model = heads * d (bf16/fp16).  Reports the
+    whole layer's time and each part's own (each part timed alone, same
+    inputs), with the projections' HBM rates."""
+    import torch
+    import generative_recommendation_attention_amd as hstu
+    torch.cuda.set_device(0)
+    case = workloads.workload(args.workload)
+    if case.dtype == "fp32":
+        print("--layer needs a bf16 or fp16 workload", file=sys.stderr)
+        return 2
+    T, H, D = case.total, case.heads, case.d
+    hd = H * D
+    dm = hd
+    tdt = torch.bfloat16 if case.dtype == "bf16" else torch.float16
+    g = torch.Generator(device="cuda").manual_seed(3000)
+    x = torch.randn((T, dm), generator=g, device="cuda").to(tdt)
+    w1 = (torch.randn((4 * hd, dm), generator=g, device="cuda") / dm ** 0.5).to(tdt)
+    b1 = 0.1 * torch.randn(4 * hd, generator=g, device="cuda")
+    w2 = (torch.randn((dm, hd), generator=g, device="cuda") / hd ** 0.5).to(tdt)
+    gamma = 1.0 + 0.1 * torch.randn(hd, generator=g, device="cuda")
+    beta = 0.1 * torch.randn(hd, generator=g, device="cuda")
+    b2 = 0.1 * torch.randn(dm, generator=g, device="cuda")
+    off = torch.from_numpy(case.offsets.astype(np.int32)).cuda()
+    uvqk = tuple(torch.empty((T, H, D), dtype=tdt, device="cuda") for _ in range(4))
+    attn = torch.empty((T, H, D), dtype=tdt, device="cuda")
+    y = torch.empty_like(x)
+
+    def p_in():
+        hstu.hstu_layer_in_proj(x, w1, b1, H, D, out=uvqk)
+
+    def p_attn():
+        hstu.hstu_attn_fwd(uvqk[2], uvqk[3], uvqk[1], off, case.alpha, case.n, out=attn)
+
+    def p_out():
+        hstu.hstu_layer_out_proj(attn, uvqk[0], x, gamma, beta, 1e-5, w2, b2, out=y)
+
+    def layer():
+        p_in()
+        p_attn()
+        p_out()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    ms_layer = timed(layer)
+    ms_in, ms_attn, ms_out = timed(p_in), timed(p_attn), timed(p_out)
+    elt = 2
+    flops_attn = case.useful_flops()
+    flops_in = 2.0 * T * dm * 4 * hd
+    flops_out = 2.0 * T * hd * dm
+    bytes_in = elt * (T * dm + 4 * hd * dm + 4 * T * hd) + 4 * 4 * hd
+    bytes_out = elt * (2 * T * hd + 2 * T * dm + dm * hd) + 4 * (2 * hd + dm)
+    total = flops_attn + flops_in + flops_out
+    line = {
+        "metric": "HSTU layer fwd (projections + attention) useful TFLOP/s",
+        "value": round(total / (ms_layer * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_layer, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": case.dtype, "data": "synthetic",
+        "config": {"workload": case.description, "d_model": dm, "heads": H, "d": D,
+                   "total_tokens": T},
+        "parts": {
+            "in_proj": {"ms": round(ms_in, 5), "hbm_GBps": round(bytes_in / ms_in / 1e6, 1),
+                        "hbm_frac": round(bytes_in / ms_in / 1e6 / PEAK_HBM_GBS, 4),
+                        "tflops": round(flops_in / ms_in / 1e9, 1)},
+            "attention": {"ms": round(ms_attn, 5),
+                          "tflops": round(flops_attn / ms_attn / 1e9, 1)},
+            "out_proj": {"ms": round(ms_out, 5), "hbm_GBps": round(bytes_out / ms_out / 1e6, 1),
+                         "hbm_frac": round(bytes_out / ms_out / 1e6 / PEAK_HBM_GBS, 4),
+                         "tflops": round(flops_out / ms_out / 1e9, 1)},
+        },
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +286,9 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--targets", action="store_true",
                     help="time the target-aware forward on 16 x (3072 history + 1024 candidates)")
+    ap.add_argument("--layer", action="store_true",
+                    help="time one HSTU layer forward (input projection, attention, output "
+                         "projection) on the 16 x 4096 workload with d_model = heads * d")
     ap.add_argument("--dense", action="store_true",
                     help="time hstu_attn_fwd_dense on the chosen workload's shape laid out "
                          "(batch, heads, seq_len, d) (equal lengths only)")
@@ -213,8 +303,10 @@ def main() -> int:
                     help="run only a plain 1 GiB device copy (3 times), the reference for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
-    if args.targets + args.cached + args.backward + args.dense > 1:
-        ap.error("--targets, --cached, --backward and --dense are separate benchmarks")
+    if args.targets + args.cached + args.backward + args.dense + args.layer > 1:
+        ap.error("--targets, --cached, --backward, --dense and --layer are separate benchmarks")
+    if args.layer:
+        return bench_layer(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(each GPU would run its own share of sequences with no exchange).",

@@ -32,7 +32,7 @@ template <int K>
 struct LayerCfg {
     static constexpr int NW = 4;
     static constexpr int ROWS = 32 * NW;           // tokens per workgroup
-    static constexpr int NC = 64;                  // output features per chunk
+    static constexpr int NC = K <= 256 ? 64 : 32;  // output features per chunk (<= 32 KB)
     static constexpr int NB = NC / 32;             // 32-feature blocks per chunk
     static constexpr int RB = 2 * K;               // bytes of one weight row
     static constexpr int CH = RB / 16;             // 16-byte chunks per row
@@ -55,7 +55,10 @@ struct WeightStage {
     using C = LayerCfg<K>;
     int goff[C::LOADS];   // global byte offset of each of this lane's loads
     int dst[C::LOADS];    // LDS byte offset (wave-uniform part) of each load
-    int rd[C::NKS];       // LDS byte offset of row l32, logical chunk 2ks + g
+    // LDS byte offset of row l32, logical chunk 2ks + g, for ks < 8; the
+    // swizzle changes only the low 4 chunk bits, so k-step ks reads at
+    // rd[ks % 8] + 256 (ks / 8).
+    int rd[8];
     __device__ WeightStage(int lane, int wv) {
 #pragma unroll
         for (int i = 0; i < C::LOADS; ++i) {
@@ -67,7 +70,7 @@ struct WeightStage {
         }
         const int g = lane >> 5, l32 = lane & 31;
 #pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) rd[ks] = l32 * C::RB + 16 * ((2 * ks + g) ^ wswz(l32));
+        for (int ks = 0; ks < 8; ++ks) rd[ks] = l32 * C::RB + 16 * ((2 * ks + g) ^ wswz(l32));
     }
     // Rows [c0, c0 + NC) of the (n x K) weight matrix into `buf`; rows past n
     // read as zero.
@@ -92,10 +95,34 @@ __device__ __forceinline__ void chunk_products(const unsigned char* buf, const W
     for (int ks = 0; ks < C::NKS; ++ks)
 #pragma unroll
         for (int b = 0; b < C::NB; ++b) {
-            const typename M::v8 wa =
-                    *reinterpret_cast<const typename M::v8*>(buf + b * 32 * C::RB + st.rd[ks]);
+            const typename M::v8 wa = *reinterpret_cast<const typename M::v8*>(
+                    buf + b * 32 * C::RB + 256 * (ks / 8) + st.rd[ks % 8]);
             acc[b] = M::mma(wa, z[ks], acc[b]);
         }
+}
+
+// Chunks [c_begin, c_end) of the weight matrix through two LDS buffers (the
+// first must already be issued into buffer 0).  Iteration c waits for chunk
+// c, issues chunk c+1, stores chunk c-1's results and then computes chunk c's
+// products: the stores drain during the products instead of holding up the
+// next wait, which counts them too.
+template <typename T, int K, typename Epi>
+__device__ __forceinline__ void chunk_loop(const uint16_t* w, int n, int c_begin, int c_end,
+                                           const WeightStage<K>& st, unsigned char* lds,
+                                           const typename Mfma<T>::v8* z, Epi& epilogue) {
+    using C = LayerCfg<K>;
+    f32x16 acc[C::NB], prev[C::NB];
+    for (int c = c_begin; c < c_end; ++c) {
+        __builtin_amdgcn_s_waitcnt(VMCNT_LE(0));
+        __syncthreads();
+        const int slot = (c - c_begin) & 1;
+        if (c + 1 < c_end) st.issue(w, n, (c + 1) * C::NC, lds + (slot ^ 1) * C::CHUNK_BYTES);
+        if (c > c_begin) epilogue(c - 1, prev);
+        chunk_products<T, K>(lds + slot * C::CHUNK_BYTES, st, z, acc);
+#pragma unroll
+        for (int b = 0; b < C::NB; ++b) prev[b] = acc[b];
+    }
+    if (c_begin < c_end) epilogue(c_end - 1, prev);
 }
 
 struct LayerInArgs {
@@ -139,35 +166,35 @@ __global__ __launch_bounds__(256, 2) void layer_in_kernel(LayerInArgs a) {
     const bool tok_live = tok < a.T;
 
     if (c_begin < c_end) st.issue(a.w1, n, c_begin * C::NC, lds);
-    for (int c = c_begin; c < c_end; ++c) {
-        __builtin_amdgcn_s_waitcnt(VMCNT_LE(0));
-        __syncthreads();
-        const int slot = (c - c_begin) & 1;
-        if (c + 1 < c_end) st.issue(a.w1, n, (c + 1) * C::NC, lds + (slot ^ 1) * C::CHUNK_BYTES);
-        f32x16 acc[C::NB];
-        chunk_products<T, K>(lds + slot * C::CHUNK_BYTES, st, z, acc);
-        // Epilogue: lane holds token `tok`, features c0 + 32 b + 8 i + 4 g + (0..3).
+    // Epilogue of chunk c: lane holds token `tok`, features c0 + 32 b + 8 i +
+    // 4 g + (0..3).  A chunk lies inside one part (heads d is a multiple of the
+    // chunk).
+    auto epilogue = [&](int c, const f32x16* acc) {
+        const int c0 = c * C::NC;
+        const int part = __builtin_amdgcn_readfirstlane(c0 / a.heads_d);
+        uint16_t* dst = part == 0 ? a.out[0] : part == 1 ? a.out[1] : part == 2 ? a.out[2]
+                                                                               : a.out[3];
+        dst += tok * a.heads_d + (c0 - part * a.heads_d) + 4 * g;
+        const float* bias_c = a.b1 + c0 + 4 * g;
         if (tok_live) {
 #pragma unroll
             for (int b = 0; b < C::NB; ++b)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int f = c * C::NC + 32 * b + 8 * i + 4 * g;   // first of 4 features
-                    const f32x4 bias = *reinterpret_cast<const f32x4*>(a.b1 + f);
+                    const f32x4 bias = *reinterpret_cast<const f32x4*>(bias_c + 32 * b + 8 * i);
                     f32x4 y;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const float s = acc[b][4 * i + j] + bias[j];
-                        y[j] = s * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * s));
+                        y[j] = s * __builtin_amdgcn_rcpf(
+                                           1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * s));
                     }
-                    const int part = f / a.heads_d;    // u, v, q, k (4 features never straddle)
-                    const int pos = f - part * a.heads_d;
                     const v4 yv = __builtin_convertvector(y, v4);
-                    *reinterpret_cast<u32x2*>(a.out[part] + tok * a.heads_d + pos) =
-                            __builtin_bit_cast(u32x2, yv);
+                    *reinterpret_cast<u32x2*>(dst + 32 * b + 8 * i) = __builtin_bit_cast(u32x2, yv);
                 }
         }
-    }
+    };
+    chunk_loop<T, K>(a.w1, n, c_begin, c_end, st, lds, z, epilogue);
 }
 
 struct LayerOutArgs {
@@ -184,6 +211,17 @@ struct LayerOutArgs {
     float eps;
     int chunks_per_wg;
 };
+
+// Hides the values of z from the optimiser (no instruction is emitted).
+template <int N, typename V>
+__device__ __forceinline__ void opaque_n(V* z) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        u32x4 w = __builtin_bit_cast(u32x4, z[i]);
+        asm volatile("" : "+v"(w));
+        z[i] = __builtin_bit_cast(V, w);
+    }
+}
 
 template <typename T, int K>
 __global__ __launch_bounds__(256, 2) void layer_out_kernel(LayerOutArgs a) {
@@ -209,6 +247,7 @@ __global__ __launch_bounds__(256, 2) void layer_out_kernel(LayerOutArgs a) {
     // its partner lane ^ 32 hold one token's features between them), scaled,
     // shifted and gated by u, rounded to T: the B operands of the product.
     v8 z[C::NKS];
+    auto opaque = [](v8* zz) { opaque_n<C::NKS>(zz); };
     const int64_t rows = a.T - t0;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.attn + t0 * K, (rows < 0 ? 0 : rows) * C::RB);
     const __amdgpu_buffer_rsrc_t ru = make_rsrc(a.u + t0 * K, (rows < 0 ? 0 : rows) * C::RB);
@@ -223,6 +262,9 @@ __global__ __launch_bounds__(256, 2) void layer_out_kernel(LayerOutArgs a) {
         for (int e = 0; e < 8; ++e) sum += (float)z[ks][e];
     sum += __shfl_xor(sum, 32);
     const float mean = sum * (1.0f / K);
+    // (each pass widens the stored values again: kept widened across the
+    // passes they would take twice the registers)
+    opaque(z);
     float sq = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks)
@@ -232,6 +274,7 @@ __global__ __launch_bounds__(256, 2) void layer_out_kernel(LayerOutArgs a) {
             sq += dlt * dlt;
         }
     sq += __shfl_xor(sq, 32);
+    opaque(z);
     const float rstd = __builtin_amdgcn_rsqf(sq * (1.0f / K) + a.eps);
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) {
@@ -254,32 +297,29 @@ __global__ __launch_bounds__(256, 2) void layer_out_kernel(LayerOutArgs a) {
     const int64_t tok = t0 + l32;
     const bool tok_live = tok < a.T;
 
-    for (int c = c_begin; c < c_end; ++c) {
-        __builtin_amdgcn_s_waitcnt(VMCNT_LE(0));
-        __syncthreads();
-        const int slot = (c - c_begin) & 1;
-        if (c + 1 < c_end) st.issue(a.w2, n, (c + 1) * C::NC, lds + (slot ^ 1) * C::CHUNK_BYTES);
-        f32x16 acc[C::NB];
-        chunk_products<T, K>(lds + slot * C::CHUNK_BYTES, st, z, acc);
-        // Epilogue: residual and bias; lane holds token `tok`, output
-        // features f .. f + 3.
+    // Epilogue of chunk c: residual and bias; lane holds token `tok`, output
+    // features f .. f + 3.
+    auto epilogue = [&](int c, const f32x16* acc) {
+        const int64_t row_f = tok * n + c * C::NC + 4 * g;
+        const float* bias_c = a.b2 + c * C::NC + 4 * g;
         if (tok_live) {
 #pragma unroll
             for (int b = 0; b < C::NB; ++b)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int f = c * C::NC + 32 * b + 8 * i + 4 * g;
-                    const f32x4 bias = *reinterpret_cast<const f32x4*>(a.b2 + f);
+                    const int fo = 32 * b + 8 * i;
+                    const f32x4 bias = *reinterpret_cast<const f32x4*>(bias_c + fo);
                     const v4 xr = __builtin_bit_cast(
-                            v4, *reinterpret_cast<const u32x2*>(a.x + tok * n + f));
+                            v4, *reinterpret_cast<const u32x2*>(a.x + row_f + fo));
                     f32x4 y;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) y[j] = acc[b][4 * i + j] + bias[j] + (float)xr[j];
                     const v4 yv = __builtin_convertvector(y, v4);
-                    *reinterpret_cast<u32x2*>(a.y + tok * n + f) = __builtin_bit_cast(u32x2, yv);
+                    *reinterpret_cast<u32x2*>(a.y + row_f + fo) = __builtin_bit_cast(u32x2, yv);
                 }
         }
-    }
+    };
+    chunk_loop<T, K>(a.w2, n, c_begin, c_end, st, lds, z, epilogue);
 }
 
 // Splits the output chunks over grid.y so that the launch has at least two
