@@ -53,11 +53,11 @@ METRIC_CACHED = "HSTU cached-history attn fwd useful TFLOP/s (M-FALCON micro-bat
 # source the bench reports traffic as null.
 TRAFFIC = {
     "kernel_source": "generative_recommendation_attention_amd/csrc/attn_fwd.hip",
-    "kernel_sha256": "7d5a1851dbe7f040b4b1212d26300bb444fa49bd3f67216a4e434d62b4c1378e",
+    "kernel_sha256": "1957238a0b42a93d6da9c811f5ea9852fa5a6963f0741d230bb5feede9d317a2",
     "fetch_scale": 2.0,
     "write_scale": 1.0,
-    "fetch_kib": {2: 102957.0},
-    "write_kib": {2: 37944.3},
+    "fetch_kib": {2: 93854.9},
+    "write_kib": {2: 37939.5},
 }
 
 
