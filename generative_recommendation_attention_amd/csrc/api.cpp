@@ -273,9 +273,9 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
     tc.sched = false;
     hipError_t e;
     if (!wl.fused) {
-        e = hstu::launch_schedule(seq_offsets, num_seqs, heads, hstu::q_tile_rows(dt, d), wl,
-                                  stream, sort, timed ? tc.e[0] : nullptr,
-                                  timed ? tc.e[1] : nullptr);
+        const int rows = hstu::q_tile_rows(dt, d, mi.hist_offsets != nullptr);
+        e = hstu::launch_schedule(seq_offsets, num_seqs, heads, rows, wl, stream, sort,
+                                  timed ? tc.e[0] : nullptr, timed ? tc.e[1] : nullptr);
         if (e != hipSuccess) return hip_fail(e);
         tc.sched = timed;
     }

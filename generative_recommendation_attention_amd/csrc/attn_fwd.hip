@@ -733,6 +733,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
 // ---------------------------------------------------------------------------
 constexpr int NW16 = 4;
 template <int D> struct QBlocks { static constexpr int value = D == 64 ? 2 : 1; };
+// The cached-history form runs one 32-row block per wave (128-row items): its
+// calls hold one micro-batch of candidates per request, and 256-row items
+// would leave half of the resident workgroups without work at 16 x 1024.
+template <int D, int MASK> struct QBlocksFor {
+    static constexpr int value = MASK == MASK_CACHED ? 1 : QBlocks<D>::value;
+};
 template <int D> struct KeyTile { static constexpr int value = D == 64 ? 64 : 32; };
 template <int D> struct Prefetch { static constexpr int value = 2; };
 constexpr int NWF = 4;
@@ -759,15 +765,16 @@ hipError_t launch16(const FwdParams& p, WorkList wl, int grid, hipStream_t strea
     a.score_scale = -p.alpha * LOG2E;
     a.out_scale = -LN2 / p.n;
     constexpr int QB = QBlocks<D>::value, BK = KeyTile<D>::value, PF = Prefetch<D>::value;
+    constexpr int QBC = QBlocksFor<D, MASK_CACHED>::value;
     const int mode = p.hist_offsets ? MASK_CACHED : p.num_targets ? MASK_TARGETS : MASK_CAUSAL;
     using Fn = void (*)(KernelArgs);
     static constexpr Fn fns[2][3] = {
             {attn_fwd_mfma16<T, D, NW16, QB, BK, PF, false, MASK_CAUSAL>,
              attn_fwd_mfma16<T, D, NW16, QB, BK, PF, false, MASK_TARGETS>,
-             attn_fwd_mfma16<T, D, NW16, QB, BK, PF, false, MASK_CACHED>},
+             attn_fwd_mfma16<T, D, NW16, QBC, BK, PF, false, MASK_CACHED>},
             {attn_fwd_mfma16<T, D, NW16, QB, BK, PF, true, MASK_CAUSAL>,
              attn_fwd_mfma16<T, D, NW16, QB, BK, PF, true, MASK_TARGETS>,
-             attn_fwd_mfma16<T, D, NW16, QB, BK, PF, true, MASK_CACHED>}};
+             attn_fwd_mfma16<T, D, NW16, QBC, BK, PF, true, MASK_CACHED>}};
     const Fn fn = fns[wl.fused ? 1 : 0][mode];
     if (grid <= 0) {
         static int cached[2][3] = {};
@@ -834,8 +841,13 @@ int device_cus() {
     return cached_cus;
 }
 
-int q_tile_rows(Dtype dt, int d) {
+int q_tile_rows(Dtype dt, int d, bool cached) {
     if (dt == Dtype::FP32) return TileF32<64, NWF, BKF>::BQ;
+    if (cached)
+        return d == 64 ? Tile16<__bf16, 64, NW16, QBlocksFor<64, MASK_CACHED>::value,
+                                KeyTile<64>::value, Prefetch<64>::value>::BQ
+                       : Tile16<__bf16, 128, NW16, QBlocksFor<128, MASK_CACHED>::value,
+                                KeyTile<128>::value, Prefetch<128>::value>::BQ;
     return d == 64 ? Tile16<__bf16, 64, NW16, QBlocks<64>::value, KeyTile<64>::value,
                             Prefetch<64>::value>::BQ
                    : Tile16<__bf16, 128, NW16, QBlocks<128>::value, KeyTile<128>::value,

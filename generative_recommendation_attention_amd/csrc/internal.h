@@ -148,7 +148,7 @@ struct FwdParams {
 };
 
 // Rows of Q handled by one work item for this element type and head size.
-int q_tile_rows(Dtype dt, int d);
+int q_tile_rows(Dtype dt, int d, bool cached = false);
 
 // Compute units of the current device.
 int device_cus();
