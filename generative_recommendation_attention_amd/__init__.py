@@ -279,8 +279,8 @@ def hstu_profile_read(reset: bool = True) -> KernelTimes:
 def hstu_attn_bwd(q, k, v, dout, seq_offsets, alpha: float, n: float, num_targets=None,
                   grads=None, stream=None):
     """Gradients (dq, dk, dv) of the forward (target-aware when num_targets is
-    given) for the upstream gradient dout.  bfloat16 / float16 only.  `grads`
-    may supply three preallocated output tensors."""
+    given) for the upstream gradient dout.  `grads` may supply three
+    preallocated output tensors."""
     import torch
     _check_tensors(q, k, v, seq_offsets, torch.empty_like(q))
     if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_cuda or \

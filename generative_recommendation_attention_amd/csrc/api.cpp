@@ -307,7 +307,6 @@ hstu_status_t attn_bwd_call(const void* q, const void* k, const void* v, const v
                             void* dq, void* dk, void* dv, hipStream_t stream, int dtype) {
     hstu_status_t st = check_args(q, k, v, seq_offsets, num_seqs, heads, d, alpha, n, dq, dtype);
     if (st != HSTU_OK) return st;
-    if (dtype == HSTU_FP32) return HSTU_ERR_UNSUPPORTED;
     if (num_seqs == 0) return HSTU_OK;
     if (!dout || !dk || !dv) return HSTU_ERR_INVALID_ARG;
     if (!aligned16(dout) || !aligned16(dk) || !aligned16(dv)) return HSTU_ERR_INVALID_ARG;

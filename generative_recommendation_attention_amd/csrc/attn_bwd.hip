@@ -520,6 +520,315 @@ hipError_t launch_bwd_mask(const BwdParams& p, WorkList wl, hipStream_t stream, 
                          : launch_bwd_typed<T, D, false>(p, wl, stream, start, stop);
 }
 
+// ---------------------------------------------------------------------------
+// fp32: v_mfma_f32_32x32x2_f32, same two kernels and item shapes, tiles staged
+// synchronously into padded LDS arrays (like the fp32 forward).  A lane's
+// k-slice is one element: accumulator register r of lane (l32, g) holds row
+// 8(r/4) + 4g + r%4, which is exactly the k index of k-step r of a product
+// that contracts over those rows, so P, dS and dS^T feed the second products
+// register by register.
+// ---------------------------------------------------------------------------
+struct BwdArgsF32 {
+    const float* q;
+    const float* k;
+    const float* v;
+    const float* dout;
+    float* dq;
+    float* dk;
+    float* dv;
+    const int32_t* offsets;
+    const int32_t* ntgt;
+    WorkList wl;
+    int num_seqs;
+    int heads;
+    float alpha;
+    float dv_scale;
+    float g_scale;
+};
+
+template <int D>
+struct BwdCfgF32 {
+    static constexpr int NW = 4;
+    static constexpr int ROWS = 32 * NW;
+    static constexpr int STR = D + 2;                    // floats per LDS row
+    static constexpr int CHUNKS = 32 * D / 4 / (NW * 64);   // float4 loads per thread per array
+    static_assert(CHUNKS * NW * 64 * 4 == 32 * D, "array must split evenly");
+};
+
+// Rows [row0, row0 + 32) of one tensor into a padded LDS array; rows at or
+// past rows_avail as zero.  Every thread of the workgroup takes part.
+template <int D>
+__device__ __forceinline__ void stage_f32(const float* base, int64_t row_stride, int row0,
+                                          int rows_avail, float* arr) {
+    using C = BwdCfgF32<D>;
+#pragma unroll
+    for (int i = 0; i < C::CHUNKS; ++i) {
+        const int id = threadIdx.x + i * C::NW * 64;
+        const int r = id / (D / 4), c4 = id % (D / 4);
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (row0 + r < rows_avail)
+            x = *reinterpret_cast<const float4*>(base + (int64_t)(row0 + r) * row_stride + 4 * c4);
+        float* d = arr + r * C::STR + 4 * c4;
+        d[0] = x.x;
+        d[1] = x.y;
+        d[2] = x.z;
+        d[3] = x.w;
+    }
+}
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+template <int D, bool FUSED, bool TGT>
+__global__ __launch_bounds__(256) void attn_bwd_dkv_f32(BwdArgsF32 a) {
+    using C = BwdCfgF32<D>;
+    constexpr int NDB = D / 32;
+    __shared__ __attribute__((aligned(16))) float ql[32 * C::STR];
+    __shared__ __attribute__((aligned(16))) float ol[32 * C::STR];
+    __shared__ int s_item[NQ];
+    __shared__ LocalTables lt;
+    __shared__ int tbl_scratch[FUSE_SEQS];
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int g = lane >> 5, l32 = lane & 31;
+    const int H = a.heads;
+    const int64_t row_stride = (int64_t)H * D;
+
+    Tables tb;
+    if constexpr (FUSED)
+        tb = build_local_tables(lt, tbl_scratch, a.offsets, a.num_seqs, H, C::ROWS, a.wl.ctl);
+    else
+        tb = global_tables(a.wl);
+    clear_next_set(a.wl.ctl, a.wl.set);
+    ItemSource src(a.wl.ctl, a.wl.set);
+    int qx, w;
+    while (src.next(tb, s_item, &qx, &w)) {
+        const Item it = decode_item(tb, a.num_seqs, H, qx, w);
+        const int start = a.offsets[it.seq];
+        const int s = a.offsets[it.seq + 1] - start;
+        const int ntile = (s + C::ROWS - 1) / C::ROWS;
+        const int kt = ntile - 1 - it.qtile;
+        const int hist = TGT ? s - min(max(a.ntgt[it.seq], 0), s) : s;
+        const int k0i = kt * C::ROWS;
+        const int kw0 = k0i + 32 * wv;
+        const bool live = kw0 < s;
+        const int q_end = (TGT && k0i >= hist) ? min(s, k0i + C::ROWS) : s;
+        const int j0 = k0i / 32;
+        const int nblk = (q_end + 31) / 32 - j0;
+        const int64_t seq_base = (int64_t)start * row_stride + (int64_t)it.head * D;
+        const int key = kw0 + l32;
+        // B operands: K and V of the lane's key, head-dim element 2 ks + g.
+        float kop[D / 2], vop[D / 2];
+#pragma unroll
+        for (int ks = 0; ks < D / 2; ++ks) {
+            const bool ok = key < s;
+            kop[ks] = ok ? a.k[seq_base + (int64_t)key * row_stride + 2 * ks + g] : 0.0f;
+            vop[ks] = ok ? a.v[seq_base + (int64_t)key * row_stride + 2 * ks + g] : 0.0f;
+        }
+        f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = (f32x16){};
+
+        for (int c = 0; c < nblk; ++c) {
+            const int q0 = 32 * (j0 + c);
+            stage_f32<D>(a.q + seq_base, row_stride, q0, q_end, ql);
+            stage_f32<D>(a.dout + seq_base, row_stride, q0, q_end, ol);
+            __syncthreads();
+            const bool skip = !live || q0 < kw0 || (TGT && kw0 >= hist && q0 > kw0);
+            if (!skip) {
+                f32x16 st = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+                for (int ks = 0; ks < D / 2; ++ks) {
+                    st = mfma_f32(ql[l32 * C::STR + 2 * ks + g], kop[ks], st);
+                    dp = mfma_f32(ol[l32 * C::STR + 2 * ks + g], vop[ks], dp);
+                }
+                const bool masked = q0 == kw0 || (TGT && kw0 + 31 >= hist);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float pr, dsr;
+                    pointwise(st[r], dp[r], a.alpha, &pr, &dsr);
+                    const int qrow = 8 * (r >> 2) + 4 * g + (r & 3);   // row inside the block
+                    if (masked) {
+                        const int qr = q0 + qrow;
+                        const bool keep = key <= qr && (key < hist || key == qr);
+                        pr = keep ? pr : 0.0f;
+                        dsr = keep ? dsr : 0.0f;
+                    }
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        dv[db] = mfma_f32(ol[qrow * C::STR + 32 * db + l32], pr, dv[db]);
+                        dk[db] = mfma_f32(ql[qrow * C::STR + 32 * db + l32], dsr, dk[db]);
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        if (live) {
+            // lane: key; registers: head-dim rows 32 db + 8 (r/4) + 4 g + r%4
+            if (key < s) {
+                float* pk = a.dk + seq_base + (int64_t)key * row_stride;
+                float* pv = a.dv + seq_base + (int64_t)key * row_stride;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int e = 32 * db + 8 * i + 4 * g;
+                        *reinterpret_cast<float4*>(pk + e) =
+                                make_float4(dk[db][4 * i] * a.g_scale, dk[db][4 * i + 1] * a.g_scale,
+                                            dk[db][4 * i + 2] * a.g_scale, dk[db][4 * i + 3] * a.g_scale);
+                        *reinterpret_cast<float4*>(pv + e) =
+                                make_float4(dv[db][4 * i] * a.dv_scale, dv[db][4 * i + 1] * a.dv_scale,
+                                            dv[db][4 * i + 2] * a.dv_scale,
+                                            dv[db][4 * i + 3] * a.dv_scale);
+                    }
+            }
+        }
+    }
+}
+
+template <int D, bool FUSED, bool TGT>
+__global__ __launch_bounds__(256) void attn_bwd_dq_f32(BwdArgsF32 a) {
+    using C = BwdCfgF32<D>;
+    constexpr int NDB = D / 32;
+    __shared__ __attribute__((aligned(16))) float kl[32 * C::STR];
+    __shared__ __attribute__((aligned(16))) float vl[32 * C::STR];
+    __shared__ int s_item[NQ];
+    __shared__ LocalTables lt;
+    __shared__ int tbl_scratch[FUSE_SEQS];
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int g = lane >> 5, l32 = lane & 31;
+    const int H = a.heads;
+    const int64_t row_stride = (int64_t)H * D;
+
+    Tables tb;
+    if constexpr (FUSED)
+        tb = build_local_tables(lt, tbl_scratch, a.offsets, a.num_seqs, H, C::ROWS, a.wl.ctl);
+    else
+        tb = global_tables(a.wl);
+    clear_next_set(a.wl.ctl, a.wl.set);
+    ItemSource src(a.wl.ctl, a.wl.set);
+    int qx, w;
+    while (src.next(tb, s_item, &qx, &w)) {
+        const Item it = decode_item(tb, a.num_seqs, H, qx, w);
+        const int start = a.offsets[it.seq];
+        const int s = a.offsets[it.seq + 1] - start;
+        const int hist = TGT ? s - min(max(a.ntgt[it.seq], 0), s) : s;
+        const int q0 = it.qtile * C::ROWS;
+        const int wr0 = q0 + 32 * wv;
+        const bool live = wr0 < s;
+        const int kv_end = min(s, q0 + C::ROWS);
+        const int nb_all = (kv_end + 31) / 32;
+        const int nh = TGT ? (hist + 31) / 32 : nb_all;
+        const int jump = TGT ? max(q0 / 32 - nh, 0) : 0;
+        const int nblk = nb_all - jump;
+        const int64_t seq_base = (int64_t)start * row_stride + (int64_t)it.head * D;
+        const int row = wr0 + l32;
+        float qop[D / 2], oop[D / 2];
+#pragma unroll
+        for (int ks = 0; ks < D / 2; ++ks) {
+            const bool ok = row < s;
+            qop[ks] = ok ? a.q[seq_base + (int64_t)row * row_stride + 2 * ks + g] : 0.0f;
+            oop[ks] = ok ? a.dout[seq_base + (int64_t)row * row_stride + 2 * ks + g] : 0.0f;
+        }
+        f32x16 dq[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) dq[db] = (f32x16){};
+
+        for (int c = 0; c < nblk; ++c) {
+            const int k0 = 32 * (c >= nh ? c + jump : c);
+            stage_f32<D>(a.k + seq_base, row_stride, k0, kv_end, kl);
+            stage_f32<D>(a.v + seq_base, row_stride, k0, kv_end, vl);
+            __syncthreads();
+            const bool skip = !live || k0 > wr0 || (TGT && k0 >= hist && k0 + 31 < wr0);
+            if (!skip) {
+                f32x16 st = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+                for (int ks = 0; ks < D / 2; ++ks) {
+                    st = mfma_f32(kl[l32 * C::STR + 2 * ks + g], qop[ks], st);
+                    dp = mfma_f32(vl[l32 * C::STR + 2 * ks + g], oop[ks], dp);
+                }
+                const bool masked = k0 + 31 >= wr0 || (TGT && k0 + 31 >= hist);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float pr, dsr;
+                    pointwise(st[r], dp[r], a.alpha, &pr, &dsr);
+                    const int krow = 8 * (r >> 2) + 4 * g + (r & 3);   // key inside the block
+                    if (masked) {
+                        const int kk = k0 + krow;
+                        dsr = (kk <= row && (kk < hist || kk == row)) ? dsr : 0.0f;
+                    }
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+                        dq[db] = mfma_f32(kl[krow * C::STR + 32 * db + l32], dsr, dq[db]);
+                }
+            }
+            __syncthreads();
+        }
+        if (live && row < s) {
+            float* pq = a.dq + seq_base + (int64_t)row * row_stride;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int e = 32 * db + 8 * i + 4 * g;
+                    *reinterpret_cast<float4*>(pq + e) =
+                            make_float4(dq[db][4 * i] * a.g_scale, dq[db][4 * i + 1] * a.g_scale,
+                                        dq[db][4 * i + 2] * a.g_scale, dq[db][4 * i + 3] * a.g_scale);
+                }
+        }
+    }
+}
+
+template <int D, bool TGT>
+hipError_t launch_bwd_f32_typed(const BwdParams& p, WorkList wl, hipStream_t stream,
+                                hipEvent_t start, hipEvent_t stop) {
+    BwdArgsF32 a;
+    a.q = static_cast<const float*>(p.q);
+    a.k = static_cast<const float*>(p.k);
+    a.v = static_cast<const float*>(p.v);
+    a.dout = static_cast<const float*>(p.dout);
+    a.dq = static_cast<float*>(p.dq);
+    a.dk = static_cast<float*>(p.dk);
+    a.dv = static_cast<float*>(p.dv);
+    a.offsets = p.offsets;
+    a.ntgt = p.num_targets;
+    a.num_seqs = p.num_seqs;
+    a.heads = p.heads;
+    a.alpha = p.alpha;
+    a.dv_scale = 1.0f / p.n;
+    a.g_scale = p.alpha / p.n;
+    using Fn = void (*)(BwdArgsF32);
+    const Fn f_dkv = wl.fused ? attn_bwd_dkv_f32<D, true, TGT> : attn_bwd_dkv_f32<D, false, TGT>;
+    const Fn f_dq = wl.fused ? attn_bwd_dq_f32<D, true, TGT> : attn_bwd_dq_f32<D, false, TGT>;
+    static int grids[2][2] = {};
+    int& g_dkv = grids[wl.fused ? 1 : 0][0];
+    int& g_dq = grids[wl.fused ? 1 : 0][1];
+    if (!g_dkv) g_dkv = resident_grid(f_dkv, 256);
+    if (!g_dq) g_dq = resident_grid(f_dq, 256);
+    a.wl = wl;
+    if (start)
+        hipExtLaunchKernelGGL(f_dkv, dim3(g_dkv), dim3(256), 0, stream, start, nullptr, 0, a);
+    else
+        hipLaunchKernelGGL(f_dkv, dim3(g_dkv), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.wl.set = wl.set ^ 1;
+    if (stop)
+        hipExtLaunchKernelGGL(f_dq, dim3(g_dq), dim3(256), 0, stream, nullptr, stop, 0, a);
+    else
+        hipLaunchKernelGGL(f_dq, dim3(g_dq), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_f32(const BwdParams& p, WorkList wl, hipStream_t stream, hipEvent_t start,
+                          hipEvent_t stop) {
+    return p.num_targets ? launch_bwd_f32_typed<D, true>(p, wl, stream, start, stop)
+                         : launch_bwd_f32_typed<D, false>(p, wl, stream, start, stop);
+}
+
 }  // namespace
 
 hipError_t launch_backward(const BwdParams& p, Dtype dt, WorkList wl, hipStream_t stream,
@@ -530,6 +839,9 @@ hipError_t launch_backward(const BwdParams& p, Dtype dt, WorkList wl, hipStream_
     if (dt == Dtype::FP16)
         return p.d == 64 ? launch_bwd_mask<_Float16, 64>(p, wl, stream, start, stop)
                          : launch_bwd_mask<_Float16, 128>(p, wl, stream, start, stop);
+    if (dt == Dtype::FP32)
+        return p.d == 64 ? launch_bwd_f32<64>(p, wl, stream, start, stop)
+                         : launch_bwd_f32<128>(p, wl, stream, start, stop);
     return hipErrorInvalidValue;
 }
 

@@ -210,9 +210,10 @@ hstu_status_t hstu_layer_out_proj(const void* attn, const void* u, const void* x
  *                    aligned, none overlapping another or any input.
  *   num_targets    : as for hstu_attn_fwd_targets (device int32[num_seqs]).
  *
- * Element types: bfloat16 and float16 only (HSTU_FP32 returns
- * HSTU_ERR_UNSUPPORTED).  P = silu(x) and the score gradient are rounded to
- * the input type before their products, as the forward rounds its weights.
+ * Element types: bfloat16 and float16 on the matrix cores with float32
+ * accumulation, P = silu(x) and the score gradient rounded to the input type
+ * before their products (as the forward rounds its weights); float32 runs
+ * every product in float32.
  * A call is two kernels (dk/dv, then dq; plus the work-list kernel on a new
  * scratch area or for more than 256 sequences).  Streams, scratch and errors
  * as for hstu_attn_fwd. */

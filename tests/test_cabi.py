@@ -153,7 +153,7 @@ def _call_bwd(lib, dout=48, dq=64, dk=80, dv=96, tg=None, **kw):
     (dict(dq=48), hstu.HSTU_ERR_INVALID_ARG),       # dq aliases dout
     (dict(dk=64), hstu.HSTU_ERR_INVALID_ARG),       # dk aliases dq
     (dict(dv=16), hstu.HSTU_ERR_INVALID_ARG),       # dv aliases q
-    (dict(dtype=hstu.HSTU_FP32), hstu.HSTU_ERR_UNSUPPORTED),
+    (dict(dtype=7), hstu.HSTU_ERR_UNSUPPORTED),
     (dict(d=96), hstu.HSTU_ERR_UNSUPPORTED),
     (dict(n=0.0), hstu.HSTU_ERR_INVALID_ARG),
     (dict(tg=0), hstu.HSTU_ERR_INVALID_ARG),        # target counts missing
