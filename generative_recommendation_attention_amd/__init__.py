@@ -32,7 +32,7 @@ HSTU_BF16, HSTU_FP16, HSTU_FP32 = 0, 1, 2
 # Every symbol include/hstu.h declares.
 EXPORTS = ("hstu_attn_fwd", "hstu_attn_fwd_bf16", "hstu_attn_fwd_fp16", "hstu_attn_fwd_fp32",
            "hstu_attn_fwd_targets", "hstu_attn_fwd_cached", "hstu_attn_fwd_dense", "hstu_attn_bwd",
-           "hstu_layer_in_proj", "hstu_layer_out_proj",
+           "hstu_attn_bwd_dense", "hstu_layer_in_proj", "hstu_layer_out_proj",
            "hstu_attn_bwd_targets", "hstu_validate_offsets", "hstu_status_string", "hstu_last_hip_error",
            "hstu_release_workspace", "hstu_profile_enable", "hstu_profile_read")
 
@@ -89,6 +89,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hstu_layer_out_proj.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, i64, i32, i32, i32, vp,
                                         vp, ctypes.c_int]
     lib.hstu_layer_out_proj.restype = ctypes.c_int
+    lib.hstu_attn_bwd_dense.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, f32, vp, vp, vp,
+                                        vp, ctypes.c_int]
+    lib.hstu_attn_bwd_dense.restype = ctypes.c_int
     lib.hstu_attn_bwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp, vp, vp,
                                   ctypes.c_int]
     lib.hstu_attn_bwd.restype = ctypes.c_int
@@ -398,3 +401,28 @@ def hstu_layer_out_proj(attn, u, x, gamma, beta, eps: float, w2, b2, out=None, s
                                  _dtype_code(attn))
     _check(st, "hstu_layer_out_proj")
     return out
+
+
+def hstu_attn_bwd_dense(q, k, v, dout, alpha: float, n: float, grads=None, stream=None):
+    """Gradients (dq, dk, dv) of hstu_attn_fwd_dense: all tensors
+    (batch, heads, seq_len, d)."""
+    import torch
+    if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, dout)):
+        raise ValueError("q, k, v, dout must share one (batch, heads, seq_len, d) shape")
+    for t in (q, k, v, dout):
+        _gpu_contig("input", t, q.dtype)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
+    for t in grads:
+        _gpu_contig("gradient output", t, q.dtype, q.shape)
+    B, heads, S, d = q.shape
+    if q.numel() == 0:
+        return grads
+    lib = load_library()
+    dq, dk, dv = grads
+    st = lib.hstu_attn_bwd_dense(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), B,
+                                 heads, S, d, float(alpha), float(n), dq.data_ptr(),
+                                 dk.data_ptr(), dv.data_ptr(), _stream_handle(stream),
+                                 _dtype_code(q))
+    _check(st, "hstu_attn_bwd_dense")
+    return grads

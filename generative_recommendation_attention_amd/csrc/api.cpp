@@ -81,6 +81,28 @@ void forget_ramp_under(Scratch* sc, size_t bytes) {
     if (sc->ramp_count && bytes > sc->ramp_at) sc->ramp_count = 0;
 }
 
+// Offsets i * len (i = 0 .. num_seqs) of the dense layout at byte `at` of the
+// area (which must hold them), written once per (area, num_seqs, len).
+hstu_status_t dense_ramp(Scratch* sc, size_t at, int num_seqs, int64_t len, hipStream_t stream,
+                         const int32_t** out) {
+    int32_t* ramp = reinterpret_cast<int32_t*>(static_cast<char*>(sc->ptr) + at);
+    bool have;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        have = sc->ramp_count == num_seqs && sc->ramp_len == len && sc->ramp_at == at;
+    }
+    if (!have) {
+        hipError_t e = hstu::launch_fill_ramp(ramp, num_seqs + 1, (int)len, stream);
+        if (e != hipSuccess) return hip_fail(e);
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        sc->ramp_count = num_seqs;
+        sc->ramp_len = len;
+        sc->ramp_at = at;
+    }
+    *out = ramp;
+    return HSTU_OK;
+}
+
 // ---- device checks ----------------------------------------------------------
 
 std::mutex g_dev_mu;
@@ -217,23 +239,8 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
     hstu::WorkList wl = hstu::worklist_carve(sc->ptr, num_seqs, heads);
     forget_ramp_under(sc, wl_bytes);
     if (mi.dense) {
-        // Offsets i * S in the scratch area, written once per (area, B, S).
-        int32_t* ramp = reinterpret_cast<int32_t*>(static_cast<char*>(sc->ptr) + wl_bytes);
-        bool have;
-        {
-            std::lock_guard<std::mutex> lock(g_scratch_mu);
-            have = sc->ramp_count == num_seqs && sc->ramp_len == mi.dense_len &&
-                   sc->ramp_at == wl_bytes;
-        }
-        if (!have) {
-            hipError_t e = hstu::launch_fill_ramp(ramp, num_seqs + 1, (int)mi.dense_len, stream);
-            if (e != hipSuccess) return hip_fail(e);
-            std::lock_guard<std::mutex> lock(g_scratch_mu);
-            sc->ramp_count = num_seqs;
-            sc->ramp_len = mi.dense_len;
-            sc->ramp_at = wl_bytes;
-        }
-        seq_offsets = ramp;
+        st = dense_ramp(sc, wl_bytes, num_seqs, mi.dense_len, stream, &seq_offsets);
+        if (st != HSTU_OK) return st;
     }
     // Small batches build their queue tables inside the attention kernel.  The
     // work-list kernel still runs when this call's counter set is not known to
@@ -301,11 +308,15 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
 
 // One backward call: the dK/dV kernel, then the dQ kernel, on one work list
 // of BWD_TILE_ROWS-row items (each launch takes one of the two counter sets).
+// dense_len > 0: the dense (B, heads, S, d) layout with S = dense_len, no offsets.
 hstu_status_t attn_bwd_call(const void* q, const void* k, const void* v, const void* dout,
                             const int32_t* seq_offsets, const int32_t* num_targets,
                             int32_t num_seqs, int32_t heads, int32_t d, float alpha, float n,
-                            void* dq, void* dk, void* dv, hipStream_t stream, int dtype) {
-    hstu_status_t st = check_args(q, k, v, seq_offsets, num_seqs, heads, d, alpha, n, dq, dtype);
+                            void* dq, void* dk, void* dv, hipStream_t stream, int dtype,
+                            int64_t dense_len = 0) {
+    // (a dense call has no offsets yet: q stands in for the pointer check)
+    const int32_t* off_check = dense_len > 0 ? reinterpret_cast<const int32_t*>(q) : seq_offsets;
+    hstu_status_t st = check_args(q, k, v, off_check, num_seqs, heads, d, alpha, n, dq, dtype);
     if (st != HSTU_OK) return st;
     if (num_seqs == 0) return HSTU_OK;
     if (!dout || !dk || !dv) return HSTU_ERR_INVALID_ARG;
@@ -322,10 +333,16 @@ hstu_status_t attn_bwd_call(const void* q, const void* k, const void* v, const v
 
     const hstu::Dtype dt = static_cast<hstu::Dtype>(dtype);
     Scratch* sc = nullptr;
-    st = scratch_for(dev, stream, hstu::worklist_bytes(num_seqs, heads), &sc);
+    const size_t wl_bytes = (hstu::worklist_bytes(num_seqs, heads) + 255) & ~(size_t)255;
+    const size_t ramp_bytes = dense_len > 0 ? sizeof(int32_t) * ((size_t)num_seqs + 1) : 0;
+    st = scratch_for(dev, stream, wl_bytes + ramp_bytes, &sc);
     if (st != HSTU_OK) return st;
     hstu::WorkList wl = hstu::worklist_carve(sc->ptr, num_seqs, heads);
-    forget_ramp_under(sc, hstu::worklist_bytes(num_seqs, heads));
+    forget_ramp_under(sc, wl_bytes);
+    if (dense_len > 0) {
+        st = dense_ramp(sc, wl_bytes, num_seqs, dense_len, stream, &seq_offsets);
+        if (st != HSTU_OK) return st;
+    }
     const hstu::SortChoice sort = sort_choice_env();
     bool clean;
     {
@@ -347,6 +364,8 @@ hstu_status_t attn_bwd_call(const void* q, const void* k, const void* v, const v
     p.dv = dv;
     p.offsets = seq_offsets;
     p.num_targets = num_targets;
+    p.dense = dense_len > 0;
+    p.dense_len = dense_len;
     p.num_seqs = num_seqs;
     p.heads = heads;
     p.d = d;
@@ -519,6 +538,21 @@ hstu_status_t hstu_attn_bwd_targets(const void* q, const void* k, const void* v,
         return HSTU_ERR_INVALID_ARG;
     return attn_bwd_call(q, k, v, dout, seq_offsets, num_targets, num_seqs, heads, d, alpha, n,
                          dq, dk, dv, stream, dtype);
+}
+
+hstu_status_t hstu_attn_bwd_dense(const void* q, const void* k, const void* v, const void* dout,
+                                  int32_t batch, int32_t heads, int32_t seq_len, int32_t d,
+                                  float alpha, float n, void* dq, void* dk, void* dv,
+                                  hipStream_t stream, hstu_dtype_t dtype) {
+    if (dtype != HSTU_BF16 && dtype != HSTU_FP16 && dtype != HSTU_FP32) return HSTU_ERR_UNSUPPORTED;
+    if (batch < 0 || heads < 1 || seq_len < 0) return HSTU_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return HSTU_ERR_UNSUPPORTED;
+    if ((long long)batch * seq_len > 0x7fffffffLL || (long long)batch * heads > 0x7fffffffLL)
+        return HSTU_ERR_UNSUPPORTED;
+    if (!std::isfinite(alpha) || !std::isfinite(n) || n == 0.0f) return HSTU_ERR_INVALID_ARG;
+    if (batch == 0 || seq_len == 0) return HSTU_OK;
+    return attn_bwd_call(q, k, v, dout, nullptr, nullptr, batch, heads, d, alpha, n, dq, dk, dv,
+                         stream, dtype, seq_len);
 }
 
 hstu_status_t hstu_attn_fwd_cached(const void* q, const void* k, const void* v,

@@ -59,6 +59,10 @@ struct BwdArgs {
     const int32_t* offsets;
     const int32_t* ntgt;   // candidates per sequence (target-aware mask), or null
     WorkList wl;
+    // (T, heads, D) jagged: rows heads * D apart, heads D apart; dense
+    // (B, heads, S, D): rows D apart, heads S * D apart (offsets i * S)
+    int64_t row_stride;
+    int64_t head_stride;
     int num_seqs;
     int heads;
     float alpha;
@@ -224,7 +228,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv(BwdArgs a) {
     const int g = lane >> 5;
     const int l32 = lane & 31;
     const int H = a.heads;
-    const int64_t row_stride = (int64_t)H * D;
+    const int64_t row_stride = a.row_stride;
     const int row_bytes = (int)(row_stride * 2);
     const LaneOffsets<D> lo(lane, wv, row_bytes);
 
@@ -255,7 +259,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv(BwdArgs a) {
         const int q_end = (TGT && k0i >= hist) ? min(s, k0i + C::ROWS) : s;
         const int j0 = k0i / 32;
         const int nblk = (q_end + 31) / 32 - j0;
-        const int64_t seq_base = (int64_t)start * row_stride + (int64_t)head * D;
+        const int64_t seq_base = (int64_t)start * H * D + (int64_t)head * a.head_stride;
         const uint16_t* qb = a.q + seq_base;
         const uint16_t* ob = a.dout + seq_base;
 
@@ -367,7 +371,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdArgs a) {
     const int g = lane >> 5;
     const int l32 = lane & 31;
     const int H = a.heads;
-    const int64_t row_stride = (int64_t)H * D;
+    const int64_t row_stride = a.row_stride;
     const int row_bytes = (int)(row_stride * 2);
     const LaneOffsets<D> lo(lane, wv, row_bytes);
 
@@ -399,7 +403,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdArgs a) {
         const int nh = TGT ? (hist + 31) / 32 : nb_all;
         const int jump = TGT ? max(q0 / 32 - nh, 0) : 0;
         const int nblk = nb_all - jump;
-        const int64_t seq_base = (int64_t)start * row_stride + (int64_t)head * D;
+        const int64_t seq_base = (int64_t)start * H * D + (int64_t)head * a.head_stride;
         const uint16_t* kb = a.k + seq_base;
         const uint16_t* vb = a.v + seq_base;
 
@@ -485,6 +489,8 @@ hipError_t launch_bwd_typed(const BwdParams& p, WorkList wl, hipStream_t stream,
     a.ntgt = p.num_targets;
     a.num_seqs = p.num_seqs;
     a.heads = p.heads;
+    a.row_stride = p.dense ? p.d : (int64_t)p.heads * p.d;
+    a.head_stride = p.dense ? p.dense_len * p.d : p.d;
     a.alpha = p.alpha;
     a.dv_scale = 1.0f / p.n;
     a.g_scale = p.alpha / p.n;
@@ -539,6 +545,8 @@ struct BwdArgsF32 {
     const int32_t* offsets;
     const int32_t* ntgt;
     WorkList wl;
+    int64_t row_stride;
+    int64_t head_stride;
     int num_seqs;
     int heads;
     float alpha;
@@ -593,7 +601,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_f32(BwdArgsF32 a) {
     const int wv = threadIdx.x >> 6;
     const int g = lane >> 5, l32 = lane & 31;
     const int H = a.heads;
-    const int64_t row_stride = (int64_t)H * D;
+    const int64_t row_stride = a.row_stride;
 
     Tables tb;
     if constexpr (FUSED)
@@ -616,7 +624,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_f32(BwdArgsF32 a) {
         const int q_end = (TGT && k0i >= hist) ? min(s, k0i + C::ROWS) : s;
         const int j0 = k0i / 32;
         const int nblk = (q_end + 31) / 32 - j0;
-        const int64_t seq_base = (int64_t)start * row_stride + (int64_t)it.head * D;
+        const int64_t seq_base = (int64_t)start * H * D + (int64_t)it.head * a.head_stride;
         const int key = kw0 + l32;
         // B operands: K and V of the lane's key, head-dim element 2 ks + g.
         float kop[D / 2], vop[D / 2];
@@ -700,7 +708,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f32(BwdArgsF32 a) {
     const int wv = threadIdx.x >> 6;
     const int g = lane >> 5, l32 = lane & 31;
     const int H = a.heads;
-    const int64_t row_stride = (int64_t)H * D;
+    const int64_t row_stride = a.row_stride;
 
     Tables tb;
     if constexpr (FUSED)
@@ -723,7 +731,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f32(BwdArgsF32 a) {
         const int nh = TGT ? (hist + 31) / 32 : nb_all;
         const int jump = TGT ? max(q0 / 32 - nh, 0) : 0;
         const int nblk = nb_all - jump;
-        const int64_t seq_base = (int64_t)start * row_stride + (int64_t)it.head * D;
+        const int64_t seq_base = (int64_t)start * H * D + (int64_t)it.head * a.head_stride;
         const int row = wr0 + l32;
         float qop[D / 2], oop[D / 2];
 #pragma unroll
@@ -796,6 +804,8 @@ hipError_t launch_bwd_f32_typed(const BwdParams& p, WorkList wl, hipStream_t str
     a.ntgt = p.num_targets;
     a.num_seqs = p.num_seqs;
     a.heads = p.heads;
+    a.row_stride = p.dense ? p.d : (int64_t)p.heads * p.d;
+    a.head_stride = p.dense ? p.dense_len * p.d : p.d;
     a.alpha = p.alpha;
     a.dv_scale = 1.0f / p.n;
     a.g_scale = p.alpha / p.n;

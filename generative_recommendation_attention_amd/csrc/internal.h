@@ -203,6 +203,8 @@ struct BwdParams {
     void* dv;
     const int32_t* offsets;
     const int32_t* num_targets;   // candidates per sequence, or null (plain causal)
+    bool dense = false;           // dense (B, heads, S, D) layout, S = dense_len
+    int64_t dense_len = 0;
     int num_seqs;
     int heads;
     int d;

@@ -227,6 +227,14 @@ hstu_status_t hstu_attn_bwd_targets(const void* q, const void* k, const void* v,
                                     int32_t d, float alpha, float n, void* dq, void* dk,
                                     void* dv, hipStream_t stream, hstu_dtype_t dtype);
 
+/* The backward on the dense (batch, heads, seq_len, d) layout of
+ * hstu_attn_fwd_dense (causal mask over all seq_len positions); q, k, v, dout,
+ * dq, dk, dv all have that layout.  Other conventions as in hstu_attn_bwd. */
+hstu_status_t hstu_attn_bwd_dense(const void* q, const void* k, const void* v, const void* dout,
+                                  int32_t batch, int32_t heads, int32_t seq_len, int32_t d,
+                                  float alpha, float n, void* dq, void* dk, void* dv,
+                                  hipStream_t stream, hstu_dtype_t dtype);
+
 /* Checks device offsets synchronously: off[0] == 0 and non-decreasing.  Writes
  * T = off[num_seqs] to *total (may be NULL).  Returns HSTU_OK or
  * HSTU_ERR_BAD_OFFSETS; synchronises `stream`. */

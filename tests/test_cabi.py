@@ -233,6 +233,18 @@ def test_layer_out_argument_checks(lib, kw, status):
                                    None, a["dtype"]) == status
 
 
+@pytest.mark.parametrize("args,status", [
+    ((None, 16, 16, 48, 2, 1, 8, 64, 0.1, 1.0, 64, 80, 96), hstu.HSTU_ERR_INVALID_ARG),
+    ((16, 16, 16, None, 2, 1, 8, 64, 0.1, 1.0, 64, 80, 96), hstu.HSTU_ERR_INVALID_ARG),
+    ((16, 16, 16, 48, 2, 1, 8, 64, 0.1, 1.0, 48, 80, 96), hstu.HSTU_ERR_INVALID_ARG),  # dq = dout
+    ((16, 16, 16, 48, -1, 1, 8, 64, 0.1, 1.0, 64, 80, 96), hstu.HSTU_ERR_INVALID_ARG),
+    ((16, 16, 16, 48, 2, 1, 8, 96, 0.1, 1.0, 64, 80, 96), hstu.HSTU_ERR_UNSUPPORTED),
+    ((None, None, None, None, 0, 1, 8, 64, 0.1, 1.0, None, None, None), hstu.HSTU_OK),
+])
+def test_dense_bwd_argument_checks(lib, args, status):
+    assert lib.hstu_attn_bwd_dense(*args, None, hstu.HSTU_BF16) == status
+
+
 def test_status_strings(lib):
     for st in (0, -1, -2, -3, -4, -5):
         assert lib.hstu_status_string(st)

@@ -100,3 +100,21 @@ def test_dense_blog_shape_sampled_rows():
                       tok, hs.astype(np.int32))
     mr, l2 = assert_close(got, ref, "bf16", "dense blog shape")
     log(f"  max|err|/max|ref| = {mr:.3e}, rel L2 = {l2:.3e}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_dense_backward_full_compare(dtype, d):
+    B, H, S = 3, 2, 200
+    case, dense = dense_case(B, H, S, d, dtype, seed=850 + d)
+    dout_j = workloads.make_case([S] * B, H, d, dtype, seed=851,
+                                 sigma=0.5 if dtype == "fp16" else 1.0).q
+    dout = np.ascontiguousarray(dout_j.reshape(B, S, H, d).transpose(0, 2, 1, 3))
+    q, k, v, do = (to_torch(x, dtype) for x in (*dense, dout))
+    grads = hstu.hstu_attn_bwd_dense(q, k, v, do, case.alpha, case.n)
+    torch.cuda.synchronize()
+    ref = oracle.bwd(case.q, case.k, case.v, dout_j, case.offsets, H, d, case.alpha, case.n,
+                     dtype)
+    for name, g, r in zip(("dq", "dk", "dv"), grads, ref):
+        got = to_jagged(from_torch(g, dtype), B, H, S, d)
+        assert_close(got, r, dtype, f"dense backward {name} {dtype} d{d}")
