@@ -53,11 +53,11 @@ METRIC_CACHED = "HSTU cached-history attn fwd useful TFLOP/s (M-FALCON micro-bat
 # source the bench reports traffic as null.
 TRAFFIC = {
     "kernel_source": "generative_recommendation_attention_amd/csrc/attn_fwd.hip",
-    "kernel_sha256": "1957238a0b42a93d6da9c811f5ea9852fa5a6963f0741d230bb5feede9d317a2",
+    "kernel_sha256": "b0841190025ee82bf0f9859c2539c086b824cfd6444bc509324ac4d66fdb58cb",
     "fetch_scale": 2.0,
     "write_scale": 1.0,
-    "fetch_kib": {2: 93854.9},
-    "write_kib": {2: 37939.5},
+    "fetch_kib": {2: 94116.3},
+    "write_kib": {2: 37939.1},
 }
 
 
