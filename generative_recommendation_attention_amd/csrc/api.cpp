@@ -28,8 +28,8 @@ hstu_status_t hip_fail(hipError_t e) {
 struct Scratch {
     void* ptr = nullptr;
     size_t bytes = 0;
-    unsigned epoch = 0;   // calls completed on this area; call e uses counter set e % 2
-    bool clean = false;   // counter set epoch % 2 is known to be zero
+    unsigned epoch = 0;   // counter sets consumed on this area; a call starts at set epoch % NSETS
+    bool clean = false;   // sets epoch and epoch + 1 (mod NSETS) are known to be zero
     // Offsets i * len of the dense layout, written at ramp_at by an earlier
     // call on this area (ramp_count = 0: none).
     size_t ramp_at = 0;
@@ -250,7 +250,7 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
     bool clean;
     {
         std::lock_guard<std::mutex> lock(g_scratch_mu);
-        wl.set = (int)(sc->epoch & 1u);
+        wl.set = (int)(sc->epoch % hstu::NSETS);
         clean = sc->clean;
         sc->clean = false;   // until this call's launches succeed
     }
@@ -290,7 +290,7 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
                                timed ? tc.e[3] : nullptr);
     if (e != hipSuccess) return hip_fail(e);
     {
-        // The attention launch clears the other counter set for the next call.
+        // The attention launch used one counter set and cleared the next two.
         std::lock_guard<std::mutex> lock(g_scratch_mu);
         sc->epoch++;
         sc->clean = true;
@@ -307,7 +307,7 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
 }
 
 // One backward call: the dK/dV kernel, then the dQ kernel, on one work list
-// of BWD_TILE_ROWS-row items (each launch takes one of the two counter sets).
+// of BWD_TILE_ROWS-row items (a counter set per kernel).
 // dense_len > 0: the dense (B, heads, S, d) layout with S = dense_len, no offsets.
 hstu_status_t attn_bwd_call(const void* q, const void* k, const void* v, const void* dout,
                             const int32_t* seq_offsets, const int32_t* num_targets,
@@ -347,7 +347,7 @@ hstu_status_t attn_bwd_call(const void* q, const void* k, const void* v, const v
     bool clean;
     {
         std::lock_guard<std::mutex> lock(g_scratch_mu);
-        wl.set = (int)(sc->epoch & 1u);
+        wl.set = (int)(sc->epoch % hstu::NSETS);
         clean = sc->clean;
         sc->clean = false;
     }
@@ -386,8 +386,7 @@ hstu_status_t attn_bwd_call(const void* q, const void* k, const void* v, const v
                               timed ? tc.e[3] : nullptr);
     if (e != hipSuccess) return hip_fail(e);
     {
-        // Two launches: this call's set, then the other; the second cleared
-        // this call's set, which the next call takes again.
+        // Two launches, two counter sets; between them they cleared the next two.
         std::lock_guard<std::mutex> lock(g_scratch_mu);
         sc->epoch += 2;
         sc->clean = true;

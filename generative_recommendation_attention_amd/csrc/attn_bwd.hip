@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv(BwdArgs a) {
                                 a.wl.ctl);
     else
         tb = global_tables(a.wl);
-    clear_next_set(a.wl.ctl, a.wl.set);
+    clear_sets(a.wl.ctl, a.wl.set + 2, 1);   // (the next call's sets: see the launcher)
     ItemSource src(a.wl.ctl, a.wl.set);
     int qx, w;
     while (src.next(tb, s_item, &qx, &w)) {
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdArgs a) {
                                 a.wl.ctl);
     else
         tb = global_tables(a.wl);
-    clear_next_set(a.wl.ctl, a.wl.set);
+    clear_sets(a.wl.ctl, a.wl.set + 2, 1);   // (the next call's sets: see the launcher)
     ItemSource src(a.wl.ctl, a.wl.set);
     int qx, w;
     while (src.next(tb, s_item, &qx, &w)) {
@@ -502,8 +502,8 @@ hipError_t launch_bwd_typed(const BwdParams& p, WorkList wl, hipStream_t stream,
     int& g_dq = grids[wl.fused ? 1 : 0][1];
     if (!g_dkv) g_dkv = resident_grid(f_dkv, 256);
     if (!g_dq) g_dq = resident_grid(f_dq, 256);
-    // dK/dV on this call's counter set, then dQ on the other one (each launch
-    // clears the set the one after it uses).
+    // dK/dV on this call's first counter set, dQ on the next; each launch
+    // clears the set two after its own, so the two clear the next call's pair.
     a.wl = wl;
     if (start)
         hipExtLaunchKernelGGL(f_dkv, dim3(g_dkv), dim3(256), 0, stream, start, nullptr, 0, a);
@@ -511,7 +511,7 @@ hipError_t launch_bwd_typed(const BwdParams& p, WorkList wl, hipStream_t stream,
         hipLaunchKernelGGL(f_dkv, dim3(g_dkv), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    a.wl.set = wl.set ^ 1;
+    a.wl.set = (wl.set + 1) % NSETS;
     if (stop)
         hipExtLaunchKernelGGL(f_dq, dim3(g_dq), dim3(256), 0, stream, nullptr, stop, 0, a);
     else
@@ -608,7 +608,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_f32(BwdArgsF32 a) {
         tb = build_local_tables(lt, tbl_scratch, a.offsets, a.num_seqs, H, C::ROWS, a.wl.ctl);
     else
         tb = global_tables(a.wl);
-    clear_next_set(a.wl.ctl, a.wl.set);
+    clear_sets(a.wl.ctl, a.wl.set + 2, 1);   // (the next call's sets: see the launcher)
     ItemSource src(a.wl.ctl, a.wl.set);
     int qx, w;
     while (src.next(tb, s_item, &qx, &w)) {
@@ -715,7 +715,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f32(BwdArgsF32 a) {
         tb = build_local_tables(lt, tbl_scratch, a.offsets, a.num_seqs, H, C::ROWS, a.wl.ctl);
     else
         tb = global_tables(a.wl);
-    clear_next_set(a.wl.ctl, a.wl.set);
+    clear_sets(a.wl.ctl, a.wl.set + 2, 1);   // (the next call's sets: see the launcher)
     ItemSource src(a.wl.ctl, a.wl.set);
     int qx, w;
     while (src.next(tb, s_item, &qx, &w)) {
@@ -824,7 +824,7 @@ hipError_t launch_bwd_f32_typed(const BwdParams& p, WorkList wl, hipStream_t str
         hipLaunchKernelGGL(f_dkv, dim3(g_dkv), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    a.wl.set = wl.set ^ 1;
+    a.wl.set = (wl.set + 1) % NSETS;
     if (stop)
         hipExtLaunchKernelGGL(f_dq, dim3(g_dq), dim3(256), 0, stream, nullptr, stop, 0, a);
     else

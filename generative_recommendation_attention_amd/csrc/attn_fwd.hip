@@ -198,7 +198,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
                                 a.wl.ctl);
     else
         tb = global_tables(a.wl);
-    clear_next_set(a.wl.ctl, a.wl.set);
+    clear_sets(a.wl.ctl, a.wl.set + 1, 2);
     ItemSource src(a.wl.ctl, a.wl.set);
     int qx, w;
     while (src.next(tb, s_item, &qx, &w)) {
@@ -616,7 +616,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
                                 a.wl.ctl);
     else
         tb = global_tables(a.wl);
-    clear_next_set(a.wl.ctl, a.wl.set);
+    clear_sets(a.wl.ctl, a.wl.set + 1, 2);
     ItemSource src(a.wl.ctl, a.wl.set);
     int qx, w;
     while (src.next(tb, s_item, &qx, &w)) {

@@ -12,12 +12,16 @@ namespace hstu {
 // on, so the items sharing one sequence's keys and values run under one L2).
 constexpr int NQ = 8;
 constexpr int CTL_LINE = 32;  // ints per queue counter: one 128-byte line each
+// Queue counter sets.  A call takes one (forward) or two (backward: one per
+// pass) consecutive sets, and clears the two after them, so whichever call
+// comes next finds its sets at zero.
+constexpr int NSETS = 4;
 
 // Words at the start of the scratch area (int32).
 enum : int {
     CTL_NEXT = 0,                 // NEXT + CTL_LINE*(NQ*set + x): next item of queue x for
-                                  // the calls of counter set `set` (0, 1; device atomic)
-    CTL_TOTAL = 2 * NQ * CTL_LINE,  // TOTAL + x: items in queue x
+                                  // counter set `set` (0 .. NSETS-1; device atomic)
+    CTL_TOTAL = NSETS * NQ * CTL_LINE,  // TOTAL + x: items in queue x
     CTL_FLAGS = CTL_TOTAL + NQ,   // bit 0: off[0] != 0, bit 1: a decreasing offset,
                                   // bit 2: item count overflow
     CTL_MODE = CTL_FLAGS + 1,     // QUEUE_BANDS or QUEUE_PAIRS
@@ -30,9 +34,8 @@ static_assert(CTL_MODE < CTL_WORDS, "control block layout");
 // its start (the tables are a few KB; building them costs less than a second
 // kernel launch).  Up to FUSE_SEQS sequences and FUSE_PAIRS (sequence, head)
 // pairs.  Either way the queue counters are zero when a launch starts: calls
-// on one work list alternate between two counter sets, and each attention
-// launch clears the set the next call will use (the work-list kernel clears
-// both).
+// on one work list rotate through NSETS counter sets, and each launch clears
+// the sets the next call will use (the work-list kernel clears all).
 constexpr int FUSE_SEQS = 256;
 constexpr int FUSE_PAIRS = 2048;
 constexpr int FUSE_QLEN = FUSE_PAIRS / NQ;
@@ -64,7 +67,7 @@ struct WorkList {
     int* qprefix;  // [NQ * (qlen + 1)] first item of each band of a queue, then the total
     int qlen;      // max pairs per queue = ceil(num_seqs * heads / NQ)
     int fused;     // 1: the attention kernel builds the tables in LDS (FUSE_* limits)
-    int set;       // counter set of this call (0 or 1)
+    int set;       // first counter set of this call (0 .. NSETS-1)
 };
 
 // The tables item decoding reads: the work list in global memory, or the
@@ -212,9 +215,9 @@ struct BwdParams {
     float n;
 };
 
-// Enqueues the dK/dV kernel (on counter set wl.set) and then the dQ kernel
-// (on the other set).  `start` / `stop`, when given, are recorded on the
-// first and second dispatch.
+// Enqueues the dK/dV kernel (counter set wl.set) and then the dQ kernel (the
+// next set); each clears one of the two sets after those.  `start` / `stop`,
+// when given, are recorded on the first and second dispatch.
 hipError_t launch_backward(const BwdParams& p, Dtype dt, WorkList wl, hipStream_t stream,
                            hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 

@@ -247,13 +247,16 @@ struct ItemSource {
     }
 };
 
-// Clears the counter set the next call on this work list will use (the other
-// set).  Called by every thread; workgroup 0's first NQ threads do it.  No
-// workgroup of this launch touches that set.
-__device__ inline void clear_next_set(int* ctl, int set) {
-    if (blockIdx.x == 0 && threadIdx.x < NQ)
-        __hip_atomic_store(ctl + CTL_NEXT + CTL_LINE * (NQ * (1 - set) + threadIdx.x), 0,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Clears counter sets first .. first + count - 1 (mod NSETS): the sets the
+// next call on this work list will use, none of which this launch touches.
+// Called by every thread; workgroup 0's first NQ * count threads do it.
+__device__ inline void clear_sets(int* ctl, int first, int count) {
+    const int t = threadIdx.x;
+    if (blockIdx.x == 0 && t < NQ * count) {
+        const int set = (first + t / NQ) % NSETS;
+        __hip_atomic_store(ctl + CTL_NEXT + CTL_LINE * (NQ * set + t % NQ), 0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 }  // namespace hstu

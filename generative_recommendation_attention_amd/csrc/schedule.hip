@@ -224,8 +224,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
         const int pos = (full & 1) ? NQ - 1 - tid : tid;
         const int n = full + (pos < rem ? 1 : 0);
         wl.qprefix[tid * row + n] = (int)total;
-        wl.ctl[CTL_NEXT + CTL_LINE * tid] = 0;
-        wl.ctl[CTL_NEXT + CTL_LINE * (NQ + tid)] = 0;
+        for (int set = 0; set < NSETS; ++set) wl.ctl[CTL_NEXT + CTL_LINE * (NQ * set + tid)] = 0;
         wl.ctl[CTL_TOTAL + tid] = (int)total;
     }
     if (flags) atomicOr(&sh.flags, flags);
