@@ -10,6 +10,16 @@ call raises.
 
 q, k, v: (T, heads, d) CUDA tensors (bfloat16, float16 or float32), contiguous;
 seq_offsets: int32 CUDA tensor [num_seqs + 1] of prefix sums.
+
+Also: hstu_attn_fwd_{bf16,fp16,fp32} (type fixed), hstu_attn_fwd_targets
+(target-aware mask), hstu_attn_fwd_cached (candidates against a cached
+history), hstu_attn_fwd_dense / hstu_attn_bwd_dense ((B, heads, S, d)
+tensors), hstu_attn_bwd (dq, dk, dv), hstu_layer_in_proj /
+hstu_layer_out_proj (the layer's projections), and the utilities
+hstu_validate_offsets, hstu_release_workspace, hstu_profile_enable/read.
+The offsets live on the device and are not read by the host: keeping them
+consistent with the tensors' lengths is the caller's part (see
+hstu_validate_offsets).
 """
 from __future__ import annotations
 
@@ -234,9 +244,7 @@ def _typed(name: str, code: int):
     def fn(q, k, v, seq_offsets, alpha: float, n: float, out=None, stream=None):
         if _dtype_code(q) != code:
             raise TypeError(f"{name} takes {['bfloat16', 'float16', 'float32'][code]} tensors")
-        if out is None:
-            import torch
-            out = torch.empty_like(q)
+        out = _check_tensors(q, k, v, seq_offsets, out)
         T, heads, d = q.shape
         lib = load_library()
         st = getattr(lib, name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), seq_offsets.data_ptr(),

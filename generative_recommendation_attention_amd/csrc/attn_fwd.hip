@@ -2,6 +2,9 @@
 //
 //   out[r] = (1/n) * sum_{c <= r} silu(alpha <q_r, k_c>) v_c      (per sequence, head)
 //
+// (also the target-aware and cached-history masks of M-FALCON, and the dense
+// (B, heads, S, d) layout: see MASK_* and the strides in KernelArgs)
+//
 // Ascend HSTU blog ("都是生成式推荐，为什么昇腾这么快？"): §1 gives the formula
 // and its five unfused steps; §2.1-§2.2 fuse them so the (s x s) score matrix
 // stays on chip, block by block, and the (block x d) result is accumulated;
@@ -14,8 +17,8 @@
 // Persistent workgroups pull items (sequence, head, Q tile) from the work list
 // built by schedule.hip.  Per item, each wave owns 32 or 64 query rows and
 // walks the key/value tiles 0..(last tile that reaches its rows), staged
-// through LDS and double buffered: while tile c is consumed, tile c+1 is in
-// flight from HBM.
+// through LDS: while tile c is consumed, tiles c+1 and c+2 are in flight from
+// HBM.
 //
 // Transposed products.  With v_mfma_f32_32x32x16_{bf16,f16} a lane's C/D
 // registers hold one column and 16 rows of a 32x32 block:
