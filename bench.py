@@ -53,11 +53,11 @@ METRIC_CACHED = "HSTU cached-history attn fwd useful TFLOP/s (M-FALCON micro-bat
 # source the bench reports traffic as null.
 TRAFFIC = {
     "kernel_source": "generative_recommendation_attention_amd/csrc/attn_fwd.hip",
-    "kernel_sha256": "b0841190025ee82bf0f9859c2539c086b824cfd6444bc509324ac4d66fdb58cb",
+    "kernel_sha256": "f9edb4e830faf7360735429ceeacbbac8f6315327b854bac06a1d201e5c3a00f",
     "fetch_scale": 2.0,
     "write_scale": 1.0,
-    "fetch_kib": {2: 94116.3},
-    "write_kib": {2: 37939.1},
+    "fetch_kib": {2: 94200.0},
+    "write_kib": {2: 37940.7},
 }
 
 
