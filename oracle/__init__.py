@@ -31,6 +31,12 @@ derivative of the forward definition, per kept (row, key) pair, for an
 upstream gradient dout (the pages only say that the backward recomputes the
 attention instead of storing it, HSTU paper translation Appendix G).
 
+``fwd_rab`` / ``rows_rab`` add the relative attention bias rab_{p,t} (HSTU
+paper translation §3 and Appendix G) to the scaled score before SiLU, under
+the causal mask: rab(r, c) = wpos[r - c] (0 from npos on) +
+wtime[min(floor(log2(ts_r - ts_c + 1)), ntime - 1)] (a negative gap in the
+last bucket), the tables shared by all heads.
+
 ``layer_in`` / ``layer_out`` are the layer's surroundings (HSTU paper
 translation §3, §3.3): [u | v | q | k] = silu(W1 x + b1) per token, and
 y = x + W2 (LN(a) * u) + b2 with LN over heads * d.
@@ -111,6 +117,14 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hstu_oracle_layer_out.argtypes = [vp, vp, vp, vp, vp, f64, vp, vp, ctypes.c_int, i64,
                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     lib.hstu_oracle_layer_out.restype = ctypes.c_int
+    lib.hstu_oracle_fwd_rab.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, ctypes.c_int, vp,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        f64, f64, vp]
+    lib.hstu_oracle_fwd_rab.restype = ctypes.c_int
+    lib.hstu_oracle_rows_rab.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, ctypes.c_int, vp,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         f64, f64, vp, vp, i64, vp]
+    lib.hstu_oracle_rows_rab.restype = ctypes.c_int
     lib.hstu_oracle_threads.argtypes = []
     lib.hstu_oracle_threads.restype = ctypes.c_int
     _libs[path] = lib
@@ -250,6 +264,61 @@ def bwd(q, k, v, dout, offsets, heads: int, d: int, alpha: float, n: float, dtyp
     if rc != 0:
         raise ValueError("oracle rejected the arguments (malformed offsets or sizes)")
     return dq, dk, dv
+
+
+def _rab_args(q, k, v, offsets, timestamps, pos_bias, time_bias, heads, d, dtype):
+    q, k, v = (_storage(a, dtype) for a in (q, k, v))
+    off = np.ascontiguousarray(offsets, dtype=np.int32)
+    T = int(off[-1]) if len(off) else 0
+    ts = np.ascontiguousarray(timestamps, dtype=np.int32)
+    wp = np.ascontiguousarray(pos_bias, dtype=np.float64)
+    wt = np.ascontiguousarray(time_bias, dtype=np.float64)
+    for a in (q, k, v):
+        if a.size < T * heads * d:
+            raise ValueError("q/k/v smaller than offsets imply")
+    if ts.shape != (T,):
+        raise ValueError("one timestamp per token")
+    if wp.ndim != 1 or wt.ndim != 1:
+        raise ValueError("bias tables are 1-D")
+    return q, k, v, off, ts, wp, wt
+
+
+def fwd_rab(q, k, v, offsets, timestamps, pos_bias, time_bias, heads: int, d: int,
+            alpha: float, n: float, dtype: str, lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+    """Full fp64 output (T, heads, d) of the causal forward with the relative
+    attention bias; pos_bias / time_bias are given as the float32 values the
+    GPU call gets (widened exactly)."""
+    lib = lib or load()
+    q, k, v, off, ts, wp, wt = _rab_args(q, k, v, offsets, timestamps, pos_bias, time_bias,
+                                         heads, d, dtype)
+    out = np.zeros((int(off[-1]) if len(off) else 0, heads, d), dtype=np.float64)
+    rc = lib.hstu_oracle_fwd_rab(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[dtype], _ptr(off),
+                                 _ptr(ts), _ptr(wp), len(wp), _ptr(wt), len(wt), len(off) - 1,
+                                 heads, d, float(alpha), float(n), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments (malformed offsets or sizes)")
+    return out
+
+
+def rows_rab(q, k, v, offsets, timestamps, pos_bias, time_bias, heads: int, d: int,
+             alpha: float, n: float, dtype: str, tokens, head_ids,
+             lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+    """fp64 outputs (m, d) at global tokens[m], heads head_ids[m], of the same."""
+    lib = lib or load()
+    q, k, v, off, ts, wp, wt = _rab_args(q, k, v, offsets, timestamps, pos_bias, time_bias,
+                                         heads, d, dtype)
+    tok = np.ascontiguousarray(tokens, dtype=np.int64)
+    hd = np.ascontiguousarray(head_ids, dtype=np.int32)
+    if tok.shape != hd.shape:
+        raise ValueError("tokens and head_ids differ in length")
+    out = np.zeros((len(tok), d), dtype=np.float64)
+    rc = lib.hstu_oracle_rows_rab(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[dtype], _ptr(off),
+                                  _ptr(ts), _ptr(wp), len(wp), _ptr(wt), len(wt), len(off) - 1,
+                                  heads, d, float(alpha), float(n), _ptr(tok), _ptr(hd),
+                                  len(tok), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle rejected the sampled rows")
+    return out
 
 
 BWD_KIND = {"dq": 0, "dk": 1, "dv": 2}

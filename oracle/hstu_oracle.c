@@ -63,6 +63,16 @@
  * Readings: the split order U, V, Q, K and each part's (heads, d) layout; no
  * dropout (inference); the residual adds x.
  *
+ * Relative attention bias (the *_rab entry points): HSTU paper translation,
+ * §3 (the spatial aggregation adds rab_{p,t}, a relative attention bias that
+ * merges position p and time t, before phi_2 = SiLU; the equation itself is
+ * lost from the page) and Appendix G (the bias is built from its parameters
+ * inside the attention operator rather than read as a tensor).  Reading: per
+ * (row r, key c <= r) of a sequence with token timestamps ts,
+ *   rab(r, c) = wpos[r - c] + wtime[min(floor(log2(ts_r - ts_c + 1)), ntime - 1)]
+ * with wpos[j] = 0 for j >= npos and a negative gap in the last time bucket,
+ * added after alpha: out[r] = (1/n) sum_{c <= r} silu(alpha <q_r, k_c> + rab(r, c)) v_c.
+ *
  * Readings taken where the pages are silent (each listed in the design notes):
  *   - alpha multiplies the scores before SiLU; n is a caller-given scalar;
  *   - the mask multiplies after SiLU (0/1), so masked terms are exactly 0;
@@ -565,6 +575,128 @@ int hstu_oracle_rows_cached(const void* q, const void* k, const void* v, const v
             cached_row(q, k, v, kc, vc, dtype, tok[m], hoff[lo],
                        (int64_t)hoff[lo + 1] - hoff[lo], heads, d, hd[m], alpha, n, qrow,
                        out_rows + m * (int64_t)d);
+        }
+    }
+    return 0;
+}
+
+/* ---- relative attention bias ----------------------------------------------- */
+
+/* Time bucket of the gap between a query token's timestamp and a key token's:
+ * floor(log2(gap + 1)) for gap >= 0, at most ntime - 1; a negative gap (a key
+ * later than the query) falls in the last bucket.  Integer arithmetic only. */
+static int time_bucket(int64_t gap, int ntime) {
+    if (gap < 0) return ntime - 1;
+    int b = 0;
+#if ORACLE_PLANT == 20
+    while (b < 62 && (gap >> (b + 1)) != 0) ++b; /* planted: log2(gap), not log2(gap + 1) */
+#else
+    while (b < 62 && ((gap + 1) >> (b + 1)) != 0) ++b;
+#endif
+    return b < ntime - 1 ? b : ntime - 1;
+}
+
+/* rab(r, c) for local query row r and key c <= r of one sequence whose token
+ * timestamps are ts[0..s): a position term, wpos[r - c] (zero for distances
+ * of npos and beyond), plus a time term, wtime[bucket(ts[r] - ts[c])]. */
+static double rab_value(int64_t r, int64_t c, const int32_t* ts, const double* wpos, int npos,
+                        const double* wtime, int ntime) {
+    int64_t dist = r - c;
+#if ORACLE_PLANT == 19
+    dist = dist + 1; /* planted: relative position off by one */
+#endif
+    double p = dist < npos ? wpos[dist] : 0.0;
+    return p + wtime[time_bucket((int64_t)ts[r] - (int64_t)ts[c], ntime)];
+}
+
+/* One output row under the causal mask with the relative attention bias added
+ * to the scaled score before SiLU:
+ *   out[r] = (1/n) sum_{c <= r} silu(alpha <q_r, k_c> + rab(r, c)) v_c
+ * ts points at the sequence's first token's timestamp. */
+static void rab_row(const void* q, const void* k, const void* v, int dtype, int64_t s0,
+                    int64_t r, const int32_t* ts, const double* wpos, int npos,
+                    const double* wtime, int ntime, int heads, int d, int h, double alpha,
+                    double n, double* qrow, double* acc) {
+    const int64_t row_stride = (int64_t)heads * d;
+    for (int e = 0; e < d; ++e) {
+        qrow[e] = load_elem(q, dtype, (s0 + r) * row_stride + (int64_t)h * d + e);
+        acc[e] = 0.0;
+    }
+    for (int64_t c = 0; c <= r; ++c) {
+        const int64_t krow = s0 + c;
+        double dot = 0.0;
+        for (int e = 0; e < d; ++e)
+            dot += qrow[e] * load_elem(k, dtype, krow * row_stride + (int64_t)h * d + e);
+        const double bias = rab_value(r, c, ts, wpos, npos, wtime, ntime);
+#if ORACLE_PLANT == 18
+        const double w = silu(alpha * (dot + bias)); /* planted: bias scaled by alpha */
+#elif ORACLE_PLANT == 21
+        const double w = silu(alpha * dot) + bias; /* planted: bias added after SiLU */
+#else
+        const double w = silu(alpha * dot + bias);
+#endif
+        for (int e = 0; e < d; ++e)
+            acc[e] += w * load_elem(v, dtype, krow * row_stride + (int64_t)h * d + e);
+    }
+    for (int e = 0; e < d; ++e) acc[e] /= n;
+}
+
+/* Causal forward with the relative attention bias.  ts: int32 timestamp of
+ * every token (T entries, the jagged layout of q); wpos[npos], wtime[ntime]:
+ * the bias tables, shared by all heads (fp64 images of the values the GPU
+ * call gets).  out is fp64 (T, heads, d).  Returns 0, or -1 on malformed
+ * offsets or sizes (npos >= 1, 1 <= ntime <= 32, d <= 1024). */
+int hstu_oracle_fwd_rab(const void* q, const void* k, const void* v, int dtype,
+                        const int32_t* off, const int32_t* ts, const double* wpos, int npos,
+                        const double* wtime, int ntime, int num_seqs, int heads, int d,
+                        double alpha, double n, double* out) {
+    if (num_seqs < 0 || heads < 1 || d < 1 || d > 1024) return -1;
+    if (npos < 1 || ntime < 1 || ntime > 32 || !offsets_ok(off, num_seqs)) return -1;
+    const int64_t row_stride = (int64_t)heads * d;
+    const int64_t items = (int64_t)num_seqs * heads;
+#pragma omp parallel
+    {
+        double qrow[1024], acc[1024];
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t it = 0; it < items; ++it) {
+            int i = (int)(it / heads), h = (int)(it % heads);
+            int64_t s0 = off[i], len = (int64_t)off[i + 1] - off[i];
+            for (int64_t r = 0; r < len; ++r) {
+                rab_row(q, k, v, dtype, s0, r, ts + s0, wpos, npos, wtime, ntime, heads, d, h,
+                        alpha, n, qrow, acc);
+                double* o = out + (s0 + r) * row_stride + (int64_t)h * d;
+                for (int e = 0; e < d; ++e) o[e] = acc[e];
+            }
+        }
+    }
+    return 0;
+}
+
+/* Sampled rows of the same: out_rows[m, 0..d) at global token tok[m], head
+ * hd[m].  Returns 0, or -1 on a token or head out of range. */
+int hstu_oracle_rows_rab(const void* q, const void* k, const void* v, int dtype,
+                         const int32_t* off, const int32_t* ts, const double* wpos, int npos,
+                         const double* wtime, int ntime, int num_seqs, int heads, int d,
+                         double alpha, double n, const int64_t* tok, const int32_t* hd,
+                         int64_t count, double* out_rows) {
+    if (num_seqs < 1 || heads < 1 || d < 1 || d > 1024) return -1;
+    if (npos < 1 || ntime < 1 || ntime > 32 || !offsets_ok(off, num_seqs)) return -1;
+    int64_t T = off[num_seqs];
+    for (int64_t m = 0; m < count; ++m)
+        if (tok[m] < 0 || tok[m] >= T || hd[m] < 0 || hd[m] >= heads) return -1;
+#pragma omp parallel
+    {
+        double qrow[1024];
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t m = 0; m < count; ++m) {
+            int lo = 0, hi = num_seqs - 1;   /* largest i with off[i] <= tok */
+            while (lo < hi) {
+                int mid = (lo + hi + 1) / 2;
+                if (off[mid] <= tok[m]) lo = mid; else hi = mid - 1;
+            }
+            const int64_t s0 = off[lo];
+            rab_row(q, k, v, dtype, s0, tok[m] - s0, ts + s0, wpos, npos, wtime, ntime, heads, d,
+                    hd[m], alpha, n, qrow, out_rows + m * (int64_t)d);
         }
     }
     return 0;

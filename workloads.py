@@ -303,3 +303,54 @@ def cached_workload(history: int = 3072, candidates: int = 1024, users: int = 16
                          alpha=1.0 / 8.0, n=float(history + candidates))
     c.cand.description = CACHED_DESCRIPTION
     return c
+
+
+# ---------------------------------------------------------------------------
+# Relative attention bias inputs: token timestamps and the two bias tables.
+# ---------------------------------------------------------------------------
+
+RAB_DESCRIPTION = ("causal with relative attention bias, 16 x 4096, heads 4, d 64, bf16, "
+                   "4096 position entries, 16 time buckets")
+
+
+@dataclasses.dataclass
+class RabInputs:
+    """int32 timestamps, one per token, and float32 position / time tables."""
+
+    timestamps: np.ndarray  # int32 [T]
+    pos_bias: np.ndarray    # float32 [npos]
+    time_bias: np.ndarray   # float32 [ntime]
+
+
+def make_rab_inputs(offsets, npos: int, ntime: int, seed: int, sigma: float = 0.5,
+                    max_log_gap: int = 16) -> RabInputs:
+    """Per sequence, a start time drawn uniformly in [0, 2^30) and then gaps
+    floor(2^(u * max_log_gap)) - 1, u ~ U(0, 1), between consecutive tokens
+    (non-decreasing timestamps whose gaps spread over every log2 bucket up to
+    max_log_gap); tables i.i.d. N(0, sigma^2)."""
+    rng = np.random.default_rng(seed)
+    off = np.asarray(offsets, dtype=np.int64)
+    T = int(off[-1]) if len(off) else 0
+    ts = np.zeros(T, dtype=np.int64)
+    for i in range(len(off) - 1):
+        a, b = int(off[i]), int(off[i + 1])
+        if b == a:
+            continue
+        gaps = np.floor(np.exp2(rng.random(b - a - 1) * max_log_gap)).astype(np.int64) - 1
+        ts[a] = rng.integers(0, 1 << 30)
+        ts[a + 1:b] = ts[a] + np.cumsum(gaps)
+    if T and ts.max() >= (1 << 31) - 1:
+        raise ValueError("timestamps overflow int32; use shorter sequences or smaller gaps")
+    wpos = (rng.standard_normal(npos, dtype=np.float32) * np.float32(sigma)).astype(np.float32)
+    wtime = (rng.standard_normal(ntime, dtype=np.float32) * np.float32(sigma)).astype(np.float32)
+    return RabInputs(timestamps=ts.astype(np.int32), pos_bias=wpos, time_bias=wtime)
+
+
+def rab_workload(values: bool = True):
+    """The causal workload of 16 sequences of 4096 tokens (heads 4, d 64,
+    bf16) with a relative attention bias: a position entry per distance and
+    16 time buckets.  Seed 1300."""
+    case = make_case([4096] * 16, 4, 64, "bf16", seed=1300, alpha=1.0 / 8.0, n=4096.0,
+                     name="rab", description=RAB_DESCRIPTION) if values else None
+    offsets = case.offsets if case is not None else offsets_from_lengths([4096] * 16)
+    return case, make_rab_inputs(offsets, 4096, 16, seed=1301)
