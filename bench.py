@@ -21,7 +21,10 @@ hstu_attn_fwd_cached on 16 users x (3072 cached history rows, 1024 candidates)
 times hstu_attn_bwd (dq, dk, dv) on the 16 x 4096 workload: useful FLOPs are
 the five products of a recomputing backward, 10 * heads * d per kept pair
 (2.5x the forward's); the kernels run seven (S and dP are formed by both the
-dK/dV and the dQ kernel).
+dK/dV and the dQ kernel).  --rab times hstu_attn_fwd_rab (the relative
+attention bias, HSTU paper translation §3 and Appendix G) on the 16 x 4096
+workload with a position entry per distance and 16 time buckets; useful FLOPs
+are the plain forward's (the bias terms are not counted).
 """
 from __future__ import annotations
 
@@ -45,6 +48,7 @@ METRIC_TARGETS = "HSTU target-aware attn fwd useful TFLOP/s (M-FALCON mask)"
 METRIC_DENSE = "HSTU attn fwd useful TFLOP/s, dense (b, heads, s, d) layout"
 METRIC_BWD = "HSTU attn bwd (dq, dk, dv) useful TFLOP/s"
 METRIC_CACHED = "HSTU cached-history attn fwd useful TFLOP/s (M-FALCON micro-batch)"
+METRIC_RAB = "HSTU attn fwd with relative attention bias useful TFLOP/s"
 # HBM traffic per dispatch of the attention kernel, from two rocprofv3 --pmc
 # runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
 # same counter reads for a plain 1 GiB device copy (bench.py --copy-calibrate):
@@ -53,11 +57,11 @@ METRIC_CACHED = "HSTU cached-history attn fwd useful TFLOP/s (M-FALCON micro-bat
 # source the bench reports traffic as null.
 TRAFFIC = {
     "kernel_source": "generative_recommendation_attention_amd/csrc/attn_fwd.hip",
-    "kernel_sha256": "f9edb4e830faf7360735429ceeacbbac8f6315327b854bac06a1d201e5c3a00f",
+    "kernel_sha256": "52f7c417aa9a1671e541b5c7747445ce0a2b1fb58cc054aecb5769d3b559f90c",
     "fetch_scale": 2.0,
     "write_scale": 1.0,
-    "fetch_kib": {2: 94200.0},
-    "write_kib": {2: 37940.7},
+    "fetch_kib": {2: 93861.8},
+    "write_kib": {2: 37938.6},
 }
 
 
@@ -154,7 +158,7 @@ def cpu_baseline_bwd(case, dout, budget_s: float):
                       f"{threads} threads available"}
 
 
-def cpu_baseline(case, budget_s: float):
+def cpu_baseline(case, budget_s: float, rab=None):
     """Time the oracle on whole sequences of the workload (all heads).  Each
     oracle call takes enough sequences to give every OpenMP thread a
     (sequence, head) pair; calls continue in input order until about budget_s
@@ -172,8 +176,13 @@ def cpu_baseline(case, budget_s: float):
         sub = (off[i:j + 1] - off[i]).astype(np.int32)
         t0 = time.perf_counter()
         tg = None if case.num_targets is None else case.num_targets[i:j]
-        oracle.fwd(case.q[a:b], case.k[a:b], case.v[a:b], sub, case.heads, case.d, case.alpha,
-                   case.n, case.dtype, lib=lib, num_targets=tg)
+        if rab is not None:
+            oracle.fwd_rab(case.q[a:b], case.k[a:b], case.v[a:b], sub, rab.timestamps[a:b],
+                           rab.pos_bias, rab.time_bias, case.heads, case.d, case.alpha, case.n,
+                           case.dtype, lib=lib)
+        else:
+            oracle.fwd(case.q[a:b], case.k[a:b], case.v[a:b], sub, case.heads, case.d,
+                       case.alpha, case.n, case.dtype, lib=lib, num_targets=tg)
         done_s += time.perf_counter() - t0
         part = workloads.Case(name="", dtype=case.dtype, heads=case.heads, d=case.d,
                               offsets=sub, q=case.q[:0], k=case.k[:0], v=case.v[:0],
@@ -297,14 +306,18 @@ def main() -> int:
     ap.add_argument("--cached", action="store_true",
                     help="time the cached-history forward on 16 x (3072 cached rows, "
                          "1024 candidates)")
+    ap.add_argument("--rab", action="store_true",
+                    help="time the forward with the relative attention bias on 16 x 4096 "
+                         "(a position entry per distance, 16 time buckets)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="run only a plain 1 GiB device copy (3 times), the reference for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
-    if args.targets + args.cached + args.backward + args.dense + args.layer > 1:
-        ap.error("--targets, --cached, --backward, --dense and --layer are separate benchmarks")
+    if args.targets + args.cached + args.backward + args.dense + args.layer + args.rab > 1:
+        ap.error("--targets, --cached, --backward, --dense, --layer and --rab are separate "
+                 "benchmarks")
     if args.layer:
         return bench_layer(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -326,10 +339,12 @@ def main() -> int:
         print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
                           "copies": 3}), flush=True)
         return 0
-    cc = None
+    cc = rab = None
     if args.cached:
         cc = workloads.cached_workload()
         case = cc.cand
+    elif args.rab:
+        case, rab = workloads.rab_workload()
     elif args.targets:
         case = workloads.targets_workload()
     else:
@@ -351,6 +366,14 @@ def main() -> int:
 
         def call():
             hstu.hstu_attn_fwd_cached(q, k, v, off, kc, vc, hoff, case.alpha, case.n, out=out)
+    elif args.rab:
+        ts = torch.from_numpy(rab.timestamps).cuda()
+        wp = torch.from_numpy(rab.pos_bias).cuda()
+        wt = torch.from_numpy(rab.time_bias).cuda()
+        alg_bytes += 4.0 * case.total + 4.0 * (rab.pos_bias.size + rab.time_bias.size)
+
+        def call():
+            hstu.hstu_attn_fwd_rab(q, k, v, off, ts, wp, wt, case.alpha, case.n, out=out)
     elif args.targets:
         tg = torch.from_numpy(case.num_targets.astype(np.int32)).cuda()
 
@@ -408,7 +431,7 @@ def main() -> int:
     sched_ms = kt.sched_ms / max(1, kt.calls)
     achieved = flops / (attn_ms * 1e-3) / 1e12
     peak = PEAK_MFMA_TFLOPS[case.dtype]
-    traffic = (None if (args.targets or args.cached or args.backward or args.dense)
+    traffic = (None if (args.targets or args.cached or args.backward or args.dense or args.rab)
                else traffic_bytes(args.workload))
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
@@ -424,12 +447,13 @@ def main() -> int:
         elif args.backward:
             cpu = cpu_baseline_bwd(case, dout_host, args.cpu_budget)
         else:
-            cpu = cpu_baseline(case, args.cpu_budget)
+            cpu = cpu_baseline(case, args.cpu_budget, rab=rab)
 
     L = case.lengths
     line = {
         "metric": (METRIC_CACHED if args.cached else METRIC_TARGETS if args.targets else
-                   METRIC_BWD if args.backward else METRIC_DENSE if args.dense else METRIC),
+                   METRIC_BWD if args.backward else METRIC_DENSE if args.dense else
+                   METRIC_RAB if args.rab else METRIC),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -448,6 +472,8 @@ def main() -> int:
                    **({"candidates_per_seq": int(case.num_targets[0])} if args.targets else {}),
                    **({"cached_history_per_seq": int(cc.hist_lengths[0])} if args.cached else {}),
                    **({"layout": "(batch, heads, seq_len, d)"} if args.dense else {}),
+                   **({"rab_positions": int(rab.pos_bias.size),
+                       "rab_time_buckets": int(rab.time_bias.size)} if args.rab else {}),
                    "useful_gflop": round(flops / 1e9, 3)},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -12,9 +12,10 @@ q, k, v: (T, heads, d) CUDA tensors (bfloat16, float16 or float32), contiguous;
 seq_offsets: int32 CUDA tensor [num_seqs + 1] of prefix sums.
 
 Also: hstu_attn_fwd_{bf16,fp16,fp32} (type fixed), hstu_attn_fwd_targets
-(target-aware mask), hstu_attn_fwd_cached (candidates against a cached
-history), hstu_attn_fwd_dense / hstu_attn_bwd_dense ((B, heads, S, d)
-tensors), hstu_attn_bwd (dq, dk, dv), hstu_layer_in_proj /
+(target-aware mask), hstu_attn_fwd_rab (relative attention bias),
+hstu_attn_fwd_cached (candidates against a cached history),
+hstu_attn_fwd_dense / hstu_attn_bwd_dense ((B, heads, S, d) tensors),
+hstu_attn_bwd (dq, dk, dv), hstu_layer_in_proj /
 hstu_layer_out_proj (the layer's projections), and the utilities
 hstu_validate_offsets, hstu_release_workspace, hstu_profile_enable/read.
 The offsets live on the device and are not read by the host: keeping them
@@ -41,7 +42,8 @@ HSTU_BF16, HSTU_FP16, HSTU_FP32 = 0, 1, 2
 
 # Every symbol include/hstu.h declares.
 EXPORTS = ("hstu_attn_fwd", "hstu_attn_fwd_bf16", "hstu_attn_fwd_fp16", "hstu_attn_fwd_fp32",
-           "hstu_attn_fwd_targets", "hstu_attn_fwd_cached", "hstu_attn_fwd_dense", "hstu_attn_bwd",
+           "hstu_attn_fwd_targets", "hstu_attn_fwd_cached", "hstu_attn_fwd_dense",
+           "hstu_attn_fwd_rab", "hstu_attn_bwd",
            "hstu_attn_bwd_dense", "hstu_layer_in_proj", "hstu_layer_out_proj",
            "hstu_attn_bwd_targets", "hstu_validate_offsets", "hstu_status_string", "hstu_last_hip_error",
            "hstu_release_workspace", "hstu_profile_enable", "hstu_profile_read")
@@ -92,6 +94,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hstu_attn_fwd_dense.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, f32, vp, vp,
                                         ctypes.c_int]
     lib.hstu_attn_fwd_dense.restype = ctypes.c_int
+    lib.hstu_attn_fwd_rab.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, f32,
+                                      f32, vp, vp, ctypes.c_int]
+    lib.hstu_attn_fwd_rab.restype = ctypes.c_int
     i64 = ctypes.c_int64
     lib.hstu_layer_in_proj.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp,
                                        ctypes.c_int]
@@ -179,6 +184,33 @@ def hstu_attn_fwd(q, k, v, seq_offsets, alpha: float, n: float, out=None, stream
                            num_seqs, heads, d, float(alpha), float(n), out.data_ptr(),
                            _stream_handle(stream), _dtype_code(q))
     _check(st, "hstu_attn_fwd")
+    return out
+
+
+def hstu_attn_fwd_rab(q, k, v, seq_offsets, timestamps, pos_bias, time_bias, alpha: float,
+                      n: float, out=None, stream=None):
+    """Jagged causal HSTU attention forward with the relative attention bias
+    rab(r, c) = pos_bias[r - c] + time_bias[min(floor(log2(ts_r - ts_c + 1)),
+    len(time_bias) - 1)] added to alpha * <q_r, k_c> before SiLU.
+    timestamps: int32 GPU tensor of T entries; pos_bias, time_bias: float32
+    GPU tensors (the time table holds 1 to 32 entries)."""
+    import torch
+    out = _check_tensors(q, k, v, seq_offsets, out)
+    T, heads, d = q.shape
+    if (timestamps.dtype != torch.int32 or timestamps.shape != (T,) or not timestamps.is_cuda or
+            not timestamps.is_contiguous()):
+        raise ValueError("timestamps must be a contiguous int32 GPU tensor of T entries")
+    for name, t in (("pos_bias", pos_bias), ("time_bias", time_bias)):
+        if t.dtype != torch.float32 or t.dim() != 1 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 1-D float32 GPU tensor")
+    num_seqs = seq_offsets.numel() - 1
+    lib = load_library()
+    st = lib.hstu_attn_fwd_rab(q.data_ptr(), k.data_ptr(), v.data_ptr(), seq_offsets.data_ptr(),
+                               timestamps.data_ptr(), pos_bias.data_ptr(), pos_bias.numel(),
+                               time_bias.data_ptr(), time_bias.numel(), num_seqs, heads, d,
+                               float(alpha), float(n), out.data_ptr(), _stream_handle(stream),
+                               _dtype_code(q))
+    _check(st, "hstu_attn_fwd_rab")
     return out
 
 

@@ -214,6 +214,12 @@ struct MaskInputs {
     // Dense (B, heads, S, D) layout: num_seqs = B, dense_len = S, no offsets.
     bool dense = false;
     int64_t dense_len = 0;
+    // Relative attention bias (causal mask).
+    const int32_t* timestamps = nullptr;
+    const float* pos_bias = nullptr;
+    const float* time_bias = nullptr;
+    int num_pos = 0;
+    int num_time = 0;
 };
 
 // One forward call.
@@ -269,6 +275,11 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
     p.hist_offsets = mi.hist_offsets;
     p.dense = mi.dense;
     p.dense_len = mi.dense_len;
+    p.timestamps = mi.timestamps;
+    p.pos_bias = mi.pos_bias;
+    p.time_bias = mi.time_bias;
+    p.num_pos = mi.num_pos;
+    p.num_time = mi.num_time;
     p.num_seqs = num_seqs;
     p.heads = heads;
     p.d = d;
@@ -280,7 +291,8 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
     tc.sched = false;
     hipError_t e;
     if (!wl.fused) {
-        const int rows = hstu::q_tile_rows(dt, d, mi.hist_offsets != nullptr);
+        const int rows =
+                hstu::q_tile_rows(dt, d, mi.hist_offsets != nullptr || mi.timestamps != nullptr);
         e = hstu::launch_schedule(seq_offsets, num_seqs, heads, rows, wl, stream, sort,
                                   timed ? tc.e[0] : nullptr, timed ? tc.e[1] : nullptr);
         if (e != hipSuccess) return hip_fail(e);
@@ -415,6 +427,33 @@ hstu_status_t hstu_attn_fwd_targets(const void* q, const void* k, const void* v,
         return HSTU_ERR_INVALID_ARG;
     MaskInputs mi;
     mi.num_targets = num_targets;
+    return attn_fwd_call(q, k, v, seq_offsets, mi, num_seqs, heads, d, alpha, n, out, stream,
+                         dtype);
+}
+
+hstu_status_t hstu_attn_fwd_rab(const void* q, const void* k, const void* v,
+                                const int32_t* seq_offsets, const int32_t* timestamps,
+                                const float* pos_bias, int32_t num_pos, const float* time_bias,
+                                int32_t num_time, int32_t num_seqs, int32_t heads, int32_t d,
+                                float alpha, float n, void* out, hipStream_t stream,
+                                hstu_dtype_t dtype) {
+    if (num_pos < 1 || num_pos > (1 << 28) || num_time < 1 || num_time > 32)
+        return HSTU_ERR_INVALID_ARG;
+    // The kernels carry the bias in units of the raw score (rab / alpha).
+    if (!(alpha != 0.0f) || !std::isfinite((float)(1.0 / (double)alpha)))
+        return HSTU_ERR_INVALID_ARG;
+    if (num_seqs > 0) {
+        const uintptr_t bad = reinterpret_cast<uintptr_t>(timestamps) |
+                              reinterpret_cast<uintptr_t>(pos_bias) |
+                              reinterpret_cast<uintptr_t>(time_bias);
+        if (!timestamps || !pos_bias || !time_bias || (bad & 3u) != 0) return HSTU_ERR_INVALID_ARG;
+    }
+    MaskInputs mi;
+    mi.timestamps = timestamps;
+    mi.pos_bias = pos_bias;
+    mi.time_bias = time_bias;
+    mi.num_pos = num_pos;
+    mi.num_time = num_time;
     return attn_fwd_call(q, k, v, seq_offsets, mi, num_seqs, heads, d, alpha, n, out, stream,
                          dtype);
 }

@@ -65,6 +65,17 @@ struct KernelArgs {
     float out_scale;    // -ln(2) / n
 };
 
+// The relative-attention-bias kernel's arguments (a separate type, so that
+// the other modes' kernels keep their argument block).
+struct KernelArgsRab : KernelArgs {
+    const int32_t* ts;     // token timestamps
+    const float* wpos;     // relative attention bias tables
+    const float* wtime;
+    int npos;              // entries of wpos (distances 0 .. npos-1)
+    int ntime;             // entries of wtime (1 .. 32)
+    float bias_scale;      // 1 / alpha: the bias joins the raw score in the accumulators
+};
+
 // Which keys a query row sees.
 //  CAUSAL : key <= row.
 //  TARGETS: the last t tokens of a sequence are candidates that see the
@@ -76,7 +87,21 @@ struct KernelArgs {
 //           keys, read from the cache), then the candidates (read from k, v,
 //           rows hist.. of the virtual sequence); the mask is TARGETS' with
 //           that hist.  Zero keys and values add exactly nothing.
-enum : int { MASK_CAUSAL = 0, MASK_TARGETS = 1, MASK_CACHED = 2 };
+//  RAB    : CAUSAL, with the relative attention bias added to every score
+//           before SiLU (below).
+enum : int { MASK_CAUSAL = 0, MASK_TARGETS = 1, MASK_CACHED = 2, MASK_RAB = 3 };
+
+// Relative attention bias (HSTU paper translation, §3 and Appendix G: a bias
+// merging relative position and time, built inside the operator from its
+// parameters).  For query row r and key c <= r of a sequence with token
+// timestamps ts:
+//   rab(r, c) = wpos[r - c] + wtime[min(floor(log2(ts_r - ts_c + 1)), ntime - 1)]
+// (wpos[j] = 0 for j >= npos; a negative gap takes the last time bucket).
+// floor(log2(x)) = 31 - v_ffbh_u32(x) for x != 0, and v_ffbh_u32(0) = -1 (the
+// gap -1), so the kernel keeps a 33-entry LDS table indexed by
+// v_ffbh_u32(ts_r + 1 - ts_c) + 1 that already holds the capped bucket's
+// entry.  Position entries reach a wave through LDS as well: per key tile, the
+// window of wpos that the tile's (row, key) pairs index, staged with the tile.
 
 // -log2(e) * silu(alpha*s), given m = -alpha*log2(e)*s.
 __device__ __forceinline__ float silu_scaled(float m) {
@@ -122,6 +147,10 @@ struct Tile16 {
     static constexpr int LDS_BYTES = 2 * NSLOT * TILE_BYTES;
     static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;   // rows one wave load covers
     static constexpr int LOADS = TILE_BYTES / 1024 / NW;     // loads per wave per tensor
+    // Relative attention bias, per wave and slot: 64 key timestamps (BK used),
+    // then RAB_WIN entries of wpos, distances wr0 - k0 - BK .. + RAB_WIN - 1.
+    static constexpr int RAB_WIN = (ROWS_W + BK + 63) / 64 * 64;
+    static constexpr int RAB_WORDS = 64 + RAB_WIN;
     static_assert(LOADS * NW * 1024 == TILE_BYTES, "tile must split into whole wave loads");
     static_assert(BK % 32 == 0 && D % 32 == 0, "tile shape");
     static_assert(PF >= 2 && (PF - 1) * 2 * LOADS <= 63, "prefetch depth");
@@ -130,9 +159,13 @@ struct Tile16 {
 
 // MASK: one of the MASK_* modes; separate instantiations, so that the plain
 // causal form carries none of the other modes' registers.
+template <int MASK> struct ArgsOf { using type = KernelArgs; };
+template <> struct ArgsOf<MASK_RAB> { using type = KernelArgsRab; };
+
 template <typename T, int D, int NW, int QB, int BK, int PF, bool FUSED, int MASK>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
-    constexpr bool TGT = MASK != MASK_CAUSAL;    // hist-based mask
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MASK>::type a) {
+    constexpr bool TGT = MASK == MASK_TARGETS || MASK == MASK_CACHED;   // hist-based mask
+    constexpr bool RAB = MASK == MASK_RAB;
     using Cfg = Tile16<T, D, NW, QB, BK, PF>;
     using M = Mfma<T>;
     using v8 = typename M::v8;
@@ -146,9 +179,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
     constexpr int NKS = D / 16;    // k-steps of the first product
     constexpr int NDB = D / 32;    // 32-wide head-dim blocks of the output
 
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[Cfg::LDS_BYTES];
+    constexpr int RAB_BYTES = RAB ? Cfg::NSLOT * NW * Cfg::RAB_WORDS * 4 : 0;
+    static_assert(!RAB || (PF == 2 && Cfg::RAB_WIN % 64 == 0 && BK <= 64),
+                  "bias staging: one tile ahead, whole-wave window loads");
+    static_assert(Cfg::LDS_BYTES + RAB_BYTES <= 65536, "LDS reads use 16-bit immediate offsets");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[Cfg::LDS_BYTES + RAB_BYTES];
     __shared__ int s_item[NQ];
     __shared__ LocalTables lt;
+    __shared__ float ttab[RAB ? 33 : 1];   // time term by v_ffbh_u32(gap + 1) + 1, over alpha
     static_assert(NW * 64 >= FUSE_SEQS && NW * 64 >= 32 * NQ, "fused tables need a thread per sequence");
 
     const int tid = threadIdx.x;
@@ -190,6 +228,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
         v_hi[db] = (v_row + 8) * RB + 16 * ((cb >> 4) ^ vswz<CH>(v_row + 8)) + (cb & 15);
     }
     constexpr int NS = Cfg::NSLOT;
+    // Bias staging: this wave's area in slot 0 (byte offsets from the end of
+    // the K/V slots) for the key timestamps at 4g, and the lane's window base:
+    // the pair (row wr0 + 32qb + l32, key k0 + o) reads window entry
+    // 32qb + l32 - o + BK = (l32 - 4g + 5) + 32qb + (RAB_CMAX - o + 4g), where
+    // o - 4g = 32kb + 8(r/4) + r%4 <= RAB_CMAX (register r) keeps the rest an
+    // immediate offset.
+    constexpr int RAB_CMAX = BK - 5;
+    const int rab_tk = (wv * Cfg::RAB_WORDS + 4 * g) * 4;
+    const int rab_wb = (wv * Cfg::RAB_WORDS + 64 + l32 - 4 * g + 5) * 4;
+    if constexpr (RAB) {
+        if (tid < 33) {
+            const int b = tid == 0 ? a.ntime - 1 : min(32 - tid, a.ntime - 1);
+            ttab[tid] = a.wtime[b] * a.bias_scale;
+        }
+    }
 
     // The tile slots are free until the first item: a fused launch builds its
     // queue tables there and in lt.
@@ -286,6 +339,43 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
             }
         };
 
+        // Bias staging through registers: the key timestamps and the wpos
+        // window of loop tile c, loaded when the tile's K/V are issued and
+        // written to this wave's area of the tile's slot one barrier later.
+        uint32_t rab_ts = 0, trp1[QB];
+        float rab_w[RAB ? Cfg::RAB_WIN / 64 : 1];
+        auto issue_rab = [&](int c) {
+            if constexpr (RAB) {
+                const int k0 = c * BK;
+                rab_ts = __builtin_amdgcn_raw_buffer_load_b32(
+                        make_rsrc32(a.ts + start + k0, min(kv_end - k0, BK) * 4), lane * 4, 0, 0);
+                const __amdgpu_buffer_rsrc_t rp = make_rsrc32(a.wpos, a.npos * 4);
+                const int jw0 = wr0 - k0 - BK;   // negative entries read as zero
+#pragma unroll
+                for (int u = 0; u < Cfg::RAB_WIN / 64; ++u)
+                    rab_w[u] = __builtin_bit_cast(
+                            float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           rp, 4 * (jw0 + lane + 64 * u), 0, 0));
+            }
+        };
+        auto rab_store = [&](int c) {
+            if constexpr (RAB) {
+                float* area = reinterpret_cast<float*>(lds + Cfg::LDS_BYTES) +
+                              ((c % NS) * NW + wv) * Cfg::RAB_WORDS;
+                area[lane] = __builtin_bit_cast(float, rab_ts);
+#pragma unroll
+                for (int u = 0; u < Cfg::RAB_WIN / 64; ++u)
+                    area[64 + 64 * u + lane] = rab_w[u] * a.bias_scale;
+            }
+        };
+        if constexpr (RAB) {
+            const __amdgpu_buffer_rsrc_t rt =
+                    make_rsrc(a.ts + start + wr0, (int64_t)(s - wr0) * 4);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+                trp1[qb] = __builtin_amdgcn_raw_buffer_load_b32(rt, (qb * 32 + l32) * 4, 0, 0) + 1u;
+        }
+
         // Q^T operand: query rows wr0 + 32*qb + l32, head-dim slice [16ks + 8g, +8).
         v8 qop[QB][NKS];
         {
@@ -307,11 +397,41 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
             for (int qb = 0; qb < QB; ++qb) o[db][qb] = (f32x16){};
 
         // ---- building blocks ------------------------------------------------
+        // Initial value of the S^T accumulators for key block kb of the tile
+        // in `slot`: zero, or with the bias, rab / alpha (so that the score
+        // the pointwise pass scales by alpha is alpha <q, k> + rab).  Register
+        // r of lane (l32, g) is key 32kb + 8(r/4) + 4g + r%4 of query row
+        // wr0 + 32qb + l32.
+        auto acc_init = [&](int slot, int kb, f32x16* acc) {
+            if constexpr (RAB) {
+                const unsigned char* ra = lds + Cfg::LDS_BYTES + slot * NW * Cfg::RAB_WORDS * 4;
+                u32x4 tk[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    tk[j] = *reinterpret_cast<const u32x4*>(ra + rab_tk + 4 * (32 * kb + 8 * j));
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int o = 32 * kb + 8 * (r >> 2) + (r & 3);
+                        const float bp = *reinterpret_cast<const float*>(
+                                ra + rab_wb + 4 * (32 * qb + RAB_CMAX - o));
+                        const uint32_t x = trp1[qb] - tk[r >> 2][r & 3];
+                        int f;
+                        asm("v_ffbh_u32 %0, %1" : "=v"(f) : "v"(x));
+                        acc[qb][r] = bp + ttab[f + 1];
+                    }
+            }
+        };
         // S^T for key block kb of the tile in `slot` into st[qb].
         auto qk = [&](int slot, int kb, f32x16* st) {
             const unsigned char* kl = lds + slot * TB + kb * 32 * RB;
+            if constexpr (RAB) {
+                acc_init(slot, kb, st);
+            } else {
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) st[qb] = (f32x16){};
+                for (int qb = 0; qb < QB; ++qb) st[qb] = (f32x16){};
+            }
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const v8 ka = *reinterpret_cast<const v8*>(kl + k_off[ks]);
@@ -398,9 +518,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
         // range is empty, so they read nothing), which keeps the number of loads
         // in flight after tile c+1 fixed: a wait on the load counter then
         // covers exactly the tiles up to c+1.  Loads return in issue order.
+        if constexpr (RAB) {
+            // (tile 0's bias values are written once its loads are in; tile
+            // 1's are loaded then, and written at the first barrier)
+            issue_loads(0);
+            issue_rab(0);
 #pragma unroll
-        for (int c = 0; c < PF; ++c) issue_loads(c);
-        __builtin_amdgcn_s_waitcnt(VMCNT_LE((PF - 1) * 2 * Cfg::LOADS));
+            for (int c = 1; c < PF; ++c) issue_loads(c);
+            __builtin_amdgcn_s_waitcnt(VMCNT_LE((PF - 1) * 2 * Cfg::LOADS));
+            rab_store(0);
+            issue_rab(1);
+        } else {
+#pragma unroll
+            for (int c = 0; c < PF; ++c) issue_loads(c);
+            __builtin_amdgcn_s_waitcnt(VMCNT_LE((PF - 1) * 2 * Cfg::LOADS));
+        }
         __syncthreads();
 
         // One barrier per tile.  At barrier c every wave has finished its loads
@@ -417,8 +549,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
         // faster on 16 x 4096, 3 % on 8 x 8k-20k).
         auto tile_sync = [&](int c) {
             __builtin_amdgcn_s_waitcnt(VMCNT_LE((PF - 2) * 2 * Cfg::LOADS));
+            if constexpr (RAB) rab_store(c + 1);
             __syncthreads();
             issue_loads(c + PF);
+            if constexpr (RAB) issue_rab(c + PF);
             if ((((c >> 1) + (blockIdx.x >= gridDim.x / 2 ? 1 : 0)) & 1) != 0)
                 __builtin_amdgcn_s_setprio(1);
             else
@@ -463,8 +597,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(KernelArgs a) {
             v8 p0[QB], p1[QB];
             weights(cur, 0, p0);
             mma_pv(v1d, p1d);
+            if constexpr (RAB) {
+                acc_init(next_slot, next_kb, nxt);
+            } else {
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) nxt[qb] = (f32x16){};
+                for (int qb = 0; qb < QB; ++qb) nxt[qb] = (f32x16){};
+            }
 #pragma unroll
             for (int ks = 0; ks < NKS / 2; ++ks)
 #pragma unroll
@@ -586,6 +724,11 @@ struct KernelArgsF32 {
     const float* kc;       // cached history K, V, or null
     const float* vc;
     const int32_t* hoff;   // history offsets: the cached-history form when non-null
+    const int32_t* ts;     // token timestamps: the relative attention bias when non-null
+    const float* wpos;
+    const float* wtime;
+    int npos;
+    int ntime;
     WorkList wl;
     int64_t row_stride;
     int64_t head_stride;
@@ -646,6 +789,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
         const bool wave_live = wr0 < s;
         const int my_row = wr0 + l32;
         const int64_t seq_base = (int64_t)start * H * D + (int64_t)it.head * a.head_stride;
+        // relative attention bias: this row's timestamp + 1
+        const uint32_t trp1 = (a.ts && my_row < s) ? (uint32_t)a.ts[start + my_row] + 1u : 0u;
 
         float qf[D / 2];
         {
@@ -698,7 +843,18 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int kvl = kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                        float p = silu_scaled(st[r] * a.score_scale);
+                        float p;
+                        if (a.ts) {
+                            const int key = k0 + kvl;
+                            const int dist = my_row - key;
+                            float bias = (dist >= 0 && dist < a.npos) ? a.wpos[dist] : 0.0f;
+                            const uint32_t x = trp1 - (key < s ? (uint32_t)a.ts[start + key] : 0u);
+                            const int lz = __clz((int)x);   // 32 for x == 0 (gap -1)
+                            bias += a.wtime[lz == 32 ? a.ntime - 1 : min(31 - lz, a.ntime - 1)];
+                            p = silu_scaled(__builtin_fmaf(st[r], a.score_scale, bias * -LOG2E));
+                        } else {
+                            p = silu_scaled(st[r] * a.score_scale);
+                        }
                         if (partial) {
                             const int key = k0 + kvl;
                             p = (key <= my_row && (key < hist || key == my_row)) ? p : 0.0f;
@@ -738,9 +894,11 @@ constexpr int NW16 = 4;
 template <int D> struct QBlocks { static constexpr int value = D == 64 ? 2 : 1; };
 // The cached-history form runs one 32-row block per wave (128-row items): its
 // calls hold one micro-batch of candidates per request, and 256-row items
-// would leave half of the resident workgroups without work at 16 x 1024.
+// would leave half of the resident workgroups without work at 16 x 1024.  So
+// does the relative-attention-bias form, whose bias terms need the registers
+// a second block would take.
 template <int D, int MASK> struct QBlocksFor {
-    static constexpr int value = MASK == MASK_CACHED ? 1 : QBlocks<D>::value;
+    static constexpr int value = MASK == MASK_CACHED || MASK == MASK_RAB ? 1 : QBlocks<D>::value;
 };
 template <int D> struct KeyTile { static constexpr int value = D == 64 ? 64 : 32; };
 template <int D> struct Prefetch { static constexpr int value = 2; };
@@ -769,6 +927,30 @@ hipError_t launch16(const FwdParams& p, WorkList wl, int grid, hipStream_t strea
     a.out_scale = -LN2 / p.n;
     constexpr int QB = QBlocks<D>::value, BK = KeyTile<D>::value, PF = Prefetch<D>::value;
     constexpr int QBC = QBlocksFor<D, MASK_CACHED>::value;
+    if (p.timestamps) {
+        KernelArgsRab ar;
+        static_cast<KernelArgs&>(ar) = a;
+        ar.ts = p.timestamps;
+        ar.wpos = p.pos_bias;
+        ar.wtime = p.time_bias;
+        ar.npos = p.num_pos;
+        ar.ntime = p.num_time;
+        ar.bias_scale = (float)(1.0 / (double)p.alpha);
+        constexpr int QBR = QBlocksFor<D, MASK_RAB>::value;
+        auto fn = wl.fused ? attn_fwd_mfma16<T, D, NW16, QBR, BK, PF, true, MASK_RAB>
+                           : attn_fwd_mfma16<T, D, NW16, QBR, BK, PF, false, MASK_RAB>;
+        if (grid <= 0) {
+            static int cached[2] = {};
+            int& c = cached[wl.fused ? 1 : 0];
+            if (!c) c = resident_grid(fn, NW16 * 64);
+            grid = c;
+        }
+        if (start)
+            hipExtLaunchKernelGGL(fn, dim3(grid), dim3(NW16 * 64), 0, stream, start, stop, 0, ar);
+        else
+            hipLaunchKernelGGL(fn, dim3(grid), dim3(NW16 * 64), 0, stream, ar);
+        return hipGetLastError();
+    }
     const int mode = p.hist_offsets ? MASK_CACHED : p.num_targets ? MASK_TARGETS : MASK_CAUSAL;
     using Fn = void (*)(KernelArgs);
     static constexpr Fn fns[2][3] = {
@@ -805,6 +987,11 @@ hipError_t launch_f32(const FwdParams& p, WorkList wl, int grid, hipStream_t str
     a.kc = static_cast<const float*>(p.k_cache);
     a.vc = static_cast<const float*>(p.v_cache);
     a.hoff = p.hist_offsets;
+    a.ts = p.timestamps;
+    a.wpos = p.pos_bias;
+    a.wtime = p.time_bias;
+    a.npos = p.num_pos;
+    a.ntime = p.num_time;
     a.row_stride = p.dense ? p.d : (int64_t)p.heads * p.d;
     a.head_stride = p.dense ? p.dense_len * p.d : p.d;
     a.wl = wl;
@@ -844,9 +1031,9 @@ int device_cus() {
     return cached_cus;
 }
 
-int q_tile_rows(Dtype dt, int d, bool cached) {
+int q_tile_rows(Dtype dt, int d, bool single_block) {
     if (dt == Dtype::FP32) return TileF32<64, NWF, BKF>::BQ;
-    if (cached)
+    if (single_block)
         return d == 64 ? Tile16<__bf16, 64, NW16, QBlocksFor<64, MASK_CACHED>::value,
                                 KeyTile<64>::value, Prefetch<64>::value>::BQ
                        : Tile16<__bf16, 128, NW16, QBlocksFor<128, MASK_CACHED>::value,

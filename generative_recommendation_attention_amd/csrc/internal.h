@@ -143,6 +143,13 @@ struct FwdParams {
     // Dense (B, heads, S, D) layout: offsets are then i * S, S = dense_len.
     bool dense = false;
     int64_t dense_len = 0;
+    // Relative attention bias (causal mask, jagged layout only): token
+    // timestamps (T), position table [num_pos], time table [num_time <= 32].
+    const int32_t* timestamps = nullptr;
+    const float* pos_bias = nullptr;
+    const float* time_bias = nullptr;
+    int num_pos = 0;
+    int num_time = 0;
     int num_seqs;
     int heads;
     int d;
@@ -150,8 +157,10 @@ struct FwdParams {
     float n;
 };
 
-// Rows of Q handled by one work item for this element type and head size.
-int q_tile_rows(Dtype dt, int d, bool cached = false);
+// Rows of Q handled by one work item for this element type and head size;
+// single_block: the cached-history and relative-attention-bias forms, whose
+// waves hold one 32-row block each.
+int q_tile_rows(Dtype dt, int d, bool single_block = false);
 
 // Compute units of the current device.
 int device_cus();

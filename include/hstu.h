@@ -193,6 +193,39 @@ hstu_status_t hstu_layer_out_proj(const void* attn, const void* u, const void* x
                                   int32_t d_model, int32_t heads, int32_t d, void* y,
                                   hipStream_t stream, hstu_dtype_t dtype);
 
+/* Causal forward with the relative attention bias rab_{p,t} (HSTU paper
+ * translation, §3: a bias merging relative position and time is added to the
+ * scores before phi_2 = SiLU; Appendix G: the bias is built inside the
+ * attention operator from its parameters instead of being read as a
+ * tensor).  The page's equation is lost; this call takes the reading
+ *
+ *   out[r] = (1/n) * sum_{c <= r} silu(alpha <q[r], k[c]> + rab(r, c)) * v[c]
+ *   rab(r, c) = pos_bias[r - c] + time_bias[min(floor(log2(ts[r] - ts[c] + 1)), num_time - 1)]
+ *
+ * per sequence and head, r and c local rows, ts the sequence's timestamps;
+ * pos_bias[j] counts as 0 for j >= num_pos, and a negative gap (a key later
+ * than its query) takes bucket num_time - 1.  The tables are shared by all
+ * heads.
+ *
+ *   q, k, v, out, seq_offsets : as in hstu_attn_fwd (jagged layout).
+ *   timestamps   : device int32[T], T = seq_offsets[num_seqs], one per token, 4-byte
+ *                  aligned; within one sequence every gap ts[r] - ts[c] must lie
+ *                  in (-2^31 + 1, 2^31 - 1) (for example non-decreasing
+ *                  timestamps spanning less than 2^31 - 1).
+ *   pos_bias     : device float[num_pos], 1 <= num_pos <= 2^28, 4-byte aligned.
+ *   time_bias    : device float[num_time], 1 <= num_time <= 32, 4-byte aligned.
+ * All three are caller-owned and read only.  alpha must be non-zero with a
+ * finite float reciprocal (the kernels add rab / alpha to the raw score).
+ * Null or misaligned pointers (with num_seqs > 0), table sizes out of range or
+ * such an alpha give HSTU_ERR_INVALID_ARG before anything is enqueued.  Element types, streams, scratch and errors as
+ * in hstu_attn_fwd. */
+hstu_status_t hstu_attn_fwd_rab(const void* q, const void* k, const void* v,
+                                const int32_t* seq_offsets, const int32_t* timestamps,
+                                const float* pos_bias, int32_t num_pos, const float* time_bias,
+                                int32_t num_time, int32_t num_seqs, int32_t heads, int32_t d,
+                                float alpha, float n, void* out, hipStream_t stream,
+                                hstu_dtype_t dtype);
+
 /* Backward: gradients of hstu_attn_fwd (or, with num_targets, of
  * hstu_attn_fwd_targets) with respect to q, k and v, for the upstream
  * gradient dout = dLoss/dout.  The attention is recomputed block by block and

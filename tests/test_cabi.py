@@ -103,6 +103,43 @@ def test_targets_empty_batch_is_a_no_op(lib):
                          num_seqs=0) == hstu.HSTU_OK
 
 
+def _call_rab(lib, ts=48, wpos=64, npos=8, wtime=80, ntime=4, **kw):
+    a = dict(q=16, k=16, v=16, off=16, num_seqs=1, heads=1, d=64, alpha=0.1, n=1.0, out=32,
+             dtype=hstu.HSTU_BF16)
+    a.update(kw)
+    return lib.hstu_attn_fwd_rab(a["q"], a["k"], a["v"], a["off"], ts, wpos, npos, wtime, ntime,
+                                 a["num_seqs"], a["heads"], a["d"], a["alpha"], a["n"], a["out"],
+                                 None, a["dtype"])
+
+
+# (every case has one invalid argument: nothing reaches a device)
+@pytest.mark.parametrize("kw,status", [
+    (dict(ts=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(wpos=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(wtime=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(ts=50), hstu.HSTU_ERR_INVALID_ARG),      # misaligned timestamps
+    (dict(wtime=82), hstu.HSTU_ERR_INVALID_ARG),   # misaligned table
+    (dict(npos=0), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(npos=(1 << 28) + 1), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(ntime=0), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(ntime=33), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(alpha=0.0), hstu.HSTU_ERR_INVALID_ARG),  # the bias is carried as rab / alpha
+    (dict(alpha=1e-39), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(q=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(d=96), hstu.HSTU_ERR_UNSUPPORTED),
+    (dict(dtype=5), hstu.HSTU_ERR_UNSUPPORTED),
+    (dict(n=0.0), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(out=16), hstu.HSTU_ERR_INVALID_ARG),
+])
+def test_rab_argument_checks(lib, kw, status):
+    assert _call_rab(lib, **kw) == status
+
+
+def test_rab_empty_batch_is_a_no_op(lib):
+    assert _call_rab(lib, ts=None, wpos=None, wtime=None, q=None, k=None, v=None, off=None,
+                     out=None, num_seqs=0) == hstu.HSTU_OK
+
+
 def _call_cached(lib, kc=64, vc=80, hoff=96, **kw):
     a = dict(q=16, k=16, v=16, off=16, num_seqs=1, heads=1, d=64, alpha=0.1, n=1.0, out=32,
              dtype=hstu.HSTU_BF16)
