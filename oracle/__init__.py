@@ -44,7 +44,9 @@ y = x + W2 (LN(a) * u) + b2 with LN over heads * d.
 Parity status: pinned.  The test suite ties these functions to closed forms
 (hand-worked 2- and 3-token cases), to identities that reduce to textbook
 operations (sign-flip -> masked GEMM, constant rows -> prefix sum, row 0),
-and to invariants (linearity, causality, segment independence).
+and to invariants (linearity, causality, segment independence); the bias
+form also to a plain forward with extra head dimensions and to buckets found
+by floating-point log2.
 """
 from __future__ import annotations
 
