@@ -127,6 +127,15 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          f64, f64, vp, vp, i64, vp]
     lib.hstu_oracle_rows_rab.restype = ctypes.c_int
+    lib.hstu_oracle_bwd_rab.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, ctypes.c_int, vp,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        f64, f64, vp, vp, vp, vp, vp]
+    lib.hstu_oracle_bwd_rab.restype = ctypes.c_int
+    lib.hstu_oracle_bwd_rab_rows.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
+                                             ctypes.c_int, vp, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, f64, f64, ctypes.c_int,
+                                             vp, vp, i64, vp]
+    lib.hstu_oracle_bwd_rab_rows.restype = ctypes.c_int
     lib.hstu_oracle_threads.argtypes = []
     lib.hstu_oracle_threads.restype = ctypes.c_int
     _libs[path] = lib
@@ -323,7 +332,52 @@ def rows_rab(q, k, v, offsets, timestamps, pos_bias, time_bias, heads: int, d: i
     return out
 
 
+def bwd_rab(q, k, v, dout, offsets, timestamps, pos_bias, time_bias, heads: int, d: int,
+            alpha: float, n: float, dtype: str, lib: Optional[ctypes.CDLL] = None):
+    """(dq, dk, dv, dpos, dtime): fp64 gradients of fwd_rab for upstream
+    gradient dout; dq/dk/dv (T, heads, d), dpos [npos], dtime [ntime]."""
+    lib = lib or load()
+    q, k, v, off, ts, wp, wt = _rab_args(q, k, v, offsets, timestamps, pos_bias, time_bias,
+                                         heads, d, dtype)
+    dout = _storage(dout, dtype)
+    T = int(off[-1]) if len(off) else 0
+    if dout.size < T * heads * d:
+        raise ValueError("dout smaller than offsets imply")
+    dq, dk, dv = (np.zeros((T, heads, d), dtype=np.float64) for _ in range(3))
+    dpos, dtime = np.zeros(len(wp)), np.zeros(len(wt))
+    rc = lib.hstu_oracle_bwd_rab(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _DTYPE_CODE[dtype],
+                                 _ptr(off), _ptr(ts), _ptr(wp), len(wp), _ptr(wt), len(wt),
+                                 len(off) - 1, heads, d, float(alpha), float(n), _ptr(dq),
+                                 _ptr(dk), _ptr(dv), _ptr(dpos), _ptr(dtime))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments (malformed offsets or sizes)")
+    return dq, dk, dv, dpos, dtime
+
+
 BWD_KIND = {"dq": 0, "dk": 1, "dv": 2}
+
+
+def bwd_rab_rows(q, k, v, dout, offsets, timestamps, pos_bias, time_bias, heads: int, d: int,
+                 alpha: float, n: float, dtype: str, kind: str, tokens, head_ids,
+                 lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+    """Sampled rows (m, d) of dq (at query tokens), dk or dv (at key tokens)
+    of bwd_rab."""
+    lib = lib or load()
+    q, k, v, off, ts, wp, wt = _rab_args(q, k, v, offsets, timestamps, pos_bias, time_bias,
+                                         heads, d, dtype)
+    dout = _storage(dout, dtype)
+    tok = np.ascontiguousarray(tokens, dtype=np.int64)
+    hd = np.ascontiguousarray(head_ids, dtype=np.int32)
+    if tok.shape != hd.shape:
+        raise ValueError("tokens and head_ids differ in length")
+    out = np.zeros((len(tok), d), dtype=np.float64)
+    rc = lib.hstu_oracle_bwd_rab_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _DTYPE_CODE[dtype],
+                                      _ptr(off), _ptr(ts), _ptr(wp), len(wp), _ptr(wt), len(wt),
+                                      len(off) - 1, heads, d, float(alpha), float(n),
+                                      BWD_KIND[kind], _ptr(tok), _ptr(hd), len(tok), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle rejected the sampled rows")
+    return out
 
 
 def bwd_rows(q, k, v, dout, offsets, heads: int, d: int, alpha: float, n: float, dtype: str,

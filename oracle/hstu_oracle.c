@@ -72,6 +72,11 @@
  *   rab(r, c) = wpos[r - c] + wtime[min(floor(log2(ts_r - ts_c + 1)), ntime - 1)]
  * with wpos[j] = 0 for j >= npos and a negative gap in the last time bucket,
  * added after alpha: out[r] = (1/n) sum_{c <= r} silu(alpha <q_r, k_c> + rab(r, c)) v_c.
+ * Its gradients (the *_bwd_rab entry points) differentiate that definition:
+ * per kept pair, dx = silu'(x) <dO_r, v_c> / n with x the biased score;
+ * dq_r += alpha dx k_c, dk_c += alpha dx q_r, dv_c += silu(x) / n dO_r, and
+ * dx is added to wpos[r - c] (r - c < npos) and to the pair's time bucket
+ * (the tables' gradients, summed over sequences and heads).
  *
  * Readings taken where the pages are silent (each listed in the design notes):
  *   - alpha multiplies the scores before SiLU; n is a caller-given scalar;
@@ -87,6 +92,7 @@
  * parity is always compiled with ORACLE_PLANT=0.
  */
 #include <math.h>
+#include <stdlib.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -697,6 +703,122 @@ int hstu_oracle_rows_rab(const void* q, const void* k, const void* v, int dtype,
             const int64_t s0 = off[lo];
             rab_row(q, k, v, dtype, s0, tok[m] - s0, ts + s0, wpos, npos, wtime, ntime, heads, d,
                     hd[m], alpha, n, qrow, out_rows + m * (int64_t)d);
+        }
+    }
+    return 0;
+}
+
+/* Gradient terms of one kept pair (r, c) of a sequence with the relative
+ * attention bias: x = alpha <q_r, k_c> + rab(r, c); returns dx = dLoss/dx and
+ * adds to dq_r, dk_c, dv_c (each d elements, any may be null). */
+static double rab_pair_grads(const void* q, const void* k, const void* v, const void* dout,
+                             int dtype, int64_t s0, int64_t r, int64_t c, const int32_t* ts,
+                             const double* wpos, int npos, const double* wtime, int ntime,
+                             int heads, int d, int h, double alpha, double n, double* dq_r,
+                             double* dk_c, double* dv_c) {
+    const int64_t rs = (int64_t)heads * d, ho = (int64_t)h * d;
+    const int64_t qr = (s0 + r) * rs + ho, kc = (s0 + c) * rs + ho;
+    double dot = 0.0, dov = 0.0;
+    for (int e = 0; e < d; ++e) {
+        dot += load_elem(q, dtype, qr + e) * load_elem(k, dtype, kc + e);
+        dov += load_elem(dout, dtype, qr + e) * load_elem(v, dtype, kc + e);
+    }
+    const double x = alpha * dot + rab_value(r, c, ts, wpos, npos, wtime, ntime);
+    const double dx = dsilu(x) * dov / n;
+    const double w = silu(x) / n;
+    for (int e = 0; e < d; ++e) {
+        if (dq_r) dq_r[e] += alpha * dx * load_elem(k, dtype, kc + e);
+        if (dk_c) dk_c[e] += alpha * dx * load_elem(q, dtype, qr + e);
+        if (dv_c) dv_c[e] += w * load_elem(dout, dtype, qr + e);
+    }
+#if ORACLE_PLANT == 22
+    return alpha * dx; /* planted: the bias gradient scaled by alpha */
+#else
+    return dx;
+#endif
+}
+
+/* Gradients of hstu_oracle_fwd_rab for upstream gradient dout: dq, dk, dv fp64
+ * (T, heads, d), and the tables' gradients dwpos[npos], dwtime[ntime] (summed
+ * over sequences and heads), all overwritten.  The table sums are taken per
+ * (sequence, head) pair and then added in pair order, so the result does not
+ * depend on the thread count.  Returns 0, or -1 on bad arguments. */
+int hstu_oracle_bwd_rab(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                        const int32_t* off, const int32_t* ts, const double* wpos, int npos,
+                        const double* wtime, int ntime, int num_seqs, int heads, int d,
+                        double alpha, double n, double* dq, double* dk, double* dv,
+                        double* dwpos, double* dwtime) {
+    if (num_seqs < 0 || heads < 1 || d < 1) return -1;
+    if (npos < 1 || ntime < 1 || ntime > 32 || !offsets_ok(off, num_seqs)) return -1;
+    const int64_t rs = (int64_t)heads * d;
+    const int64_t T = num_seqs > 0 ? off[num_seqs] : 0;
+    const int64_t items = (int64_t)num_seqs * heads;
+    const int64_t nt = (int64_t)npos + ntime;
+    double* part = (double*)calloc((size_t)(items > 0 ? items : 1) * (size_t)nt, sizeof(double));
+    if (!part) return -1;
+    memset(dq, 0, sizeof(double) * T * rs);
+    memset(dk, 0, sizeof(double) * T * rs);
+    memset(dv, 0, sizeof(double) * T * rs);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t it = 0; it < items; ++it) {
+        const int i = (int)(it / heads), h = (int)(it % heads);
+        const int64_t s0 = off[i], len = (int64_t)off[i + 1] - off[i];
+        double* pp = part + it * nt;
+        for (int64_t r = 0; r < len; ++r)
+            for (int64_t c = 0; c <= r; ++c) {
+                const double dx = rab_pair_grads(
+                        q, k, v, dout, dtype, s0, r, c, ts + s0, wpos, npos, wtime, ntime, heads,
+                        d, h, alpha, n, dq + (s0 + r) * rs + (int64_t)h * d,
+                        dk + (s0 + c) * rs + (int64_t)h * d, dv + (s0 + c) * rs + (int64_t)h * d);
+                int64_t dist = r - c;
+#if ORACLE_PLANT == 23
+                dist = dist + 1; /* planted: position gradient one distance off */
+#endif
+                if (dist < npos) pp[dist] += dx;
+                pp[npos + time_bucket((int64_t)ts[s0 + r] - (int64_t)ts[s0 + c], ntime)] += dx;
+            }
+    }
+    for (int64_t j = 0; j < nt; ++j) {
+        double acc = 0.0;
+        for (int64_t it = 0; it < items; ++it) acc += part[it * nt + j];
+        if (j < npos) dwpos[j] = acc; else dwtime[j - npos] = acc;
+    }
+    free(part);
+    return 0;
+}
+
+/* Sampled gradient rows of the same: kind 0 = dq at query token tok[m], 1 =
+ * dk and 2 = dv at key token tok[m], head hd[m]; out_rows[m, 0..d).  Returns
+ * 0, or -1 on bad arguments. */
+int hstu_oracle_bwd_rab_rows(const void* q, const void* k, const void* v, const void* dout,
+                             int dtype, const int32_t* off, const int32_t* ts, const double* wpos,
+                             int npos, const double* wtime, int ntime, int num_seqs, int heads,
+                             int d, double alpha, double n, int kind, const int64_t* tok,
+                             const int32_t* hd, int64_t count, double* out_rows) {
+    if (num_seqs < 1 || heads < 1 || d < 1 || kind < 0 || kind > 2) return -1;
+    if (npos < 1 || ntime < 1 || ntime > 32 || !offsets_ok(off, num_seqs)) return -1;
+    const int64_t T = off[num_seqs];
+    for (int64_t m = 0; m < count; ++m)
+        if (tok[m] < 0 || tok[m] >= T || hd[m] < 0 || hd[m] >= heads) return -1;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t m = 0; m < count; ++m) {
+        int lo = 0, hi = num_seqs - 1;   /* largest i with off[i] <= tok */
+        while (lo < hi) {
+            int mid = (lo + hi + 1) / 2;
+            if (off[mid] <= tok[m]) lo = mid; else hi = mid - 1;
+        }
+        const int64_t s0 = off[lo], len = (int64_t)off[lo + 1] - off[lo], t = tok[m] - s0;
+        double* o = out_rows + m * (int64_t)d;
+        for (int e = 0; e < d; ++e) o[e] = 0.0;
+        if (kind == 0) {
+            for (int64_t c = 0; c <= t; ++c)
+                rab_pair_grads(q, k, v, dout, dtype, s0, t, c, ts + s0, wpos, npos, wtime, ntime,
+                               heads, d, hd[m], alpha, n, o, 0, 0);
+        } else {
+            for (int64_t r = t; r < len; ++r)
+                rab_pair_grads(q, k, v, dout, dtype, s0, r, t, ts + s0, wpos, npos, wtime, ntime,
+                               heads, d, hd[m], alpha, n, 0, kind == 1 ? o : 0,
+                               kind == 2 ? o : 0);
         }
     }
     return 0;

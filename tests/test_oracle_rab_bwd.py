@@ -1,0 +1,31 @@
+"""The oracle's gradients of the relative-attention-bias forward against
+their pins, and two planted mistakes (ORACLE_PLANT=22: the bias gradient
+scaled by alpha; 23: the position gradient credited one distance off), each
+caught by at least two pins."""
+import os
+
+import pytest
+
+import oracle
+import pins_rab_bwd
+
+
+@pytest.mark.parametrize("pin", pins_rab_bwd.RAB_BWD_PINS, ids=lambda p: p.__name__)
+def test_rab_bwd_pin(pin):
+    pin(oracle.load())
+
+
+PLANTS = {22: "bias gradient scaled by alpha", 23: "position gradient one distance off"}
+
+
+@pytest.mark.parametrize("plant", sorted(PLANTS), ids=lambda p: PLANTS[p])
+def test_planted_rab_bwd_mistake_is_caught(tmp_path, plant):
+    path = oracle.build(os.path.join(str(tmp_path), f"libmutant{plant}.so"), plant=plant)
+    lib = oracle.load(path)
+    caught = []
+    for pin in pins_rab_bwd.RAB_BWD_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert len(caught) >= 2, f"planted mistake {PLANTS[plant]!r} caught only by {caught}"
