@@ -24,7 +24,8 @@ the five products of a recomputing backward, 10 * heads * d per kept pair
 dK/dV and the dQ kernel).  --rab times hstu_attn_fwd_rab (the relative
 attention bias, HSTU paper translation §3 and Appendix G) on the 16 x 4096
 workload with a position entry per distance and 16 time buckets; useful FLOPs
-are the plain forward's (the bias terms are not counted).
+are the plain forward's (the bias terms are not counted); --backward --rab
+times hstu_attn_bwd_rab (dq, dk, dv and both tables' gradients) on it.
 """
 from __future__ import annotations
 
@@ -49,6 +50,7 @@ METRIC_DENSE = "HSTU attn fwd useful TFLOP/s, dense (b, heads, s, d) layout"
 METRIC_BWD = "HSTU attn bwd (dq, dk, dv) useful TFLOP/s"
 METRIC_CACHED = "HSTU cached-history attn fwd useful TFLOP/s (M-FALCON micro-batch)"
 METRIC_RAB = "HSTU attn fwd with relative attention bias useful TFLOP/s"
+METRIC_RAB_BWD = "HSTU attn bwd with relative attention bias (dq, dk, dv, table gradients) useful TFLOP/s"
 # HBM traffic per dispatch of the attention kernel, from two rocprofv3 --pmc
 # runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
 # same counter reads for a plain 1 GiB device copy (bench.py --copy-calibrate):
@@ -131,7 +133,7 @@ def cpu_baseline_cached(cc, budget_s: float):
                       f"{threads} threads available"}
 
 
-def cpu_baseline_bwd(case, dout, budget_s: float):
+def cpu_baseline_bwd(case, dout, budget_s: float, rab=None):
     """The oracle's backward on whole sequences, in input order, until about
     budget_s of wall time has been spent."""
     import oracle
@@ -144,8 +146,14 @@ def cpu_baseline_bwd(case, dout, budget_s: float):
         j = min(case.num_seqs, i + per_call)
         a, b = int(off[i]), int(off[j])
         t0 = time.perf_counter()
-        oracle.bwd(case.q[a:b], case.k[a:b], case.v[a:b], dout[a:b], off[i:j + 1] - off[i],
-                   case.heads, case.d, case.alpha, case.n, case.dtype, lib=lib)
+        if rab is not None:
+            oracle.bwd_rab(case.q[a:b], case.k[a:b], case.v[a:b], dout[a:b],
+                           off[i:j + 1] - off[i], rab.timestamps[a:b], rab.pos_bias,
+                           rab.time_bias, case.heads, case.d, case.alpha, case.n, case.dtype,
+                           lib=lib)
+        else:
+            oracle.bwd(case.q[a:b], case.k[a:b], case.v[a:b], dout[a:b], off[i:j + 1] - off[i],
+                       case.heads, case.d, case.alpha, case.n, case.dtype, lib=lib)
         done_s += time.perf_counter() - t0
         s = case.lengths[i:j].astype(np.float64)
         done_flops += float(np.sum(10.0 * case.heads * case.d * s * (s + 1.0) / 2.0))
@@ -315,9 +323,10 @@ def main() -> int:
                     help="run only a plain 1 GiB device copy (3 times), the reference for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
-    if args.targets + args.cached + args.backward + args.dense + args.layer + args.rab > 1:
+    modes = args.targets + args.cached + args.backward + args.dense + args.layer + args.rab
+    if modes > 1 and not (modes == 2 and args.backward and args.rab):
         ap.error("--targets, --cached, --backward, --dense, --layer and --rab are separate "
-                 "benchmarks")
+                 "benchmarks (except --backward --rab)")
     if args.layer:
         return bench_layer(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -366,7 +375,7 @@ def main() -> int:
 
         def call():
             hstu.hstu_attn_fwd_cached(q, k, v, off, kc, vc, hoff, case.alpha, case.n, out=out)
-    elif args.rab:
+    elif args.rab and not args.backward:
         ts = torch.from_numpy(rab.timestamps).cuda()
         wp = torch.from_numpy(rab.pos_bias).cuda()
         wt = torch.from_numpy(rab.time_bias).cuda()
@@ -400,9 +409,19 @@ def main() -> int:
         flops *= 2.5
         # q, k, v, dout read once, dq, dk, dv written once
         alg_bytes *= 7.0 / 4.0
+        if args.rab:
+            ts = torch.from_numpy(rab.timestamps).cuda()
+            wp = torch.from_numpy(rab.pos_bias).cuda()
+            wt = torch.from_numpy(rab.time_bias).cuda()
+            rgrads = grads + (torch.empty_like(wp), torch.empty_like(wt))
+            alg_bytes += 4.0 * case.total + 8.0 * (rab.pos_bias.size + rab.time_bias.size)
 
-        def call():
-            hstu.hstu_attn_bwd(q, k, v, dout, off, case.alpha, case.n, grads=grads)
+            def call():
+                hstu.hstu_attn_bwd_rab(q, k, v, dout, off, ts, wp, wt, case.alpha, case.n,
+                                       grads=rgrads)
+        else:
+            def call():
+                hstu.hstu_attn_bwd(q, k, v, dout, off, case.alpha, case.n, grads=grads)
     else:
         def call():
             hstu.hstu_attn_fwd(q, k, v, off, case.alpha, case.n, out=out)
@@ -435,7 +454,8 @@ def main() -> int:
                else traffic_bytes(args.workload))
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-                "kernel": ("attn_bwd_dkv + attn_bwd_dq" if args.backward else
+                "kernel": ("attn_bwd_dkv + attn_bwd_dq + table-gradient sum" if args.backward and
+                           args.rab else "attn_bwd_dkv + attn_bwd_dq" if args.backward else
                            "attn_fwd_mfma16" if case.dtype != "fp32" else "attn_fwd_mfma_f32"),
                 "kernel_ms": round(attn_ms, 5), "sched_kernel_ms": round(sched_ms, 5),
                 "hbm_frac": round(alg_bytes / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
@@ -445,13 +465,14 @@ def main() -> int:
         if args.cached:
             cpu = cpu_baseline_cached(cc, args.cpu_budget)
         elif args.backward:
-            cpu = cpu_baseline_bwd(case, dout_host, args.cpu_budget)
+            cpu = cpu_baseline_bwd(case, dout_host, args.cpu_budget, rab=rab)
         else:
             cpu = cpu_baseline(case, args.cpu_budget, rab=rab)
 
     L = case.lengths
     line = {
         "metric": (METRIC_CACHED if args.cached else METRIC_TARGETS if args.targets else
+                   METRIC_RAB_BWD if args.backward and args.rab else
                    METRIC_BWD if args.backward else METRIC_DENSE if args.dense else
                    METRIC_RAB if args.rab else METRIC),
         "value": round(value, 2),

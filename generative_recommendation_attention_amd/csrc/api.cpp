@@ -321,11 +321,23 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
 // One backward call: the dK/dV kernel, then the dQ kernel, on one work list
 // of BWD_TILE_ROWS-row items (a counter set per kernel).
 // dense_len > 0: the dense (B, heads, S, d) layout with S = dense_len, no offsets.
+// The relative-attention-bias inputs and table-gradient outputs of a
+// backward call (null: no bias).
+struct RabGrads {
+    const int32_t* timestamps;
+    const float* pos_bias;
+    const float* time_bias;
+    int num_pos;
+    int num_time;
+    float* d_pos_bias;
+    float* d_time_bias;
+};
+
 hstu_status_t attn_bwd_call(const void* q, const void* k, const void* v, const void* dout,
                             const int32_t* seq_offsets, const int32_t* num_targets,
                             int32_t num_seqs, int32_t heads, int32_t d, float alpha, float n,
                             void* dq, void* dk, void* dv, hipStream_t stream, int dtype,
-                            int64_t dense_len = 0) {
+                            int64_t dense_len = 0, const RabGrads* rab = nullptr) {
     // (a dense call has no offsets yet: q stands in for the pointer check)
     const int32_t* off_check = dense_len > 0 ? reinterpret_cast<const int32_t*>(q) : seq_offsets;
     hstu_status_t st = check_args(q, k, v, off_check, num_seqs, heads, d, alpha, n, dq, dtype);
@@ -347,10 +359,14 @@ hstu_status_t attn_bwd_call(const void* q, const void* k, const void* v, const v
     Scratch* sc = nullptr;
     const size_t wl_bytes = (hstu::worklist_bytes(num_seqs, heads) + 255) & ~(size_t)255;
     const size_t ramp_bytes = dense_len > 0 ? sizeof(int32_t) * ((size_t)num_seqs + 1) : 0;
-    st = scratch_for(dev, stream, wl_bytes + ramp_bytes, &sc);
+    const size_t part_bytes =
+            rab ? sizeof(float) * (size_t)hstu::RAB_PARTS * hstu::rab_partial_stride(rab->num_pos)
+                : 0;
+    st = scratch_for(dev, stream, wl_bytes + ramp_bytes + part_bytes, &sc);
     if (st != HSTU_OK) return st;
     hstu::WorkList wl = hstu::worklist_carve(sc->ptr, num_seqs, heads);
-    forget_ramp_under(sc, wl_bytes);
+    // (the bias partials follow the work list and overwrite what was there)
+    forget_ramp_under(sc, wl_bytes + part_bytes);
     if (dense_len > 0) {
         st = dense_ramp(sc, wl_bytes, num_seqs, dense_len, stream, &seq_offsets);
         if (st != HSTU_OK) return st;
@@ -378,6 +394,16 @@ hstu_status_t attn_bwd_call(const void* q, const void* k, const void* v, const v
     p.num_targets = num_targets;
     p.dense = dense_len > 0;
     p.dense_len = dense_len;
+    if (rab) {
+        p.timestamps = rab->timestamps;
+        p.pos_bias = rab->pos_bias;
+        p.time_bias = rab->time_bias;
+        p.num_pos = rab->num_pos;
+        p.num_time = rab->num_time;
+        p.d_pos_bias = rab->d_pos_bias;
+        p.d_time_bias = rab->d_time_bias;
+        p.rab_partials = reinterpret_cast<float*>(static_cast<char*>(sc->ptr) + wl_bytes);
+    }
     p.num_seqs = num_seqs;
     p.heads = heads;
     p.d = d;
@@ -576,6 +602,34 @@ hstu_status_t hstu_attn_bwd_targets(const void* q, const void* k, const void* v,
         return HSTU_ERR_INVALID_ARG;
     return attn_bwd_call(q, k, v, dout, seq_offsets, num_targets, num_seqs, heads, d, alpha, n,
                          dq, dk, dv, stream, dtype);
+}
+
+hstu_status_t hstu_attn_bwd_rab(const void* q, const void* k, const void* v, const void* dout,
+                                const int32_t* seq_offsets, const int32_t* timestamps,
+                                const float* pos_bias, int32_t num_pos, const float* time_bias,
+                                int32_t num_time, int32_t num_seqs, int32_t heads, int32_t d,
+                                float alpha, float n, void* dq, void* dk, void* dv,
+                                float* d_pos_bias, float* d_time_bias, hipStream_t stream,
+                                hstu_dtype_t dtype) {
+    if (dtype == HSTU_FP32) return HSTU_ERR_UNSUPPORTED;
+    if (num_pos < 1 || num_pos > (1 << 18) || num_time < 1 || num_time > 32)
+        return HSTU_ERR_INVALID_ARG;
+    if (!(alpha != 0.0f) || !std::isfinite((float)(1.0 / (double)alpha)))
+        return HSTU_ERR_INVALID_ARG;
+    if (num_seqs > 0) {
+        const uintptr_t bad = reinterpret_cast<uintptr_t>(timestamps) |
+                              reinterpret_cast<uintptr_t>(pos_bias) |
+                              reinterpret_cast<uintptr_t>(time_bias) |
+                              reinterpret_cast<uintptr_t>(d_pos_bias) |
+                              reinterpret_cast<uintptr_t>(d_time_bias);
+        if (!timestamps || !pos_bias || !time_bias || !d_pos_bias || !d_time_bias ||
+            (bad & 3u) != 0)
+            return HSTU_ERR_INVALID_ARG;
+    }
+    const RabGrads rab{timestamps, pos_bias, time_bias, num_pos, num_time, d_pos_bias,
+                       d_time_bias};
+    return attn_bwd_call(q, k, v, dout, seq_offsets, nullptr, num_seqs, heads, d, alpha, n, dq,
+                         dk, dv, stream, dtype, 0, &rab);
 }
 
 hstu_status_t hstu_attn_bwd_dense(const void* q, const void* k, const void* v, const void* dout,

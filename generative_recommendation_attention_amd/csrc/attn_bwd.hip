@@ -70,6 +70,60 @@ struct BwdArgs {
     float g_scale;    // alpha / n
 };
 
+// Relative attention bias (the forward's reading: rab(r, c) = wpos[r - c] +
+// wtime[bucket(ts_r - ts_c)], added to alpha <q_r, k_c> before SiLU).  Both
+// kernels recompute it and start the score accumulators at rab / alpha; the
+// dQ kernel, which holds one query per lane and 16 keys per lane in registers,
+// also sums each kept pair's score gradient into the two tables' gradients.
+// (A separate argument type, so that the other kernels keep their argument
+// block.)
+struct BwdArgsRab : BwdArgs {
+    const int32_t* ts;     // token timestamps
+    const float* wpos;
+    const float* wtime;
+    float* gpart;          // [nparts][gstride] table-gradient partials: npos entries, then 32
+    int npos;
+    int ntime;
+    int gstride;
+    int nparts;
+    float bias_scale;      // 1 / alpha
+};
+template <bool RAB> struct BwdArgsOf { using type = BwdArgs; };
+template <> struct BwdArgsOf<true> { using type = BwdArgsRab; };
+
+// Bias staging per slot: the timestamps of the block's 32 streamed rows (64
+// words: one wave load), then RABB_WIN entries of wpos, the distances the
+// block's pairs with the item's 128 rows can take.
+constexpr int RABB_TS = 64;
+constexpr int RABB_WIN = 192;
+constexpr int RABB_WORDS = RABB_TS + RABB_WIN;
+
+// 4-byte load from a raw buffer straight into LDS: lane l's word lands at
+// lds_base + 4*l (lds_base wave-uniform); out-of-range lanes write zero.
+__device__ __forceinline__ void load4_to_lds(__amdgpu_buffer_rsrc_t r, unsigned char* lds_base,
+                                             int voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef __attribute__((address_space(3))) void lds_void;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 4, voffset, 0, 0, 0);
+#else
+    (void)r;
+    (void)lds_base;
+    (void)voffset;
+#endif
+}
+
+// Time table by v_ffbh_u32(gap + 1) + 1 (index 0: a zero argument, gap -1),
+// already capped at the last bucket, as the forward keeps it.
+__device__ __forceinline__ int rab_time_bucket(int idx, int ntime) {
+    return idx == 0 ? ntime - 1 : min(32 - idx, ntime - 1);
+}
+
+__device__ __forceinline__ int ffbh_u32(uint32_t x) {
+    int f;
+    asm("v_ffbh_u32 %0, %1" : "=v"(f) : "v"(x));
+    return f;
+}
+
 // Shapes shared by both kernels: 4 waves of 32 rows (128 rows per item), 32-row
 // streamed blocks.
 template <int D>
@@ -208,19 +262,23 @@ __device__ __forceinline__ void store_rows(uint16_t* base, int rows, int row_byt
 // and the rest are full.  LDS slot: Q (row reads), Q (transposed), dO (row
 // reads), dO (transposed).
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool FUSED, bool TGT>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dkv(BwdArgs a) {
+template <typename T, int D, bool FUSED, bool TGT, bool RAB = false>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkv(typename BwdArgsOf<RAB>::type a) {
     using C = BwdCfg<D>;
     using M = Mfma<T>;
     using v8 = typename M::v8;
     constexpr int SLOT = 4 * C::ARR;
     constexpr int PF = C::PF, NS = PF + 1;
     constexpr int LT = 4 * C::LPA;   // loads per wave per block
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[NS * SLOT];
+    constexpr int RAB_BYTES = RAB ? NS * RABB_WORDS * 4 : 0;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[NS * SLOT + RAB_BYTES];
     __shared__ int s_item[NQ];
     __shared__ LocalTables lt;
+    __shared__ float ttab[RAB ? 33 : 1];
     static_assert(C::NW * 64 >= FUSE_SEQS && C::NW * 64 >= 32 * NQ, "fused tables need a thread per sequence");
-    static_assert(NS * SLOT + (int)sizeof(LocalTables) <= 80 * 1024, "LDS for two workgroups per CU");
+    static_assert(NS * SLOT + RAB_BYTES + (int)sizeof(LocalTables) <= 80 * 1024,
+                  "LDS for two workgroups per CU");
+    static_assert(!RAB || (PF == 1 && !TGT), "bias: one block ahead, causal mask");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -231,6 +289,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv(BwdArgs a) {
     const int64_t row_stride = a.row_stride;
     const int row_bytes = (int)(row_stride * 2);
     const LaneOffsets<D> lo(lane, wv, row_bytes);
+    if constexpr (RAB) {
+        if (tid < 33) ttab[tid] = a.wtime[rab_time_bucket(tid, a.ntime)];
+    }
 
     Tables tb;
     if constexpr (FUSED)
@@ -271,6 +332,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv(BwdArgs a) {
         f32x16 dk[C::NDB], dv[C::NDB];
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) dk[db] = dv[db] = (f32x16){};
+        // With the bias: 1 - ts of this lane's key, so that ts_q + c1 = gap + 1.
+        uint32_t c1 = 0;
+        if constexpr (RAB)
+            c1 = 1u - __builtin_amdgcn_raw_buffer_load_b32(
+                              make_rsrc(a.ts + start + kw0, (int64_t)(s - kw0) * 4), l32 * 4, 0, 0);
 
         // Block c into slot c % NS; blocks are issued PF ahead, also past the
         // last one (an empty buffer range: nothing is read), so that a wait
@@ -283,6 +349,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv(BwdArgs a) {
             stage<D>(qb, row_stride, row0, q_end, row_bytes, sl + C::ARR, lo, true);
             stage<D>(ob, row_stride, row0, q_end, row_bytes, sl + 2 * C::ARR, lo, false);
             stage<D>(ob, row_stride, row0, q_end, row_bytes, sl + 3 * C::ARR, lo, true);
+            if constexpr (RAB) {
+                // wave 0: the block's query timestamps; waves 1-3: wpos at
+                // distances row0 - k0i - 128 + 64 (wv - 1) + lane
+                unsigned char* ra = lds + NS * SLOT + (c % NS) * RABB_WORDS * 4;
+                if (wv == 0)
+                    load4_to_lds(make_rsrc32(a.ts + start + row0, min(q_end - row0, 32) * 4), ra,
+                                 lane * 4);
+                else
+                    load4_to_lds(make_rsrc32(a.wpos, a.npos * 4),
+                                 ra + 4 * RABB_TS + 256 * (wv - 1),
+                                 4 * (row0 - k0i - 128 + 64 * (wv - 1) + lane));
+            }
         };
 #pragma unroll
         for (int c = 0; c < PF; ++c) issue(c);
@@ -295,6 +373,23 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv(BwdArgs a) {
             const bool skip = !live || q0 < kw0 || (TGT && kw0 >= hist && q0 > kw0);
             if (!skip) {
                 f32x16 st = (f32x16){}, dp = (f32x16){};
+                if constexpr (RAB) {
+                    // rab / alpha for query q0 + 8(r/4) + 4g + r%4 and key kw0 + l32:
+                    // distance q - key = window entry 128 - 32wv - l32 + 4g + 8(r/4) + r%4
+                    const unsigned char* ra = lds + NS * SLOT + (c % NS) * RABB_WORDS * 4;
+                    const float* win = reinterpret_cast<const float*>(ra + 4 * RABB_TS) +
+                                       (128 - 32 * wv - l32 + 4 * g);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const u32x4 tq =
+                                *reinterpret_cast<const u32x4*>(ra + 4 * (4 * g + 8 * j));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int f = ffbh_u32(tq[e] + c1);
+                            st[4 * j + e] = (win[8 * j + e] + ttab[f + 1]) * a.bias_scale;
+                        }
+                    }
+                }
 #pragma unroll
                 for (int ks = 0; ks < C::NKS; ++ks) {
                     st = M::mma(row_read<T, D>(sl, lo.rowrd[ks]), kop[ks], st);
@@ -352,18 +447,42 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv(BwdArgs a) {
 // below the workgroup's rows are skipped altogether.  LDS slot: K (row reads),
 // K (transposed), V (row reads).
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool FUSED, bool TGT>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdArgs a) {
+// With the bias, the table gradients: a pair's score gradient (dS / n) goes
+// to the position entry of its distance and to its time bucket.  (LDS float
+// atomics cost on the order of a hundred cycles per instruction here, so the
+// sums avoid them where they can.)
+//  Position: a wave first sums its 32 x 32 block of dS along each diagonal
+//  with cross-lane shuffles (lane l ends with the sums for distances
+//  wr0 - k0 + l and wr0 - k0 + l - 32), then adds them to a 256-entry ring of
+//  its own in LDS
+//  (distance mod 256; plain read-add-write, the wave being its only writer).
+//  A block of keys k0 .. k0+31 touches distances q0 - k0 - 31 .. q0 - k0 + 127
+//  of the item's rows, so once block c is done, distances above
+//  q0 - 32(c+1) + 127 are final for the item: the four rings' entries are
+//  added to the workgroup's partial in global memory.
+//  Time: each lane sums runs of equal (capped) buckets over its keys
+//  (ascending, so with ordered timestamps a run usually spans the block, and
+//  all pairs past the last bucket's gap share it) and adds a run to a
+//  per-workgroup LDS bin when its bucket changes; at the block's end, when
+//  every lane's run has the same bucket, the wave sums the runs first and
+//  one lane adds them.  The bins go to the partial at the end.
+template <typename T, int D, bool FUSED, bool TGT, bool RAB = false>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::type a) {
     using C = BwdCfg<D>;
     using M = Mfma<T>;
     using v8 = typename M::v8;
     constexpr int SLOT = 3 * C::ARR;
     constexpr int PF = C::PF, NS = PF + 1;
     constexpr int LT = 3 * C::LPA;   // loads per wave per block
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[NS * SLOT];
+    constexpr int RAB_BYTES = RAB ? NS * RABB_WORDS * 4 : 0;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[NS * SLOT + RAB_BYTES];
     __shared__ int s_item[NQ];
     __shared__ LocalTables lt;
+    __shared__ float ttab[RAB ? 33 : 1];
+    __shared__ float ring[RAB ? 4 * 256 : 1];   // per wave: position-gradient sums by distance mod 256
+    __shared__ float tbins[RAB ? 32 : 1];        // time-gradient sums by bucket
     static_assert(C::NW * 64 >= FUSE_SEQS && C::NW * 64 >= 32 * NQ, "fused tables need a thread per sequence");
+    static_assert(!RAB || (PF == 1 && !TGT), "bias: one block ahead, causal mask");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -374,6 +493,30 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdArgs a) {
     const int64_t row_stride = a.row_stride;
     const int row_bytes = (int)(row_stride * 2);
     const LaneOffsets<D> lo(lane, wv, row_bytes);
+    float* gpart = nullptr;
+    if constexpr (RAB) {
+        if (tid < 33) ttab[tid] = a.wtime[rab_time_bucket(tid, a.ntime)];
+        if (tid < 32) tbins[tid] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ring[tid + 256 * i] = 0.0f;
+        gpart = a.gpart + (int64_t)(blockIdx.x % a.nparts) * a.gstride;
+    }
+    // Adds the four rings' entries of distances [lo_d, hi_d] (at most 256 of
+    // them) to the partial and clears them; called by every thread between
+    // barriers.
+    auto flush_ring = [&](int lo_d, int hi_d) {
+        if constexpr (RAB) {
+            const int dd = hi_d - tid;
+            if (dd >= lo_d && dd >= 0) {
+                const int e = dd & 255;
+                const float x = ring[e] + ring[256 + e] + ring[512 + e] + ring[768 + e];
+                ring[e] = ring[256 + e] = ring[512 + e] = ring[768 + e] = 0.0f;
+                if (dd < a.npos && x != 0.0f)
+                    __hip_atomic_fetch_add(gpart + dd, x * a.dv_scale, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    };
 
     Tables tb;
     if constexpr (FUSED)
@@ -415,6 +558,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdArgs a) {
         f32x16 dq[C::NDB];
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) dq[db] = (f32x16){};
+        // With the bias: ts of this lane's query + 1.
+        uint32_t trp1 = 0;
+        if constexpr (RAB)
+            trp1 = __builtin_amdgcn_raw_buffer_load_b32(
+                           make_rsrc(a.ts + start + wr0, (int64_t)(s - wr0) * 4), l32 * 4, 0, 0) +
+                   1u;
 
         // (staged PF ahead as in the dK/dV kernel)
         auto issue = [&](int c) {
@@ -423,6 +572,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdArgs a) {
             stage<D>(kb, row_stride, row0, kv_end, row_bytes, sl, lo, false);
             stage<D>(kb, row_stride, row0, kv_end, row_bytes, sl + C::ARR, lo, true);
             stage<D>(vb, row_stride, row0, kv_end, row_bytes, sl + 2 * C::ARR, lo, false);
+            if constexpr (RAB) {
+                // wave 0: the block's key timestamps; waves 1-3: wpos at
+                // distances q0 - row0 - 32 + 64 (wv - 1) + lane
+                unsigned char* ra = lds + NS * SLOT + (c % NS) * RABB_WORDS * 4;
+                if (wv == 0)
+                    load4_to_lds(make_rsrc32(a.ts + start + row0, min(kv_end - row0, 32) * 4), ra,
+                                 lane * 4);
+                else
+                    load4_to_lds(make_rsrc32(a.wpos, a.npos * 4),
+                                 ra + 4 * RABB_TS + 256 * (wv - 1),
+                                 4 * (q0 - row0 - 32 + 64 * (wv - 1) + lane));
+            }
         };
 #pragma unroll
         for (int c = 0; c < PF; ++c) issue(c);
@@ -430,11 +591,30 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdArgs a) {
             __builtin_amdgcn_s_waitcnt(VMCNT_LE((PF - 1) * LT));
             __syncthreads();
             issue(c + PF);
+            // (block c-1 done by every wave: distances only it could touch are final)
+            if (c > 0) flush_ring(q0 - 32 * c + 128, q0 - 32 * c + 159);
             const unsigned char* sl = lds + (c % NS) * SLOT;
             const int k0 = 32 * (c >= nh ? c + jump : c);
             const bool skip = !live || k0 > wr0 || (TGT && k0 >= hist && k0 + 31 < wr0);
             if (!skip) {
                 f32x16 st = (f32x16){}, dp = (f32x16){};
+                u32x4 tk[4];
+                if constexpr (RAB) {
+                    // rab / alpha for query wr0 + l32 and key k0 + 8(r/4) + 4g + r%4:
+                    // distance = window entry 32wv + l32 + 32 - 4g - 8(r/4) - r%4
+                    const unsigned char* ra = lds + NS * SLOT + (c % NS) * RABB_WORDS * 4;
+                    const float* win = reinterpret_cast<const float*>(ra + 4 * RABB_TS) +
+                                       (32 * wv + l32 + 5 - 4 * g);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        tk[j] = *reinterpret_cast<const u32x4*>(ra + 4 * (4 * g + 8 * j));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int f = ffbh_u32(trp1 - tk[j][e]);
+                            st[4 * j + e] = (win[27 - 8 * j - e] + ttab[f + 1]) * a.bias_scale;
+                        }
+                    }
+                }
 #pragma unroll
                 for (int ks = 0; ks < C::NKS; ++ks) {
                     st = M::mma(row_read<T, D>(sl, lo.rowrd[ks]), qop[ks], st);
@@ -454,6 +634,58 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdArgs a) {
                     }
                     ds[r] = dsr;
                 }
+                if constexpr (RAB) {
+                    // distance of register r: wr0 + l32 - k0 - 4g - (8(r/4) + r%4);
+                    // masked pairs add exactly zero
+                    // Diagonal sums: register r of lane (g, l) holds query wr0 + l,
+                    // key k0 + o, o = 8(r/4) + 4g + r%4.  Lane (g, l) takes register
+                    // r from lane (g, (l + o) mod 32): query wr0 + l + o, distance
+                    // wr0 - k0 + l, or, when l + o wraps past 31, query
+                    // wr0 + l + o - 32, distance wr0 - k0 + l - 32.  Every pair is
+                    // taken by exactly one lane.
+                    float dhi = 0.0f, dlo = 0.0f;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int o = 8 * (r >> 2) + 4 * g + (r & 3);
+                        const float x = __shfl(ds[r], 32 * g + ((l32 + o) & 31), 64);
+                        if (l32 + o <= 31)
+                            dhi += x;
+                        else
+                            dlo += x;
+                    }
+                    dhi += __shfl(dhi, l32 + 32, 64);   // the other half's keys
+                    dlo += __shfl(dlo, l32 + 32, 64);
+                    if (g == 0) {
+                        float* rw = ring + 256 * wv;
+                        rw[(wr0 - k0 + l32) & 255] += dhi;
+                        rw[(wr0 - k0 + l32 - 32) & 255] += dlo;
+                    }
+                    // Time buckets: runs of equal buckets along the lane's keys.  The
+                    // capped bucket of v_ffbh_u32 result f is min(31 - f, ntime - 1)
+                    // (f = -1, a gap of -1, gives 32: the last bucket too).
+                    const int cap = a.ntime - 1;
+                    int prev = min(31 - ffbh_u32(trp1 - tk[0][0]), cap);
+                    float run = 0.0f;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int b = min(31 - ffbh_u32(trp1 - tk[r >> 2][r & 3]), cap);
+                        if (b != prev) {
+                            atomicAdd(&tbins[prev], run);
+                            run = 0.0f;
+                            prev = b;
+                        }
+                        run += ds[r];
+                    }
+                    const int p0 = __builtin_amdgcn_readfirstlane(prev);
+                    if (__all(prev == p0)) {
+                        float t = run;
+#pragma unroll
+                        for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o, 64);
+                        if (lane == 0) atomicAdd(&tbins[p0], t);
+                    } else {
+                        atomicAdd(&tbins[prev], run);
+                    }
+                }
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     f32x8 df;
@@ -471,6 +703,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdArgs a) {
         if (live)
             store_rows<T, D>(a.dq + seq_base + (int64_t)wr0 * row_stride, s - wr0, row_bytes, l32,
                              g, dq, a.g_scale);
+        if constexpr (RAB) {
+            // the item's remaining distances: those of its last block
+            // (every ring update of the item is done: the barrier above)
+            const int last = q0 - 32 * (nblk - 1);
+            flush_ring(last - 31, last + 127);
+        }
+    }
+    if constexpr (RAB) {
+        __syncthreads();
+        if (tid < a.ntime && tbins[tid] != 0.0f)
+            __hip_atomic_fetch_add(gpart + a.npos + tid, tbins[tid] * a.dv_scale,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -519,9 +763,95 @@ hipError_t launch_bwd_typed(const BwdParams& p, WorkList wl, hipStream_t stream,
     return hipGetLastError();
 }
 
+// Bias gradients: the partials are zeroed first and summed last.
+__global__ void rab_zero_kernel(float* p, int64_t count) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0.0f;
+}
+
+__global__ void rab_reduce_kernel(const float* gpart, int nparts, int gstride, int npos,
+                                  int ntime, float* dpos, float* dtime) {
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= npos + ntime) return;
+    float acc = 0.0f;   // (position entries, then time buckets at npos + b)
+    for (int w = 0; w < nparts; ++w) acc += gpart[(int64_t)w * gstride + j];
+    if (j < npos)
+        dpos[j] = acc;
+    else
+        dtime[j - npos] = acc;
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_rab(const BwdParams& p, WorkList wl, hipStream_t stream, hipEvent_t start,
+                          hipEvent_t stop) {
+    BwdArgsRab a;
+    a.q = static_cast<const uint16_t*>(p.q);
+    a.k = static_cast<const uint16_t*>(p.k);
+    a.v = static_cast<const uint16_t*>(p.v);
+    a.dout = static_cast<const uint16_t*>(p.dout);
+    a.dq = static_cast<uint16_t*>(p.dq);
+    a.dk = static_cast<uint16_t*>(p.dk);
+    a.dv = static_cast<uint16_t*>(p.dv);
+    a.offsets = p.offsets;
+    a.ntgt = nullptr;
+    a.num_seqs = p.num_seqs;
+    a.heads = p.heads;
+    a.row_stride = (int64_t)p.heads * p.d;
+    a.head_stride = p.d;
+    a.alpha = p.alpha;
+    a.dv_scale = 1.0f / p.n;
+    a.g_scale = p.alpha / p.n;
+    a.ts = p.timestamps;
+    a.wpos = p.pos_bias;
+    a.wtime = p.time_bias;
+    a.gpart = p.rab_partials;
+    a.npos = p.num_pos;
+    a.ntime = p.num_time;
+    a.gstride = rab_partial_stride(p.num_pos);
+    a.nparts = RAB_PARTS;
+    a.bias_scale = (float)(1.0 / (double)p.alpha);
+    using Fn = void (*)(BwdArgsRab);
+    const Fn f_dkv = wl.fused ? attn_bwd_dkv<T, D, true, false, true>
+                              : attn_bwd_dkv<T, D, false, false, true>;
+    const Fn f_dq = wl.fused ? attn_bwd_dq<T, D, true, false, true>
+                             : attn_bwd_dq<T, D, false, false, true>;
+    static int grids[2][2] = {};
+    int& g_dkv = grids[wl.fused ? 1 : 0][0];
+    int& g_dq = grids[wl.fused ? 1 : 0][1];
+    if (!g_dkv) g_dkv = resident_grid(f_dkv, 256);
+    if (!g_dq) g_dq = resident_grid(f_dq, 256);
+    const int64_t cells = (int64_t)RAB_PARTS * a.gstride;
+    hipLaunchKernelGGL(rab_zero_kernel, dim3(256), dim3(256), 0, stream, a.gpart, cells);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.wl = wl;
+    if (start)
+        hipExtLaunchKernelGGL(f_dkv, dim3(g_dkv), dim3(256), 0, stream, start, nullptr, 0, a);
+    else
+        hipLaunchKernelGGL(f_dkv, dim3(g_dkv), dim3(256), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.wl.set = (wl.set + 1) % NSETS;
+    hipLaunchKernelGGL(f_dq, dim3(g_dq), dim3(256), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int n_out = p.num_pos + p.num_time;
+    if (stop)
+        hipExtLaunchKernelGGL(rab_reduce_kernel, dim3((n_out + 255) / 256), dim3(256), 0, stream,
+                              nullptr, stop, 0, (const float*)a.gpart, a.nparts, a.gstride,
+                              p.num_pos, p.num_time, p.d_pos_bias, p.d_time_bias);
+    else
+        hipLaunchKernelGGL(rab_reduce_kernel, dim3((n_out + 255) / 256), dim3(256), 0, stream,
+                           (const float*)a.gpart, a.nparts, a.gstride, p.num_pos, p.num_time,
+                           p.d_pos_bias, p.d_time_bias);
+    return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_bwd_mask(const BwdParams& p, WorkList wl, hipStream_t stream, hipEvent_t start,
                            hipEvent_t stop) {
+    if (p.timestamps) return launch_bwd_rab<T, D>(p, wl, stream, start, stop);
     return p.num_targets ? launch_bwd_typed<T, D, true>(p, wl, stream, start, stop)
                          : launch_bwd_typed<T, D, false>(p, wl, stream, start, stop);
 }
@@ -849,6 +1179,7 @@ hipError_t launch_backward(const BwdParams& p, Dtype dt, WorkList wl, hipStream_
     if (dt == Dtype::FP16)
         return p.d == 64 ? launch_bwd_mask<_Float16, 64>(p, wl, stream, start, stop)
                          : launch_bwd_mask<_Float16, 128>(p, wl, stream, start, stop);
+    if (dt == Dtype::FP32 && p.timestamps) return hipErrorInvalidValue;
     if (dt == Dtype::FP32)
         return p.d == 64 ? launch_bwd_f32<64>(p, wl, stream, start, stop)
                          : launch_bwd_f32<128>(p, wl, stream, start, stop);

@@ -217,12 +217,29 @@ struct BwdParams {
     const int32_t* num_targets;   // candidates per sequence, or null (plain causal)
     bool dense = false;           // dense (B, heads, S, D) layout, S = dense_len
     int64_t dense_len = 0;
+    // Relative attention bias (bf16 / fp16, jagged causal): the forward's
+    // inputs, the tables' gradients (fp32, overwritten) and the partials
+    // buffer (RAB_PARTS * rab_partial_stride(num_pos) floats of scratch).
+    const int32_t* timestamps = nullptr;
+    const float* pos_bias = nullptr;
+    const float* time_bias = nullptr;
+    int num_pos = 0;
+    int num_time = 0;
+    float* d_pos_bias = nullptr;
+    float* d_time_bias = nullptr;
+    float* rab_partials = nullptr;
     int num_seqs;
     int heads;
     int d;
     float alpha;
     float n;
 };
+
+// Table-gradient partials of the bias backward: workgroup w of the dQ kernel
+// adds to partial w % RAB_PARTS (global atomics), so a few workgroups share
+// one; a last kernel sums the partials.
+constexpr int RAB_PARTS = 64;
+inline int rab_partial_stride(int num_pos) { return (num_pos + 32 + 63) / 64 * 64; }
 
 // Enqueues the dK/dV kernel (counter set wl.set) and then the dQ kernel (the
 // next set); each clears one of the two sets after those.  `start` / `stop`,

@@ -260,6 +260,39 @@ hstu_status_t hstu_attn_bwd_targets(const void* q, const void* k, const void* v,
                                     int32_t d, float alpha, float n, void* dq, void* dk,
                                     void* dv, hipStream_t stream, hstu_dtype_t dtype);
 
+/* Backward of hstu_attn_fwd_rab: dq, dk, dv as in hstu_attn_bwd, for the
+ * biased scores x = alpha <q_r, k_c> + rab(r, c), plus the gradients of the
+ * two bias tables (HSTU paper translation, Appendix G: the backward recomputes
+ * the attention and the relative bias and accumulates the bias gradients on
+ * chip).  Per kept pair, with dx = silu'(x) <dout_r, v_c> / n:
+ *
+ *   dq_r += alpha dx k_c,  dk_c += alpha dx q_r,  dv_c += silu(x) / n dout_r
+ *   d_pos_bias[r - c] += dx   (r - c < num_pos)
+ *   d_time_bias[min(floor(log2(ts[r] - ts[c] + 1)), num_time - 1)] += dx
+ *
+ * summed over all sequences and heads.
+ *
+ *   q, k, v, dout, dq, dk, dv, seq_offsets : as in hstu_attn_bwd.
+ *   timestamps, pos_bias, time_bias        : as in hstu_attn_fwd_rab, but
+ *                                            1 <= num_pos <= 2^18.
+ *   d_pos_bias   : device float[num_pos], overwritten, 4-byte aligned.
+ *   d_time_bias  : device float[num_time], overwritten, 4-byte aligned.
+ *
+ * bfloat16 and float16 only (float32 returns HSTU_ERR_UNSUPPORTED).  The table
+ * gradients are sums taken with float atomics: not bitwise reproducible
+ * across calls (dq, dk, dv are).  The call also uses 64 * (num_pos + 32)
+ * floats of library scratch.  A call is four kernels (zeroing the partials,
+ * dk/dv, dq with the table sums, the partials' reduction; plus the work-list
+ * kernel as in hstu_attn_bwd).  Other conventions and errors as in
+ * hstu_attn_fwd_rab and hstu_attn_bwd. */
+hstu_status_t hstu_attn_bwd_rab(const void* q, const void* k, const void* v, const void* dout,
+                                const int32_t* seq_offsets, const int32_t* timestamps,
+                                const float* pos_bias, int32_t num_pos, const float* time_bias,
+                                int32_t num_time, int32_t num_seqs, int32_t heads, int32_t d,
+                                float alpha, float n, void* dq, void* dk, void* dv,
+                                float* d_pos_bias, float* d_time_bias, hipStream_t stream,
+                                hstu_dtype_t dtype);
+
 /* The backward on the dense (batch, heads, seq_len, d) layout of
  * hstu_attn_fwd_dense (causal mask over all seq_len positions); q, k, v, dout,
  * dq, dk, dv all have that layout.  Other conventions as in hstu_attn_bwd. */

@@ -140,6 +140,33 @@ def test_rab_empty_batch_is_a_no_op(lib):
                      out=None, num_seqs=0) == hstu.HSTU_OK
 
 
+def _call_bwd_rab(lib, ts=48, wpos=64, npos=8, wtime=80, ntime=4, gpos=112, gtime=128, **kw):
+    a = dict(q=16, k=16, v=16, dout=144, off=16, num_seqs=1, heads=1, d=64, alpha=0.1, n=1.0,
+             dq=160, dk=176, dv=192, dtype=hstu.HSTU_BF16)
+    a.update(kw)
+    return lib.hstu_attn_bwd_rab(a["q"], a["k"], a["v"], a["dout"], a["off"], ts, wpos, npos,
+                                 wtime, ntime, a["num_seqs"], a["heads"], a["d"], a["alpha"],
+                                 a["n"], a["dq"], a["dk"], a["dv"], gpos, gtime, None, a["dtype"])
+
+
+# (every case has one invalid argument: nothing reaches a device)
+@pytest.mark.parametrize("kw,status", [
+    (dict(ts=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(gpos=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(gtime=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(gtime=130), hstu.HSTU_ERR_INVALID_ARG),   # misaligned table gradient
+    (dict(npos=(1 << 18) + 1), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(ntime=33), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(alpha=0.0), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(dtype=hstu.HSTU_FP32), hstu.HSTU_ERR_UNSUPPORTED),
+    (dict(d=96), hstu.HSTU_ERR_UNSUPPORTED),
+    (dict(dq=16), hstu.HSTU_ERR_INVALID_ARG),       # dq aliases q
+    (dict(dout=None), hstu.HSTU_ERR_INVALID_ARG),
+])
+def test_bwd_rab_argument_checks(lib, kw, status):
+    assert _call_bwd_rab(lib, **kw) == status
+
+
 def _call_cached(lib, kc=64, vc=80, hoff=96, **kw):
     a = dict(q=16, k=16, v=16, off=16, num_seqs=1, heads=1, d=64, alpha=0.1, n=1.0, out=32,
              dtype=hstu.HSTU_BF16)
