@@ -43,3 +43,29 @@ def test_workload_is_deterministic():
     a = workloads.workload(1)
     b = workloads.workload(1)
     assert np.array_equal(a.q, b.q) and np.array_equal(a.v, b.v)
+
+
+def test_rab_inputs_shapes_ranges_and_determinism():
+    off = workloads.offsets_from_lengths([0, 5, 300, 1])
+    a = workloads.make_rab_inputs(off, 40, 12, seed=9)
+    b = workloads.make_rab_inputs(off, 40, 12, seed=9)
+    assert a.timestamps.dtype == np.int32 and a.timestamps.shape == (306,)
+    assert a.pos_bias.dtype == np.float32 and a.pos_bias.shape == (40,)
+    assert a.time_bias.dtype == np.float32 and a.time_bias.shape == (12,)
+    for x, y in ((a.timestamps, b.timestamps), (a.pos_bias, b.pos_bias),
+                 (a.time_bias, b.time_bias)):
+        assert np.array_equal(x, y)
+    # non-decreasing inside each sequence, gaps below 2^16, starts in [0, 2^30)
+    for i in range(len(off) - 1):
+        t = a.timestamps[off[i]:off[i + 1]].astype(np.int64)
+        if len(t):
+            assert 0 <= t[0] < (1 << 30)
+            g = np.diff(t)
+            assert np.all(g >= 0) and np.all(g < (1 << 16))
+
+
+def test_rab_workload_shape():
+    case, r = workloads.rab_workload(values=False)
+    assert case is None
+    assert r.timestamps.shape == (16 * 4096,)
+    assert r.pos_bias.shape == (4096,) and r.time_bias.shape == (16,)
