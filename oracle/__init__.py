@@ -127,6 +127,15 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          f64, f64, vp, vp, i64, vp]
     lib.hstu_oracle_rows_rab.restype = ctypes.c_int
+    lib.hstu_oracle_fwd_rab_targets.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
+                                                ctypes.c_int, vp, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_int, ctypes.c_int, f64, f64, vp]
+    lib.hstu_oracle_fwd_rab_targets.restype = ctypes.c_int
+    lib.hstu_oracle_rows_rab_targets.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
+                                                 ctypes.c_int, vp, ctypes.c_int, ctypes.c_int,
+                                                 ctypes.c_int, ctypes.c_int, f64, f64, vp, vp,
+                                                 i64, vp]
+    lib.hstu_oracle_rows_rab_targets.restype = ctypes.c_int
     lib.hstu_oracle_bwd_rab.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, ctypes.c_int, vp,
                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         f64, f64, vp, vp, vp, vp, vp]
@@ -295,17 +304,21 @@ def _rab_args(q, k, v, offsets, timestamps, pos_bias, time_bias, heads, d, dtype
 
 
 def fwd_rab(q, k, v, offsets, timestamps, pos_bias, time_bias, heads: int, d: int,
-            alpha: float, n: float, dtype: str, lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+            alpha: float, n: float, dtype: str, lib: Optional[ctypes.CDLL] = None,
+            num_targets=None) -> np.ndarray:
     """Full fp64 output (T, heads, d) of the causal forward with the relative
-    attention bias; pos_bias / time_bias are given as the float32 values the
-    GPU call gets (widened exactly)."""
+    attention bias (target-aware mask and candidate positions when
+    num_targets is given); pos_bias / time_bias are given as the float32
+    values the GPU call gets (widened exactly)."""
     lib = lib or load()
     q, k, v, off, ts, wp, wt = _rab_args(q, k, v, offsets, timestamps, pos_bias, time_bias,
                                          heads, d, dtype)
+    tg = _targets(num_targets, len(off) - 1)
     out = np.zeros((int(off[-1]) if len(off) else 0, heads, d), dtype=np.float64)
-    rc = lib.hstu_oracle_fwd_rab(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[dtype], _ptr(off),
-                                 _ptr(ts), _ptr(wp), len(wp), _ptr(wt), len(wt), len(off) - 1,
-                                 heads, d, float(alpha), float(n), _ptr(out))
+    rc = lib.hstu_oracle_fwd_rab_targets(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[dtype],
+                                         _ptr(off), None if tg is None else _ptr(tg), _ptr(ts),
+                                         _ptr(wp), len(wp), _ptr(wt), len(wt), len(off) - 1,
+                                         heads, d, float(alpha), float(n), _ptr(out))
     if rc != 0:
         raise ValueError("oracle rejected the arguments (malformed offsets or sizes)")
     return out
@@ -313,20 +326,22 @@ def fwd_rab(q, k, v, offsets, timestamps, pos_bias, time_bias, heads: int, d: in
 
 def rows_rab(q, k, v, offsets, timestamps, pos_bias, time_bias, heads: int, d: int,
              alpha: float, n: float, dtype: str, tokens, head_ids,
-             lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+             lib: Optional[ctypes.CDLL] = None, num_targets=None) -> np.ndarray:
     """fp64 outputs (m, d) at global tokens[m], heads head_ids[m], of the same."""
     lib = lib or load()
     q, k, v, off, ts, wp, wt = _rab_args(q, k, v, offsets, timestamps, pos_bias, time_bias,
                                          heads, d, dtype)
+    tg = _targets(num_targets, len(off) - 1)
     tok = np.ascontiguousarray(tokens, dtype=np.int64)
     hd = np.ascontiguousarray(head_ids, dtype=np.int32)
     if tok.shape != hd.shape:
         raise ValueError("tokens and head_ids differ in length")
     out = np.zeros((len(tok), d), dtype=np.float64)
-    rc = lib.hstu_oracle_rows_rab(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[dtype], _ptr(off),
-                                  _ptr(ts), _ptr(wp), len(wp), _ptr(wt), len(wt), len(off) - 1,
-                                  heads, d, float(alpha), float(n), _ptr(tok), _ptr(hd),
-                                  len(tok), _ptr(out))
+    rc = lib.hstu_oracle_rows_rab_targets(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[dtype],
+                                          _ptr(off), None if tg is None else _ptr(tg), _ptr(ts),
+                                          _ptr(wp), len(wp), _ptr(wt), len(wt), len(off) - 1,
+                                          heads, d, float(alpha), float(n), _ptr(tok), _ptr(hd),
+                                          len(tok), _ptr(out))
     if rc != 0:
         raise ValueError("oracle rejected the sampled rows")
     return out

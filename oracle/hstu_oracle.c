@@ -72,6 +72,11 @@
  *   rab(r, c) = wpos[r - c] + wtime[min(floor(log2(ts_r - ts_c + 1)), ntime - 1)]
  * with wpos[j] = 0 for j >= npos and a negative gap in the last time bucket,
  * added after alpha: out[r] = (1/n) sum_{c <= r} silu(alpha <q_r, k_c> + rab(r, c)) v_c.
+ * Under the target-aware mask (the *_rab_targets entry points; HSTU paper
+ * translation §3.4: M-FALCON adjusts the mask and rab_{p,t} so that every
+ * candidate of a micro-batch runs the same operations) a candidate row takes
+ * the position right after the history: distance hist - c to a history key
+ * c, and 0 to itself; the time term keeps the real timestamps.
  * Its gradients (the *_bwd_rab entry points) differentiate that definition:
  * per kept pair, dx = silu'(x) <dO_r, v_c> / n with x the biased score;
  * dq_r += alpha dx k_c, dk_c += alpha dx q_r, dv_c += silu(x) / n dO_r, and
@@ -604,10 +609,16 @@ static int time_bucket(int64_t gap, int ntime) {
 
 /* rab(r, c) for local query row r and key c <= r of one sequence whose token
  * timestamps are ts[0..s): a position term, wpos[r - c] (zero for distances
- * of npos and beyond), plus a time term, wtime[bucket(ts[r] - ts[c])]. */
-static double rab_value(int64_t r, int64_t c, const int32_t* ts, const double* wpos, int npos,
-                        const double* wtime, int ntime) {
-    int64_t dist = r - c;
+ * of npos and beyond), plus a time term, wtime[bucket(ts[r] - ts[c])].
+ * Under the target-aware mask (history length hist < s), a candidate row
+ * r >= hist takes the position it would have right after the history:
+ * distance hist - c to a history key, 0 to itself. */
+static double rab_value_hist(int64_t r, int64_t c, int64_t hist, const int32_t* ts,
+                             const double* wpos, int npos, const double* wtime, int ntime) {
+    int64_t dist = r >= hist ? (c == r ? 0 : hist - c) : r - c;
+#if ORACLE_PLANT == 24
+    if (r >= hist) dist = r - c; /* planted: candidates keep their own positions */
+#endif
 #if ORACLE_PLANT == 19
     dist = dist + 1; /* planted: relative position off by one */
 #endif
@@ -615,12 +626,17 @@ static double rab_value(int64_t r, int64_t c, const int32_t* ts, const double* w
     return p + wtime[time_bucket((int64_t)ts[r] - (int64_t)ts[c], ntime)];
 }
 
+static double rab_value(int64_t r, int64_t c, const int32_t* ts, const double* wpos, int npos,
+                        const double* wtime, int ntime) {
+    return rab_value_hist(r, c, INT64_MAX, ts, wpos, npos, wtime, ntime);
+}
+
 /* One output row under the causal mask with the relative attention bias added
  * to the scaled score before SiLU:
  *   out[r] = (1/n) sum_{c <= r} silu(alpha <q_r, k_c> + rab(r, c)) v_c
  * ts points at the sequence's first token's timestamp. */
 static void rab_row(const void* q, const void* k, const void* v, int dtype, int64_t s0,
-                    int64_t r, const int32_t* ts, const double* wpos, int npos,
+                    int64_t r, int64_t hist, const int32_t* ts, const double* wpos, int npos,
                     const double* wtime, int ntime, int heads, int d, int h, double alpha,
                     double n, double* qrow, double* acc) {
     const int64_t row_stride = (int64_t)heads * d;
@@ -629,11 +645,12 @@ static void rab_row(const void* q, const void* k, const void* v, int dtype, int6
         acc[e] = 0.0;
     }
     for (int64_t c = 0; c <= r; ++c) {
+        if (c >= hist && c != r) continue; /* a candidate key is seen by its own row only */
         const int64_t krow = s0 + c;
         double dot = 0.0;
         for (int e = 0; e < d; ++e)
             dot += qrow[e] * load_elem(k, dtype, krow * row_stride + (int64_t)h * d + e);
-        const double bias = rab_value(r, c, ts, wpos, npos, wtime, ntime);
+        const double bias = rab_value_hist(r, c, hist, ts, wpos, npos, wtime, ntime);
 #if ORACLE_PLANT == 18
         const double w = silu(alpha * (dot + bias)); /* planted: bias scaled by alpha */
 #elif ORACLE_PLANT == 21
@@ -652,10 +669,11 @@ static void rab_row(const void* q, const void* k, const void* v, int dtype, int6
  * the bias tables, shared by all heads (fp64 images of the values the GPU
  * call gets).  out is fp64 (T, heads, d).  Returns 0, or -1 on malformed
  * offsets or sizes (npos >= 1, 1 <= ntime <= 32, d <= 1024). */
-int hstu_oracle_fwd_rab(const void* q, const void* k, const void* v, int dtype,
-                        const int32_t* off, const int32_t* ts, const double* wpos, int npos,
-                        const double* wtime, int ntime, int num_seqs, int heads, int d,
-                        double alpha, double n, double* out) {
+int hstu_oracle_fwd_rab_targets(const void* q, const void* k, const void* v, int dtype,
+                                const int32_t* off, const int32_t* ntgt, const int32_t* ts,
+                                const double* wpos, int npos, const double* wtime, int ntime,
+                                int num_seqs, int heads, int d, double alpha, double n,
+                                double* out) {
     if (num_seqs < 0 || heads < 1 || d < 1 || d > 1024) return -1;
     if (npos < 1 || ntime < 1 || ntime > 32 || !offsets_ok(off, num_seqs)) return -1;
     const int64_t row_stride = (int64_t)heads * d;
@@ -667,9 +685,13 @@ int hstu_oracle_fwd_rab(const void* q, const void* k, const void* v, int dtype,
         for (int64_t it = 0; it < items; ++it) {
             int i = (int)(it / heads), h = (int)(it % heads);
             int64_t s0 = off[i], len = (int64_t)off[i + 1] - off[i];
+            int64_t t = ntgt ? ntgt[i] : 0;
+            if (t < 0) t = 0;
+            if (t > len) t = len;
+            const int64_t hist = ntgt ? len - t : INT64_MAX;
             for (int64_t r = 0; r < len; ++r) {
-                rab_row(q, k, v, dtype, s0, r, ts + s0, wpos, npos, wtime, ntime, heads, d, h,
-                        alpha, n, qrow, acc);
+                rab_row(q, k, v, dtype, s0, r, hist, ts + s0, wpos, npos, wtime, ntime, heads, d,
+                        h, alpha, n, qrow, acc);
                 double* o = out + (s0 + r) * row_stride + (int64_t)h * d;
                 for (int e = 0; e < d; ++e) o[e] = acc[e];
             }
@@ -678,13 +700,23 @@ int hstu_oracle_fwd_rab(const void* q, const void* k, const void* v, int dtype,
     return 0;
 }
 
+int hstu_oracle_fwd_rab(const void* q, const void* k, const void* v, int dtype,
+                        const int32_t* off, const int32_t* ts, const double* wpos, int npos,
+                        const double* wtime, int ntime, int num_seqs, int heads, int d,
+                        double alpha, double n, double* out) {
+    return hstu_oracle_fwd_rab_targets(q, k, v, dtype, off, 0, ts, wpos, npos, wtime, ntime,
+                                       num_seqs, heads, d, alpha, n, out);
+}
+
 /* Sampled rows of the same: out_rows[m, 0..d) at global token tok[m], head
- * hd[m].  Returns 0, or -1 on a token or head out of range. */
-int hstu_oracle_rows_rab(const void* q, const void* k, const void* v, int dtype,
-                         const int32_t* off, const int32_t* ts, const double* wpos, int npos,
-                         const double* wtime, int ntime, int num_seqs, int heads, int d,
-                         double alpha, double n, const int64_t* tok, const int32_t* hd,
-                         int64_t count, double* out_rows) {
+ * hd[m].  ntgt as for hstu_oracle_fwd_rab_targets (null: causal).  Returns 0,
+ * or -1 on a token or head out of range. */
+int hstu_oracle_rows_rab_targets(const void* q, const void* k, const void* v, int dtype,
+                                 const int32_t* off, const int32_t* ntgt, const int32_t* ts,
+                                 const double* wpos, int npos, const double* wtime, int ntime,
+                                 int num_seqs, int heads, int d, double alpha, double n,
+                                 const int64_t* tok, const int32_t* hd, int64_t count,
+                                 double* out_rows) {
     if (num_seqs < 1 || heads < 1 || d < 1 || d > 1024) return -1;
     if (npos < 1 || ntime < 1 || ntime > 32 || !offsets_ok(off, num_seqs)) return -1;
     int64_t T = off[num_seqs];
@@ -700,12 +732,25 @@ int hstu_oracle_rows_rab(const void* q, const void* k, const void* v, int dtype,
                 int mid = (lo + hi + 1) / 2;
                 if (off[mid] <= tok[m]) lo = mid; else hi = mid - 1;
             }
-            const int64_t s0 = off[lo];
-            rab_row(q, k, v, dtype, s0, tok[m] - s0, ts + s0, wpos, npos, wtime, ntime, heads, d,
-                    hd[m], alpha, n, qrow, out_rows + m * (int64_t)d);
+            const int64_t s0 = off[lo], len = (int64_t)off[lo + 1] - off[lo];
+            int64_t t = ntgt ? ntgt[lo] : 0;
+            if (t < 0) t = 0;
+            if (t > len) t = len;
+            const int64_t hist = ntgt ? len - t : INT64_MAX;
+            rab_row(q, k, v, dtype, s0, tok[m] - s0, hist, ts + s0, wpos, npos, wtime, ntime,
+                    heads, d, hd[m], alpha, n, qrow, out_rows + m * (int64_t)d);
         }
     }
     return 0;
+}
+
+int hstu_oracle_rows_rab(const void* q, const void* k, const void* v, int dtype,
+                         const int32_t* off, const int32_t* ts, const double* wpos, int npos,
+                         const double* wtime, int ntime, int num_seqs, int heads, int d,
+                         double alpha, double n, const int64_t* tok, const int32_t* hd,
+                         int64_t count, double* out_rows) {
+    return hstu_oracle_rows_rab_targets(q, k, v, dtype, off, 0, ts, wpos, npos, wtime, ntime,
+                                        num_seqs, heads, d, alpha, n, tok, hd, count, out_rows);
 }
 
 /* Gradient terms of one kept pair (r, c) of a sequence with the relative

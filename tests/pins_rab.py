@@ -184,3 +184,83 @@ def pin_rab_rows_match(lib) -> None:
 RAB_PINS = [pin_rab_hand_worked, pin_rab_constant_bias_is_one_more_dimension,
             pin_rab_linear_position_is_two_more_dimensions, pin_rab_time_buckets_by_float_log2,
             pin_rab_zero_tables_is_plain, pin_rab_relative_only, pin_rab_rows_match]
+
+
+# ---- the bias under the target-aware mask (M-FALCON) ----------------------
+# HSTU paper translation §3.4: M-FALCON changes the mask and rab_{p,t} so that
+# the candidates of a micro-batch all run the same operations.  Reading: a
+# candidate takes the position right after the history (distance hist - c to
+# a history key, 0 to itself); timestamps stay its own.
+
+def _targets_case(seed):
+    lens, tgts = [9, 12, 5, 1], [3, 0, 5, 1]
+    case = workloads.make_case(lens, 2, 64, "fp32", seed=seed, n=12.0)
+    r = workloads.make_rab_inputs(case.offsets, 10, 8, seed=seed + 1)
+    return case, r, np.array(tgts, np.int32)
+
+
+def pin_rab_targets_candidate_is_history_plus_itself(lib) -> None:
+    """Algorithm 1's equivalence: each candidate's row equals the last row of
+    the causal bias forward over the history followed by that candidate alone
+    (placed at position hist)."""
+    case, r, tg = _targets_case(301)
+    got = oracle.fwd_rab(case.q, case.k, case.v, case.offsets, r.timestamps, r.pos_bias,
+                         r.time_bias, 2, 64, case.alpha, case.n, "fp32", lib=lib, num_targets=tg)
+    checked = 0
+    for i in range(case.num_seqs):
+        a, b = int(case.offsets[i]), int(case.offsets[i + 1])
+        hist = (b - a) - int(tg[i])
+        for row in range(a + hist, b):
+            idx = list(range(a, a + hist)) + [row]
+            one = oracle.fwd_rab(case.q[idx], case.k[idx], case.v[idx], [0, hist + 1],
+                                 r.timestamps[idx], r.pos_bias, r.time_bias, 2, 64, case.alpha,
+                                 case.n, "fp32", lib=lib)
+            assert np.allclose(got[row], one[hist], rtol=0, atol=1e-14), (i, row)
+            checked += 1
+    assert checked == 9
+
+
+def pin_rab_targets_candidate_order(lib) -> None:
+    """Reordering a sequence's candidates (their q, k, v and timestamps)
+    reorders their outputs and changes nothing else."""
+    case, r, tg = _targets_case(311)
+    base = oracle.fwd_rab(case.q, case.k, case.v, case.offsets, r.timestamps, r.pos_bias,
+                          r.time_bias, 2, 64, case.alpha, case.n, "fp32", lib=lib,
+                          num_targets=tg)
+    perm = np.arange(case.total)
+    a, b = int(case.offsets[2]), int(case.offsets[3])   # 5 tokens, all candidates
+    perm[a:b] = perm[a:b][::-1]
+    a, b = int(case.offsets[0]), int(case.offsets[1])   # 9 tokens, the last 3 candidates
+    perm[b - 3:b] = perm[b - 3:b][[2, 0, 1]]
+    got = oracle.fwd_rab(case.q[perm], case.k[perm], case.v[perm], case.offsets,
+                         r.timestamps[perm], r.pos_bias, r.time_bias, 2, 64, case.alpha, case.n,
+                         "fp32", lib=lib, num_targets=tg)
+    assert np.allclose(got, base[perm], rtol=0, atol=1e-14)
+
+
+def pin_rab_targets_without_candidates_is_causal(lib) -> None:
+    """No candidates: the causal bias forward."""
+    case, r, _ = _targets_case(321)
+    got = oracle.fwd_rab(case.q, case.k, case.v, case.offsets, r.timestamps, r.pos_bias,
+                         r.time_bias, 2, 64, case.alpha, case.n, "fp32", lib=lib,
+                         num_targets=np.zeros(4, np.int32))
+    ref = oracle.fwd_rab(case.q, case.k, case.v, case.offsets, r.timestamps, r.pos_bias,
+                         r.time_bias, 2, 64, case.alpha, case.n, "fp32", lib=lib)
+    assert np.array_equal(got, ref)
+
+
+def pin_rab_targets_rows_match(lib) -> None:
+    case, r, tg = _targets_case(331)
+    full = oracle.fwd_rab(case.q, case.k, case.v, case.offsets, r.timestamps, r.pos_bias,
+                          r.time_bias, 2, 64, case.alpha, case.n, "fp32", lib=lib,
+                          num_targets=tg)
+    toks = np.arange(case.total, dtype=np.int64)
+    hds = (toks % 2).astype(np.int32)
+    got = oracle.rows_rab(case.q, case.k, case.v, case.offsets, r.timestamps, r.pos_bias,
+                          r.time_bias, 2, 64, case.alpha, case.n, "fp32", toks, hds, lib=lib,
+                          num_targets=tg)
+    assert np.array_equal(got, full[toks, hds])
+
+
+RAB_PINS += [pin_rab_targets_candidate_is_history_plus_itself, pin_rab_targets_candidate_order,
+             pin_rab_targets_without_candidates_is_causal, pin_rab_targets_rows_match]

@@ -1,7 +1,8 @@
-"""The oracle's relative-attention-bias form against its pins, and the four
+"""The oracle's relative-attention-bias form against its pins, and the five
 planted mistakes of that form (ORACLE_PLANT=18: bias scaled by alpha; 19:
 relative position off by one; 20: time bucket of log2(gap) instead of
-log2(gap + 1); 21: bias added after SiLU) each caught by at least two pins."""
+log2(gap + 1); 21: bias added after SiLU; 24: candidates keep their own
+positions under the target-aware mask) each caught by at least two pins."""
 import os
 
 import pytest
@@ -16,7 +17,8 @@ def test_rab_pin(pin):
 
 
 PLANTS = {18: "bias scaled by alpha", 19: "relative position off by one",
-          20: "time bucket of log2(gap)", 21: "bias added after SiLU"}
+          20: "time bucket of log2(gap)", 21: "bias added after SiLU",
+          24: "candidates keep their own positions"}
 
 
 @pytest.mark.parametrize("plant", sorted(PLANTS), ids=lambda p: PLANTS[p])
