@@ -55,6 +55,8 @@ METRIC_DENSE = "HSTU attn fwd useful TFLOP/s, dense (b, heads, s, d) layout"
 METRIC_BWD = "HSTU attn bwd (dq, dk, dv) useful TFLOP/s"
 METRIC_CACHED = "HSTU cached-history attn fwd useful TFLOP/s (M-FALCON micro-batch)"
 METRIC_RAB = "HSTU attn fwd with relative attention bias useful TFLOP/s"
+METRIC_RAB_TARGETS = ("HSTU target-aware attn fwd with relative attention bias useful TFLOP/s "
+                      "(M-FALCON mask and bias)")
 METRIC_RAB_BWD = "HSTU attn bwd with relative attention bias (dq, dk, dv, table gradients) useful TFLOP/s"
 # HBM traffic per dispatch of the attention kernel, from two rocprofv3 --pmc
 # runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
@@ -192,7 +194,7 @@ def cpu_baseline(case, budget_s: float, rab=None):
         if rab is not None:
             oracle.fwd_rab(case.q[a:b], case.k[a:b], case.v[a:b], sub, rab.timestamps[a:b],
                            rab.pos_bias, rab.time_bias, case.heads, case.d, case.alpha, case.n,
-                           case.dtype, lib=lib)
+                           case.dtype, lib=lib, num_targets=tg)
         else:
             oracle.fwd(case.q[a:b], case.k[a:b], case.v[a:b], sub, case.heads, case.d,
                        case.alpha, case.n, case.dtype, lib=lib, num_targets=tg)
@@ -321,7 +323,9 @@ def main() -> int:
                          "1024 candidates)")
     ap.add_argument("--rab", action="store_true",
                     help="time the forward with the relative attention bias on 16 x 4096 "
-                         "(a position entry per distance, 16 time buckets)")
+                         "(a position entry per distance, 16 time buckets); with --targets, "
+                         "the target-aware forward with the bias on the --targets workload; "
+                         "with --backward, the backward with the bias")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibrate", action="store_true",
@@ -329,9 +333,9 @@ def main() -> int:
                          "scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     modes = args.targets + args.cached + args.backward + args.dense + args.layer + args.rab
-    if modes > 1 and not (modes == 2 and args.backward and args.rab):
+    if modes > 1 and not (modes == 2 and args.rab and (args.backward or args.targets)):
         ap.error("--targets, --cached, --backward, --dense, --layer and --rab are separate "
-                 "benchmarks (except --backward --rab)")
+                 "benchmarks (except --backward --rab and --targets --rab)")
     if args.layer:
         return bench_layer(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -357,6 +361,8 @@ def main() -> int:
     if args.cached:
         cc = workloads.cached_workload()
         case = cc.cand
+    elif args.rab and args.targets:
+        case, rab = workloads.rab_targets_workload()
     elif args.rab:
         case, rab = workloads.rab_workload()
     elif args.targets:
@@ -385,9 +391,16 @@ def main() -> int:
         wp = torch.from_numpy(rab.pos_bias).cuda()
         wt = torch.from_numpy(rab.time_bias).cuda()
         alg_bytes += 4.0 * case.total + 4.0 * (rab.pos_bias.size + rab.time_bias.size)
+        if args.targets:
+            tg = torch.from_numpy(case.num_targets.astype(np.int32)).cuda()
+            alg_bytes += 4.0 * case.num_seqs
 
-        def call():
-            hstu.hstu_attn_fwd_rab(q, k, v, off, ts, wp, wt, case.alpha, case.n, out=out)
+            def call():
+                hstu.hstu_attn_fwd_rab_targets(q, k, v, off, tg, ts, wp, wt, case.alpha, case.n,
+                                               out=out)
+        else:
+            def call():
+                hstu.hstu_attn_fwd_rab(q, k, v, off, ts, wp, wt, case.alpha, case.n, out=out)
     elif args.targets:
         tg = torch.from_numpy(case.num_targets.astype(np.int32)).cuda()
 
@@ -478,7 +491,9 @@ def main() -> int:
     plain_w2 = (args.workload == 2 and not (args.targets or args.cached or args.backward or
                                             args.dense or args.rab))
     line = {
-        "metric": (METRIC_CACHED if args.cached else METRIC_TARGETS if args.targets else
+        "metric": (METRIC_CACHED if args.cached else
+                   METRIC_RAB_TARGETS if args.targets and args.rab else
+                   METRIC_TARGETS if args.targets else
                    METRIC_RAB_BWD if args.backward and args.rab else
                    METRIC_BWD if args.backward else METRIC_DENSE if args.dense else
                    METRIC_RAB if args.rab else METRIC),

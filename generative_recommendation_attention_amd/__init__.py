@@ -13,7 +13,8 @@ seq_offsets: int32 CUDA tensor [num_seqs + 1] of prefix sums.
 
 Also: hstu_attn_fwd_{bf16,fp16,fp32} (type fixed), hstu_attn_fwd_targets
 (target-aware mask), hstu_attn_fwd_rab / hstu_attn_bwd_rab (relative
-attention bias),
+attention bias), hstu_attn_fwd_rab_targets (the bias under the target-aware
+mask),
 hstu_attn_fwd_cached (candidates against a cached history),
 hstu_attn_fwd_dense / hstu_attn_bwd_dense ((B, heads, S, d) tensors),
 hstu_attn_bwd (dq, dk, dv), hstu_layer_in_proj /
@@ -44,7 +45,7 @@ HSTU_BF16, HSTU_FP16, HSTU_FP32 = 0, 1, 2
 # Every symbol include/hstu.h declares.
 EXPORTS = ("hstu_attn_fwd", "hstu_attn_fwd_bf16", "hstu_attn_fwd_fp16", "hstu_attn_fwd_fp32",
            "hstu_attn_fwd_targets", "hstu_attn_fwd_cached", "hstu_attn_fwd_dense",
-           "hstu_attn_fwd_rab", "hstu_attn_bwd_rab", "hstu_attn_bwd",
+           "hstu_attn_fwd_rab", "hstu_attn_fwd_rab_targets", "hstu_attn_bwd_rab", "hstu_attn_bwd",
            "hstu_attn_bwd_dense", "hstu_layer_in_proj", "hstu_layer_out_proj",
            "hstu_attn_bwd_targets", "hstu_validate_offsets", "hstu_status_string", "hstu_last_hip_error",
            "hstu_release_workspace", "hstu_profile_enable", "hstu_profile_read")
@@ -98,6 +99,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hstu_attn_fwd_rab.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, f32,
                                       f32, vp, vp, ctypes.c_int]
     lib.hstu_attn_fwd_rab.restype = ctypes.c_int
+    lib.hstu_attn_fwd_rab_targets.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32,
+                                              i32, f32, f32, vp, vp, ctypes.c_int]
+    lib.hstu_attn_fwd_rab_targets.restype = ctypes.c_int
     lib.hstu_attn_bwd_rab.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, f32,
                                       f32, vp, vp, vp, vp, vp, vp, ctypes.c_int]
     lib.hstu_attn_bwd_rab.restype = ctypes.c_int
@@ -198,15 +202,9 @@ def hstu_attn_fwd_rab(q, k, v, seq_offsets, timestamps, pos_bias, time_bias, alp
     len(time_bias) - 1)] added to alpha * <q_r, k_c> before SiLU.
     timestamps: int32 GPU tensor of T entries; pos_bias, time_bias: float32
     GPU tensors (the time table holds 1 to 32 entries)."""
-    import torch
     out = _check_tensors(q, k, v, seq_offsets, out)
     T, heads, d = q.shape
-    if (timestamps.dtype != torch.int32 or timestamps.shape != (T,) or not timestamps.is_cuda or
-            not timestamps.is_contiguous()):
-        raise ValueError("timestamps must be a contiguous int32 GPU tensor of T entries")
-    for name, t in (("pos_bias", pos_bias), ("time_bias", time_bias)):
-        if t.dtype != torch.float32 or t.dim() != 1 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous 1-D float32 GPU tensor")
+    _check_rab(T, timestamps, pos_bias, time_bias)
     num_seqs = seq_offsets.numel() - 1
     lib = load_library()
     st = lib.hstu_attn_fwd_rab(q.data_ptr(), k.data_ptr(), v.data_ptr(), seq_offsets.data_ptr(),
@@ -218,18 +216,55 @@ def hstu_attn_fwd_rab(q, k, v, seq_offsets, timestamps, pos_bias, time_bias, alp
     return out
 
 
+def _check_rab(T, timestamps, pos_bias, time_bias):
+    import torch
+    if (timestamps.dtype != torch.int32 or timestamps.shape != (T,) or not timestamps.is_cuda or
+            not timestamps.is_contiguous()):
+        raise ValueError("timestamps must be a contiguous int32 GPU tensor of T entries")
+    for name, t in (("pos_bias", pos_bias), ("time_bias", time_bias)):
+        if t.dtype != torch.float32 or t.dim() != 1 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 1-D float32 GPU tensor")
+
+
+def _check_targets(num_targets, num_seqs):
+    import torch
+    if (num_targets.dtype != torch.int32 or num_targets.dim() != 1 or
+            num_targets.numel() != num_seqs or not num_targets.is_cuda or
+            not num_targets.is_contiguous()):
+        raise ValueError("num_targets must be a contiguous 1-D int32 GPU tensor of num_seqs entries")
+
+
+def hstu_attn_fwd_rab_targets(q, k, v, seq_offsets, num_targets, timestamps, pos_bias, time_bias,
+                              alpha: float, n: float, out=None, stream=None):
+    """hstu_attn_fwd_rab under the target-aware mask of hstu_attn_fwd_targets
+    (M-FALCON): a candidate row takes the position right after its sequence's
+    history (distance hist - c to history key c, 0 to itself) and keeps its
+    own timestamp, so each candidate's output is that of the history followed
+    by that candidate alone."""
+    out = _check_tensors(q, k, v, seq_offsets, out)
+    T, heads, d = q.shape
+    num_seqs = seq_offsets.numel() - 1
+    _check_targets(num_targets, num_seqs)
+    _check_rab(T, timestamps, pos_bias, time_bias)
+    lib = load_library()
+    st = lib.hstu_attn_fwd_rab_targets(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                       seq_offsets.data_ptr(), num_targets.data_ptr(),
+                                       timestamps.data_ptr(), pos_bias.data_ptr(),
+                                       pos_bias.numel(), time_bias.data_ptr(), time_bias.numel(),
+                                       num_seqs, heads, d, float(alpha), float(n), out.data_ptr(),
+                                       _stream_handle(stream), _dtype_code(q))
+    _check(st, "hstu_attn_fwd_rab_targets")
+    return out
+
+
 def hstu_attn_fwd_targets(q, k, v, seq_offsets, num_targets, alpha: float, n: float, out=None,
                           stream=None):
     """HSTU attention forward under the target-aware mask: the last
     num_targets[i] tokens of sequence i are candidates that see the history
     and themselves only.  num_targets: int32 device tensor of num_seqs entries."""
-    import torch
     out = _check_tensors(q, k, v, seq_offsets, out)
     num_seqs = seq_offsets.numel() - 1
-    if (num_targets.dtype != torch.int32 or num_targets.dim() != 1 or
-            num_targets.numel() != num_seqs or not num_targets.is_cuda or
-            not num_targets.is_contiguous()):
-        raise ValueError("num_targets must be a contiguous 1-D int32 GPU tensor of num_seqs entries")
+    _check_targets(num_targets, num_seqs)
     T, heads, d = q.shape
     lib = load_library()
     st = lib.hstu_attn_fwd_targets(q.data_ptr(), k.data_ptr(), v.data_ptr(),

@@ -457,12 +457,11 @@ hstu_status_t hstu_attn_fwd_targets(const void* q, const void* k, const void* v,
                          dtype);
 }
 
-hstu_status_t hstu_attn_fwd_rab(const void* q, const void* k, const void* v,
-                                const int32_t* seq_offsets, const int32_t* timestamps,
-                                const float* pos_bias, int32_t num_pos, const float* time_bias,
-                                int32_t num_time, int32_t num_seqs, int32_t heads, int32_t d,
-                                float alpha, float n, void* out, hipStream_t stream,
-                                hstu_dtype_t dtype) {
+// The bias inputs of a forward call, checked (num_seqs > 0: non-null and
+// 4-byte aligned tables and timestamps).
+static hstu_status_t rab_inputs(const int32_t* timestamps, const float* pos_bias,
+                                int32_t num_pos, const float* time_bias, int32_t num_time,
+                                int32_t num_seqs, float alpha, MaskInputs* mi) {
     if (num_pos < 1 || num_pos > (1 << 28) || num_time < 1 || num_time > 32)
         return HSTU_ERR_INVALID_ARG;
     // The kernels carry the bias in units of the raw score (rab / alpha).
@@ -474,12 +473,42 @@ hstu_status_t hstu_attn_fwd_rab(const void* q, const void* k, const void* v,
                               reinterpret_cast<uintptr_t>(time_bias);
         if (!timestamps || !pos_bias || !time_bias || (bad & 3u) != 0) return HSTU_ERR_INVALID_ARG;
     }
+    mi->timestamps = timestamps;
+    mi->pos_bias = pos_bias;
+    mi->time_bias = time_bias;
+    mi->num_pos = num_pos;
+    mi->num_time = num_time;
+    return HSTU_OK;
+}
+
+hstu_status_t hstu_attn_fwd_rab(const void* q, const void* k, const void* v,
+                                const int32_t* seq_offsets, const int32_t* timestamps,
+                                const float* pos_bias, int32_t num_pos, const float* time_bias,
+                                int32_t num_time, int32_t num_seqs, int32_t heads, int32_t d,
+                                float alpha, float n, void* out, hipStream_t stream,
+                                hstu_dtype_t dtype) {
     MaskInputs mi;
-    mi.timestamps = timestamps;
-    mi.pos_bias = pos_bias;
-    mi.time_bias = time_bias;
-    mi.num_pos = num_pos;
-    mi.num_time = num_time;
+    const hstu_status_t st =
+            rab_inputs(timestamps, pos_bias, num_pos, time_bias, num_time, num_seqs, alpha, &mi);
+    if (st != HSTU_OK) return st;
+    return attn_fwd_call(q, k, v, seq_offsets, mi, num_seqs, heads, d, alpha, n, out, stream,
+                         dtype);
+}
+
+hstu_status_t hstu_attn_fwd_rab_targets(const void* q, const void* k, const void* v,
+                                        const int32_t* seq_offsets, const int32_t* num_targets,
+                                        const int32_t* timestamps, const float* pos_bias,
+                                        int32_t num_pos, const float* time_bias,
+                                        int32_t num_time, int32_t num_seqs, int32_t heads,
+                                        int32_t d, float alpha, float n, void* out,
+                                        hipStream_t stream, hstu_dtype_t dtype) {
+    if (num_seqs > 0 && (!num_targets || (reinterpret_cast<uintptr_t>(num_targets) & 3u) != 0))
+        return HSTU_ERR_INVALID_ARG;
+    MaskInputs mi;
+    const hstu_status_t st =
+            rab_inputs(timestamps, pos_bias, num_pos, time_bias, num_time, num_seqs, alpha, &mi);
+    if (st != HSTU_OK) return st;
+    mi.num_targets = num_targets;
     return attn_fwd_call(q, k, v, seq_offsets, mi, num_seqs, heads, d, alpha, n, out, stream,
                          dtype);
 }

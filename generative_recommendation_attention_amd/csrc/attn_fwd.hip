@@ -89,7 +89,11 @@ struct KernelArgsRab : KernelArgs {
 //           that hist.  Zero keys and values add exactly nothing.
 //  RAB    : CAUSAL, with the relative attention bias added to every score
 //           before SiLU (below).
-enum : int { MASK_CAUSAL = 0, MASK_TARGETS = 1, MASK_CACHED = 2, MASK_RAB = 3 };
+//  RAB_TGT: TARGETS with the bias; M-FALCON (HSTU paper translation, §3.4)
+//           adjusts the bias with the mask: a candidate row takes position
+//           hist, so its distance to history key c is hist - c and to itself
+//           0, while its time gaps use its own timestamp.
+enum : int { MASK_CAUSAL = 0, MASK_TARGETS = 1, MASK_CACHED = 2, MASK_RAB = 3, MASK_RAB_TGT = 4 };
 
 // Relative attention bias (HSTU paper translation, §3 and Appendix G: a bias
 // merging relative position and time, built inside the operator from its
@@ -161,11 +165,12 @@ struct Tile16 {
 // causal form carries none of the other modes' registers.
 template <int MASK> struct ArgsOf { using type = KernelArgs; };
 template <> struct ArgsOf<MASK_RAB> { using type = KernelArgsRab; };
+template <> struct ArgsOf<MASK_RAB_TGT> { using type = KernelArgsRab; };
 
 template <typename T, int D, int NW, int QB, int BK, int PF, bool FUSED, int MASK>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MASK>::type a) {
-    constexpr bool TGT = MASK == MASK_TARGETS || MASK == MASK_CACHED;   // hist-based mask
-    constexpr bool RAB = MASK == MASK_RAB;
+    constexpr bool TGT = MASK == MASK_TARGETS || MASK == MASK_CACHED || MASK == MASK_RAB_TGT;
+    constexpr bool RAB = MASK == MASK_RAB || MASK == MASK_RAB_TGT;   // (TGT: hist-based mask)
     using Cfg = Tile16<T, D, NW, QB, BK, PF>;
     using M = Mfma<T>;
     using v8 = typename M::v8;
@@ -182,6 +187,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
     constexpr int RAB_BYTES = RAB ? Cfg::NSLOT * NW * Cfg::RAB_WORDS * 4 : 0;
     static_assert(!RAB || (PF == 2 && Cfg::RAB_WIN % 64 == 0 && BK <= 64),
                   "bias staging: one tile ahead, whole-wave window loads");
+    static_assert(MASK != MASK_RAB_TGT || QB == 1, "candidate rows: one lane base per item");
     static_assert(Cfg::LDS_BYTES + RAB_BYTES <= 65536, "LDS reads use 16-bit immediate offsets");
     __shared__ __attribute__((aligned(1024))) unsigned char lds[Cfg::LDS_BYTES + RAB_BYTES];
     __shared__ int s_item[NQ];
@@ -268,7 +274,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
         // by every later row (s for the causal mask); shift: virtual row of
         // the first query row.
         int s = len, hist = len, shift = 0, hstart = 0, hlen = 0;
-        if constexpr (MASK == MASK_TARGETS)
+        if constexpr (MASK == MASK_TARGETS || MASK == MASK_RAB_TGT)
             hist = len - min(max(__builtin_amdgcn_readfirstlane(a.ntgt[seq]), 0), len);
         if constexpr (MASK == MASK_CACHED) {
             hstart = __builtin_amdgcn_readfirstlane(a.hoff[seq]);
@@ -344,18 +350,30 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
         // written to this wave's area of the tile's slot one barrier later.
         uint32_t rab_ts = 0, trp1[QB];
         float rab_w[RAB ? Cfg::RAB_WIN / 64 : 1];
+        // The bias sees a candidate row (row >= hist) at position hist, so
+        // the window follows the effective rows min(row, hist): the wave's
+        // first one, and the lane's lead over it (row - wr0 when causal).
+        const int wr_eff0 = TGT ? min(wr0, hist) : wr0;
+        const int rab_wb_it = TGT ? rab_wb + 4 * (min(wr0 + l32, hist) - wr_eff0 - l32) : rab_wb;
         auto issue_rab = [&](int c) {
             if constexpr (RAB) {
-                const int k0 = c * BK;
+                const int k0 = (TGT && c >= nh ? c + jump : c) * BK;
                 rab_ts = __builtin_amdgcn_raw_buffer_load_b32(
                         make_rsrc32(a.ts + start + k0, min(kv_end - k0, BK) * 4), lane * 4, 0, 0);
                 const __amdgpu_buffer_rsrc_t rp = make_rsrc32(a.wpos, a.npos * 4);
-                const int jw0 = wr0 - k0 - BK;   // negative entries read as zero
+                // Negative distances belong to masked pairs only (they read
+                // as zero), except under the target-aware mask, where a
+                // candidate's own key, at distance hist - row <= 0 from the
+                // row's effective position hist, takes distance 0: there they
+                // read wpos[0].
+                const int jw0 = wr_eff0 - k0 - BK;
 #pragma unroll
                 for (int u = 0; u < Cfg::RAB_WIN / 64; ++u)
                     rab_w[u] = __builtin_bit_cast(
                             float, __builtin_amdgcn_raw_buffer_load_b32(
-                                           rp, 4 * (jw0 + lane + 64 * u), 0, 0));
+                                           rp, 4 * (TGT ? max(jw0 + lane + 64 * u, 0)
+                                                        : jw0 + lane + 64 * u),
+                                           0, 0));
             }
         };
         auto rab_store = [&](int c) {
@@ -415,7 +433,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
                     for (int r = 0; r < 16; ++r) {
                         const int o = 32 * kb + 8 * (r >> 2) + (r & 3);
                         const float bp = *reinterpret_cast<const float*>(
-                                ra + rab_wb + 4 * (32 * qb + RAB_CMAX - o));
+                                ra + rab_wb_it + 4 * (32 * qb + RAB_CMAX - o));
                         const uint32_t x = trp1[qb] - tk[r >> 2][r & 3];
                         int f;
                         asm("v_ffbh_u32 %0, %1" : "=v"(f) : "v"(x));
@@ -846,7 +864,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
                         float p;
                         if (a.ts) {
                             const int key = k0 + kvl;
-                            const int dist = my_row - key;
+                            // (a candidate row sits at position hist; its own
+                            // key at distance 0)
+                            const int dist = key == my_row ? 0 : min(my_row, hist) - key;
                             float bias = (dist >= 0 && dist < a.npos) ? a.wpos[dist] : 0.0f;
                             const uint32_t x = trp1 - (key < s ? (uint32_t)a.ts[start + key] : 0u);
                             const int lz = __clz((int)x);   // 32 for x == 0 (gap -1)
@@ -898,7 +918,8 @@ template <int D> struct QBlocks { static constexpr int value = D == 64 ? 2 : 1; 
 // does the relative-attention-bias form, whose bias terms need the registers
 // a second block would take.
 template <int D, int MASK> struct QBlocksFor {
-    static constexpr int value = MASK == MASK_CACHED || MASK == MASK_RAB ? 1 : QBlocks<D>::value;
+    static constexpr int value =
+            MASK == MASK_CACHED || MASK == MASK_RAB || MASK == MASK_RAB_TGT ? 1 : QBlocks<D>::value;
 };
 template <int D> struct KeyTile { static constexpr int value = D == 64 ? 64 : 32; };
 template <int D> struct Prefetch { static constexpr int value = 2; };
@@ -937,11 +958,18 @@ hipError_t launch16(const FwdParams& p, WorkList wl, int grid, hipStream_t strea
         ar.ntime = p.num_time;
         ar.bias_scale = (float)(1.0 / (double)p.alpha);
         constexpr int QBR = QBlocksFor<D, MASK_RAB>::value;
-        auto fn = wl.fused ? attn_fwd_mfma16<T, D, NW16, QBR, BK, PF, true, MASK_RAB>
-                           : attn_fwd_mfma16<T, D, NW16, QBR, BK, PF, false, MASK_RAB>;
+        static_assert(QBlocksFor<D, MASK_RAB_TGT>::value == QBR, "one item shape for both");
+        using FnR = void (*)(KernelArgsRab);
+        static constexpr FnR fnr[2][2] = {
+                {attn_fwd_mfma16<T, D, NW16, QBR, BK, PF, false, MASK_RAB>,
+                 attn_fwd_mfma16<T, D, NW16, QBR, BK, PF, false, MASK_RAB_TGT>},
+                {attn_fwd_mfma16<T, D, NW16, QBR, BK, PF, true, MASK_RAB>,
+                 attn_fwd_mfma16<T, D, NW16, QBR, BK, PF, true, MASK_RAB_TGT>}};
+        const int tg = p.num_targets ? 1 : 0;
+        const FnR fn = fnr[wl.fused ? 1 : 0][tg];
         if (grid <= 0) {
-            static int cached[2] = {};
-            int& c = cached[wl.fused ? 1 : 0];
+            static int cached[2][2] = {};
+            int& c = cached[wl.fused ? 1 : 0][tg];
             if (!c) c = resident_grid(fn, NW16 * 64);
             grid = c;
         }

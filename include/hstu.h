@@ -226,6 +226,36 @@ hstu_status_t hstu_attn_fwd_rab(const void* q, const void* k, const void* v,
                                 float alpha, float n, void* out, hipStream_t stream,
                                 hstu_dtype_t dtype);
 
+/* hstu_attn_fwd_rab under the target-aware mask of hstu_attn_fwd_targets
+ * (HSTU paper translation, §3.4: M-FALCON adjusts the attention mask and
+ * rab_{p,t} together so that every candidate of a micro-batch runs the same
+ * operations).  The page gives no formula; this call takes the reading that a
+ * candidate row sits at the position right after the history, hist = s - t,
+ * and keeps its own timestamp:
+ *
+ *   out[r] = (1/n) * sum over the keys c that row r sees of
+ *            silu(alpha <q[r], k[c]> + rab_t(r, c)) * v[c]
+ *   rab_t(r, c) = rab(r, c)                                   for r < hist
+ *               = pos_bias[hist - c] + time term of (r, c)    for r >= hist, c < hist
+ *               = pos_bias[0] + time_bias[0]                  for r >= hist, c = r
+ *
+ * with rab's time term as in hstu_attn_fwd_rab.  A candidate's output thus
+ * equals the last row of hstu_attn_fwd_rab over the history followed by that
+ * candidate alone, whatever the other candidates are.
+ *
+ *   num_targets : as in hstu_attn_fwd_targets (device int32[num_seqs],
+ *                 clamped to [0, length]).
+ *   the rest    : as in hstu_attn_fwd_rab.
+ * Errors as in hstu_attn_fwd_rab; a null or misaligned num_targets (with
+ * num_seqs > 0) also gives HSTU_ERR_INVALID_ARG. */
+hstu_status_t hstu_attn_fwd_rab_targets(const void* q, const void* k, const void* v,
+                                        const int32_t* seq_offsets, const int32_t* num_targets,
+                                        const int32_t* timestamps, const float* pos_bias,
+                                        int32_t num_pos, const float* time_bias,
+                                        int32_t num_time, int32_t num_seqs, int32_t heads,
+                                        int32_t d, float alpha, float n, void* out,
+                                        hipStream_t stream, hstu_dtype_t dtype);
+
 /* Backward: gradients of hstu_attn_fwd (or, with num_targets, of
  * hstu_attn_fwd_targets) with respect to q, k and v, for the upstream
  * gradient dout = dLoss/dout.  The attention is recomputed block by block and

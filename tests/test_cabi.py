@@ -140,6 +140,35 @@ def test_rab_empty_batch_is_a_no_op(lib):
                      out=None, num_seqs=0) == hstu.HSTU_OK
 
 
+def _call_rab_targets(lib, tg=96, ts=48, wpos=64, npos=8, wtime=80, ntime=4, **kw):
+    a = dict(q=16, k=16, v=16, off=16, num_seqs=1, heads=1, d=64, alpha=0.1, n=1.0, out=32,
+             dtype=hstu.HSTU_BF16)
+    a.update(kw)
+    return lib.hstu_attn_fwd_rab_targets(a["q"], a["k"], a["v"], a["off"], tg, ts, wpos, npos,
+                                         wtime, ntime, a["num_seqs"], a["heads"], a["d"],
+                                         a["alpha"], a["n"], a["out"], None, a["dtype"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(tg=None), hstu.HSTU_ERR_INVALID_ARG),    # candidate counts missing
+    (dict(tg=98), hstu.HSTU_ERR_INVALID_ARG),      # misaligned counts
+    (dict(ts=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(wpos=66), hstu.HSTU_ERR_INVALID_ARG),    # misaligned table
+    (dict(npos=0), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(ntime=33), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(alpha=0.0), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(d=96), hstu.HSTU_ERR_UNSUPPORTED),
+    (dict(out=16), hstu.HSTU_ERR_INVALID_ARG),
+])
+def test_rab_targets_argument_checks(lib, kw, status):
+    assert _call_rab_targets(lib, **kw) == status
+
+
+def test_rab_targets_empty_batch_is_a_no_op(lib):
+    assert _call_rab_targets(lib, tg=None, ts=None, wpos=None, wtime=None, q=None, k=None,
+                             v=None, off=None, out=None, num_seqs=0) == hstu.HSTU_OK
+
+
 def _call_bwd_rab(lib, ts=48, wpos=64, npos=8, wtime=80, ntime=4, gpos=112, gtime=128, **kw):
     a = dict(q=16, k=16, v=16, dout=144, off=16, num_seqs=1, heads=1, d=64, alpha=0.1, n=1.0,
              dq=160, dk=176, dv=192, dtype=hstu.HSTU_BF16)

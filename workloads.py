@@ -354,3 +354,11 @@ def rab_workload(values: bool = True):
                      name="rab", description=RAB_DESCRIPTION) if values else None
     offsets = case.offsets if case is not None else offsets_from_lengths([4096] * 16)
     return case, make_rab_inputs(offsets, 4096, 16, seed=1301)
+
+
+def rab_targets_workload(values: bool = True):
+    """The target-aware workload (16 x (3072 history + 1024 candidates),
+    heads 4, d 64, bf16) with a relative attention bias: a position entry per
+    distance and 16 time buckets.  Seeds 1100 (q, k, v) and 1311 (bias)."""
+    case = targets_workload(values)
+    return case, make_rab_inputs(case.offsets, 4096, 16, seed=1311)
