@@ -66,11 +66,11 @@ METRIC_RAB_BWD = "HSTU attn bwd with relative attention bias (dq, dk, dv, table 
 # source the bench reports traffic as null.
 TRAFFIC = {
     "kernel_source": "generative_recommendation_attention_amd/csrc/attn_fwd.hip",
-    "kernel_sha256": "52f7c417aa9a1671e541b5c7747445ce0a2b1fb58cc054aecb5769d3b559f90c",
+    "kernel_sha256": "2c218ab872c2639f95a87a4a87430274c6cea76a358f61a0b129bbdb97592f11",
     "fetch_scale": 2.0,
     "write_scale": 1.0,
-    "fetch_kib": {2: 93861.8},
-    "write_kib": {2: 37938.6},
+    "fetch_kib": {2: 99252.0},
+    "write_kib": {2: 37939.1},
 }
 
 
