@@ -326,6 +326,10 @@ def main() -> int:
                          "(a position entry per distance, 16 time buckets); with --targets, "
                          "the target-aware forward with the bias on the --targets workload; "
                          "with --backward, the backward with the bias")
+    ap.add_argument("--graph", action="store_true",
+                    help="record one call into a HIP graph (torch.cuda.CUDAGraph) and time its "
+                         "replays instead of eager calls (the library's kernel timers are off "
+                         "under capture, so the roofline uses the whole replay)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibrate", action="store_true",
@@ -336,6 +340,8 @@ def main() -> int:
     if modes > 1 and not (modes == 2 and args.rab and (args.backward or args.targets)):
         ap.error("--targets, --cached, --backward, --dense, --layer and --rab are separate "
                  "benchmarks (except --backward --rab and --targets --rab)")
+    if args.graph and args.layer:
+        ap.error("--graph records the attention calls; --layer has no graph form here")
     if args.layer:
         return bench_layer(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -447,6 +453,24 @@ def main() -> int:
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
+    if args.graph:
+        eager_call = call
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            eager_call()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            eager_call()
+        torch.cuda.synchronize()
+
+        def call():
+            graph.replay()
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
 
     hstu.hstu_profile_read(reset=True)
     hstu.hstu_profile_enable(True)
@@ -464,17 +488,18 @@ def main() -> int:
     ms = total_ms / args.steps
     value = flops / (ms * 1e-3) / 1e12
 
-    attn_ms = kt.attn_ms / max(1, kt.calls)
+    attn_ms = kt.attn_ms / max(1, kt.calls) if kt.calls else ms
     sched_ms = kt.sched_ms / max(1, kt.calls)
     achieved = flops / (attn_ms * 1e-3) / 1e12
     peak = PEAK_MFMA_TFLOPS[case.dtype]
-    traffic = (None if (args.targets or args.cached or args.backward or args.dense or args.rab)
-               else traffic_bytes(args.workload))
+    traffic = (None if (args.targets or args.cached or args.backward or args.dense or args.rab or
+                        args.graph) else traffic_bytes(args.workload))
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel": ("attn_bwd_dkv + attn_bwd_dq + table-gradient sum" if args.backward and
                            args.rab else "attn_bwd_dkv + attn_bwd_dq" if args.backward else
-                           "attn_fwd_mfma16" if case.dtype != "fp32" else "attn_fwd_mfma_f32"),
+                           "attn_fwd_mfma16" if case.dtype != "fp32" else "attn_fwd_mfma_f32") +
+                          (" (graph replay, whole call)" if args.graph else ""),
                 "kernel_ms": round(attn_ms, 5), "sched_kernel_ms": round(sched_ms, 5),
                 "hbm_frac": round(alg_bytes / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
@@ -489,7 +514,7 @@ def main() -> int:
 
     L = case.lengths
     plain_w2 = (args.workload == 2 and not (args.targets or args.cached or args.backward or
-                                            args.dense or args.rab))
+                                            args.dense or args.rab or args.graph))
     line = {
         "metric": (METRIC_CACHED if args.cached else
                    METRIC_RAB_TARGETS if args.targets and args.rab else
@@ -516,6 +541,7 @@ def main() -> int:
                    **({"candidates_per_seq": int(case.num_targets[0])} if args.targets else {}),
                    **({"cached_history_per_seq": int(cc.hist_lengths[0])} if args.cached else {}),
                    **({"layout": "(batch, heads, seq_len, d)"} if args.dense else {}),
+                   **({"launch": "HIP graph replay"} if args.graph else {}),
                    **({"rab_positions": int(rab.pos_bias.size),
                        "rab_time_buckets": int(rab.time_bias.size)} if args.rab else {}),
                    "useful_gflop": round(flops / 1e9, 3)},

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <list>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -72,6 +73,78 @@ hstu_status_t scratch_for(int dev, hipStream_t stream, size_t bytes, Scratch** o
     }
     *out = &s;
     return HSTU_OK;
+}
+
+// ---- calls captured into a graph ----------------------------------------------
+//
+// A graph keeps the addresses its kernels were captured with and replays them
+// in any order relative to later eager calls, so a captured call shares no
+// state with anything else: it gets a scratch area of its own, allocated
+// during capture (the thread switches to relaxed capture mode for the
+// allocation) and kept until the process ends, and its first captured kernel
+// zeroes the area's counter sets, so that every replay starts from zero.
+// Eager state (the per-stream area, its counter rotation and cached dense
+// ramp) is left as it was.
+
+std::list<Scratch> g_graph_areas;   // under g_scratch_mu; never freed
+
+bool is_capturing(hipStream_t stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(stream, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
+}
+
+hstu_status_t graph_scratch(size_t bytes, Scratch** out) {
+    size_t want = bytes < 4096 ? 4096 : bytes;
+    want = (want + 4095) & ~(size_t)4095;
+    if (getenv("HSTU_FAIL_ALLOC") && atoi(getenv("HSTU_FAIL_ALLOC")) != 0)
+        return HSTU_ERR_NO_MEMORY;
+    hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+    hipError_t e = hipThreadExchangeStreamCaptureMode(&mode);
+    if (e != hipSuccess) return hip_fail(e);
+    void* p = nullptr;
+    e = hipMalloc(&p, want);
+    (void)hipThreadExchangeStreamCaptureMode(&mode);   // the caller's mode again
+    if (e != hipSuccess) {
+        g_last_hip = (int)e;
+        return HSTU_ERR_NO_MEMORY;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    g_graph_areas.emplace_back();
+    Scratch& s = g_graph_areas.back();
+    s.ptr = p;
+    s.bytes = want;
+    *out = &s;
+    return HSTU_OK;
+}
+
+// The scratch area of one call and its first counter set (`sets` consecutive
+// sets are used); *clean tells whether they are known to be zero.
+hstu_status_t call_scratch(int dev, hipStream_t stream, bool graph, size_t bytes, Scratch** sc,
+                           hstu::WorkList* wl, int num_seqs, int heads, bool* clean) {
+    hstu_status_t st = graph ? graph_scratch(bytes, sc) : scratch_for(dev, stream, bytes, sc);
+    if (st != HSTU_OK) return st;
+    *wl = hstu::worklist_carve((*sc)->ptr, num_seqs, heads);
+    if (graph) {
+        const hipError_t e = hstu::launch_clear_counters(wl->ctl, stream);
+        if (e != hipSuccess) return hip_fail(e);
+        wl->set = 0;
+        *clean = true;
+        return HSTU_OK;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    wl->set = (int)((*sc)->epoch % hstu::NSETS);
+    *clean = (*sc)->clean;
+    (*sc)->clean = false;   // until this call's launches succeed
+    return HSTU_OK;
+}
+
+// After a call's launches succeeded: `sets` counter sets consumed, and the
+// launches cleared the next two (nothing to record for a captured call).
+void call_done(Scratch* sc, bool graph, unsigned sets) {
+    if (graph) return;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    sc->epoch += sets;
+    sc->clean = true;
 }
 
 // A call whose work list reaches `bytes` into the area overwrites a dense
@@ -237,12 +310,15 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
     if (st != HSTU_OK) return st;
 
     const hstu::Dtype dt = static_cast<hstu::Dtype>(dtype);
+    const bool graph = is_capturing(stream);
     Scratch* sc = nullptr;
     const size_t wl_bytes = (hstu::worklist_bytes(num_seqs, heads) + 255) & ~(size_t)255;
     const size_t ramp_bytes = mi.dense ? sizeof(int32_t) * ((size_t)num_seqs + 1) : 0;
-    st = scratch_for(dev, stream, wl_bytes + ramp_bytes, &sc);
+    hstu::WorkList wl;
+    bool clean;
+    st = call_scratch(dev, stream, graph, wl_bytes + ramp_bytes, &sc, &wl, num_seqs, heads,
+                      &clean);
     if (st != HSTU_OK) return st;
-    hstu::WorkList wl = hstu::worklist_carve(sc->ptr, num_seqs, heads);
     forget_ramp_under(sc, wl_bytes);
     if (mi.dense) {
         st = dense_ramp(sc, wl_bytes, num_seqs, mi.dense_len, stream, &seq_offsets);
@@ -253,13 +329,6 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
     // be zero (a new scratch area, or a failed launch before; it zeroes both
     // sets) and when a test forces one of its ranking paths.
     const hstu::SortChoice sort = sort_choice_env();
-    bool clean;
-    {
-        std::lock_guard<std::mutex> lock(g_scratch_mu);
-        wl.set = (int)(sc->epoch % hstu::NSETS);
-        clean = sc->clean;
-        sc->clean = false;   // until this call's launches succeed
-    }
     wl.fused = clean && sort == hstu::SortChoice::AUTO && num_seqs <= hstu::FUSE_SEQS &&
                (long long)num_seqs * heads <= hstu::FUSE_PAIRS;
 
@@ -287,7 +356,7 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
     p.n = n;
 
     TimedCall tc;
-    const bool timed = prof_take(&tc);
+    const bool timed = !graph && prof_take(&tc);
     tc.sched = false;
     hipError_t e;
     if (!wl.fused) {
@@ -301,14 +370,9 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
     e = hstu::launch_attention(p, dt, wl, 0, stream, timed ? tc.e[2] : nullptr,
                                timed ? tc.e[3] : nullptr);
     if (e != hipSuccess) return hip_fail(e);
-    {
-        // The attention launch used one counter set and cleared the next two.
-        std::lock_guard<std::mutex> lock(g_scratch_mu);
-        sc->epoch++;
-        sc->clean = true;
-    }
+    call_done(sc, graph, 1);   // one counter set used, the next two cleared
     if (timed) prof_commit(tc);
-    if (validate_env()) {
+    if (!graph && validate_env()) {
         int ctl[hstu::CTL_WORDS];
         e = hipMemcpyAsync(ctl, wl.ctl, sizeof ctl, hipMemcpyDeviceToHost, stream);
         if (e == hipSuccess) e = hipStreamSynchronize(stream);
@@ -356,15 +420,18 @@ hstu_status_t attn_bwd_call(const void* q, const void* k, const void* v, const v
     if (st != HSTU_OK) return st;
 
     const hstu::Dtype dt = static_cast<hstu::Dtype>(dtype);
+    const bool graph = is_capturing(stream);
     Scratch* sc = nullptr;
     const size_t wl_bytes = (hstu::worklist_bytes(num_seqs, heads) + 255) & ~(size_t)255;
     const size_t ramp_bytes = dense_len > 0 ? sizeof(int32_t) * ((size_t)num_seqs + 1) : 0;
     const size_t part_bytes =
             rab ? sizeof(float) * (size_t)hstu::RAB_PARTS * hstu::rab_partial_stride(rab->num_pos)
                 : 0;
-    st = scratch_for(dev, stream, wl_bytes + ramp_bytes + part_bytes, &sc);
+    hstu::WorkList wl;
+    bool clean;
+    st = call_scratch(dev, stream, graph, wl_bytes + ramp_bytes + part_bytes, &sc, &wl, num_seqs,
+                      heads, &clean);
     if (st != HSTU_OK) return st;
-    hstu::WorkList wl = hstu::worklist_carve(sc->ptr, num_seqs, heads);
     // (the bias partials follow the work list and overwrite what was there)
     forget_ramp_under(sc, wl_bytes + part_bytes);
     if (dense_len > 0) {
@@ -372,13 +439,6 @@ hstu_status_t attn_bwd_call(const void* q, const void* k, const void* v, const v
         if (st != HSTU_OK) return st;
     }
     const hstu::SortChoice sort = sort_choice_env();
-    bool clean;
-    {
-        std::lock_guard<std::mutex> lock(g_scratch_mu);
-        wl.set = (int)(sc->epoch % hstu::NSETS);
-        clean = sc->clean;
-        sc->clean = false;
-    }
     wl.fused = clean && sort == hstu::SortChoice::AUTO && num_seqs <= hstu::FUSE_SEQS &&
                (long long)num_seqs * heads <= hstu::FUSE_PAIRS;
 
@@ -411,7 +471,7 @@ hstu_status_t attn_bwd_call(const void* q, const void* k, const void* v, const v
     p.n = n;
 
     TimedCall tc;
-    const bool timed = prof_take(&tc);
+    const bool timed = !graph && prof_take(&tc);
     tc.sched = false;
     hipError_t e;
     if (!wl.fused) {
@@ -423,12 +483,7 @@ hstu_status_t attn_bwd_call(const void* q, const void* k, const void* v, const v
     e = hstu::launch_backward(p, dt, wl, stream, timed ? tc.e[2] : nullptr,
                               timed ? tc.e[3] : nullptr);
     if (e != hipSuccess) return hip_fail(e);
-    {
-        // Two launches, two counter sets; between them they cleared the next two.
-        std::lock_guard<std::mutex> lock(g_scratch_mu);
-        sc->epoch += 2;
-        sc->clean = true;
-    }
+    call_done(sc, graph, 2);   // two launches, two counter sets; the next two cleared
     if (timed) prof_commit(tc);
     return HSTU_OK;
 }

@@ -128,6 +128,10 @@ enum class Dtype : int { BF16 = 0, FP16 = 1, FP32 = 2 };
 
 // Writes dst[i] = i * step for i < count (offsets of equal-length sequences).
 hipError_t launch_fill_ramp(int32_t* dst, int count, int step, hipStream_t stream);
+// Zeroes every counter set of the work list whose control block is ctl (one
+// small kernel): the first kernel of a call captured into a graph, so that
+// each replay starts from zero counters without a memset node.
+hipError_t launch_clear_counters(int* ctl, hipStream_t stream);
 
 struct FwdParams {
     const void* q;

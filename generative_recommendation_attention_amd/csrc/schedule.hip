@@ -244,6 +244,19 @@ __global__ void fill_ramp_kernel(int32_t* dst, int count, int step) {
 }
 }  // namespace
 
+namespace {
+__global__ void clear_counters_kernel(int* ctl) {
+    static_assert(NSETS * NQ <= 64, "one wave clears every counter");
+    const int t = threadIdx.x;
+    if (t < NSETS * NQ) ctl[CTL_NEXT + CTL_LINE * t] = 0;
+}
+}  // namespace
+
+hipError_t launch_clear_counters(int* ctl, hipStream_t stream) {
+    hipLaunchKernelGGL(clear_counters_kernel, dim3(1), dim3(64), 0, stream, ctl);
+    return hipGetLastError();
+}
+
 hipError_t launch_fill_ramp(int32_t* dst, int count, int step, hipStream_t stream) {
     if (count <= 0) return hipSuccess;
     hipLaunchKernelGGL(fill_ramp_kernel, dim3((count + 255) / 256), dim3(256), 0, stream, dst,

@@ -44,6 +44,16 @@
  * otherwise (a work-list kernel, then the attention kernel); the first call on
  * a new scratch area always takes the two-kernel form.
  *
+ * Graph capture: a call made while `stream` is being captured into a HIP
+ * graph (hipStreamIsCapturing) is recorded with a scratch area of its own,
+ * allocated during the capture (the calling thread switches to relaxed
+ * capture mode for that allocation) and kept until the process ends, since
+ * the graph holds its address; its first recorded kernel zeroes that area's
+ * queue counters, so every replay starts from the same state whatever ran
+ * before it.  Captured calls share nothing with eager calls or with each
+ * other; replaying one graph on two streams at once races on its area.
+ * Under capture, HSTU_VALIDATE and the kernel timers are ignored.
+ *
  * Errors: argument checks happen on the host before anything is enqueued; a
  * failed check returns a negative status and leaves the stream untouched.  A
  * failed HIP call returns HSTU_ERR_HIP and its hipError_t is kept for
