@@ -695,7 +695,6 @@ hstu_status_t hstu_attn_bwd_rab(const void* q, const void* k, const void* v, con
                                 float alpha, float n, void* dq, void* dk, void* dv,
                                 float* d_pos_bias, float* d_time_bias, hipStream_t stream,
                                 hstu_dtype_t dtype) {
-    if (dtype == HSTU_FP32) return HSTU_ERR_UNSUPPORTED;
     if (num_pos < 1 || num_pos > (1 << 18) || num_time < 1 || num_time > 32)
         return HSTU_ERR_INVALID_ARG;
     if (!(alpha != 0.0f) || !std::isfinite((float)(1.0 / (double)alpha)))

@@ -882,7 +882,35 @@ struct BwdArgsF32 {
     float alpha;
     float dv_scale;
     float g_scale;
+    // relative attention bias (RAB instantiations only)
+    const int32_t* ts;
+    const float* wpos;
+    const float* wtime;
+    float* gpart;   // [nparts][gstride]: npos position entries, then the time buckets
+    int npos;
+    int ntime;
+    int gstride;
+    int nparts;
+    float bias_scale;   // 1 / alpha
 };
+
+// The bias of pair (row, key) of a sequence over alpha, read from global
+// memory (the float32 kernels are the reference-precision path, not the fast
+// one); ttab is the time table by v_ffbh_u32(gap + 1) + 1, already over
+// alpha.  Rows or keys at or past the sequence's end get 0 (their terms are
+// zero anyway).  *dist and *bucket name the table entries the pair uses.
+__device__ __forceinline__ float bias_over_alpha_f32(const BwdArgsF32& a, const float* ttab,
+                                                     int start, int s, int row, int key,
+                                                     int* dist, int* bucket) {
+    *dist = row - key;
+    *bucket = 0;
+    if (row >= s || key >= s) return 0.0f;
+    const uint32_t x = (uint32_t)a.ts[start + row] + 1u - (uint32_t)a.ts[start + key];
+    const int f = ffbh_u32(x);
+    *bucket = rab_time_bucket(f + 1, a.ntime);
+    const float pos = (*dist >= 0 && *dist < a.npos) ? a.wpos[*dist] * a.bias_scale : 0.0f;
+    return pos + ttab[f + 1];
+}
 
 template <int D>
 struct BwdCfgF32 {
@@ -918,20 +946,26 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-template <int D, bool FUSED, bool TGT>
+template <int D, bool FUSED, bool TGT, bool RAB = false>
 __global__ __launch_bounds__(256) void attn_bwd_dkv_f32(BwdArgsF32 a) {
     using C = BwdCfgF32<D>;
     constexpr int NDB = D / 32;
+    static_assert(!RAB || !TGT, "bias: causal mask");
     __shared__ __attribute__((aligned(16))) float ql[32 * C::STR];
     __shared__ __attribute__((aligned(16))) float ol[32 * C::STR];
     __shared__ int s_item[NQ];
     __shared__ LocalTables lt;
     __shared__ int tbl_scratch[FUSE_SEQS];
+    __shared__ float ttab[RAB ? 33 : 1];
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int g = lane >> 5, l32 = lane & 31;
     const int H = a.heads;
     const int64_t row_stride = a.row_stride;
+    if constexpr (RAB) {
+        if (threadIdx.x < 33)
+            ttab[threadIdx.x] = a.wtime[rab_time_bucket(threadIdx.x, a.ntime)] * a.bias_scale;
+    }
 
     Tables tb;
     if constexpr (FUSED)
@@ -985,8 +1019,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_f32(BwdArgsF32 a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     float pr, dsr;
-                    pointwise(st[r], dp[r], a.alpha, &pr, &dsr);
                     const int qrow = 8 * (r >> 2) + 4 * g + (r & 3);   // row inside the block
+                    if constexpr (RAB) {
+                        int dist, bucket;
+                        st[r] += bias_over_alpha_f32(a, ttab, start, s, q0 + qrow, key, &dist,
+                                                     &bucket);
+                    }
+                    pointwise(st[r], dp[r], a.alpha, &pr, &dsr);
                     if (masked) {
                         const int qr = q0 + qrow;
                         const bool keep = key <= qr && (key < hist || key == qr);
@@ -1025,20 +1064,33 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_f32(BwdArgsF32 a) {
     }
 }
 
-template <int D, bool FUSED, bool TGT>
+template <int D, bool FUSED, bool TGT, bool RAB = false>
 __global__ __launch_bounds__(256) void attn_bwd_dq_f32(BwdArgsF32 a) {
     using C = BwdCfgF32<D>;
     constexpr int NDB = D / 32;
+    static_assert(!RAB || !TGT, "bias: causal mask");
     __shared__ __attribute__((aligned(16))) float kl[32 * C::STR];
     __shared__ __attribute__((aligned(16))) float vl[32 * C::STR];
     __shared__ int s_item[NQ];
     __shared__ LocalTables lt;
     __shared__ int tbl_scratch[FUSE_SEQS];
+    __shared__ float ttab[RAB ? 33 : 1];
+    __shared__ float tbins[RAB ? 32 : 1];   // time-gradient sums by bucket
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int g = lane >> 5, l32 = lane & 31;
     const int H = a.heads;
     const int64_t row_stride = a.row_stride;
+    // Table gradients: position entries straight into this workgroup's
+    // partial with float atomics, time buckets summed in LDS and added to the
+    // partial at the end.
+    float* gpart = nullptr;
+    if constexpr (RAB) {
+        if (threadIdx.x < 33)
+            ttab[threadIdx.x] = a.wtime[rab_time_bucket(threadIdx.x, a.ntime)] * a.bias_scale;
+        if (threadIdx.x < 32) tbins[threadIdx.x] = 0.0f;
+        gpart = a.gpart + (int64_t)(blockIdx.x % a.nparts) * a.gstride;
+    }
 
     Tables tb;
     if constexpr (FUSED)
@@ -1091,11 +1143,25 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f32(BwdArgsF32 a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     float pr, dsr;
-                    pointwise(st[r], dp[r], a.alpha, &pr, &dsr);
                     const int krow = 8 * (r >> 2) + 4 * g + (r & 3);   // key inside the block
+                    int dist = 0, bucket = 0;
+                    if constexpr (RAB)
+                        st[r] += bias_over_alpha_f32(a, ttab, start, s, row, k0 + krow, &dist,
+                                                     &bucket);
+                    pointwise(st[r], dp[r], a.alpha, &pr, &dsr);
                     if (masked) {
                         const int kk = k0 + krow;
                         dsr = (kk <= row && (kk < hist || kk == row)) ? dsr : 0.0f;
+                    }
+                    if constexpr (RAB) {
+                        // (pairs past the sequence or the diagonal have dsr = 0)
+                        if (dsr != 0.0f) {
+                            if (dist < a.npos)
+                                __hip_atomic_fetch_add(gpart + dist, dsr * a.dv_scale,
+                                                       __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+                            atomicAdd(&tbins[bucket], dsr);
+                        }
                     }
 #pragma unroll
                     for (int db = 0; db < NDB; ++db)
@@ -1117,9 +1183,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f32(BwdArgsF32 a) {
                 }
         }
     }
+    if constexpr (RAB) {
+        __syncthreads();
+        if (threadIdx.x < a.ntime && tbins[threadIdx.x] != 0.0f)
+            __hip_atomic_fetch_add(gpart + a.npos + threadIdx.x, tbins[threadIdx.x] * a.dv_scale,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
-template <int D, bool TGT>
+template <int D, bool TGT, bool RAB = false>
 hipError_t launch_bwd_f32_typed(const BwdParams& p, WorkList wl, hipStream_t stream,
                                 hipEvent_t start, hipEvent_t stop) {
     BwdArgsF32 a;
@@ -1139,32 +1211,63 @@ hipError_t launch_bwd_f32_typed(const BwdParams& p, WorkList wl, hipStream_t str
     a.alpha = p.alpha;
     a.dv_scale = 1.0f / p.n;
     a.g_scale = p.alpha / p.n;
+    a.ts = p.timestamps;
+    a.wpos = p.pos_bias;
+    a.wtime = p.time_bias;
+    a.gpart = p.rab_partials;
+    a.npos = p.num_pos;
+    a.ntime = p.num_time;
+    a.gstride = RAB ? rab_partial_stride(p.num_pos) : 0;
+    a.nparts = RAB_PARTS;
+    a.bias_scale = RAB ? (float)(1.0 / (double)p.alpha) : 0.0f;
     using Fn = void (*)(BwdArgsF32);
-    const Fn f_dkv = wl.fused ? attn_bwd_dkv_f32<D, true, TGT> : attn_bwd_dkv_f32<D, false, TGT>;
-    const Fn f_dq = wl.fused ? attn_bwd_dq_f32<D, true, TGT> : attn_bwd_dq_f32<D, false, TGT>;
+    const Fn f_dkv = wl.fused ? attn_bwd_dkv_f32<D, true, TGT, RAB>
+                              : attn_bwd_dkv_f32<D, false, TGT, RAB>;
+    const Fn f_dq = wl.fused ? attn_bwd_dq_f32<D, true, TGT, RAB>
+                             : attn_bwd_dq_f32<D, false, TGT, RAB>;
     static int grids[2][2] = {};
     int& g_dkv = grids[wl.fused ? 1 : 0][0];
     int& g_dq = grids[wl.fused ? 1 : 0][1];
     if (!g_dkv) g_dkv = resident_grid(f_dkv, 256);
     if (!g_dq) g_dq = resident_grid(f_dq, 256);
     a.wl = wl;
+    hipError_t e;
+    if constexpr (RAB) {
+        const int64_t cells = (int64_t)RAB_PARTS * a.gstride;
+        hipLaunchKernelGGL(rab_zero_kernel, dim3(256), dim3(256), 0, stream, a.gpart, cells);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     if (start)
         hipExtLaunchKernelGGL(f_dkv, dim3(g_dkv), dim3(256), 0, stream, start, nullptr, 0, a);
     else
         hipLaunchKernelGGL(f_dkv, dim3(g_dkv), dim3(256), 0, stream, a);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.wl.set = (wl.set + 1) % NSETS;
-    if (stop)
-        hipExtLaunchKernelGGL(f_dq, dim3(g_dq), dim3(256), 0, stream, nullptr, stop, 0, a);
+    hipEvent_t dq_stop = RAB ? nullptr : stop;
+    if (dq_stop)
+        hipExtLaunchKernelGGL(f_dq, dim3(g_dq), dim3(256), 0, stream, nullptr, dq_stop, 0, a);
     else
         hipLaunchKernelGGL(f_dq, dim3(g_dq), dim3(256), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess || !RAB) return e;
+    const int n_out = p.num_pos + p.num_time;
+    if (stop)
+        hipExtLaunchKernelGGL(rab_reduce_kernel, dim3((n_out + 255) / 256), dim3(256), 0, stream,
+                              nullptr, stop, 0, (const float*)a.gpart, a.nparts, a.gstride,
+                              p.num_pos, p.num_time, p.d_pos_bias, p.d_time_bias);
+    else
+        hipLaunchKernelGGL(rab_reduce_kernel, dim3((n_out + 255) / 256), dim3(256), 0, stream,
+                           (const float*)a.gpart, a.nparts, a.gstride, p.num_pos, p.num_time,
+                           p.d_pos_bias, p.d_time_bias);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_bwd_f32(const BwdParams& p, WorkList wl, hipStream_t stream, hipEvent_t start,
                           hipEvent_t stop) {
+    if (p.timestamps) return launch_bwd_f32_typed<D, false, true>(p, wl, stream, start, stop);
     return p.num_targets ? launch_bwd_f32_typed<D, true>(p, wl, stream, start, stop)
                          : launch_bwd_f32_typed<D, false>(p, wl, stream, start, stop);
 }
@@ -1179,7 +1282,6 @@ hipError_t launch_backward(const BwdParams& p, Dtype dt, WorkList wl, hipStream_
     if (dt == Dtype::FP16)
         return p.d == 64 ? launch_bwd_mask<_Float16, 64>(p, wl, stream, start, stop)
                          : launch_bwd_mask<_Float16, 128>(p, wl, stream, start, stop);
-    if (dt == Dtype::FP32 && p.timestamps) return hipErrorInvalidValue;
     if (dt == Dtype::FP32)
         return p.d == 64 ? launch_bwd_f32<64>(p, wl, stream, start, stop)
                          : launch_bwd_f32<128>(p, wl, stream, start, stop);

@@ -318,9 +318,11 @@ hstu_status_t hstu_attn_bwd_targets(const void* q, const void* k, const void* v,
  *   d_pos_bias   : device float[num_pos], overwritten, 4-byte aligned.
  *   d_time_bias  : device float[num_time], overwritten, 4-byte aligned.
  *
- * bfloat16 and float16 only (float32 returns HSTU_ERR_UNSUPPORTED).  The table
- * gradients are sums taken with float atomics: not bitwise reproducible
- * across calls (dq, dk, dv are).  The call also uses 64 * (num_pos + 32)
+ * bfloat16 and float16 on the matrix cores as in hstu_attn_bwd; float32 runs
+ * every product in float32 and reads the bias per element from global memory
+ * (the reference-precision path, not a fast one).  The table gradients are
+ * sums taken with float atomics: not bitwise reproducible across calls (dq,
+ * dk, dv are).  The call also uses 64 * (num_pos + 32)
  * floats of library scratch.  A call is four kernels (zeroing the partials,
  * dk/dv, dq with the table sums, the partials' reduction; plus the work-list
  * kernel as in hstu_attn_bwd).  Other conventions and errors as in

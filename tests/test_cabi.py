@@ -187,7 +187,8 @@ def _call_bwd_rab(lib, ts=48, wpos=64, npos=8, wtime=80, ntime=4, gpos=112, gtim
     (dict(npos=(1 << 18) + 1), hstu.HSTU_ERR_INVALID_ARG),
     (dict(ntime=33), hstu.HSTU_ERR_INVALID_ARG),
     (dict(alpha=0.0), hstu.HSTU_ERR_INVALID_ARG),
-    (dict(dtype=hstu.HSTU_FP32), hstu.HSTU_ERR_UNSUPPORTED),
+    (dict(dtype=9), hstu.HSTU_ERR_UNSUPPORTED),
+    (dict(dtype=hstu.HSTU_FP32, gpos=None), hstu.HSTU_ERR_INVALID_ARG),
     (dict(d=96), hstu.HSTU_ERR_UNSUPPORTED),
     (dict(dq=16), hstu.HSTU_ERR_INVALID_ARG),       # dq aliases q
     (dict(dout=None), hstu.HSTU_ERR_INVALID_ARG),

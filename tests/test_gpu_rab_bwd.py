@@ -56,7 +56,7 @@ def compare(case, dout, r, res, what):
         log(f"  {name}: max|err|/max|ref| = {mr:.2e}, rel L2 = {l2:.2e}")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("npos,ntime", [(400, 16), (50, 32), (1, 1)])
 def test_rab_bwd_full_compare(dtype, d, npos, ntime):
@@ -71,7 +71,7 @@ def test_rab_bwd_decreasing_timestamps():
     compare(case, dout, r, run_bwd_rab(case, dout, r), "rab bwd decreasing timestamps")
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("fp16", 128)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("fp16", 128), ("fp32", 64)])
 def test_rab_bwd_zero_tables_match_plain_bitwise(dtype, d):
     case, dout, r = make(LENGTHS + [513], 3, d, dtype, 30, 5, seed=1520)
     r.pos_bias[:] = 0
