@@ -66,11 +66,11 @@ METRIC_RAB_BWD = "HSTU attn bwd with relative attention bias (dq, dk, dv, table 
 # source the bench reports traffic as null.
 TRAFFIC = {
     "kernel_source": "generative_recommendation_attention_amd/csrc/attn_fwd.hip",
-    "kernel_sha256": "ffc75b3279a13d151d75ec60d6a84b1c6a3ff969e0681b801d6b7d78f50b58d0",
+    "kernel_sha256": "b8bf6a7c6e0d86adeb56993150b36d7d3eae3f3bdb93e3a470acf75c789425d1",
     "fetch_scale": 2.0,
     "write_scale": 1.0,
-    "fetch_kib": {2: 94278.2},
-    "write_kib": {2: 37940.3},
+    "fetch_kib": {2: 94096.7},
+    "write_kib": {2: 37939.6},
 }
 
 

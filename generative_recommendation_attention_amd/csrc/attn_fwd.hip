@@ -171,6 +171,9 @@ template <typename T, int D, int NW, int QB, int BK, int PF, bool FUSED, int MAS
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MASK>::type a) {
     constexpr bool TGT = MASK == MASK_TARGETS || MASK == MASK_CACHED || MASK == MASK_RAB_TGT;
     constexpr bool RAB = MASK == MASK_RAB || MASK == MASK_RAB_TGT;   // (TGT: hist-based mask)
+    // Last-bucket blocks (below) at d = 64 only: at d = 128 the extra path
+    // costs the bias kernel some 30-80 more spilled registers.
+    constexpr bool FAR = RAB && D == 64;
     using Cfg = Tile16<T, D, NW, QB, BK, PF>;
     using M = Mfma<T>;
     using v8 = typename M::v8;
@@ -243,7 +246,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
     constexpr int RAB_CMAX = BK - 5;
     const int rab_tk = (wv * Cfg::RAB_WORDS + 4 * g) * 4;
     const int rab_wb = (wv * Cfg::RAB_WORDS + 64 + l32 - 4 * g + 5) * 4;
+    // (gap at and above which a pair is in the last time bucket)
+    int64_t far_gap = 0;
     if constexpr (RAB) {
+        far_gap = ((int64_t)1 << (a.ntime - 1)) - 1;
         if (tid < 33) {
             const int b = tid == 0 ? a.ntime - 1 : min(32 - tid, a.ntime - 1);
             ttab[tid] = a.wtime[b] * a.bias_scale;
@@ -355,6 +361,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
         // first one, and the lane's lead over it (row - wr0 when causal).
         const int wr_eff0 = TGT ? min(wr0, hist) : wr0;
         const int rab_wb_it = TGT ? rab_wb + 4 * (min(wr0 + l32, hist) - wr_eff0 - l32) : rab_wb;
+        // Blocks whose every pair lies in the last time bucket (the keys'
+        // latest timestamp at least 2^(ntime-1) - 1 before the wave's
+        // earliest row: typical far from the diagonal once the table is
+        // shorter than the span of the gaps) take the time term as one
+        // constant.  far_mask bit 2 slot + kb marks such a block of the tile
+        // in `slot`; rmin is the wave's earliest row timestamp.
+        uint32_t far_mask = 0;
+        int rmin = 0;
         auto issue_rab = [&](int c) {
             if constexpr (RAB) {
                 const int k0 = (TGT && c >= nh ? c + jump : c) * BK;
@@ -384,6 +398,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
 #pragma unroll
                 for (int u = 0; u < Cfg::RAB_WIN / 64; ++u)
                     area[64 + 64 * u + lane] = rab_w[u] * a.bias_scale;
+                // latest key timestamp of each 32-key block (lanes past the
+                // tile or the sequence read 0, which can only make a block
+                // look nearer)
+                if constexpr (FAR) {
+                    int m = (int)rab_ts;
+#pragma unroll
+                    for (int off = 1; off < 32; off <<= 1) m = max(m, __shfl_xor(m, off));
+                    const int sh = 2 * (c % NS);
+                    uint32_t bits = 0;
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb) {
+                        const int kmax = __builtin_amdgcn_readlane(m, 32 * kb);
+                        if ((int64_t)rmin - kmax >= far_gap) bits |= 1u << kb;
+                    }
+                    far_mask = (far_mask & ~(3u << sh)) | (bits << sh);
+                }
             }
         };
         if constexpr (RAB) {
@@ -423,6 +453,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
         auto acc_init = [&](int slot, int kb, f32x16* acc) {
             if constexpr (RAB) {
                 const unsigned char* ra = lds + Cfg::LDS_BYTES + slot * NW * Cfg::RAB_WORDS * 4;
+                if (FAR && ((far_mask >> (2 * slot + kb)) & 1u)) {
+                    const float tlast = ttab[0];   // the last bucket's entry
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int o = 32 * kb + 8 * (r >> 2) + (r & 3);
+                            acc[qb][r] = *reinterpret_cast<const float*>(
+                                                 ra + rab_wb_it + 4 * (32 * qb + RAB_CMAX - o)) +
+                                         tlast;
+                        }
+                    return;
+                }
                 u32x4 tk[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -544,6 +587,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
 #pragma unroll
             for (int c = 1; c < PF; ++c) issue_loads(c);
             __builtin_amdgcn_s_waitcnt(VMCNT_LE((PF - 1) * 2 * Cfg::LOADS));
+            if constexpr (FAR) {
+                int t = 0x7fffffff;   // rows past the sequence do not count
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    if (wr0 + 32 * qb + l32 < s) t = min(t, (int)(trp1[qb] - 1u));
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) t = min(t, __shfl_xor(t, off));
+                rmin = __builtin_amdgcn_readfirstlane(t);
+            }
             rab_store(0);
             issue_rab(1);
         } else {
