@@ -142,3 +142,19 @@ def test_rab_repeat_is_deterministic():
     a = run_rab(case, r)
     b = run_rab(case, r)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("step", [3, 4, 5, 64])
+def test_rab_last_bucket_boundary(step):
+    """Evenly spaced timestamps put the last-bucket boundary (gap
+    2^(ntime-1) - 1 = 127 with 8 buckets) a fixed number of keys below each
+    row, so some 32-key blocks lie entirely in the last bucket and their
+    neighbours do not; with one time entry per bucket well apart, a block
+    given the constant last-bucket term by mistake would show."""
+    case = workloads.make_case([300, 129, 64, 513], 2, 64, "bf16", seed=1460)
+    r = workloads.make_rab_inputs(case.offsets, 600, 8, seed=1461)
+    r.timestamps = (np.arange(case.total, dtype=np.int64) * step).astype(np.int32)
+    r.time_bias = (np.arange(8, dtype=np.float32) * np.float32(0.75) - np.float32(2.0))
+    log(f"rab last-bucket boundary, timestamp step {step}")
+    got = from_torch(run_rab(case, r), "bf16")
+    assert_close(got, oracle_rab(case, r), "bf16", f"rab last bucket step {step}")
