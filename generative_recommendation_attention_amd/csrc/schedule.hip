@@ -57,6 +57,29 @@ __device__ long long segmented_scan(long long v, int seg, SchedShared& sh) {
     return v + sh.wave_sum[wave][lane % seg];
 }
 
+// counters[t] += 1 for every active lane of the wave, with one LDS atomic
+// per distinct t in the wave instead of one per lane (a batch of short
+// sequences has only a few tile counts, and per-lane atomics on those few
+// addresses serialise).  Returns the lane's slot: the counter's old value
+// plus the lane's rank among the wave's lanes with the same t.  Called by
+// every lane of the wave.
+__device__ inline int wave_counted_add(int* counters, int t, bool active) {
+    const int lane = threadIdx.x & 63;
+    unsigned long long pending = __ballot(active);
+    int slot = 0;
+    while (pending) {
+        const int leader = __builtin_ctzll(pending);
+        const int v = __builtin_amdgcn_readlane(t, leader);
+        const unsigned long long same = __ballot(active && t == v);
+        int base = 0;
+        if (lane == leader) base = atomicAdd(&counters[v], __popcll(same));
+        base = __builtin_amdgcn_readlane(base, leader);
+        if (active && t == v) slot = base + __popcll(same & ((1ull << lane) - 1ull));
+        pending &= ~same;
+    }
+    return slot;
+}
+
 __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
         const int32_t* __restrict__ off, int num_seqs, int heads, int bq, WorkList wl,
         int force_kind) {
@@ -99,6 +122,19 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
         }
         for (int i = tid + CACHE * SCHED_THREADS; i < num_seqs; i += SCHED_THREADS) f(i, tiles_of(i));
     };
+    // f(i, tiles of i, i < num_seqs) on every lane, with the wave converged.
+    auto for_each_lane = [&](auto f) {
+#pragma unroll
+        for (int k = 0; k < CACHE; ++k) {
+            const int i = tid + k * SCHED_THREADS;
+            f(i, tcache[k], i < num_seqs);
+        }
+        for (int base = CACHE * SCHED_THREADS; base < num_seqs; base += SCHED_THREADS) {
+            const int i = base + tid;
+            const bool active = i < num_seqs;
+            f(i, active ? tiles_of(i) : 0, active);
+        }
+    };
 
     // ---- 1. ranking -------------------------------------------------------
     int my_max = 0;
@@ -120,7 +156,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
     if (kind == RANK_COUNTING) {
         for (int v = tid; v <= maxT; v += SCHED_THREADS) hist[v] = 0;
         __syncthreads();
-        for_each_seq([&](int, int t) { atomicAdd(&hist[t], 1); });
+        for_each_lane([&](int, int t, bool active) { wave_counted_add(hist, t, active); });
         __syncthreads();
         // cursor[v] = number of sequences with more than v tiles (scan over v descending).
         for (int base = 0; base <= maxT; base += SCHED_THREADS) {
@@ -132,11 +168,13 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
             if (tid == SCHED_THREADS - 1) sh.carry[0] += inc;
             __syncthreads();
         }
-        for_each_seq([&](int i, int t) {
-            const int pos = atomicAdd(&cursor[t], 1);
-            wl.order[pos] = i;
-            wl.ntile[pos] = t;
-            sorted[pos] = t;
+        for_each_lane([&](int i, int t, bool active) {
+            const int pos = wave_counted_add(cursor, t, active);
+            if (active) {
+                wl.order[pos] = i;
+                wl.ntile[pos] = t;
+                sorted[pos] = t;
+            }
         });
     } else if (kind == RANK_BITONIC) {
         int P = 1;
