@@ -872,7 +872,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) o[db] = (f32x16){};
 
-        for (int c = 0; c < n_tiles - jump; ++c) {
+        // Tile c's K and V into registers (this thread's chunks), and from
+        // there into LDS: the loads of tile c + 1 are in flight while tile c
+        // is computed.
+        const int n_iter = n_tiles - jump;
+        float4 pk[Cfg::CHUNKS], pv[Cfg::CHUNKS];
+        auto fetch = [&](int c) {
             const int k0 = (c >= nh ? c + jump : c) * BK;
             const bool from_cache = a.hoff && k0 < hist;
 #pragma unroll
@@ -893,11 +898,23 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
                     xk = *reinterpret_cast<const float4*>(a.k + off);
                     xv = *reinterpret_cast<const float4*>(a.v + off);
                 }
+                pk[i] = xk;
+                pv[i] = xv;
+            }
+        };
+        if (n_iter > 0) fetch(0);
+        for (int c = 0; c < n_iter; ++c) {
+            const int k0 = (c >= nh ? c + jump : c) * BK;
+#pragma unroll
+            for (int i = 0; i < Cfg::CHUNKS; ++i) {
+                const int id = tid + i * Cfg::THREADS;
+                const int r = id / (D / 4), c4 = id % (D / 4);
                 float* kd = kl + r * Cfg::KSTR + c4 * 4;
-                kd[0] = xk.x; kd[1] = xk.y; kd[2] = xk.z; kd[3] = xk.w;
-                *reinterpret_cast<float4*>(vl + r * Cfg::VSTR + c4 * 4) = xv;
+                kd[0] = pk[i].x; kd[1] = pk[i].y; kd[2] = pk[i].z; kd[3] = pk[i].w;
+                *reinterpret_cast<float4*>(vl + r * Cfg::VSTR + c4 * 4) = pv[i];
             }
             __syncthreads();
+            if (c + 1 < n_iter) fetch(c + 1);
             // Skip tiles no row of the wave sees: past its last row, or all
             // candidate keys below its first row.
             const bool skip = !wave_live || k0 > wr0 + 31 || (k0 >= hist && k0 + BK - 1 < wr0);
