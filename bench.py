@@ -66,11 +66,11 @@ METRIC_RAB_BWD = "HSTU attn bwd with relative attention bias (dq, dk, dv, table 
 # source the bench reports traffic as null.
 TRAFFIC = {
     "kernel_source": "generative_recommendation_attention_amd/csrc/attn_fwd.hip",
-    "kernel_sha256": "b8bf6a7c6e0d86adeb56993150b36d7d3eae3f3bdb93e3a470acf75c789425d1",
+    "kernel_sha256": "01c318e4cd96e0d05bab6f52757666ffe16df37f042baec275a2904aa32904b0",
     "fetch_scale": 2.0,
     "write_scale": 1.0,
-    "fetch_kib": {2: 94096.7},
-    "write_kib": {2: 37939.6},
+    "fetch_kib": {2: 93987.8},
+    "write_kib": {2: 37938.6},
 }
 
 
