@@ -778,8 +778,14 @@ template <int D, int NW, int BK>
 struct TileF32 {
     static constexpr int BQ = NW * 32;
     static constexpr int THREADS = NW * 64;
-    static constexpr int KSTR = D + 2;   // floats
-    static constexpr int VSTR = D + 8;   // floats
+    // K rows hold a row's even features, then its odd ones (the two k-slices
+    // the lane halves read), so a lane reads four k-steps' operands with one
+    // 16-byte read; V is held transposed (a head-dim row per feature, keys
+    // along it), so one 16-byte read gives four keys' operands.  Strides in
+    // floats, multiples of 4 with 4 mod 32, which spreads 16-byte reads of
+    // consecutive rows over the banks.
+    static constexpr int KSTR = D + 4;
+    static constexpr int VTSTR = BK + 4;
     static constexpr int CHUNKS = BK * D / 4 / THREADS;  // 16-byte loads per thread per tensor
     static_assert(CHUNKS * THREADS * 4 == BK * D, "tile must split evenly");
 };
@@ -809,11 +815,11 @@ struct KernelArgsF32 {
 };
 
 template <int D, int NW, int BK, bool FUSED>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma_f32(KernelArgsF32 a) {
     using Cfg = TileF32<D, NW, BK>;
     constexpr int BQ = Cfg::BQ;
     __shared__ __attribute__((aligned(16))) float kl[BK * Cfg::KSTR];
-    __shared__ __attribute__((aligned(16))) float vl[BK * Cfg::VSTR];
+    __shared__ __attribute__((aligned(16))) float vt[D * Cfg::VTSTR];
     __shared__ int s_item[NQ];
     __shared__ LocalTables lt;
     static_assert(NW * 64 >= FUSE_SEQS && NW * 64 >= 32 * NQ, "fused tables need a thread per sequence");
@@ -909,9 +915,16 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
             for (int i = 0; i < Cfg::CHUNKS; ++i) {
                 const int id = tid + i * Cfg::THREADS;
                 const int r = id / (D / 4), c4 = id % (D / 4);
-                float* kd = kl + r * Cfg::KSTR + c4 * 4;
-                kd[0] = pk[i].x; kd[1] = pk[i].y; kd[2] = pk[i].z; kd[3] = pk[i].w;
-                *reinterpret_cast<float4*>(vl + r * Cfg::VSTR + c4 * 4) = pv[i];
+                // features 4 c4 .. 4 c4 + 3: the even ones to 2 c4, 2 c4 + 1,
+                // the odd ones to D/2 + 2 c4, D/2 + 2 c4 + 1
+                float* kd = kl + r * Cfg::KSTR;
+                *reinterpret_cast<float2*>(kd + 2 * c4) = make_float2(pk[i].x, pk[i].z);
+                *reinterpret_cast<float2*>(kd + D / 2 + 2 * c4) = make_float2(pk[i].y, pk[i].w);
+                float* vd = vt + 4 * c4 * Cfg::VTSTR + r;
+                vd[0] = pv[i].x;
+                vd[Cfg::VTSTR] = pv[i].y;
+                vd[2 * Cfg::VTSTR] = pv[i].z;
+                vd[3 * Cfg::VTSTR] = pv[i].w;
             }
             __syncthreads();
             if (c + 1 < n_iter) fetch(c + 1);
@@ -923,35 +936,55 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_mfma_f32(KernelArgsF32 a) {
 #pragma unroll
                 for (int kb = 0; kb < BK / 32; ++kb) {
                     f32x16 st = (f32x16){};
+                    // k-step ks takes feature 2 ks + g of key row kb*32 + l32
+                    const float* krow = kl + (kb * 32 + l32) * Cfg::KSTR + g * (D / 2);
 #pragma unroll
-                    for (int ks = 0; ks < D / 2; ++ks)
-                        st = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                                kl[(kb * 32 + l32) * Cfg::KSTR + 2 * ks + g], qf[ks], st, 0, 0, 0);
+                    for (int j = 0; j < D / 8; ++j) {
+                        const float4 kv = *reinterpret_cast<const float4*>(krow + 4 * j);
+                        st = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.x, qf[4 * j], st, 0, 0, 0);
+                        st = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.y, qf[4 * j + 1], st, 0, 0, 0);
+                        st = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.z, qf[4 * j + 2], st, 0, 0, 0);
+                        st = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.w, qf[4 * j + 3], st, 0, 0, 0);
+                    }
+                    // Registers 4 rq .. 4 rq + 3 hold keys kb*32 + 8 rq + 4 g + 0..3:
+                    // one 16-byte read of V^T per head-dim block feeds their
+                    // four k-steps of the second product.
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int kvl = kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                        float p;
-                        if (a.ts) {
-                            const int key = k0 + kvl;
-                            // (a candidate row sits at position hist; its own
-                            // key at distance 0)
-                            const int dist = key == my_row ? 0 : min(my_row, hist) - key;
-                            float bias = (dist >= 0 && dist < a.npos) ? a.wpos[dist] : 0.0f;
-                            const uint32_t x = trp1 - (key < s ? (uint32_t)a.ts[start + key] : 0u);
-                            const int lz = __clz((int)x);   // 32 for x == 0 (gap -1)
-                            bias += a.wtime[lz == 32 ? a.ntime - 1 : min(31 - lz, a.ntime - 1)];
-                            p = silu_scaled(__builtin_fmaf(st[r], a.score_scale, bias * -LOG2E));
-                        } else {
-                            p = silu_scaled(st[r] * a.score_scale);
+                    for (int rq = 0; rq < 4; ++rq) {
+                        float p4[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = 4 * rq + i;
+                            const int kvl = kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                            float p;
+                            if (a.ts) {
+                                const int key = k0 + kvl;
+                                // (a candidate row sits at position hist; its own
+                                // key at distance 0)
+                                const int dist = key == my_row ? 0 : min(my_row, hist) - key;
+                                float bias = (dist >= 0 && dist < a.npos) ? a.wpos[dist] : 0.0f;
+                                const uint32_t x = trp1 - (key < s ? (uint32_t)a.ts[start + key] : 0u);
+                                const int lz = __clz((int)x);   // 32 for x == 0 (gap -1)
+                                bias += a.wtime[lz == 32 ? a.ntime - 1 : min(31 - lz, a.ntime - 1)];
+                                p = silu_scaled(__builtin_fmaf(st[r], a.score_scale, bias * -LOG2E));
+                            } else {
+                                p = silu_scaled(st[r] * a.score_scale);
+                            }
+                            if (partial) {
+                                const int key = k0 + kvl;
+                                p = (key <= my_row && (key < hist || key == my_row)) ? p : 0.0f;
+                            }
+                            p4[i] = p;
                         }
-                        if (partial) {
-                            const int key = k0 + kvl;
-                            p = (key <= my_row && (key < hist || key == my_row)) ? p : 0.0f;
-                        }
 #pragma unroll
-                        for (int db = 0; db < D / 32; ++db)
-                            o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                                    vl[kvl * Cfg::VSTR + db * 32 + l32], p, o[db], 0, 0, 0);
+                        for (int db = 0; db < D / 32; ++db) {
+                            const float4 vv = *reinterpret_cast<const float4*>(
+                                    vt + (db * 32 + l32) * Cfg::VTSTR + kb * 32 + 8 * rq + 4 * g);
+                            o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.x, p4[0], o[db], 0, 0, 0);
+                            o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.y, p4[1], o[db], 0, 0, 0);
+                            o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.z, p4[2], o[db], 0, 0, 0);
+                            o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.w, p4[3], o[db], 0, 0, 0);
+                        }
                     }
                 }
             }
