@@ -66,11 +66,11 @@ METRIC_RAB_BWD = "HSTU attn bwd with relative attention bias (dq, dk, dv, table 
 # source the bench reports traffic as null.
 TRAFFIC = {
     "kernel_source": "generative_recommendation_attention_amd/csrc/attn_fwd.hip",
-    "kernel_sha256": "01c318e4cd96e0d05bab6f52757666ffe16df37f042baec275a2904aa32904b0",
+    "kernel_sha256": "74eeb4f0558d0e61af4c1d3efcc3fab7e55984322bc1fc976963011773781737",
     "fetch_scale": 2.0,
     "write_scale": 1.0,
-    "fetch_kib": {2: 93987.8},
-    "write_kib": {2: 37938.6},
+    "fetch_kib": {2: 93835.1},
+    "write_kib": {2: 37940.2},
 }
 
 
