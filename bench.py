@@ -494,14 +494,24 @@ def main() -> int:
     peak = PEAK_MFMA_TFLOPS[case.dtype]
     traffic = (None if (args.targets or args.cached or args.backward or args.dense or args.rab or
                         args.graph) else traffic_bytes(args.workload))
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+    # The bound is the roofline the workload's arithmetic intensity (useful
+    # FLOPs per algorithmic byte) falls under: HBM below the ridge point
+    # (peak FLOP/s over 8 TB/s), the matrix cores above it.
+    hbm_gbs = alg_bytes / (attn_ms * 1e-3) / 1e9
+    if flops / alg_bytes < peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+        bound = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": PEAK_HBM_GBS,
+                 "unit": "GB/s", "frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
+                 "mfma_frac": round(achieved / peak, 4)}
+    else:
+        bound = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
+    roofline = {**bound, "traffic": traffic,
                 "kernel": ("attn_bwd_dkv + attn_bwd_dq + table-gradient sum" if args.backward and
                            args.rab else "attn_bwd_dkv + attn_bwd_dq" if args.backward else
                            "attn_fwd_mfma16" if case.dtype != "fp32" else "attn_fwd_mfma_f32") +
                           (" (graph replay, whole call)" if args.graph else ""),
                 "kernel_ms": round(attn_ms, 5), "sched_kernel_ms": round(sched_ms, 5),
-                "hbm_frac": round(alg_bytes / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4)}
 
     cpu = None
     if args.cpu_budget > 0:
