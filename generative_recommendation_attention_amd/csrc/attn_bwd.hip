@@ -124,6 +124,28 @@ __device__ __forceinline__ int ffbh_u32(uint32_t x) {
     return f;
 }
 
+// Wave-wide minimum / maximum (every lane takes part; the result is uniform).
+__device__ __forceinline__ int wave_min_i32(int x) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) x = min(x, __shfl_xor(x, o, 64));
+    return __builtin_amdgcn_readfirstlane(x);
+}
+__device__ __forceinline__ int wave_max_i32(int x) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) x = max(x, __shfl_xor(x, o, 64));
+    return __builtin_amdgcn_readfirstlane(x);
+}
+
+// Blocks whose every pair lies in the last time bucket (the latest key at
+// least 2^(ntime-1) - 1 before the earliest query) take the time term as one
+// constant, the last bucket's entry, instead of a per-pair lookup: the same
+// values, since every such pair's capped bucket is the last one.  At d = 64
+// only: at d = 128 the second path costs the bias kernels 12-20 more
+// spilled registers.
+__device__ __forceinline__ bool rab_far(int rmin, int kmax, int ntime) {
+    return (int64_t)rmin - kmax >= ((int64_t)1 << (ntime - 1)) - 1;
+}
+
 // Shapes shared by both kernels: 4 waves of 32 rows (128 rows per item), 32-row
 // streamed blocks.
 template <int D>
@@ -334,9 +356,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv(typename BwdArgsOf<RAB>::
         for (int db = 0; db < C::NDB; ++db) dk[db] = dv[db] = (f32x16){};
         // With the bias: 1 - ts of this lane's key, so that ts_q + c1 = gap + 1.
         uint32_t c1 = 0;
-        if constexpr (RAB)
+        int kmax = 0;   // the wave's latest key timestamp
+        if constexpr (RAB) {
             c1 = 1u - __builtin_amdgcn_raw_buffer_load_b32(
                               make_rsrc(a.ts + start + kw0, (int64_t)(s - kw0) * 4), l32 * 4, 0, 0);
+            if constexpr (D == 64)
+                kmax = wave_max_i32(kw0 + l32 < s ? (int)(1u - c1) : INT32_MIN);
+        }
 
         // Block c into slot c % NS; blocks are issued PF ahead, also past the
         // last one (an empty buffer range: nothing is read), so that a wait
@@ -379,14 +405,27 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv(typename BwdArgsOf<RAB>::
                     const unsigned char* ra = lds + NS * SLOT + (c % NS) * RABB_WORDS * 4;
                     const float* win = reinterpret_cast<const float*>(ra + 4 * RABB_TS) +
                                        (128 - 32 * wv - l32 + 4 * g);
+                    // (query rows past the sequence read 0: a block holding
+                    // them only looks nearer)
+                    bool far = false;
+                    if constexpr (D == 64)
+                        far = rab_far(wave_min_i32(reinterpret_cast<const int*>(ra)[l32]), kmax,
+                                      a.ntime);
+                    if (far) {
+                        const float tlast = ttab[0];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const u32x4 tq =
-                                *reinterpret_cast<const u32x4*>(ra + 4 * (4 * g + 8 * j));
+                        for (int r = 0; r < 16; ++r)
+                            st[r] = (win[8 * (r >> 2) + (r & 3)] + tlast) * a.bias_scale;
+                    } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int f = ffbh_u32(tq[e] + c1);
-                            st[4 * j + e] = (win[8 * j + e] + ttab[f + 1]) * a.bias_scale;
+                        for (int j = 0; j < 4; ++j) {
+                            const u32x4 tq =
+                                    *reinterpret_cast<const u32x4*>(ra + 4 * (4 * g + 8 * j));
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const int f = ffbh_u32(tq[e] + c1);
+                                st[4 * j + e] = (win[8 * j + e] + ttab[f + 1]) * a.bias_scale;
+                            }
                         }
                     }
                 }
@@ -560,10 +599,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
         for (int db = 0; db < C::NDB; ++db) dq[db] = (f32x16){};
         // With the bias: ts of this lane's query + 1.
         uint32_t trp1 = 0;
-        if constexpr (RAB)
+        int rmin = 0;   // the wave's earliest query timestamp
+        if constexpr (RAB) {
             trp1 = __builtin_amdgcn_raw_buffer_load_b32(
                            make_rsrc(a.ts + start + wr0, (int64_t)(s - wr0) * 4), l32 * 4, 0, 0) +
                    1u;
+            if constexpr (D == 64)
+                rmin = wave_min_i32(wr0 + l32 < s ? (int)(trp1 - 1u) : INT32_MAX);
+        }
 
         // (staged PF ahead as in the dK/dV kernel)
         auto issue = [&](int c) {
@@ -599,19 +642,34 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
             if (!skip) {
                 f32x16 st = (f32x16){}, dp = (f32x16){};
                 u32x4 tk[4];
+                bool far = false;
                 if constexpr (RAB) {
                     // rab / alpha for query wr0 + l32 and key k0 + 8(r/4) + 4g + r%4:
                     // distance = window entry 32wv + l32 + 32 - 4g - 8(r/4) - r%4
                     const unsigned char* ra = lds + NS * SLOT + (c % NS) * RABB_WORDS * 4;
                     const float* win = reinterpret_cast<const float*>(ra + 4 * RABB_TS) +
                                        (32 * wv + l32 + 5 - 4 * g);
+                    // (keys past the sequence read 0: a block holding them
+                    // only looks nearer)
+                    if constexpr (D == 64)
+                        far = rab_far(rmin,
+                                      wave_max_i32(reinterpret_cast<const int*>(ra)[l32]),
+                                      a.ntime);
+                    if (far) {
+                        const float tlast = ttab[0];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        tk[j] = *reinterpret_cast<const u32x4*>(ra + 4 * (4 * g + 8 * j));
+                        for (int r = 0; r < 16; ++r)
+                            st[r] = (win[27 - 8 * (r >> 2) - (r & 3)] + tlast) * a.bias_scale;
+                    } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int f = ffbh_u32(trp1 - tk[j][e]);
-                            st[4 * j + e] = (win[27 - 8 * j - e] + ttab[f + 1]) * a.bias_scale;
+                        for (int j = 0; j < 4; ++j) {
+                            tk[j] = *reinterpret_cast<const u32x4*>(ra + 4 * (4 * g + 8 * j));
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const int f = ffbh_u32(trp1 - tk[j][e]);
+                                st[4 * j + e] =
+                                        (win[27 - 8 * j - e] + ttab[f + 1]) * a.bias_scale;
+                            }
                         }
                     }
                 }
@@ -664,17 +722,23 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
                     // capped bucket of v_ffbh_u32 result f is min(31 - f, ntime - 1)
                     // (f = -1, a gap of -1, gives 32: the last bucket too).
                     const int cap = a.ntime - 1;
-                    int prev = min(31 - ffbh_u32(trp1 - tk[0][0]), cap);
+                    int prev = cap;
                     float run = 0.0f;
+                    if (D == 64 && far) {   // every pair in the last bucket
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int b = min(31 - ffbh_u32(trp1 - tk[r >> 2][r & 3]), cap);
-                        if (b != prev) {
-                            atomicAdd(&tbins[prev], run);
-                            run = 0.0f;
-                            prev = b;
+                        for (int r = 0; r < 16; ++r) run += ds[r];
+                    } else {
+                        prev = min(31 - ffbh_u32(trp1 - tk[0][0]), cap);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int b = min(31 - ffbh_u32(trp1 - tk[r >> 2][r & 3]), cap);
+                            if (b != prev) {
+                                atomicAdd(&tbins[prev], run);
+                                run = 0.0f;
+                                prev = b;
+                            }
+                            run += ds[r];
                         }
-                        run += ds[r];
                     }
                     const int p0 = __builtin_amdgcn_readfirstlane(prev);
                     if (__all(prev == p0)) {
