@@ -138,3 +138,17 @@ def test_rab_bwd_qkv_deterministic():
     b = run_bwd_rab(case, dout, r)
     for x, y in zip(a[:3], b[:3]):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+@pytest.mark.parametrize("step", [3, 4, 64])
+def test_rab_bwd_last_bucket_boundary(step):
+    """Evenly spaced timestamps put the last-bucket boundary (gap 127 with 8
+    buckets) a fixed number of keys below each query, so some 32-row blocks
+    lie entirely in the last bucket and their neighbours do not; one time
+    entry per bucket, well apart, makes a block misjudged either way show in
+    dq, dk, dv and in the time table's gradient."""
+    case, dout, r = make([300, 129, 64, 513], 2, 64, "bf16", 600, 8, seed=1570)
+    r.timestamps = (np.arange(case.total, dtype=np.int64) * step).astype(np.int32)
+    r.time_bias = (np.arange(8, dtype=np.float32) * np.float32(0.75) - np.float32(2.0))
+    log(f"rab bwd last-bucket boundary, timestamp step {step}")
+    compare(case, dout, r, run_bwd_rab(case, dout, r), f"rab bwd last bucket step {step}")
