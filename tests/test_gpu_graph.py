@@ -149,3 +149,27 @@ def test_forward_then_backward_with_bias_in_one_graph():
         return [out] + list(hstu.hstu_attn_bwd_rab(q, k, v, dout, off, ts, wp, wt, c.alpha,
                                                    c.n))
     check_replays(fn, exact=[0, 1, 2, 3], close=[4, 5], name="bias forward + backward")
+
+
+def test_layer_in_one_graph():
+    """Input projection, attention on its q, k, v, output projection: one
+    recorded layer, replayed against the eager layer."""
+    T_lengths = [300, 77, 129]
+    H, d, dm = 4, 64, 256
+    c = workloads.make_case(T_lengths, H, d, "bf16", seed=3150)
+    off = torch.from_numpy(c.offsets).cuda()
+    T = c.total
+    g = torch.Generator(device="cpu").manual_seed(3151)
+    x = (torch.randn(T, dm, generator=g) * 0.5).to(torch.bfloat16).cuda()
+    w1 = (torch.randn(4 * H * d, dm, generator=g) / 16).to(torch.bfloat16).cuda()
+    b1 = (torch.randn(4 * H * d, generator=g) * 0.1).cuda()
+    w2 = (torch.randn(dm, H * d, generator=g) / 16).to(torch.bfloat16).cuda()
+    b2 = (torch.randn(dm, generator=g) * 0.1).cuda()
+    gamma = (1.0 + 0.1 * torch.randn(H * d, generator=g)).cuda()
+    beta = (0.1 * torch.randn(H * d, generator=g)).cuda()
+
+    def fn():
+        u, v, q, k = hstu.hstu_layer_in_proj(x, w1, b1, H, d)
+        a = hstu.hstu_attn_fwd(q, k, v, off, c.alpha, c.n)
+        return [hstu.hstu_layer_out_proj(a, u, x, gamma, beta, 1e-5, w2, b2)]
+    check_replays(fn, name="layer")
