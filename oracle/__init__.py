@@ -10,11 +10,13 @@ Two independent evaluations of the same definition live here:
 
 * ``fwd`` / ``rows``: the plain row-by-row fp64 loop in ``hstu_oracle.c``
   (OpenMP over (sequence, head) pairs), built with gcc;
-* ``dense_unfused``: numpy fp64, one sequence at a time, written as the five
-  unfused steps the Ascend HSTU blog ("都是生成式推荐，为什么昇腾这么快？",
-  §1) gives as its PyTorch definition: scores = Q K^T, scores *= alpha,
-  silu, multiply by mask / n with an explicit lower-triangular 0/1 mask
-  (§3.1-§3.2), then scores @ V.  Jagged packing follows §4.2 of that page.
+* ``dense_pairs``: numpy fp64, one sequence at a time, written from the
+  definition as a sum over kept (row, key) pairs: a boolean matrix says which
+  keys each row sees (key <= row for the causal mask, the Ascend HSTU blog
+  "都是生成式推荐，为什么昇腾这么快？" §3.1-§3.2), every score of a kept pair
+  is formed with einsum, weighted by silu(alpha * score), and the weighted
+  values of a row's kept keys are summed and divided by n.  Jagged packing
+  follows §4.2 of that page.
 
 The ``num_targets`` arguments give the target-aware (M-FALCON) mask of the
 HSTU paper translation (§3.4, Appendix H, Algorithm 1 and Fig. 11): the last
@@ -468,7 +470,7 @@ def threads(lib: Optional[ctypes.CDLL] = None) -> int:
 
 
 # ---------------------------------------------------------------------------
-# Dense unfused evaluation (numpy fp64), for small inputs.
+# Dense pair-set evaluation (numpy fp64), for small inputs.
 # ---------------------------------------------------------------------------
 
 def widen(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -486,25 +488,25 @@ def _silu(x: np.ndarray) -> np.ndarray:
     return x * sig
 
 
-def falcon_mask(s: int, t: int) -> np.ndarray:
-    """The (s, s) 0/1 mask of Algorithm 1 (HSTU paper translation, Appendix H):
-    lower-triangular, then entries (i, j) with i, j >= s - t and i != j
-    cleared, so the last t (candidate) rows see the history and themselves."""
-    m = np.tril(np.ones((s, s), dtype=np.float64))
+def sees(s: int, t: int = 0) -> np.ndarray:
+    """Boolean (s, s) matrix: entry (row, key) is True iff the row sees the
+    key.  Causal: key <= row.  With t candidates (HSTU paper translation,
+    Appendix H, Algorithm 1), rows and keys past the history h = s - t also
+    need key < h or key == row."""
+    r = np.arange(s)[:, None]
+    c = np.arange(s)[None, :]
     h = s - t
-    for i in range(h, s):
-        for j in range(h, s):
-            if i != j:
-                m[i, j] = 0.0
-    return m
+    return (c <= r) & ((c < h) | (c == r))
 
 
-def dense_unfused(q, k, v, offsets, heads: int, d: int, alpha: float, n: float,
-                  dtype: str, num_targets=None) -> np.ndarray:
-    """Per sequence: the (heads, s, s) score tensor is formed in full, then
-    scaled, passed through SiLU, multiplied by the 0/1 mask / n and applied to
-    V.  The mask is tril(ones), or falcon_mask with the sequence's candidate
-    count when num_targets is given."""
+def dense_pairs(q, k, v, offsets, heads: int, d: int, alpha: float, n: float,
+                dtype: str, num_targets=None) -> np.ndarray:
+    """out[r, h] = (1/n) * sum over keys c that row r sees of
+    silu(alpha * <q[r, h], k[c, h]>) * v[c, h], per sequence, every
+    (row, key) pair's score formed with einsum and pairs the row does not see
+    left out of the sum (their weight is set to zero before the sum over keys).
+    The visibility is ``sees`` (causal, or target-aware with the sequence's
+    candidate count)."""
     Q, K, V = (widen(a, dtype).reshape(-1, heads, d) for a in (q, k, v))
     off = np.asarray(offsets, dtype=np.int64)
     out = np.zeros((int(off[-1]), heads, d), dtype=np.float64)
@@ -513,17 +515,9 @@ def dense_unfused(q, k, v, offsets, heads: int, d: int, alpha: float, n: float,
         s = b - a
         if s == 0:
             continue
-        Qi = Q[a:b].transpose(1, 0, 2)  # (heads, s, d)
-        Ki = K[a:b].transpose(1, 0, 2)
-        Vi = V[a:b].transpose(1, 0, 2)
-        x = np.matmul(Qi, Ki.transpose(0, 2, 1))  # (heads, s, s)
-        x = x * alpha
-        x = _silu(x)
-        if num_targets is None:
-            mask = np.tril(np.ones((s, s), dtype=np.float64))
-        else:
-            mask = falcon_mask(s, min(max(int(num_targets[i]), 0), s))
-        x = x * (mask / n)
-        o = np.matmul(x, Vi)  # (heads, s, d)
-        out[a:b] = o.transpose(1, 0, 2)
+        t = 0 if num_targets is None else min(max(int(num_targets[i]), 0), s)
+        seen = sees(s, t)
+        score = np.einsum("rhe,che->hrc", Q[a:b], K[a:b])
+        w = np.where(seen[None, :, :], _silu(alpha * score), 0.0)
+        out[a:b] = np.einsum("hrc,che->rhe", w, V[a:b]) / n
     return out

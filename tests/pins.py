@@ -7,8 +7,7 @@ functions run against copies of the oracle built with a planted mistake (see
 test_oracle_mutants.py), to show that each plausible mistake fails at least one
 of them.
 
-Definition being pinned (Ascend HSTU blog, §1 formula and five-step
-definition; §3.2 causal diagonal; §4.2 jagged layout):
+Definition being pinned (Ascend HSTU blog, §1 formula; §3.2 causal diagonal; §4.2 jagged layout):
     out[r] = (1/n) * sum_{c <= r, same sequence} silu(alpha <q_r, k_c>) v_c
 """
 from __future__ import annotations
@@ -242,18 +241,19 @@ def pin_invariants(lib) -> None:
 
 
 # ---------------------------------------------------------------------------
-# Brute force: the unfused dense evaluation on tiny inputs
+# Brute force: the dense pair-set evaluation on tiny inputs
 # ---------------------------------------------------------------------------
 
 def pin_dense_bruteforce(lib) -> None:
-    """The loop oracle against the five-step dense evaluation (explicit
-    (s, s) score tensor and tril mask), on tiny inputs in every dtype."""
+    """The loop oracle against the dense evaluation over every (row, key)
+    pair (einsum scores, boolean visibility matrix), on tiny inputs in every
+    dtype."""
     specs = [([1], 1, 1), ([2, 3], 1, 2), ([16, 1, 0, 7, 5], 3, 8), ([9, 4], 2, 3)]
     for dtype in ("fp32", "fp16", "bf16"):
         for seed, (lengths, heads, d) in enumerate(specs):
             c = workloads.make_case(lengths, heads, d, dtype, 100 + seed, alpha=0.37, n=6.0)
             a = oracle.fwd(c.q, c.k, c.v, c.offsets, heads, d, c.alpha, c.n, dtype, lib=lib)
-            b = oracle.dense_unfused(c.q, c.k, c.v, c.offsets, heads, d, c.alpha, c.n, dtype)
+            b = oracle.dense_pairs(c.q, c.k, c.v, c.offsets, heads, d, c.alpha, c.n, dtype)
             err = np.max(np.abs(a - b))
             assert err <= 1e-12 * max(1.0, np.max(np.abs(b))), (dtype, lengths, err)
 

@@ -25,7 +25,7 @@ def _case(lengths, heads, d, seed, targets=None, alpha=0.7, n=3.0):
 
 def _dense_loss(q, k, v, dout, offsets, heads, d, alpha, n, targets):
     """sum(dout * out) with out from the numpy dense evaluation (float64 in)."""
-    out = oracle.dense_unfused(q, k, v, offsets, heads, d, alpha, n, "fp32",
+    out = oracle.dense_pairs(q, k, v, offsets, heads, d, alpha, n, "fp32",
                                num_targets=targets)
     return float(np.sum(dout * out))
 

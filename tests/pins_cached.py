@@ -6,7 +6,7 @@ candidates only and attends, under the target-aware mask, to the cached
 history's K and V plus itself.  Each pin raises AssertionError when the
 oracle disagrees with a closed form, with the equivalence the appendix states
 (the cached pass gives the candidates exactly what one pass over history +
-candidates gives), with the five unfused steps on the concatenated sequence,
+candidates gives), with the dense pair-set evaluation on the concatenated sequence,
 or with separate causal passes per candidate.
 """
 from __future__ import annotations
@@ -106,12 +106,12 @@ def pin_cached_equals_one_pass(lib) -> None:
     """Appendix H: with the history's K and V taken from the cache, a
     micro-batch's candidates get what one pass over history + candidates under
     the target-aware mask gives them (here: the row loop with the mask, and the
-    five unfused steps with the explicit mask matrix)."""
+    dense pair-set evaluation with its visibility matrix)."""
     hc, cc = random_cached([7, 0, 40, 3], [3, 2, 5, 0], 2, 64, "bf16", seed=61, n=40.0)
     got = cached_of(hc, cc, "bf16", lib)
     q, k, v, off, tg = concatenated(hc, cc)
     loop = oracle.fwd(q, k, v, off, 2, 64, cc.alpha, cc.n, "bf16", lib=lib, num_targets=tg)
-    dense = oracle.dense_unfused(q, k, v, off, 2, 64, cc.alpha, cc.n, "bf16", num_targets=tg)
+    dense = oracle.dense_pairs(q, k, v, off, 2, 64, cc.alpha, cc.n, "bf16", num_targets=tg)
     for ref in (cand_rows_of_concat(hc, cc, loop), cand_rows_of_concat(hc, cc, dense)):
         assert np.max(np.abs(got - ref)) <= 1e-12 * max(1.0, float(np.max(np.abs(ref))))
 

@@ -58,13 +58,13 @@ def pin_targets_separate_passes(lib) -> None:
 
 
 def pin_targets_dense_mask(lib) -> None:
-    """Against the five unfused steps with the 0/1 mask built as Algorithm 1
-    builds it (lower-triangular, then candidate-candidate entries cleared)."""
+    """Against the dense pair-set evaluation, whose visibility matrix follows
+    Algorithm 1 (lower-triangular, candidate-candidate entries cleared)."""
     case = workloads.make_case([6, 1, 0, 9, 4], 3, 64, "bf16", seed=41)
     tg = np.array([2, 1, 0, 9, 1], dtype=np.int32)
     got = oracle.fwd(case.q, case.k, case.v, case.offsets, 3, 64, case.alpha, case.n, "bf16",
                      lib=lib, num_targets=tg)
-    ref = oracle.dense_unfused(case.q, case.k, case.v, case.offsets, 3, 64, case.alpha, case.n,
+    ref = oracle.dense_pairs(case.q, case.k, case.v, case.offsets, 3, 64, case.alpha, case.n,
                                "bf16", num_targets=tg)
     assert np.max(np.abs(got - ref)) <= 1e-12 * max(1.0, float(np.max(np.abs(ref))))
 
