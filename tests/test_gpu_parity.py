@@ -1,17 +1,18 @@
 """Parity of the HIP path against the fp64 CPU oracle, through the C ABI.
 
-Small cases are compared element by element over the whole output; the five
-named workloads at full size are compared on sampled rows (tile boundaries,
-first/last rows, random rows) that the oracle evaluates one by one, and
-checked for properties that hold at any size.
+Small cases and the five named workloads at full size (the Ascend HSTU blog's
+QKV (16, 4, 4096, 64) shape of §3.2 among them, lengths up to its 20480 bound
+of §3.1) are compared element by element over the whole output, with both
+tolerances taken over every T * heads * d element; properties that hold at
+any size (the sign-flip identity, determinism, sequence independence) are
+checked as well.
 """
 import numpy as np
 import pytest
 
 import oracle
 import workloads
-from helpers import (assert_close, device_case, errors, from_torch, log, sample_rows, to_torch,
-                     TOL)
+from helpers import assert_close, device_case, errors, from_torch, log, to_torch, TOL
 
 torch = pytest.importorskip("torch")
 hstu = pytest.importorskip("generative_recommendation_attention_amd")
@@ -72,22 +73,20 @@ def test_workload1_full_compare():
 
 
 @pytest.mark.parametrize("num", [2, 3, 4, 5])
-def test_workload_sampled_rows(num):
+def test_workload_full_compare(num):
+    """The whole output of the workload against the oracle's whole output,
+    in the launch configuration the benchmark times."""
     case = workloads.workload(num)
     log(f"workload {num}: {case.description}; T={case.total}")
-    got = run_gpu(case)
-    tok, hd = sample_rows(case)
-    log(f"  checking {len(tok)} sampled rows")
-    g = from_torch(got[torch.from_numpy(tok).cuda(), torch.from_numpy(hd.astype(np.int64)).cuda()],
-                   case.dtype)
-    ref = oracle.rows(case.q, case.k, case.v, case.offsets, case.heads, case.d, case.alpha,
-                      case.n, case.dtype, tok, hd)
-    mr, l2 = assert_close(g, ref, case.dtype, f"workload {num} sampled")
-    log(f"  max|err|/max|ref| = {mr:.3e}, rel L2 = {l2:.3e}")
-    assert torch.isfinite(got.float()).all().item()
+    got = from_torch(run_gpu(case), case.dtype)
+    log(f"  oracle over all {case.total * case.heads} rows")
+    ref = oracle.fwd(case.q, case.k, case.v, case.offsets, case.heads, case.d, case.alpha,
+                     case.n, case.dtype)
+    mr, l2 = assert_close(got, ref, case.dtype, f"workload {num} whole output")
+    log(f"  max|err|/max|ref| = {mr:.3e}, rel L2 = {l2:.3e} over {got.size} elements")
 
 
-@pytest.mark.parametrize("num", [2, 5])
+@pytest.mark.parametrize("num", [2, 3, 4, 5])
 def test_sign_flip_identity_full_size(num):
     """hstu(Q) - hstu(-Q) = (alpha/n) tril(Q K^T) V for every sequence and head,
     checked over the whole output with torch's float32 matmul as reference."""
@@ -199,13 +198,9 @@ def test_more_sequences_than_the_sort_takes():
     lengths = [int(x) for x in rng.integers(0, 40, size=20000)]
     case = workloads.make_case(lengths, 1, 64, "bf16", seed=18, n=40.0)
     log(f"20000 sequences, T={case.total}")
-    got = run_gpu(case)
-    tok, hd = sample_rows(case, max_seqs=200)
-    g = from_torch(got[torch.from_numpy(tok).cuda(), torch.from_numpy(hd.astype(np.int64)).cuda()],
-                   "bf16")
-    ref = oracle.rows(case.q, case.k, case.v, case.offsets, 1, 64, case.alpha, case.n, "bf16",
-                      tok, hd)
-    assert_close(g, ref, "bf16", "20000 sequences")
+    got = from_torch(run_gpu(case), "bf16")
+    ref = oracle.fwd(case.q, case.k, case.v, case.offsets, 1, 64, case.alpha, case.n, "bf16")
+    assert_close(got, ref, "bf16", "20000 sequences")
 
 
 @pytest.mark.parametrize("sort", ["bitonic", "input"])
