@@ -59,7 +59,9 @@ class HstuError(RuntimeError):
 
 class KernelTimes(ctypes.Structure):
     _fields_ = [("calls", ctypes.c_int64), ("sched_ms", ctypes.c_double),
-                ("attn_ms", ctypes.c_double), ("dropped", ctypes.c_int64)]
+                ("attn_ms", ctypes.c_double), ("dropped", ctypes.c_int64),
+                ("attn_min_ms", ctypes.c_double), ("attn_median_ms", ctypes.c_double),
+                ("clock_mhz", ctypes.c_double)]
 
 
 _lib: Optional[ctypes.CDLL] = None

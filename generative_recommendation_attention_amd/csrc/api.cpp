@@ -3,11 +3,13 @@
 // and the two launches (work list, attention) on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <list>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <utility>
 #include <vector>
@@ -40,6 +42,26 @@ struct Scratch {
 
 std::mutex g_scratch_mu;
 std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
+
+// One call at a time per (device, stream): a call reads the area's counter-set
+// rotation, may grow the area, launches, and then advances the rotation; two
+// host threads interleaving those steps on one stream could share a counter
+// set or see the area freed under them.  Held from before the scratch lookup
+// to after the rotation is advanced (not for captured calls, which take an
+// area of their own).
+std::map<std::pair<int, hipStream_t>, std::unique_ptr<std::mutex>> g_call_mu;
+
+std::unique_lock<std::mutex> stream_call_lock(int dev, hipStream_t stream, bool graph) {
+    if (graph) return std::unique_lock<std::mutex>();
+    std::mutex* m;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        auto& slot = g_call_mu[std::make_pair(dev, stream)];
+        if (!slot) slot.reset(new std::mutex);
+        m = slot.get();
+    }
+    return std::unique_lock<std::mutex>(*m);
+}
 
 // Returns a scratch area of at least `bytes` for (device, stream).  Growing an
 // area first waits for the stream, so no kernel still reads the old one.
@@ -212,7 +234,32 @@ std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::vector<TimedCall> g_prof_pending;
 std::vector<TimedCall> g_prof_free;
-hstu_kernel_times_t g_prof_total = {0, 0.0, 0.0, 0};
+hstu_kernel_times_t g_prof_total = {0, 0.0, 0.0, 0, 0.0, 0.0, 0.0};
+std::vector<float> g_prof_attn;   // per-call attention-kernel times since the last reset
+// Per-device clock record of timed forward calls (CLK_SLOTS workgroups,
+// CLK_WORDS words each), the id the last timed call wrote and its device.
+std::map<int, unsigned long long*> g_clk_buf;
+unsigned g_clk_next = 0;
+int g_clk_last_dev = -1;
+unsigned g_clk_last_id = 0;
+
+// The clock record for a timed call on `dev` (allocated on first use), or
+// null if that fails; *id receives the call's id.
+unsigned long long* clock_slot(int dev, unsigned* id) {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    unsigned long long*& b = g_clk_buf[dev];
+    if (!b) {
+        void* ptr = nullptr;
+        if (hipMalloc(&ptr, sizeof(unsigned long long) * hstu::CLK_WORDS * hstu::CLK_SLOTS) !=
+            hipSuccess)
+            return nullptr;
+        b = static_cast<unsigned long long*>(ptr);
+    }
+    *id = ++g_clk_next;
+    g_clk_last_dev = dev;
+    g_clk_last_id = *id;
+    return b;
+}
 constexpr size_t PROF_RING = 4096;
 
 bool prof_take(TimedCall* tc) {
@@ -311,6 +358,7 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
 
     const hstu::Dtype dt = static_cast<hstu::Dtype>(dtype);
     const bool graph = is_capturing(stream);
+    const std::unique_lock<std::mutex> call_lock = stream_call_lock(dev, stream, graph);
     Scratch* sc = nullptr;
     const size_t wl_bytes = (hstu::worklist_bytes(num_seqs, heads) + 255) & ~(size_t)255;
     const size_t ramp_bytes = mi.dense ? sizeof(int32_t) * ((size_t)num_seqs + 1) : 0;
@@ -357,6 +405,7 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
 
     TimedCall tc;
     const bool timed = !graph && prof_take(&tc);
+    if (timed) p.clk = clock_slot(dev, &p.clk_id);
     tc.sched = false;
     hipError_t e;
     if (!wl.fused) {
@@ -421,6 +470,7 @@ hstu_status_t attn_bwd_call(const void* q, const void* k, const void* v, const v
 
     const hstu::Dtype dt = static_cast<hstu::Dtype>(dtype);
     const bool graph = is_capturing(stream);
+    const std::unique_lock<std::mutex> call_lock = stream_call_lock(dev, stream, graph);
     Scratch* sc = nullptr;
     const size_t wl_bytes = (hstu::worklist_bytes(num_seqs, heads) + 255) & ~(size_t)255;
     const size_t ramp_bytes = dense_len > 0 ? sizeof(int32_t) * ((size_t)num_seqs + 1) : 0;
@@ -838,11 +888,46 @@ hstu_status_t hstu_profile_read(hstu_kernel_times_t* out, int reset) {
         g_prof_total.calls++;
         g_prof_total.sched_ms += a;
         g_prof_total.attn_ms += b;
+        g_prof_attn.push_back(b);
         g_prof_free.push_back(tc);
     }
     g_prof_pending.clear();
+    if (!g_prof_attn.empty()) {
+        std::vector<float> t(g_prof_attn);
+        std::sort(t.begin(), t.end());
+        const size_t m = t.size();
+        g_prof_total.attn_min_ms = t[0];
+        g_prof_total.attn_median_ms = m % 2 ? t[m / 2] : 0.5 * ((double)t[m / 2 - 1] + t[m / 2]);
+    }
+    // The clock of the last timed forward call: per workgroup, the shader
+    // clock counter's advance over the 100 MHz counter's, averaged.
+    g_prof_total.clock_mhz = 0.0;
+    if (g_clk_last_dev >= 0 && g_clk_last_id != 0) {
+        std::vector<unsigned long long> h((size_t)hstu::CLK_WORDS * hstu::CLK_SLOTS);
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e == hipSuccess) e = hipSetDevice(g_clk_last_dev);
+        if (e == hipSuccess)
+            e = hipMemcpy(h.data(), g_clk_buf[g_clk_last_dev], h.size() * sizeof(h[0]),
+                          hipMemcpyDeviceToHost);
+        (void)hipSetDevice(cur);
+        if (e != hipSuccess) return hip_fail(e);
+        double sum = 0.0;
+        int cnt = 0;
+        for (int w = 0; w < hstu::CLK_SLOTS; ++w) {
+            const unsigned long long* r = &h[(size_t)hstu::CLK_WORDS * w];
+            if (r[4] != g_clk_last_id || r[3] <= r[1]) continue;
+            sum += 100.0 * (double)(r[2] - r[0]) / (double)(r[3] - r[1]);
+            ++cnt;
+        }
+        if (cnt) g_prof_total.clock_mhz = sum / cnt;
+    }
     *out = g_prof_total;
-    if (reset) g_prof_total = hstu_kernel_times_t{0, 0.0, 0.0, 0};
+    if (reset) {
+        g_prof_total = hstu_kernel_times_t{0, 0.0, 0.0, 0, 0.0, 0.0, 0.0};
+        g_prof_attn.clear();
+        g_clk_last_id = 0;
+    }
     return HSTU_OK;
 }
 

@@ -63,6 +63,8 @@ struct KernelArgs {
     int heads;
     float score_scale;  // -alpha * log2(e)
     float out_scale;    // -ln(2) / n
+    unsigned long long* clk;   // clock record per workgroup (timed calls), or null
+    unsigned clk_id;
 };
 
 // The relative-attention-bias kernel's arguments (a separate type, so that
@@ -106,6 +108,33 @@ enum : int { MASK_CAUSAL = 0, MASK_TARGETS = 1, MASK_CACHED = 2, MASK_RAB = 3, M
 // v_ffbh_u32(ts_r + 1 - ts_c) + 1 that already holds the capped bucket's
 // entry.  Position entries reach a wave through LDS as well: per key tile, the
 // window of wpos that the tile's (row, key) pairs index, staged with the tile.
+
+// Clock record of a timed call: the shader-clock counter and the constant
+// 100 MHz counter at a workgroup's start and end (their ratio is the clock the
+// workgroup ran at), written by thread 0 with the call's id.
+struct ClockMark {
+    unsigned long long t, r;
+};
+__device__ __forceinline__ ClockMark clock_mark(const unsigned long long* clk) {
+    ClockMark m = {0, 0};
+    if (clk) {
+        m.t = __builtin_amdgcn_s_memtime();
+        m.r = __builtin_amdgcn_s_memrealtime();
+    }
+    return m;
+}
+__device__ __forceinline__ void clock_record(unsigned long long* clk, unsigned id, ClockMark m0) {
+    if (clk && threadIdx.x == 0 && blockIdx.x < (unsigned)CLK_SLOTS) {
+        const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+        const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+        unsigned long long* w = clk + (size_t)CLK_WORDS * blockIdx.x;
+        w[0] = m0.t;
+        w[1] = m0.r;
+        w[2] = t1;
+        w[3] = r1;
+        w[4] = id;
+    }
+}
 
 // -log2(e) * silu(alpha*s), given m = -alpha*log2(e)*s.
 __device__ __forceinline__ float silu_scaled(float m) {
@@ -198,6 +227,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
     __shared__ float ttab[RAB ? 33 : 1];   // time term by v_ffbh_u32(gap + 1) + 1, over alpha
     static_assert(NW * 64 >= FUSE_SEQS && NW * 64 >= 32 * NQ, "fused tables need a thread per sequence");
 
+    const ClockMark clk0 = clock_mark(a.clk);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -284,7 +314,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
             hist = len - min(max(__builtin_amdgcn_readfirstlane(a.ntgt[seq]), 0), len);
         if constexpr (MASK == MASK_CACHED) {
             hstart = __builtin_amdgcn_readfirstlane(a.hoff[seq]);
-            hlen = max(__builtin_amdgcn_readfirstlane(a.hoff[seq + 1]) - hstart, 0);
+            // (no cache: every history is empty, whatever the offsets say)
+            hlen = a.kc ? max(__builtin_amdgcn_readfirstlane(a.hoff[seq + 1]) - hstart, 0) : 0;
             hist = (hlen + BK - 1) / BK * BK;
             shift = hist;
             s = hist + len;
@@ -767,6 +798,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
                     }
         }
     }
+    clock_record(a.clk, a.clk_id, clk0);
 }
 
 // ---------------------------------------------------------------------------
@@ -812,6 +844,8 @@ struct KernelArgsF32 {
     int heads;
     float score_scale;
     float out_scale;
+    unsigned long long* clk;   // clock record per workgroup (timed calls), or null
+    unsigned clk_id;
 };
 
 template <int D, int NW, int BK, bool FUSED>
@@ -824,6 +858,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma_f32(KernelArgsF32 a)
     __shared__ LocalTables lt;
     static_assert(NW * 64 >= FUSE_SEQS && NW * 64 >= 32 * NQ, "fused tables need a thread per sequence");
 
+    const ClockMark clk0 = clock_mark(a.clk);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
@@ -849,7 +884,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma_f32(KernelArgsF32 a)
         int s = len, hist = len, shift = 0, hstart = 0, hlen = 0;
         if (a.hoff) {
             hstart = a.hoff[it.seq];
-            hlen = max(a.hoff[it.seq + 1] - hstart, 0);
+            // (no cache: every history is empty, whatever the offsets say)
+            hlen = a.kc ? max(a.hoff[it.seq + 1] - hstart, 0) : 0;
             hist = (hlen + BK - 1) / BK * BK;
             shift = hist;
             s = hist + len;
@@ -1007,6 +1043,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma_f32(KernelArgsF32 a)
             }
         }
     }
+    clock_record(a.clk, a.clk_id, clk0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1053,6 +1090,8 @@ hipError_t launch16(const FwdParams& p, WorkList wl, int grid, hipStream_t strea
     a.heads = p.heads;
     a.score_scale = -p.alpha * LOG2E;
     a.out_scale = -LN2 / p.n;
+    a.clk = p.clk;
+    a.clk_id = p.clk_id;
     constexpr int QB = QBlocks<D>::value, BK = KeyTile<D>::value, PF = Prefetch<D>::value;
     constexpr int QBC = QBlocksFor<D, MASK_CACHED>::value;
     if (p.timestamps) {
@@ -1134,6 +1173,8 @@ hipError_t launch_f32(const FwdParams& p, WorkList wl, int grid, hipStream_t str
     a.heads = p.heads;
     a.score_scale = -p.alpha * LOG2E;
     a.out_scale = -LN2 / p.n;
+    a.clk = p.clk;
+    a.clk_id = p.clk_id;
     auto fn = wl.fused ? attn_fwd_mfma_f32<D, NWF, BKF, true> : attn_fwd_mfma_f32<D, NWF, BKF, false>;
     if (grid <= 0) {
         static int cached[2] = {0, 0};

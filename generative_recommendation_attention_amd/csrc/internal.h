@@ -159,7 +159,14 @@ struct FwdParams {
     int d;
     float alpha;
     float n;
+    // Timed calls only: workgroup w of the attention kernel writes
+    // clk[CLK_WORDS w + 0..4] = shader-clock counter and 100 MHz counter at
+    // its start, the same at its end, then clk_id (w < CLK_SLOTS), or null.
+    unsigned long long* clk = nullptr;
+    unsigned clk_id = 0;
 };
+constexpr int CLK_WORDS = 8;
+constexpr int CLK_SLOTS = 4096;
 
 // Rows of Q handled by one work item for this element type and head size;
 // single_block: the cached-history and relative-attention-bias forms, whose

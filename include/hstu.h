@@ -38,7 +38,9 @@
  * (device, stream): a work list of 12 bytes per sequence plus a header.  It is
  * allocated on the first call that needs more; later calls with no more
  * sequences allocate nothing.  Two calls on the same stream are ordered by the
- * stream; calls on different streams use different scratch areas.  A call is
+ * stream; calls on different streams use different scratch areas.  Host
+ * threads may call on one stream concurrently: the library serialises the
+ * enqueueing of calls per (device, stream).  A call is
  * one kernel for batches of up to 256 sequences and 2048 (sequence, head)
  * pairs (the attention kernel ranks the sequences itself), two kernels
  * otherwise (a work-list kernel, then the attention kernel); the first call on
@@ -141,8 +143,9 @@ hstu_status_t hstu_attn_fwd_targets(const void* q, const void* k, const void* v,
  *   k_cache, v_cache : the cached history K and V, (T_hist, heads, d), same element
  *                      type, 16-byte aligned, T_hist = hist_offsets[num_seqs];
  *                      read only; out must not overlap them.  Both may be NULL
- *                      when T_hist = 0 (every hist_offsets entry 0): then no
- *                      cache row is read.
+ *                      when there is no history (T_hist = 0): then no cache row
+ *                      is read and every history counts as empty, whatever
+ *                      hist_offsets holds.
  *   hist_offsets     : device int32[num_seqs + 1], off[0] = 0, non-decreasing (an
  *                      empty history is allowed: candidates then see themselves only).
  *
@@ -367,6 +370,11 @@ typedef struct {
     double sched_ms;      /* total time of the work-list kernel (0 for one-kernel calls) */
     double attn_ms;       /* total time of the attention kernel */
     int64_t dropped;      /* calls not timed because the event ring was full */
+    double attn_min_ms;   /* shortest attention-kernel time of one call (0 if none) */
+    double attn_median_ms;/* median attention-kernel time of one call (0 if none) */
+    double clock_mhz;     /* shader clock during the last timed forward call, averaged over
+                           * its workgroups (each reads the shader-clock counter and the
+                           * 100 MHz counter at its start and end); 0 if none */
 } hstu_kernel_times_t;
 
 /* on != 0: from now on each forward call records start and stop events on
@@ -374,7 +382,8 @@ typedef struct {
 hstu_status_t hstu_profile_enable(int on);
 
 /* Waits for the recorded events, adds their durations to *out and, if reset,
- * clears the accumulated totals. */
+ * clears the accumulated totals.  Reads the clock record of the last timed
+ * forward call back from the device (a synchronous copy). */
 hstu_status_t hstu_profile_read(hstu_kernel_times_t* out, int reset);
 
 #ifdef __cplusplus

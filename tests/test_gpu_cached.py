@@ -181,3 +181,18 @@ def test_cached_empty_inputs():
     cc = workloads.make_cached_case([0, 0], [3, 40], 2, 64, "bf16", seed=641, n=2.0)
     got = from_torch(run_cached(cc), "bf16")
     assert_close(got, oracle_cached(cc), "bf16", "cached, empty cache tensors")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_cached_null_cache_ignores_history_offsets(dtype):
+    """Empty cache tensors (null cache pointers at the C ABI) with history
+    offsets that claim rows: no cache row is read and every candidate sees
+    itself only, as with all-zero history offsets."""
+    cc = workloads.make_cached_case([0, 0, 0], [5, 70, 33], 2, 64, dtype, seed=651, n=7.0)
+    q, k, v, coff, _, _, _ = device(cc)
+    empty = torch.zeros((0, 2, 64), dtype=q.dtype, device="cuda")
+    hoff = torch.tensor([0, 40, 40, 300], dtype=torch.int32, device="cuda")
+    got = from_torch(hstu.hstu_attn_fwd_cached(q, k, v, coff, empty, empty, hoff, cc.cand.alpha,
+                                               cc.cand.n), dtype)
+    torch.cuda.synchronize()
+    assert_close(got, oracle_cached(cc), dtype, "cached, null cache with non-zero offsets")
