@@ -18,7 +18,8 @@ mask),
 hstu_attn_fwd_cached (candidates against a cached history),
 hstu_attn_fwd_dense / hstu_attn_bwd_dense ((B, heads, S, d) tensors),
 hstu_attn_bwd (dq, dk, dv), hstu_layer_in_proj /
-hstu_layer_out_proj (the layer's projections), and the utilities
+hstu_layer_out_proj (the layer's projections), hstu_attn_fwd_noalloc (the
+forward with no allocation in the library), and the utilities
 hstu_validate_offsets, hstu_release_workspace, hstu_profile_enable/read.
 The offsets live on the device and are not read by the host: keeping them
 consistent with the tensors' lengths is the caller's part (see
@@ -39,6 +40,8 @@ HSTU_ERR_UNSUPPORTED = -2
 HSTU_ERR_HIP = -3
 HSTU_ERR_NO_MEMORY = -4
 HSTU_ERR_BAD_OFFSETS = -5
+HSTU_ERR_SCRATCH_LIMIT = -6
+HSTU_NOALLOC_SCRATCH_BYTES = 1 << 20
 
 HSTU_BF16, HSTU_FP16, HSTU_FP32 = 0, 1, 2
 
@@ -48,7 +51,7 @@ EXPORTS = ("hstu_attn_fwd", "hstu_attn_fwd_bf16", "hstu_attn_fwd_fp16", "hstu_at
            "hstu_attn_fwd_rab", "hstu_attn_fwd_rab_targets", "hstu_attn_bwd_rab", "hstu_attn_bwd",
            "hstu_attn_bwd_dense", "hstu_layer_in_proj", "hstu_layer_out_proj",
            "hstu_attn_bwd_targets", "hstu_validate_offsets", "hstu_status_string", "hstu_last_hip_error",
-           "hstu_release_workspace", "hstu_profile_enable", "hstu_profile_read")
+           "hstu_release_workspace", "hstu_profile_enable", "hstu_profile_read", "hstu_attn_fwd_noalloc")
 
 
 class HstuError(RuntimeError):
@@ -86,6 +89,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     fwd = [vp, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp]
     lib.hstu_attn_fwd.argtypes = fwd + [ctypes.c_int]
     lib.hstu_attn_fwd.restype = ctypes.c_int
+    lib.hstu_attn_fwd_noalloc.argtypes = fwd + [ctypes.c_int]
+    lib.hstu_attn_fwd_noalloc.restype = ctypes.c_int
     for name in ("hstu_attn_fwd_bf16", "hstu_attn_fwd_fp16", "hstu_attn_fwd_fp32"):
         getattr(lib, name).argtypes = fwd
         getattr(lib, name).restype = ctypes.c_int
@@ -194,6 +199,23 @@ def hstu_attn_fwd(q, k, v, seq_offsets, alpha: float, n: float, out=None, stream
                            num_seqs, heads, d, float(alpha), float(n), out.data_ptr(),
                            _stream_handle(stream), _dtype_code(q))
     _check(st, "hstu_attn_fwd")
+    return out
+
+
+def hstu_attn_fwd_noalloc(q, k, v, seq_offsets, alpha: float, n: float, out=None, stream=None):
+    """hstu_attn_fwd through the library's allocation-free entry point (its
+    work list in a fixed per-GPU device array; see include/hstu.h).  The
+    library allocates nothing; `out` is allocated here with torch if not
+    given."""
+    out = _check_tensors(q, k, v, seq_offsets, out)
+    T, heads, d = q.shape
+    num_seqs = seq_offsets.numel() - 1
+    lib = load_library()
+    st = lib.hstu_attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                   seq_offsets.data_ptr(), num_seqs, heads, d, float(alpha),
+                                   float(n), out.data_ptr(), _stream_handle(stream),
+                                   _dtype_code(q))
+    _check(st, "hstu_attn_fwd_noalloc")
     return out
 
 

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libhstu.so")
-SOURCES = ["api.cpp", "schedule.hip", "attn_fwd.hip", "attn_bwd.hip", "layer.hip"]
+SOURCES = ["api.cpp", "schedule.hip", "attn_fwd.hip", "attn_bwd.hip", "layer.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 

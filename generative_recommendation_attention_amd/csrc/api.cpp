@@ -343,10 +343,14 @@ struct MaskInputs {
 };
 
 // One forward call.
+// fixed_area: the caller's device area of fixed_bytes for the work list (the
+// allocation-free entry point), instead of the library's per-stream scratch.
+// Such a call keeps no host-side state: it zeroes the queue counters itself.
 hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
                             const int32_t* seq_offsets, const MaskInputs& mi, int32_t num_seqs,
                             int32_t heads, int32_t d, float alpha, float n, void* out,
-                            hipStream_t stream, int dtype) {
+                            hipStream_t stream, int dtype, void* fixed_area = nullptr,
+                            size_t fixed_bytes = 0) {
     // (the dense entry point checks its own arguments and passes no offsets)
     hstu_status_t st = mi.dense ? HSTU_OK
                                 : check_args(q, k, v, seq_offsets, num_seqs, heads, d, alpha, n,
@@ -358,27 +362,44 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
 
     const hstu::Dtype dt = static_cast<hstu::Dtype>(dtype);
     const bool graph = is_capturing(stream);
-    const std::unique_lock<std::mutex> call_lock = stream_call_lock(dev, stream, graph);
+    const bool fixed = fixed_area != nullptr;
+    const std::unique_lock<std::mutex> call_lock = stream_call_lock(dev, stream, graph || fixed);
     Scratch* sc = nullptr;
     const size_t wl_bytes = (hstu::worklist_bytes(num_seqs, heads) + 255) & ~(size_t)255;
     const size_t ramp_bytes = mi.dense ? sizeof(int32_t) * ((size_t)num_seqs + 1) : 0;
     hstu::WorkList wl;
     bool clean;
-    st = call_scratch(dev, stream, graph, wl_bytes + ramp_bytes, &sc, &wl, num_seqs, heads,
-                      &clean);
-    if (st != HSTU_OK) return st;
-    forget_ramp_under(sc, wl_bytes);
-    if (mi.dense) {
-        st = dense_ramp(sc, wl_bytes, num_seqs, mi.dense_len, stream, &seq_offsets);
-        if (st != HSTU_OK) return st;
-    }
     // Small batches build their queue tables inside the attention kernel.  The
     // work-list kernel still runs when this call's counter set is not known to
     // be zero (a new scratch area, or a failed launch before; it zeroes both
     // sets) and when a test forces one of its ranking paths.
     const hstu::SortChoice sort = sort_choice_env();
-    wl.fused = clean && sort == hstu::SortChoice::AUTO && num_seqs <= hstu::FUSE_SEQS &&
-               (long long)num_seqs * heads <= hstu::FUSE_PAIRS;
+    const bool fusable = sort == hstu::SortChoice::AUTO && num_seqs <= hstu::FUSE_SEQS &&
+                         (long long)num_seqs * heads <= hstu::FUSE_PAIRS;
+    if (fixed) {
+        if (mi.dense) return HSTU_ERR_INVALID_ARG;
+        if (wl_bytes > fixed_bytes) return HSTU_ERR_SCRATCH_LIMIT;
+        wl = hstu::worklist_carve(fixed_area, num_seqs, heads);
+        wl.set = 0;
+        // The one-kernel form needs counter set 0 at zero: a one-wave kernel
+        // clears every set first (the work-list kernel of the two-kernel form
+        // clears them itself).
+        clean = fusable;
+        if (fusable) {
+            const hipError_t e = hstu::launch_clear_counters(wl.ctl, stream);
+            if (e != hipSuccess) return hip_fail(e);
+        }
+    } else {
+        st = call_scratch(dev, stream, graph, wl_bytes + ramp_bytes, &sc, &wl, num_seqs, heads,
+                          &clean);
+        if (st != HSTU_OK) return st;
+        forget_ramp_under(sc, wl_bytes);
+        if (mi.dense) {
+            st = dense_ramp(sc, wl_bytes, num_seqs, mi.dense_len, stream, &seq_offsets);
+            if (st != HSTU_OK) return st;
+        }
+    }
+    wl.fused = clean && fusable;
 
     hstu::FwdParams p;
     p.q = q;
@@ -404,7 +425,9 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
     p.n = n;
 
     TimedCall tc;
-    const bool timed = !graph && prof_take(&tc);
+    // (the allocation-free form is never timed: timing creates events and a
+    // clock buffer)
+    const bool timed = !graph && !fixed && prof_take(&tc);
     if (timed) p.clk = clock_slot(dev, &p.clk_id);
     tc.sched = false;
     hipError_t e;
@@ -419,7 +442,7 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
     e = hstu::launch_attention(p, dt, wl, 0, stream, timed ? tc.e[2] : nullptr,
                                timed ? tc.e[3] : nullptr);
     if (e != hipSuccess) return hip_fail(e);
-    call_done(sc, graph, 1);   // one counter set used, the next two cleared
+    if (!fixed) call_done(sc, graph, 1);   // one counter set used, the next two cleared
     if (timed) prof_commit(tc);
     if (!graph && validate_env()) {
         int ctl[hstu::CTL_WORDS];
@@ -539,6 +562,21 @@ hstu_status_t attn_bwd_call(const void* q, const void* k, const void* v, const v
 }
 
 }  // namespace
+
+namespace hstu {
+
+hstu_status_t attn_fwd_fixed_area(const void* q, const void* k, const void* v,
+                                  const int32_t* seq_offsets, int32_t num_seqs, int32_t heads,
+                                  int32_t d, float alpha, float n, void* out, hipStream_t stream,
+                                  int dtype, void* area, size_t area_bytes) {
+    if (!area || area_bytes == 0) return HSTU_ERR_INVALID_ARG;
+    return attn_fwd_call(q, k, v, seq_offsets, MaskInputs{}, num_seqs, heads, d, alpha, n, out,
+                         stream, dtype, area, area_bytes);
+}
+
+hstu_status_t hip_error_status(hipError_t e) { return hip_fail(e); }
+
+}  // namespace hstu
 
 extern "C" {
 
@@ -849,6 +887,7 @@ const char* hstu_status_string(hstu_status_t status) {
     case HSTU_ERR_HIP: return "HIP runtime error";
     case HSTU_ERR_NO_MEMORY: return "scratch allocation failed";
     case HSTU_ERR_BAD_OFFSETS: return "malformed sequence offsets";
+    case HSTU_ERR_SCRATCH_LIMIT: return "work list larger than the fixed scratch area";
     }
     return "unknown status";
 }

@@ -5,7 +5,19 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "hstu.h"
+
 namespace hstu {
+
+// The forward (causal mask, jagged layout) with its work list in `area`
+// (area_bytes long) instead of the library's per-stream scratch: used by the
+// allocation-free entry point.  Allocates nothing and keeps no host state.
+hstu_status_t attn_fwd_fixed_area(const void* q, const void* k, const void* v,
+                                  const int32_t* seq_offsets, int32_t num_seqs, int32_t heads,
+                                  int32_t d, float alpha, float n, void* out, hipStream_t stream,
+                                  int dtype, void* area, size_t area_bytes);
+// Records e as the calling thread's last HIP error; returns HSTU_ERR_HIP.
+hstu_status_t hip_error_status(hipError_t e);
 
 // Work items are (sequence, head, Q tile) triples, split over NQ queues (one
 // per XCD of an MI355X; a workgroup starts with the queue of the XCD it runs

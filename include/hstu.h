@@ -81,7 +81,8 @@ typedef enum {
     HSTU_ERR_UNSUPPORTED = -2, /* d or dtype not supported, or no gfx950 device */
     HSTU_ERR_HIP = -3,         /* a HIP runtime call failed (see hstu_last_hip_error) */
     HSTU_ERR_NO_MEMORY = -4,   /* the scratch area could not be grown */
-    HSTU_ERR_BAD_OFFSETS = -5  /* hstu_validate_offsets found malformed offsets */
+    HSTU_ERR_BAD_OFFSETS = -5, /* hstu_validate_offsets found malformed offsets */
+    HSTU_ERR_SCRATCH_LIMIT = -6 /* hstu_attn_fwd_noalloc: the work list does not fit */
 } hstu_status_t;
 
 typedef enum { HSTU_BF16 = 0, HSTU_FP16 = 1, HSTU_FP32 = 2 } hstu_dtype_t;
@@ -351,6 +352,29 @@ hstu_status_t hstu_attn_bwd_dense(const void* q, const void* k, const void* v, c
  * HSTU_ERR_BAD_OFFSETS; synchronises `stream`. */
 hstu_status_t hstu_validate_offsets(const int32_t* seq_offsets, int32_t num_seqs,
                                     int64_t* total, hipStream_t stream);
+
+/* Bytes of the fixed device array behind hstu_attn_fwd_noalloc (one per GPU). */
+#define HSTU_NOALLOC_SCRATCH_BYTES (1u << 20)
+
+/* The forward of hstu_attn_fwd (causal mask, jagged layout, same arguments,
+ * same result bit for bit), for callers that cannot allocate: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * calls no allocating routine: its work list lives in a fixed device array of
+ * HSTU_NOALLOC_SCRATCH_BYTES per GPU, which the library holds until the
+ * process ends, instead of the per-stream scratch area; it is never timed by
+ * hstu_profile_* (timing creates events).  A batch whose work list does not
+ * fit, about (8 + 4 heads) bytes per sequence plus 1.3 KB, returns
+ * HSTU_ERR_SCRATCH_LIMIT before anything is enqueued.  Every call on one GPU
+ * shares that GPU's array and leaves its contents there: calls that overlap
+ * on one GPU (on two streams, or a graph replay beside another call) race on
+ * it and may give wrong results; calls ordered on one stream are safe, since
+ * each call zeroes the array's queue counters itself (with one extra one-wave
+ * kernel for batches of up to 256 sequences and 2048 (sequence, head) pairs;
+ * larger batches' work-list kernel does it). */
+hstu_status_t hstu_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                                    const int32_t* seq_offsets, int32_t num_seqs, int32_t heads,
+                                    int32_t d, float alpha, float n, void* out,
+                                    hipStream_t stream, hstu_dtype_t dtype);
 
 /* Human-readable name of a status. */
 const char* hstu_status_string(hstu_status_t status);
