@@ -98,20 +98,6 @@ constexpr int RABB_TS = 64;
 constexpr int RABB_WIN = 192;
 constexpr int RABB_WORDS = RABB_TS + RABB_WIN;
 
-// 4-byte load from a raw buffer straight into LDS: lane l's word lands at
-// lds_base + 4*l (lds_base wave-uniform); out-of-range lanes write zero.
-__device__ __forceinline__ void load4_to_lds(__amdgpu_buffer_rsrc_t r, unsigned char* lds_base,
-                                             int voffset) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    typedef __attribute__((address_space(3))) void lds_void;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 4, voffset, 0, 0, 0);
-#else
-    (void)r;
-    (void)lds_base;
-    (void)voffset;
-#endif
-}
-
 // Time table by v_ffbh_u32(gap + 1) + 1 (index 0: a zero argument, gap -1),
 // already capped at the last bucket, as the forward keeps it.
 __device__ __forceinline__ int rab_time_bucket(int idx, int ntime) {

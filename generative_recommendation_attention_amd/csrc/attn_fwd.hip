@@ -379,6 +379,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
             int cs = c;
             asm volatile("" : "+s"(cs));
             const int slot = cs % NS;
+            // (every read of a slot is ordered by the explicit waits of the
+            // prologue, tile_sync and the item's end)
 #pragma unroll
             for (int i = 0; i < Cfg::LOADS; ++i) {
                 const int dst = (wv + NW * i) * 1024;

@@ -68,21 +68,53 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc32(const void* base, 
                                              RSRC_WORD3);
 }
 
-// 16-byte load from a raw buffer straight into LDS: lane l's bytes land at
-// lds_base + 16*l (lds_base must be wave-uniform).  The builtin exists only
-// for the device; the host pass, which compiles kernel bodies into launch
-// stubs but never runs them, gets an empty body.
+// Loads from a raw buffer straight into LDS (buffer_load ... lds): lane l's
+// bytes land at lds_base + size * l (lds_base wave-uniform, set in M0);
+// out-of-range lanes write zero.
+//
+// They are issued through inline assembly so that the compiler does not track
+// them.  The compiler cannot tell which LDS bytes a load still in flight will
+// write, so after a tracked one it waits for every outstanding load (s_waitcnt
+// vmcnt(0)) before any LDS read: a kernel that reads one tile while the next
+// ones stream in would then wait for those next tiles first.  Every caller
+// therefore orders its LDS reads itself, with explicit vmcnt waits (and
+// barriers between waves) before it reads a staged tile.  The instructions
+// write no VGPR; M0 is set inside, with the wait state an M0 write needs
+// before an LDS DMA, and given back its value afterwards (the load reads M0
+// when it issues).  The host pass, which compiles kernel bodies into launch
+// stubs but never runs them, gets empty bodies.
+#define HSTU_LDS_DMA(op)                                                                   \
+    typedef __attribute__((address_space(3))) unsigned char lds_u8;                          \
+    const unsigned m0 = (unsigned)(uintptr_t)(lds_u8*)lds_base;                              \
+    unsigned saved;                                                                          \
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t" op                    \
+                 " %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"                                   \
+                 : "=&s"(saved)                                                              \
+                 : "s"(m0), "v"(voffset), "s"(r)                                             \
+                 : "memory")
+
 __device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, unsigned char* lds_base,
                                               int voffset) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    typedef __attribute__((address_space(3))) void lds_void;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voffset, 0, 0, 0);
+    HSTU_LDS_DMA("buffer_load_dwordx4");
 #else
     (void)r;
     (void)lds_base;
     (void)voffset;
 #endif
 }
+
+__device__ __forceinline__ void load4_to_lds(__amdgpu_buffer_rsrc_t r, unsigned char* lds_base,
+                                             int voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    HSTU_LDS_DMA("buffer_load_dword");
+#else
+    (void)r;
+    (void)lds_base;
+    (void)voffset;
+#endif
+}
+#undef HSTU_LDS_DMA
 
 // LDS transposing read of four 16-bit values (gfx950 ds_read_b64_tr_b16).
 // Within each group of 16 lanes, lane i receives element (i % 4) of the

@@ -363,7 +363,7 @@ hstu_status_t hstu_validate_offsets(const int32_t* seq_offsets, int32_t num_seqs
  * HSTU_NOALLOC_SCRATCH_BYTES per GPU, which the library holds until the
  * process ends, instead of the per-stream scratch area; it is never timed by
  * hstu_profile_* (timing creates events).  A batch whose work list does not
- * fit, about (8 + 4 heads) bytes per sequence plus 1.3 KB, returns
+ * fit, about (8 + 4 heads) bytes per sequence plus 5 KB, returns
  * HSTU_ERR_SCRATCH_LIMIT before anything is enqueued.  Every call on one GPU
  * shares that GPU's array and leaves its contents there: calls that overlap
  * on one GPU (on two streams, or a graph replay beside another call) race on
