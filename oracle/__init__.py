@@ -37,7 +37,8 @@ attention instead of storing it, HSTU paper translation Appendix G).
 paper translation §3 and Appendix G) to the scaled score before SiLU, under
 the causal mask: rab(r, c) = wpos[r - c] (0 from npos on) +
 wtime[min(floor(log2(ts_r - ts_c + 1)), ntime - 1)] (a negative gap in the
-last bucket), the tables shared by all heads.
+last bucket), the tables shared by all heads; ``bwd_rab`` / ``bwd_rab_rows``
+are its gradients, the tables' included, under either mask.
 
 ``layer_in`` / ``layer_out`` are the layer's surroundings (HSTU paper
 translation §3, §3.3): [u | v | q | k] = silu(W1 x + b1) per token, and
@@ -147,6 +148,16 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                              ctypes.c_int, ctypes.c_int, f64, f64, ctypes.c_int,
                                              vp, vp, i64, vp]
     lib.hstu_oracle_bwd_rab_rows.restype = ctypes.c_int
+    lib.hstu_oracle_bwd_rab_targets.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
+                                                ctypes.c_int, vp, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_int, ctypes.c_int, f64, f64, vp, vp, vp,
+                                                vp, vp]
+    lib.hstu_oracle_bwd_rab_targets.restype = ctypes.c_int
+    lib.hstu_oracle_bwd_rab_rows_targets.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, vp,
+                                                     vp, ctypes.c_int, vp, ctypes.c_int,
+                                                     ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                     f64, f64, ctypes.c_int, vp, vp, i64, vp]
+    lib.hstu_oracle_bwd_rab_rows_targets.restype = ctypes.c_int
     lib.hstu_oracle_threads.argtypes = []
     lib.hstu_oracle_threads.restype = ctypes.c_int
     _libs[path] = lib
@@ -350,22 +361,27 @@ def rows_rab(q, k, v, offsets, timestamps, pos_bias, time_bias, heads: int, d: i
 
 
 def bwd_rab(q, k, v, dout, offsets, timestamps, pos_bias, time_bias, heads: int, d: int,
-            alpha: float, n: float, dtype: str, lib: Optional[ctypes.CDLL] = None):
-    """(dq, dk, dv, dpos, dtime): fp64 gradients of fwd_rab for upstream
-    gradient dout; dq/dk/dv (T, heads, d), dpos [npos], dtime [ntime]."""
+            alpha: float, n: float, dtype: str, lib: Optional[ctypes.CDLL] = None,
+            num_targets=None):
+    """(dq, dk, dv, dpos, dtime): fp64 gradients of fwd_rab (with num_targets:
+    of its target-aware form) for upstream gradient dout; dq/dk/dv
+    (T, heads, d), dpos [npos], dtime [ntime]."""
     lib = lib or load()
     q, k, v, off, ts, wp, wt = _rab_args(q, k, v, offsets, timestamps, pos_bias, time_bias,
                                          heads, d, dtype)
+    tg = _targets(num_targets, len(off) - 1)
     dout = _storage(dout, dtype)
     T = int(off[-1]) if len(off) else 0
     if dout.size < T * heads * d:
         raise ValueError("dout smaller than offsets imply")
     dq, dk, dv = (np.zeros((T, heads, d), dtype=np.float64) for _ in range(3))
     dpos, dtime = np.zeros(len(wp)), np.zeros(len(wt))
-    rc = lib.hstu_oracle_bwd_rab(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _DTYPE_CODE[dtype],
-                                 _ptr(off), _ptr(ts), _ptr(wp), len(wp), _ptr(wt), len(wt),
-                                 len(off) - 1, heads, d, float(alpha), float(n), _ptr(dq),
-                                 _ptr(dk), _ptr(dv), _ptr(dpos), _ptr(dtime))
+    rc = lib.hstu_oracle_bwd_rab_targets(_ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                         _DTYPE_CODE[dtype], _ptr(off),
+                                         None if tg is None else _ptr(tg), _ptr(ts), _ptr(wp),
+                                         len(wp), _ptr(wt), len(wt), len(off) - 1, heads, d,
+                                         float(alpha), float(n), _ptr(dq), _ptr(dk), _ptr(dv),
+                                         _ptr(dpos), _ptr(dtime))
     if rc != 0:
         raise ValueError("oracle rejected the arguments (malformed offsets or sizes)")
     return dq, dk, dv, dpos, dtime
@@ -376,22 +392,25 @@ BWD_KIND = {"dq": 0, "dk": 1, "dv": 2}
 
 def bwd_rab_rows(q, k, v, dout, offsets, timestamps, pos_bias, time_bias, heads: int, d: int,
                  alpha: float, n: float, dtype: str, kind: str, tokens, head_ids,
-                 lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+                 lib: Optional[ctypes.CDLL] = None, num_targets=None) -> np.ndarray:
     """Sampled rows (m, d) of dq (at query tokens), dk or dv (at key tokens)
     of bwd_rab."""
     lib = lib or load()
     q, k, v, off, ts, wp, wt = _rab_args(q, k, v, offsets, timestamps, pos_bias, time_bias,
                                          heads, d, dtype)
+    tg = _targets(num_targets, len(off) - 1)
     dout = _storage(dout, dtype)
     tok = np.ascontiguousarray(tokens, dtype=np.int64)
     hd = np.ascontiguousarray(head_ids, dtype=np.int32)
     if tok.shape != hd.shape:
         raise ValueError("tokens and head_ids differ in length")
     out = np.zeros((len(tok), d), dtype=np.float64)
-    rc = lib.hstu_oracle_bwd_rab_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _DTYPE_CODE[dtype],
-                                      _ptr(off), _ptr(ts), _ptr(wp), len(wp), _ptr(wt), len(wt),
-                                      len(off) - 1, heads, d, float(alpha), float(n),
-                                      BWD_KIND[kind], _ptr(tok), _ptr(hd), len(tok), _ptr(out))
+    rc = lib.hstu_oracle_bwd_rab_rows_targets(_ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                              _DTYPE_CODE[dtype], _ptr(off),
+                                              None if tg is None else _ptr(tg), _ptr(ts),
+                                              _ptr(wp), len(wp), _ptr(wt), len(wt), len(off) - 1,
+                                              heads, d, float(alpha), float(n), BWD_KIND[kind],
+                                              _ptr(tok), _ptr(hd), len(tok), _ptr(out))
     if rc != 0:
         raise ValueError("oracle rejected the sampled rows")
     return out

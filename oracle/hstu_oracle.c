@@ -77,11 +77,13 @@
  * candidate of a micro-batch runs the same operations) a candidate row takes
  * the position right after the history: distance hist - c to a history key
  * c, and 0 to itself; the time term keeps the real timestamps.
- * Its gradients (the *_bwd_rab entry points) differentiate that definition:
- * per kept pair, dx = silu'(x) <dO_r, v_c> / n with x the biased score;
- * dq_r += alpha dx k_c, dk_c += alpha dx q_r, dv_c += silu(x) / n dO_r, and
- * dx is added to wpos[r - c] (r - c < npos) and to the pair's time bucket
- * (the tables' gradients, summed over sequences and heads).
+ * Its gradients (the *_bwd_rab entry points, also under the target-aware
+ * mask) differentiate that definition: per kept pair, dx = silu'(x) <dO_r,
+ * v_c> / n with x the biased score; dq_r += alpha dx k_c, dk_c += alpha dx
+ * q_r, dv_c += silu(x) / n dO_r, and dx is added to the position entry of the
+ * distance the pair's bias used (r - c, or a candidate's hist - c and 0; only
+ * below npos) and to the pair's time bucket (the tables' gradients, summed
+ * over sequences and heads).
  *
  * Readings taken where the pages are silent (each listed in the design notes):
  *   - alpha multiplies the scores before SiLU; n is a caller-given scalar;
@@ -613,9 +615,13 @@ static int time_bucket(int64_t gap, int ntime) {
  * Under the target-aware mask (history length hist < s), a candidate row
  * r >= hist takes the position it would have right after the history:
  * distance hist - c to a history key, 0 to itself. */
+static int64_t rab_dist(int64_t r, int64_t c, int64_t hist) {
+    return r >= hist ? (c == r ? 0 : hist - c) : r - c;
+}
+
 static double rab_value_hist(int64_t r, int64_t c, int64_t hist, const int32_t* ts,
                              const double* wpos, int npos, const double* wtime, int ntime) {
-    int64_t dist = r >= hist ? (c == r ? 0 : hist - c) : r - c;
+    int64_t dist = rab_dist(r, c, hist);
 #if ORACLE_PLANT == 24
     if (r >= hist) dist = r - c; /* planted: candidates keep their own positions */
 #endif
@@ -624,11 +630,6 @@ static double rab_value_hist(int64_t r, int64_t c, int64_t hist, const int32_t* 
 #endif
     double p = dist < npos ? wpos[dist] : 0.0;
     return p + wtime[time_bucket((int64_t)ts[r] - (int64_t)ts[c], ntime)];
-}
-
-static double rab_value(int64_t r, int64_t c, const int32_t* ts, const double* wpos, int npos,
-                        const double* wtime, int ntime) {
-    return rab_value_hist(r, c, INT64_MAX, ts, wpos, npos, wtime, ntime);
 }
 
 /* One output row under the causal mask with the relative attention bias added
@@ -754,10 +755,12 @@ int hstu_oracle_rows_rab(const void* q, const void* k, const void* v, int dtype,
 }
 
 /* Gradient terms of one kept pair (r, c) of a sequence with the relative
- * attention bias: x = alpha <q_r, k_c> + rab(r, c); returns dx = dLoss/dx and
- * adds to dq_r, dk_c, dv_c (each d elements, any may be null). */
+ * attention bias: x = alpha <q_r, k_c> + rab(r, c) (with the candidate
+ * positions of history length hist; INT64_MAX: causal); returns dx = dLoss/dx
+ * and adds to dq_r, dk_c, dv_c (each d elements, any may be null). */
 static double rab_pair_grads(const void* q, const void* k, const void* v, const void* dout,
-                             int dtype, int64_t s0, int64_t r, int64_t c, const int32_t* ts,
+                             int dtype, int64_t s0, int64_t r, int64_t c, int64_t hist,
+                             const int32_t* ts,
                              const double* wpos, int npos, const double* wtime, int ntime,
                              int heads, int d, int h, double alpha, double n, double* dq_r,
                              double* dk_c, double* dv_c) {
@@ -768,7 +771,7 @@ static double rab_pair_grads(const void* q, const void* k, const void* v, const 
         dot += load_elem(q, dtype, qr + e) * load_elem(k, dtype, kc + e);
         dov += load_elem(dout, dtype, qr + e) * load_elem(v, dtype, kc + e);
     }
-    const double x = alpha * dot + rab_value(r, c, ts, wpos, npos, wtime, ntime);
+    const double x = alpha * dot + rab_value_hist(r, c, hist, ts, wpos, npos, wtime, ntime);
     const double dx = dsilu(x) * dov / n;
     const double w = silu(x) / n;
     for (int e = 0; e < d; ++e) {
@@ -783,16 +786,20 @@ static double rab_pair_grads(const void* q, const void* k, const void* v, const 
 #endif
 }
 
-/* Gradients of hstu_oracle_fwd_rab for upstream gradient dout: dq, dk, dv fp64
- * (T, heads, d), and the tables' gradients dwpos[npos], dwtime[ntime] (summed
- * over sequences and heads), all overwritten.  The table sums are taken per
+/* Gradients of hstu_oracle_fwd_rab_targets (ntgt null: of hstu_oracle_fwd_rab)
+ * for upstream gradient dout: dq, dk, dv fp64 (T, heads, d), and the tables'
+ * gradients dwpos[npos], dwtime[ntime] (summed over sequences and heads), all
+ * overwritten.  Each kept pair's dx goes to the position entry of the
+ * distance its bias used (a candidate's distance hist - c to a history key, 0
+ * to itself) and to its time bucket.  The table sums are taken per
  * (sequence, head) pair and then added in pair order, so the result does not
  * depend on the thread count.  Returns 0, or -1 on bad arguments. */
-int hstu_oracle_bwd_rab(const void* q, const void* k, const void* v, const void* dout, int dtype,
-                        const int32_t* off, const int32_t* ts, const double* wpos, int npos,
-                        const double* wtime, int ntime, int num_seqs, int heads, int d,
-                        double alpha, double n, double* dq, double* dk, double* dv,
-                        double* dwpos, double* dwtime) {
+int hstu_oracle_bwd_rab_targets(const void* q, const void* k, const void* v, const void* dout,
+                                int dtype, const int32_t* off, const int32_t* ntgt,
+                                const int32_t* ts, const double* wpos, int npos,
+                                const double* wtime, int ntime, int num_seqs, int heads, int d,
+                                double alpha, double n, double* dq, double* dk, double* dv,
+                                double* dwpos, double* dwtime) {
     if (num_seqs < 0 || heads < 1 || d < 1) return -1;
     if (npos < 1 || ntime < 1 || ntime > 32 || !offsets_ok(off, num_seqs)) return -1;
     const int64_t rs = (int64_t)heads * d;
@@ -808,16 +815,24 @@ int hstu_oracle_bwd_rab(const void* q, const void* k, const void* v, const void*
     for (int64_t it = 0; it < items; ++it) {
         const int i = (int)(it / heads), h = (int)(it % heads);
         const int64_t s0 = off[i], len = (int64_t)off[i + 1] - off[i];
+        int64_t t = ntgt ? ntgt[i] : 0;
+        if (t < 0) t = 0;
+        if (t > len) t = len;
+        const int64_t hist = ntgt ? len - t : INT64_MAX;
         double* pp = part + it * nt;
         for (int64_t r = 0; r < len; ++r)
             for (int64_t c = 0; c <= r; ++c) {
+                if (!sees(r, c, hist)) continue;
                 const double dx = rab_pair_grads(
-                        q, k, v, dout, dtype, s0, r, c, ts + s0, wpos, npos, wtime, ntime, heads,
-                        d, h, alpha, n, dq + (s0 + r) * rs + (int64_t)h * d,
+                        q, k, v, dout, dtype, s0, r, c, hist, ts + s0, wpos, npos, wtime, ntime,
+                        heads, d, h, alpha, n, dq + (s0 + r) * rs + (int64_t)h * d,
                         dk + (s0 + c) * rs + (int64_t)h * d, dv + (s0 + c) * rs + (int64_t)h * d);
-                int64_t dist = r - c;
+                int64_t dist = rab_dist(r, c, hist);
 #if ORACLE_PLANT == 23
                 dist = dist + 1; /* planted: position gradient one distance off */
+#endif
+#if ORACLE_PLANT == 25
+                dist = r - c; /* planted: candidates' position gradient at their own distance */
 #endif
                 if (dist < npos) pp[dist] += dx;
                 pp[npos + time_bucket((int64_t)ts[s0 + r] - (int64_t)ts[s0 + c], ntime)] += dx;
@@ -832,14 +847,26 @@ int hstu_oracle_bwd_rab(const void* q, const void* k, const void* v, const void*
     return 0;
 }
 
+int hstu_oracle_bwd_rab(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                        const int32_t* off, const int32_t* ts, const double* wpos, int npos,
+                        const double* wtime, int ntime, int num_seqs, int heads, int d,
+                        double alpha, double n, double* dq, double* dk, double* dv,
+                        double* dwpos, double* dwtime) {
+    return hstu_oracle_bwd_rab_targets(q, k, v, dout, dtype, off, 0, ts, wpos, npos, wtime,
+                                       ntime, num_seqs, heads, d, alpha, n, dq, dk, dv, dwpos,
+                                       dwtime);
+}
+
 /* Sampled gradient rows of the same: kind 0 = dq at query token tok[m], 1 =
- * dk and 2 = dv at key token tok[m], head hd[m]; out_rows[m, 0..d).  Returns
- * 0, or -1 on bad arguments. */
-int hstu_oracle_bwd_rab_rows(const void* q, const void* k, const void* v, const void* dout,
-                             int dtype, const int32_t* off, const int32_t* ts, const double* wpos,
-                             int npos, const double* wtime, int ntime, int num_seqs, int heads,
-                             int d, double alpha, double n, int kind, const int64_t* tok,
-                             const int32_t* hd, int64_t count, double* out_rows) {
+ * dk and 2 = dv at key token tok[m], head hd[m]; out_rows[m, 0..d).  ntgt as
+ * for hstu_oracle_bwd_rab_targets.  Returns 0, or -1 on bad arguments. */
+int hstu_oracle_bwd_rab_rows_targets(const void* q, const void* k, const void* v,
+                                     const void* dout, int dtype, const int32_t* off,
+                                     const int32_t* ntgt, const int32_t* ts, const double* wpos,
+                                     int npos, const double* wtime, int ntime, int num_seqs,
+                                     int heads, int d, double alpha, double n, int kind,
+                                     const int64_t* tok, const int32_t* hd, int64_t count,
+                                     double* out_rows) {
     if (num_seqs < 1 || heads < 1 || d < 1 || kind < 0 || kind > 2) return -1;
     if (npos < 1 || ntime < 1 || ntime > 32 || !offsets_ok(off, num_seqs)) return -1;
     const int64_t T = off[num_seqs];
@@ -852,21 +879,37 @@ int hstu_oracle_bwd_rab_rows(const void* q, const void* k, const void* v, const 
             int mid = (lo + hi + 1) / 2;
             if (off[mid] <= tok[m]) lo = mid; else hi = mid - 1;
         }
-        const int64_t s0 = off[lo], len = (int64_t)off[lo + 1] - off[lo], t = tok[m] - s0;
+        const int64_t s0 = off[lo], len = (int64_t)off[lo + 1] - off[lo], x = tok[m] - s0;
+        int64_t t = ntgt ? ntgt[lo] : 0;
+        if (t < 0) t = 0;
+        if (t > len) t = len;
+        const int64_t hist = ntgt ? len - t : INT64_MAX;
         double* o = out_rows + m * (int64_t)d;
         for (int e = 0; e < d; ++e) o[e] = 0.0;
         if (kind == 0) {
-            for (int64_t c = 0; c <= t; ++c)
-                rab_pair_grads(q, k, v, dout, dtype, s0, t, c, ts + s0, wpos, npos, wtime, ntime,
-                               heads, d, hd[m], alpha, n, o, 0, 0);
+            for (int64_t c = 0; c <= x; ++c)
+                if (sees(x, c, hist))
+                    rab_pair_grads(q, k, v, dout, dtype, s0, x, c, hist, ts + s0, wpos, npos,
+                                   wtime, ntime, heads, d, hd[m], alpha, n, o, 0, 0);
         } else {
-            for (int64_t r = t; r < len; ++r)
-                rab_pair_grads(q, k, v, dout, dtype, s0, r, t, ts + s0, wpos, npos, wtime, ntime,
-                               heads, d, hd[m], alpha, n, 0, kind == 1 ? o : 0,
-                               kind == 2 ? o : 0);
+            for (int64_t r = x; r < len; ++r)
+                if (sees(r, x, hist))
+                    rab_pair_grads(q, k, v, dout, dtype, s0, r, x, hist, ts + s0, wpos, npos,
+                                   wtime, ntime, heads, d, hd[m], alpha, n, 0,
+                                   kind == 1 ? o : 0, kind == 2 ? o : 0);
         }
     }
     return 0;
+}
+
+int hstu_oracle_bwd_rab_rows(const void* q, const void* k, const void* v, const void* dout,
+                             int dtype, const int32_t* off, const int32_t* ts, const double* wpos,
+                             int npos, const double* wtime, int ntime, int num_seqs, int heads,
+                             int d, double alpha, double n, int kind, const int64_t* tok,
+                             const int32_t* hd, int64_t count, double* out_rows) {
+    return hstu_oracle_bwd_rab_rows_targets(q, k, v, dout, dtype, off, 0, ts, wpos, npos, wtime,
+                                            ntime, num_seqs, heads, d, alpha, n, kind, tok, hd,
+                                            count, out_rows);
 }
 
 /* Number of threads an OpenMP parallel region here uses (for reporting). */
