@@ -61,11 +61,12 @@ METRIC_RAB_BWD = "HSTU attn bwd with relative attention bias (dq, dk, dv, table 
 # source the bench reports traffic as null.
 TRAFFIC = {
     "kernel_source": "generative_recommendation_attention_amd/csrc/attn_fwd.hip",
-    "kernel_sha256": "74eeb4f0558d0e61af4c1d3efcc3fab7e55984322bc1fc976963011773781737",
+    "kernel_sha256": "fd5bc37d2dabaa9ba965cb87ff96a73c68008845a3c50d79aed707d3edee0437",
     "fetch_scale": 2.0,
     "write_scale": 1.0,
-    "fetch_kib": {2: 93835.1},
-    "write_kib": {2: 37940.2},
+    # mean over the launches that take the timed calls' form
+    "fetch_kib": {1: 291.7, 2: 95320.6, 3: 1232491.8, 4: 376766.9, 5: 529559.1},
+    "write_kib": {1: 200.8, 2: 39513.2, 3: 141169.8, 4: 54576.8, 5: 264993.7},
 }
 
 
@@ -514,7 +515,7 @@ def main() -> int:
     else:
         bound = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                  "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
-    roofline = {**bound, "traffic": traffic,
+    roofline = {**bound, "traffic": traffic, "algorithmic_bytes": round(alg_bytes),
                 "kernel": ("attn_bwd_dkv + attn_bwd_dq + table-gradient sum" if args.backward and
                            args.rab else "attn_bwd_dkv + attn_bwd_dq" if args.backward else
                            "attn_fwd_mfma16" if case.dtype != "fp32" else "attn_fwd_mfma_f32") +
