@@ -149,18 +149,22 @@ def cpu_baseline_bwd(case, dout, budget_s: float, rab=None):
     while i < case.num_seqs and done_s < budget_s:
         j = min(case.num_seqs, i + per_call)
         a, b = int(off[i]), int(off[j])
+        tg = None if case.num_targets is None else case.num_targets[i:j]
         t0 = time.perf_counter()
         if rab is not None:
             oracle.bwd_rab(case.q[a:b], case.k[a:b], case.v[a:b], dout[a:b],
                            off[i:j + 1] - off[i], rab.timestamps[a:b], rab.pos_bias,
                            rab.time_bias, case.heads, case.d, case.alpha, case.n, case.dtype,
-                           lib=lib)
+                           lib=lib, num_targets=tg)
         else:
             oracle.bwd(case.q[a:b], case.k[a:b], case.v[a:b], dout[a:b], off[i:j + 1] - off[i],
-                       case.heads, case.d, case.alpha, case.n, case.dtype, lib=lib)
+                       case.heads, case.d, case.alpha, case.n, case.dtype, lib=lib,
+                       num_targets=tg)
         done_s += time.perf_counter() - t0
-        s = case.lengths[i:j].astype(np.float64)
-        done_flops += float(np.sum(10.0 * case.heads * case.d * s * (s + 1.0) / 2.0))
+        part = workloads.Case(name="", dtype=case.dtype, heads=case.heads, d=case.d,
+                              offsets=off[i:j + 1] - off[i], q=case.q[:0], k=case.k[:0],
+                              v=case.v[:0], alpha=case.alpha, n=case.n, num_targets=tg)
+        done_flops += 10.0 * case.heads * case.d * seen_pairs(part)
         seqs += j - i
         i = j
     return {"value": done_flops / done_s / 1e12, "unit": "TFLOP/s",
@@ -339,9 +343,9 @@ def main() -> int:
                          "scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     modes = args.targets + args.cached + args.backward + args.dense + args.layer + args.rab
-    if modes > 1 and not (modes == 2 and args.rab and (args.backward or args.targets)):
-        ap.error("--targets, --cached, --backward, --dense, --layer and --rab are separate "
-                 "benchmarks (except --backward --rab and --targets --rab)")
+    if modes > 1 and (args.cached or args.dense or args.layer):
+        ap.error("--cached, --dense and --layer are separate benchmarks; --targets, --backward "
+                 "and --rab combine")
     if args.graph and args.layer:
         ap.error("--graph records the attention calls; --layer has no graph form here")
     if args.layer:
@@ -409,7 +413,7 @@ def main() -> int:
         else:
             def call():
                 hstu.hstu_attn_fwd_rab(q, k, v, off, ts, wp, wt, case.alpha, case.n, out=out)
-    elif args.targets:
+    elif args.targets and not args.backward:
         tg = torch.from_numpy(case.num_targets.astype(np.int32)).cuda()
 
         def call():
@@ -435,19 +439,28 @@ def main() -> int:
         flops *= 2.5
         # q, k, v, dout read once, dq, dk, dv written once
         alg_bytes *= 7.0 / 4.0
+        tg = None
+        if args.targets:
+            tg = torch.from_numpy(case.num_targets.astype(np.int32)).cuda()
+            alg_bytes += 4.0 * case.num_seqs
         if args.rab:
             ts = torch.from_numpy(rab.timestamps).cuda()
             wp = torch.from_numpy(rab.pos_bias).cuda()
             wt = torch.from_numpy(rab.time_bias).cuda()
             rgrads = grads + (torch.empty_like(wp), torch.empty_like(wt))
             alg_bytes += 4.0 * case.total + 8.0 * (rab.pos_bias.size + rab.time_bias.size)
-
-            def call():
-                hstu.hstu_attn_bwd_rab(q, k, v, dout, off, ts, wp, wt, case.alpha, case.n,
-                                       grads=rgrads)
+            if tg is not None:
+                def call():
+                    hstu.hstu_attn_bwd_rab_targets(q, k, v, dout, off, tg, ts, wp, wt,
+                                                   case.alpha, case.n, grads=rgrads)
+            else:
+                def call():
+                    hstu.hstu_attn_bwd_rab(q, k, v, dout, off, ts, wp, wt, case.alpha, case.n,
+                                           grads=rgrads)
         else:
             def call():
-                hstu.hstu_attn_bwd(q, k, v, dout, off, case.alpha, case.n, grads=grads)
+                hstu.hstu_attn_bwd(q, k, v, dout, off, case.alpha, case.n, grads=grads,
+                                   num_targets=tg)
     else:
         def call():
             hstu.hstu_attn_fwd(q, k, v, off, case.alpha, case.n, out=out)
@@ -540,11 +553,12 @@ def main() -> int:
 
     L = case.lengths
     line = {
-        "metric": (METRIC_CACHED if args.cached else
+        "metric": ((METRIC_RAB_BWD if args.rab else METRIC_BWD) +
+                   (" (target-aware mask)" if args.targets else "") if args.backward else
+                   METRIC_CACHED if args.cached else
                    METRIC_RAB_TARGETS if args.targets and args.rab else
                    METRIC_TARGETS if args.targets else
-                   METRIC_RAB_BWD if args.backward and args.rab else
-                   METRIC_BWD if args.backward else METRIC_DENSE if args.dense else
+                   METRIC_DENSE if args.dense else
                    METRIC_RAB if args.rab else METRIC),
         "value": round(value, 2),
         "unit": "TFLOP/s",

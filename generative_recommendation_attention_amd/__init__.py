@@ -13,8 +13,8 @@ seq_offsets: int32 CUDA tensor [num_seqs + 1] of prefix sums.
 
 Also: hstu_attn_fwd_{bf16,fp16,fp32} (type fixed), hstu_attn_fwd_targets
 (target-aware mask), hstu_attn_fwd_rab / hstu_attn_bwd_rab (relative
-attention bias), hstu_attn_fwd_rab_targets (the bias under the target-aware
-mask),
+attention bias), hstu_attn_fwd_rab_targets / hstu_attn_bwd_rab_targets (the
+bias under the target-aware mask),
 hstu_attn_fwd_cached (candidates against a cached history),
 hstu_attn_fwd_dense / hstu_attn_bwd_dense ((B, heads, S, d) tensors),
 hstu_attn_bwd (dq, dk, dv), hstu_layer_in_proj /
@@ -51,7 +51,8 @@ EXPORTS = ("hstu_attn_fwd", "hstu_attn_fwd_bf16", "hstu_attn_fwd_fp16", "hstu_at
            "hstu_attn_fwd_rab", "hstu_attn_fwd_rab_targets", "hstu_attn_bwd_rab", "hstu_attn_bwd",
            "hstu_attn_bwd_dense", "hstu_layer_in_proj", "hstu_layer_out_proj",
            "hstu_attn_bwd_targets", "hstu_validate_offsets", "hstu_status_string", "hstu_last_hip_error",
-           "hstu_release_workspace", "hstu_profile_enable", "hstu_profile_read", "hstu_attn_fwd_noalloc")
+           "hstu_release_workspace", "hstu_profile_enable", "hstu_profile_read",
+           "hstu_attn_fwd_noalloc", "hstu_attn_bwd_rab_targets")
 
 
 class HstuError(RuntimeError):
@@ -112,6 +113,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hstu_attn_bwd_rab.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, f32,
                                       f32, vp, vp, vp, vp, vp, vp, ctypes.c_int]
     lib.hstu_attn_bwd_rab.restype = ctypes.c_int
+    lib.hstu_attn_bwd_rab_targets.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32,
+                                              i32, i32, f32, f32, vp, vp, vp, vp, vp, vp,
+                                              ctypes.c_int]
+    lib.hstu_attn_bwd_rab_targets.restype = ctypes.c_int
     i64 = ctypes.c_int64
     lib.hstu_layer_in_proj.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp,
                                        ctypes.c_int]
@@ -425,18 +430,30 @@ def hstu_attn_bwd_rab(q, k, v, dout, seq_offsets, timestamps, pos_bias, time_bia
     """Gradients of hstu_attn_fwd_rab for the upstream gradient dout:
     (dq, dk, dv, d_pos_bias, d_time_bias), the last two float32 like the
     tables.  `grads` may supply the five output tensors."""
+    return _bwd_rab(q, k, v, dout, seq_offsets, None, timestamps, pos_bias, time_bias, alpha, n,
+                    grads, stream)
+
+
+def hstu_attn_bwd_rab_targets(q, k, v, dout, seq_offsets, num_targets, timestamps, pos_bias,
+                              time_bias, alpha: float, n: float, grads=None, stream=None):
+    """Gradients of hstu_attn_fwd_rab_targets (num_targets: int32 [num_seqs]),
+    returned as in hstu_attn_bwd_rab."""
+    return _bwd_rab(q, k, v, dout, seq_offsets, num_targets, timestamps, pos_bias, time_bias,
+                    alpha, n, grads, stream)
+
+
+def _bwd_rab(q, k, v, dout, seq_offsets, num_targets, timestamps, pos_bias, time_bias,
+             alpha: float, n: float, grads, stream):
     import torch
     _check_tensors(q, k, v, seq_offsets, torch.empty_like(q))
     T, heads, d = q.shape
+    num_seqs = seq_offsets.numel() - 1
     if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_cuda or \
             not dout.is_contiguous():
         raise ValueError("dout must be a contiguous GPU tensor shaped and typed like q")
-    if (timestamps.dtype != torch.int32 or timestamps.shape != (T,) or not timestamps.is_cuda or
-            not timestamps.is_contiguous()):
-        raise ValueError("timestamps must be a contiguous int32 GPU tensor of T entries")
-    for name, t in (("pos_bias", pos_bias), ("time_bias", time_bias)):
-        if t.dtype != torch.float32 or t.dim() != 1 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous 1-D float32 GPU tensor")
+    _check_rab(T, timestamps, pos_bias, time_bias)
+    if num_targets is not None:
+        _check_targets(num_targets, num_seqs)
     if grads is None:
         grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q),
                  torch.empty_like(pos_bias), torch.empty_like(time_bias))
@@ -449,19 +466,21 @@ def hstu_attn_bwd_rab(q, k, v, dout, seq_offsets, timestamps, pos_bias, time_bia
                 not t.is_cuda:
             raise ValueError("table gradients must be contiguous float32 GPU tensors shaped "
                              "like the tables")
-    num_seqs = seq_offsets.numel() - 1
     if T == 0:
         dpos.zero_()
         dtime.zero_()
         return dq, dk, dv, dpos, dtime
     lib = load_library()
-    st = lib.hstu_attn_bwd_rab(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
-                               seq_offsets.data_ptr(), timestamps.data_ptr(), pos_bias.data_ptr(),
-                               pos_bias.numel(), time_bias.data_ptr(), time_bias.numel(),
-                               num_seqs, heads, d, float(alpha), float(n), dq.data_ptr(),
-                               dk.data_ptr(), dv.data_ptr(), dpos.data_ptr(), dtime.data_ptr(),
-                               _stream_handle(stream), _dtype_code(q))
-    _check(st, "hstu_attn_bwd_rab")
+    head = (q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), seq_offsets.data_ptr())
+    tail = (timestamps.data_ptr(), pos_bias.data_ptr(), pos_bias.numel(), time_bias.data_ptr(),
+            time_bias.numel(), num_seqs, heads, d, float(alpha), float(n), dq.data_ptr(),
+            dk.data_ptr(), dv.data_ptr(), dpos.data_ptr(), dtime.data_ptr(),
+            _stream_handle(stream), _dtype_code(q))
+    if num_targets is None:
+        _check(lib.hstu_attn_bwd_rab(*head, *tail), "hstu_attn_bwd_rab")
+    else:
+        _check(lib.hstu_attn_bwd_rab_targets(*head, num_targets.data_ptr(), *tail),
+               "hstu_attn_bwd_rab_targets")
     return dq, dk, dv, dpos, dtime
 
 

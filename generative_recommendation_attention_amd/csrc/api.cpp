@@ -776,13 +776,16 @@ hstu_status_t hstu_attn_bwd_targets(const void* q, const void* k, const void* v,
                          dq, dk, dv, stream, dtype);
 }
 
-hstu_status_t hstu_attn_bwd_rab(const void* q, const void* k, const void* v, const void* dout,
-                                const int32_t* seq_offsets, const int32_t* timestamps,
-                                const float* pos_bias, int32_t num_pos, const float* time_bias,
-                                int32_t num_time, int32_t num_seqs, int32_t heads, int32_t d,
-                                float alpha, float n, void* dq, void* dk, void* dv,
-                                float* d_pos_bias, float* d_time_bias, hipStream_t stream,
-                                hstu_dtype_t dtype) {
+// (shared checks of the two bias backward entry points)
+static hstu_status_t attn_bwd_rab_call(const void* q, const void* k, const void* v,
+                                       const void* dout, const int32_t* seq_offsets,
+                                       const int32_t* num_targets, const int32_t* timestamps,
+                                       const float* pos_bias, int32_t num_pos,
+                                       const float* time_bias, int32_t num_time,
+                                       int32_t num_seqs, int32_t heads, int32_t d, float alpha,
+                                       float n, void* dq, void* dk, void* dv, float* d_pos_bias,
+                                       float* d_time_bias, hipStream_t stream,
+                                       hstu_dtype_t dtype) {
     if (num_pos < 1 || num_pos > (1 << 18) || num_time < 1 || num_time > 32)
         return HSTU_ERR_INVALID_ARG;
     if (!(alpha != 0.0f) || !std::isfinite((float)(1.0 / (double)alpha)))
@@ -799,8 +802,36 @@ hstu_status_t hstu_attn_bwd_rab(const void* q, const void* k, const void* v, con
     }
     const RabGrads rab{timestamps, pos_bias, time_bias, num_pos, num_time, d_pos_bias,
                        d_time_bias};
-    return attn_bwd_call(q, k, v, dout, seq_offsets, nullptr, num_seqs, heads, d, alpha, n, dq,
-                         dk, dv, stream, dtype, 0, &rab);
+    return attn_bwd_call(q, k, v, dout, seq_offsets, num_targets, num_seqs, heads, d, alpha, n,
+                         dq, dk, dv, stream, dtype, 0, &rab);
+}
+
+hstu_status_t hstu_attn_bwd_rab(const void* q, const void* k, const void* v, const void* dout,
+                                const int32_t* seq_offsets, const int32_t* timestamps,
+                                const float* pos_bias, int32_t num_pos, const float* time_bias,
+                                int32_t num_time, int32_t num_seqs, int32_t heads, int32_t d,
+                                float alpha, float n, void* dq, void* dk, void* dv,
+                                float* d_pos_bias, float* d_time_bias, hipStream_t stream,
+                                hstu_dtype_t dtype) {
+    return attn_bwd_rab_call(q, k, v, dout, seq_offsets, nullptr, timestamps, pos_bias, num_pos,
+                             time_bias, num_time, num_seqs, heads, d, alpha, n, dq, dk, dv,
+                             d_pos_bias, d_time_bias, stream, dtype);
+}
+
+hstu_status_t hstu_attn_bwd_rab_targets(const void* q, const void* k, const void* v,
+                                        const void* dout, const int32_t* seq_offsets,
+                                        const int32_t* num_targets, const int32_t* timestamps,
+                                        const float* pos_bias, int32_t num_pos,
+                                        const float* time_bias, int32_t num_time,
+                                        int32_t num_seqs, int32_t heads, int32_t d, float alpha,
+                                        float n, void* dq, void* dk, void* dv, float* d_pos_bias,
+                                        float* d_time_bias, hipStream_t stream,
+                                        hstu_dtype_t dtype) {
+    if (num_seqs > 0 && (!num_targets || (reinterpret_cast<uintptr_t>(num_targets) & 3u) != 0))
+        return HSTU_ERR_INVALID_ARG;
+    return attn_bwd_rab_call(q, k, v, dout, seq_offsets, num_targets, timestamps, pos_bias,
+                             num_pos, time_bias, num_time, num_seqs, heads, d, alpha, n, dq, dk,
+                             dv, d_pos_bias, d_time_bias, stream, dtype);
 }
 
 hstu_status_t hstu_attn_bwd_dense(const void* q, const void* k, const void* v, const void* dout,

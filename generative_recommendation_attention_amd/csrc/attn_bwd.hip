@@ -132,6 +132,26 @@ __device__ __forceinline__ bool rab_far(int rmin, int kmax, int ntime) {
     return (int64_t)rmin - kmax >= ((int64_t)1 << (ntime - 1)) - 1;
 }
 
+// Sum of each of a lane's 16 registers over the 32 lanes of its half-wave,
+// by recursive halving (four exchanges that each halve the registers a lane
+// carries, then one that completes the sum): lane l ends with the sum of
+// register (l >> 1) & 15.
+__device__ __forceinline__ float half_wave_column_sum(const f32x16& x, int l32) {
+    const bool b4 = l32 & 16, b3 = l32 & 8, b2 = l32 & 4, b1 = l32 & 2;
+    float y[8], z[4], w[2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        y[i] = (b4 ? x[i + 8] : x[i]) + __shfl_xor(b4 ? x[i] : x[i + 8], 16, 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        z[i] = (b3 ? y[i + 4] : y[i]) + __shfl_xor(b3 ? y[i] : y[i + 4], 8, 64);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        w[i] = (b2 ? z[i + 2] : z[i]) + __shfl_xor(b2 ? z[i] : z[i + 2], 4, 64);
+    const float u = (b1 ? w[1] : w[0]) + __shfl_xor(b1 ? w[0] : w[1], 2, 64);
+    return u + __shfl_xor(u, 1, 64);
+}
+
 // Shapes shared by both kernels: 4 waves of 32 rows (128 rows per item), 32-row
 // streamed blocks.
 template <int D>
@@ -286,7 +306,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv(typename BwdArgsOf<RAB>::
     static_assert(C::NW * 64 >= FUSE_SEQS && C::NW * 64 >= 32 * NQ, "fused tables need a thread per sequence");
     static_assert(NS * SLOT + RAB_BYTES + (int)sizeof(LocalTables) <= 80 * 1024,
                   "LDS for two workgroups per CU");
-    static_assert(!RAB || (PF == 1 && !TGT), "bias: one block ahead, causal mask");
+    static_assert(!RAB || PF == 1, "bias: one block ahead");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -343,11 +363,21 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv(typename BwdArgsOf<RAB>::
         // With the bias: 1 - ts of this lane's key, so that ts_q + c1 = gap + 1.
         uint32_t c1 = 0;
         int kmax = 0;   // the wave's latest key timestamp
+        // Target-aware mask: a candidate row sits right after the history, so
+        // its position term is wpos[hist - key] for this lane's history key
+        // (pos_c) and wpos[0] for its own key (pos_0).
+        float pos_c = 0.0f, pos_0 = 0.0f;
         if constexpr (RAB) {
             c1 = 1u - __builtin_amdgcn_raw_buffer_load_b32(
                               make_rsrc(a.ts + start + kw0, (int64_t)(s - kw0) * 4), l32 * 4, 0, 0);
             if constexpr (D == 64)
                 kmax = wave_max_i32(kw0 + l32 < s ? (int)(1u - c1) : INT32_MIN);
+            if constexpr (TGT) {
+                const int dc = hist - (kw0 + l32);
+                const float w = a.wpos[min(max(dc, 0), a.npos - 1)];
+                pos_c = (dc >= 1 && dc < a.npos) ? w : 0.0f;
+                pos_0 = a.wpos[0];
+            }
         }
 
         // Block c into slot c % NS; blocks are issued PF ahead, also past the
@@ -391,6 +421,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv(typename BwdArgsOf<RAB>::
                     const unsigned char* ra = lds + NS * SLOT + (c % NS) * RABB_WORDS * 4;
                     const float* win = reinterpret_cast<const float*>(ra + 4 * RABB_TS) +
                                        (128 - 32 * wv - l32 + 4 * g);
+                    // position term of register r (candidate rows: see pos_c)
+                    const bool cand = TGT && q0 + 31 >= hist;
+                    auto posv = [&](int r) {
+                        const float w = win[8 * (r >> 2) + (r & 3)];
+                        if (!cand) return w;
+                        const int qr = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
+                        return qr < hist ? w : (qr == kw0 + l32 ? pos_0 : pos_c);
+                    };
                     // (query rows past the sequence read 0: a block holding
                     // them only looks nearer)
                     bool far = false;
@@ -400,8 +438,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv(typename BwdArgsOf<RAB>::
                     if (far) {
                         const float tlast = ttab[0];
 #pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            st[r] = (win[8 * (r >> 2) + (r & 3)] + tlast) * a.bias_scale;
+                        for (int r = 0; r < 16; ++r) st[r] = (posv(r) + tlast) * a.bias_scale;
                     } else {
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
@@ -410,7 +447,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv(typename BwdArgsOf<RAB>::
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
                                 const int f = ffbh_u32(tq[e] + c1);
-                                st[4 * j + e] = (win[8 * j + e] + ttab[f + 1]) * a.bias_scale;
+                                st[4 * j + e] = (posv(4 * j + e) + ttab[f + 1]) * a.bias_scale;
                             }
                         }
                     }
@@ -505,9 +542,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
     __shared__ LocalTables lt;
     __shared__ float ttab[RAB ? 33 : 1];
     __shared__ float ring[RAB ? 4 * 256 : 1];   // per wave: position-gradient sums by distance mod 256
-    __shared__ float tbins[RAB ? 32 : 1];        // time-gradient sums by bucket
+    // time-gradient sums by bucket; [32]: candidates' pairs with themselves
+    // (position distance 0, target-aware mask)
+    __shared__ float tbins[RAB ? 33 : 1];
     static_assert(C::NW * 64 >= FUSE_SEQS && C::NW * 64 >= 32 * NQ, "fused tables need a thread per sequence");
-    static_assert(!RAB || (PF == 1 && !TGT), "bias: one block ahead, causal mask");
+    static_assert(!RAB || PF == 1, "bias: one block ahead");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -521,7 +560,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
     float* gpart = nullptr;
     if constexpr (RAB) {
         if (tid < 33) ttab[tid] = a.wtime[rab_time_bucket(tid, a.ntime)];
-        if (tid < 32) tbins[tid] = 0.0f;
+        if (tid < 33) tbins[tid] = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) ring[tid + 256 * i] = 0.0f;
         gpart = a.gpart + (int64_t)(blockIdx.x % a.nparts) * a.gstride;
@@ -571,6 +610,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
         const int nh = TGT ? (hist + 31) / 32 : nb_all;
         const int jump = TGT ? max(q0 / 32 - nh, 0) : 0;
         const int nblk = nb_all - jump;
+        auto k0_of = [&](int c) { return 32 * (c >= nh ? c + jump : c); };
+        // The bias sees a candidate row (row >= hist) at position hist: the
+        // item's distances are those of effective rows min(row, hist), which
+        // start at q0e.
+        const int q0e = TGT ? min(q0, hist) : q0;
+        const bool cand_w = TGT && wr0 + 31 >= hist;   // the wave has candidate rows
         const int64_t seq_base = (int64_t)start * H * D + (int64_t)head * a.head_stride;
         const uint16_t* kb = a.k + seq_base;
         const uint16_t* vb = a.v + seq_base;
@@ -586,6 +631,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
         // With the bias: ts of this lane's query + 1.
         uint32_t trp1 = 0;
         int rmin = 0;   // the wave's earliest query timestamp
+        float pos_0 = 0.0f, d0 = 0.0f;   // wpos[0]; this lane's candidate-with-itself dS
+        if constexpr (RAB && TGT) pos_0 = a.wpos[0];
         if constexpr (RAB) {
             trp1 = __builtin_amdgcn_raw_buffer_load_b32(
                            make_rsrc(a.ts + start + wr0, (int64_t)(s - wr0) * 4), l32 * 4, 0, 0) +
@@ -603,7 +650,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
             stage<D>(vb, row_stride, row0, kv_end, row_bytes, sl + 2 * C::ARR, lo, false);
             if constexpr (RAB) {
                 // wave 0: the block's key timestamps; waves 1-3: wpos at
-                // distances q0 - row0 - 32 + 64 (wv - 1) + lane
+                // distances q0e - row0 - 32 + 64 (wv - 1) + lane
                 unsigned char* ra = lds + NS * SLOT + (c % NS) * RABB_WORDS * 4;
                 if (wv == 0)
                     load4_to_lds(make_rsrc32(a.ts + start + row0, min(kv_end - row0, 32) * 4), ra,
@@ -611,7 +658,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
                 else
                     load4_to_lds(make_rsrc32(a.wpos, a.npos * 4),
                                  ra + 4 * RABB_TS + 256 * (wv - 1),
-                                 4 * (q0 - row0 - 32 + 64 * (wv - 1) + lane));
+                                 4 * (q0e - row0 - 32 + 64 * (wv - 1) + lane));
             }
         };
 #pragma unroll
@@ -620,8 +667,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
             __builtin_amdgcn_s_waitcnt(VMCNT_LE((PF - 1) * LT));
             __syncthreads();
             issue(c + PF);
-            // (block c-1 done by every wave: distances only it could touch are final)
-            if (c > 0) flush_ring(q0 - 32 * c + 128, q0 - 32 * c + 159);
+            // (block c-1 done by every wave: distances only it or the blocks
+            // jumped over could touch are final; what can still be non-zero
+            // lies within block c-1's own range)
+            if (c > 0)
+                flush_ring(max(q0e + 128 - k0_of(c), q0e - k0_of(c - 1) - 31),
+                           q0e + 127 - k0_of(c - 1));
             const unsigned char* sl = lds + (c % NS) * SLOT;
             const int k0 = 32 * (c >= nh ? c + jump : c);
             const bool skip = !live || k0 > wr0 || (TGT && k0 >= hist && k0 + 31 < wr0);
@@ -631,10 +682,19 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
                 bool far = false;
                 if constexpr (RAB) {
                     // rab / alpha for query wr0 + l32 and key k0 + 8(r/4) + 4g + r%4:
-                    // distance = window entry 32wv + l32 + 32 - 4g - 8(r/4) - r%4
+                    // distance = window entry erow - q0e + 32 - 4g - 8(r/4) - r%4,
+                    // erow the lane's effective row (a candidate and its own
+                    // key: distance 0, pos_0)
                     const unsigned char* ra = lds + NS * SLOT + (c % NS) * RABB_WORDS * 4;
+                    const int erow = TGT ? min(wr0 + l32, hist) : wr0 + l32;
                     const float* win = reinterpret_cast<const float*>(ra + 4 * RABB_TS) +
-                                       (32 * wv + l32 + 5 - 4 * g);
+                                       (erow - q0e + 5 - 4 * g);
+                    auto posv = [&](int r) {
+                        const float w = win[27 - 8 * (r >> 2) - (r & 3)];
+                        if (!cand_w) return w;
+                        const int key = k0 + 8 * (r >> 2) + 4 * g + (r & 3);
+                        return (wr0 + l32 >= hist && key == wr0 + l32) ? pos_0 : w;
+                    };
                     // (keys past the sequence read 0: a block holding them
                     // only looks nearer)
                     if constexpr (D == 64)
@@ -644,8 +704,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
                     if (far) {
                         const float tlast = ttab[0];
 #pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            st[r] = (win[27 - 8 * (r >> 2) - (r & 3)] + tlast) * a.bias_scale;
+                        for (int r = 0; r < 16; ++r) st[r] = (posv(r) + tlast) * a.bias_scale;
                     } else {
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
@@ -653,8 +712,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
                                 const int f = ffbh_u32(trp1 - tk[j][e]);
-                                st[4 * j + e] =
-                                        (win[27 - 8 * j - e] + ttab[f + 1]) * a.bias_scale;
+                                st[4 * j + e] = (posv(4 * j + e) + ttab[f + 1]) * a.bias_scale;
                             }
                         }
                     }
@@ -679,6 +737,29 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
                     ds[r] = dsr;
                 }
                 if constexpr (RAB) {
+                    f32x16 dgl = ds;   // the pairs credited along diagonals (row - key)
+                    if constexpr (TGT) {
+                        if (cand_w) {
+                            // A candidate row's pairs with history keys go to
+                            // distance hist - key (column sums over the wave's
+                            // candidate rows), its pair with itself to
+                            // distance 0 (d0, added once per item).
+                            const bool crow = row >= hist;
+                            f32x16 dcol;
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int key = k0 + 8 * (r >> 2) + 4 * g + (r & 3);
+                                dcol[r] = (crow && key < hist) ? ds[r] : 0.0f;
+                                d0 += (crow && key == row) ? ds[r] : 0.0f;
+                                dgl[r] = crow ? 0.0f : ds[r];
+                            }
+                            const float u = half_wave_column_sum(dcol, l32);
+                            const int cr = (l32 >> 1) & 15;
+                            const int ckey = k0 + 8 * (cr >> 2) + 4 * g + (cr & 3);
+                            if ((l32 & 1) == 0 && ckey < hist)
+                                ring[256 * wv + ((hist - ckey) & 255)] += u;
+                        }
+                    }
                     // distance of register r: wr0 + l32 - k0 - 4g - (8(r/4) + r%4);
                     // masked pairs add exactly zero
                     // Diagonal sums: register r of lane (g, l) holds query wr0 + l,
@@ -691,7 +772,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int o = 8 * (r >> 2) + 4 * g + (r & 3);
-                        const float x = __shfl(ds[r], 32 * g + ((l32 + o) & 31), 64);
+                        const float x = __shfl(dgl[r], 32 * g + ((l32 + o) & 31), 64);
                         if (l32 + o <= 31)
                             dhi += x;
                         else
@@ -756,8 +837,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
         if constexpr (RAB) {
             // the item's remaining distances: those of its last block
             // (every ring update of the item is done: the barrier above)
-            const int last = q0 - 32 * (nblk - 1);
+            const int last = q0e - k0_of(nblk - 1);
             flush_ring(last - 31, last + 127);
+            if (cand_w) {
+                float t = d0;
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o, 64);
+                if (lane == 0 && t != 0.0f) atomicAdd(&tbins[32], t);
+            }
         }
     }
     if constexpr (RAB) {
@@ -765,6 +852,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
         if (tid < a.ntime && tbins[tid] != 0.0f)
             __hip_atomic_fetch_add(gpart + a.npos + tid, tbins[tid] * a.dv_scale,
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (TGT && tid == 32 && tbins[32] != 0.0f)
+            __hip_atomic_fetch_add(gpart, tbins[32] * a.dv_scale, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -832,7 +922,7 @@ __global__ void rab_reduce_kernel(const float* gpart, int nparts, int gstride, i
         dtime[j - npos] = acc;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool TGT>
 hipError_t launch_bwd_rab(const BwdParams& p, WorkList wl, hipStream_t stream, hipEvent_t start,
                           hipEvent_t stop) {
     BwdArgsRab a;
@@ -844,7 +934,7 @@ hipError_t launch_bwd_rab(const BwdParams& p, WorkList wl, hipStream_t stream, h
     a.dk = static_cast<uint16_t*>(p.dk);
     a.dv = static_cast<uint16_t*>(p.dv);
     a.offsets = p.offsets;
-    a.ntgt = nullptr;
+    a.ntgt = TGT ? p.num_targets : nullptr;
     a.num_seqs = p.num_seqs;
     a.heads = p.heads;
     a.row_stride = (int64_t)p.heads * p.d;
@@ -862,10 +952,10 @@ hipError_t launch_bwd_rab(const BwdParams& p, WorkList wl, hipStream_t stream, h
     a.nparts = RAB_PARTS;
     a.bias_scale = (float)(1.0 / (double)p.alpha);
     using Fn = void (*)(BwdArgsRab);
-    const Fn f_dkv = wl.fused ? attn_bwd_dkv<T, D, true, false, true>
-                              : attn_bwd_dkv<T, D, false, false, true>;
-    const Fn f_dq = wl.fused ? attn_bwd_dq<T, D, true, false, true>
-                             : attn_bwd_dq<T, D, false, false, true>;
+    const Fn f_dkv = wl.fused ? attn_bwd_dkv<T, D, true, TGT, true>
+                              : attn_bwd_dkv<T, D, false, TGT, true>;
+    const Fn f_dq = wl.fused ? attn_bwd_dq<T, D, true, TGT, true>
+                             : attn_bwd_dq<T, D, false, TGT, true>;
     static int grids[2][2] = {};
     int& g_dkv = grids[wl.fused ? 1 : 0][0];
     int& g_dq = grids[wl.fused ? 1 : 0][1];
@@ -901,7 +991,9 @@ hipError_t launch_bwd_rab(const BwdParams& p, WorkList wl, hipStream_t stream, h
 template <typename T, int D>
 hipError_t launch_bwd_mask(const BwdParams& p, WorkList wl, hipStream_t stream, hipEvent_t start,
                            hipEvent_t stop) {
-    if (p.timestamps) return launch_bwd_rab<T, D>(p, wl, stream, start, stop);
+    if (p.timestamps)
+        return p.num_targets ? launch_bwd_rab<T, D, true>(p, wl, stream, start, stop)
+                             : launch_bwd_rab<T, D, false>(p, wl, stream, start, stop);
     return p.num_targets ? launch_bwd_typed<T, D, true>(p, wl, stream, start, stop)
                          : launch_bwd_typed<T, D, false>(p, wl, stream, start, stop);
 }
@@ -948,11 +1040,13 @@ struct BwdArgsF32 {
 // memory (the float32 kernels are the reference-precision path, not the fast
 // one); ttab is the time table by v_ffbh_u32(gap + 1) + 1, already over
 // alpha.  Rows or keys at or past the sequence's end get 0 (their terms are
-// zero anyway).  *dist and *bucket name the table entries the pair uses.
+// zero anyway).  *dist and *bucket name the table entries the pair uses; a
+// candidate row (row >= hist) sits right after the history: distance
+// hist - key to a history key, 0 to itself.
 __device__ __forceinline__ float bias_over_alpha_f32(const BwdArgsF32& a, const float* ttab,
-                                                     int start, int s, int row, int key,
+                                                     int start, int s, int hist, int row, int key,
                                                      int* dist, int* bucket) {
-    *dist = row - key;
+    *dist = row >= hist ? (key == row ? 0 : hist - key) : row - key;
     *bucket = 0;
     if (row >= s || key >= s) return 0.0f;
     const uint32_t x = (uint32_t)a.ts[start + row] + 1u - (uint32_t)a.ts[start + key];
@@ -1000,7 +1094,6 @@ template <int D, bool FUSED, bool TGT, bool RAB = false>
 __global__ __launch_bounds__(256) void attn_bwd_dkv_f32(BwdArgsF32 a) {
     using C = BwdCfgF32<D>;
     constexpr int NDB = D / 32;
-    static_assert(!RAB || !TGT, "bias: causal mask");
     __shared__ __attribute__((aligned(16))) float ql[32 * C::STR];
     __shared__ __attribute__((aligned(16))) float ol[32 * C::STR];
     __shared__ int s_item[NQ];
@@ -1072,8 +1165,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_f32(BwdArgsF32 a) {
                     const int qrow = 8 * (r >> 2) + 4 * g + (r & 3);   // row inside the block
                     if constexpr (RAB) {
                         int dist, bucket;
-                        st[r] += bias_over_alpha_f32(a, ttab, start, s, q0 + qrow, key, &dist,
-                                                     &bucket);
+                        st[r] += bias_over_alpha_f32(a, ttab, start, s, hist, q0 + qrow, key,
+                                                     &dist, &bucket);
                     }
                     pointwise(st[r], dp[r], a.alpha, &pr, &dsr);
                     if (masked) {
@@ -1118,7 +1211,6 @@ template <int D, bool FUSED, bool TGT, bool RAB = false>
 __global__ __launch_bounds__(256) void attn_bwd_dq_f32(BwdArgsF32 a) {
     using C = BwdCfgF32<D>;
     constexpr int NDB = D / 32;
-    static_assert(!RAB || !TGT, "bias: causal mask");
     __shared__ __attribute__((aligned(16))) float kl[32 * C::STR];
     __shared__ __attribute__((aligned(16))) float vl[32 * C::STR];
     __shared__ int s_item[NQ];
@@ -1196,8 +1288,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f32(BwdArgsF32 a) {
                     const int krow = 8 * (r >> 2) + 4 * g + (r & 3);   // key inside the block
                     int dist = 0, bucket = 0;
                     if constexpr (RAB)
-                        st[r] += bias_over_alpha_f32(a, ttab, start, s, row, k0 + krow, &dist,
-                                                     &bucket);
+                        st[r] += bias_over_alpha_f32(a, ttab, start, s, hist, row, k0 + krow,
+                                                     &dist, &bucket);
                     pointwise(st[r], dp[r], a.alpha, &pr, &dsr);
                     if (masked) {
                         const int kk = k0 + krow;
@@ -1317,7 +1409,9 @@ hipError_t launch_bwd_f32_typed(const BwdParams& p, WorkList wl, hipStream_t str
 template <int D>
 hipError_t launch_bwd_f32(const BwdParams& p, WorkList wl, hipStream_t stream, hipEvent_t start,
                           hipEvent_t stop) {
-    if (p.timestamps) return launch_bwd_f32_typed<D, false, true>(p, wl, stream, start, stop);
+    if (p.timestamps)
+        return p.num_targets ? launch_bwd_f32_typed<D, true, true>(p, wl, stream, start, stop)
+                             : launch_bwd_f32_typed<D, false, true>(p, wl, stream, start, stop);
     return p.num_targets ? launch_bwd_f32_typed<D, true>(p, wl, stream, start, stop)
                          : launch_bwd_f32_typed<D, false>(p, wl, stream, start, stop);
 }

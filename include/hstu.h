@@ -339,6 +339,31 @@ hstu_status_t hstu_attn_bwd_rab(const void* q, const void* k, const void* v, con
                                 float* d_pos_bias, float* d_time_bias, hipStream_t stream,
                                 hstu_dtype_t dtype);
 
+/* Backward of hstu_attn_fwd_rab_targets (HSTU paper translation, §3.4:
+ * M-FALCON changes the mask and rab_{p,t} together; Appendix G: the bias
+ * gradients are accumulated on chip): hstu_attn_bwd_rab's gradients for the
+ * target-aware mask and its bias reading.  A kept pair's score gradient goes
+ * to the position entry of the distance its bias used: r - c for a history
+ * row, hist - c for a candidate row and a history key, 0 for a candidate and
+ * itself (hist = s - t); the time bucket is the pair's real one.  So each
+ * candidate's share equals the last row's share of hstu_attn_bwd_rab over the
+ * history followed by that candidate alone.
+ *
+ *   num_targets : as in hstu_attn_fwd_targets (device int32[num_seqs],
+ *                 clamped to [0, length]).
+ *   the rest    : as in hstu_attn_bwd_rab.
+ * Errors as in hstu_attn_bwd_rab; a null or misaligned num_targets (with
+ * num_seqs > 0) also gives HSTU_ERR_INVALID_ARG. */
+hstu_status_t hstu_attn_bwd_rab_targets(const void* q, const void* k, const void* v,
+                                        const void* dout, const int32_t* seq_offsets,
+                                        const int32_t* num_targets, const int32_t* timestamps,
+                                        const float* pos_bias, int32_t num_pos,
+                                        const float* time_bias, int32_t num_time,
+                                        int32_t num_seqs, int32_t heads, int32_t d, float alpha,
+                                        float n, void* dq, void* dk, void* dv, float* d_pos_bias,
+                                        float* d_time_bias, hipStream_t stream,
+                                        hstu_dtype_t dtype);
+
 /* The backward on the dense (batch, heads, seq_len, d) layout of
  * hstu_attn_fwd_dense (causal mask over all seq_len positions); q, k, v, dout,
  * dq, dk, dv all have that layout.  Other conventions as in hstu_attn_bwd. */
