@@ -525,9 +525,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv(typename BwdArgsOf<RAB>::
 //  Time: each lane sums runs of equal (capped) buckets over its keys
 //  (ascending, so with ordered timestamps a run usually spans the block, and
 //  all pairs past the last bucket's gap share it) and adds a run to a
-//  per-workgroup LDS bin when its bucket changes; at the block's end, when
-//  every lane's run has the same bucket, the wave sums the runs first and
-//  one lane adds them.  The bins go to the partial at the end.
+//  per-workgroup LDS bin when its bucket changes; runs in the last bucket,
+//  nearly all of them past the diagonal blocks, stay in a register for the
+//  whole launch and are summed over the wave once at its end (this measured
+//  1.313 -> 1.249 ms for the bias backward at 16 x 4096; per-block wave sums
+//  and LDS atomics before).  The bins go to the partial at the end.
 template <typename T, int D, bool FUSED, bool TGT, bool RAB = false>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::type a) {
     using C = BwdCfg<D>;
@@ -558,6 +560,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
     const int row_bytes = (int)(row_stride * 2);
     const LaneOffsets<D> lo(lane, wv, row_bytes);
     float* gpart = nullptr;
+    float tlast = 0.0f;   // this lane's time-gradient sum in the last bucket
     if constexpr (RAB) {
         if (tid < 33) ttab[tid] = a.wtime[rab_time_bucket(tid, a.ntime)];
         if (tid < 33) tbins[tid] = 0.0f;
@@ -807,15 +810,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
                             run += ds[r];
                         }
                     }
-                    const int p0 = __builtin_amdgcn_readfirstlane(prev);
-                    if (__all(prev == p0)) {
-                        float t = run;
-#pragma unroll
-                        for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o, 64);
-                        if (lane == 0) atomicAdd(&tbins[p0], t);
-                    } else {
+                    // (the last bucket, where nearly every run ends: in a register)
+                    if (prev == cap)
+                        tlast += run;
+                    else
                         atomicAdd(&tbins[prev], run);
-                    }
                 }
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
@@ -848,6 +847,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
         }
     }
     if constexpr (RAB) {
+        float t = tlast;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o, 64);
+        if (lane == 0 && t != 0.0f) atomicAdd(&tbins[a.ntime - 1], t);
         __syncthreads();
         if (tid < a.ntime && tbins[tid] != 0.0f)
             __hip_atomic_fetch_add(gpart + a.npos + tid, tbins[tid] * a.dv_scale,
