@@ -57,25 +57,33 @@ METRIC_RAB_BWD = "HSTU attn bwd with relative attention bias (dq, dk, dv, table 
 # runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
 # same counter reads for a plain 1 GiB device copy (bench.py --copy-calibrate):
 # FETCH_SIZE reads 0.5 GiB for that copy's 1 GiB of reads, WRITE_SIZE 1 GiB.
-# The figures hold for the kernel source with the SHA-256 below; for any other
-# source the bench reports traffic as null.
+# The figures hold for the kernel and work-list sources with the SHA-256 below
+# (the queue order decides which key/value re-reads hit the L2); for any other
+# sources the bench reports traffic as null.
 TRAFFIC = {
-    "kernel_source": "generative_recommendation_attention_amd/csrc/attn_fwd.hip",
-    "kernel_sha256": "fd5bc37d2dabaa9ba965cb87ff96a73c68008845a3c50d79aed707d3edee0437",
+    "sources": ("generative_recommendation_attention_amd/csrc/attn_fwd.hip",
+                "generative_recommendation_attention_amd/csrc/schedule.h",
+                "generative_recommendation_attention_amd/csrc/schedule.hip"),
+    "sha256": "",
     "fetch_scale": 2.0,
     "write_scale": 1.0,
     # mean over the launches that take the timed calls' form
-    "fetch_kib": {1: 291.7, 2: 95320.6, 3: 1232491.8, 4: 376766.9, 5: 529559.1},
-    "write_kib": {1: 200.8, 2: 39513.2, 3: 141169.8, 4: 54576.8, 5: 264993.7},
+    "fetch_kib": {},
+    "write_kib": {},
 }
 
 
-def traffic_bytes(workload: int):
+def sources_sha256() -> str:
     import hashlib
-    path = os.path.join(ROOT, TRAFFIC["kernel_source"])
-    with open(path, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if sha != TRAFFIC["kernel_sha256"] or workload not in TRAFFIC["fetch_kib"]:
+    h = hashlib.sha256()
+    for rel in TRAFFIC["sources"]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_bytes(workload: int):
+    if sources_sha256() != TRAFFIC["sha256"] or workload not in TRAFFIC["fetch_kib"]:
         return None
     kib = (TRAFFIC["fetch_kib"][workload] * TRAFFIC["fetch_scale"] +
            TRAFFIC["write_kib"][workload] * TRAFFIC["write_scale"])

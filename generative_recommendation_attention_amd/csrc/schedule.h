@@ -97,9 +97,10 @@ __device__ inline Tables global_tables(const WorkList& wl) {
 
 // Builds the queue tables of a fused launch in LDS, with every thread of the
 // workgroup (blockDim.x >= FUSE_SEQS, a multiple of 64).  The same ranking and
-// band numbering as the work-list kernel: sequences by Q-tile count, largest
-// first (ties by index), pairs dealt to the queues in snake order, per queue
-// the first item of each band.  Workgroup 0 publishes the offset flags.
+// numbering as the work-list kernel: sequences by Q-tile count, largest first
+// (ties by index), pairs dealt to the queues in snake order, per queue the
+// first item of each band (or of each pair, when no sequence has more than
+// PAIRS_MAX_TILES tiles).  Workgroup 0 publishes the offset flags.
 __device__ inline Tables build_local_tables(LocalTables& lt, int* scratch, const int32_t* off,
                                             int num_seqs, int heads, int bq, int* ctl) {
     const int tid = threadIdx.x;
@@ -130,7 +131,9 @@ __device__ inline Tables build_local_tables(LocalTables& lt, int* scratch, const
         lt.ntile[rank] = t;
     }
     __syncthreads();
-    // Band prefix: threads 32x .. 32x+31 scan queue x, CHUNK positions each.
+    // Band (or pair) prefix: threads 32x .. 32x+31 scan queue x, CHUNK
+    // positions each.  (ntile[0]: the largest tile count)
+    const int mode = lt.ntile[0] <= PAIRS_MAX_TILES ? QUEUE_PAIRS : QUEUE_BANDS;
     const int pairs = num_seqs * heads;
     const int qlen = (pairs + NQ - 1) / NQ;
     const int full = pairs / NQ, rem = pairs % NQ;
@@ -153,7 +156,7 @@ __device__ inline Tables build_local_tables(LocalTables& lt, int* scratch, const
                 const long long ti = lt.ntile[queue_pair(i, x) / heads];
                 const long long tn =
                         position_exists(i + 1, x) ? lt.ntile[queue_pair(i + 1, x) / heads] : 0;
-                v = (ti - tn) * (i + 1);
+                v = mode == QUEUE_PAIRS ? ti : (ti - tn) * (i + 1);
             }
             term[c] = v;
             sum += v;
@@ -186,7 +189,7 @@ __device__ inline Tables build_local_tables(LocalTables& lt, int* scratch, const
     __syncthreads();
     if (blockIdx.x == 0 && tid == 0) {
         ctl[CTL_FLAGS] = lt.flags;
-        ctl[CTL_MODE] = QUEUE_BANDS;
+        ctl[CTL_MODE] = mode;
     }
     Tables tb;
     tb.order = lt.order;
@@ -194,7 +197,7 @@ __device__ inline Tables build_local_tables(LocalTables& lt, int* scratch, const
     tb.qprefix = lt.qprefix;
     tb.totals = lt.totals;
     tb.qlen = qlen;
-    tb.mode = QUEUE_BANDS;
+    tb.mode = mode;
     return tb;
 }
 

@@ -219,6 +219,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
         if (kind == RANK_BITONIC) return (int)(keys[m] >> 32);
         return tiles_of(m);
     };
+    const int mode = (kind == RANK_INPUT || maxT <= PAIRS_MAX_TILES) ? QUEUE_PAIRS : QUEUE_BANDS;
 
     // ---- 2. per-queue band prefix --------------------------------------------
     // Thread t of a chunk takes queue x = t % NQ, position i = (base + t) / NQ.
@@ -241,7 +242,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
         if (here) {
             const long long ti = tiles_at_rank(queue_pair(i, x) / heads);
             const long long tn = position_exists(i + 1, x) ? tiles_at_rank(queue_pair(i + 1, x) / heads) : 0;
-            term = (kind == RANK_INPUT) ? ti : (ti - tn) * (long long)(i + 1);
+            term = (mode == QUEUE_PAIRS) ? ti : (ti - tn) * (long long)(i + 1);
         }
         const long long inc = segmented_scan(term, NQ, sh);
         const long long exc = sh.carry[x] + inc - term;
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void schedule_kernel(
     __syncthreads();
     if (tid == 0) {
         wl.ctl[CTL_FLAGS] = sh.flags;
-        wl.ctl[CTL_MODE] = (kind == RANK_INPUT) ? QUEUE_PAIRS : QUEUE_BANDS;
+        wl.ctl[CTL_MODE] = mode;
     }
 }
 

@@ -3,8 +3,9 @@
 The model follows the rules of schedule.hip / schedule.h: sequences ranked by
 Q-tile count (largest first; input order above the sort limit), (rank, head)
 pairs dealt to NQ queues in snake order, items of a sorted queue numbered
-level by level from the last Q tile down (bands), items of an unsorted queue
-pair by pair, and a per-queue prefix decoded by a 64-way search.  On random
+level by level from the last Q tile down (bands), items of an unsorted queue,
+or of any queue when no sequence has more than PAIRS_MAX_TILES tiles, pair by
+pair, and a per-queue prefix decoded by a 64-way search.  On random
 jagged batches it checks that the queues together produce every
 (sequence, head, Q tile) exactly once, never a tile past a sequence's end, and
 that a sorted queue hands out items in non-increasing cost.
@@ -13,6 +14,7 @@ import numpy as np
 import pytest
 
 NQ = 8
+PAIRS_MAX_TILES = 2
 
 
 def queue_pair(i, x):
@@ -23,8 +25,9 @@ def build(lengths, heads, bq, sort_limit=16384):
     L = np.asarray(lengths, np.int64)
     nt = (np.maximum(L, 0) + bq - 1) // bq
     N = len(L)
-    bands = N <= sort_limit
-    if bands:
+    sort = N <= sort_limit
+    bands = sort and N > 0 and int(nt.max()) > PAIRS_MAX_TILES
+    if sort:
         order = sorted(range(N), key=lambda i: (-nt[i], i))
     else:
         order = list(range(N))
@@ -85,6 +88,8 @@ def test_every_item_once(seed):
     lengths[rng.random(N) < 0.2] = 0
     heads = int(rng.integers(1, 5))
     bq = int(rng.choice([32, 64, 128, 256]))
+    if seed % 4 == 3:   # short sequences only: pair order on sorted ranks
+        lengths = np.minimum(lengths, 2 * bq)
     limit = 16384 if seed % 3 else 10  # exercise the input-order path too
     bands, order, ntile, qprefix, counts = build(lengths, heads, bq, sort_limit=limit)
     seen = set()
@@ -136,6 +141,7 @@ def build_local(lengths, heads, bq):
     pairs = n * heads
     qlen = (pairs + NQ - 1) // NQ
     full, rem = pairs // NQ, pairs % NQ
+    bands = ntile[0] > PAIRS_MAX_TILES
 
     def exists(i, x):
         if i < full:
@@ -157,7 +163,7 @@ def build_local(lengths, heads, bq):
                 if exists(i, x):
                     ti = ntile[queue_pair(i, x) // heads]
                     tn = ntile[queue_pair(i + 1, x) // heads] if exists(i + 1, x) else 0
-                    v = (ti - tn) * (i + 1)
+                    v = (ti - tn) * (i + 1) if bands else ti
                 tl.append(v)
             terms.append(tl)
             sums.append(sum(tl))
@@ -173,7 +179,7 @@ def build_local(lengths, heads, bq):
         nx = full + (1 if pos < rem else 0)
         qprefix[x, nx] = int(inc[31])
         totals[x] = int(inc[31])
-    return order, ntile, qprefix, totals
+    return bands, order, ntile, qprefix, totals
 
 
 @pytest.mark.parametrize("seed", range(10))
@@ -185,9 +191,11 @@ def test_local_tables_match_model(seed):
     lengths = rng.integers(0, 3000, size=N)
     lengths[rng.random(N) < 0.2] = 0
     bq = int(rng.choice([32, 128, 256]))
-    order, ntile, qprefix, totals = build_local(lengths, heads, bq)
+    if seed % 3 == 2:   # short sequences only: pair order
+        lengths = np.minimum(lengths, 2 * bq)
+    l_bands, order, ntile, qprefix, totals = build_local(lengths, heads, bq)
     bands, m_order, m_ntile, m_qprefix, counts = build(lengths, heads, bq)
-    assert bands and order == m_order and ntile == m_ntile
+    assert l_bands == bands and order == m_order and ntile == m_ntile
     for x in range(NQ):
         n = int(counts[x])
         assert list(qprefix[x, :n + 1]) == list(m_qprefix[x, :n + 1])
@@ -196,7 +204,7 @@ def test_local_tables_match_model(seed):
     seen = set()
     for x in range(NQ):
         for w in range(totals[x]):
-            i, h, j = decode(True, order, ntile, qprefix, counts, heads, x, w)
+            i, h, j = decode(bands, order, ntile, qprefix, counts, heads, x, w)
             assert 0 <= h < heads and 0 <= j and j * bq < lengths[i]
             seen.add((i, h, j))
     assert len(seen) == sum(int((l + bq - 1) // bq) for l in lengths) * heads
