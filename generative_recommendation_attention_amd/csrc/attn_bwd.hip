@@ -253,12 +253,14 @@ __device__ __forceinline__ void load_rows_b(const uint16_t* base, int64_t row_st
 }
 
 // P and dS for one accumulator register: x = alpha s, sig = 1/(1 + e^-x),
-// p = silu(x) = x sig, ds = dp * sig (1 + x (1 - sig)).
+// p = silu(x) = x sig, and silu'(x) = sig (1 + x (1 - sig)) = sig + p (1 - sig),
+// so ds = dp * fma(p, 1 - sig, sig): one multiply fewer than the first form.
 __device__ __forceinline__ void pointwise(float s, float dp, float alpha, float* p, float* ds) {
     const float x = alpha * s;
     const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-BWD_LOG2E * x));
-    *p = x * sig;
-    *ds = dp * (sig * __builtin_fmaf(x, 1.0f - sig, 1.0f));
+    const float pr = x * sig;
+    *p = pr;
+    *ds = dp * __builtin_fmaf(pr, 1.0f - sig, sig);
 }
 
 // Whether a block's pointwise pass applies the mask: a compile-time constant
