@@ -64,12 +64,12 @@ TRAFFIC = {
     "sources": ("generative_recommendation_attention_amd/csrc/attn_fwd.hip",
                 "generative_recommendation_attention_amd/csrc/schedule.h",
                 "generative_recommendation_attention_amd/csrc/schedule.hip"),
-    "sha256": "",
+    "sha256": "c2629f378770ceb242c52f0148d0f9a5f6662f695d1ba0022281a2c56ffd25d2",
     "fetch_scale": 2.0,
     "write_scale": 1.0,
     # mean over the launches that take the timed calls' form
-    "fetch_kib": {},
-    "write_kib": {},
+    "fetch_kib": {1: 289.8, 2: 94770.2, 3: 1243958.2, 4: 392706.0, 5: 397326.4},
+    "write_kib": {1: 200.7, 2: 39509.7, 3: 141267.2, 4: 54574.5, 5: 264969.9},
 }
 
 
