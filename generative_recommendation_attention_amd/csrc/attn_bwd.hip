@@ -754,7 +754,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
                 const bool masked = k0 + 31 >= wr0 || (TGT && k0 + 31 >= hist);
                 const int row = wr0 + l32;
                 f32x16 ds;
-                // (two copies at d = 64, as in the dK/dV kernel)
+                // (one copy with the mask folded in: two, as in the dK/dV
+                // kernel, take this kernel from 165 to 180 VGPRs at d = 64 and
+                // from three workgroups per CU to two, which cost more than
+                // the selects: 4.85 -> 5.64 M active cycles at 16 x 4096)
                 auto pointwise_block = [&](auto masked_c) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
@@ -767,14 +770,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::t
                         ds[r] = dsr;
                     }
                 };
-                if constexpr (D == 64 && !(RAB && TGT)) {
-                    if (masked)
-                        pointwise_block(std::true_type{});
-                    else
-                        pointwise_block(std::false_type{});
-                } else {
-                    pointwise_block(masked);
-                }
+                pointwise_block(masked);
                 if constexpr (RAB) {
                     f32x16 dgl = ds;   // the pairs credited along diagonals (row - key)
                     if constexpr (TGT) {
