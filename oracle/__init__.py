@@ -26,7 +26,9 @@ only.  ``num_targets=None`` is the plain causal mask.
 ``fwd_cached`` / ``rows_cached`` are the later micro-batches of the same
 algorithm (Appendix H, the encoder-level K/V cache): candidates with their own
 q, k, v attend to a cached history's K and V plus themselves, each request's
-history and candidates given by their own offsets.
+history and candidates given by their own offsets; ``fwd_rab_cached`` /
+``rows_rab_cached`` add the relative attention bias to that form (a candidate
+right after its history, real timestamps).
 
 ``bwd`` / ``bwd_rows`` are the gradients with respect to q, k and v: the
 derivative of the forward definition, per kept (row, key) pair, for an
@@ -148,6 +150,15 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                              ctypes.c_int, ctypes.c_int, f64, f64, ctypes.c_int,
                                              vp, vp, i64, vp]
     lib.hstu_oracle_bwd_rab_rows.restype = ctypes.c_int
+    lib.hstu_oracle_fwd_rab_cached.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
+                                               vp, ctypes.c_int, vp, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_int, f64, f64, vp]
+    lib.hstu_oracle_fwd_rab_cached.restype = ctypes.c_int
+    lib.hstu_oracle_rows_rab_cached.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
+                                                vp, ctypes.c_int, vp, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_int, ctypes.c_int, f64, f64, vp, vp, i64,
+                                                vp]
+    lib.hstu_oracle_rows_rab_cached.restype = ctypes.c_int
     lib.hstu_oracle_bwd_rab_targets.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
                                                 ctypes.c_int, vp, ctypes.c_int, ctypes.c_int,
                                                 ctypes.c_int, ctypes.c_int, f64, f64, vp, vp, vp,
@@ -314,6 +325,63 @@ def _rab_args(q, k, v, offsets, timestamps, pos_bias, time_bias, heads, d, dtype
     if wp.ndim != 1 or wt.ndim != 1:
         raise ValueError("bias tables are 1-D")
     return q, k, v, off, ts, wp, wt
+
+
+def _rab_cached_args(q, k, v, k_cache, v_cache, cand_offsets, hist_offsets, timestamps,
+                     hist_timestamps, pos_bias, time_bias, heads, d, dtype):
+    q, k, v, kc, vc, coff, hoff = _cached_args(q, k, v, k_cache, v_cache, cand_offsets,
+                                               hist_offsets, heads, d, dtype)
+    ts = np.ascontiguousarray(timestamps, dtype=np.int32)
+    hts = np.ascontiguousarray(hist_timestamps, dtype=np.int32)
+    if ts.size < int(coff[-1]) or hts.size < int(hoff[-1]):
+        raise ValueError("timestamps shorter than the offsets imply")
+    wp = np.ascontiguousarray(pos_bias, dtype=np.float64)
+    wt = np.ascontiguousarray(time_bias, dtype=np.float64)
+    return q, k, v, kc, vc, coff, hoff, ts, hts, wp, wt
+
+
+def fwd_rab_cached(q, k, v, cand_offsets, k_cache, v_cache, hist_offsets, timestamps,
+                   hist_timestamps, pos_bias, time_bias, heads: int, d: int, alpha: float,
+                   n: float, dtype: str, lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+    """fp64 (T, heads, d): the cached-history form with the relative attention
+    bias; timestamps per candidate token, hist_timestamps per cached token."""
+    lib = lib or load()
+    q, k, v, kc, vc, coff, hoff, ts, hts, wp, wt = _rab_cached_args(
+            q, k, v, k_cache, v_cache, cand_offsets, hist_offsets, timestamps, hist_timestamps,
+            pos_bias, time_bias, heads, d, dtype)
+    out = np.zeros((int(coff[-1]), heads, d), dtype=np.float64)
+    rc = lib.hstu_oracle_fwd_rab_cached(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc),
+                                        _DTYPE_CODE[dtype], _ptr(coff), _ptr(hoff), _ptr(ts),
+                                        _ptr(hts), _ptr(wp), len(wp), _ptr(wt), len(wt),
+                                        len(coff) - 1, heads, d, float(alpha), float(n),
+                                        _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments (malformed offsets or sizes)")
+    return out
+
+
+def rows_rab_cached(q, k, v, cand_offsets, k_cache, v_cache, hist_offsets, timestamps,
+                    hist_timestamps, pos_bias, time_bias, heads: int, d: int, alpha: float,
+                    n: float, dtype: str, tokens, head_ids,
+                    lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+    """Sampled candidate rows (m, d) of fwd_rab_cached."""
+    lib = lib or load()
+    q, k, v, kc, vc, coff, hoff, ts, hts, wp, wt = _rab_cached_args(
+            q, k, v, k_cache, v_cache, cand_offsets, hist_offsets, timestamps, hist_timestamps,
+            pos_bias, time_bias, heads, d, dtype)
+    tok = np.ascontiguousarray(tokens, dtype=np.int64)
+    hd = np.ascontiguousarray(head_ids, dtype=np.int32)
+    if tok.shape != hd.shape:
+        raise ValueError("tokens and head_ids differ in length")
+    out = np.zeros((len(tok), d), dtype=np.float64)
+    rc = lib.hstu_oracle_rows_rab_cached(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc),
+                                         _DTYPE_CODE[dtype], _ptr(coff), _ptr(hoff), _ptr(ts),
+                                         _ptr(hts), _ptr(wp), len(wp), _ptr(wt), len(wt),
+                                         len(coff) - 1, heads, d, float(alpha), float(n),
+                                         _ptr(tok), _ptr(hd), len(tok), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle rejected the sampled rows")
+    return out
 
 
 def fwd_rab(q, k, v, offsets, timestamps, pos_bias, time_bias, heads: int, d: int,

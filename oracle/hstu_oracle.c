@@ -84,6 +84,11 @@
  * distance the pair's bias used (r - c, or a candidate's hist - c and 0; only
  * below npos) and to the pair's time bucket (the tables' gradients, summed
  * over sequences and heads).
+ * With the cached history (the *_rab_cached entry points) a candidate takes
+ * the same positions as under the target-aware mask, right after its
+ * request's h cached keys: distance h - c to cached key c, 0 to itself, and
+ * the time terms of the real gaps (candidate timestamp minus the cached
+ * key's; zero to itself).
  *
  * Readings taken where the pages are silent (each listed in the design notes):
  *   - alpha multiplies the scores before SiLU; n is a caller-given scalar;
@@ -752,6 +757,116 @@ int hstu_oracle_rows_rab(const void* q, const void* k, const void* v, int dtype,
                          int64_t count, double* out_rows) {
     return hstu_oracle_rows_rab_targets(q, k, v, dtype, off, 0, ts, wpos, npos, wtime, ntime,
                                         num_seqs, heads, d, alpha, n, tok, hd, count, out_rows);
+}
+
+/* One candidate row of the cached-history form (hstu_oracle_fwd_cached) with
+ * the relative attention bias: the candidate sits right after its request's
+ * history of hlen cached keys, so, as under the target-aware mask, its bias
+ * to history key c is wpos[hlen - c] plus the time term of ts_cand - ts_hist[c],
+ * and to its own key wpos[0] plus the time term of a zero gap.
+ *   out[row] = (1/n) (sum_{c < hlen} silu(alpha <q, kc_c> + rab(c)) vc_c
+ *                     + silu(alpha <q, k_row> + rab(self)) v_row)
+ * ts_c: the candidate's timestamp; hts: the history's timestamps. */
+static void rab_cached_row(const void* q, const void* k, const void* v, const void* kc,
+                           const void* vc, int dtype, int64_t row, int64_t hs0, int64_t hlen,
+                           int32_t ts_c, const int32_t* hts, const double* wpos, int npos,
+                           const double* wtime, int ntime, int heads, int d, int h,
+                           double alpha, double n, double* qrow, double* acc) {
+    const int64_t row_stride = (int64_t)heads * d;
+    const int64_t hoff = (int64_t)h * d;
+    for (int e = 0; e < d; ++e) {
+        qrow[e] = load_elem(q, dtype, row * row_stride + hoff + e);
+        acc[e] = 0.0;
+    }
+    for (int64_t c = 0; c < hlen; ++c) {
+        double dot = 0.0;
+        for (int e = 0; e < d; ++e)
+            dot += qrow[e] * load_elem(kc, dtype, (hs0 + c) * row_stride + hoff + e);
+        int64_t dist = hlen - c;
+#if ORACLE_PLANT == 26
+        dist = hlen + (row & 3) - c; /* planted: candidates spread over positions */
+#endif
+        int64_t gap = (int64_t)ts_c - (int64_t)hts[hs0 + c];
+#if ORACLE_PLANT == 27
+        gap = -gap; /* planted: time gap taken the other way */
+#endif
+        const double bias = (dist < npos ? wpos[dist] : 0.0) + wtime[time_bucket(gap, ntime)];
+        const double w = silu(alpha * dot + bias);
+        for (int e = 0; e < d; ++e)
+            acc[e] += w * load_elem(vc, dtype, (hs0 + c) * row_stride + hoff + e);
+    }
+    double dot = 0.0;
+    for (int e = 0; e < d; ++e) dot += qrow[e] * load_elem(k, dtype, row * row_stride + hoff + e);
+    const double w = silu(alpha * dot + wpos[0] + wtime[time_bucket(0, ntime)]);
+    for (int e = 0; e < d; ++e) acc[e] += w * load_elem(v, dtype, row * row_stride + hoff + e);
+    for (int e = 0; e < d; ++e) acc[e] /= n;
+}
+
+/* The cached-history form with the relative attention bias: as
+ * hstu_oracle_fwd_cached, plus ts (int32 per candidate token, the jagged
+ * layout of q), hts (int32 per cached history token, the layout of kc) and
+ * the bias tables wpos[npos], wtime[ntime].  out is fp64 (T, heads, d).
+ * Returns 0, or -1 on malformed offsets or sizes. */
+int hstu_oracle_fwd_rab_cached(const void* q, const void* k, const void* v, const void* kc,
+                               const void* vc, int dtype, const int32_t* coff,
+                               const int32_t* hoff, const int32_t* ts, const int32_t* hts,
+                               const double* wpos, int npos, const double* wtime, int ntime,
+                               int num_seqs, int heads, int d, double alpha, double n,
+                               double* out) {
+    if (num_seqs < 0 || heads < 1 || d < 1 || d > 1024) return -1;
+    if (npos < 1 || ntime < 1 || ntime > 32) return -1;
+    if (!offsets_ok(coff, num_seqs) || !offsets_ok(hoff, num_seqs)) return -1;
+    const int64_t row_stride = (int64_t)heads * d;
+    const int64_t items = (int64_t)num_seqs * heads;
+#pragma omp parallel
+    {
+        double qrow[1024], acc[1024];
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t it = 0; it < items; ++it) {
+            const int i = (int)(it / heads), h = (int)(it % heads);
+            for (int64_t row = coff[i]; row < coff[i + 1]; ++row) {
+                rab_cached_row(q, k, v, kc, vc, dtype, row, hoff[i],
+                               (int64_t)hoff[i + 1] - hoff[i], ts[row], hts, wpos, npos, wtime,
+                               ntime, heads, d, h, alpha, n, qrow, acc);
+                double* o = out + row * row_stride + (int64_t)h * d;
+                for (int e = 0; e < d; ++e) o[e] = acc[e];
+            }
+        }
+    }
+    return 0;
+}
+
+/* Sampled rows of the same: out_rows[m, 0..d) is candidate row tok[m], head
+ * hd[m].  Returns 0, or -1 on bad arguments. */
+int hstu_oracle_rows_rab_cached(const void* q, const void* k, const void* v, const void* kc,
+                                const void* vc, int dtype, const int32_t* coff,
+                                const int32_t* hoff, const int32_t* ts, const int32_t* hts,
+                                const double* wpos, int npos, const double* wtime, int ntime,
+                                int num_seqs, int heads, int d, double alpha, double n,
+                                const int64_t* tok, const int32_t* hd, int64_t count,
+                                double* out_rows) {
+    if (num_seqs < 1 || heads < 1 || d < 1 || d > 1024) return -1;
+    if (npos < 1 || ntime < 1 || ntime > 32) return -1;
+    if (!offsets_ok(coff, num_seqs) || !offsets_ok(hoff, num_seqs)) return -1;
+    const int64_t T = coff[num_seqs];
+    for (int64_t m = 0; m < count; ++m)
+        if (tok[m] < 0 || tok[m] >= T || hd[m] < 0 || hd[m] >= heads) return -1;
+#pragma omp parallel
+    {
+        double qrow[1024];
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t m = 0; m < count; ++m) {
+            int lo = 0, hi = num_seqs - 1;   /* largest i with coff[i] <= tok */
+            while (lo < hi) {
+                int mid = (lo + hi + 1) / 2;
+                if (coff[mid] <= tok[m]) lo = mid; else hi = mid - 1;
+            }
+            rab_cached_row(q, k, v, kc, vc, dtype, tok[m], hoff[lo],
+                           (int64_t)hoff[lo + 1] - hoff[lo], ts[tok[m]], hts, wpos, npos, wtime,
+                           ntime, heads, d, hd[m], alpha, n, qrow, out_rows + m * (int64_t)d);
+        }
+    }
+    return 0;
 }
 
 /* Gradient terms of one kept pair (r, c) of a sequence with the relative

@@ -346,6 +346,27 @@ def make_rab_inputs(offsets, npos: int, ntime: int, seed: int, sigma: float = 0.
     return RabInputs(timestamps=ts.astype(np.int32), pos_bias=wpos, time_bias=wtime)
 
 
+def make_cached_rab_inputs(hist_offsets, cand_offsets, npos: int, ntime: int, seed: int,
+                           sigma: float = 0.5, max_log_gap: int = 16):
+    """Timestamps for the cached-history form: per request, one timeline as in
+    make_rab_inputs over its history followed by its candidates, split into the
+    history's (hist_ts, the layout of the cache) and the candidates'
+    (cand_ts, the layout of q).  Returns (RabInputs with the candidates'
+    timestamps, hist_ts)."""
+    hoff = np.asarray(hist_offsets, dtype=np.int64)
+    coff = np.asarray(cand_offsets, dtype=np.int64)
+    hl, cl = np.diff(hoff), np.diff(coff)
+    joint = offsets_from_lengths((hl + cl).tolist())
+    r = make_rab_inputs(joint, npos, ntime, seed, sigma=sigma, max_log_gap=max_log_gap)
+    hts = np.zeros(int(hoff[-1]) if len(hoff) else 0, dtype=np.int32)
+    cts = np.zeros(int(coff[-1]) if len(coff) else 0, dtype=np.int32)
+    for i in range(len(hl)):
+        j0 = int(joint[i])
+        hts[hoff[i]:hoff[i + 1]] = r.timestamps[j0:j0 + hl[i]]
+        cts[coff[i]:coff[i + 1]] = r.timestamps[j0 + hl[i]:j0 + hl[i] + cl[i]]
+    return RabInputs(timestamps=cts, pos_bias=r.pos_bias, time_bias=r.time_bias), hts
+
+
 def rab_workload(values: bool = True):
     """The causal workload of 16 sequences of 4096 tokens (heads 4, d 64,
     bf16) with a relative attention bias: a position entry per distance and
