@@ -52,6 +52,8 @@ METRIC_CACHED = "HSTU cached-history attn fwd useful TFLOP/s (M-FALCON micro-bat
 METRIC_RAB = "HSTU attn fwd with relative attention bias useful TFLOP/s"
 METRIC_RAB_TARGETS = ("HSTU target-aware attn fwd with relative attention bias useful TFLOP/s "
                       "(M-FALCON mask and bias)")
+METRIC_RAB_CACHED = ("HSTU cached-history attn fwd with relative attention bias useful TFLOP/s "
+                     "(M-FALCON micro-batch)")
 METRIC_RAB_BWD = "HSTU attn bwd with relative attention bias (dq, dk, dv, table gradients) useful TFLOP/s"
 # HBM traffic per dispatch of the attention kernel, from two rocprofv3 --pmc
 # runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
@@ -113,9 +115,10 @@ def seen_pairs(case) -> float:
     return float(np.sum(h * (h + 1.0) / 2.0 + t * (h + 1.0)))
 
 
-def cpu_baseline_cached(cc, budget_s: float):
-    """The oracle's cached-history form on whole requests, in input order,
-    until about budget_s of wall time has been spent."""
+def cpu_baseline_cached(cc, budget_s: float, rab=None, hist_ts=None):
+    """The oracle's cached-history form (with the relative attention bias when
+    rab is given) on whole requests, in input order, until about budget_s of
+    wall time has been spent."""
     import oracle
     lib = oracle.load()
     threads = oracle.threads(lib)
@@ -127,10 +130,17 @@ def cpu_baseline_cached(cc, budget_s: float):
         a, b = int(c.offsets[i]), int(c.offsets[j])
         ha, hb = int(cc.hist_offsets[i]), int(cc.hist_offsets[j])
         t0 = time.perf_counter()
-        oracle.fwd_cached(c.q[a:b], c.k[a:b], c.v[a:b], c.offsets[i:j + 1] - c.offsets[i],
-                          cc.k_cache[ha:hb], cc.v_cache[ha:hb],
-                          cc.hist_offsets[i:j + 1] - cc.hist_offsets[i], c.heads, c.d, c.alpha,
-                          c.n, c.dtype, lib=lib)
+        if rab is None:
+            oracle.fwd_cached(c.q[a:b], c.k[a:b], c.v[a:b], c.offsets[i:j + 1] - c.offsets[i],
+                              cc.k_cache[ha:hb], cc.v_cache[ha:hb],
+                              cc.hist_offsets[i:j + 1] - cc.hist_offsets[i], c.heads, c.d,
+                              c.alpha, c.n, c.dtype, lib=lib)
+        else:
+            oracle.fwd_rab_cached(c.q[a:b], c.k[a:b], c.v[a:b], c.offsets[i:j + 1] - c.offsets[i],
+                                  cc.k_cache[ha:hb], cc.v_cache[ha:hb],
+                                  cc.hist_offsets[i:j + 1] - cc.hist_offsets[i],
+                                  rab.timestamps[a:b], hist_ts[ha:hb], rab.pos_bias,
+                                  rab.time_bias, c.heads, c.d, c.alpha, c.n, c.dtype, lib=lib)
         done_s += time.perf_counter() - t0
         t = c.lengths[i:j].astype(np.float64)
         h = cc.hist_lengths[i:j].astype(np.float64)
@@ -351,9 +361,10 @@ def main() -> int:
                          "scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     modes = args.targets + args.cached + args.backward + args.dense + args.layer + args.rab
-    if modes > 1 and (args.cached or args.dense or args.layer):
-        ap.error("--cached, --dense and --layer are separate benchmarks; --targets, --backward "
-                 "and --rab combine")
+    if modes > 1 and (args.dense or args.layer or
+                      (args.cached and modes - args.rab > 1)):
+        ap.error("--dense and --layer are separate benchmarks; --cached combines with --rab "
+                 "only; --targets, --backward and --rab combine")
     if args.graph and args.layer:
         ap.error("--graph records the attention calls; --layer has no graph form here")
     if args.layer:
@@ -377,8 +388,11 @@ def main() -> int:
         print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
                           "copies": 3}), flush=True)
         return 0
-    cc = rab = None
-    if args.cached:
+    cc = rab = hist_ts = None
+    if args.cached and args.rab:
+        cc, rab, hist_ts = workloads.rab_cached_workload()
+        case = cc.cand
+    elif args.cached:
         cc = workloads.cached_workload()
         case = cc.cand
     elif args.rab and args.targets:
@@ -403,9 +417,21 @@ def main() -> int:
         flops = float(np.sum(4.0 * case.heads * case.d * t * (cc.hist_lengths + 1.0)))
         elt = 4 if case.dtype == "fp32" else 2
         alg_bytes += 2.0 * elt * cc.k_cache.size + 4 * (case.num_seqs + 1)
+        if args.rab:
+            ts = torch.from_numpy(rab.timestamps).cuda()
+            hts = torch.from_numpy(hist_ts).cuda()
+            wp = torch.from_numpy(rab.pos_bias).cuda()
+            wt = torch.from_numpy(rab.time_bias).cuda()
+            alg_bytes += 4.0 * (case.total + hist_ts.size) + 4.0 * (rab.pos_bias.size +
+                                                                     rab.time_bias.size)
 
-        def call():
-            hstu.hstu_attn_fwd_cached(q, k, v, off, kc, vc, hoff, case.alpha, case.n, out=out)
+            def call():
+                hstu.hstu_attn_fwd_rab_cached(q, k, v, off, kc, vc, hoff, ts, hts, wp, wt,
+                                              case.alpha, case.n, out=out)
+        else:
+            def call():
+                hstu.hstu_attn_fwd_cached(q, k, v, off, kc, vc, hoff, case.alpha, case.n,
+                                          out=out)
     elif args.rab and not args.backward:
         ts = torch.from_numpy(rab.timestamps).cuda()
         wp = torch.from_numpy(rab.pos_bias).cuda()
@@ -553,7 +579,7 @@ def main() -> int:
     cpu = None
     if args.cpu_budget > 0:
         if args.cached:
-            cpu = cpu_baseline_cached(cc, args.cpu_budget)
+            cpu = cpu_baseline_cached(cc, args.cpu_budget, rab=rab, hist_ts=hist_ts)
         elif args.backward:
             cpu = cpu_baseline_bwd(case, dout_host, args.cpu_budget, rab=rab)
         else:
@@ -563,6 +589,7 @@ def main() -> int:
     line = {
         "metric": ((METRIC_RAB_BWD if args.rab else METRIC_BWD) +
                    (" (target-aware mask)" if args.targets else "") if args.backward else
+                   METRIC_RAB_CACHED if args.cached and args.rab else
                    METRIC_CACHED if args.cached else
                    METRIC_RAB_TARGETS if args.targets and args.rab else
                    METRIC_TARGETS if args.targets else

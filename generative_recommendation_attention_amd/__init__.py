@@ -52,7 +52,7 @@ EXPORTS = ("hstu_attn_fwd", "hstu_attn_fwd_bf16", "hstu_attn_fwd_fp16", "hstu_at
            "hstu_attn_bwd_dense", "hstu_layer_in_proj", "hstu_layer_out_proj",
            "hstu_attn_bwd_targets", "hstu_validate_offsets", "hstu_status_string", "hstu_last_hip_error",
            "hstu_release_workspace", "hstu_profile_enable", "hstu_profile_read",
-           "hstu_attn_fwd_noalloc", "hstu_attn_bwd_rab_targets")
+           "hstu_attn_fwd_noalloc", "hstu_attn_bwd_rab_targets", "hstu_attn_fwd_rab_cached")
 
 
 class HstuError(RuntimeError):
@@ -110,6 +110,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hstu_attn_fwd_rab_targets.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32,
                                               i32, f32, f32, vp, vp, ctypes.c_int]
     lib.hstu_attn_fwd_rab_targets.restype = ctypes.c_int
+    lib.hstu_attn_fwd_rab_cached.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32,
+                                             i32, i32, i32, f32, f32, vp, vp, ctypes.c_int]
+    lib.hstu_attn_fwd_rab_cached.restype = ctypes.c_int
     lib.hstu_attn_bwd_rab.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, f32,
                                       f32, vp, vp, vp, vp, vp, vp, ctypes.c_int]
     lib.hstu_attn_bwd_rab.restype = ctypes.c_int
@@ -304,15 +307,8 @@ def hstu_attn_fwd_targets(q, k, v, seq_offsets, num_targets, alpha: float, n: fl
     return out
 
 
-def hstu_attn_fwd_cached(q, k, v, cand_offsets, k_cache, v_cache, hist_offsets, alpha: float,
-                         n: float, out=None, stream=None):
-    """Candidates (q, k, v: (T_cand, heads, d), offsets cand_offsets) scored
-    against a cached history (k_cache, v_cache: (T_hist, heads, d), offsets
-    hist_offsets): each candidate sees its request's history and itself."""
+def _check_cache(q, k_cache, v_cache, hist_offsets, num_seqs):
     import torch
-    out = _check_tensors(q, k, v, cand_offsets, out)
-    num_seqs = cand_offsets.numel() - 1
-    T, heads, d = q.shape
     for t in (k_cache, v_cache):
         if (t.dim() != 3 or t.shape[1:] != q.shape[1:] or t.dtype != q.dtype or not t.is_cuda
                 or not t.is_contiguous()):
@@ -325,6 +321,17 @@ def hstu_attn_fwd_cached(q, k, v, cand_offsets, k_cache, v_cache, hist_offsets, 
             not hist_offsets.is_contiguous()):
         raise ValueError("hist_offsets must be a contiguous 1-D int32 GPU tensor of "
                          "num_seqs + 1 entries")
+
+
+def hstu_attn_fwd_cached(q, k, v, cand_offsets, k_cache, v_cache, hist_offsets, alpha: float,
+                         n: float, out=None, stream=None):
+    """Candidates (q, k, v: (T_cand, heads, d), offsets cand_offsets) scored
+    against a cached history (k_cache, v_cache: (T_hist, heads, d), offsets
+    hist_offsets): each candidate sees its request's history and itself."""
+    out = _check_tensors(q, k, v, cand_offsets, out)
+    num_seqs = cand_offsets.numel() - 1
+    T, heads, d = q.shape
+    _check_cache(q, k_cache, v_cache, hist_offsets, num_seqs)
     lib = load_library()
     if T == 0:
         return out   # no candidate rows: nothing to compute
@@ -337,6 +344,41 @@ def hstu_attn_fwd_cached(q, k, v, cand_offsets, k_cache, v_cache, hist_offsets, 
                                   d, float(alpha), float(n), out.data_ptr(),
                                   _stream_handle(stream), _dtype_code(q))
     _check(st, "hstu_attn_fwd_cached")
+    return out
+
+
+def hstu_attn_fwd_rab_cached(q, k, v, cand_offsets, k_cache, v_cache, hist_offsets, timestamps,
+                             hist_timestamps, pos_bias, time_bias, alpha: float, n: float,
+                             out=None, stream=None):
+    """hstu_attn_fwd_cached with the relative attention bias: a candidate sits
+    right after its request's cached history (distance h - c to history row c,
+    0 to itself) and keeps its own timestamp.  timestamps: int32 GPU tensor of
+    T_cand entries; hist_timestamps: int32 GPU tensor of T_hist entries (the
+    layout of k_cache); pos_bias, time_bias as in hstu_attn_fwd_rab."""
+    import torch
+    out = _check_tensors(q, k, v, cand_offsets, out)
+    num_seqs = cand_offsets.numel() - 1
+    T, heads, d = q.shape
+    _check_cache(q, k_cache, v_cache, hist_offsets, num_seqs)
+    _check_rab(T, timestamps, pos_bias, time_bias)
+    if (hist_timestamps.dtype != torch.int32 or hist_timestamps.shape != (k_cache.shape[0],) or
+            not hist_timestamps.is_cuda or not hist_timestamps.is_contiguous()):
+        raise ValueError("hist_timestamps must be a contiguous int32 GPU tensor of T_hist entries")
+    lib = load_library()
+    if T == 0:
+        return out
+    empty_cache = k_cache.numel() == 0
+    st = lib.hstu_attn_fwd_rab_cached(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                      cand_offsets.data_ptr(),
+                                      None if empty_cache else k_cache.data_ptr(),
+                                      None if empty_cache else v_cache.data_ptr(),
+                                      hist_offsets.data_ptr(), timestamps.data_ptr(),
+                                      None if empty_cache else hist_timestamps.data_ptr(),
+                                      pos_bias.data_ptr(), pos_bias.numel(), time_bias.data_ptr(),
+                                      time_bias.numel(), num_seqs, heads, d, float(alpha),
+                                      float(n), out.data_ptr(), _stream_handle(stream),
+                                      _dtype_code(q))
+    _check(st, "hstu_attn_fwd_rab_cached")
     return out
 
 

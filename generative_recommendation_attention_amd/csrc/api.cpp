@@ -334,8 +334,9 @@ struct MaskInputs {
     // Dense (B, heads, S, D) layout: num_seqs = B, dense_len = S, no offsets.
     bool dense = false;
     int64_t dense_len = 0;
-    // Relative attention bias (causal mask).
+    // Relative attention bias.
     const int32_t* timestamps = nullptr;
+    const int32_t* hist_timestamps = nullptr;   // with a cached history
     const float* pos_bias = nullptr;
     const float* time_bias = nullptr;
     int num_pos = 0;
@@ -414,6 +415,7 @@ hstu_status_t attn_fwd_call(const void* q, const void* k, const void* v,
     p.dense = mi.dense;
     p.dense_len = mi.dense_len;
     p.timestamps = mi.timestamps;
+    p.hist_timestamps = mi.hist_timestamps;
     p.pos_bias = mi.pos_bias;
     p.time_bias = mi.time_bias;
     p.num_pos = mi.num_pos;
@@ -849,11 +851,10 @@ hstu_status_t hstu_attn_bwd_dense(const void* q, const void* k, const void* v, c
                          stream, dtype, seq_len);
 }
 
-hstu_status_t hstu_attn_fwd_cached(const void* q, const void* k, const void* v,
-                                   const int32_t* cand_offsets, const void* k_cache,
-                                   const void* v_cache, const int32_t* hist_offsets,
-                                   int32_t num_seqs, int32_t heads, int32_t d, float alpha,
-                                   float n, void* out, hipStream_t stream, hstu_dtype_t dtype) {
+// The cache inputs of a cached-history call, checked (num_seqs > 0).
+static hstu_status_t cache_inputs(const void* k_cache, const void* v_cache,
+                                  const int32_t* hist_offsets, const void* out, int32_t num_seqs,
+                                  MaskInputs* mi) {
     if (num_seqs > 0) {
         // Both caches null: no request has a history (T_hist = 0).
         if (!hist_offsets || (!k_cache) != (!v_cache)) return HSTU_ERR_INVALID_ARG;
@@ -861,10 +862,43 @@ hstu_status_t hstu_attn_fwd_cached(const void* q, const void* k, const void* v,
         if ((reinterpret_cast<uintptr_t>(hist_offsets) & 3u) != 0) return HSTU_ERR_INVALID_ARG;
         if (out == k_cache || out == v_cache) return HSTU_ERR_INVALID_ARG;
     }
+    mi->k_cache = k_cache;
+    mi->v_cache = v_cache;
+    mi->hist_offsets = hist_offsets;
+    return HSTU_OK;
+}
+
+hstu_status_t hstu_attn_fwd_cached(const void* q, const void* k, const void* v,
+                                   const int32_t* cand_offsets, const void* k_cache,
+                                   const void* v_cache, const int32_t* hist_offsets,
+                                   int32_t num_seqs, int32_t heads, int32_t d, float alpha,
+                                   float n, void* out, hipStream_t stream, hstu_dtype_t dtype) {
     MaskInputs mi;
-    mi.k_cache = k_cache;
-    mi.v_cache = v_cache;
-    mi.hist_offsets = hist_offsets;
+    const hstu_status_t st = cache_inputs(k_cache, v_cache, hist_offsets, out, num_seqs, &mi);
+    if (st != HSTU_OK) return st;
+    return attn_fwd_call(q, k, v, cand_offsets, mi, num_seqs, heads, d, alpha, n, out, stream,
+                         dtype);
+}
+
+hstu_status_t hstu_attn_fwd_rab_cached(const void* q, const void* k, const void* v,
+                                       const int32_t* cand_offsets, const void* k_cache,
+                                       const void* v_cache, const int32_t* hist_offsets,
+                                       const int32_t* timestamps,
+                                       const int32_t* hist_timestamps, const float* pos_bias,
+                                       int32_t num_pos, const float* time_bias,
+                                       int32_t num_time, int32_t num_seqs, int32_t heads,
+                                       int32_t d, float alpha, float n, void* out,
+                                       hipStream_t stream, hstu_dtype_t dtype) {
+    MaskInputs mi;
+    hstu_status_t st = cache_inputs(k_cache, v_cache, hist_offsets, out, num_seqs, &mi);
+    if (st != HSTU_OK) return st;
+    st = rab_inputs(timestamps, pos_bias, num_pos, time_bias, num_time, num_seqs, alpha, &mi);
+    if (st != HSTU_OK) return st;
+    // (a history needs its timestamps; with no cache there is no history)
+    if (num_seqs > 0 && k_cache &&
+        (!hist_timestamps || (reinterpret_cast<uintptr_t>(hist_timestamps) & 3u) != 0))
+        return HSTU_ERR_INVALID_ARG;
+    mi.hist_timestamps = k_cache ? hist_timestamps : nullptr;
     return attn_fwd_call(q, k, v, cand_offsets, mi, num_seqs, heads, d, alpha, n, out, stream,
                          dtype);
 }

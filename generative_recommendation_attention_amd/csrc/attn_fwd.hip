@@ -75,7 +75,8 @@ struct KernelArgs {
 // The relative-attention-bias kernel's arguments (a separate type, so that
 // the other modes' kernels keep their argument block).
 struct KernelArgsRab : KernelArgs {
-    const int32_t* ts;     // token timestamps
+    const int32_t* ts;     // token timestamps (the candidates' with a cached history)
+    const int32_t* hts;    // the cached history's timestamps (MASK_RAB_CACHED), or null
     const float* wpos;     // relative attention bias tables
     const float* wtime;
     int npos;              // entries of wpos (distances 0 .. npos-1)
@@ -100,7 +101,19 @@ struct KernelArgsRab : KernelArgs {
 //           adjusts the bias with the mask: a candidate row takes position
 //           hist, so its distance to history key c is hist - c and to itself
 //           0, while its time gaps use its own timestamp.
-enum : int { MASK_CAUSAL = 0, MASK_TARGETS = 1, MASK_CACHED = 2, MASK_RAB = 3, MASK_RAB_TGT = 4 };
+//  RAB_CACHED: CACHED with the bias of RAB_TGT: a candidate takes position
+//           hlen, the real (unpadded) history length, so its distance to
+//           cached key c is hlen - c and to itself 0; the keys' timestamps
+//           come from the history's timestamps below the virtual history
+//           and from the candidates' above it.
+enum : int {
+    MASK_CAUSAL = 0,
+    MASK_TARGETS = 1,
+    MASK_CACHED = 2,
+    MASK_RAB = 3,
+    MASK_RAB_TGT = 4,
+    MASK_RAB_CACHED = 5
+};
 
 // Relative attention bias (HSTU paper translation, §3 and Appendix G: a bias
 // merging relative position and time, built inside the operator from its
@@ -200,11 +213,14 @@ struct Tile16 {
 template <int MASK> struct ArgsOf { using type = KernelArgs; };
 template <> struct ArgsOf<MASK_RAB> { using type = KernelArgsRab; };
 template <> struct ArgsOf<MASK_RAB_TGT> { using type = KernelArgsRab; };
+template <> struct ArgsOf<MASK_RAB_CACHED> { using type = KernelArgsRab; };
 
 template <typename T, int D, int NW, int QB, int BK, int PF, bool FUSED, int MASK>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MASK>::type a) {
-    constexpr bool TGT = MASK == MASK_TARGETS || MASK == MASK_CACHED || MASK == MASK_RAB_TGT;
-    constexpr bool RAB = MASK == MASK_RAB || MASK == MASK_RAB_TGT;   // (TGT: hist-based mask)
+    constexpr bool CACHED = MASK == MASK_CACHED || MASK == MASK_RAB_CACHED;
+    constexpr bool TGT = MASK == MASK_TARGETS || MASK == MASK_RAB_TGT || CACHED;
+    // (TGT: hist-based mask)
+    constexpr bool RAB = MASK == MASK_RAB || MASK == MASK_RAB_TGT || MASK == MASK_RAB_CACHED;
     // Last-bucket blocks (below) at d = 64 only: at d = 128 the extra path
     // costs the bias kernel some 30-80 more spilled registers.
     constexpr bool FAR = RAB && D == 64;
@@ -224,7 +240,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
     constexpr int RAB_BYTES = RAB ? Cfg::NSLOT * NW * Cfg::RAB_WORDS * 4 : 0;
     static_assert(!RAB || (PF == 2 && Cfg::RAB_WIN % 64 == 0 && BK <= 64),
                   "bias staging: one tile ahead, whole-wave window loads");
-    static_assert(MASK != MASK_RAB_TGT || QB == 1, "candidate rows: one lane base per item");
+    static_assert(!(RAB && TGT) || QB == 1, "candidate rows: one lane base per item");
     static_assert(Cfg::LDS_BYTES + RAB_BYTES <= 65536, "LDS reads use 16-bit immediate offsets");
     __shared__ __attribute__((aligned(1024))) unsigned char lds[Cfg::LDS_BYTES + RAB_BYTES];
     __shared__ int s_item[NQ];
@@ -317,7 +333,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
         int s = len, hist = len, shift = 0, hstart = 0, hlen = 0;
         if constexpr (MASK == MASK_TARGETS || MASK == MASK_RAB_TGT)
             hist = len - min(max(__builtin_amdgcn_readfirstlane(a.ntgt[seq]), 0), len);
-        if constexpr (MASK == MASK_CACHED) {
+        if constexpr (CACHED) {
             hstart = __builtin_amdgcn_readfirstlane(a.hoff[seq]);
             // (no cache: every history is empty, whatever the offsets say)
             hlen = a.kc ? max(__builtin_amdgcn_readfirstlane(a.hoff[seq + 1]) - hstart, 0) : 0;
@@ -360,7 +376,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
             const uint16_t* kp;
             const uint16_t* vp;
             int bytes;
-            if (MASK == MASK_CACHED && kt < nh) {
+            if (CACHED && kt < nh) {
                 const int64_t off = ((int64_t)hstart + k0) * row_stride + (int64_t)head * D;
                 kp = a.kc + off;
                 vp = a.vc + off;
@@ -397,8 +413,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
         // The bias sees a candidate row (row >= hist) at position hist, so
         // the window follows the effective rows min(row, hist): the wave's
         // first one, and the lane's lead over it (row - wr0 when causal).
-        const int wr_eff0 = TGT ? min(wr0, hist) : wr0;
-        const int rab_wb_it = TGT ? rab_wb + 4 * (min(wr0 + l32, hist) - wr_eff0 - l32) : rab_wb;
+        // With a cached history every row is a candidate at position hlen
+        // (the virtual history is padded to whole tiles; hlen is its real
+        // length).
+        const int wr_eff0 = CACHED ? hlen : TGT ? min(wr0, hist) : wr0;
+        const int rab_wb_it = CACHED ? rab_wb - 4 * l32
+                              : TGT  ? rab_wb + 4 * (min(wr0 + l32, hist) - wr_eff0 - l32)
+                                     : rab_wb;
         // Blocks whose every pair lies in the last time bucket (the keys'
         // latest timestamp at least 2^(ntime-1) - 1 before the wave's
         // earliest row: typical far from the diagonal once the table is
@@ -410,8 +431,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
         auto issue_rab = [&](int c) {
             if constexpr (RAB) {
                 const int k0 = (TGT && c >= nh ? c + jump : c) * BK;
-                rab_ts = __builtin_amdgcn_raw_buffer_load_b32(
-                        make_rsrc32(a.ts + start + k0, min(kv_end - k0, BK) * 4), lane * 4, 0, 0);
+                // (with a cached history: the history's timestamps below the
+                // virtual history, padding rows reading 0, then the candidates')
+                const __amdgpu_buffer_rsrc_t rts =
+                        !CACHED ? make_rsrc32(a.ts + start + k0, min(kv_end - k0, BK) * 4)
+                        : k0 < hist
+                                ? make_rsrc32(a.hts + hstart + k0, min(hlen - k0, BK) * 4)
+                                : make_rsrc32(a.ts + start + (k0 - shift), min(kv_end - k0, BK) * 4);
+                rab_ts = __builtin_amdgcn_raw_buffer_load_b32(rts, lane * 4, 0, 0);
                 const __amdgpu_buffer_rsrc_t rp = make_rsrc32(a.wpos, a.npos * 4);
                 // Negative distances belong to masked pairs only (they read
                 // as zero), except under the target-aware mask, where a
@@ -456,7 +483,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
         };
         if constexpr (RAB) {
             const __amdgpu_buffer_rsrc_t rt =
-                    make_rsrc(a.ts + start + wr0, (int64_t)(s - wr0) * 4);
+                    make_rsrc(a.ts + start + (wr0 - shift), (int64_t)(s - wr0) * 4);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
                 trp1[qb] = __builtin_amdgcn_raw_buffer_load_b32(rt, (qb * 32 + l32) * 4, 0, 0) + 1u;
@@ -847,6 +874,7 @@ struct KernelArgsF32 {
     const float* vc;
     const int32_t* hoff;   // history offsets: the cached-history form when non-null
     const int32_t* ts;     // token timestamps: the relative attention bias when non-null
+    const int32_t* hts;    // the cached history's timestamps (bias with a cached history)
     const float* wpos;
     const float* wtime;
     int npos;
@@ -915,8 +943,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma_f32(KernelArgsF32 a)
         const bool wave_live = wr0 < s;
         const int my_row = wr0 + l32;
         const int64_t seq_base = (int64_t)start * H * D + (int64_t)it.head * a.head_stride;
-        // relative attention bias: this row's timestamp + 1
-        const uint32_t trp1 = (a.ts && my_row < s) ? (uint32_t)a.ts[start + my_row] + 1u : 0u;
+        // relative attention bias: this row's timestamp + 1, and the position
+        // its distances are taken from (a candidate sits right after the
+        // history: hlen with a cached history, hist under the target-aware mask)
+        const uint32_t trp1 =
+                (a.ts && my_row < s) ? (uint32_t)a.ts[start + my_row - shift] + 1u : 0u;
+        const int pos_row = a.hoff ? hlen : min(my_row, hist);
 
         float qf[D / 2];
         {
@@ -1011,9 +1043,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma_f32(KernelArgsF32 a)
                                 const int key = k0 + kvl;
                                 // (a candidate row sits at position hist; its own
                                 // key at distance 0)
-                                const int dist = key == my_row ? 0 : min(my_row, hist) - key;
+                                const int dist = key == my_row ? 0 : pos_row - key;
                                 float bias = (dist >= 0 && dist < a.npos) ? a.wpos[dist] : 0.0f;
-                                const uint32_t x = trp1 - (key < s ? (uint32_t)a.ts[start + key] : 0u);
+                                // key timestamp: the cached history's below hist
+                                // (its padding, masked by zero V, reads none)
+                                uint32_t tk = 0u;
+                                if (a.hoff && key < hist)
+                                    tk = key < hlen ? (uint32_t)a.hts[hstart + key] : 0u;
+                                else if (key < s)
+                                    tk = (uint32_t)a.ts[start + key - shift];
+                                const uint32_t x = trp1 - tk;
                                 const int lz = __clz((int)x);   // 32 for x == 0 (gap -1)
                                 bias += a.wtime[lz == 32 ? a.ntime - 1 : min(31 - lz, a.ntime - 1)];
                                 p = silu_scaled(__builtin_fmaf(st[r], a.score_scale, bias * -LOG2E));
@@ -1072,7 +1111,10 @@ template <int D> struct QBlocks { static constexpr int value = D == 64 ? 2 : 1; 
 // a second block would take.
 template <int D, int MASK> struct QBlocksFor {
     static constexpr int value =
-            MASK == MASK_CACHED || MASK == MASK_RAB || MASK == MASK_RAB_TGT ? 1 : QBlocks<D>::value;
+            MASK == MASK_CACHED || MASK == MASK_RAB || MASK == MASK_RAB_TGT ||
+                            MASK == MASK_RAB_CACHED
+                    ? 1
+                    : QBlocks<D>::value;
 };
 template <int D> struct KeyTile { static constexpr int value = D == 64 ? 64 : 32; };
 // Key tiles in flight: two at d = 64; three at d = 128, whose 32-key tiles
@@ -1112,6 +1154,7 @@ hipError_t launch16(const FwdParams& p, WorkList wl, int grid, hipStream_t strea
         KernelArgsRab ar;
         static_cast<KernelArgs&>(ar) = a;
         ar.ts = p.timestamps;
+        ar.hts = p.hist_timestamps;
         ar.wpos = p.pos_bias;
         ar.wtime = p.time_bias;
         ar.npos = p.num_pos;
@@ -1120,17 +1163,22 @@ hipError_t launch16(const FwdParams& p, WorkList wl, int grid, hipStream_t strea
         // the scaled Q: rab * (-log2(e)))
         ar.bias_scale = -LOG2E;
         constexpr int QBR = QBlocksFor<D, MASK_RAB>::value;
-        static_assert(QBlocksFor<D, MASK_RAB_TGT>::value == QBR, "one item shape for both");
+        static_assert(QBlocksFor<D, MASK_RAB_TGT>::value == QBR &&
+                              QBlocksFor<D, MASK_RAB_CACHED>::value == QBR &&
+                              QBlocksFor<D, MASK_CACHED>::value == QBR,
+                      "one item shape for the bias forms and the cached history");
         using FnR = void (*)(KernelArgsRab);
-        static constexpr FnR fnr[2][2] = {
+        static constexpr FnR fnr[2][3] = {
                 {attn_fwd_mfma16<T, D, NW16, QBR, BK, PF_RAB, false, MASK_RAB>,
-                 attn_fwd_mfma16<T, D, NW16, QBR, BK, PF_RAB, false, MASK_RAB_TGT>},
+                 attn_fwd_mfma16<T, D, NW16, QBR, BK, PF_RAB, false, MASK_RAB_TGT>,
+                 attn_fwd_mfma16<T, D, NW16, QBR, BK, PF_RAB, false, MASK_RAB_CACHED>},
                 {attn_fwd_mfma16<T, D, NW16, QBR, BK, PF_RAB, true, MASK_RAB>,
-                 attn_fwd_mfma16<T, D, NW16, QBR, BK, PF_RAB, true, MASK_RAB_TGT>}};
-        const int tg = p.num_targets ? 1 : 0;
+                 attn_fwd_mfma16<T, D, NW16, QBR, BK, PF_RAB, true, MASK_RAB_TGT>,
+                 attn_fwd_mfma16<T, D, NW16, QBR, BK, PF_RAB, true, MASK_RAB_CACHED>}};
+        const int tg = p.hist_offsets ? 2 : p.num_targets ? 1 : 0;
         const FnR fn = fnr[wl.fused ? 1 : 0][tg];
         if (grid <= 0) {
-            static int cached[2][2] = {};
+            static int cached[2][3] = {};
             int& c = cached[wl.fused ? 1 : 0][tg];
             if (!c) c = resident_grid(fn, NW16 * 64);
             grid = c;
@@ -1178,6 +1226,7 @@ hipError_t launch_f32(const FwdParams& p, WorkList wl, int grid, hipStream_t str
     a.vc = static_cast<const float*>(p.v_cache);
     a.hoff = p.hist_offsets;
     a.ts = p.timestamps;
+    a.hts = p.hist_timestamps;
     a.wpos = p.pos_bias;
     a.wtime = p.time_bias;
     a.npos = p.num_pos;

@@ -167,9 +167,11 @@ struct FwdParams {
     // Dense (B, heads, S, D) layout: offsets are then i * S, S = dense_len.
     bool dense = false;
     int64_t dense_len = 0;
-    // Relative attention bias (causal mask, jagged layout only): token
-    // timestamps (T), position table [num_pos], time table [num_time <= 32].
+    // Relative attention bias (jagged layout only): token timestamps (T),
+    // position table [num_pos], time table [num_time <= 32]; with a cached
+    // history also the history's timestamps (T_hist).
     const int32_t* timestamps = nullptr;
+    const int32_t* hist_timestamps = nullptr;
     const float* pos_bias = nullptr;
     const float* time_bias = nullptr;
     int num_pos = 0;

@@ -270,6 +270,45 @@ hstu_status_t hstu_attn_fwd_rab_targets(const void* q, const void* k, const void
                                         int32_t d, float alpha, float n, void* out,
                                         hipStream_t stream, hstu_dtype_t dtype);
 
+/* hstu_attn_fwd_cached with the relative attention bias (HSTU paper
+ * translation, §3.4: M-FALCON adjusts rab_{p,t} with the mask; Appendix H:
+ * the history's K and V come from a cache).  Read as in
+ * hstu_attn_fwd_rab_targets, with the history taken from the cache: a
+ * candidate sits at the position right after its request's h_i cached rows
+ * and keeps its own timestamp.  Candidate j of request i (global row
+ * cand_offsets[i] + j, history rows hist_offsets[i] + c) gets
+ *
+ *   out[j] = (1/n) * ( sum_{c < h_i} silu(alpha <q[j], k_cache[.. + c]> + rab_c(j, c))
+ *                                     * v_cache[.. + c]
+ *                      + silu(alpha <q[j], k[j]> + pos_bias[0] + time_bias[0]) * v[j] )
+ *   rab_c(j, c) = pos_bias[h_i - c] (0 past the table)
+ *               + time_bias[min(floor(log2(timestamps[j] - hist_timestamps[.. + c] + 1)),
+ *                               num_time - 1)]   (a negative gap: the last entry)
+ *
+ * so a candidate's output equals the last row of hstu_attn_fwd_rab over its
+ * history followed by that candidate alone.
+ *
+ *   q, k, v, out, cand_offsets, k_cache, v_cache, hist_offsets :
+ *                     as in hstu_attn_fwd_cached.
+ *   timestamps      : device int32[T_cand], the candidates' timestamps, 4-byte aligned.
+ *   hist_timestamps : device int32[T_hist], the cached rows' timestamps (the
+ *                     layout of k_cache), 4-byte aligned; ignored (may be
+ *                     NULL) when the caches are NULL.
+ *   pos_bias, num_pos, time_bias, num_time : as in hstu_attn_fwd_rab.
+ *
+ * Element types, streams, scratch and errors as in hstu_attn_fwd_cached and
+ * hstu_attn_fwd_rab; a null or misaligned hist_timestamps with non-null
+ * caches (num_seqs > 0) also gives HSTU_ERR_INVALID_ARG. */
+hstu_status_t hstu_attn_fwd_rab_cached(const void* q, const void* k, const void* v,
+                                       const int32_t* cand_offsets, const void* k_cache,
+                                       const void* v_cache, const int32_t* hist_offsets,
+                                       const int32_t* timestamps,
+                                       const int32_t* hist_timestamps, const float* pos_bias,
+                                       int32_t num_pos, const float* time_bias,
+                                       int32_t num_time, int32_t num_seqs, int32_t heads,
+                                       int32_t d, float alpha, float n, void* out,
+                                       hipStream_t stream, hstu_dtype_t dtype);
+
 /* Backward: gradients of hstu_attn_fwd (or, with num_targets, of
  * hstu_attn_fwd_targets) with respect to q, k and v, for the upstream
  * gradient dout = dLoss/dout.  The attention is recomputed block by block and

@@ -227,6 +227,41 @@ def test_cached_empty_batch_is_a_no_op(lib):
                         out=None, num_seqs=0) == hstu.HSTU_OK
 
 
+def _call_rab_cached(lib, kc=64, vc=80, hoff=96, ts=48, hts=112, wpos=128, npos=8, wtime=144,
+                     ntime=4, **kw):
+    a = dict(q=16, k=16, v=16, off=16, num_seqs=1, heads=1, d=64, alpha=0.1, n=1.0, out=32,
+             dtype=hstu.HSTU_BF16)
+    a.update(kw)
+    return lib.hstu_attn_fwd_rab_cached(a["q"], a["k"], a["v"], a["off"], kc, vc, hoff, ts, hts,
+                                        wpos, npos, wtime, ntime, a["num_seqs"], a["heads"],
+                                        a["d"], a["alpha"], a["n"], a["out"], None, a["dtype"])
+
+
+# (every case has one invalid argument: nothing reaches a device)
+@pytest.mark.parametrize("kw,status", [
+    (dict(hts=None), hstu.HSTU_ERR_INVALID_ARG),    # history timestamps missing
+    (dict(hts=114), hstu.HSTU_ERR_INVALID_ARG),     # misaligned history timestamps
+    (dict(kc=None, vc=None, hts=None, d=96), hstu.HSTU_ERR_UNSUPPORTED),  # no caches: allowed
+    (dict(ts=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(kc=None), hstu.HSTU_ERR_INVALID_ARG),     # one cache without the other
+    (dict(hoff=None), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(wtime=146), hstu.HSTU_ERR_INVALID_ARG),   # misaligned table
+    (dict(npos=0), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(ntime=33), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(alpha=0.0), hstu.HSTU_ERR_INVALID_ARG),
+    (dict(out=64), hstu.HSTU_ERR_INVALID_ARG),      # out aliases the cached K
+    (dict(d=96), hstu.HSTU_ERR_UNSUPPORTED),
+])
+def test_rab_cached_argument_checks(lib, kw, status):
+    assert _call_rab_cached(lib, **kw) == status
+
+
+def test_rab_cached_empty_batch_is_a_no_op(lib):
+    assert _call_rab_cached(lib, kc=None, vc=None, hoff=None, ts=None, hts=None, wpos=None,
+                            wtime=None, q=None, k=None, v=None, off=None, out=None,
+                            num_seqs=0) == hstu.HSTU_OK
+
+
 def _call_bwd(lib, dout=48, dq=64, dk=80, dv=96, tg=None, **kw):
     a = dict(q=16, k=16, v=16, off=16, num_seqs=1, heads=1, d=64, alpha=0.1, n=1.0,
              dtype=hstu.HSTU_BF16)

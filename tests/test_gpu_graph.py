@@ -115,13 +115,19 @@ def test_cached_and_dense_replay():
     coff = torch.from_numpy(cand.offsets).cuda()
     kc, vc = to_torch(cc.k_cache, "bf16"), to_torch(cc.v_cache, "bf16")
     hoff = torch.from_numpy(cc.hist_offsets).cuda()
+    r, hist_ts = workloads.make_cached_rab_inputs(cc.hist_offsets, cand.offsets, 150, 10,
+                                                  seed=3122)
+    ts, hts = torch.from_numpy(r.timestamps).cuda(), torch.from_numpy(hist_ts).cuda()
+    wp, wt = torch.from_numpy(r.pos_bias).cuda(), torch.from_numpy(r.time_bias).cuda()
     dc = workloads.make_case([256] * 3, 2, 64, "bf16", seed=3121)
     dq, dk, dv, _ = device_case(dc)
     qd, kd, vd = (x.reshape(3, 256, 2, 64).permute(0, 2, 1, 3).contiguous() for x in (dq, dk, dv))
     check_replays(lambda: [hstu.hstu_attn_fwd_cached(cq, ck, cv, coff, kc, vc, hoff, cand.alpha,
                                                      cand.n),
+                           hstu.hstu_attn_fwd_rab_cached(cq, ck, cv, coff, kc, vc, hoff, ts, hts,
+                                                         wp, wt, cand.alpha, cand.n),
                            hstu.hstu_attn_fwd_dense(qd, kd, vd, dc.alpha, dc.n)],
-                  name="cached history, dense")
+                  name="cached history, cached history with bias, dense")
 
 
 @pytest.mark.parametrize("size", ["small", "many"])

@@ -377,6 +377,17 @@ def rab_workload(values: bool = True):
     return case, make_rab_inputs(offsets, 4096, 16, seed=1301)
 
 
+def rab_cached_workload():
+    """The cached-history workload (16 x (3072 cached + 1024 candidates),
+    heads 4, d 64, bf16) with a relative attention bias: a position entry per
+    distance and 16 time buckets.  Seeds 1200 (K, V, q, k, v) and 1321 (bias).
+    Returns (CachedCase, RabInputs with the candidates' timestamps, the
+    history's timestamps)."""
+    cc = cached_workload()
+    r, hts = make_cached_rab_inputs(cc.hist_offsets, cc.cand.offsets, 4096, 16, seed=1321)
+    return cc, r, hts
+
+
 def rab_targets_workload(values: bool = True):
     """The target-aware workload (16 x (3072 history + 1024 candidates),
     heads 4, d 64, bf16) with a relative attention bias: a position entry per
