@@ -705,10 +705,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
         // Body of block b: the SiLU of S(b) on the vector ALUs while the matrix
         // cores run S(b+1) and P(b) V.  All operands of the body are read from
         // LDS first; the SiLU of the first 16 keys overlaps the products of the
-        // previous block's last 16 keys and the first half of S(b+1), the SiLU
-        // of the last 16 keys overlaps P V of the first 16 and the second half
-        // of S(b+1); the product of the last 16 keys waits for the next body (so
-        // no product has to wait for the SiLU right before it).  Tile c's
+        // previous block's last 16 keys and S(b+1), the SiLU of the last 16
+        // keys overlaps P V of the first 16; the product of the last 16 keys
+        // waits for the next body (so no product has to wait for the SiLU right
+        // before it), and S(b+1) is complete well before the next body's SiLU
+        // reads it.  Tile c's
         // barrier comes right before the body of its last block, the first body
         // that reads tile c+1 (its K).  Two score arrays alternate by block
         // parity, so nothing is copied.  The main loop
@@ -727,6 +728,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
         for (int db = 0; db < NDB; ++db) v1d[db] = (v8){};
         auto body = [&](int slot, int kb, int next_slot, int next_kb, bool sync, int c,
                         f32x16* cur, f32x16* nxt) {
+            // (the compiler's exp/MFMA interleaving strategy for this block:
+            // measured 0.5-1 % faster than its default schedule)
+            __builtin_amdgcn_iglp_opt(2);
             if (sync) tile_sync(c);
             v8 ka[NKS], va0[NDB], va1[NDB];
 #pragma unroll
@@ -746,15 +750,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
                 for (int qb = 0; qb < QB; ++qb) nxt[qb] = (f32x16){};
             }
 #pragma unroll
-            for (int ks = 0; ks < NKS / 2; ++ks)
+            for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) nxt[qb] = M::mma(ka[ks], qop[qb][ks], nxt[qb]);
             weights(cur, 1, p1);
             mma_pv(va0, p0);
-#pragma unroll
-            for (int ks = NKS / 2; ks < NKS; ++ks)
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) nxt[qb] = M::mma(ka[ks], qop[qb][ks], nxt[qb]);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) p1d[qb] = p1[qb];
 #pragma unroll
