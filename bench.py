@@ -66,12 +66,12 @@ TRAFFIC = {
     "sources": ("generative_recommendation_attention_amd/csrc/attn_fwd.hip",
                 "generative_recommendation_attention_amd/csrc/schedule.h",
                 "generative_recommendation_attention_amd/csrc/schedule.hip"),
-    "sha256": "c2629f378770ceb242c52f0148d0f9a5f6662f695d1ba0022281a2c56ffd25d2",
+    "sha256": "1d3e2a655df6fe361cf973e89f6337d8cfa1c8aa70c39da7d7595e092a978ab5",
     "fetch_scale": 2.0,
     "write_scale": 1.0,
     # mean over the launches that take the timed calls' form
-    "fetch_kib": {1: 289.8, 2: 94770.2, 3: 1243958.2, 4: 392706.0, 5: 397326.4},
-    "write_kib": {1: 200.7, 2: 39509.7, 3: 141267.2, 4: 54574.5, 5: 264969.9},
+    "fetch_kib": {1: 293.7, 2: 94411.1, 3: 1232176.1, 4: 366012.7, 5: 397340.2},
+    "write_kib": {1: 176.7, 2: 39525.5, 3: 141282.9, 4: 54574.0, 5: 264995.4},
 }
 
 
