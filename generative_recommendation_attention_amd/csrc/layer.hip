@@ -14,10 +14,11 @@
 // most 512), so each wave keeps its 32 tokens' whole K-long rows as MFMA B
 // operands in registers: layer_out normalises and gates them there (the
 // prologue), then both kernels stream the weight matrix through LDS in
-// chunks of output features (double buffered, one barrier per chunk) and
-// apply bias, SiLU or residual in the epilogue.  The products are computed
-// transposed (features down, tokens across), so a lane ends with one token
-// and runs of 4 consecutive features: 8-byte stores.
+// chunks of output features (one barrier per chunk) and apply bias, SiLU or
+// residual in the epilogue.  The products are computed transposed (features
+// down, tokens across), so a lane ends with one token and runs of 4
+// consecutive features; layer_in turns its tile around in LDS and stores
+// whole 64-byte token rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -104,29 +105,41 @@ __device__ __forceinline__ void chunk_products(const unsigned char* buf, const W
         }
 }
 
-// Chunks [c_begin, c_end) of the weight matrix through two LDS buffers (the
-// first must already be issued into buffer 0).  Iteration c waits for chunk
-// c, issues chunk c+1, stores chunk c-1's results and then computes chunk c's
-// products: the stores drain during the products instead of holding up the
-// next wait, which counts them too.
-template <typename T, int K, typename Epi>
+// Chunks [c_begin, c_end) of the weight matrix through PF + 1 LDS buffers
+// (chunks c_begin .. c_begin + PF - 1 must already be issued into buffers
+// 0 .. PF - 1, those past c_end as empty loads).  Iteration c waits for
+// chunk c, issues chunk c + PF (an empty load past c_end, so that PF - 1
+// chunks' loads always follow chunk c's), stores chunk c-1's results and
+// then computes chunk c's products.  The wait counts loads only in the
+// sense that matters: loads complete in issue order, so while chunk c's are
+// outstanding so are the (PF - 1) * LOADS issued after them; the epilogue's
+// stores, also counted, can only make it wait longer.  The epilogue must not
+// read global memory (the compiler would wait for every load before it, the
+// chunks in flight included).
+template <typename T, int K, int PF, typename Epi>
 __device__ __forceinline__ void chunk_loop(const uint16_t* w, int n, int c_begin, int c_end,
                                            const WeightStage<K>& st, unsigned char* lds,
                                            const typename Mfma<T>::v8* z, Epi& epilogue) {
     using C = LayerCfg<K>;
+    constexpr int NS = PF + 1;
     f32x16 acc[C::NB], prev[C::NB];
+    const int n_end = min(n, c_end * C::NC);
     for (int c = c_begin; c < c_end; ++c) {
-        __builtin_amdgcn_s_waitcnt(VMCNT_LE(0));
+        __builtin_amdgcn_s_waitcnt(VMCNT_LE((PF - 1) * C::LOADS));
         __syncthreads();
-        const int slot = (c - c_begin) & 1;
-        if (c + 1 < c_end) st.issue(w, n, (c + 1) * C::NC, lds + (slot ^ 1) * C::CHUNK_BYTES);
+        const int i = c - c_begin;
+        st.issue(w, n_end, (c + PF) * C::NC, lds + ((i + PF) % NS) * C::CHUNK_BYTES);
         if (c > c_begin) epilogue(c - 1, prev);
-        chunk_products<T, K>(lds + slot * C::CHUNK_BYTES, st, z, acc);
+        chunk_products<T, K>(lds + (i % NS) * C::CHUNK_BYTES, st, z, acc);
 #pragma unroll
         for (int b = 0; b < C::NB; ++b) prev[b] = acc[b];
     }
+    __builtin_amdgcn_s_waitcnt(VMCNT_LE(0));   // (the empty loads past the end)
     if (c_begin < c_end) epilogue(c_end - 1, prev);
 }
+
+// Chunks in flight: two at K <= 256, one at K = 512 (its 32 KB chunks).
+template <int K> struct LayerPf { static constexpr int value = K <= 256 ? 2 : 1; };
 
 struct LayerInArgs {
     const uint16_t* x;
@@ -143,7 +156,13 @@ __global__ __launch_bounds__(256, 2) void layer_in_kernel(LayerInArgs a) {
     using C = LayerCfg<K>;
     using M = Mfma<T>;
     using v4 = typename M::v4;
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * C::CHUNK_BYTES];
+    constexpr int PF = LayerPf<K>::value;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[(PF + 1) * C::CHUNK_BYTES];
+    __shared__ __attribute__((aligned(16))) float sbias[4 * 512];   // b1 (4 heads d <= 2048)
+    // Per wave, a 32 x 32 tile of results on its way out: token rows of 64
+    // bytes, 16-byte chunks swizzled by row so that both the writes (a lane
+    // per token) and the reads (four lanes per token) spread over the banks.
+    __shared__ __attribute__((aligned(16))) unsigned char tbuf[C::NW * 32 * 64];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 5, l32 = lane & 31;
@@ -167,37 +186,55 @@ __global__ __launch_bounds__(256, 2) void layer_in_kernel(LayerInArgs a) {
     }
     const int64_t tok = t0 + l32;
     const bool tok_live = tok < a.T;
+    // b1 into LDS (the epilogue reads no global memory); the chunk loop's
+    // first barrier orders these writes before any read.
+    for (int i = threadIdx.x; i < n; i += 256) sbias[i] = a.b1[i];
 
-    if (c_begin < c_end) st.issue(a.w1, n, c_begin * C::NC, lds);
+    {
+        const int n_end = min(n, c_end * C::NC);
+#pragma unroll
+        for (int j = 0; j < PF; ++j)
+            st.issue(a.w1, n_end, (c_begin + j) * C::NC, lds + j * C::CHUNK_BYTES);
+    }
     // Epilogue of chunk c: lane holds token `tok`, features c0 + 32 b + 8 i +
     // 4 g + (0..3).  A chunk lies inside one part (heads d is a multiple of the
     // chunk).
+    // Epilogue of chunk c: bias and SiLU in the product's layout (lane: token
+    // `tok`, features c0 + 8 i + 4 g + (0..3)), through the wave's tile in LDS
+    // (LDS operations of one wave complete in order), then stored a token row
+    // of 64 bytes per four lanes.  A chunk lies inside one part (heads d is a
+    // multiple of the chunk).
+    static_assert(C::NB == 1, "one 32-feature block per chunk");
+    unsigned char* tw = tbuf + wv * 32 * 64;
+    auto tsw = [](int r, int q) { return r * 64 + 16 * (q ^ ((r >> 1) & 3)); };
     auto epilogue = [&](int c, const f32x16* acc) {
         const int c0 = c * C::NC;
         const int part = __builtin_amdgcn_readfirstlane(c0 / a.heads_d);
         uint16_t* dst = part == 0 ? a.out[0] : part == 1 ? a.out[1] : part == 2 ? a.out[2]
                                                                                : a.out[3];
-        dst += tok * a.heads_d + (c0 - part * a.heads_d) + 4 * g;
-        const float* bias_c = a.b1 + c0 + 4 * g;
-        if (tok_live) {
+        dst += (c0 - part * a.heads_d);
+        const float* bias_c = sbias + c0 + 4 * g;
 #pragma unroll
-            for (int b = 0; b < C::NB; ++b)
+        for (int i = 0; i < 4; ++i) {
+            const f32x4 bias = *reinterpret_cast<const f32x4*>(bias_c + 8 * i);
+            f32x4 y;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const f32x4 bias = *reinterpret_cast<const f32x4*>(bias_c + 32 * b + 8 * i);
-                    f32x4 y;
+            for (int j = 0; j < 4; ++j) {
+                const float s = acc[0][4 * i + j] + bias[j];
+                y[j] = s * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * s));
+            }
+            const v4 yv = __builtin_convertvector(y, v4);
+            *reinterpret_cast<u32x2*>(tw + tsw(l32, i) + 8 * g) = __builtin_bit_cast(u32x2, yv);
+        }
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float s = acc[b][4 * i + j] + bias[j];
-                        y[j] = s * __builtin_amdgcn_rcpf(
-                                           1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * s));
-                    }
-                    const v4 yv = __builtin_convertvector(y, v4);
-                    *reinterpret_cast<u32x2*>(dst + 32 * b + 8 * i) = __builtin_bit_cast(u32x2, yv);
-                }
+        for (int h = 0; h < 2; ++h) {
+            const int r = 16 * h + (lane >> 2), q = lane & 3;
+            const u32x4 row = *reinterpret_cast<const u32x4*>(tw + tsw(r, q));
+            if (t0 + r < a.T)
+                *reinterpret_cast<u32x4*>(dst + (t0 + r) * a.heads_d + 8 * q) = row;
         }
     };
-    chunk_loop<T, K>(a.w1, n, c_begin, c_end, st, lds, z, epilogue);
+    chunk_loop<T, K, PF>(a.w1, n, c_begin, c_end, st, lds, z, epilogue);
 }
 
 struct LayerOutArgs {
@@ -243,7 +280,7 @@ __global__ __launch_bounds__(256, 2) void layer_out_kernel(LayerOutArgs a) {
     const int c_begin = blockIdx.y * a.chunks_per_wg;
     const int c_end = min(nchunks, c_begin + a.chunks_per_wg);
     const WeightStage<K> st(lane, wv);
-    if (c_begin < c_end) st.issue(a.w2, n, c_begin * C::NC, lds);   // overlaps the prologue
+    st.issue(a.w2, min(n, c_end * C::NC), c_begin * C::NC, lds);   // overlaps the prologue
 
     // Prologue: the attention rows of the wave's 32 tokens (token l32,
     // features 16 ks + 8 g ..), normalised over all K features (the lane and
@@ -322,7 +359,7 @@ __global__ __launch_bounds__(256, 2) void layer_out_kernel(LayerOutArgs a) {
                 }
         }
     };
-    chunk_loop<T, K>(a.w2, n, c_begin, c_end, st, lds, z, epilogue);
+    chunk_loop<T, K, 1>(a.w2, n, c_begin, c_end, st, lds, z, epilogue);
 }
 
 // Splits the output chunks over grid.y so that the launch has at least two
