@@ -17,8 +17,10 @@
 // chunks of output features (one barrier per chunk) and apply bias, SiLU or
 // residual in the epilogue.  The products are computed transposed (features
 // down, tokens across), so a lane ends with one token and runs of 4
-// consecutive features; layer_in turns its tile around in LDS and stores
-// whole 64-byte token rows.
+// consecutive features; each wave turns its 32 x 32 result tile around in
+// LDS and stores whole 64-byte token rows (layer_out first brings the
+// residual rows into that tile straight from HBM, so neither epilogue reads
+// global memory).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -270,7 +272,13 @@ __global__ __launch_bounds__(256, 2) void layer_out_kernel(LayerOutArgs a) {
     using v8 = typename M::v8;
     using v4 = typename M::v4;
     typedef float f32x8v __attribute__((ext_vector_type(8)));
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * C::CHUNK_BYTES];
+    constexpr int PF = LayerPf<K>::value;
+    constexpr int NS = PF + 1;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[NS * C::CHUNK_BYTES];
+    __shared__ __attribute__((aligned(16))) float sbias[512];   // b2 (d_model <= 512)
+    // Per wave, the chunk's residual rows (32 tokens x 64 bytes, loaded
+    // straight from HBM), overwritten by the results on their way out.
+    __shared__ __attribute__((aligned(16))) unsigned char xt[C::NW * 2048];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 5, l32 = lane & 31;
@@ -279,8 +287,13 @@ __global__ __launch_bounds__(256, 2) void layer_out_kernel(LayerOutArgs a) {
     const int nchunks = n / C::NC;
     const int c_begin = blockIdx.y * a.chunks_per_wg;
     const int c_end = min(nchunks, c_begin + a.chunks_per_wg);
+    const int n_end = min(n, c_end * C::NC);
     const WeightStage<K> st(lane, wv);
-    st.issue(a.w2, min(n, c_end * C::NC), c_begin * C::NC, lds);   // overlaps the prologue
+    // (b2 first: its loads are waited for before the LDS writes)
+    for (int i = threadIdx.x; i < n; i += 256) sbias[i] = a.b2[i];
+#pragma unroll
+    for (int j = 0; j < PF; ++j)   // (overlaps the prologue)
+        st.issue(a.w2, n_end, (c_begin + j) * C::NC, lds + j * C::CHUNK_BYTES);
 
     // Prologue: the attention rows of the wave's 32 tokens (token l32,
     // features 16 ks + 8 g ..), normalised over all K features (the lane and
@@ -334,32 +347,66 @@ __global__ __launch_bounds__(256, 2) void layer_out_kernel(LayerOutArgs a) {
         }
         z[ks] = __builtin_convertvector(zz, v8);
     }
-    const int64_t tok = t0 + l32;
-    const bool tok_live = tok < a.T;
 
-    // Epilogue of chunk c: residual and bias; lane holds token `tok`, output
-    // features f .. f + 3.
+    // Chunk c's residual rows into the wave's tile: lane l brings 16 bytes of
+    // token row 16 i + l / 4 (rows past T read as zero).
+    unsigned char* xw = xt + wv * 2048;
+    const int64_t rows_left = a.T - t0;
+    const __amdgpu_buffer_rsrc_t rx =
+            make_rsrc(a.x + t0 * n, (rows_left < 0 ? 0 : rows_left) * n * 2);
+    auto issue_x = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            load16_to_lds(rx, xw + 1024 * i, (16 * i + (lane >> 2)) * n * 2 + c * 64 + 16 * (lane & 3));
+    };
+    // Epilogue of chunk c: residual and bias in the product's layout (lane:
+    // token t0 + l32, features 8 i + 4 g + (0..3)), written over the residual
+    // in the tile (LDS operations of one wave complete in order), then stored
+    // a token row of 64 bytes per four lanes.
+    static_assert(C::NB == 1, "one 32-feature block per chunk");
     auto epilogue = [&](int c, const f32x16* acc) {
-        const int64_t row_f = tok * n + c * C::NC + 4 * g;
-        const float* bias_c = a.b2 + c * C::NC + 4 * g;
-        if (tok_live) {
+        const int c0 = c * C::NC;
 #pragma unroll
-            for (int b = 0; b < C::NB; ++b)
+        for (int i = 0; i < 4; ++i) {
+            unsigned char* px = xw + l32 * 64 + 16 * i + 8 * g;
+            const f32x4 bias = *reinterpret_cast<const f32x4*>(sbias + c0 + 8 * i + 4 * g);
+            const v4 xr = __builtin_bit_cast(v4, *reinterpret_cast<const u32x2*>(px));
+            f32x4 y;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int fo = 32 * b + 8 * i;
-                    const f32x4 bias = *reinterpret_cast<const f32x4*>(bias_c + fo);
-                    const v4 xr = __builtin_bit_cast(
-                            v4, *reinterpret_cast<const u32x2*>(a.x + row_f + fo));
-                    f32x4 y;
+            for (int j = 0; j < 4; ++j) y[j] = acc[0][4 * i + j] + bias[j] + (float)xr[j];
+            *reinterpret_cast<u32x2*>(px) = __builtin_bit_cast(u32x2, __builtin_convertvector(y, v4));
+        }
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) y[j] = acc[b][4 * i + j] + bias[j] + (float)xr[j];
-                    const v4 yv = __builtin_convertvector(y, v4);
-                    *reinterpret_cast<u32x2*>(a.y + row_f + fo) = __builtin_bit_cast(u32x2, yv);
-                }
+        for (int h = 0; h < 2; ++h) {
+            const int r = 16 * h + (lane >> 2), q = lane & 3;
+            const u32x4 row = *reinterpret_cast<const u32x4*>(xw + r * 64 + 16 * q);
+            if (t0 + r < a.T) *reinterpret_cast<u32x4*>(a.y + (t0 + r) * n + c0 + 8 * q) = row;
         }
     };
-    chunk_loop<T, K, 1>(a.w2, n, c_begin, c_end, st, lds, z, epilogue);
+    // Iteration c waits for weight chunk c and the residual of chunk c - 1,
+    // finishes chunk c - 1, brings chunk c's residual into the tile just
+    // freed, issues weight chunk c + PF (empty past c_end) and computes chunk
+    // c's products.  Per iteration x(c) is issued before w(c + PF), so the
+    // loads that may still fly at the wait are w(c + PF - 1)'s (PF = 2) or
+    // none (PF = 1); loads complete in issue order, and the stores counted
+    // with them can only make the wait longer.
+    f32x16 acc[C::NB], prev[C::NB];
+    for (int c = c_begin; c < c_end; ++c) {
+        __builtin_amdgcn_s_waitcnt(VMCNT_LE(PF == 1 ? 0 : C::LOADS));
+        __syncthreads();
+        const int i = c - c_begin;
+        if (c > c_begin) epilogue(c - 1, prev);
+        // (the tile's LDS reads done before the next residual lands in it:
+        // lgkmcnt 0, the other counters left open)
+        __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));
+        issue_x(c);
+        st.issue(a.w2, n_end, (c + PF) * C::NC, lds + ((i + PF) % NS) * C::CHUNK_BYTES);
+        chunk_products<T, K>(lds + (i % NS) * C::CHUNK_BYTES, st, z, acc);
+#pragma unroll
+        for (int b = 0; b < C::NB; ++b) prev[b] = acc[b];
+    }
+    __builtin_amdgcn_s_waitcnt(VMCNT_LE(0));
+    if (c_begin < c_end) epilogue(c_end - 1, prev);
 }
 
 // Splits the output chunks over grid.y so that the launch has at least two
