@@ -168,7 +168,10 @@ struct BwdCfg {
     static constexpr int NKS = D / 16;                // k-steps over the head dim
     static constexpr int NDB = D / 32;                // 32-wide head-dim blocks
     // Blocks staged ahead.  (Two at d = 64 measured slower: 0.80 ms instead of
-    // 0.69 ms for the dK/dV + dQ pair at 16 x 4096.)
+    // 0.69 ms for the dK/dV + dQ pair at 16 x 4096; again with the loads the
+    // compiler does not track: 0.612 -> 0.640 ms with two in the dK/dV kernel
+    // only, 0.690 with two in both, whose dQ kernel then needs 180 VGPRs and
+    // loses its third workgroup per CU.)
     static constexpr int PF = 1;
     static_assert(LPA * NW * 1024 == ARR, "array must split into whole wave loads");
 };
