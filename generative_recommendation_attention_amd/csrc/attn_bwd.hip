@@ -303,8 +303,13 @@ __device__ __forceinline__ void store_rows(uint16_t* base, int rows, int row_byt
 // and the rest are full.  LDS slot: Q (row reads), Q (transposed), dO (row
 // reads), dO (transposed).
 // ---------------------------------------------------------------------------
+// Three workgroups per CU (at most 168 VGPRs, some spilled) for the bias form
+// under the target-aware mask at d = 64: 1.503 -> 1.403 ms for its backward
+// at 16 x (3072 + 1024); the causal bias form and the plain kernels measured
+// slower that way (1.126 -> 1.239, 0.640 -> 0.692 ms).
 template <typename T, int D, bool FUSED, bool TGT, bool RAB = false>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dkv(typename BwdArgsOf<RAB>::type a) {
+__global__ __launch_bounds__(256, (RAB && TGT && D == 64) ? 3 : 2) void attn_bwd_dkv(
+        typename BwdArgsOf<RAB>::type a) {
     using C = BwdCfg<D>;
     using M = Mfma<T>;
     using v8 = typename M::v8;
@@ -558,8 +563,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv(typename BwdArgsOf<RAB>::
 //  whole launch and are summed over the wave once at its end (this measured
 //  1.313 -> 1.249 ms for the bias backward at 16 x 4096; per-block wave sums
 //  and LDS atomics before).  The bins go to the partial at the end.
+//  Three workgroups per CU (168 VGPRs, about 45 spilled) for the causal bias
+//  form at d = 64, whose waves wait on LDS for most of their cycles:
+//  1.244 -> 1.126 ms for its backward at 16 x 4096; under the target-aware
+//  mask (some 70 spilled) it measured slower, 1.498 -> 1.790.
 template <typename T, int D, bool FUSED, bool TGT, bool RAB = false>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dq(typename BwdArgsOf<RAB>::type a) {
+__global__ __launch_bounds__(256, (RAB && !TGT && D == 64) ? 3 : 2) void attn_bwd_dq(
+        typename BwdArgsOf<RAB>::type a) {
     using C = BwdCfg<D>;
     using M = Mfma<T>;
     using v8 = typename M::v8;
