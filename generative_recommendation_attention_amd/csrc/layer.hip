@@ -186,8 +186,6 @@ __global__ __launch_bounds__(256, 2) void layer_in_kernel(LayerInArgs a) {
                                        __builtin_amdgcn_raw_buffer_load_b128(
                                                r, l32 * C::RB + (16 * ks + 8 * g) * 2, 0, 0));
     }
-    const int64_t tok = t0 + l32;
-    const bool tok_live = tok < a.T;
     // b1 into LDS (the epilogue reads no global memory); the chunk loop's
     // first barrier orders these writes before any read.
     for (int i = threadIdx.x; i < n; i += 256) sbias[i] = a.b1[i];
