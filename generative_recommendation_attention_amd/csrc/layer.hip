@@ -196,11 +196,8 @@ __global__ __launch_bounds__(256, 2) void layer_in_kernel(LayerInArgs a) {
         for (int j = 0; j < PF; ++j)
             st.issue(a.w1, n_end, (c_begin + j) * C::NC, lds + j * C::CHUNK_BYTES);
     }
-    // Epilogue of chunk c: lane holds token `tok`, features c0 + 32 b + 8 i +
-    // 4 g + (0..3).  A chunk lies inside one part (heads d is a multiple of the
-    // chunk).
     // Epilogue of chunk c: bias and SiLU in the product's layout (lane: token
-    // `tok`, features c0 + 8 i + 4 g + (0..3)), through the wave's tile in LDS
+    // t0 + l32, features c0 + 8 i + 4 g + (0..3)), through the wave's tile in LDS
     // (LDS operations of one wave complete in order), then stored a token row
     // of 64 bytes per four lanes.  A chunk lies inside one part (heads d is a
     // multiple of the chunk).
