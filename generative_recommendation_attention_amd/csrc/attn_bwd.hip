@@ -67,14 +67,15 @@ struct BwdArgs {
     int64_t head_stride;
     int num_seqs;
     int heads;
-    float alpha;
-    float dv_scale;   // 1 / n
-    float g_scale;    // alpha / n
+    float score_scale;   // -alpha log2(e): the S operand's scale (K in dK/dV, Q in dQ)
+    float dv_scale;      // 1 / n
+    float g_scale;       // alpha / n
 };
 
 // Relative attention bias (the forward's reading: rab(r, c) = wpos[r - c] +
 // wtime[bucket(ts_r - ts_c)], added to alpha <q_r, k_c> before SiLU).  Both
-// kernels recompute it and start the score accumulators at rab / alpha; the
+// kernels recompute it and start the score accumulators at -log2(e) rab (the
+// scores being -log2(e) alpha s, from the pre-scaled operand); the
 // dQ kernel, which holds one query per lane and 16 keys per lane in registers,
 // also sums each kept pair's score gradient into the two tables' gradients.
 // (A separate argument type, so that the other kernels keep their argument
@@ -88,7 +89,7 @@ struct BwdArgsRab : BwdArgs {
     int ntime;
     int gstride;
     int nparts;
-    float bias_scale;      // 1 / alpha
+    float bias_scale;      // -log2(e)
 };
 template <bool RAB> struct BwdArgsOf { using type = BwdArgs; };
 template <> struct BwdArgsOf<true> { using type = BwdArgsRab; };
@@ -266,6 +267,16 @@ __device__ __forceinline__ void pointwise(float s, float dp, float alpha, float*
     *ds = dp * __builtin_fmaf(pr, 1.0f - sig, sig);
 }
 
+// The same from m = -log2(e) x, the score of an operand pre-scaled by
+// -alpha log2(e) (the 16-bit kernels): x = -ln(2) m, sig = 1/(1 + 2^m).
+__device__ __forceinline__ void pointwise_m(float m, float dp, float* p, float* ds) {
+    const float x = -0.69314718055994531f * m;
+    const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(m));
+    const float pr = x * sig;
+    *p = pr;
+    *ds = dp * __builtin_fmaf(pr, 1.0f - sig, sig);
+}
+
 // Whether a block's pointwise pass applies the mask: a compile-time constant
 // (std::true_type / std::false_type) or a run-time flag.
 __device__ __forceinline__ bool mask_on(bool m) { return m; }
@@ -375,6 +386,12 @@ __global__ __launch_bounds__(256, (RAB && TGT && D == 64) ? 3 : 2) void attn_bwd
                           row_bytes, l32, g, kop);
         load_rows_b<T, D>(a.v + seq_base + (int64_t)kw0 * row_stride, row_stride, s - kw0,
                           row_bytes, l32, g, vop);
+        // K * (-alpha log2(e)), rounded to T (nearest even): S^T then holds
+        // m = -log2(e) alpha s, the exponent the pointwise pass needs.
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks)
+            kop[ks] = __builtin_convertvector(
+                    __builtin_convertvector(kop[ks], f32x8) * a.score_scale, v8);
         f32x16 dk[C::NDB], dv[C::NDB];
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) dk[db] = dv[db] = (f32x16){};
@@ -488,7 +505,7 @@ __global__ __launch_bounds__(256, (RAB && TGT && D == 64) ? 3 : 2) void attn_bwd
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         float pr, dsr;
-                        pointwise(st[r], dp[r], a.alpha, &pr, &dsr);
+                        pointwise_m(st[r], dp[r], &pr, &dsr);
                         if (mask_on(masked_c)) {
                             const int qr = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
                             const bool keep = key <= qr && (key < hist || key == qr);
@@ -666,6 +683,11 @@ __global__ __launch_bounds__(256, (RAB && !TGT && D == 64) ? 3 : 2) void attn_bw
                           row_bytes, l32, g, qop);
         load_rows_b<T, D>(a.dout + seq_base + (int64_t)wr0 * row_stride, row_stride, s - wr0,
                           row_bytes, l32, g, oop);
+        // Q * (-alpha log2(e)), rounded to T, as K in the dK/dV kernel.
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks)
+            qop[ks] = __builtin_convertvector(
+                    __builtin_convertvector(qop[ks], f32x8) * a.score_scale, v8);
         f32x16 dq[C::NDB];
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) dq[db] = (f32x16){};
@@ -775,7 +797,7 @@ __global__ __launch_bounds__(256, (RAB && !TGT && D == 64) ? 3 : 2) void attn_bw
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         float pr, dsr;
-                        pointwise(st[r], dp[r], a.alpha, &pr, &dsr);
+                        pointwise_m(st[r], dp[r], &pr, &dsr);
                         if (mask_on(masked_c)) {
                             const int key = k0 + 8 * (r >> 2) + 4 * g + (r & 3);
                             dsr = (key <= row && (key < hist || key == row)) ? dsr : 0.0f;
@@ -923,7 +945,7 @@ hipError_t launch_bwd_typed(const BwdParams& p, WorkList wl, hipStream_t stream,
     a.heads = p.heads;
     a.row_stride = p.dense ? p.d : (int64_t)p.heads * p.d;
     a.head_stride = p.dense ? p.dense_len * p.d : p.d;
-    a.alpha = p.alpha;
+    a.score_scale = -p.alpha * BWD_LOG2E;
     a.dv_scale = 1.0f / p.n;
     a.g_scale = p.alpha / p.n;
     using Fn = void (*)(BwdArgs);
@@ -987,7 +1009,7 @@ hipError_t launch_bwd_rab(const BwdParams& p, WorkList wl, hipStream_t stream, h
     a.heads = p.heads;
     a.row_stride = (int64_t)p.heads * p.d;
     a.head_stride = p.d;
-    a.alpha = p.alpha;
+    a.score_scale = -p.alpha * BWD_LOG2E;
     a.dv_scale = 1.0f / p.n;
     a.g_scale = p.alpha / p.n;
     a.ts = p.timestamps;
@@ -998,7 +1020,7 @@ hipError_t launch_bwd_rab(const BwdParams& p, WorkList wl, hipStream_t stream, h
     a.ntime = p.num_time;
     a.gstride = rab_partial_stride(p.num_pos);
     a.nparts = RAB_PARTS;
-    a.bias_scale = (float)(1.0 / (double)p.alpha);
+    a.bias_scale = -BWD_LOG2E;
     using Fn = void (*)(BwdArgsRab);
     const Fn f_dkv = wl.fused ? attn_bwd_dkv<T, D, true, TGT, true>
                               : attn_bwd_dkv<T, D, false, TGT, true>;
