@@ -268,13 +268,16 @@ __device__ __forceinline__ void pointwise(float s, float dp, float alpha, float*
 }
 
 // The same from m = -log2(e) x, the score of an operand pre-scaled by
-// -alpha log2(e) (the 16-bit kernels): x = -ln(2) m, sig = 1/(1 + 2^m).
+// -alpha log2(e) (the 16-bit kernels): sig = 1/(1 + 2^m), and with x =
+// -ln(2) m the weight comes out divided by -ln(2), p' = m sig (the dV
+// epilogue multiplies the -ln(2) back in), while ds = dp (sig + p (1 - sig))
+// = dp fma(p', ln(2) (sig - 1), sig).
+constexpr float BWD_LN2 = 0.69314718055994531f;
 __device__ __forceinline__ void pointwise_m(float m, float dp, float* p, float* ds) {
-    const float x = -0.69314718055994531f * m;
     const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(m));
-    const float pr = x * sig;
+    const float pr = m * sig;
     *p = pr;
-    *ds = dp * __builtin_fmaf(pr, 1.0f - sig, sig);
+    *ds = dp * __builtin_fmaf(pr, __builtin_fmaf(sig, BWD_LN2, -BWD_LN2), sig);
 }
 
 // Whether a block's pointwise pass applies the mask: a compile-time constant
@@ -547,7 +550,8 @@ __global__ __launch_bounds__(256, (RAB && TGT && D == 64) ? 3 : 2) void attn_bwd
         if (live) {
             const int64_t off = seq_base + (int64_t)kw0 * row_stride;
             store_rows<T, D>(a.dk + off, s - kw0, row_bytes, l32, g, dk, a.g_scale);
-            store_rows<T, D>(a.dv + off, s - kw0, row_bytes, l32, g, dv, a.dv_scale);
+            // (the weights were m sig = silu(x) / -ln(2))
+            store_rows<T, D>(a.dv + off, s - kw0, row_bytes, l32, g, dv, -BWD_LN2 * a.dv_scale);
         }
     }
 }
