@@ -334,7 +334,7 @@ __global__ __launch_bounds__(256, (RAB && TGT && D == 64) ? 3 : 2) void attn_bwd
     __shared__ __attribute__((aligned(1024))) unsigned char lds[NS * SLOT + RAB_BYTES];
     __shared__ int s_item[NQ];
     __shared__ LocalTables lt;
-    __shared__ float ttab[RAB ? 33 : 1];
+    __shared__ float ttab[RAB ? 33 : 1];   // time term by v_ffbh_u32(gap + 1) + 1, times -log2(e)
     static_assert(C::NW * 64 >= FUSE_SEQS && C::NW * 64 >= 32 * NQ, "fused tables need a thread per sequence");
     static_assert(NS * SLOT + RAB_BYTES + (int)sizeof(LocalTables) <= 80 * 1024,
                   "LDS for two workgroups per CU");
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(256, (RAB && TGT && D == 64) ? 3 : 2) void attn_bwd
     const int row_bytes = (int)(row_stride * 2);
     const LaneOffsets<D> lo(lane, wv, row_bytes);
     if constexpr (RAB) {
-        if (tid < 33) ttab[tid] = a.wtime[rab_time_bucket(tid, a.ntime)];
+        if (tid < 33) ttab[tid] = a.wtime[rab_time_bucket(tid, a.ntime)] * a.bias_scale;
     }
 
     Tables tb;
@@ -476,7 +476,7 @@ __global__ __launch_bounds__(256, (RAB && TGT && D == 64) ? 3 : 2) void attn_bwd
                     if (far) {
                         const float tlast = ttab[0];
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) st[r] = (posv(r) + tlast) * a.bias_scale;
+                        for (int r = 0; r < 16; ++r) st[r] = __builtin_fmaf(posv(r), a.bias_scale, tlast);
                     } else {
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
@@ -485,7 +485,8 @@ __global__ __launch_bounds__(256, (RAB && TGT && D == 64) ? 3 : 2) void attn_bwd
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
                                 const int f = ffbh_u32(tq[e] + c1);
-                                st[4 * j + e] = (posv(4 * j + e) + ttab[f + 1]) * a.bias_scale;
+                                st[4 * j + e] =
+                                        __builtin_fmaf(posv(4 * j + e), a.bias_scale, ttab[f + 1]);
                             }
                         }
                     }
@@ -601,7 +602,7 @@ __global__ __launch_bounds__(256, (RAB && !TGT && D == 64) ? 3 : 2) void attn_bw
     __shared__ __attribute__((aligned(1024))) unsigned char lds[NS * SLOT + RAB_BYTES];
     __shared__ int s_item[NQ];
     __shared__ LocalTables lt;
-    __shared__ float ttab[RAB ? 33 : 1];
+    __shared__ float ttab[RAB ? 33 : 1];   // time term by v_ffbh_u32(gap + 1) + 1, times -log2(e)
     __shared__ float ring[RAB ? 4 * 256 : 1];   // per wave: position-gradient sums by distance mod 256
     // time-gradient sums by bucket; [32]: candidates' pairs with themselves
     // (position distance 0, target-aware mask)
@@ -621,7 +622,7 @@ __global__ __launch_bounds__(256, (RAB && !TGT && D == 64) ? 3 : 2) void attn_bw
     float* gpart = nullptr;
     float tlast = 0.0f;   // this lane's time-gradient sum in the last bucket
     if constexpr (RAB) {
-        if (tid < 33) ttab[tid] = a.wtime[rab_time_bucket(tid, a.ntime)];
+        if (tid < 33) ttab[tid] = a.wtime[rab_time_bucket(tid, a.ntime)] * a.bias_scale;
         if (tid < 33) tbins[tid] = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) ring[tid + 256 * i] = 0.0f;
@@ -771,7 +772,7 @@ __global__ __launch_bounds__(256, (RAB && !TGT && D == 64) ? 3 : 2) void attn_bw
                     if (far) {
                         const float tlast = ttab[0];
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) st[r] = (posv(r) + tlast) * a.bias_scale;
+                        for (int r = 0; r < 16; ++r) st[r] = __builtin_fmaf(posv(r), a.bias_scale, tlast);
                     } else {
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
@@ -779,7 +780,8 @@ __global__ __launch_bounds__(256, (RAB && !TGT && D == 64) ? 3 : 2) void attn_bw
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
                                 const int f = ffbh_u32(trp1 - tk[j][e]);
-                                st[4 * j + e] = (posv(4 * j + e) + ttab[f + 1]) * a.bias_scale;
+                                st[4 * j + e] =
+                                        __builtin_fmaf(posv(4 * j + e), a.bias_scale, ttab[f + 1]);
                             }
                         }
                     }
