@@ -3,7 +3,8 @@ paper translation Appendix H) against the fp64 CPU oracle, through the C ABI.
 
 Candidates with their own q, k, v attend to a cached history's K and V plus
 themselves.  Small cases are compared element by element; the 16 x (3072
-cached + 1024 candidates) workload on sampled rows.  Properties: the result
+cached + 1024 candidates) workload element by element too, and on sampled
+rows through the oracle's row function.  Properties: the result
 equals the candidate rows of one target-aware pass over history + candidates
 (GPU against GPU, within tolerance), and a request without history gives
 each candidate silu(alpha <q, k>) v / n.
@@ -143,7 +144,7 @@ def sample_cached_rows(cc, seed=13, per_seq_random=8):
     return np.array(toks, np.int64), np.array(hds, np.int32)
 
 
-def test_cached_workload_sampled_rows():
+def test_cached_workload_whole_output_and_sampled_rows():
     cc = workloads.cached_workload()
     c = cc.cand
     log(f"cached workload: {c.description}")
@@ -156,6 +157,9 @@ def test_cached_workload_sampled_rows():
                              c.heads, c.d, c.alpha, c.n, c.dtype, tok, hd)
     mr, l2 = assert_close(g, ref, c.dtype, "cached workload sampled")
     log(f"  max|err|/max|ref| = {mr:.3e}, rel L2 = {l2:.3e}")
+    mr, l2 = assert_close(from_torch(got, c.dtype), oracle_cached(cc), c.dtype,
+                          "cached workload whole output")
+    log(f"  whole output: max|err|/max|ref| = {mr:.3e}, rel L2 = {l2:.3e}")
     assert torch.isfinite(got.float()).all().item()
 
 

@@ -84,8 +84,9 @@ def test_dense_offset_ramp_reuse_and_invalidation():
     torch.cuda.synchronize()
 
 
-def test_dense_blog_shape_sampled_rows():
-    """QKV (16, 4, 4096, 64) in bf16, the shape the blog times, on sampled rows."""
+def test_dense_blog_shape_whole_output_and_sampled_rows():
+    """QKV (16, 4, 4096, 64) in bf16, the shape the blog times: the whole
+    output, and sampled rows through the oracle's row function."""
     B, H, S, d = 16, 4, 4096, 64
     case, dense = dense_case(B, H, S, d, "bf16", seed=840, alpha=0.125, n=4096.0)
     out = run_dense(case, dense, B, H, S, d)
@@ -100,6 +101,10 @@ def test_dense_blog_shape_sampled_rows():
                       tok, hs.astype(np.int32))
     mr, l2 = assert_close(got, ref, "bf16", "dense blog shape")
     log(f"  max|err|/max|ref| = {mr:.3e}, rel L2 = {l2:.3e}")
+    whole = to_jagged(from_torch(out, "bf16"), B, H, S, d)
+    ref = oracle.fwd(case.q, case.k, case.v, case.offsets, H, d, case.alpha, case.n, "bf16")
+    mr, l2 = assert_close(whole, ref, "bf16", "dense blog shape whole output")
+    log(f"  whole output: max|err|/max|ref| = {mr:.3e}, rel L2 = {l2:.3e}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])

@@ -3,8 +3,8 @@ CPU oracle, through the C ABI (HSTU paper translation §3: rab_{p,t} is added
 to the scores before SiLU; Appendix G: it is built inside the operator from
 its parameters; the reading of the lost equation is the oracle's).
 
-Small cases are compared element by element, the 16 x 4096 workload on sampled
-rows.  Properties: zero tables give the plain causal result bit for bit (the
+Small cases and the 16 x 4096 workload are compared element by element (the
+workload also on sampled rows through the oracle's row function).  Properties: zero tables give the plain causal result bit for bit (the
 bias only sets the score accumulators' initial value), and a bias that does
 not depend on the pair shifts every score like one more head dimension.
 """
@@ -118,11 +118,12 @@ def test_rab_many_sequences_worklist_path():
     assert_close(got, oracle_rab(case, r), "bf16", "rab 300 sequences")
 
 
-def test_rab_workload_sampled_rows():
+def test_rab_workload_whole_output_and_sampled_rows():
     """16 x 4096, heads 4, d 64, bf16, a position entry per distance and 16
-    time buckets: sampled rows (tile edges and random) of every head."""
+    time buckets: the whole output, and sampled rows (tile edges and random)
+    of every head through the oracle's row function."""
     case, r = workloads.rab_workload()
-    log("rab workload 16 x 4096 (sampled rows)")
+    log("rab workload 16 x 4096 (whole output and sampled rows)")
     out = run_rab(case, r)
     rng = np.random.default_rng(11)
     seqs = rng.integers(0, 16, size=24)
@@ -134,6 +135,9 @@ def test_rab_workload_sampled_rows():
                           r.time_bias, 4, 64, case.alpha, case.n, "bf16", tok, hd)
     mr, l2 = assert_close(got, ref, "bf16", "rab workload rows")
     log(f"  max|err|/max|ref| = {mr:.3e}, rel L2 = {l2:.3e}")
+    mr, l2 = assert_close(from_torch(out, "bf16"), oracle_rab(case, r), "bf16",
+                          "rab workload whole output")
+    log(f"  whole output: max|err|/max|ref| = {mr:.3e}, rel L2 = {l2:.3e}")
 
 
 def test_rab_repeat_is_deterministic():

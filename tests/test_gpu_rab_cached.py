@@ -9,7 +9,7 @@ Small cases are compared element by element: histories on and around the
 32/64-key tiles (the kernel pads the history to whole tiles and reads zero K,
 V and timestamps there), empty histories and micro-batches, position tables
 shorter than the distances.  The 16 x (3072 cached + 1024 candidates)
-workload on sampled rows.  Properties: zero tables give the cached forward
+workload element by element and on sampled rows.  Properties: zero tables give the cached forward
 without bias bit for bit; the result equals the candidate rows of one
 target-aware bias pass over history + candidates (GPU against GPU, within the
 tolerance: the candidates' own keys sit in other key blocks there).
@@ -170,9 +170,10 @@ def test_rab_cached_null_cache_ignores_history_offsets(dtype):
                  "rab cached, null cache with non-zero offsets")
 
 
-def test_rab_cached_workload_sampled_rows():
+def test_rab_cached_workload_whole_output_and_sampled_rows():
     """16 x (3072 cached + 1024 candidates), heads 4, d 64, bf16, a position
-    entry per distance and 16 time buckets: sampled candidate rows."""
+    entry per distance and 16 time buckets: the whole output, and sampled
+    candidate rows through the oracle's row function."""
     cc, r, hts = workloads.rab_cached_workload()
     c = cc.cand
     log(f"rab cached workload: Tc={c.total} Th={int(cc.hist_offsets[-1])}")
@@ -190,6 +191,9 @@ def test_rab_cached_workload_sampled_rows():
                                  c.heads, c.d, c.alpha, c.n, c.dtype, tok, hd)
     mr, l2 = assert_close(g, ref, c.dtype, "rab cached workload sampled")
     log(f"  max|err|/max|ref| = {mr:.3e}, rel L2 = {l2:.3e}")
+    mr, l2 = assert_close(from_torch(got, c.dtype), oracle_fwd(cc, r, hts), c.dtype,
+                          "rab cached workload whole output")
+    log(f"  whole output: max|err|/max|ref| = {mr:.3e}, rel L2 = {l2:.3e}")
     assert torch.isfinite(got.float()).all().item()
 
 

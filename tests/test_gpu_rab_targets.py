@@ -4,8 +4,9 @@ translation §3.4: M-FALCON adjusts the mask and rab_{p,t} together; the
 reading, a candidate at the position right after the history with its own
 timestamp, is the oracle's).
 
-Small cases are compared element by element, the 16 x (3072 + 1024) ranking
-workload on sampled rows around the history/candidate boundary.  Properties:
+Small cases and the 16 x (3072 + 1024) ranking workload are compared element
+by element (the workload also on sampled rows around the history/candidate
+boundary through the oracle's row function).  Properties:
 no candidates gives the causal bias forward bit for bit, and so does one
 candidate per sequence (the last row is then its own candidate at its own
 position); zero tables give the target-aware forward without bias bit for bit.
@@ -131,10 +132,11 @@ def test_rab_targets_many_sequences_worklist_path():
     assert_close(got, oracle_fwd(case, r), "bf16", "rab targets 300 sequences")
 
 
-def test_rab_targets_workload_sampled_rows():
+def test_rab_targets_workload_whole_output_and_sampled_rows():
     """16 x (3072 history + 1024 candidates), heads 4, d 64, bf16, a position
-    entry per distance and 16 time buckets: rows on both sides of the
-    history/candidate boundary, tile edges and random rows, every head."""
+    entry per distance and 16 time buckets: the whole output, and rows on
+    both sides of the history/candidate boundary, tile edges and random rows
+    through the oracle's row function."""
     case, r = workloads.rab_targets_workload()
     log(f"rab targets workload: T={case.total}")
     out = run(case, r)
@@ -150,6 +152,9 @@ def test_rab_targets_workload_sampled_rows():
                           num_targets=case.num_targets)
     mr, l2 = assert_close(got, ref, "bf16", "rab targets workload rows")
     log(f"  max|err|/max|ref| = {mr:.3e}, rel L2 = {l2:.3e}")
+    mr, l2 = assert_close(from_torch(out, "bf16"), oracle_fwd(case, r), "bf16",
+                          "rab targets workload whole output")
+    log(f"  whole output: max|err|/max|ref| = {mr:.3e}, rel L2 = {l2:.3e}")
     assert torch.isfinite(out.float()).all().item()
 
 

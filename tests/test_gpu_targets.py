@@ -3,7 +3,8 @@ through the C ABI (HSTU paper translation §3.4, Appendix H, Fig. 11: the last
 t tokens of a sequence are candidates that see the history and themselves).
 
 Small cases are compared element by element; the 16 x (3072 + 1024) ranking
-workload is compared on sampled rows around the history/candidate boundary.
+workload element by element too, and on sampled rows around the
+history/candidate boundary through the oracle's row function.
 Properties: t = 0 and t = 1 give the plain causal result bit for bit, history
 rows are untouched by the candidates, and each candidate's row equals the
 plain causal result of its history followed by that candidate alone.
@@ -168,7 +169,7 @@ def sample_target_rows(case, seed=11, per_seq_random=8):
     return np.array(toks, np.int64), np.array(hds, np.int32)
 
 
-def test_targets_workload_sampled_rows():
+def test_targets_workload_whole_output_and_sampled_rows():
     case = workloads.targets_workload()
     log(f"targets workload: {case.description}; T={case.total}")
     got = run_targets(case)
@@ -180,6 +181,9 @@ def test_targets_workload_sampled_rows():
                       case.n, case.dtype, tok, hd, num_targets=case.num_targets)
     mr, l2 = assert_close(g, ref, case.dtype, "targets workload sampled")
     log(f"  max|err|/max|ref| = {mr:.3e}, rel L2 = {l2:.3e}")
+    mr, l2 = assert_close(from_torch(got, case.dtype), oracle_fwd(case), case.dtype,
+                          "targets workload whole output")
+    log(f"  whole output: max|err|/max|ref| = {mr:.3e}, rel L2 = {l2:.3e}")
     assert torch.isfinite(got.float()).all().item()
 
 
