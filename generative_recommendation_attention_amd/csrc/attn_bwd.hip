@@ -280,12 +280,6 @@ __device__ __forceinline__ void pointwise_m(float m, float dp, float* p, float* 
     *ds = dp * __builtin_fmaf(pr, __builtin_fmaf(sig, BWD_LN2, -BWD_LN2), sig);
 }
 
-// Whether a block's pointwise pass applies the mask: a compile-time constant
-// (std::true_type / std::false_type) or a run-time flag.
-__device__ __forceinline__ bool mask_on(bool m) { return m; }
-template <bool B>
-__device__ __forceinline__ constexpr bool mask_on(std::integral_constant<bool, B>) { return B; }
-
 // Writes a transposed accumulator (head-dim rows x 32 tokens: lane = token
 // l32, registers = head-dim rows 32db + 8(r/4) + 4g + r%4) scaled, rounded to
 // T; tokens at or past `rows` are dropped.
@@ -500,33 +494,30 @@ __global__ __launch_bounds__(256, (RAB && TGT && D == 64) ? 3 : 2) void attn_bwd
                 const bool masked = q0 == kw0 || (TGT && kw0 + 31 >= hist);
                 const int key = kw0 + l32;
                 f32x16 p, ds;
-                // At d = 64, two copies under a uniform branch: folded into
-                // one, every block paid the masked blocks' selects (0.673 ->
-                // 0.641 ms for the backward at 16 x 4096).  At d = 128 (and in
-                // the bias kernels under the target-aware mask) the second
-                // copy costs more in spilled registers than it saves.
-                auto pointwise_block = [&](auto masked_c) {
+                // A pair its query row does not see gets the score operand
+                // +2^100: exp2 overflows to +inf, its reciprocal is 0, and the
+                // pair's weight and dS come out as (signed) zeros.  The
+                // selects sit under one uniform branch, so the pointwise pass
+                // is one straight-line block for every block (a select folded
+                // into it became a branch per element; two copies of it cost
+                // registers).  With o = query - q0 - 4g (a constant per
+                // register) and kq = key - q0 - 4g: the row sees the key iff
+                // o >= kq and (key < hist or o == kq).
+                if (masked) {
+                    const int kq = key - q0 - 4 * g;
+                    const bool kh = key < hist;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        float pr, dsr;
-                        pointwise_m(st[r], dp[r], &pr, &dsr);
-                        if (mask_on(masked_c)) {
-                            const int qr = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
-                            const bool keep = key <= qr && (key < hist || key == qr);
-                            pr = keep ? pr : 0.0f;
-                            dsr = keep ? dsr : 0.0f;
-                        }
-                        p[r] = pr;
-                        ds[r] = dsr;
+                        const int o = 8 * (r >> 2) + (r & 3);
+                        st[r] = (o >= kq && (kh || o == kq)) ? st[r] : 0x1p100f;
                     }
-                };
-                if constexpr (D == 64 && !(RAB && TGT)) {
-                    if (masked)
-                        pointwise_block(std::true_type{});
-                    else
-                        pointwise_block(std::false_type{});
-                } else {
-                    pointwise_block(masked);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float pr, dsr;
+                    pointwise_m(st[r], dp[r], &pr, &dsr);
+                    p[r] = pr;
+                    ds[r] = dsr;
                 }
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
@@ -795,23 +786,31 @@ __global__ __launch_bounds__(256, (RAB && !TGT && D == 64) ? 3 : 2) void attn_bw
                 const bool masked = k0 + 31 >= wr0 || (TGT && k0 + 31 >= hist);
                 const int row = wr0 + l32;
                 f32x16 ds;
-                // (one copy with the mask folded in: two, as in the dK/dV
-                // kernel, take this kernel from 165 to 180 VGPRs at d = 64 and
-                // from three workgroups per CU to two, which cost more than
-                // the selects: 4.85 -> 5.64 M active cycles at 16 x 4096)
-                auto pointwise_block = [&](auto masked_c) {
+                // A pair the row does not see gets the score operand +2^100:
+                // exp2 overflows to +inf, its reciprocal is 0, so the pair's
+                // weight and dS come out as (signed) zeros with no select
+                // after the pointwise pass.  The selects sit under one
+                // uniform branch, so the pointwise pass stays one
+                // straight-line block (a select per element folded into it
+                // became a branch per element, with the loop-invariant key
+                // offsets spilled to scratch).  With o = key - k0 - 4g (a
+                // constant per register): the row sees o <= eq and (o < hh
+                // or o == eq).
+                if (masked) {
+                    const int eq = row - k0 - 4 * g;
+                    const int hh = hist - k0 - 4 * g;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        float pr, dsr;
-                        pointwise_m(st[r], dp[r], &pr, &dsr);
-                        if (mask_on(masked_c)) {
-                            const int key = k0 + 8 * (r >> 2) + 4 * g + (r & 3);
-                            dsr = (key <= row && (key < hist || key == row)) ? dsr : 0.0f;
-                        }
-                        ds[r] = dsr;
+                        const int o = 8 * (r >> 2) + (r & 3);
+                        st[r] = (o <= eq && (o < hh || o == eq)) ? st[r] : 0x1p100f;
                     }
-                };
-                pointwise_block(masked);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float pr, dsr;
+                    pointwise_m(st[r], dp[r], &pr, &dsr);
+                    ds[r] = dsr;
+                }
                 if constexpr (RAB) {
                     f32x16 dgl = ds;   // the pairs credited along diagonals (row - key)
                     if constexpr (TGT) {
