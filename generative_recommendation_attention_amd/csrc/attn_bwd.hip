@@ -311,12 +311,13 @@ __device__ __forceinline__ void store_rows(uint16_t* base, int rows, int row_byt
 // and the rest are full.  LDS slot: Q (row reads), Q (transposed), dO (row
 // reads), dO (transposed).
 // ---------------------------------------------------------------------------
-// Three workgroups per CU (at most 168 VGPRs, some spilled) for the bias form
-// under the target-aware mask at d = 64: 1.503 -> 1.403 ms for its backward
-// at 16 x (3072 + 1024); the causal bias form and the plain kernels measured
-// slower that way (1.126 -> 1.239, 0.640 -> 0.692 ms).
+// Three workgroups per CU (at most 168 VGPRs) at d = 64 for the plain kernels
+// (no spills: 0.616 -> 0.605 ms for the backward at 16 x 4096) and for the
+// bias form under the target-aware mask (some spilled, none inside the block
+// loop: 1.503 -> 1.403 ms for its backward at 16 x (3072 + 1024)); the causal
+// bias form measured slower that way (1.126 -> 1.239 ms).
 template <typename T, int D, bool FUSED, bool TGT, bool RAB = false>
-__global__ __launch_bounds__(256, (RAB && TGT && D == 64) ? 3 : 2) void attn_bwd_dkv(
+__global__ __launch_bounds__(256, (D == 64 && (TGT || !RAB)) ? 3 : 2) void attn_bwd_dkv(
         typename BwdArgsOf<RAB>::type a) {
     using C = BwdCfg<D>;
     using M = Mfma<T>;
@@ -576,10 +577,13 @@ __global__ __launch_bounds__(256, (RAB && TGT && D == 64) ? 3 : 2) void attn_bwd
 //  whole launch and are summed over the wave once at its end (this measured
 //  1.313 -> 1.249 ms for the bias backward at 16 x 4096; per-block wave sums
 //  and LDS atomics before).  The bins go to the partial at the end.
-//  Three workgroups per CU (168 VGPRs, about 45 spilled) for the causal bias
-//  form at d = 64, whose waves wait on LDS for most of their cycles:
-//  1.244 -> 1.126 ms for its backward at 16 x 4096; under the target-aware
-//  mask (some 70 spilled) it measured slower, 1.498 -> 1.790.
+//  Three workgroups per CU (168 VGPRs, about 20 spilled, none reloaded inside
+//  the block loop) for the causal bias form at d = 64, whose waves wait on
+//  LDS for most of their cycles: 1.244 -> 1.126 ms for its backward at
+//  16 x 4096; under the target-aware mask (some 70 spilled) it measured
+//  slower, 1.498 -> 1.790.  A spill reloaded inside the loop costs more than
+//  its load: the compiler's wait for it counts the tile loads issued before
+//  it too, so the next block's prefetch stops overlapping.
 template <typename T, int D, bool FUSED, bool TGT, bool RAB = false>
 __global__ __launch_bounds__(256, (RAB && !TGT && D == 64) ? 3 : 2) void attn_bwd_dq(
         typename BwdArgsOf<RAB>::type a) {
@@ -870,6 +874,14 @@ __global__ __launch_bounds__(256, (RAB && !TGT && D == 64) ? 3 : 2) void attn_bw
 #pragma unroll
                         for (int r = 0; r < 16; ++r) run += ds[r];
                     } else {
+                        // (the keys' timestamps read again: kept in registers
+                        // across the products they pushed this kernel's
+                        // loop-invariant values out to scratch)
+                        const unsigned char* ra = lds + NS * SLOT + (c % NS) * RABB_WORDS * 4;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            tk[j] = *reinterpret_cast<const volatile u32x4*>(
+                                    ra + 4 * (4 * g + 8 * j));
                         prev = min(31 - ffbh_u32(trp1 - tk[0][0]), cap);
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
