@@ -1033,14 +1033,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma_f32(KernelArgsF32 a)
                     // four k-steps of the second product.
 #pragma unroll
                     for (int rq = 0; rq < 4; ++rq) {
-                        float p4[4];
+                        // The exp2 argument of each pair; one the row does not
+                        // see gets +2^100, whose weight m / (1 + 2^m) comes out
+                        // as 0.  (Each run-time choice is taken once per four
+                        // keys, not per key, so the SiLU of the four is
+                        // straight-line code.)
+                        float m[4];
+                        if (a.ts) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int r = 4 * rq + i;
-                            const int kvl = kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                            float p;
-                            if (a.ts) {
-                                const int key = k0 + kvl;
+                            for (int i = 0; i < 4; ++i) {
+                                const int key = k0 + kb * 32 + 8 * rq + 4 * g + i;
                                 // (a candidate row sits at position hist; its own
                                 // key at distance 0)
                                 const int dist = key == my_row ? 0 : pos_row - key;
@@ -1054,17 +1056,25 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma_f32(KernelArgsF32 a)
                                     tk = (uint32_t)a.ts[start + key - shift];
                                 const uint32_t x = trp1 - tk;
                                 const int lz = __clz((int)x);   // 32 for x == 0 (gap -1)
-                                bias += a.wtime[lz == 32 ? a.ntime - 1 : min(31 - lz, a.ntime - 1)];
-                                p = silu_scaled(__builtin_fmaf(st[r], a.score_scale, bias * -LOG2E));
-                            } else {
-                                p = silu_scaled(st[r] * a.score_scale);
+                                bias += a.wtime[lz == 32 ? a.ntime - 1
+                                                         : min(31 - lz, a.ntime - 1)];
+                                m[i] = __builtin_fmaf(st[4 * rq + i], a.score_scale, bias * -LOG2E);
                             }
-                            if (partial) {
-                                const int key = k0 + kvl;
-                                p = (key <= my_row && (key < hist || key == my_row)) ? p : 0.0f;
-                            }
-                            p4[i] = p;
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) m[i] = st[4 * rq + i] * a.score_scale;
                         }
+                        if (partial) {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int key = k0 + kb * 32 + 8 * rq + 4 * g + i;
+                                m[i] = (key <= my_row && (key < hist || key == my_row)) ? m[i]
+                                                                                      : 0x1p100f;
+                            }
+                        }
+                        float p4[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) p4[i] = silu_scaled(m[i]);
 #pragma unroll
                         for (int db = 0; db < D / 32; ++db) {
                             const float4 vv = *reinterpret_cast<const float4*>(
