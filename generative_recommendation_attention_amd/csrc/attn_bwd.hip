@@ -311,13 +311,13 @@ __device__ __forceinline__ void store_rows(uint16_t* base, int rows, int row_byt
 // and the rest are full.  LDS slot: Q (row reads), Q (transposed), dO (row
 // reads), dO (transposed).
 // ---------------------------------------------------------------------------
-// Three workgroups per CU (at most 168 VGPRs) at d = 64 for the plain kernels
-// (no spills: 0.616 -> 0.605 ms for the backward at 16 x 4096) and for the
-// bias form under the target-aware mask (some spilled, none inside the block
-// loop: 1.503 -> 1.403 ms for its backward at 16 x (3072 + 1024)); the causal
-// bias form measured slower that way (1.126 -> 1.239 ms).
+// Three workgroups per CU (at most 168 VGPRs) at d = 64: the plain kernels fit
+// without spills (0.616 -> 0.605 ms for the backward at 16 x 4096), the bias
+// forms spill a few registers outside the block loop (causal: 0.933 -> 0.865
+// ms for its backward at 16 x 4096; under the target-aware mask 1.503 ->
+// 1.403 ms at 16 x (3072 + 1024)).  At d = 128 two.
 template <typename T, int D, bool FUSED, bool TGT, bool RAB = false>
-__global__ __launch_bounds__(256, (D == 64 && (TGT || !RAB)) ? 3 : 2) void attn_bwd_dkv(
+__global__ __launch_bounds__(256, (D == 64) ? 3 : 2) void attn_bwd_dkv(
         typename BwdArgsOf<RAB>::type a) {
     using C = BwdCfg<D>;
     using M = Mfma<T>;
@@ -877,11 +877,13 @@ __global__ __launch_bounds__(256, (RAB && !TGT && D == 64) ? 3 : 2) void attn_bw
                         // (the keys' timestamps read again: kept in registers
                         // across the products they pushed this kernel's
                         // loop-invariant values out to scratch)
+                        // (the empty asm with a memory clobber keeps the
+                        // compiler from reusing the first read)
                         const unsigned char* ra = lds + NS * SLOT + (c % NS) * RABB_WORDS * 4;
+                        asm volatile("" ::: "memory");
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
-                            tk[j] = *reinterpret_cast<const volatile u32x4*>(
-                                    ra + 4 * (4 * g + 8 * j));
+                            tk[j] = *reinterpret_cast<const u32x4*>(ra + 4 * (4 * g + 8 * j));
                         prev = min(31 - ffbh_u32(trp1 - tk[0][0]), cap);
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
