@@ -66,12 +66,12 @@ TRAFFIC = {
     "sources": ("generative_recommendation_attention_amd/csrc/attn_fwd.hip",
                 "generative_recommendation_attention_amd/csrc/schedule.h",
                 "generative_recommendation_attention_amd/csrc/schedule.hip"),
-    "sha256": "1d3e2a655df6fe361cf973e89f6337d8cfa1c8aa70c39da7d7595e092a978ab5",
+    "sha256": "f71bb715f40468874d3c6e853353c641dcd412704f4a0b88b897255f27920fb0",
     "fetch_scale": 2.0,
     "write_scale": 1.0,
     # mean over the launches that take the timed calls' form
-    "fetch_kib": {1: 293.7, 2: 94411.1, 3: 1232176.1, 4: 366012.7, 5: 397340.2},
-    "write_kib": {1: 176.7, 2: 39525.5, 3: 141282.9, 4: 54574.0, 5: 264995.4},
+    "fetch_kib": {1: 293.2, 2: 94920.4, 3: 1279169.6, 4: 369688.0, 5: 397331.0},
+    "write_kib": {1: 200.7, 2: 39523.3, 3: 141291.6, 4: 54578.8, 5: 264972.9},
 }
 
 
