@@ -850,23 +850,26 @@ void attn_bwd_dq(
                     // r from lane (g, (l + o) mod 32): query wr0 + l + o, distance
                     // wr0 - k0 + l, or, when l + o wraps past 31, query
                     // wr0 + l + o - 32, distance wr0 - k0 + l - 32.  Every pair is
-                    // taken by exactly one lane.
-                    float dhi = 0.0f, dlo = 0.0f;
+                    // taken by exactly one lane.  (A wave of candidate rows
+                    // only has nothing to add along diagonals: skipped.)
+                    if (!TGT || wr0 < hist) {
+                        float dhi = 0.0f, dlo = 0.0f;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int o = 8 * (r >> 2) + 4 * g + (r & 3);
-                        const float x = __shfl(dgl[r], 32 * g + ((l32 + o) & 31), 64);
-                        if (l32 + o <= 31)
-                            dhi += x;
-                        else
-                            dlo += x;
-                    }
-                    dhi += __shfl(dhi, l32 + 32, 64);   // the other half's keys
-                    dlo += __shfl(dlo, l32 + 32, 64);
-                    if (g == 0) {
-                        float* rw = ring + 256 * wv;
-                        rw[(wr0 - k0 + l32) & 255] += dhi;
-                        rw[(wr0 - k0 + l32 - 32) & 255] += dlo;
+                        for (int r = 0; r < 16; ++r) {
+                            const int o = 8 * (r >> 2) + 4 * g + (r & 3);
+                            const float x = __shfl(dgl[r], 32 * g + ((l32 + o) & 31), 64);
+                            if (l32 + o <= 31)
+                                dhi += x;
+                            else
+                                dlo += x;
+                        }
+                        dhi += __shfl(dhi, l32 + 32, 64);   // the other half's keys
+                        dlo += __shfl(dlo, l32 + 32, 64);
+                        if (g == 0) {
+                            float* rw = ring + 256 * wv;
+                            rw[(wr0 - k0 + l32) & 255] += dhi;
+                            rw[(wr0 - k0 + l32 - 32) & 255] += dlo;
+                        }
                     }
                     // Time buckets: runs of equal buckets along the lane's keys.  The
                     // capped bucket of v_ffbh_u32 result f is min(31 - f, ntime - 1)
