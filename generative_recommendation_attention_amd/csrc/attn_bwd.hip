@@ -138,21 +138,44 @@ __device__ __forceinline__ bool rab_far(int rmin, int kmax, int ntime) {
 // Sum of each of a lane's 16 registers over the 32 lanes of its half-wave,
 // by recursive halving (four exchanges that each halve the registers a lane
 // carries, then one that completes the sum): lane l ends with the sum of
-// register (l >> 1) & 15.
+// register (l >> 1) & 15.  The exchanges run on the vector ALUs, not through
+// LDS: partners l ^ 16 by v_permlane16_swap (which swaps the odd 16-lane rows
+// of one register with the even rows of another, so each lane of a row pair
+// ends with its own half and its partner's, no select needed), then l ^ 15,
+// l ^ 7, l ^ 2 and l ^ 1 by DPP (row mirror, half-row mirror, two quad
+// permutations).  Those partners differ from l in bit 3, 2, 1 and 0 in turn,
+// and together with 16 they reach all 32 lanes, so every lane's total covers
+// its half-wave.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32c(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                             0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float half_wave_column_sum(const f32x16& x, int l32) {
-    const bool b4 = l32 & 16, b3 = l32 & 8, b2 = l32 & 4, b1 = l32 & 2;
+    constexpr int ROW_MIRROR = 0x140, ROW_HALF_MIRROR = 0x141;
+    constexpr int QUAD_XOR2 = 2 | (3 << 2) | (0 << 4) | (1 << 6);
+    constexpr int QUAD_XOR1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);
+    const bool b3 = l32 & 8, b2 = l32 & 4, b1 = l32 & 2;
     float y[8], z[4], w[2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        y[i] = (b4 ? x[i + 8] : x[i]) + __shfl_xor(b4 ? x[i] : x[i + 8], 16, 64);
+    for (int i = 0; i < 8; ++i) {
+        // (vector elements copied to scalars first: __builtin_bit_cast of an
+        // element of a vector-typed value reads element 0 with this compiler)
+        const float lo = x[i], hi = x[i + 8];
+        const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, lo),
+                                                         __builtin_bit_cast(unsigned, hi), false,
+                                                         false);
+        const unsigned r0 = r[0], r1 = r[1];
+        y[i] = __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        z[i] = (b3 ? y[i + 4] : y[i]) + __shfl_xor(b3 ? y[i] : y[i + 4], 8, 64);
+        z[i] = (b3 ? y[i + 4] : y[i]) + dpp_f32c<ROW_MIRROR>(b3 ? y[i] : y[i + 4]);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-        w[i] = (b2 ? z[i + 2] : z[i]) + __shfl_xor(b2 ? z[i] : z[i + 2], 4, 64);
-    const float u = (b1 ? w[1] : w[0]) + __shfl_xor(b1 ? w[0] : w[1], 2, 64);
-    return u + __shfl_xor(u, 1, 64);
+        w[i] = (b2 ? z[i + 2] : z[i]) + dpp_f32c<ROW_HALF_MIRROR>(b2 ? z[i] : z[i + 2]);
+    const float u = (b1 ? w[1] : w[0]) + dpp_f32c<QUAD_XOR2>(b1 ? w[0] : w[1]);
+    return u + dpp_f32c<QUAD_XOR1>(u);
 }
 
 // Shapes shared by both kernels: 4 waves of 32 rows (128 rows per item), 32-row
