@@ -600,18 +600,19 @@ __global__ __launch_bounds__(256, (D == 64) ? 3 : 2) void attn_bwd_dkv(
 //  whole launch and are summed over the wave once at its end (this measured
 //  1.313 -> 1.249 ms for the bias backward at 16 x 4096; per-block wave sums
 //  and LDS atomics before).  The bins go to the partial at the end.
-//  Three workgroups per CU (168 VGPRs, about 20 spilled, none reloaded inside
-//  the block loop) for the causal bias form at d = 64, whose waves wait on
-//  LDS for most of their cycles: 1.244 -> 1.126 ms for its backward at
-//  16 x 4096; under the target-aware mask (some 70 spilled) it measured
-//  slower, 1.498 -> 1.790.  A spill reloaded inside the loop costs more than
+//  Three workgroups per CU (168 VGPRs, 10-15 spilled, none reloaded inside
+//  the block loop) for the bias forms at d = 64, whose waves wait on LDS for
+//  most of their cycles: 1.244 -> 1.126 ms for the causal form's backward at
+//  16 x 4096; under the target-aware mask (about 30 spilled since the column
+//  sums left LDS) 1.065 -> 0.921 ms at 16 x (3072 + 1024), where it had
+//  measured slower with 70 spilled.  A spill reloaded inside the loop costs more than
 //  its load: the compiler's wait for it counts the tile loads issued before
 //  it too, so the next block's prefetch stops overlapping.
 // Four workgroups per CU for the plain forms at d = 64 (128 VGPRs, no
 // spills; 35 KB of LDS each): 0.577 -> 0.564 ms for the backward at
 // 16 x 4096.
 template <typename T, int D, bool FUSED, bool TGT, bool RAB = false>
-__global__ __launch_bounds__(256, (!RAB && D == 64) ? 4 : (RAB && !TGT && D == 64) ? 3 : 2)
+__global__ __launch_bounds__(256, (!RAB && D == 64) ? 4 : (RAB && D == 64) ? 3 : 2)
 void attn_bwd_dq(
         typename BwdArgsOf<RAB>::type a) {
     using C = BwdCfg<D>;
@@ -886,13 +887,18 @@ void attn_bwd_dq(
                             else
                                 dlo += x;
                         }
-                        dhi += __shfl(dhi, l32 + 32, 64);   // the other half's keys
-                        dlo += __shfl(dlo, l32 + 32, 64);
-                        if (g == 0) {
-                            float* rw = ring + 256 * wv;
-                            rw[(wr0 - k0 + l32) & 255] += dhi;
-                            rw[(wr0 - k0 + l32 - 32) & 255] += dlo;
-                        }
+                        // The two halves' keys combined by one v_permlane32_swap
+                        // (the upper 32 lanes of dhi trade places with the lower
+                        // 32 of dlo): lanes 0-31 end with both halves' dhi,
+                        // lanes 32-63 with both halves' dlo, and every lane adds
+                        // its sum to the ring at its own distance.
+                        const unsigned hi_u = __builtin_bit_cast(unsigned, dhi);
+                        const unsigned lo_u = __builtin_bit_cast(unsigned, dlo);
+                        const auto sw = __builtin_amdgcn_permlane32_swap(hi_u, lo_u, false, false);
+                        const unsigned s0 = sw[0], s1 = sw[1];
+                        float* rw = ring + 256 * wv;
+                        rw[(wr0 - k0 + l32 - 32 * g) & 255] +=
+                                __builtin_bit_cast(float, s0) + __builtin_bit_cast(float, s1);
                     }
                     // Time buckets: runs of equal buckets along the lane's keys.  The
                     // capped bucket of v_ffbh_u32 result f is min(31 - f, ntime - 1)
