@@ -39,6 +39,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "device_common.h"
 #include "internal.h"
@@ -176,6 +177,57 @@ __device__ __forceinline__ float half_wave_column_sum(const f32x16& x, int l32) 
         w[i] = (b2 ? z[i + 2] : z[i]) + dpp_f32c<ROW_HALF_MIRROR>(b2 ? z[i] : z[i + 2]);
     const float u = (b1 ? w[1] : w[0]) + dpp_f32c<QUAD_XOR2>(b1 ? w[0] : w[1]);
     return u + dpp_f32c<QUAD_XOR1>(u);
+}
+
+// One register's share of the diagonal sums of a 32 x 32 score block, on the
+// vector ALUs.  Lane (g, l) holds query l and, in register r, key
+// S + 4g with S = 8(r/4) + r%4.  Both half-waves take the same pattern, as if
+// their key were S: dhi[l] += x[l + S] (no wrap) and dlo[l] += x[l + S - 32]
+// (wrap), within the half-wave; the second half's real key is 4 further, so
+// its sums sit 4 distances lower, which the combine below accounts for.  A
+// 32-lane shift is a row shift (DPP) for the part within a 16-lane row and,
+// for the part crossing into the other row, a row shift of the other row's
+// values, which one v_permlane16_swap of the register with itself provides
+// (op holds the even row's values in the odd rows, sp the odd row's in the
+// even rows); row masks send each part to dhi or dlo.
+template <int R>
+__device__ __forceinline__ void diag_step(float x, float& dhi, float& dlo) {
+    constexpr int S = 8 * (R >> 2) + (R & 3);
+    constexpr int ROW_SHL = 0x100, ROW_SHR = 0x110, QUAD_ID = 0xE4;
+    constexpr int EVEN_ROWS = 0x5, ODD_ROWS = 0xA;
+    const unsigned xu = __builtin_bit_cast(unsigned, x);
+    auto moved = [](unsigned v, auto ctrl_c, auto rows_c) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0u, v, decltype(ctrl_c)::value,
+                                                                     decltype(rows_c)::value, 0xF,
+                                                                     true));
+    };
+    using std::integral_constant;
+    if constexpr (S == 0) {
+        dhi += x;
+    } else {
+        const auto sw = __builtin_amdgcn_permlane16_swap(xu, xu, false, false);
+        const unsigned op = sw[0], sp = sw[1];
+        if constexpr (S < 16) {
+            dhi += moved(xu, integral_constant<int, ROW_SHL + S>{}, integral_constant<int, 0xF>{});
+            dhi += moved(sp, integral_constant<int, ROW_SHR + 16 - S>{},
+                         integral_constant<int, EVEN_ROWS>{});
+            dlo += moved(op, integral_constant<int, ROW_SHR + 16 - S>{},
+                         integral_constant<int, ODD_ROWS>{});
+        } else {
+            constexpr int B = S - 16;
+            constexpr int CTRL = B == 0 ? QUAD_ID : ROW_SHL + B;
+            dhi += moved(sp, integral_constant<int, CTRL>{}, integral_constant<int, EVEN_ROWS>{});
+            dlo += moved(op, integral_constant<int, CTRL>{}, integral_constant<int, ODD_ROWS>{});
+            if constexpr (B > 0)
+                dlo += moved(xu, integral_constant<int, ROW_SHR + 16 - B>{},
+                             integral_constant<int, 0xF>{});
+        }
+    }
+}
+template <int... Rs>
+__device__ __forceinline__ void diag_steps(const f32x16& d, float& dhi, float& dlo,
+                                           std::integer_sequence<int, Rs...>) {
+    (diag_step<Rs>(static_cast<float>(d[Rs]), dhi, dlo), ...);
 }
 
 // Shapes shared by both kernels: 4 waves of 32 rows (128 rows per item), 32-row
@@ -878,27 +930,23 @@ void attn_bwd_dq(
                     // only has nothing to add along diagonals: skipped.)
                     if (!TGT || wr0 < hist) {
                         float dhi = 0.0f, dlo = 0.0f;
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int o = 8 * (r >> 2) + 4 * g + (r & 3);
-                            const float x = __shfl(dgl[r], 32 * g + ((l32 + o) & 31), 64);
-                            if (l32 + o <= 31)
-                                dhi += x;
-                            else
-                                dlo += x;
-                        }
-                        // The two halves' keys combined by one v_permlane32_swap
-                        // (the upper 32 lanes of dhi trade places with the lower
-                        // 32 of dlo): lanes 0-31 end with both halves' dhi,
-                        // lanes 32-63 with both halves' dlo, and every lane adds
-                        // its sum to the ring at its own distance.
+                        diag_steps(dgl, dhi, dlo, std::make_integer_sequence<int, 16>{});
+                        // The halves combined: one v_permlane32_swap (the upper
+                        // 32 lanes of dhi trade places with the lower 32 of dlo)
+                        // leaves the first half's dhi, dlo in lanes 0-31, 32-63
+                        // of s0 and the second half's in s1; the second half's
+                        // sums sit 4 distances lower, so s1 is read 4 lanes on
+                        // (mod 64, which carries its dhi of distances -4 .. -1
+                        // into the wrapped sums).  Lanes 0-31 end with distance
+                        // l, lanes 32-63 with l - 32, and every lane adds its
+                        // sum to the ring at its own distance.
                         const unsigned hi_u = __builtin_bit_cast(unsigned, dhi);
                         const unsigned lo_u = __builtin_bit_cast(unsigned, dlo);
                         const auto sw = __builtin_amdgcn_permlane32_swap(hi_u, lo_u, false, false);
                         const unsigned s0 = sw[0], s1 = sw[1];
+                        const float s1n = __shfl(__builtin_bit_cast(float, s1), (lane + 4) & 63, 64);
                         float* rw = ring + 256 * wv;
-                        rw[(wr0 - k0 + l32 - 32 * g) & 255] +=
-                                __builtin_bit_cast(float, s0) + __builtin_bit_cast(float, s1);
+                        rw[(wr0 - k0 + l32 - 32 * g) & 255] += __builtin_bit_cast(float, s0) + s1n;
                     }
                     // Time buckets: runs of equal buckets along the lane's keys.  The
                     // capped bucket of v_ffbh_u32 result f is min(31 - f, ntime - 1)
