@@ -115,16 +115,22 @@ __device__ __forceinline__ int ffbh_u32(uint32_t x) {
 }
 
 // Wave-wide minimum / maximum (every lane takes part; the result is uniform).
-__device__ __forceinline__ int wave_min_i32(int x) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) x = min(x, __shfl_xor(x, o, 64));
-    return __builtin_amdgcn_readfirstlane(x);
+// Minimum / maximum over the wave without LDS: within each 16-lane row by
+// DPP (quad permutations xor 1 and xor 2, then the half-row and row mirrors,
+// which pair each quad and then each half-row with the other), then the four
+// rows' results read out to scalars.  Every lane must be active.
+template <bool MAX>
+__device__ __forceinline__ int wave_reduce_i32(int x) {
+    auto op = [](int u, int v) { return MAX ? max(u, v) : min(u, v); };
+    x = op(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));    // quad xor 1
+    x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));    // quad xor 2
+    x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false));   // row half mirror
+    x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false));   // row mirror
+    return op(op(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+              op(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
-__device__ __forceinline__ int wave_max_i32(int x) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) x = max(x, __shfl_xor(x, o, 64));
-    return __builtin_amdgcn_readfirstlane(x);
-}
+__device__ __forceinline__ int wave_min_i32(int x) { return wave_reduce_i32<false>(x); }
+__device__ __forceinline__ int wave_max_i32(int x) { return wave_reduce_i32<true>(x); }
 
 // Blocks whose every pair lies in the last time bucket (the latest key at
 // least 2^(ntime-1) - 1 before the earliest query) take the time term as one
