@@ -466,15 +466,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_mfma16(typename ArgsOf<MA
                 // latest key timestamp of each 32-key block (lanes past the
                 // tile or the sequence read 0, which can only make a block
                 // look nearer)
+                // (the maximum within each 16-lane row by DPP: quad
+                // permutations xor 1 and xor 2, then the half-row and row
+                // mirrors; a block's is the larger of its two rows')
                 if constexpr (FAR) {
                     int m = (int)rab_ts;
-#pragma unroll
-                    for (int off = 1; off < 32; off <<= 1) m = max(m, __shfl_xor(m, off));
+                    m = max(m, __builtin_amdgcn_update_dpp(m, m, 0xB1, 0xF, 0xF, false));
+                    m = max(m, __builtin_amdgcn_update_dpp(m, m, 0x4E, 0xF, 0xF, false));
+                    m = max(m, __builtin_amdgcn_update_dpp(m, m, 0x141, 0xF, 0xF, false));
+                    m = max(m, __builtin_amdgcn_update_dpp(m, m, 0x140, 0xF, 0xF, false));
                     const int sh = 2 * (c % NS);
                     uint32_t bits = 0;
 #pragma unroll
                     for (int kb = 0; kb < NKB; ++kb) {
-                        const int kmax = __builtin_amdgcn_readlane(m, 32 * kb);
+                        const int kmax = max(__builtin_amdgcn_readlane(m, 32 * kb),
+                                             __builtin_amdgcn_readlane(m, 32 * kb + 16));
                         if ((int64_t)rmin - kmax >= far_gap) bits |= 1u << kb;
                     }
                     far_mask = (far_mask & ~(3u << sh)) | (bits << sh);
