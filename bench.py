@@ -66,12 +66,12 @@ TRAFFIC = {
     "sources": ("generative_recommendation_attention_amd/csrc/attn_fwd.hip",
                 "generative_recommendation_attention_amd/csrc/schedule.h",
                 "generative_recommendation_attention_amd/csrc/schedule.hip"),
-    "sha256": "f71bb715f40468874d3c6e853353c641dcd412704f4a0b88b897255f27920fb0",
+    "sha256": "ee703a20371daf55b3106a940942e2629fd849947452290a65960569e7976662",
     "fetch_scale": 2.0,
     "write_scale": 1.0,
     # mean over the launches that take the timed calls' form
-    "fetch_kib": {1: 293.2, 2: 94920.4, 3: 1279169.6, 4: 369688.0, 5: 397331.0},
-    "write_kib": {1: 200.7, 2: 39523.3, 3: 141291.6, 4: 54578.8, 5: 264972.9},
+    "fetch_kib": {1: 294.0, 2: 94499.5, 3: 1234048.4, 4: 387225.0, 5: 397324.7},
+    "write_kib": {1: 200.7, 2: 39525.2, 3: 141251.6, 4: 54574.7, 5: 264980.7},
 }
 
 
