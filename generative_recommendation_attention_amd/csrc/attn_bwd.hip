@@ -394,7 +394,7 @@ __device__ __forceinline__ void store_rows(uint16_t* base, int rows, int row_byt
 // ---------------------------------------------------------------------------
 // Three workgroups per CU (at most 168 VGPRs) at d = 64: the plain kernels fit
 // without spills (0.616 -> 0.605 ms for the backward at 16 x 4096), the bias
-// forms spill a few registers outside the block loop (causal: 0.933 -> 0.865
+// forms spill none (causal) or a few outside the block loop (causal: 0.933 -> 0.865
 // ms for its backward at 16 x 4096; under the target-aware mask 1.503 ->
 // 1.403 ms at 16 x (3072 + 1024)).  At d = 128 two.
 template <typename T, int D, bool FUSED, bool TGT, bool RAB = false>
@@ -642,9 +642,9 @@ __global__ __launch_bounds__(256, (D == 64) ? 3 : 2) void attn_bwd_dkv(
 // atomics cost on the order of a hundred cycles per instruction here, so the
 // sums avoid them where they can.)
 //  Position: a wave first sums its 32 x 32 block of dS along each diagonal
-//  with cross-lane shuffles (lane l ends with the sums for distances
-//  wr0 - k0 + l and wr0 - k0 + l - 32), then adds them to a 256-entry ring of
-//  its own in LDS
+//  with DPP row shifts and lane swaps (lane l < 32 ends with the sum for
+//  distance wr0 - k0 + l, lane 32 + l with wr0 - k0 + l - 32), then adds them
+//  to a 256-entry ring of its own in LDS
 //  (distance mod 256; plain read-add-write, the wave being its only writer).
 //  A block of keys k0 .. k0+31 touches distances q0 - k0 - 31 .. q0 - k0 + 127
 //  of the item's rows, so once block c is done, distances above
@@ -658,9 +658,9 @@ __global__ __launch_bounds__(256, (D == 64) ? 3 : 2) void attn_bwd_dkv(
 //  whole launch and are summed over the wave once at its end (this measured
 //  1.313 -> 1.249 ms for the bias backward at 16 x 4096; per-block wave sums
 //  and LDS atomics before).  The bins go to the partial at the end.
-//  Three workgroups per CU (168 VGPRs, 10-15 spilled, none reloaded inside
-//  the block loop) for the bias forms at d = 64, whose waves wait on LDS for
-//  most of their cycles: 1.244 -> 1.126 ms for the causal form's backward at
+//  Three workgroups per CU (168 VGPRs, no spills since the cross-lane sums
+//  moved to DPP) for the bias forms at d = 64, whose waves then waited on LDS
+//  for most of their cycles: 1.244 -> 1.126 ms for the causal form's backward at
 //  16 x 4096; under the target-aware mask (about 30 spilled since the column
 //  sums left LDS) 1.065 -> 0.921 ms at 16 x (3072 + 1024), where it had
 //  measured slower with 70 spilled.  A spill reloaded inside the loop costs more than
@@ -928,12 +928,13 @@ void attn_bwd_dq(
                     // distance of register r: wr0 + l32 - k0 - 4g - (8(r/4) + r%4);
                     // masked pairs add exactly zero
                     // Diagonal sums: register r of lane (g, l) holds query wr0 + l,
-                    // key k0 + o, o = 8(r/4) + 4g + r%4.  Lane (g, l) takes register
-                    // r from lane (g, (l + o) mod 32): query wr0 + l + o, distance
-                    // wr0 - k0 + l, or, when l + o wraps past 31, query
-                    // wr0 + l + o - 32, distance wr0 - k0 + l - 32.  Every pair is
-                    // taken by exactly one lane.  (A wave of candidate rows
-                    // only has nothing to add along diagonals: skipped.)
+                    // key k0 + o, o = 8(r/4) + 4g + r%4.  Lane (g, l) gathers
+                    // register r of lane (g, (l + S) mod 32), S = o - 4g (see
+                    // diag_step): a pair of distance l - 4g, or, when l + S
+                    // wraps past 31, of distance l - 4g - 32 (relative to
+                    // wr0 - k0).  Every pair is taken by exactly one lane.  (A
+                    // wave of candidate rows only has nothing to add along
+                    // diagonals: skipped.)
                     if (!TGT || wr0 < hist) {
                         float dhi = 0.0f, dlo = 0.0f;
                         diag_steps(dgl, dhi, dlo, std::make_integer_sequence<int, 16>{});
