@@ -264,7 +264,7 @@ struct LaneOffsets {
     using C = BwdCfg<D>;
     int gk[C::LPA], gv[C::LPA];   // global byte offsets of this lane's loads (row-read, transposed swizzle)
     int dst[C::LPA];              // LDS byte offset of each load inside an array
-    int rowrd[C::NKS];            // row read of row l32, k-step ks
+    int rowrd[C::NKS];            // row read of row l32, k-step ks (= rowrd[0] ^ 32 ks)
     int tr_lo[C::NDB], tr_hi[C::NDB];   // transposing reads, head-dim block db
     __device__ LaneOffsets(int lane, int wv, int row_bytes) {
         constexpr int CH = C::CH;
@@ -287,6 +287,29 @@ struct LaneOffsets {
             const int cb = 64 * db + v_colb;
             tr_lo[db] = v_row * C::RB + 16 * ((cb >> 4) ^ vswz<CH>(v_row)) + (cb & 15);
             tr_hi[db] = (v_row + 8) * C::RB + 16 * ((cb >> 4) ^ vswz<CH>(v_row + 8)) + (cb & 15);
+        }
+    }
+};
+
+// The row-read offsets of a block's k-steps.  (2 ks + g) ^ swizzle =
+// 2 ks ^ (g ^ swizzle), so k-step ks's offset is k-step 0's XOR 32 ks (the
+// row's base has no bits below the row size).  At d = 128 the eight offsets
+// held across the block loop pushed other values to scratch, whose reloads
+// inside the loop waited for the prefetched tiles too; there the offsets are
+// rebuilt from k-step 0's per block (an empty asm makes that value new in
+// each block, so the compiler does not hoist the XORs back out).
+template <int D>
+struct RowReads {
+    int r[BwdCfg<D>::NKS];
+    __device__ __forceinline__ explicit RowReads(const LaneOffsets<D>& lo) {
+        if constexpr (D == 128) {
+            int r0 = lo.rowrd[0];
+            asm volatile("" : "+v"(r0));
+#pragma unroll
+            for (int ks = 0; ks < BwdCfg<D>::NKS; ++ks) r[ks] = r0 ^ (32 * ks);
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < BwdCfg<D>::NKS; ++ks) r[ks] = lo.rowrd[ks];
         }
     }
 };
@@ -567,10 +590,11 @@ __global__ __launch_bounds__(256, (D == 64) ? 3 : 2) void attn_bwd_dkv(
                         }
                     }
                 }
+                const RowReads<D> rr(lo);
 #pragma unroll
                 for (int ks = 0; ks < C::NKS; ++ks) {
-                    st = M::mma(row_read<T, D>(sl, lo.rowrd[ks]), kop[ks], st);
-                    dp = M::mma(row_read<T, D>(sl + 2 * C::ARR, lo.rowrd[ks]), vop[ks], dp);
+                    st = M::mma(row_read<T, D>(sl, rr.r[ks]), kop[ks], st);
+                    dp = M::mma(row_read<T, D>(sl + 2 * C::ARR, rr.r[ks]), vop[ks], dp);
                 }
                 // lane: key kw0 + l32; register r: query q0 + 8(r/4) + 4g + r%4
                 const bool masked = q0 == kw0 || (TGT && kw0 + 31 >= hist);
@@ -867,10 +891,11 @@ void attn_bwd_dq(
                         }
                     }
                 }
+                const RowReads<D> rr(lo);
 #pragma unroll
                 for (int ks = 0; ks < C::NKS; ++ks) {
-                    st = M::mma(row_read<T, D>(sl, lo.rowrd[ks]), qop[ks], st);
-                    dp = M::mma(row_read<T, D>(sl + 2 * C::ARR, lo.rowrd[ks]), oop[ks], dp);
+                    st = M::mma(row_read<T, D>(sl, rr.r[ks]), qop[ks], st);
+                    dp = M::mma(row_read<T, D>(sl + 2 * C::ARR, rr.r[ks]), oop[ks], dp);
                 }
                 // lane: query wr0 + l32; register r: key k0 + 8(r/4) + 4g + r%4
                 const bool masked = k0 + 31 >= wr0 || (TGT && k0 + 31 >= hist);
