@@ -196,40 +196,59 @@ __device__ __forceinline__ float half_wave_column_sum(const f32x16& x, int l32) 
 // values, which one v_permlane16_swap of the register with itself provides
 // (op holds the even row's values in the odd rows, sp the odd row's in the
 // even rows); row masks send each part to dhi or dlo.
+// acc += src moved by a DPP pattern, in the rows of a row mask only (the
+// other rows keep acc: a DPP add leaves the lanes of disabled rows
+// unwritten).  One instruction; the compiler's own form was a DPP move into
+// a zeroed register and an add.  (The s_nop covers the wait states a DPP read
+// needs after the instruction that wrote its source.)
+#define HSTU_ADD_DPP(acc, src, pattern, rows)                                             \
+    asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %0 " pattern " row_mask:" rows                \
+        " bank_mask:0xf bound_ctrl:1"                                                      \
+        : "+v"(acc)                                                                        \
+        : "v"(src))
+#define HSTU_ROW_SHL(n) "row_shl:" #n
+#define HSTU_ROW_SHR(n) "row_shr:" #n
 template <int R>
 __device__ __forceinline__ void diag_step(float x, float& dhi, float& dlo) {
     constexpr int S = 8 * (R >> 2) + (R & 3);
-    constexpr int ROW_SHL = 0x100, ROW_SHR = 0x110, QUAD_ID = 0xE4;
-    constexpr int EVEN_ROWS = 0x5, ODD_ROWS = 0xA;
-    const unsigned xu = __builtin_bit_cast(unsigned, x);
-    auto moved = [](unsigned v, auto ctrl_c, auto rows_c) {
-        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0u, v, decltype(ctrl_c)::value,
-                                                                     decltype(rows_c)::value, 0xF,
-                                                                     true));
-    };
-    using std::integral_constant;
     if constexpr (S == 0) {
         dhi += x;
-    } else {
-        const auto sw = __builtin_amdgcn_permlane16_swap(xu, xu, false, false);
-        const unsigned op = sw[0], sp = sw[1];
-        if constexpr (S < 16) {
-            dhi += moved(xu, integral_constant<int, ROW_SHL + S>{}, integral_constant<int, 0xF>{});
-            dhi += moved(sp, integral_constant<int, ROW_SHR + 16 - S>{},
-                         integral_constant<int, EVEN_ROWS>{});
-            dlo += moved(op, integral_constant<int, ROW_SHR + 16 - S>{},
-                         integral_constant<int, ODD_ROWS>{});
-        } else {
-            constexpr int B = S - 16;
-            constexpr int CTRL = B == 0 ? QUAD_ID : ROW_SHL + B;
-            dhi += moved(sp, integral_constant<int, CTRL>{}, integral_constant<int, EVEN_ROWS>{});
-            dlo += moved(op, integral_constant<int, CTRL>{}, integral_constant<int, ODD_ROWS>{});
-            if constexpr (B > 0)
-                dlo += moved(xu, integral_constant<int, ROW_SHR + 16 - B>{},
-                             integral_constant<int, 0xF>{});
-        }
+        return;
     }
+    const unsigned xu = __builtin_bit_cast(unsigned, x);
+    const auto sw = __builtin_amdgcn_permlane16_swap(xu, xu, false, false);
+    const unsigned opu = sw[0], spu = sw[1];
+    const float op = __builtin_bit_cast(float, opu), sp = __builtin_bit_cast(float, spu);
+    // S < 16: dhi += row_shl:S(x) (all rows), dhi += row_shr:16-S(sp) (even
+    // rows), dlo += row_shr:16-S(op) (odd rows).  S = 16 + B: dhi +=
+    // row_shl:B(sp) (even rows), dlo += row_shl:B(op) (odd rows), dlo +=
+    // row_shr:16-B(x) (all rows); B = 0 moves sp and op unshifted.
+#define HSTU_DIAG_LO(s, r16)                                                                \
+    if constexpr (S == s) {                                                                \
+        HSTU_ADD_DPP(dhi, x, HSTU_ROW_SHL(s), "0xf");                                     \
+        HSTU_ADD_DPP(dhi, sp, HSTU_ROW_SHR(r16), "0x5");                                  \
+        HSTU_ADD_DPP(dlo, op, HSTU_ROW_SHR(r16), "0xa");                                  \
+    }
+#define HSTU_DIAG_HI(s, b, r16)                                                             \
+    if constexpr (S == s) {                                                                \
+        HSTU_ADD_DPP(dhi, sp, HSTU_ROW_SHL(b), "0x5");                                    \
+        HSTU_ADD_DPP(dlo, op, HSTU_ROW_SHL(b), "0xa");                                    \
+        HSTU_ADD_DPP(dlo, x, HSTU_ROW_SHR(r16), "0xf");                                   \
+    }
+    HSTU_DIAG_LO(1, 15) HSTU_DIAG_LO(2, 14) HSTU_DIAG_LO(3, 13)
+    HSTU_DIAG_LO(8, 8) HSTU_DIAG_LO(9, 7) HSTU_DIAG_LO(10, 6) HSTU_DIAG_LO(11, 5)
+    if constexpr (S == 16) {
+        HSTU_ADD_DPP(dhi, sp, "quad_perm:[0,1,2,3]", "0x5");
+        HSTU_ADD_DPP(dlo, op, "quad_perm:[0,1,2,3]", "0xa");
+    }
+    HSTU_DIAG_HI(17, 1, 15) HSTU_DIAG_HI(18, 2, 14) HSTU_DIAG_HI(19, 3, 13)
+    HSTU_DIAG_HI(24, 8, 8) HSTU_DIAG_HI(25, 9, 7) HSTU_DIAG_HI(26, 10, 6) HSTU_DIAG_HI(27, 11, 5)
+#undef HSTU_DIAG_LO
+#undef HSTU_DIAG_HI
 }
+#undef HSTU_ROW_SHL
+#undef HSTU_ROW_SHR
+#undef HSTU_ADD_DPP
 template <int... Rs>
 __device__ __forceinline__ void diag_steps(const f32x16& d, float& dhi, float& dlo,
                                            std::integer_sequence<int, Rs...>) {
